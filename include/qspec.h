@@ -1,0 +1,208 @@
+/*
+ * qspec.h -- C ABI of libqspec.so: the hot path of quantization-based
+ * self-speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * One packed INT4 weight buffer is read by two modes of the same linear layer:
+ * a W4A4 drafter (weights and activations at four bits) and a W4A16 verifier
+ * (weights at four bits, bf16 activations); a verify step then accepts or
+ * rewrites the drafted tokens.
+ *   Pages: "QSpec: Speculative Decoding with Complementary Quantization
+ *   Schemes", Abstract (arXiv) -- low-precision joint quantization drafts,
+ *   high-precision weight-only quantization verifies, weights and KV cache are
+ *   reused across the two stages; the tech-dashboard summary of QSpec,
+ *   paragraphs 2-4 (W4A16 vs W4A4; draft-then-verify; one shared set of
+ *   quantized weights); the agihunt.info review of SpecQuant, method paragraph
+ *   (a full match is accepted, the first mismatch is rewritten by the parent).
+ * The pages print no formula, layout or precision for these operations; the
+ * readings used are stated at each call.
+ *
+ * Conventions for every call
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps a pointer after the call returns.
+ *  - Arrays are dense and row-major; sizes are int64_t element counts; every
+ *    array pointer must be 16-byte aligned (QSPEC_ERR_ALIGN otherwise).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    null stream).  Buffers must stay alive until that work completes.
+ *  - Outputs are fully overwritten, never accumulated into.  Inputs and
+ *    outputs must not overlap.
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is launched and the status says why (qspec_last_error()
+ *    gives a thread-local message).  A failed launch returns QSPEC_ERR_HIP.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - Calls never abort or exit the process.  They are thread-safe; the only
+ *    global state is a per-device cache of the device check.
+ *  - Non-finite inputs (NaN/Inf weights, activations or logits) are not
+ *    supported: results are unspecified, but every kernel still terminates.
+ */
+#ifndef QSPEC_H_
+#define QSPEC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int qspec_status;
+typedef void* qspec_stream;
+
+enum {
+  QSPEC_OK = 0,
+  QSPEC_ERR_NULL = -1,        /* a required pointer is NULL                  */
+  QSPEC_ERR_SHAPE = -2,       /* a size is out of range or inconsistent      */
+  QSPEC_ERR_UNSUPPORTED = -3, /* group != 128, unknown mode or variant       */
+  QSPEC_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned            */
+  QSPEC_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required     */
+  QSPEC_ERR_DEVICE = -6,      /* current device is not gfx950                */
+  QSPEC_ERR_HIP = -7          /* a HIP runtime call or launch failed         */
+};
+
+/* operation ids for qspec_workspace_bytes */
+enum { QSPEC_OP_GEMM_W4A4 = 1, QSPEC_OP_GEMM_W4A16 = 2, QSPEC_OP_VERIFY = 3 };
+
+/* verify modes */
+enum { QSPEC_VERIFY_GREEDY = 0, QSPEC_VERIFY_SAMPLE = 1 };
+
+/* GEMM kernel families.  Within one family every output row is computed by
+ * the same sequence of operations whatever M is, so row r of Y is bitwise
+ * identical at any M; a caller that needs this (for example greedy
+ * self-speculation that must reproduce plain verifier decoding token for
+ * token) passes the same explicit family for every M.  AUTO picks by M. */
+enum {
+  QSPEC_GEMM_AUTO = 0,
+  QSPEC_GEMM_GEMV = 1,   /* W4A16 only: VALU GEMV with wavefront reduction   */
+  QSPEC_GEMM_SKINNY = 2, /* MFMA, weights streamed once per 64 rows of M     */
+  QSPEC_GEMM_TILED = 3   /* MFMA, LDS-tiled over M and N (prefill shapes)    */
+};
+
+#define QSPEC_GROUP 128
+#define QSPEC_MAX_GAMMA 16
+
+const char* qspec_status_str(qspec_status s);
+const char* qspec_last_error(void);
+const char* qspec_version(void);
+
+/* QSPEC_OK if the current HIP device is gfx950, QSPEC_ERR_DEVICE if not,
+ * QSPEC_ERR_HIP if the runtime cannot be queried.  Every compute call below
+ * performs this check first. */
+qspec_status qspec_device_check(void);
+
+/* Bytes of scratch `ws` that the call with these sizes needs (0 = none).
+ *   QSPEC_OP_GEMM_W4A4 / QSPEC_OP_GEMM_W4A16: (M, N, K)
+ *   QSPEC_OP_VERIFY:                           (B, gamma, V)
+ * The answer is the maximum over all variants and modes, so one workspace
+ * sized by it serves every call of that op with sizes no larger. */
+size_t qspec_workspace_bytes(int op, int64_t a, int64_t b, int64_t c);
+
+/* ---------------------------------------------------------------------------
+ * qspec_pack_w4 -- quantize fp32 weights to the shared INT4 buffer.
+ * One buffer serves both modes (QSpec Abstract: weights reused across the
+ * stages; tech-dashboard summary, paragraph 4: both configurations share the
+ * same quantized weights).  Reading of the unspecified format: per row n and
+ * group j of 128 consecutive k,
+ *     a = max|W[n,k]|;  s = fp16(a / 7.0f)  (IEEE fp32 divide, then RNE);
+ *     q[n,k] = clamp(rne(W[n,k] / float(s)), -8, 7), all 0 when s == 0.
+ *   W   [N][K] fp32 (in).   N >= 1, K >= 128, K % 128 == 0.
+ *   Wq  [N][K/2] u8 (out): byte i of a row holds q[2i] in bits 0-3 and
+ *       q[2i+1] in bits 4-7, two's complement.
+ *   Ws  [N][K/128] fp16 bits (out).
+ *   group must be 128.  Non-finite W, or a/7 beyond the fp16 range, is
+ *   unsupported (results unspecified).
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_pack_w4(const float* W, int64_t N, int64_t K, int group,
+                           uint8_t* Wq, uint16_t* Ws, qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * qspec_quant_act -- per-token INT4 quantization of bf16 activations (the
+ * W4A4 drafter quantizes activations as well as weights: tech-dashboard
+ * summary, paragraph 2; QSpec Abstract, "low-precision joint quantization").
+ * Reading: per row m, a = max_k |x|, s = a / 7.0f kept in fp32, and
+ * q = clamp(rne(x / s), -8, 7) with an IEEE fp32 divide (not a reciprocal
+ * multiply), all codes 0 when a == 0; subnormals are kept.
+ *   X   [M][K] bf16 bits (in).  M >= 1, K >= 128, K % 128 == 0.
+ *   Xq  [M][K/2] u8 (out), same nibble layout as Wq.
+ *   Xs  [M] fp32 (out).
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_quant_act(const uint16_t* X, int64_t M, int64_t K,
+                             uint8_t* Xq, float* Xs, qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * qspec_gemm_w4a4 -- the drafter's linear layer (QSpec Abstract: W4A4 joint
+ * quantization drafts).  Reading:
+ *     P[m,n,g] = sum_{k in group g} qa[m,k] * qw[n,k]     (exact int32)
+ *     Y[m,n]   = Xs[m] * sum_g float(Ws[n,g]) * P[m,n,g]  (fp32 epilogue)
+ * computed with int8 MFMA on the unpacked codes.
+ *   Xq [M][K/2], Xs [M]   from qspec_quant_act.
+ *   Wq [N][K/2], Ws [N][K/128] from qspec_pack_w4.
+ *   Y  [M][N] fp32 (out).
+ *   P  [M][N][K/128] int32 (out, optional: NULL skips it).
+ *   variant: QSPEC_GEMM_AUTO, _SKINNY or _TILED (GEMV is W4A16-only).
+ *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_GEMM_W4A4,M,N,K)
+ *   bytes (NULL allowed when that is 0).
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_gemm_w4a4(const uint8_t* Xq, const float* Xs,
+                             const uint8_t* Wq, const uint16_t* Ws,
+                             int64_t M, int64_t N, int64_t K, int group,
+                             int variant, float* Y, int32_t* P,
+                             void* ws, size_t ws_bytes, qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * qspec_gemm_w4a16 -- the verifier's linear layer (QSpec Abstract:
+ * weight-only quantization verifies; tech-dashboard summary, paragraph 2:
+ * W4A16 keeps activations at higher precision).  Reading:
+ *     Y[m,n] = sum_g float(Ws[n,g]) * sum_{k in g} x[m,k] * q[n,k]
+ * with the codes turned into bf16 in registers, bf16 MFMA (or VALU dot
+ * products for the GEMV family) accumulating each group in fp32, and the
+ * fp16 scale applied in fp32 per group.
+ *   X  [M][K] bf16 bits (in);  Wq, Ws as above;  Y [M][N] fp32 (out).
+ *   variant: QSPEC_GEMM_AUTO, _GEMV, _SKINNY or _TILED.
+ *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_GEMM_W4A16,M,N,K).
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_gemm_w4a16(const uint16_t* X, const uint8_t* Wq,
+                              const uint16_t* Ws, int64_t M, int64_t N,
+                              int64_t K, int group, int variant, float* Y,
+                              void* ws, size_t ws_bytes, qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * qspec_verify -- accept or reject gamma drafted tokens per sequence.
+ * Greedy (mode 0; SpecQuant review, method paragraph: a full match is
+ * accepted and the first mismatch is rewritten by the parent):
+ *     t_i = argmax_v target[b,i,v] (lowest index on ties), i = 0..gamma;
+ *     n = first i < gamma with draft[b,i] != t_i, else gamma;
+ *     out = draft[b,0..n-1], t_n, then -1.
+ * Sampling at temperature 1 (mode 1; tech-dashboard summary, paragraph 3:
+ * the output distribution equals the target's -- the rule of the
+ * speculative-sampling papers QSpec builds on):
+ *     p_i = softmax(target[b,i]), q_i = softmax(draft_logits[b,i]);
+ *     accept draft d_i iff u_accept[b,i] <= p_i(d_i) / q_i(d_i)
+ *     (q_i(d_i) == 0: accept iff p_i(d_i) > 0);
+ *     first reject at n: r = max(0, p_n - q_n) (r = p_n if that sums to 0);
+ *     all accepted: n = gamma, r = p_gamma;
+ *     emitted = smallest j with cumsum(r)_j > u_sample[b] * sum(r)
+ *     (if none: the last j with r_j > 0).
+ *   draft_tok     [B][gamma] int32 in [0, V)   (in)
+ *   draft_logits  [B][gamma][V] fp32   (in; NULL iff greedy)
+ *   target_logits [B][gamma+1][V] fp32 (in)
+ *   u_accept      [B][gamma] fp32 in [0,1) (in; NULL iff greedy)
+ *   u_sample      [B] fp32 in [0,1)        (in; NULL iff greedy)
+ *   n_accept      [B] int32 (out);  out_tok [B][gamma+1] int32 (out, -1 pad)
+ *   1 <= gamma <= QSPEC_MAX_GAMMA, B >= 1, V >= 1.  Out-of-range draft
+ *   tokens are not supported (they are clamped into [0, V) on the device).
+ *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_VERIFY,B,gamma,V).
+ * Decisions are taken in fp32; they can differ from exact arithmetic only
+ * where p/q or the sampling threshold sits within about 1e-6 (relative) of
+ * the decision boundary.
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V,
+                          const int32_t* draft_tok, const float* draft_logits,
+                          const float* target_logits, const float* u_accept,
+                          const float* u_sample, int32_t* n_accept,
+                          int32_t* out_tok, void* ws, size_t ws_bytes,
+                          qspec_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSPEC_H_ */

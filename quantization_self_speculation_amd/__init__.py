@@ -1,0 +1,27 @@
+"""MI355X (gfx950) hot path of quantization-based self-speculative decoding.
+
+One packed INT4 weight buffer serves a W4A4 drafter and a W4A16 verifier; a
+verify step accepts or rewrites the drafted tokens.  Every step runs in the
+hand-written HIP kernels of ``libqspec.so`` (C ABI in ``include/qspec.h``);
+this package only marshals torch tensors (device memory and streams) into
+those calls.  There is no CPU fallback: if the library is missing the calls
+raise.
+"""
+
+from .binding import (  # noqa: F401
+    QSpecError,
+    lib,
+    lib_path,
+    pack_w4,
+    quant_act,
+    gemm_w4a4,
+    gemm_w4a16,
+    verify,
+    workspace_bytes,
+    GEMM_AUTO,
+    GEMM_GEMV,
+    GEMM_SKINNY,
+    GEMM_TILED,
+    VERIFY_GREEDY,
+    VERIFY_SAMPLE,
+)

@@ -1,0 +1,192 @@
+"""ctypes binding of libqspec.so: argument marshalling only.
+
+Each function takes CUDA (HIP) torch tensors, checks dtypes/shapes/contiguity
+on the host, allocates outputs and scratch through torch's caching allocator,
+and calls the C entry point of the same name on torch's current stream.  All
+arithmetic happens in the library's kernels.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqspec.so")
+_lock = threading.Lock()
+_lib = None
+
+GEMM_AUTO, GEMM_GEMV, GEMM_SKINNY, GEMM_TILED = 0, 1, 2, 3
+VERIFY_GREEDY, VERIFY_SAMPLE = 0, 1
+OP_GEMM_W4A4, OP_GEMM_W4A16, OP_VERIFY = 1, 2, 3
+GROUP = 128
+
+
+class QSpecError(RuntimeError):
+    def __init__(self, status, name, detail):
+        super().__init__(f"{name}: status {status} ({detail})")
+        self.status = status
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def lib():
+    """Load libqspec.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m quantization_self_speculation_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        sig = {
+            "qspec_status_str": (ctypes.c_char_p, [I]),
+            "qspec_last_error": (ctypes.c_char_p, []),
+            "qspec_version": (ctypes.c_char_p, []),
+            "qspec_device_check": (I, []),
+            "qspec_workspace_bytes": (SZ, [I, I64, I64, I64]),
+            "qspec_pack_w4": (I, [P, I64, I64, I, P, P, P]),
+            "qspec_quant_act": (I, [P, I64, I64, P, P, P]),
+            "qspec_gemm_w4a4": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
+            "qspec_gemm_w4a16": (I, [P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
+            "qspec_verify": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+        return L
+
+
+def _check(status, name):
+    if status != 0:
+        L = lib()
+        raise QSpecError(status, name, f"{L.qspec_status_str(status).decode()}: "
+                                       f"{L.qspec_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def workspace_bytes(op, a, b, c):
+    return int(lib().qspec_workspace_bytes(op, a, b, c))
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws, ws.numel() * ws.element_size()
+    w = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return w, nbytes
+
+
+def pack_w4(W, Wq=None, Ws=None):
+    """fp32 [N, K] -> (Wq uint8 [N, K/2], Ws float16 [N, K/128])."""
+    _need(W, "W", torch.float32)
+    N, K = W.shape
+    if Wq is None:
+        Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    if Ws is None:
+        Ws = torch.empty((N, max(K // GROUP, 1)), dtype=torch.float16, device=W.device)
+    _check(lib().qspec_pack_w4(_ptr(W), N, K, GROUP, _ptr(Wq), _ptr(Ws), _stream()),
+           "qspec_pack_w4")
+    return Wq, Ws
+
+
+def quant_act(X, Xq=None, Xs=None):
+    """bf16 [M, K] -> (Xq uint8 [M, K/2], Xs float32 [M])."""
+    _need(X, "X", torch.bfloat16)
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if Xs is None:
+        Xs = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _check(lib().qspec_quant_act(_ptr(X), M, K, _ptr(Xq), _ptr(Xs), _stream()), "qspec_quant_act")
+    return Xq, Xs
+
+
+def gemm_w4a4(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, partials=False, Y=None, P=None, ws=None):
+    """Draft-mode linear layer -> Y fp32 [M, N] (and int32 partials [M, N, K/128])."""
+    _need(Xq, "Xq", torch.uint8)
+    _need(Wq, "Wq", torch.uint8)
+    _need(Xs, "Xs", torch.float32)
+    _need(Ws, "Ws", torch.float16)
+    M, K = Xq.shape[0], 2 * Xq.shape[1]
+    N = Wq.shape[0]
+    _need(Xs, "Xs", torch.float32, (M,))
+    _need(Wq, "Wq", torch.uint8, (N, K // 2))
+    _need(Ws, "Ws", torch.float16, (N, K // GROUP))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    if partials and P is None:
+        P = torch.empty((M, N, K // GROUP), dtype=torch.int32, device=Xq.device)
+    w, wb = _workspace(workspace_bytes(OP_GEMM_W4A4, M, N, K), Xq.device, ws)
+    _check(lib().qspec_gemm_w4a4(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), M, N, K, GROUP, variant,
+                                 _ptr(Y), _ptr(P), _ptr(w), wb, _stream()), "qspec_gemm_w4a4")
+    return (Y, P) if partials else Y
+
+
+def gemm_w4a16(X, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None):
+    """Verify-mode linear layer -> Y fp32 [M, N]."""
+    _need(X, "X", torch.bfloat16)
+    M, K = X.shape
+    N = Wq.shape[0]
+    _need(Wq, "Wq", torch.uint8, (N, K // 2))
+    _need(Ws, "Ws", torch.float16, (N, K // GROUP))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    w, wb = _workspace(workspace_bytes(OP_GEMM_W4A16, M, N, K), X.device, ws)
+    _check(lib().qspec_gemm_w4a16(_ptr(X), _ptr(Wq), _ptr(Ws), M, N, K, GROUP, variant, _ptr(Y),
+                                  _ptr(w), wb, _stream()), "qspec_gemm_w4a16")
+    return Y
+
+
+def verify(mode, target_logits, draft_tok, draft_logits=None, u_accept=None, u_sample=None,
+           n_accept=None, out_tok=None, ws=None):
+    """-> (n_accept int32 [B], out_tok int32 [B, gamma+1] padded with -1)."""
+    _need(target_logits, "target_logits", torch.float32)
+    B, G1, V = target_logits.shape
+    gamma = G1 - 1
+    _need(draft_tok, "draft_tok", torch.int32, (B, gamma))
+    if mode == VERIFY_SAMPLE:
+        _need(draft_logits, "draft_logits", torch.float32, (B, gamma, V))
+        _need(u_accept, "u_accept", torch.float32, (B, gamma))
+        _need(u_sample, "u_sample", torch.float32, (B,))
+    dev = target_logits.device
+    if n_accept is None:
+        n_accept = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_tok is None:
+        out_tok = torch.empty((B, G1), dtype=torch.int32, device=dev)
+    w, wb = _workspace(workspace_bytes(OP_VERIFY, B, gamma, V), dev, ws)
+    _check(lib().qspec_verify(mode, B, gamma, V, _ptr(draft_tok), _ptr(draft_logits),
+                              _ptr(target_logits), _ptr(u_accept), _ptr(u_sample), _ptr(n_accept),
+                              _ptr(out_tok), _ptr(w), wb, _stream()), "qspec_verify")
+    return n_accept, out_tok

@@ -1,0 +1,88 @@
+// Internal helpers shared by the HIP sources of libqspec.so (not part of the
+// C ABI).  gfx950 only: 64-lane wavefronts, MFMA, 160 KiB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "qspec.h"
+
+namespace qspec {
+
+// thread-local error text behind qspec_last_error()
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+qspec_status fail(qspec_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+const char* last_error();
+qspec_status device_check();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+constexpr int kGroup = 128;
+
+// ---------------------------------------------------------------- vector types
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- device math
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight packed two's-complement nibbles (codes k0..k7, k0 in bits 0-3) ->
+// four words of bf16 pairs holding 136 + q: (k0,k4) (k1,k5) (k2,k6) (k3,k7).
+// 0x4300 | u is the bf16 of 128 + u, and u = q + 8 is the nibble with its
+// sign bit flipped, so every value is exact.
+__device__ __forceinline__ void w4_to_bf16_biased(uint32_t p, uint32_t o[4]) {
+  const uint32_t x = p ^ 0x88888888u;
+  o[0] = (x & 0x000F000Fu) | 0x43004300u;
+  o[1] = ((x >> 4) & 0x000F000Fu) | 0x43004300u;
+  o[2] = ((x >> 8) & 0x000F000Fu) | 0x43004300u;
+  o[3] = ((x >> 12) & 0x000F000Fu) | 0x43004300u;
+}
+constexpr float kW4Bias = 136.0f;
+
+// Eight natural-order bf16 values in four words -> the pair order of
+// w4_to_bf16_biased: (x0,x4) (x1,x5) (x2,x6) (x3,x7).
+__device__ __forceinline__ void bf16x8_interleave(const uint32_t x[4], uint32_t o[4]) {
+  o[0] = __builtin_amdgcn_perm(x[2], x[0], 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(x[2], x[0], 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(x[3], x[1], 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(x[3], x[1], 0x07060302u);
+}
+
+// Eight packed nibbles -> two words of int8 holding 16 * q:
+// lo = codes k0,k2,k4,k6 and hi = codes k1,k3,k5,k7 (byte i of each word).
+__device__ __forceinline__ uint32_t w4_lo_x16(uint32_t p) { return (p << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t w4_hi_x16(uint32_t p) { return p & 0xF0F0F0F0u; }
+
+// Fixed-order sum of eight natural-order bf16 values (four words).
+__device__ __forceinline__ float bf16x8_sum(const uint32_t x[4]) {
+  float a = bf16_lo(x[0]) + bf16_hi(x[0]);
+  float b = bf16_lo(x[1]) + bf16_hi(x[1]);
+  float c = bf16_lo(x[2]) + bf16_hi(x[2]);
+  float d = bf16_lo(x[3]) + bf16_hi(x[3]);
+  return (a + b) + (c + d);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+}  // namespace qspec

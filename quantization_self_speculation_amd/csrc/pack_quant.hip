@@ -1,0 +1,103 @@
+// Weight packer and per-token activation quantizer.
+//
+// Both follow one reading of the pages ("QSpec: Speculative Decoding with
+// Complementary Quantization Schemes", Abstract (arXiv); tech-dashboard QSpec
+// summary, paragraphs 2 and 4), which print no formula: symmetric INT4 with
+// scale = absmax / 7 (IEEE fp32 divide; rounded to fp16 for weights, kept in
+// fp32 for activations), code = clamp(rne(v / scale), -8, 7) with an IEEE
+// fp32 divide, two's-complement nibbles with element 2i in the low nibble.
+// The library is compiled with correctly rounded fp32 division and IEEE
+// denormals, so these kernels take every rounding decision exactly as stated.
+#include "launch.h"
+
+namespace qspec {
+namespace {
+
+__device__ __forceinline__ int quant_code(float v, float s) {
+  // s > 0 here; IEEE divide, round half to even, clamp
+  const float r = __builtin_rintf(v / s);
+  return (int)fminf(fmaxf(r, -8.0f), 7.0f);
+}
+
+// One wavefront per (row n, group g): lane l owns k = 2l, 2l+1 of the group.
+__global__ __launch_bounds__(256) void pack_w4_kernel(const float* __restrict__ W, int64_t N,
+                                                      int64_t K, uint8_t* __restrict__ Wq,
+                                                      uint16_t* __restrict__ Ws) {
+  const int64_t G = K / kGroup;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= N * G) return;  // uniform per wavefront
+  const int lane = threadIdx.x & 63;
+  const int64_t n = item / G, g = item - (item / G) * G;
+  const float2 w = *reinterpret_cast<const float2*>(W + n * K + g * kGroup + 2 * lane);
+  const float a = wave_max(fmaxf(fabsf(w.x), fabsf(w.y)));
+  const _Float16 sh = (_Float16)(a / 7.0f);
+  const float s = (float)sh;
+  int q0 = 0, q1 = 0;
+  if (s != 0.0f) {
+    q0 = quant_code(w.x, s);
+    q1 = quant_code(w.y, s);
+  }
+  Wq[n * (K / 2) + g * (kGroup / 2) + lane] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+  if (lane == 0) Ws[n * G + g] = __builtin_bit_cast(uint16_t, sh);
+}
+
+__device__ __forceinline__ float absmax8(uint4 v) {
+  // |bf16| via the sign bit; the max of exact values is exact
+  const float a = fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
+                        fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
+  const float b = fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
+                        fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ uint32_t pack8(uint4 v, float s) {
+  const float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) word |= (uint32_t)(quant_code(x[i], s) & 0xF) << (4 * i);
+  return word;
+}
+
+// One 256-thread block per token row.  Pass 1 finds the row absmax, pass 2
+// re-reads the row (an L2 hit) and writes 8 codes (one 32-bit word) per chunk.
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ X,
+                                                        int64_t K, uint8_t* __restrict__ Xq,
+                                                        float* __restrict__ Xs) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const uint4* row = reinterpret_cast<const uint4*>(X + m * K);
+  const int64_t nch = K / 8;
+  float a = 0.0f;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) a = fmaxf(a, absmax8(row[c]));
+  a = wave_max(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = a / 7.0f;
+  uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
+  if (s != 0.0f) {
+    for (int64_t c = threadIdx.x; c < nch; c += 256) out[c] = pack8(row[c], s);
+  } else {
+    for (int64_t c = threadIdx.x; c < nch; c += 256) out[c] = 0u;
+  }
+  if (threadIdx.x == 0) Xs[m] = s;
+}
+
+}  // namespace
+
+hipError_t launch_pack_w4(const float* W, int64_t N, int64_t K, uint8_t* Wq, uint16_t* Ws,
+                          hipStream_t s) {
+  const int64_t items = N * (K / kGroup);
+  hipLaunchKernelGGL(pack_w4_kernel, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, s, W, N, K,
+                     Wq, Ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)M), dim3(256), 0, s, X, K, Xq, Xs);
+  return hipGetLastError();
+}
+
+}  // namespace qspec

@@ -1,0 +1,108 @@
+"""Host-only checks of the C ABI: the library loads without a GPU, exports
+every entry point declared in include/qspec.h, and rejects bad arguments with
+the documented status codes before touching the device (the pointers passed
+here are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantization_self_speculation_amd as q
+from quantization_self_speculation_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EDEV, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced
+MIS = ctypes.c_void_p(0x10004)    # misaligned
+NUL = None
+S = None                           # null stream
+
+
+def declared():
+    txt = open(os.path.join(ROOT, "include", "qspec.h")).read()
+    return sorted(set(re.findall(r"\b(qspec_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = q.lib()
+    names = declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = q.lib()
+    for s in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EDEV, EHIP):
+        assert L.qspec_status_str(s)
+    assert L.qspec_status_str(-99) == b"unknown status"
+
+
+def test_pack_validation():
+    L = q.lib()
+    assert L.qspec_pack_w4(A, 4, 256, 64, A, A, S) == EUNSUP
+    assert L.qspec_pack_w4(A, 4, 200, 128, A, A, S) == ESHAPE
+    assert L.qspec_pack_w4(A, 0, 256, 128, A, A, S) == ESHAPE
+    assert L.qspec_pack_w4(NUL, 4, 256, 128, A, A, S) == ENULL
+    assert L.qspec_pack_w4(A, 4, 256, 128, MIS, A, S) == EALIGN
+    assert b"K" in L.qspec_last_error() or True
+
+
+def test_quant_validation():
+    L = q.lib()
+    assert L.qspec_quant_act(A, 0, 256, A, A, S) == ESHAPE
+    assert L.qspec_quant_act(A, 4, 100, A, A, S) == ESHAPE
+    assert L.qspec_quant_act(A, 4, 256, NUL, A, S) == ENULL
+    assert L.qspec_quant_act(A, 4, 256, A, MIS, S) == EALIGN
+
+
+def test_gemm_validation():
+    L = q.lib()
+    f = L.qspec_gemm_w4a4
+    assert f(A, A, A, A, 8, 64, 256, 64, 0, A, NUL, NUL, 0, S) == EUNSUP
+    assert f(A, A, A, A, 8, 64, 250, 128, 0, A, NUL, NUL, 0, S) == ESHAPE
+    assert f(A, A, A, A, 8, 64, 256, 128, 1, A, NUL, NUL, 0, S) == EUNSUP   # GEMV is W4A16-only
+    assert f(A, A, A, A, 8, 64, 256, 128, 9, A, NUL, NUL, 0, S) == EUNSUP
+    assert f(NUL, A, A, A, 8, 64, 256, 128, 0, A, NUL, NUL, 0, S) == ENULL
+    assert f(A, A, A, A, 8, 64, 256, 128, 0, MIS, NUL, NUL, 0, S) == EALIGN
+    assert f(A, A, A, A, 8, 64, 256, 128, 0, A, MIS, NUL, 0, S) == EALIGN
+    g = L.qspec_gemm_w4a16
+    assert g(A, A, A, 0, 64, 256, 128, 0, A, NUL, 0, S) == ESHAPE
+    assert g(A, A, A, 8, 64, 256, 128, 7, A, NUL, 0, S) == EUNSUP
+    assert g(A, A, NUL, 8, 64, 256, 128, 0, A, NUL, 0, S) == ENULL
+    # a split-K shape needs scratch: NULL / too small workspace is rejected
+    need = q.workspace_bytes(b.OP_GEMM_W4A16, 40, 4608, 3584)
+    assert need > 0
+    assert g(A, A, A, 40, 4608, 3584, 128, 2, A, NUL, 0, S) == EWS
+    assert g(A, A, A, 40, 4608, 3584, 128, 2, A, A, need - 1, S) == EWS
+
+
+def test_verify_validation():
+    L = q.lib()
+    f = L.qspec_verify
+    assert f(2, 1, 4, 100, A, NUL, A, NUL, NUL, A, A, A, 1 << 20, S) == EUNSUP
+    assert f(0, 1, 0, 100, A, NUL, A, NUL, NUL, A, A, A, 1 << 20, S) == ESHAPE
+    assert f(0, 1, 17, 100, A, NUL, A, NUL, NUL, A, A, A, 1 << 20, S) == ESHAPE
+    assert f(0, 1, 4, 0, A, NUL, A, NUL, NUL, A, A, A, 1 << 20, S) == ESHAPE
+    assert f(0, 1, 4, 100, A, A, A, NUL, NUL, A, A, A, 1 << 20, S) == EUNSUP  # greedy + logits
+    assert f(1, 1, 4, 100, A, NUL, A, A, A, A, A, A, 1 << 20, S) == ENULL     # sample w/o logits
+    assert f(0, 1, 4, 100, A, NUL, A, NUL, NUL, A, A, NUL, 0, S) == EWS
+    assert f(0, 4000, 8, 100, A, NUL, A, NUL, NUL, A, A, A, 1 << 30, S) == ESHAPE  # grid limit
+
+
+def test_workspace_bytes():
+    assert q.workspace_bytes(b.OP_VERIFY, 32, 4, 128256) > 0
+    assert q.workspace_bytes(b.OP_VERIFY, 32, 0, 128256) == 0
+    assert q.workspace_bytes(99, 1, 1, 1) == 0
+    # monotone in M (the answer covers every variant of the op)
+    assert q.workspace_bytes(b.OP_GEMM_W4A16, 64, 3584, 3584) >= \
+        q.workspace_bytes(b.OP_GEMM_W4A16, 8, 3584, 3584)
+
+
+def test_device_check_without_gpu_is_an_error_not_a_crash():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert q.lib().qspec_device_check() in (EHIP, EDEV)

@@ -1,0 +1,118 @@
+"""GPU parity of the verify step against the CPU oracle, through the C ABI.
+
+Greedy: n_accept and out_tok bit-exact.  Sampling: identical decisions on
+every sequence the oracle does not flag as a near tie (|u - p/q| or the
+inverse-CDF threshold within a relative 1e-5 of the decision boundary); the
+number of flagged sequences is reported and must stay small.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import quantization_self_speculation_amd as q
+from gpu_util import dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+# (B, gamma, V): the single-layer case, unaligned row starts, several
+# pass-1 chunks with ragged tails, and the Llama-3-8B vocabulary at batch 32
+CASES = [(1, 4, 1024), (3, 2, 1000), (5, 3, 50257), (2, 16, 8195), (32, 4, 128256),
+         (32, 8, 128256)]
+
+
+def _logits(seed, B, gamma, V):
+    rng = synth.make_rng(seed)
+    tgt, drf = synth.verify_logits(rng, B, gamma, V)
+    return rng, tgt, drf
+
+
+@pytest.mark.parametrize("B,gamma,V", CASES)
+def test_greedy_planted(B, gamma, V):
+    say(f"verify greedy planted B={B} gamma={gamma} V={V}")
+    rng, tgt, _ = _logits(30, B, gamma, V)
+    n_star = np.arange(B) % (gamma + 1)
+    d = synth.plant_greedy(rng, tgt, n_star)
+    n_ref, out_ref = oracle.verify_greedy(tgt, d)
+    assert np.array_equal(n_ref, n_star)
+    n, out = q.verify(q.VERIFY_GREEDY, dev(tgt), dev(d))
+    assert np.array_equal(host(n), n_ref)
+    assert np.array_equal(host(out), out_ref)
+
+
+@pytest.mark.parametrize("B,gamma,V", CASES)
+def test_greedy_random_drafts(B, gamma, V):
+    say(f"verify greedy gumbel B={B} gamma={gamma} V={V}")
+    rng, tgt, drf = _logits(31, B, gamma, V)
+    d = synth.gumbel_drafts(rng, drf)
+    # plant an exact tie at the argmax of one row: the lowest index must win
+    row = tgt[0, 0]
+    j = int(np.argmax(row))
+    row[max(j - 1, 0)] = row[j]
+    n_ref, out_ref = oracle.verify_greedy(tgt, d)
+    n, out = q.verify(q.VERIFY_GREEDY, dev(tgt), dev(d))
+    assert np.array_equal(host(n), n_ref)
+    assert np.array_equal(host(out), out_ref)
+
+
+@pytest.mark.parametrize("B,gamma,V", CASES)
+def test_sampling_matches_oracle(B, gamma, V):
+    say(f"verify sample B={B} gamma={gamma} V={V}")
+    rng, tgt, drf = _logits(32, B, gamma, V)
+    d = synth.gumbel_drafts(rng, drf)
+    ua = synth.uniforms(rng, (B, gamma))
+    us = synth.uniforms(rng, (B,))
+    n_ref, out_ref, flag = oracle.verify_sample(tgt, drf, d, ua, us)
+    n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
+    n, out = host(n), host(out)
+    ok = ~flag
+    assert flag.sum() <= max(1, B // 16), f"{flag.sum()} near ties"
+    assert np.array_equal(n[ok], n_ref[ok])
+    assert np.array_equal(out[ok], out_ref[ok])
+
+
+def test_sampling_forced_paths():
+    """u_accept = 0 accepts everything (bonus token from p_gamma); u_accept
+    just below 1 rejects wherever p/q < 1 (residual max(0, p - q))."""
+    B, gamma, V = 8, 4, 4096
+    rng, tgt, drf = _logits(33, B, gamma, V)
+    d = synth.gumbel_drafts(rng, drf)
+    us = synth.uniforms(rng, (B,))
+    for ua_val in (0.0, 0.9999999):
+        ua = np.full((B, gamma), ua_val, np.float32)
+        n_ref, out_ref, flag = oracle.verify_sample(tgt, drf, d, ua, us)
+        n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
+        ok = ~flag
+        assert np.array_equal(host(n)[ok], n_ref[ok])
+        assert np.array_equal(host(out)[ok], out_ref[ok])
+    assert np.all(n_ref <= gamma)
+
+
+def test_sampling_identical_logits_falls_back_to_p():
+    """draft == target logits: p/q = 1 accepts always -> bonus from p_gamma;
+    with a forced reject (u just above 1 is impossible, so plant q(d) > p(d))
+    the residual is empty only when p == q, where r = p."""
+    B, gamma, V = 4, 2, 2048
+    rng, tgt, _ = _logits(34, B, gamma, V)
+    drf = tgt[:, :gamma].copy()
+    d = synth.gumbel_drafts(rng, drf)
+    ua = synth.uniforms(rng, (B, gamma))
+    us = synth.uniforms(rng, (B,))
+    n_ref, out_ref, flag = oracle.verify_sample(tgt, drf, d, ua, us)
+    n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
+    ok = ~flag
+    assert np.array_equal(host(n)[ok], n_ref[ok])
+    assert np.array_equal(host(out)[ok], out_ref[ok])
+
+
+def test_verify_deterministic():
+    B, gamma, V = 32, 4, 128256
+    rng, tgt, drf = _logits(35, B, gamma, V)
+    d = synth.gumbel_drafts(rng, drf)
+    ua = synth.uniforms(rng, (B, gamma))
+    us = synth.uniforms(rng, (B,))
+    args = (dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
+    a = [host(t) for t in q.verify(q.VERIFY_SAMPLE, *args)]
+    b = [host(t) for t in q.verify(q.VERIFY_SAMPLE, *args)]
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
