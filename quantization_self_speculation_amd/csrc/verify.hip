@@ -22,7 +22,6 @@ namespace {
 
 constexpr int kQPC = 2048;        // float4 quads per pass-1 chunk (8192 logits)
 constexpr int kRCW = 8192;        // logits per residual chunk
-constexpr int kDecWords = 8;      // per-sequence decision record (32-bit words)
 
 __device__ __forceinline__ void argmax_merge(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) {
@@ -31,14 +30,26 @@ __device__ __forceinline__ void argmax_merge(float& bv, int& bi, float v, int i)
   }
 }
 
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-  // (m, s) represents sum exp(x - m) = s; merge two such pairs
-  if (m2 > m) {
-    s = s * __expf(m - m2) + s2;
-    m = m2;
-  } else if (m2 != -INFINITY) {
-    s = s + s2 * __expf(m2 - m);
-  }
+// exp(a - b) for fp32 a, b: the rounding error of the subtraction is carried
+// (two-sum) and applied to first order, so the result is within about 1 ulp
+// of exp of the exact difference.  a == -inf gives 0.
+__device__ __forceinline__ float exp_diff(float a, float b) {
+  if (a == -INFINITY) return 0.f;
+  const float s = a - b;
+  const float bb = s - a;
+  const float err = (a - (s - bb)) + (-b - bb);
+  const float e = expf(s);
+  return fmaf(e, err, e);
+}
+
+// merge two (max m, sum s = sum exp(x - m)) pairs; sums are fp64 and the
+// rescale uses the fp64 exp of an exact fp64 difference
+__device__ __forceinline__ void lse_merge(float& m, double& s, float m2, double s2) {
+  const float mm = fmaxf(m, m2);
+  const double a = (m == -INFINITY) ? 0.0 : s * exp((double)m - (double)mm);
+  const double b = (m2 == -INFINITY) ? 0.0 : s2 * exp((double)m2 - (double)mm);
+  s = a + b;
+  m = mm;
 }
 
 // Geometry of a row's pass-1 split: elements [0, a0) are a scalar head, then
@@ -51,13 +62,17 @@ __device__ __forceinline__ void row_geom(int64_t base, int64_t V, int64_t& a0, i
 }
 
 // pass 1.  grid = (nck, rows); rows = target rows then (sampling) draft rows.
+// Each thread keeps its (at most 8) quads in registers: greedy takes the
+// argmax (lowest index on ties); sampling takes the local max and the fp64
+// sum of exp(x - max) over the same values.
 template <bool GREEDY>
 __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tgt,
                                                     const float* __restrict__ drf, int64_t rows_t,
                                                     int64_t V, int nck, float* __restrict__ pm,
-                                                    float* __restrict__ ps, int* __restrict__ pi) {
+                                                    double* __restrict__ ps, int* __restrict__ pi) {
+  constexpr int QPT = kQPC / 256;
   __shared__ float sm[4];
-  __shared__ float ss[4];
+  __shared__ double ss[4];
   __shared__ int si[4];
   const int c = blockIdx.x;
   const int64_t row = blockIdx.y;
@@ -68,36 +83,54 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
   row_geom(rr * V, V, a0, nq);
   const int tid = threadIdx.x;
 
-  float bv = -INFINITY;  // greedy: best value / sampling: running max
-  int bi = 0x7FFFFFFF;
-  float s = 0.f;
-  auto visit = [&](float v, int idx) {
-    if (GREEDY) {
-      argmax_merge(bv, bi, v, idx);
-    } else {
-      if (v > bv) {
-        s = s * __expf(bv - v) + 1.0f;
-        bv = v;
-      } else {
-        s += __expf(v - bv);
-      }
-    }
-  };
-  if (c == 0 && tid < a0) visit(rp[tid], tid);
   const int64_t q0 = (int64_t)c * kQPC;
   const int64_t q1 = min(nq, q0 + kQPC);
   const float4* qp = reinterpret_cast<const float4*>(rp + a0);
-  for (int64_t q = q0 + tid; q < q1; q += 256) {
-    const float4 v = qp[q];
-    const int i = (int)(a0 + 4 * q);
-    visit(v.x, i);
-    visit(v.y, i + 1);
-    visit(v.z, i + 2);
-    visit(v.w, i + 3);
+  float4 v[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int64_t q = q0 + tid + 256 * k;
+    v[k] = q < q1 ? qp[q] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
   }
-  if (c == nck - 1) {
+  float hv = -INFINITY;  // head (chunk 0) or tail (last chunk) element
+  int hi = 0x7FFFFFFF;
+  if (c == 0 && tid < a0) {
+    hv = rp[tid];
+    hi = tid;
+  } else if (c == nck - 1) {
     const int64_t t0 = a0 + 4 * nq;
-    if (t0 + tid < V) visit(rp[t0 + tid], (int)(t0 + tid));
+    if (t0 + tid < V) {
+      hv = rp[t0 + tid];
+      hi = (int)(t0 + tid);
+    }
+  }
+
+  float bv = hv;
+  int bi = hi;
+  if (GREEDY) {
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int i = (int)(a0 + 4 * (q0 + tid + 256 * k));
+      argmax_merge(bv, bi, v[k].x, i);
+      argmax_merge(bv, bi, v[k].y, i + 1);
+      argmax_merge(bv, bi, v[k].z, i + 2);
+      argmax_merge(bv, bi, v[k].w, i + 3);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+      bv = fmaxf(bv, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
+  }
+  double s = 0.0;
+  if (!GREEDY && bv != -INFINITY) {
+    s = (double)exp_diff(hv, bv);
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      s += (double)exp_diff(v[k].x, bv);
+      s += (double)exp_diff(v[k].y, bv);
+      s += (double)exp_diff(v[k].z, bv);
+      s += (double)exp_diff(v[k].w, bv);
+    }
   }
 
   // wavefront then block reduction, fixed order
@@ -109,11 +142,11 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
       const int i2 = __shfl_xor(bi, o, 64);
       argmax_merge(bv, bi, v2, i2);
     } else {
-      const float s2 = __shfl_xor(s, o, 64);
+      const double s2 = __shfl_xor(s, o, 64);
       // symmetric merge so every lane holds identical bits
       const float m = fmaxf(bv, v2);
-      const float a = (bv == -INFINITY) ? 0.f : s * __expf(bv - m);
-      const float b = (v2 == -INFINITY) ? 0.f : s2 * __expf(v2 - m);
+      const double a = (bv == -INFINITY) ? 0.0 : s * exp((double)bv - (double)m);
+      const double b = (v2 == -INFINITY) ? 0.0 : s2 * exp((double)v2 - (double)m);
       s = (lane & o) ? b + a : a + b;
       bv = m;
     }
@@ -125,7 +158,8 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
   }
   __syncthreads();
   if (tid == 0) {
-    float m = sm[0], sacc = ss[0];
+    float m = sm[0];
+    double sacc = ss[0];
     int ib = si[0];
     for (int k = 1; k < 4; ++k) {
       if (GREEDY) argmax_merge(m, ib, sm[k], si[k]);
@@ -175,87 +209,100 @@ __global__ __launch_bounds__(64) void greedy_decide_kernel(const int32_t* __rest
   if (lane == 0) n_accept[b] = n;
 }
 
-// Merge the pass-1 (max, sum) pairs of one row across chunks (fixed order).
-__device__ __forceinline__ void row_lse(const float* pm, const float* ps, int64_t row, int nck,
-                                        int lane, float& M, float& S) {
+// Merge the pass-1 (max, sum) pairs of one row across chunks (fixed order:
+// lanes over chunks, then a butterfly that leaves identical bits in all lanes).
+__device__ __forceinline__ void row_lse(const float* pm, const double* ps, int64_t row, int nck,
+                                        int lane, float& M, double& S) {
   float m = -INFINITY;
   for (int c = lane; c < nck; c += 64) m = fmaxf(m, pm[row * nck + c]);
   m = wave_max(m);
-  float s = 0.f;
-  for (int c = lane; c < nck; c += 64) s += ps[row * nck + c] * __expf(pm[row * nck + c] - m);
-  S = wave_sum(s);
+  double s = 0.0;
+  for (int c = lane; c < nck; c += 64) {
+    const float mc = pm[row * nck + c];
+    if (mc != -INFINITY) s += ps[row * nck + c] * exp((double)mc - (double)m);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  S = s;
   M = m;
 }
 
-// sampling decision: one wavefront per sequence.  Writes the decision record
-// dec[b] = {n, kind (0 reject, 1 all accepted), Mt, St, Md, Sd, -, -}.
+struct Decision {
+  int n, kind;  // kind 0: rejected at n (residual max(0, p - q)); 1: all accepted (p_gamma)
+  float Mt, Md;
+  double St, Sd;
+};
+
+// sampling decision: one wavefront per sequence.  p(x) and q(x) are fp64
+// (exact fp64 exponent of the exact difference over the pass-1 sums).
 __global__ __launch_bounds__(64) void sample_decide_kernel(
     const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
     const float* __restrict__ ua, int gamma, int64_t V, int nck, const float* __restrict__ pm,
-    const float* __restrict__ ps, int64_t rows_t, float* __restrict__ dec) {
+    const double* __restrict__ ps, int64_t rows_t, Decision* __restrict__ dec) {
   const int64_t b = blockIdx.x;
   const int lane = threadIdx.x;
-  int n = gamma, kind = 1;
-  float Mt = 0.f, St = 1.f, Md = 0.f, Sd = 1.f;
+  Decision D{gamma, 1, 0.f, 0.f, 1.0, 1.0};
   for (int i = 0; i < gamma; ++i) {
     const int64_t rt = b * (gamma + 1) + i;
     const int64_t rd = rows_t + b * gamma + i;
-    float mt, st, md, sd;
+    float mt, md;
+    double st, sd;
     row_lse(pm, ps, rt, nck, lane, mt, st);
     row_lse(pm, ps, rd, nck, lane, md, sd);
     int x = dt[b * gamma + i];
     x = min(max(x, 0), (int)(V - 1));
-    const float p = expf(tgt[rt * V + x] - mt) / st;
-    const float q = expf(drf[(b * gamma + i) * V + x] - md) / sd;
-    const bool acc = q > 0.f ? (ua[b * gamma + i] <= p / q) : (p > 0.f);
+    const double p = exp((double)tgt[rt * V + x] - (double)mt) / st;
+    const double q = exp((double)drf[(b * gamma + i) * V + x] - (double)md) / sd;
+    const bool acc = q > 0.0 ? ((double)ua[b * gamma + i] <= p / q) : (p > 0.0);
     if (!acc) {
-      n = i;
-      kind = 0;
-      Mt = mt; St = st; Md = md; Sd = sd;
+      D = Decision{i, 0, mt, md, st, sd};
       break;
     }
   }
-  if (kind == 1) row_lse(pm, ps, b * (gamma + 1) + gamma, nck, lane, Mt, St);
-  if (lane == 0) {
-    float* d = dec + b * kDecWords;
-    d[0] = __int_as_float(n);
-    d[1] = __int_as_float(kind);
-    d[2] = Mt; d[3] = St; d[4] = Md; d[5] = Sd;
-  }
+  if (D.kind == 1) row_lse(pm, ps, b * (gamma + 1) + gamma, nck, lane, D.Mt, D.St);
+  if (lane == 0) dec[b] = D;
 }
 
-__device__ __forceinline__ float resid(const float* rt, const float* rd, int64_t j, int kind,
-                                       float Mt, float iSt, float Md, float iSd) {
-  const float p = __expf(rt[j] - Mt) * iSt;
+// r_j of the row a sequence samples from, in fp64
+__device__ __forceinline__ double resid(const float* rt, const float* rd, int64_t j, int kind,
+                                        float Mt, double iSt, float Md, double iSd) {
+  const double p = (double)exp_diff(rt[j], Mt) * iSt;
   if (kind == 1) return p;
-  const float q = __expf(rd[j] - Md) * iSd;
-  return fmaxf(p - q, 0.f);
+  const double q = (double)exp_diff(rd[j], Md) * iSd;
+  return p > q ? p - q : 0.0;
 }
 
 // residual chunk sums: grid = (rnck, B).  rs[b][c] = sum r, pp[b][c] = sum p.
 __global__ __launch_bounds__(256) void resid_sums_kernel(const float* __restrict__ tgt,
                                                          const float* __restrict__ drf, int gamma,
                                                          int64_t V, int rnck,
-                                                         const float* __restrict__ dec,
-                                                         float* __restrict__ rs,
-                                                         float* __restrict__ pp) {
-  __shared__ float red[2][4];
+                                                         const Decision* __restrict__ dec,
+                                                         double* __restrict__ rs,
+                                                         double* __restrict__ pp) {
+  __shared__ double red[2][4];
   const int c = blockIdx.x;
   const int64_t b = blockIdx.y;
-  const float* d = dec + b * kDecWords;
-  const int n = __float_as_int(d[0]), kind = __float_as_int(d[1]);
-  const float Mt = d[2], iSt = 1.0f / d[3], Md = d[4], iSd = 1.0f / d[5];
-  const float* rt = tgt + (b * (gamma + 1) + n) * V;
-  const float* rd = drf + (b * gamma + min(n, gamma - 1)) * V;
+  const Decision D = dec[b];
+  const double iSt = 1.0 / D.St, iSd = 1.0 / D.Sd;
+  const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
+  const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
   const int64_t j0 = (int64_t)c * kRCW, j1 = min(V, j0 + kRCW);
-  float sr = 0.f, sp = 0.f;
+  double sr = 0.0, sp = 0.0;
   for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
-    const float p = __expf(rt[j] - Mt) * iSt;
+    const double p = (double)exp_diff(rt[j], D.Mt) * iSt;
     sp += p;
-    sr += kind == 1 ? p : fmaxf(p - __expf(rd[j] - Md) * iSd, 0.f);
+    if (D.kind == 1) {
+      sr += p;
+    } else {
+      const double q = (double)exp_diff(rd[j], D.Md) * iSd;
+      sr += p > q ? p - q : 0.0;
+    }
   }
-  sr = wave_sum(sr);
-  sp = wave_sum(sp);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sr += __shfl_xor(sr, o, 64);
+    sp += __shfl_xor(sp, o, 64);
+  }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) {
     red[0][w] = sr;
@@ -268,38 +315,38 @@ __global__ __launch_bounds__(256) void resid_sums_kernel(const float* __restrict
   }
 }
 
-// inverse-CDF select: one 256-thread block per sequence.
+// inverse-CDF select: one 256-thread block per sequence, fp64 cumulative sums.
 __global__ __launch_bounds__(256) void sample_select_kernel(
     const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
-    const float* __restrict__ us, int gamma, int64_t V, int rnck, const float* __restrict__ dec,
-    const float* __restrict__ rs, const float* __restrict__ pp, int32_t* __restrict__ n_accept,
-    int32_t* __restrict__ out_tok) {
-  __shared__ float seg[256];
+    const float* __restrict__ us, int gamma, int64_t V, int rnck,
+    const Decision* __restrict__ dec, const double* __restrict__ rs,
+    const double* __restrict__ pp, int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tok) {
+  __shared__ double seg[256];
   __shared__ int found;
+  __shared__ int lastj;
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x;
-  const float* d = dec + b * kDecWords;
-  const int n = __float_as_int(d[0]);
-  int kind = __float_as_int(d[1]);
-  const float Mt = d[2], iSt = 1.0f / d[3], Md = d[4], iSd = 1.0f / d[5];
-  const float* rt = tgt + (b * (gamma + 1) + n) * V;
-  const float* rd = drf + (b * gamma + min(n, gamma - 1)) * V;
+  const Decision D = dec[b];
+  int kind = D.kind;
+  const double iSt = 1.0 / D.St, iSd = 1.0 / D.Sd;
+  const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
+  const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
 
   // chunk totals in fixed sequential order (every thread computes the same)
-  float R = 0.f;
-  for (int c = 0; c < rnck; ++c) R += rs[b * rnck + c];
-  const float* tot = rs + b * rnck;
-  if (R == 0.f && kind == 0) {  // p == q everywhere: sample from p
+  const double* tot = rs + b * rnck;
+  double R = 0.0;
+  for (int c = 0; c < rnck; ++c) R += tot[c];
+  if (R == 0.0 && kind == 0) {  // p == q everywhere: sample from p
     kind = 1;
     tot = pp + b * rnck;
-    R = 0.f;
+    R = 0.0;
     for (int c = 0; c < rnck; ++c) R += tot[c];
   }
-  const float thr = us[b] * R;
+  const double thr = (double)us[b] * R;
   int cs = -1;
-  float base = 0.f, run = 0.f;
+  double base = 0.0, run = 0.0;
   for (int c = 0; c < rnck; ++c) {
-    const float nx = run + tot[c];
+    const double nx = run + tot[c];
     if (nx > thr) {
       cs = c;
       base = run;
@@ -309,7 +356,7 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
   }
   int last_c = -1;  // fallback: last chunk with mass
   for (int c = rnck - 1; c >= 0; --c)
-    if (tot[c] > 0.f) {
+    if (tot[c] > 0.0) {
       last_c = c;
       break;
     }
@@ -320,15 +367,18 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
   const int64_t s0 = j0 + tid * per, s1 = min(j1, s0 + per);
 
   // per-thread segment sums, then exclusive scan over threads (sequential)
-  float ls = 0.f;
-  for (int64_t j = s0; j < s1; ++j) ls += resid(rt, rd, j, kind, Mt, iSt, Md, iSd);
+  double ls = 0.0;
+  for (int64_t j = s0; j < s1; ++j) ls += resid(rt, rd, j, kind, D.Mt, iSt, D.Md, iSd);
   seg[tid] = ls;
-  if (tid == 0) found = 0x7FFFFFFF;
+  if (tid == 0) {
+    found = 0x7FFFFFFF;
+    lastj = -1;
+  }
   __syncthreads();
   if (tid == 0) {
-    float acc = 0.f;
+    double acc = 0.0;
     for (int t = 0; t < 256; ++t) {
-      const float v = seg[t];
+      const double v = seg[t];
       seg[t] = acc;
       acc += v;
     }
@@ -336,38 +386,25 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
   __syncthreads();
   int my = 0x7FFFFFFF;
   int mylast = -1;
-  if (cs >= 0) {
-    float cum = base + seg[tid];
-    for (int64_t j = s0; j < s1; ++j) {
-      const float r = resid(rt, rd, j, kind, Mt, iSt, Md, iSd);
-      cum += r;
-      if (cum > thr) {
-        my = (int)j;
-        break;
-      }
-    }
+  double cum = base + seg[tid];
+  for (int64_t j = s0; j < s1; ++j) {
+    const double r = resid(rt, rd, j, kind, D.Mt, iSt, D.Md, iSd);
+    cum += r;
+    if (cs >= 0 && my == 0x7FFFFFFF && cum > thr) my = (int)j;
+    if (r > 0.0) mylast = (int)j;
   }
-  for (int64_t j = s0; j < s1; ++j)
-    if (resid(rt, rd, j, kind, Mt, iSt, Md, iSd) > 0.f) mylast = (int)j;
-  atomicMin(&found, my);  // LDS min of candidate indices: order-independent
+  atomicMin(&found, my);  // LDS min / max of candidate indices: order-independent
+  atomicMax(&lastj, mylast);
   __syncthreads();
   int pick = found;
-  if (pick == 0x7FFFFFFF) {
-    // no crossing (threshold at or beyond the total): last index with mass
-    __shared__ int lastj;
-    if (tid == 0) lastj = -1;
-    __syncthreads();
-    atomicMax(&lastj, mylast);
-    __syncthreads();
-    pick = lastj >= 0 ? lastj : 0;
-  }
+  if (pick == 0x7FFFFFFF) pick = lastj >= 0 ? lastj : 0;  // threshold at or past the total
   if (tid <= gamma) {
     int v = -1;
-    if (tid < n) v = dt[b * gamma + tid];
-    else if (tid == n) v = pick;
+    if (tid < D.n) v = dt[b * gamma + tid];
+    else if (tid == D.n) v = pick;
     out_tok[b * (gamma + 1) + tid] = v;
   }
-  if (tid == 0) n_accept[b] = n;
+  if (tid == 0) n_accept[b] = D.n;
 }
 
 struct VerifyLayout {
@@ -386,12 +423,12 @@ VerifyLayout layout(int64_t B, int gamma, int64_t V) {
     off += round_up(bytes, 256);
     return o;
   };
-  L.pm = take((size_t)rows * L.nck * 4);
-  L.ps = take((size_t)rows * L.nck * 4);
-  L.pi = take((size_t)B * (gamma + 1) * L.nck * 4);
-  L.dec = take((size_t)B * kDecWords * 4);
-  L.rs = take((size_t)B * L.rnck * 4);
-  L.pp = take((size_t)B * L.rnck * 4);
+  L.pm = take((size_t)rows * L.nck * sizeof(float));
+  L.ps = take((size_t)rows * L.nck * sizeof(double));
+  L.pi = take((size_t)B * (gamma + 1) * L.nck * sizeof(int));
+  L.dec = take((size_t)B * sizeof(Decision));
+  L.rs = take((size_t)B * L.rnck * sizeof(double));
+  L.pp = take((size_t)B * L.rnck * sizeof(double));
   L.total = off;
   return L;
 }
@@ -407,11 +444,11 @@ hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_
   const VerifyLayout L = layout(B, gamma, V);
   char* w = static_cast<char*>(ws);
   float* pm = reinterpret_cast<float*>(w + L.pm);
-  float* ps = reinterpret_cast<float*>(w + L.ps);
+  double* ps = reinterpret_cast<double*>(w + L.ps);
   int* pi = reinterpret_cast<int*>(w + L.pi);
-  float* dec = reinterpret_cast<float*>(w + L.dec);
-  float* rs = reinterpret_cast<float*>(w + L.rs);
-  float* pp = reinterpret_cast<float*>(w + L.pp);
+  Decision* dec = reinterpret_cast<Decision*>(w + L.dec);
+  double* rs = reinterpret_cast<double*>(w + L.rs);
+  double* pp = reinterpret_cast<double*>(w + L.pp);
   const int64_t rows_t = B * (gamma + 1);
   if (mode == QSPEC_VERIFY_GREEDY) {
     hipLaunchKernelGGL(pass1_kernel<true>, dim3(L.nck, (unsigned)rows_t), dim3(256), 0, s,
