@@ -1,0 +1,319 @@
+"""Benchmark of the dual-mode INT4 linear layer and verify step on one MI355X.
+
+Default workload (one "step" = one self-speculative round over the four
+projections of one Qwen2.5-7B-shaped decoder layer at batch 8, gamma 4):
+    4 draft passes:  per projection quant_act (M=8) + W4A4 GEMM (M=8)
+    1 verify pass:   per projection W4A16 GEMM (M = 8 * (4+1) = 40)
+    acceptance:      verify (speculative sampling) on B=8, gamma=4 logits over
+                     the Qwen2.5 vocabulary (152064)
+Projections (K -> N): QKV 3584->4608, O 3584->3584, gate|up 3584->37888,
+down 18944->3584, all reading one shared packed INT4 buffer (g=128, fp16
+scales) per pass.  Each pass reads its own copy of the packed weights (5
+copies, 601 MB) so no pass is served from the 256 MB Infinity Cache.  The
+step is captured once in a HIP graph and replayed; inputs are resident in HBM.
+
+value = whole-step algorithmic HBM bytes / step time (GB/s).
+roofline = the dominant kernel (W4A4 on gate|up at M=8, four launches per
+step): algorithmic bytes per launch / its mean duration (HIP events around
+graph replays of exactly those launches), against 8 TB/s.
+cpu_baseline = the CPU oracle on a bounded sample of the same step.
+
+Other workloads (--workload): prefill (M=2048 W4A4 vs W4A16 on the 7B
+shapes), llama (Llama-3-8B lm_head GEMV at M=1 and the verify step at B=32,
+V=128256).  Only the default prints the contract line's metric on the
+configuration it is quoted on; the others print their own lines.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+QWEN7B = [("qkv", 4608, 3584), ("o", 3584, 3584), ("gate_up", 37888, 3584),
+          ("down", 3584, 18944)]
+QWEN_VOCAB = 152064
+
+
+def wbytes(N, K):
+    """packed INT4 codes + fp16 group scales"""
+    return N * K // 2 + N * (K // 128) * 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+class Decode:
+    """Qwen2.5-7B decode layer round: B=8, gamma=4."""
+
+    name = "qwen2.5-7b-layer-selfspec-round"
+
+    def __init__(self, torch, q, B=8, gamma=4, V=QWEN_VOCAB, copies=5, seed=1):
+        import synth
+        self.torch, self.q = torch, q
+        self.B, self.gamma, self.V = B, gamma, V
+        dev = "cuda:0"
+        rng = synth.make_rng(1, 0)
+        self.proj = []
+        for name, N, K in QWEN7B:
+            W = synth.weights(rng, N, K)
+            Wd = torch.from_numpy(W).to(dev)
+            del W
+            Wq, Ws = q.pack_w4(Wd)
+            del Wd
+            cps = [(Wq, Ws)] + [(Wq.clone(), Ws.clone()) for _ in range(copies - 1)]
+            X = synth.activations(rng, B * (gamma + 1), K, n_outliers=synth.outlier_count(K))
+            Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(dev)
+            M4, M16 = B, B * (gamma + 1)
+            self.proj.append(dict(
+                name=name, N=N, K=K, copies=cps, X16=Xd, X4=Xd[:M4].contiguous(),
+                Xq=torch.empty((M4, K // 2), dtype=torch.uint8, device=dev),
+                Xs=torch.empty((M4,), dtype=torch.float32, device=dev),
+                Y4=torch.empty((M4, N), dtype=torch.float32, device=dev),
+                Y16=torch.empty((M16, N), dtype=torch.float32, device=dev),
+                ws4=torch.empty(max(1, q.workspace_bytes(1, M4, N, K)), dtype=torch.uint8, device=dev),
+                ws16=torch.empty(max(1, q.workspace_bytes(2, M16, N, K)), dtype=torch.uint8, device=dev),
+            ))
+        tgt, drf = synth.verify_logits(rng, B, gamma, V)
+        d = synth.gumbel_drafts(rng, drf)
+        self.vin = dict(tgt=torch.from_numpy(tgt).to(dev), drf=torch.from_numpy(drf).to(dev),
+                        d=torch.from_numpy(d).to(dev),
+                        ua=torch.from_numpy(synth.uniforms(rng, (B, gamma))).to(dev),
+                        us=torch.from_numpy(synth.uniforms(rng, (B,))).to(dev))
+        self.host_inputs = dict(tgt=tgt, drf=drf, d=d)
+        self.n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.out_tok = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+        self.wsv = torch.empty(q.workspace_bytes(3, B, gamma, V), dtype=torch.uint8, device=dev)
+        self.dominant = "w4a4_gate_up_M8"
+
+    # algorithmic HBM bytes --------------------------------------------------
+    def bytes_w4a4(self, p):
+        M, N, K = self.B, p["N"], p["K"]
+        return wbytes(N, K) + M * K // 2 + M * 4 + M * N * 4
+
+    def bytes_quant(self, p):
+        M, K = self.B, p["K"]
+        return M * K * 2 + M * K // 2 + M * 4
+
+    def bytes_w4a16(self, p):
+        M, N, K = self.B * (self.gamma + 1), p["N"], p["K"]
+        return wbytes(N, K) + M * K * 2 + M * N * 4
+
+    def bytes_verify(self):
+        B, g, V = self.B, self.gamma, self.V
+        # one pass over target and draft logits + the residual row pair
+        return (B * (g + 1) * V + B * g * V) * 4 + B * 2 * V * 4
+
+    def step_bytes(self):
+        tot = 0
+        for p in self.proj:
+            tot += self.gamma * (self.bytes_quant(p) + self.bytes_w4a4(p)) + self.bytes_w4a16(p)
+        return tot + self.bytes_verify()
+
+    def step_ops(self):
+        tot = 0
+        for p in self.proj:
+            tot += 2 * self.gamma * self.B * p["N"] * p["K"]
+            tot += 2 * self.B * (self.gamma + 1) * p["N"] * p["K"]
+        return tot
+
+    # launches ---------------------------------------------------------------
+    def draft_pass(self, d):
+        q = self.q
+        for p in self.proj:
+            Wq, Ws = p["copies"][d]
+            q.quant_act(p["X4"], p["Xq"], p["Xs"])
+            q.gemm_w4a4(p["Xq"], p["Xs"], Wq, Ws, Y=p["Y4"], ws=p["ws4"])
+
+    def verify_pass(self):
+        q = self.q
+        for p in self.proj:
+            Wq, Ws = p["copies"][self.gamma]
+            q.gemm_w4a16(p["X16"], Wq, Ws, Y=p["Y16"], ws=p["ws16"])
+        v = self.vin
+        q.verify(q.VERIFY_SAMPLE, v["tgt"], v["d"], v["drf"], v["ua"], v["us"],
+                 n_accept=self.n_acc, out_tok=self.out_tok, ws=self.wsv)
+
+    def step(self):
+        for d in range(self.gamma):
+            self.draft_pass(d)
+        self.verify_pass()
+
+    def dominant_launches(self):
+        """the dominant kernel's launches of one step, same buffers"""
+        q = self.q
+        p = [x for x in self.proj if x["name"] == "gate_up"][0]
+        for d in range(self.gamma):
+            Wq, Ws = p["copies"][d]
+            q.gemm_w4a4(p["Xq"], p["Xs"], Wq, Ws, Y=p["Y4"], ws=p["ws4"])
+        return self.gamma, self.bytes_w4a4(p)
+
+    # CPU oracle on a bounded sample ------------------------------------------
+    def cpu_baseline(self, frac_rows=1 / 64):
+        import oracle
+        import synth
+        rng = synth.make_rng(1, 7)
+        work = []
+        bytes_sample = 0
+        for name, N, K in QWEN7B:
+            n = max(16, int(N * frac_rows))
+            W = synth.weights(rng, n, K)
+            Wq, Ws = oracle.pack_w4(W)
+            X = synth.activations(rng, self.B * (self.gamma + 1), K,
+                                  n_outliers=synth.outlier_count(K))
+            work.append((Wq, Ws, X))
+            p = dict(N=n, K=K)
+            bytes_sample += self.gamma * (self.bytes_quant(p) + self.bytes_w4a4(p)) + self.bytes_w4a16(p)
+        bytes_sample += self.bytes_verify()
+        h = self.host_inputs
+        ua = np.asarray(self.vin["ua"].cpu())
+        us = np.asarray(self.vin["us"].cpu())
+        t0 = time.perf_counter()
+        for Wq, Ws, X in work:
+            for _ in range(self.gamma):
+                Xq, Xs = oracle.quant_act(X[:self.B])
+                oracle.gemm_w4a4(Xq, Xs, Wq, Ws)
+            oracle.gemm_w4a16(X, Wq, Ws)
+        oracle.verify_sample(h["tgt"], h["drf"], h["d"], ua, us)
+        dt = time.perf_counter() - t0
+        return dict(value=bytes_sample / dt / 1e9, unit="GB/s", cores=_blas_threads(),
+                    kind="oracle",
+                    sample=f"one round with 1/64 of every projection's output rows "
+                           f"(all K, all M) plus the full verify step; {dt:.1f} s")
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return 1
+
+
+# ---------------------------------------------------------------------------
+def timed_graph(torch, fn, reps):
+    """capture fn() in a HIP graph; time `reps` replays with HIP events on the
+    capture stream (torch's current stream during replay)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                       # warm allocations outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def run(args):
+    import torch
+    import quantization_self_speculation_amd as q
+    q.lib()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    log("setting up workload", args.workload)
+    wl = Decode(torch, q)
+    torch.cuda.synchronize()
+
+    g_step = timed_graph(torch, wl.step, 1)
+    box = {}
+
+    def dom():
+        box["n"], box["bytes"] = wl.dominant_launches()
+    g_dom = timed_graph(torch, dom, 1)
+
+    for _ in range(args.warmup):
+        g_step.replay()
+        g_dom.replay()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, bracketed by synchronize on both sides
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        g_step.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # the dominant kernel's launches alone (same buffers, same copies)
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(args.steps):
+        g_dom.replay()
+    d1.record()
+    torch.cuda.synchronize()
+    us_dom = d0.elapsed_time(d1) * 1e3 / (args.steps * box["n"])
+    achieved = box["bytes"] / (us_dom * 1e-6) / 1e9
+
+    step_bytes = wl.step_bytes()
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "traffic_w4a4_gate_up_M8.json")
+    if os.path.exists(tf):
+        try:
+            traffic = json.load(open(tf)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    line = {
+        "metric": "W4A4/W4A16 layer TOPS & HBM GB/s vs roofline; self-spec accepted tokens/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4-w/int8-mfma+bf16-mfma,fp32-acc",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) bf16 activations with 0.1% x20 "
+                "outlier channels, N(0,3) rho=0.9 logits)",
+        "config": {"workload": wl.name, "batch": wl.B, "gamma": wl.gamma,
+                   "draft_M": wl.B, "verify_M": wl.B * (wl.gamma + 1), "vocab": wl.V,
+                   "projections": {n: [k, nn] for n, nn, k in QWEN7B},
+                   "weight_copies": 5, "step_bytes": step_bytes,
+                   "step_tops": round(wl.step_ops() / (ms_step * 1e-3) / 1e12, 2)},
+        "roofline": {"bound": "hbm", "kernel": wl.dominant, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "us_per_launch": round(us_dom, 3), "bytes_per_launch": box["bytes"]},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        line["cpu_baseline"] = wl.cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

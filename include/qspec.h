@@ -104,8 +104,14 @@ size_t qspec_workspace_bytes(int op, int64_t a, int64_t b, int64_t c);
  *     a = max|W[n,k]|;  s = fp16(a / 7.0f)  (IEEE fp32 divide, then RNE);
  *     q[n,k] = clamp(rne(W[n,k] / float(s)), -8, 7), all 0 when s == 0.
  *   W   [N][K] fp32 (in).   N >= 1, K >= 128, K % 128 == 0.
- *   Wq  [N][K/2] u8 (out): byte i of a row holds q[2i] in bits 0-3 and
- *       q[2i+1] in bits 4-7, two's complement.
+ *   Wq  [Np][K/2] u8 (out), Np = ceil(N/16)*16: the codes in the tiled
+ *       storage order both GEMMs read.  Codes pack two per byte, code 2i of a
+ *       row in bits 0-3 and code 2i+1 in bits 4-7 (two's complement); the
+ *       row-major byte rows (padded with zero codes to Np rows) are stored as
+ *       1 KiB tiles, tile (b, g) for rows 16b..16b+15 and group g at byte
+ *       (b*(K/128) + g)*1024; in a tile, 16-byte slot l holds row 16b + l%16,
+ *       row bytes [64g + 16*(l/16), +16).  Each wavefront's weight load is
+ *       then one contiguous 1 KiB.
  *   Ws  [N][K/128] fp16 bits (out).
  *   group must be 128.  Non-finite W, or a/7 beyond the fp16 range, is
  *   unsupported (results unspecified).
@@ -134,7 +140,7 @@ qspec_status qspec_quant_act(const uint16_t* X, int64_t M, int64_t K,
  *     Y[m,n]   = Xs[m] * sum_g float(Ws[n,g]) * P[m,n,g]  (fp32 epilogue)
  * computed with int8 MFMA on the unpacked codes.
  *   Xq [M][K/2], Xs [M]   from qspec_quant_act.
- *   Wq [N][K/2], Ws [N][K/128] from qspec_pack_w4.
+ *   Wq [ceil(N/16)*16][K/2] (tiled), Ws [N][K/128] from qspec_pack_w4.
  *   Y  [M][N] fp32 (out).
  *   P  [M][N][K/128] int32 (out, optional: NULL skips it).
  *   variant: QSPEC_GEMM_AUTO, _SKINNY or _TILED (GEMV is W4A16-only).
@@ -187,7 +193,8 @@ qspec_status qspec_gemm_w4a16(const uint16_t* X, const uint8_t* Wq,
  *   u_accept      [B][gamma] fp32 in [0,1) (in; NULL iff greedy)
  *   u_sample      [B] fp32 in [0,1)        (in; NULL iff greedy)
  *   n_accept      [B] int32 (out);  out_tok [B][gamma+1] int32 (out, -1 pad)
- *   1 <= gamma <= QSPEC_MAX_GAMMA, B >= 1, V >= 1.  Out-of-range draft
+ *   1 <= gamma <= QSPEC_MAX_GAMMA, B >= 1, 1 <= V <= 2^23,
+ *   B * (2 gamma + 1) <= 65535.  Out-of-range draft
  *   tokens are not supported (they are clamped into [0, V) on the device).
  *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_VERIFY,B,gamma,V).
  * Decisions are taken in fp32; they can differ from exact arithmetic only

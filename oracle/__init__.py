@@ -33,6 +33,8 @@ from .quant import (  # noqa: F401
     pack_nibbles,
     unpack_nibbles,
     pack_w4,
+    tile_w4,
+    untile_w4,
     dequant_w4,
     quant_act,
     w4a4_partials,

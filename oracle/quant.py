@@ -20,6 +20,12 @@ group size, no scale precision and no bit layout.  Readings taken here:
   with an IEEE fp32 divide (not a multiply by the reciprocal).
 * packing: two's-complement nibbles, element 2i in the low nibble of byte i
   of its row, element 2i+1 in the high nibble.
+* storage order of the packed weights (a layout choice, no arithmetic): rows
+  are padded with zero codes to a multiple of 16 and the row-major bytes are
+  re-ordered in 1 KiB tiles, one per (16-row block b, group g); inside a tile,
+  16-byte slot l holds the 32 codes k in [128 g + 32 (l // 16), +32) of row
+  16 b + (l % 16).  ``tile_w4`` / ``untile_w4`` convert; the scales stay
+  row-major [N][K/128].
 * W4A4: per-group integer partials P[m,n,g] = sum_k qa*qw (exact), then
   Y = a_scale[m] * sum_g w_scale[n,g] * P[m,n,g].
 * W4A16: Y = sum_g w_scale[n,g] * sum_k x[m,k]*q[n,k] with x the bf16 value.
@@ -86,6 +92,42 @@ def unpack_nibbles(b):
     out[..., 0::2] = lo
     out[..., 1::2] = hi
     return out
+
+
+# --------------------------------------------------------------------------
+# storage order of the shared weight buffer (pure re-layout)
+# --------------------------------------------------------------------------
+TILE_ROWS = 16
+
+
+def tile_w4(Wq):
+    """row-major packed bytes [N, K/2] -> tiled bytes [ceil(N/16)*16, K/2].
+
+    Tile (b, g) = bytes [(b*G + g) * 1024, +1024) of the flat buffer; slot l
+    (16 bytes) = row 16b + l%16, row bytes [64 g + 16 (l//16), +16).
+    """
+    Wq = np.asarray(Wq, dtype=np.uint8)
+    N, KB = Wq.shape
+    if KB % 64:
+        raise ValueError("K must be a multiple of 128")
+    G = KB // 64
+    Np = -(-N // TILE_ROWS) * TILE_ROWS
+    R = np.zeros((Np, KB), dtype=np.uint8)
+    R[:N] = Wq
+    # [b, r, g, c, j] with row = 16b + r, byte = 64g + 16c + j
+    T = R.reshape(Np // 16, 16, G, 4, 16)
+    # tile order [b, g, c, r, j]: slot l = 16c + r
+    T = T.transpose(0, 2, 3, 1, 4)
+    return np.ascontiguousarray(T).reshape(Np, KB)
+
+
+def untile_w4(Wt, N):
+    """inverse of tile_w4 -> row-major [N, K/2] (padding rows dropped)."""
+    Wt = np.asarray(Wt, dtype=np.uint8)
+    Np, KB = Wt.shape
+    G = KB // 64
+    T = Wt.reshape(Np // 16, G, 4, 16, 16).transpose(0, 3, 1, 2, 4)
+    return np.ascontiguousarray(T).reshape(Np, KB)[:N]
 
 
 # --------------------------------------------------------------------------

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     lib,
     lib_path,
     pack_w4,
+    padded_rows,
     quant_act,
     gemm_w4a4,
     gemm_w4a16,

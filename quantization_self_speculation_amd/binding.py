@@ -108,12 +108,18 @@ def _workspace(nbytes, device, ws):
     return w, nbytes
 
 
-def pack_w4(W, Wq=None, Ws=None):
-    """fp32 [N, K] -> (Wq uint8 [N, K/2], Ws float16 [N, K/128])."""
+def padded_rows(N):
+    """rows of the tiled weight buffer: N rounded up to a multiple of 16"""
+    return -(-N // 16) * 16
+
+
+def pack_w4(W, Wq=None, Ws=None, N=None):
+    """fp32 [N, K] -> (Wq uint8 [ceil(N/16)*16, K/2] in the tiled storage
+    order, Ws float16 [N, K/128])."""
     _need(W, "W", torch.float32)
     N, K = W.shape
     if Wq is None:
-        Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+        Wq = torch.empty((padded_rows(N), K // 2), dtype=torch.uint8, device=W.device)
     if Ws is None:
         Ws = torch.empty((N, max(K // GROUP, 1)), dtype=torch.float16, device=W.device)
     _check(lib().qspec_pack_w4(_ptr(W), N, K, GROUP, _ptr(Wq), _ptr(Ws), _stream()),
@@ -134,15 +140,16 @@ def quant_act(X, Xq=None, Xs=None):
 
 
 def gemm_w4a4(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, partials=False, Y=None, P=None, ws=None):
-    """Draft-mode linear layer -> Y fp32 [M, N] (and int32 partials [M, N, K/128])."""
+    """Draft-mode linear layer -> Y fp32 [M, N] (and int32 partials [M, N, K/128]).
+    N is taken from the scales Ws [N, K/128]; Wq is the tiled buffer."""
     _need(Xq, "Xq", torch.uint8)
     _need(Wq, "Wq", torch.uint8)
     _need(Xs, "Xs", torch.float32)
     _need(Ws, "Ws", torch.float16)
     M, K = Xq.shape[0], 2 * Xq.shape[1]
-    N = Wq.shape[0]
+    N = Ws.shape[0]
     _need(Xs, "Xs", torch.float32, (M,))
-    _need(Wq, "Wq", torch.uint8, (N, K // 2))
+    _need(Wq, "Wq", torch.uint8, (padded_rows(N), K // 2))
     _need(Ws, "Ws", torch.float16, (N, K // GROUP))
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
@@ -158,8 +165,8 @@ def gemm_w4a16(X, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None):
     """Verify-mode linear layer -> Y fp32 [M, N]."""
     _need(X, "X", torch.bfloat16)
     M, K = X.shape
-    N = Wq.shape[0]
-    _need(Wq, "Wq", torch.uint8, (N, K // 2))
+    N = Ws.shape[0]
+    _need(Wq, "Wq", torch.uint8, (padded_rows(N), K // 2))
     _need(Ws, "Ws", torch.float16, (N, K // GROUP))
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=X.device)

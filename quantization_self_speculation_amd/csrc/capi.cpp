@@ -217,7 +217,8 @@ qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V, const int32
              "unknown verify mode %d", mode);
   QS_REQUIRE(gamma >= 1 && gamma <= QSPEC_MAX_GAMMA, QSPEC_ERR_SHAPE,
              "gamma must be in [1, %d] (got %d)", QSPEC_MAX_GAMMA, gamma);
-  QS_REQUIRE(B >= 1 && V >= 1 && V <= kMaxDim, QSPEC_ERR_SHAPE, "need B >= 1, V >= 1");
+  QS_REQUIRE(B >= 1 && V >= 1 && V <= ((int64_t)1 << 23), QSPEC_ERR_SHAPE,
+             "need B >= 1 and 1 <= V <= 2^23");
   QS_REQUIRE(B * (2 * gamma + 1) <= 65535, QSPEC_ERR_SHAPE,
              "B * (2 gamma + 1) must be at most 65535");
   QS_PTR(draft_tok);

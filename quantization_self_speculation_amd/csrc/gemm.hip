@@ -28,7 +28,40 @@
 //    epilogue per group; K is split into slices only as a function of (N, K),
 //    and slices are reduced in fixed order -- no atomics -- so an output row
 //    is bitwise the same for every M.
+#include <atomic>
+
 #include "launch.h"
+
+// Tile parameters (activation chunk CH, weight ring depth PD) per m-block
+// count; measured on MI355X.  Overridable at build time for tuning sweeps.
+#ifndef QSPEC_SK_A1
+#define QSPEC_SK_A1 4, 4   // W4A4,  M <= 16: CH, PD
+#endif
+#ifndef QSPEC_SK_A2
+#define QSPEC_SK_A2 4, 4
+#endif
+#ifndef QSPEC_SK_A3
+#define QSPEC_SK_A3 2, 4
+#endif
+#ifndef QSPEC_SK_A4
+#define QSPEC_SK_A4 2, 4
+#endif
+#ifndef QSPEC_SK_B1
+#define QSPEC_SK_B1 4, 4   // W4A16, M <= 16: CH, PD
+#endif
+#ifndef QSPEC_SK_B2
+#define QSPEC_SK_B2 2, 4
+#endif
+#ifndef QSPEC_SK_B3
+#define QSPEC_SK_B3 2, 4
+#endif
+#ifndef QSPEC_SK_B4
+#define QSPEC_SK_B4 1, 4
+#endif
+#ifndef QSPEC_SK_TARGET_WG
+#define QSPEC_SK_TARGET_WG 512
+#endif
+
 
 namespace qspec {
 namespace {
@@ -62,268 +95,134 @@ __device__ __forceinline__ float group_sum16(float v) {
 }
 
 // ============================================================================
-// W4A16, MFMA "skinny" family: weights streamed straight from HBM into
-// registers (each byte used by exactly one wavefront), activations of up to
-// 64 rows shared by the 4 wavefronts of a workgroup through LDS.
-//   grid = (ceil(N / (64 NB)), S k-slices, ceil(M / (16 MB)) m-chunks)
+// MFMA "skinny" family (both modes): the decode / verify shapes.
+//   * a workgroup = 4 wavefronts x 16 weight rows = one 64-row n-tile, one
+//     k-slice of the groups, one m-chunk of up to 64 activation rows;
+//   * weights go straight from HBM into a register ring PD groups deep (each
+//     byte is used by exactly one wavefront; PD-1 groups of compute cover the
+//     latency of every load);
+//   * activations of the m-chunk are staged through LDS, CH groups at a time,
+//     double-buffered, in the MFMA k-slot order, once per workgroup;
+//   * split-K (S slices, a function of N and K only) is reduced inside the
+//     kernel by the last slice to arrive, in fixed slice order; arrival is
+//     counted with an epoch-tagged 64-bit counter per tile in the caller's
+//     workspace that the last slice resets to 0;
+//   * block -> (tile, slice) mapping keeps the S slices of a tile on one XCD
+//     (blocks are dealt round-robin to the 8 XCDs), so partials stay in that
+//     XCD's L2.
 // ============================================================================
-template <int NB, int MB, int CH>
-__global__ __launch_bounds__(256) void w4a16_skinny_kernel(
-    const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wq,
-    const uint16_t* __restrict__ Ws, int M, int N, int K, int gps, float* __restrict__ out,
-    int64_t slice_stride) {
-  constexpr int ROWS = 16 * MB;        // activation rows per m-chunk
-  constexpr int XST = CH * 128 + 8;    // LDS row stride in bf16 (16-byte pad)
-  constexpr int WROWS = 64 * NB;       // weight rows per workgroup
-  constexpr int XCH = ROWS * CH * 16;  // 16-byte activation chunks per stage
-  constexpr int XPT = XCH / 256;       // ... per thread
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][ROWS * XST];
-  __shared__ float xsum[2][ROWS * CH];
-  __shared__ uint16_t wsl[2][CH * WROWS];
+enum { kW4A16 = 0, kW4A4 = 1 };
 
-  const int G = K / kGroup;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int n_wg = blockIdx.x * WROWS;
-  const int n_w = n_wg + wave * 16 * NB;
-  const int g_begin = blockIdx.y * gps;
-  const int g_end = min(G, g_begin + gps);
-  const int m0 = blockIdx.z * ROWS;
-  const int nchunks = (g_end - g_begin + CH - 1) / CH;
+struct SkinnyArgs {
+  const void* X;            // W4A16: bf16 [M][K]; W4A4: packed codes [M][K/2]
+  const float* Xs;          // W4A4: [M]
+  const uint8_t* Wq;
+  const uint16_t* Ws;
+  float* Y;
+  float* part;              // [S][M][N] when S > 1
+  unsigned long long* cnt;  // [T] when S > 1
+  int32_t* P;               // W4A4 int32 group partials (optional)
+  int M, N, K, S, gps, ntiles, T;
+  unsigned epoch;
+};
 
-  const uint8_t* wrow[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = min(n_w + nb * 16 + l16, N - 1);
-    wrow[nb] = Wq + (int64_t)n * (K / 2) + lg * 16;
-  }
-
-  uint4 wcur[CH][NB], wnext[CH][NB];
-  uint4 xr[XPT];
-  uint16_t sr[(CH * WROWS + 255) / 256];
-
-  auto load_w = [&](int c, uint4 (&w)[CH][NB]) {
-    const int gc = g_begin + c * CH;
-#pragma unroll
-    for (int gl = 0; gl < CH; ++gl)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        w[gl][nb] = (gc + gl < g_end)
-                        ? ld_stream(wrow[nb] + (int64_t)(gc + gl) * 64)
-                        : make_uint4(0, 0, 0, 0);
-  };
-  auto load_x = [&](int c) {
-    const int gc = g_begin + c * CH;
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int r = idx / (CH * 16), cc = idx % (CH * 16);
-      const bool ok = (m0 + r < M) && (gc + (cc >> 4) < g_end);
-      xr[i] = ok ? *reinterpret_cast<const uint4*>(X + (int64_t)(m0 + r) * K +
-                                                   (int64_t)gc * kGroup + cc * 8)
-                 : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < (CH * WROWS + 255) / 256; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      if (idx < CH * WROWS) {
-        const int gl = idx / WROWS, rr = idx % WROWS;
-        const int n = min(n_wg + rr, N - 1);
-        sr[i] = (gc + gl < g_end) ? Ws[(int64_t)n * G + gc + gl] : (uint16_t)0;
-      }
-    }
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int r = idx / (CH * 16), cc = idx % (CH * 16);
-      const uint32_t v[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-      uint32_t p[4];
-      bf16x8_interleave(v, p);
-      *reinterpret_cast<uint4*>(&xs[buf][r * XST + cc * 8]) = make_uint4(p[0], p[1], p[2], p[3]);
-      const float s = group_sum16(bf16x8_sum(v));
-      if ((cc & 15) == 0) xsum[buf][r * CH + (cc >> 4)] = s;
-    }
-#pragma unroll
-    for (int i = 0; i < (CH * WROWS + 255) / 256; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      if (idx < CH * WROWS) wsl[buf][idx] = sr[i];
-    }
-  };
-
-  v4f tot[NB][MB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) tot[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  if (nchunks > 0) {
-    load_w(0, wcur);
-    load_x(0);
-    store_x(0);
-  }
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_w(c + 1, wnext);
-      load_x(c + 1);
-    }
-    const int gc = g_begin + c * CH;
-#pragma unroll
-    for (int gl = 0; gl < CH; ++gl) {
-      if (gc + gl < g_end) {
-        v4f acc[NB][MB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v8bf b[MB];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            b[mb] = *reinterpret_cast<const v8bf*>(
-                &xs[buf][(mb * 16 + l16) * XST + gl * 128 + lg * 32 + j * 8]);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const uint4 w = wcur[gl][nb];
-            const uint32_t wd = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
-            uint32_t a4[4];
-            w4_to_bf16_biased(wd, a4);
-            const v8bf a = as_v8bf(a4[0], a4[1], a4[2], a4[3]);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[mb], acc[nb][mb], 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const float xsm = xsum[buf][(mb * 16 + l16) * CH + gl];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const uint16_t* wp = &wsl[buf][gl * WROWS + wave * 16 * NB + nb * 16 + lg * 4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float t = fmaf(-kW4Bias, xsm, acc[nb][mb][r]);
-              tot[nb][mb][r] = fmaf(half_bits_to_float(wp[r]), t, tot[nb][mb][r]);
-            }
-          }
-        }
-      }
-    }
-    if (more) store_x(buf ^ 1);
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int gl = 0; gl < CH; ++gl)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) wcur[gl][nb] = wnext[gl][nb];
-    }
-  }
-
-  float* o = out + (int64_t)blockIdx.y * slice_stride;
-  const bool vec = (N & 3) == 0;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + mb * 16 + l16;
-      const int n = n_w + nb * 16 + lg * 4;
-      if (m < M && n < N) {
-        float* dst = o + (int64_t)m * N + n;
-        if (vec) {
-          *reinterpret_cast<float4*>(dst) =
-              make_float4(tot[nb][mb][0], tot[nb][mb][1], tot[nb][mb][2], tot[nb][mb][3]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = tot[nb][mb][r];
-        }
-      }
-    }
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15) with a fixed
+// rotate-and-add tree; the value in lane 16r is what callers use.  The tree
+// depends only on a value's position in the row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));  // row_ror:4
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));   // quad xor 2
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // quad xor 1
+  return v;
 }
 
-// ============================================================================
-// W4A4, MFMA "skinny" family: same structure; codes widened to int8 (16 q),
-// v_mfma_i32_16x16x64_i8, exact int32 group partial, fp32 scale epilogue.
-// ============================================================================
-template <int NB, int MB, int CH>
-__global__ __launch_bounds__(256) void w4a4_skinny_kernel(
-    const uint8_t* __restrict__ Xq, const float* __restrict__ Xs, const uint8_t* __restrict__ Wq,
-    const uint16_t* __restrict__ Ws, int M, int N, int K, int gps, float* __restrict__ out,
-    int64_t slice_stride, int32_t* __restrict__ P, int apply_xs) {
+// Straight-line main loop: every global load is issued unconditionally (from
+// a clamped, valid address) so the compiler keeps exact load counters and the
+// weight ring stays in flight across waits; only the arithmetic of groups past
+// the end of the slice is skipped (a branch uniform over the workgroup).
+template <int MODE, int MB, int CH, int PD, bool WITHP>
+__global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
+  static_assert(PD % CH == 0, "prefetch depth must be a multiple of the chunk");
   constexpr int ROWS = 16 * MB;
-  constexpr int XST = CH * 128 + 16;   // LDS row stride in bytes (int8 codes)
-  constexpr int WROWS = 64 * NB;
-  constexpr int XCH = ROWS * CH * 4;   // 16-byte packed chunks (32 codes) per stage
+  constexpr int XSTB = (MODE == kW4A16 ? CH * 256 : CH * 128) + 16;  // LDS row bytes
+  constexpr int XCH = MODE == kW4A16 ? ROWS * CH * 16 : ROWS * CH * 4;  // 16-B chunks
   constexpr int XPT = (XCH + 255) / 256;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][ROWS * XST];
-  __shared__ uint16_t wsl[2][CH * WROWS];
+  constexpr int SPT = (CH * 64 + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][ROWS * XSTB];
+  __shared__ float xsum[2][MODE == kW4A16 ? ROWS * CH : 1];
+  __shared__ uint16_t wsl[2][CH * 64];
+  __shared__ int s_last;
 
-  const int G = K / kGroup;
+  const int b = blockIdx.x;
+  const int t = 8 * ((b >> 3) / a.S) + (b & 7);
+  const int slice = (b >> 3) % a.S;
+  if (t >= a.T) return;  // padding block (uniform)
+  const int ntile = t % a.ntiles, mchunk = t / a.ntiles;
+  const int G = a.K / kGroup;
+  const int g_begin = slice * a.gps, g_end = min(G, g_begin + a.gps);
+  const int ng = g_end - g_begin;
+  const int nblk = (ng + PD - 1) / PD;  // PD-group blocks, the last may be partial
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int n_wg = blockIdx.x * WROWS;
-  const int n_w = n_wg + wave * 16 * NB;
-  const int g_begin = blockIdx.y * gps;
-  const int g_end = min(G, g_begin + gps);
-  const int m0 = blockIdx.z * ROWS;
-  const int nchunks = (g_end - g_begin + CH - 1) / CH;
+  const int n_wg = ntile * 64, n_w = n_wg + wave * 16;
+  const int m0 = mchunk * ROWS;
+  const int M = a.M, N = a.N, K = a.K;
 
-  const uint8_t* wrow[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = min(n_w + nb * 16 + l16, N - 1);
-    wrow[nb] = Wq + (int64_t)n * (K / 2) + lg * 16;
-  }
+  // tiled weights: the wave's 16 rows x one group = one contiguous 1 KiB tile,
+  // lane l's 16 bytes = row l%16, codes 32*(l/16) .. +32 of the group
+  const int nrb = (N + 15) / 16;
+  const uint8_t* wrow =
+      a.Wq + ((int64_t)min(n_w / 16, nrb - 1) * G + g_begin) * 1024 + lane * 16;
+  auto wload = [&](int gi) { return ld_stream(wrow + (int64_t)min(gi, ng - 1) * 1024); };
 
-  uint4 wcur[CH][NB], wnext[CH][NB];
   uint4 xr[XPT];
-  uint16_t sr[(CH * WROWS + 255) / 256];
-
-  auto load_w = [&](int c, uint4 (&w)[CH][NB]) {
-    const int gc = g_begin + c * CH;
-#pragma unroll
-    for (int gl = 0; gl < CH; ++gl)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        w[gl][nb] = (gc + gl < g_end)
-                        ? ld_stream(wrow[nb] + (int64_t)(gc + gl) * 64)
-                        : make_uint4(0, 0, 0, 0);
-  };
-  auto load_x = [&](int c) {
+  uint16_t sr[SPT];
+  // every load below is unconditional: rows past M and groups past the
+  // slice read clamped (valid) addresses; their results are never used
+  // (rows past M are not stored, groups past the slice are skipped)
+  auto x_load = [&](int c) {
     const int gc = g_begin + c * CH;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int r = idx / (CH * 4), cc = idx % (CH * 4);
-      const bool ok = idx < XCH && (m0 + r < M) && (gc + (cc >> 2) < g_end);
-      xr[i] = ok ? *reinterpret_cast<const uint4*>(Xq + (int64_t)(m0 + r) * (K / 2) +
-                                                   (int64_t)gc * 64 + cc * 16)
-                 : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < (CH * WROWS + 255) / 256; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      if (idx < CH * WROWS) {
-        const int gl = idx / WROWS, rr = idx % WROWS;
-        const int n = min(n_wg + rr, N - 1);
-        sr[i] = (gc + gl < g_end) ? Ws[(int64_t)n * G + gc + gl] : (uint16_t)0;
+      const int idx = min((int)threadIdx.x + 256 * i, XCH - 1);
+      if (MODE == kW4A16) {
+        const int r = idx / (CH * 16), cc = idx % (CH * 16);
+        xr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.X) +
+                                                (int64_t)min(m0 + r, M - 1) * K +
+                                                (int64_t)min(gc + (cc >> 4), G - 1) * kGroup +
+                                                (cc & 15) * 8);
+      } else {
+        const int r = idx / (CH * 4), cc = idx % (CH * 4);
+        xr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.X) +
+                                                (int64_t)min(m0 + r, M - 1) * (K / 2) +
+                                                (int64_t)min(gc + (cc >> 2), G - 1) * 64 +
+                                                (cc & 3) * 16);
       }
     }
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int idx = min((int)threadIdx.x + 256 * i, CH * 64 - 1);
+      const int gl = idx / 64, rr = idx % 64;
+      sr[i] = a.Ws[(int64_t)min(n_wg + rr, N - 1) * G + min(gc + gl, G - 1)];
+    }
   };
-  auto store_x = [&](int buf) {
+  auto x_store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = threadIdx.x + 256 * i;
-      if (idx < XCH) {
+      if (MODE == kW4A16) {
+        const int r = idx / (CH * 16), cc = idx % (CH * 16);
+        const uint32_t v[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+        uint32_t p[4];
+        bf16x8_interleave(v, p);
+        *reinterpret_cast<uint4*>(&xs[buf][r * XSTB + cc * 16]) = make_uint4(p[0], p[1], p[2], p[3]);
+        const float s = row16_sum(bf16x8_sum(v));  // 16 chunks of a group = one DPP row
+        if ((cc & 15) == 0) xsum[buf][r * CH + (cc >> 4)] = s;
+      } else if (idx < XCH) {
         const int r = idx / (CH * 4), cc = idx % (CH * 4);
         const uint4 p = xr[i];
-        uint8_t* dst = &xs[buf][r * XST + (cc >> 2) * 128 + (cc & 3) * 32];
+        uint8_t* dst = &xs[buf][r * XSTB + (cc >> 2) * 128 + (cc & 3) * 32];
         *reinterpret_cast<uint4*>(dst) =
             make_uint4(w4_lo_x16(p.x), w4_hi_x16(p.x), w4_lo_x16(p.y), w4_hi_x16(p.y));
         *reinterpret_cast<uint4*>(dst + 16) =
@@ -331,107 +230,115 @@ __global__ __launch_bounds__(256) void w4a4_skinny_kernel(
       }
     }
 #pragma unroll
-    for (int i = 0; i < (CH * WROWS + 255) / 256; ++i) {
+    for (int i = 0; i < SPT; ++i) {
       const int idx = threadIdx.x + 256 * i;
-      if (idx < CH * WROWS) wsl[buf][idx] = sr[i];
+      if (idx < CH * 64) wsl[buf][idx] = sr[i];
     }
   };
 
-  v4f tot[NB][MB];
+  v4f tot[MB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) tot[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb) tot[mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 wr[PD];
 
-  if (nchunks > 0) {
-    load_w(0, wcur);
-    load_x(0);
-    store_x(0);
-  }
+  x_load(0);
+  x_store(0);
+#pragma unroll
+  for (int s = 0; s < PD; ++s) wr[s] = wload(s);
   __syncthreads();
+  x_load(1);
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_w(c + 1, wnext);
-      load_x(c + 1);
-    }
-    const int gc = g_begin + c * CH;
+  for (int bi = 0; bi < nblk; ++bi) {
 #pragma unroll
-    for (int gl = 0; gl < CH; ++gl) {
-      if (gc + gl < g_end) {
-        v4i acc[NB][MB];
+    for (int s = 0; s < PD; ++s) {
+      const int gi = bi * PD + s;
+      const int gl = s % CH;  // compile-time after unrolling
+      const int c = gi / CH;
+      const int buf = c & 1;
+      const uint4 w = wr[s];
+      const uint16_t* wp = &wsl[buf][gl * 64 + wave * 16 + lg * 4];
+      if (gi >= ng) {
+        // past the end of the slice: nothing to add
+      } else if (MODE == kW4A16) {
+        v4f acc[MB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          v4i b[MB];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            b[mb] = *reinterpret_cast<const v4i*>(
-                &xs[buf][(mb * 16 + l16) * XST + gl * 128 + lg * 32 + j * 16]);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const uint4 w = wcur[gl][nb];
-            const uint32_t p0 = j == 0 ? w.x : w.z, p1 = j == 0 ? w.y : w.w;
-            const v4i a = as_v4i(w4_lo_x16(p0), w4_hi_x16(p0), w4_lo_x16(p1), w4_hi_x16(p1));
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              acc[nb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[mb], acc[nb][mb], 0, 0, 0);
-          }
-        }
-        const int g = gc + gl;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const uint16_t* wp = &wsl[buf][gl * WROWS + wave * 16 * NB + nb * 16 + lg * 4];
-          float sc[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[r] = half_bits_to_float(wp[r]) * 0.00390625f;  // / 256
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t wd = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
+          uint32_t a4[4];
+          w4_to_bf16_biased(wd, a4);
+          const v8bf av = as_v8bf(a4[0], a4[1], a4[2], a4[3]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
+            const v8bf bv = *reinterpret_cast<const v8bf*>(
+                &xs[buf][(mb * 16 + l16) * XSTB + gl * 256 + lg * 64 + j * 16]);
+            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mb], 0, 0, 0);
+          }
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              tot[nb][mb][r] = fmaf(sc[r], (float)acc[nb][mb][r], tot[nb][mb][r]);
-            if (P != nullptr) {
-              const int m = m0 + mb * 16 + l16;
-              const int n = n_w + nb * 16 + lg * 4;
-              if (m < M) {
+        for (int mb = 0; mb < MB; ++mb) {
+          const float xsm = xsum[buf][(mb * 16 + l16) * CH + gl];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (n + r < N) P[((int64_t)m * N + n + r) * G + g] = acc[nb][mb][r] >> 8;
-              }
+          for (int r = 0; r < 4; ++r)
+            tot[mb][r] = fmaf(half_bits_to_float(wp[r]), fmaf(-kW4Bias, xsm, acc[mb][r]),
+                              tot[mb][r]);
+        }
+      } else {
+        v4i acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t p0 = j == 0 ? w.x : w.z, p1 = j == 0 ? w.y : w.w;
+          const v4i av = as_v4i(w4_lo_x16(p0), w4_hi_x16(p0), w4_lo_x16(p1), w4_hi_x16(p1));
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const v4i bv = *reinterpret_cast<const v4i*>(
+                &xs[buf][(mb * 16 + l16) * XSTB + gl * 128 + lg * 32 + j * 16]);
+            acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[mb], 0, 0, 0);
+          }
+        }
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = half_bits_to_float(wp[r]) * 0.00390625f;  // /256
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tot[mb][r] = fmaf(sc[r], (float)acc[mb][r], tot[mb][r]);
+          if (WITHP) {
+            const int m = m0 + mb * 16 + l16, n = n_w + lg * 4;
+            if (m < M) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (n + r < N) a.P[((int64_t)m * N + n + r) * G + g_begin + gi] = acc[mb][r] >> 8;
             }
           }
         }
       }
-    }
-    if (more) store_x(buf ^ 1);
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int gl = 0; gl < CH; ++gl)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) wcur[gl][nb] = wnext[gl][nb];
+      // refill the slot only after its old value is dead, so the new load can
+      // land in the same registers (no copies, no drain at the loop edge)
+      wr[s] = wload(gi + PD);
+      if (gl == CH - 1) {  // end of activation chunk c: publish chunk c+1, fetch c+2
+        x_store((c + 1) & 1);
+        __syncthreads();
+        x_load(c + 2);
+      }
     }
   }
 
-  float* o = out + (int64_t)blockIdx.y * slice_stride;
   const bool vec = (N & 3) == 0;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  if (a.S == 1) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = m0 + mb * 16 + l16;
-      const int n = n_w + nb * 16 + lg * 4;
+      const int n = n_w + lg * 4;
       if (m < M && n < N) {
-        const float a = apply_xs ? Xs[m] : 1.0f;
+        const float xsc = MODE == kW4A4 ? a.Xs[m] : 1.0f;
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = apply_xs ? a * tot[nb][mb][r] : tot[nb][mb][r];
-        float* dst = o + (int64_t)m * N + n;
+        for (int r = 0; r < 4; ++r) v[r] = MODE == kW4A4 ? xsc * tot[mb][r] : tot[mb][r];
+        float* dst = a.Y + (int64_t)m * N + n;
         if (vec) {
           *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
         } else {
@@ -441,82 +348,193 @@ __global__ __launch_bounds__(256) void w4a4_skinny_kernel(
         }
       }
     }
+    return;
+  }
+
+  // ---- split-K.  Partials are written and read with agent-coherent atomic
+  // accesses (they bypass the non-coherent caches), the writer waits for its
+  // stores to complete before the arrival count, and the last slice of the
+  // tile to arrive sums the S partials in slice order.
+  float* o = a.part + (int64_t)slice * M * N;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + mb * 16 + l16;
+    const int n = n_w + lg * 4;
+    if (m < M) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N)
+          __hip_atomic_store(o + (int64_t)m * N + n + r, tot[mb][r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long* slot = a.cnt + t;
+    unsigned long long cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned int count = 0;
+    for (;;) {
+      const unsigned long long nxt = ((unsigned int)(cur >> 32) == a.epoch)
+                                         ? cur + 1ull
+                                         : (((unsigned long long)a.epoch << 32) | 1ull);
+      if (__hip_atomic_compare_exchange_strong(slot, &cur, nxt, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        count = (unsigned int)(nxt & 0xffffffffull);
+        break;
+      }
+    }
+    s_last = count == (unsigned int)a.S;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // all partials of an element are requested before any is added (in slice
+  // order), 8 slices per batch
+  const int64_t MN = (int64_t)M * N;
+  constexpr int EPT = ROWS * 64 / 256;
+  float acc[EPT];
+  const float* src[EPT];
+  bool ok[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = threadIdx.x + 256 * e;
+    const int m = m0 + i / 64, n = n_wg + i % 64;
+    ok[e] = m < M && n < N;
+    src[e] = a.part + (int64_t)min(m, M - 1) * N + min(n, N - 1);
+    acc[e] = 0.f;
+  }
+  for (int s0 = 0; s0 < a.S; s0 += 8) {
+    float v[EPT][8];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[e][k] = __hip_atomic_load(src[e] + (int64_t)min(s0 + k, a.S - 1) * MN, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < a.S) acc[e] = (s0 + k == 0) ? v[e][k] : acc[e] + v[e][k];
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = threadIdx.x + 256 * e;
+    const int m = m0 + i / 64, n = n_wg + i % 64;
+    if (ok[e]) a.Y[(int64_t)m * N + n] = MODE == kW4A4 ? a.Xs[m] * acc[e] : acc[e];
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.cnt + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ============================================================================
-// W4A16 GEMV family (M <= 4): VALU dot products, one wavefront per row at a
-// time, lanes along K (16 bytes = 32 codes each, 1 KiB per row per pass),
-// cross-lane reduction per row.  Activations live in registers.
-//   grid = (ceil(N / (4 RPW)), ceil(K / 2048))
+// W4A16 GEMV family (M <= 4 per launch): VALU dot products, no MFMA.
+//   * a wavefront owns one 16-row block for a k-slice of up to 32 groups;
+//     lane l reads the tile slot of row l%16, codes 32*(l/16) .. +32 of each
+//     group -- one flat 1 KiB load per wavefront per group;
+//   * the activation slice (pair-interleaved to match the codes) and its
+//     32-element sums live in LDS, staged once per workgroup;
+//   * each lane accumulates ws * (x . (136 + q) - 136 * sum(x)) over its
+//     groups with v_dot2_f32_bf16; the four lanes of a row are reduced with
+//     two cross-lane steps at the end (the wavefront reduction).
+//   grid = (ceil(N / 64), ceil(G / 32))
 // ============================================================================
-template <int MM, int RPW>
+constexpr int kGemvGroups = 32;  // groups per k-slice
+
+template <int MM, int PD>
 __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wq,
     const uint16_t* __restrict__ Ws, int N, int K, float* __restrict__ out, int64_t slice_stride) {
+  constexpr int KS = kGemvGroups * kGroup;  // k per slice
+  __shared__ __attribute__((aligned(16))) uint32_t xs[MM][KS / 2];
+  __shared__ float xsum[MM][KS / 32];
   const int G = K / kGroup;
+  const int g0 = blockIdx.y * kGemvGroups;
+  const int ng = min(G - g0, kGemvGroups);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int k0 = blockIdx.y * 2048 + lane * 32;  // this lane's 32 codes
-  const bool kv = k0 < K;
-  const int g = k0 / kGroup;
+  const int r = lane & 15, c = lane >> 4;
 
-  // activations for the lane's 32 k, pair-interleaved to match the codes
-  uint32_t xp[MM][16];
-  float xsl[MM];
+  // stage the activation slice: MM rows x KS/8 chunks of 8
+#pragma unroll
+  for (int i = 0; i < MM * (KS / 8) / 256; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    const int m = idx / (KS / 8), c8 = idx % (KS / 8);
+    const int k = g0 * kGroup + c8 * 8;
+    uint4 v = *reinterpret_cast<const uint4*>(X + (int64_t)m * K + min(k, K - 8));
+    if (k >= K) v = make_uint4(0, 0, 0, 0);
+    const uint32_t nv[4] = {v.x, v.y, v.z, v.w};
+    uint32_t p[4];
+    bf16x8_interleave(nv, p);
+    *reinterpret_cast<uint4*>(&xs[m][c8 * 4]) = make_uint4(p[0], p[1], p[2], p[3]);
+    float s8 = bf16x8_sum(nv);  // four consecutive 8-chunks = one 32-chunk (a DPP quad)
+    s8 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s8), 0xB1, 0xF, 0xF, false));
+    s8 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s8), 0x4E, 0xF, 0xF, false));
+    if ((c8 & 3) == 0) xsum[m][c8 >> 2] = s8;
+  }
+  __syncthreads();
+
+  const int nrb = (N + 15) / 16;
+  const int rb = min(blockIdx.x * 4 + wave, nrb - 1);
+  const int n = min(rb * 16 + r, N - 1);
+  const uint8_t* wrow = Wq + ((int64_t)rb * G + g0) * 1024 + lane * 16;
+  const uint16_t* srow = Ws + (int64_t)n * G + g0;
+  auto wload = [&](int gi) { return ld_stream(wrow + (int64_t)min(gi, ng - 1) * 1024); };
+
+  float tot[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) tot[m] = 0.f;
+  uint4 wr[PD];
+  uint16_t sr[PD];
+#pragma unroll
+  for (int s = 0; s < PD; ++s) {
+    wr[s] = wload(s);
+    sr[s] = srow[min(s, ng - 1)];
+  }
+  for (int b0 = 0; b0 < ng; b0 += PD) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) {
+      const int gi = b0 + s;
+      const uint4 w = wr[s];
+      const float sc = half_bits_to_float(sr[s]);
+      if (gi < ng) {
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+        float acc[MM];
+#pragma unroll
+        for (int m = 0; m < MM; ++m) acc[m] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t a4[4];
+          w4_to_bf16_biased(wd[j], a4);
+#pragma unroll
+          for (int m = 0; m < MM; ++m) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(&xs[m][gi * 64 + c * 16 + j * 4]);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a4[i]),
+                                                       __builtin_bit_cast(v2bf, xw[i]), acc[m],
+                                                       false);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+          tot[m] = fmaf(sc, fmaf(-kW4Bias, xsum[m][gi * 4 + c], acc[m]), tot[m]);
+      }
+      wr[s] = wload(gi + PD);
+      sr[s] = srow[min(gi + PD, ng - 1)];
+    }
+  }
+  // the four lanes of a row (r, r+16, r+32, r+48) hold disjoint 32-chunks
 #pragma unroll
   for (int m = 0; m < MM; ++m) {
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint4 v = kv ? *reinterpret_cast<const uint4*>(X + (int64_t)m * K + k0 + c * 8)
-                   : make_uint4(0, 0, 0, 0);
-      const uint32_t n4[4] = {v.x, v.y, v.z, v.w};
-      uint32_t p[4];
-      bf16x8_interleave(n4, p);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xp[m][c * 4 + i] = p[i];
-      s += bf16x8_sum(n4);
-    }
-    xsl[m] = s;
+    tot[m] += __shfl_xor(tot[m], 16, 64);
+    tot[m] += __shfl_xor(tot[m], 32, 64);
   }
-
-  const int nbase = (blockIdx.x * 4 + wave) * RPW;
-  float* o = out + (int64_t)blockIdx.y * slice_stride;
-  constexpr int U = 4;  // rows in flight
-  for (int r0 = 0; r0 < RPW; r0 += U) {
-    uint4 w[U];
-    float sc[U];
+  const int nn = rb * 16 + r;
+  if (c == 0 && blockIdx.x * 4 + wave < nrb && nn < N) {
+    float* o = out + (int64_t)blockIdx.y * slice_stride;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int n = min(nbase + r0 + u, N - 1);
-      w[u] = kv ? ld_stream(Wq + (int64_t)n * (K / 2) + k0 / 2) : make_uint4(0, 0, 0, 0);
-      sc[u] = kv ? half_bits_to_float(Ws[(int64_t)n * G + g]) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t wd[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-      float acc[MM];
-#pragma unroll
-      for (int m = 0; m < MM; ++m) acc[m] = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t a4[4];
-        w4_to_bf16_biased(wd[c], a4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const v2bf a = __builtin_bit_cast(v2bf, a4[i]);
-#pragma unroll
-          for (int m = 0; m < MM; ++m)
-            acc[m] = __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(v2bf, xp[m][c * 4 + i]),
-                                                     acc[m], false);
-        }
-      }
-      const int n = nbase + r0 + u;
-#pragma unroll
-      for (int m = 0; m < MM; ++m) {
-        const float v = wave_sum(sc[u] * fmaf(-kW4Bias, xsl[m], acc[m]));
-        if (lane == 0 && n < N) o[(int64_t)m * N + n] = v;
-      }
-    }
+    for (int m = 0; m < MM; ++m) o[(int64_t)m * N + nn] = tot[m];
   }
 }
 
@@ -537,37 +555,75 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
 // Split-K depends on (N, K) only: an output row's operation order is the
 // same for every M within one family.
 struct SkinnyPlan {
-  int S, gps, MB, mchunks;
+  int S, gps, MB, mchunks, ntiles, T;
+  int64_t blocks;
+  size_t cnt_bytes, part_bytes;
 };
-constexpr int kSkinnyNB = 1;
 
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
   SkinnyPlan p;
   const int64_t G = K / kGroup;
-  const int64_t ntiles = cdiv(N, 64 * kSkinnyNB);
-  int64_t S = cdiv(512, ntiles);
-  if (S < 1) S = 1;
-  if (S > G) S = G;
+  p.ntiles = (int)cdiv(N, 64);
+  int64_t S = 1;
+  if (p.ntiles < QSPEC_SK_TARGET_WG) {
+    S = cdiv(QSPEC_SK_TARGET_WG, p.ntiles);
+    const int64_t smax = std::max<int64_t>(1, G / 4);  // at least 4 groups per slice
+    if (S > smax) S = smax;
+  }
   p.gps = (int)cdiv(G, S);
   p.S = (int)cdiv(G, p.gps);
   p.MB = (int)(M >= 64 ? 4 : cdiv(M, 16));
   p.mchunks = (int)cdiv(M, 16 * p.MB);
+  p.T = p.ntiles * p.mchunks;
+  p.blocks = 8 * cdiv(p.T, 8) * p.S;
+  p.cnt_bytes = p.S > 1 ? round_up((size_t)p.T * 8, 256) : 0;
+  p.part_bytes = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
   return p;
+}
+
+std::atomic<unsigned int> g_epoch{1};
+
+unsigned int next_epoch() {
+  unsigned int e = g_epoch.fetch_add(1, std::memory_order_relaxed);
+  if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed);  // 0 marks a free slot
+  return e;
+}
+
+template <int MODE, bool WITHP>
+hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
+  dim3 grid((unsigned)p.blocks), block(256);
+  if (MODE == kW4A16) {
+    switch (p.MB) {
+      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, QSPEC_SK_B1, WITHP>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_B2, WITHP>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_B3, WITHP>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_B4, WITHP>), grid, block, 0, s, a); break;
+    }
+  } else {
+    switch (p.MB) {
+      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, QSPEC_SK_A1, WITHP>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A4, 2, QSPEC_SK_A2, WITHP>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A4, 3, QSPEC_SK_A3, WITHP>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A4, 4, QSPEC_SK_A4, WITHP>), grid, block, 0, s, a); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_skinny(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
+  if (MODE == kW4A4 && a.P != nullptr) return launch_skinny_t<MODE, true>(a, p, s);
+  return launch_skinny_t<MODE, false>(a, p, s);
 }
 
 struct GemvPlan {
   int S;
 };
-constexpr int kGemvRPW = 16;
-GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K, 2048)}; }
+GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K / kGroup, kGemvGroups)}; }
 
 int w4a16_pick(int variant, int64_t M) {
   if (variant != QSPEC_GEMM_AUTO) return variant;
   return M <= 2 ? QSPEC_GEMM_GEMV : QSPEC_GEMM_SKINNY;
-}
-int w4a4_pick(int variant, int64_t /*M*/) {
-  if (variant != QSPEC_GEMM_AUTO) return variant;
-  return QSPEC_GEMM_SKINNY;
 }
 
 hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* Xs, float* Y,
@@ -585,8 +641,8 @@ hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* X
 size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const SkinnyPlan p = plan_skinny(M, N, K);
   const GemvPlan q = plan_gemv(K);
-  size_t a = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
-  size_t b = q.S > 1 ? (size_t)q.S * std::min<int64_t>(M, 4) * N * sizeof(float) : 0;
+  const size_t a = p.cnt_bytes + p.part_bytes;
+  const size_t b = q.S > 1 ? (size_t)q.S * std::min<int64_t>(M, 4) * N * sizeof(float) : 0;
   return std::max(a, b);
 }
 
@@ -600,13 +656,13 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
       const int mm = (int)std::min<int64_t>(4, M - m0);
       float* out = q.S > 1 ? static_cast<float*>(ws) : Y + m0 * N;
       const int64_t stride = (int64_t)mm * N;
-      dim3 grid((unsigned)cdiv(N, 4 * kGemvRPW), (unsigned)q.S);
+      dim3 grid((unsigned)cdiv(N, 64), (unsigned)q.S);
       const uint16_t* Xm = X + m0 * K;
       switch (mm) {
-        case 1: hipLaunchKernelGGL((w4a16_gemv_kernel<1, kGemvRPW>), grid, dim3(256), 0, s, Xm, Wq, Ws, (int)N, (int)K, out, stride); break;
-        case 2: hipLaunchKernelGGL((w4a16_gemv_kernel<2, kGemvRPW>), grid, dim3(256), 0, s, Xm, Wq, Ws, (int)N, (int)K, out, stride); break;
-        case 3: hipLaunchKernelGGL((w4a16_gemv_kernel<3, kGemvRPW>), grid, dim3(256), 0, s, Xm, Wq, Ws, (int)N, (int)K, out, stride); break;
-        default: hipLaunchKernelGGL((w4a16_gemv_kernel<4, kGemvRPW>), grid, dim3(256), 0, s, Xm, Wq, Ws, (int)N, (int)K, out, stride); break;
+        case 1: hipLaunchKernelGGL((w4a16_gemv_kernel<1, 8>), grid, dim3(256), 0, s, Xm, Wq, Ws, (int)N, (int)K, out, stride); break;
+        case 2: hipLaunchKernelGGL((w4a16_gemv_kernel<2, 8>), grid, dim3(256), 0, s, Xm, Wq, Ws, (int)N, (int)K, out, stride); break;
+        case 3: hipLaunchKernelGGL((w4a16_gemv_kernel<3, 8>), grid, dim3(256), 0, s, Xm, Wq, Ws, (int)N, (int)K, out, stride); break;
+        default: hipLaunchKernelGGL((w4a16_gemv_kernel<4, 8>), grid, dim3(256), 0, s, Xm, Wq, Ws, (int)N, (int)K, out, stride); break;
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -619,45 +675,40 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
   }
   // SKINNY (TILED shares it until the prefill family lands)
   const SkinnyPlan p = plan_skinny(M, N, K);
-  float* out = p.S > 1 ? static_cast<float*>(ws) : Y;
-  const int64_t stride = M * N;
-  dim3 grid((unsigned)cdiv(N, 64 * kSkinnyNB), (unsigned)p.S, (unsigned)p.mchunks);
-  switch (p.MB) {
-    case 1: hipLaunchKernelGGL((w4a16_skinny_kernel<kSkinnyNB, 1, 4>), grid, dim3(256), 0, s, X, Wq, Ws, (int)M, (int)N, (int)K, p.gps, out, stride); break;
-    case 2: hipLaunchKernelGGL((w4a16_skinny_kernel<kSkinnyNB, 2, 2>), grid, dim3(256), 0, s, X, Wq, Ws, (int)M, (int)N, (int)K, p.gps, out, stride); break;
-    case 3: hipLaunchKernelGGL((w4a16_skinny_kernel<kSkinnyNB, 3, 1>), grid, dim3(256), 0, s, X, Wq, Ws, (int)M, (int)N, (int)K, p.gps, out, stride); break;
-    default: hipLaunchKernelGGL((w4a16_skinny_kernel<kSkinnyNB, 4, 1>), grid, dim3(256), 0, s, X, Wq, Ws, (int)M, (int)N, (int)K, p.gps, out, stride); break;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.S > 1) return reduce(out, p.S, M, N, nullptr, Y, s);
-  return hipSuccess;
+  SkinnyArgs a{};
+  a.X = X;
+  a.Wq = Wq;
+  a.Ws = Ws;
+  a.Y = Y;
+  a.cnt = p.S > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
+  a.part = p.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.cnt_bytes) : nullptr;
+  a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;
+  a.epoch = next_epoch();
+  return launch_skinny<kW4A16>(a, p, s);
 }
 
 size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const SkinnyPlan p = plan_skinny(M, N, K);
-  return p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
+  return p.cnt_bytes + p.part_bytes;
 }
 
 hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
                        void* ws, hipStream_t s) {
-  (void)w4a4_pick(variant, M);
+  (void)variant;
   const SkinnyPlan p = plan_skinny(M, N, K);
-  float* out = p.S > 1 ? static_cast<float*>(ws) : Y;
-  const int apply = p.S > 1 ? 0 : 1;
-  const int64_t stride = M * N;
-  dim3 grid((unsigned)cdiv(N, 64 * kSkinnyNB), (unsigned)p.S, (unsigned)p.mchunks);
-  switch (p.MB) {
-    case 1: hipLaunchKernelGGL((w4a4_skinny_kernel<kSkinnyNB, 1, 4>), grid, dim3(256), 0, s, Xq, Xs, Wq, Ws, (int)M, (int)N, (int)K, p.gps, out, stride, P, apply); break;
-    case 2: hipLaunchKernelGGL((w4a4_skinny_kernel<kSkinnyNB, 2, 2>), grid, dim3(256), 0, s, Xq, Xs, Wq, Ws, (int)M, (int)N, (int)K, p.gps, out, stride, P, apply); break;
-    case 3: hipLaunchKernelGGL((w4a4_skinny_kernel<kSkinnyNB, 3, 2>), grid, dim3(256), 0, s, Xq, Xs, Wq, Ws, (int)M, (int)N, (int)K, p.gps, out, stride, P, apply); break;
-    default: hipLaunchKernelGGL((w4a4_skinny_kernel<kSkinnyNB, 4, 2>), grid, dim3(256), 0, s, Xq, Xs, Wq, Ws, (int)M, (int)N, (int)K, p.gps, out, stride, P, apply); break;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.S > 1) return reduce(out, p.S, M, N, Xs, Y, s);
-  return hipSuccess;
+  SkinnyArgs a{};
+  a.X = Xq;
+  a.Xs = Xs;
+  a.Wq = Wq;
+  a.Ws = Ws;
+  a.Y = Y;
+  a.P = P;
+  a.cnt = p.S > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
+  a.part = p.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.cnt_bytes) : nullptr;
+  a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;
+  a.epoch = next_epoch();
+  return launch_skinny<kW4A4>(a, p, s);
 }
 
 }  // namespace qspec

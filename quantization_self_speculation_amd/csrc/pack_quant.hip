@@ -19,26 +19,37 @@ __device__ __forceinline__ int quant_code(float v, float s) {
   return (int)fminf(fmaxf(r, -8.0f), 7.0f);
 }
 
-// One wavefront per (row n, group g): lane l owns k = 2l, 2l+1 of the group.
+// One wavefront per (row n, group g) of the row-padded matrix: lane l owns
+// k = 2l, 2l+1 of the group, i.e. byte l of the group's 64 row-major bytes,
+// and writes it to its place in the tiled storage order: 1 KiB tile per
+// (16-row block, group); inside it, 16-byte slot 16*(l/16) + n%16 holds row n's
+// bytes [16*(l/16), +16) of the group.  Padding rows (n >= N) get zero codes.
 __global__ __launch_bounds__(256) void pack_w4_kernel(const float* __restrict__ W, int64_t N,
-                                                      int64_t K, uint8_t* __restrict__ Wq,
+                                                      int64_t Np, int64_t K,
+                                                      uint8_t* __restrict__ Wq,
                                                       uint16_t* __restrict__ Ws) {
   const int64_t G = K / kGroup;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= N * G) return;  // uniform per wavefront
+  if (item >= Np * G) return;  // uniform per wavefront
   const int lane = threadIdx.x & 63;
   const int64_t n = item / G, g = item - (item / G) * G;
-  const float2 w = *reinterpret_cast<const float2*>(W + n * K + g * kGroup + 2 * lane);
-  const float a = wave_max(fmaxf(fabsf(w.x), fabsf(w.y)));
-  const _Float16 sh = (_Float16)(a / 7.0f);
-  const float s = (float)sh;
-  int q0 = 0, q1 = 0;
-  if (s != 0.0f) {
-    q0 = quant_code(w.x, s);
-    q1 = quant_code(w.y, s);
+  uint8_t byte = 0;
+  if (n < N) {  // uniform per wavefront
+    const float2 w = *reinterpret_cast<const float2*>(W + n * K + g * kGroup + 2 * lane);
+    const float a = wave_max(fmaxf(fabsf(w.x), fabsf(w.y)));
+    const _Float16 sh = (_Float16)(a / 7.0f);
+    const float s = (float)sh;
+    int q0 = 0, q1 = 0;
+    if (s != 0.0f) {
+      q0 = quant_code(w.x, s);
+      q1 = quant_code(w.y, s);
+    }
+    byte = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+    if (lane == 0) Ws[n * G + g] = __builtin_bit_cast(uint16_t, sh);
   }
-  Wq[n * (K / 2) + g * (kGroup / 2) + lane] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
-  if (lane == 0) Ws[n * G + g] = __builtin_bit_cast(uint16_t, sh);
+  const int64_t tile = (n >> 4) * G + g;
+  const int slot = (lane >> 4) * 16 + (int)(n & 15);
+  Wq[(tile * 64 + slot) * 16 + (lane & 15)] = byte;
 }
 
 __device__ __forceinline__ float absmax8(uint4 v) {
@@ -59,11 +70,75 @@ __device__ __forceinline__ uint32_t pack8(uint4 v, float s) {
   return word;
 }
 
-// One 256-thread block per token row.  Pass 1 finds the row absmax, pass 2
-// re-reads the row (an L2 hit) and writes 8 codes (one 32-bit word) per chunk.
+// One 256-thread block per token row.  The row is read once into registers
+// (NC 16-byte chunks per thread), reduced to its absmax, then coded.
+template <int NC>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ X,
                                                         int64_t K, uint8_t* __restrict__ Xq,
                                                         float* __restrict__ Xs) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const uint4* row = reinterpret_cast<const uint4*>(X + m * K);
+  const int nch = (int)(K / 8);
+  uint4 v[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    v[i] = c < nch ? row[c] : make_uint4(0, 0, 0, 0);
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) a = fmaxf(a, absmax8(v[i]));
+  a = wave_max(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = a / 7.0f;
+  uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nch) out[c] = s != 0.0f ? pack8(v[i], s) : 0u;
+  }
+  if (threadIdx.x == 0) Xs[m] = s;
+}
+
+// Short rows (K <= 8192): one wavefront per row, no block barrier; NC 16-byte
+// chunks per lane held in registers.
+template <int NC>
+__global__ __launch_bounds__(256) void quant_act_wave_kernel(const uint16_t* __restrict__ X,
+                                                             int64_t M, int64_t K,
+                                                             uint8_t* __restrict__ Xq,
+                                                             float* __restrict__ Xs) {
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;  // uniform per wavefront
+  const int lane = threadIdx.x & 63;
+  const uint4* row = reinterpret_cast<const uint4*>(X + m * K);
+  const int nch = (int)(K / 8);
+  uint4 v[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = row[min(c, nch - 1)];
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) a = fmaxf(a, absmax8(v[i]));
+  a = wave_max(a);
+  const float s = a / 7.0f;
+  uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) out[c] = s != 0.0f ? pack8(v[i], s) : 0u;
+  }
+  if (lane == 0) Xs[m] = s;
+}
+
+// rows longer than 256 * 16 * 8 = 32768: two passes (the second hits L2)
+__global__ __launch_bounds__(256) void quant_act_long_kernel(const uint16_t* __restrict__ X,
+                                                             int64_t K, uint8_t* __restrict__ Xq,
+                                                             float* __restrict__ Xs) {
   __shared__ float red[4];
   const int64_t m = blockIdx.x;
   const uint4* row = reinterpret_cast<const uint4*>(X + m * K);
@@ -76,11 +151,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = a / 7.0f;
   uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
-  if (s != 0.0f) {
-    for (int64_t c = threadIdx.x; c < nch; c += 256) out[c] = pack8(row[c], s);
-  } else {
-    for (int64_t c = threadIdx.x; c < nch; c += 256) out[c] = 0u;
-  }
+  for (int64_t c = threadIdx.x; c < nch; c += 256) out[c] = s != 0.0f ? pack8(row[c], s) : 0u;
   if (threadIdx.x == 0) Xs[m] = s;
 }
 
@@ -88,15 +159,30 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 
 hipError_t launch_pack_w4(const float* W, int64_t N, int64_t K, uint8_t* Wq, uint16_t* Ws,
                           hipStream_t s) {
-  const int64_t items = N * (K / kGroup);
-  hipLaunchKernelGGL(pack_w4_kernel, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, s, W, N, K,
+  const int64_t Np = cdiv(N, 16) * 16;
+  const int64_t items = Np * (K / kGroup);
+  hipLaunchKernelGGL(pack_w4_kernel, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, s, W, N, Np, K,
                      Wq, Ws);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
                             hipStream_t s) {
-  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)M), dim3(256), 0, s, X, K, Xq, Xs);
+  const int64_t perw = cdiv(K / 8, 64);  // 16-byte chunks per lane, one wavefront per row
+  if (perw <= 16) {
+    const dim3 g((unsigned)cdiv(M, 4)), b(256);
+    if (perw <= 4) hipLaunchKernelGGL(quant_act_wave_kernel<4>, g, b, 0, s, X, M, K, Xq, Xs);
+    else if (perw <= 8) hipLaunchKernelGGL(quant_act_wave_kernel<8>, g, b, 0, s, X, M, K, Xq, Xs);
+    else hipLaunchKernelGGL(quant_act_wave_kernel<16>, g, b, 0, s, X, M, K, Xq, Xs);
+    return hipGetLastError();
+  }
+  const int64_t per = cdiv(K / 8, 256);  // 16-byte chunks per thread
+  const dim3 g((unsigned)M), b(256);
+  if (per <= 2) hipLaunchKernelGGL(quant_act_kernel<2>, g, b, 0, s, X, K, Xq, Xs);
+  else if (per <= 4) hipLaunchKernelGGL(quant_act_kernel<4>, g, b, 0, s, X, K, Xq, Xs);
+  else if (per <= 8) hipLaunchKernelGGL(quant_act_kernel<8>, g, b, 0, s, X, K, Xq, Xs);
+  else if (per <= 16) hipLaunchKernelGGL(quant_act_kernel<16>, g, b, 0, s, X, K, Xq, Xs);
+  else hipLaunchKernelGGL(quant_act_long_kernel, g, b, 0, s, X, K, Xq, Xs);
   return hipGetLastError();
 }
 

@@ -21,7 +21,8 @@ namespace qspec {
 namespace {
 
 constexpr int kQPC = 2048;        // float4 quads per pass-1 chunk (8192 logits)
-constexpr int kRCW = 8192;        // logits per residual chunk
+constexpr int kRCW = 2048;        // logits per residual chunk (8 per thread)
+constexpr int kMaxRChunks = 4096; // V <= kRCW * kMaxRChunks
 
 __device__ __forceinline__ void argmax_merge(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) {
@@ -105,9 +106,10 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
     }
   }
 
-  float bv = hv;
-  int bi = hi;
+  const int lane = tid & 63, w = tid >> 6;
   if (GREEDY) {
+    float bv = hv;
+    int bi = hi;
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       const int i = (int)(a0 + 4 * (q0 + tid + 256 * k));
@@ -116,59 +118,52 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
       argmax_merge(bv, bi, v[k].z, i + 2);
       argmax_merge(bv, bi, v[k].w, i + 3);
     }
-  } else {
 #pragma unroll
-    for (int k = 0; k < QPT; ++k)
-      bv = fmaxf(bv, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
-  }
-  double s = 0.0;
-  if (!GREEDY && bv != -INFINITY) {
-    s = (double)exp_diff(hv, bv);
-#pragma unroll
-    for (int k = 0; k < QPT; ++k) {
-      s += (double)exp_diff(v[k].x, bv);
-      s += (double)exp_diff(v[k].y, bv);
-      s += (double)exp_diff(v[k].z, bv);
-      s += (double)exp_diff(v[k].w, bv);
-    }
-  }
-
-  // wavefront then block reduction, fixed order
-  const int lane = tid & 63, w = tid >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(bv, o, 64);
-    if (GREEDY) {
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o, 64);
       const int i2 = __shfl_xor(bi, o, 64);
       argmax_merge(bv, bi, v2, i2);
-    } else {
-      const double s2 = __shfl_xor(s, o, 64);
-      // symmetric merge so every lane holds identical bits
-      const float m = fmaxf(bv, v2);
-      const double a = (bv == -INFINITY) ? 0.0 : s * exp((double)bv - (double)m);
-      const double b = (v2 == -INFINITY) ? 0.0 : s2 * exp((double)v2 - (double)m);
-      s = (lane & o) ? b + a : a + b;
-      bv = m;
+    }
+    if (lane == 0) {
+      sm[w] = bv;
+      si[w] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float m = sm[0];
+      int ib = si[0];
+      for (int k = 1; k < 4; ++k) argmax_merge(m, ib, sm[k], si[k]);
+      pm[row * nck + c] = m;
+      pi[row * nck + c] = ib;
+    }
+    return;
+  }
+  // sampling: the chunk max first, then every exponential relative to it
+  float mx = hv;
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) mx = fmaxf(mx, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
+  mx = wave_max(mx);
+  if (lane == 0) sm[w] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  double s = 0.0;
+  if (mx != -INFINITY) {
+    s = (double)exp_diff(hv, mx);
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      // four terms in fp32 (each within ~1 ulp), then into the fp64 sum
+      const float e = (exp_diff(v[k].x, mx) + exp_diff(v[k].y, mx)) +
+                      (exp_diff(v[k].z, mx) + exp_diff(v[k].w, mx));
+      s += (double)e;
     }
   }
-  if (lane == 0) {
-    sm[w] = bv;
-    ss[w] = s;
-    si[w] = bi;
-  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (lane == 0) ss[w] = s;
   __syncthreads();
   if (tid == 0) {
-    float m = sm[0];
-    double sacc = ss[0];
-    int ib = si[0];
-    for (int k = 1; k < 4; ++k) {
-      if (GREEDY) argmax_merge(m, ib, sm[k], si[k]);
-      else lse_merge(m, sacc, sm[k], ss[k]);
-    }
-    const int64_t o = row * nck + c;
-    pm[o] = m;
-    if (GREEDY) pi[o] = ib;
-    else ps[o] = sacc;
+    pm[row * nck + c] = mx;
+    ps[row * nck + c] = (ss[0] + ss[1]) + (ss[2] + ss[3]);
   }
 }
 
@@ -233,34 +228,51 @@ struct Decision {
   double St, Sd;
 };
 
-// sampling decision: one wavefront per sequence.  p(x) and q(x) are fp64
-// (exact fp64 exponent of the exact difference over the pass-1 sums).
-__global__ __launch_bounds__(64) void sample_decide_kernel(
+// sampling decision: one 256-thread block per sequence.  The 2*gamma+1 row
+// normalizers are merged in parallel (one wavefront per row), the logits at
+// the drafted tokens are fetched in parallel, then one thread runs the
+// accept tests in order.  p(x) and q(x) are fp64: exact fp64 exponent of the
+// exact difference over the pass-1 sums.
+__global__ __launch_bounds__(256) void sample_decide_kernel(
     const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
     const float* __restrict__ ua, int gamma, int64_t V, int nck, const float* __restrict__ pm,
     const double* __restrict__ ps, int64_t rows_t, Decision* __restrict__ dec) {
+  __shared__ float lm[2 * QSPEC_MAX_GAMMA + 1];
+  __shared__ double lsum[2 * QSPEC_MAX_GAMMA + 1];
+  __shared__ float lxt[QSPEC_MAX_GAMMA], lxd[QSPEC_MAX_GAMMA];
   const int64_t b = blockIdx.x;
-  const int lane = threadIdx.x;
-  Decision D{gamma, 1, 0.f, 0.f, 1.0, 1.0};
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nr = 2 * gamma + 1;  // target rows 0..gamma, then draft rows
+  for (int r = w; r < nr; r += 4) {
+    const int64_t row = r <= gamma ? b * (gamma + 1) + r : rows_t + b * gamma + (r - gamma - 1);
+    float M;
+    double S;
+    row_lse(pm, ps, row, nck, lane, M, S);
+    if (lane == 0) {
+      lm[r] = M;
+      lsum[r] = S;
+    }
+  }
+  if (tid < gamma) {
+    const int x = min(max(dt[b * gamma + tid], 0), (int)(V - 1));
+    lxt[tid] = tgt[(b * (gamma + 1) + tid) * V + x];
+    lxd[tid] = drf[(b * gamma + tid) * V + x];
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  Decision D{gamma, 1, lm[gamma], 0.f, lsum[gamma], 1.0};
   for (int i = 0; i < gamma; ++i) {
-    const int64_t rt = b * (gamma + 1) + i;
-    const int64_t rd = rows_t + b * gamma + i;
-    float mt, md;
-    double st, sd;
-    row_lse(pm, ps, rt, nck, lane, mt, st);
-    row_lse(pm, ps, rd, nck, lane, md, sd);
-    int x = dt[b * gamma + i];
-    x = min(max(x, 0), (int)(V - 1));
-    const double p = exp((double)tgt[rt * V + x] - (double)mt) / st;
-    const double q = exp((double)drf[(b * gamma + i) * V + x] - (double)md) / sd;
+    const float mt = lm[i], md = lm[gamma + 1 + i];
+    const double st = lsum[i], sd = lsum[gamma + 1 + i];
+    const double p = exp((double)lxt[i] - (double)mt) / st;
+    const double q = exp((double)lxd[i] - (double)md) / sd;
     const bool acc = q > 0.0 ? ((double)ua[b * gamma + i] <= p / q) : (p > 0.0);
     if (!acc) {
       D = Decision{i, 0, mt, md, st, sd};
       break;
     }
   }
-  if (D.kind == 1) row_lse(pm, ps, b * (gamma + 1) + gamma, nck, lane, D.Mt, D.St);
-  if (lane == 0) dec[b] = D;
+  dec[b] = D;
 }
 
 // r_j of the row a sequence samples from, in fp64
@@ -272,13 +284,15 @@ __device__ __forceinline__ double resid(const float* rt, const float* rd, int64_
   return p > q ? p - q : 0.0;
 }
 
-// residual chunk sums: grid = (rnck, B).  rs[b][c] = sum r, pp[b][c] = sum p.
+// residual chunk sums: grid = (rnck, B), kRCW logits per block (8 per
+// thread, coalesced).  rs[b][c] = sum r, pp[b][c] = sum p (fp64).
 __global__ __launch_bounds__(256) void resid_sums_kernel(const float* __restrict__ tgt,
                                                          const float* __restrict__ drf, int gamma,
                                                          int64_t V, int rnck,
                                                          const Decision* __restrict__ dec,
                                                          double* __restrict__ rs,
                                                          double* __restrict__ pp) {
+  constexpr int EPT = kRCW / 256;
   __shared__ double red[2][4];
   const int c = blockIdx.x;
   const int64_t b = blockIdx.y;
@@ -286,17 +300,21 @@ __global__ __launch_bounds__(256) void resid_sums_kernel(const float* __restrict
   const double iSt = 1.0 / D.St, iSd = 1.0 / D.Sd;
   const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
   const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
-  const int64_t j0 = (int64_t)c * kRCW, j1 = min(V, j0 + kRCW);
+  const int64_t j0 = (int64_t)c * kRCW;
+  float lt[EPT], ld[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int64_t j = j0 + threadIdx.x + 256 * k;
+    lt[k] = j < V ? rt[j] : -INFINITY;
+    ld[k] = (j < V && D.kind == 0) ? rd[j] : -INFINITY;
+  }
   double sr = 0.0, sp = 0.0;
-  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
-    const double p = (double)exp_diff(rt[j], D.Mt) * iSt;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const double p = (double)exp_diff(lt[k], D.Mt) * iSt;
+    const double q = (double)exp_diff(ld[k], D.Md) * iSd;
     sp += p;
-    if (D.kind == 1) {
-      sr += p;
-    } else {
-      const double q = (double)exp_diff(rd[j], D.Md) * iSd;
-      sr += p > q ? p - q : 0.0;
-    }
+    sr += D.kind == 1 ? p : (p > q ? p - q : 0.0);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -316,82 +334,117 @@ __global__ __launch_bounds__(256) void resid_sums_kernel(const float* __restrict
 }
 
 // inverse-CDF select: one 256-thread block per sequence, fp64 cumulative sums.
+// The chunk holding the threshold is found from the chunk totals (sequential,
+// fixed order); inside it each thread takes 8 consecutive logits, and a
+// block-wide exclusive scan gives every thread its starting cumulative sum.
 __global__ __launch_bounds__(256) void sample_select_kernel(
     const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
     const float* __restrict__ us, int gamma, int64_t V, int rnck,
     const Decision* __restrict__ dec, const double* __restrict__ rs,
     const double* __restrict__ pp, int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tok) {
-  __shared__ double seg[256];
+  constexpr int EPT = kRCW / 256;
+  __shared__ double wsum[4];
+  __shared__ double tr[kMaxRChunks], tp[kMaxRChunks];
   __shared__ int found;
   __shared__ int lastj;
+  __shared__ int sh_cs, sh_cc, sh_kind;
+  __shared__ double sh_base, sh_thr;
   const int64_t b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const Decision D = dec[b];
-  int kind = D.kind;
   const double iSt = 1.0 / D.St, iSd = 1.0 / D.Sd;
   const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
   const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
 
-  // chunk totals in fixed sequential order (every thread computes the same)
-  const double* tot = rs + b * rnck;
-  double R = 0.0;
-  for (int c = 0; c < rnck; ++c) R += tot[c];
-  if (R == 0.0 && kind == 0) {  // p == q everywhere: sample from p
-    kind = 1;
-    tot = pp + b * rnck;
-    R = 0.0;
+  for (int c = tid; c < rnck; c += 256) {
+    tr[c] = rs[b * rnck + c];
+    tp[c] = pp[b * rnck + c];
+  }
+  __syncthreads();
+  if (tid == 0) {  // chunk totals in fixed sequential order
+    int kind = D.kind;
+    const double* tot = tr;
+    double R = 0.0;
     for (int c = 0; c < rnck; ++c) R += tot[c];
-  }
-  const double thr = (double)us[b] * R;
-  int cs = -1;
-  double base = 0.0, run = 0.0;
-  for (int c = 0; c < rnck; ++c) {
-    const double nx = run + tot[c];
-    if (nx > thr) {
-      cs = c;
-      base = run;
-      break;
+    if (R == 0.0 && kind == 0) {  // p == q everywhere: sample from p
+      kind = 1;
+      tot = tp;
+      R = 0.0;
+      for (int c = 0; c < rnck; ++c) R += tot[c];
     }
-    run = nx;
-  }
-  int last_c = -1;  // fallback: last chunk with mass
-  for (int c = rnck - 1; c >= 0; --c)
-    if (tot[c] > 0.0) {
-      last_c = c;
-      break;
+    const double thr = (double)us[b] * R;
+    int cs = -1;
+    double base = 0.0, run = 0.0;
+    for (int c = 0; c < rnck; ++c) {
+      const double nx = run + tot[c];
+      if (nx > thr) {
+        cs = c;
+        base = run;
+        break;
+      }
+      run = nx;
     }
-  const int cc = cs >= 0 ? cs : (last_c >= 0 ? last_c : 0);
-  const int64_t j0 = (int64_t)cc * kRCW, j1 = min(V, j0 + kRCW);
-  const int64_t len = j1 - j0;
-  const int64_t per = (len + 255) / 256;  // contiguous segment per thread
-  const int64_t s0 = j0 + tid * per, s1 = min(j1, s0 + per);
-
-  // per-thread segment sums, then exclusive scan over threads (sequential)
+    int last_c = -1;  // fallback: last chunk with mass
+    for (int c = rnck - 1; c >= 0; --c)
+      if (tot[c] > 0.0) {
+        last_c = c;
+        break;
+      }
+    sh_cs = cs;
+    sh_cc = cs >= 0 ? cs : (last_c >= 0 ? last_c : 0);
+    sh_kind = kind;
+    sh_base = base;
+    sh_thr = thr;
+  }
+  __syncthreads();
+  const int cs = sh_cs, cc = sh_cc, kind = sh_kind;
+  const double base = sh_base, thr = sh_thr;
+  const int64_t js = (int64_t)cc * kRCW + (int64_t)tid * EPT;  // this thread's 8 logits
+  double r[EPT];
   double ls = 0.0;
-  for (int64_t j = s0; j < s1; ++j) ls += resid(rt, rd, j, kind, D.Mt, iSt, D.Md, iSd);
-  seg[tid] = ls;
+  int mylast = -1;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int64_t j = js + k;
+    double v = 0.0;
+    if (j < V) {
+      const double p = (double)exp_diff(rt[j], D.Mt) * iSt;
+      if (kind == 1) {
+        v = p;
+      } else {
+        const double q = (double)exp_diff(rd[j], D.Md) * iSd;
+        v = p > q ? p - q : 0.0;
+      }
+    }
+    r[k] = v;
+    ls += v;
+    if (v > 0.0) mylast = (int)j;
+  }
+  // inclusive scan of the thread sums within the wavefront, then across waves
+  double inc = ls;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  double exc = __shfl_up(inc, 1, 64);  // exclusive prefix within the wavefront
+  if (lane == 0) exc = 0.0;
+  if (lane == 63) wsum[w] = inc;
   if (tid == 0) {
     found = 0x7FFFFFFF;
     lastj = -1;
   }
   __syncthreads();
-  if (tid == 0) {
-    double acc = 0.0;
-    for (int t = 0; t < 256; ++t) {
-      const double v = seg[t];
-      seg[t] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
+  double wbase = 0.0;
+  for (int k = 0; k < w; ++k) wbase += wsum[k];
   int my = 0x7FFFFFFF;
-  int mylast = -1;
-  double cum = base + seg[tid];
-  for (int64_t j = s0; j < s1; ++j) {
-    const double r = resid(rt, rd, j, kind, D.Mt, iSt, D.Md, iSd);
-    cum += r;
-    if (cs >= 0 && my == 0x7FFFFFFF && cum > thr) my = (int)j;
-    if (r > 0.0) mylast = (int)j;
+  if (cs >= 0) {
+    double cum = base + wbase + exc;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      cum += r[k];
+      if (my == 0x7FFFFFFF && cum > thr) my = (int)(js + k);
+    }
   }
   atomicMin(&found, my);  // LDS min / max of candidate indices: order-independent
   atomicMax(&lastj, mylast);
@@ -464,7 +517,7 @@ hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_
                      target_logits, draft_logits, rows_t, V, L.nck, pm, ps, pi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sample_decide_kernel, dim3((unsigned)B), dim3(64), 0, s, target_logits,
+  hipLaunchKernelGGL(sample_decide_kernel, dim3((unsigned)B), dim3(256), 0, s, target_logits,
                      draft_logits, draft_tok, u_accept, gamma, V, L.nck, pm, ps, rows_t, dec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(resid_sums_kernel, dim3(L.rnck, (unsigned)B), dim3(256), 0, s,

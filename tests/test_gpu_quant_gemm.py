@@ -32,6 +32,11 @@ SHAPES = [
 ]
 
 
+def dev_w(Wq):
+    """oracle row-major packed bytes -> device buffer in the tiled storage order"""
+    return dev(oracle.tile_w4(Wq))
+
+
 def _case(seed, M, N, K, outliers=None):
     rng = synth.make_rng(seed)
     W = synth.weights(rng, N, K)
@@ -49,7 +54,7 @@ def test_pack_w4_bitexact(N, K):
     W[min(1, N - 1), 128:256] = 0        # an all-zero group
     Wq_ref, Ws_ref = oracle.pack_w4(W)
     Wq, Ws = q.pack_w4(dev(W))
-    assert np.array_equal(host(Wq), Wq_ref)
+    assert np.array_equal(host(Wq), oracle.tile_w4(Wq_ref))
     assert np.array_equal(host_bits16(Ws), Ws_ref)
 
 
@@ -64,7 +69,7 @@ def test_pack_w4_hand_and_subnormal(golden):
     W[2, 0] = np.float32(2.0 ** -27)           # scale underflows to 0
     Wq_ref, Ws_ref = oracle.pack_w4(W)
     Wq, Ws = q.pack_w4(dev(W))
-    assert np.array_equal(host(Wq), Wq_ref)
+    assert np.array_equal(host(Wq), oracle.tile_w4(Wq_ref))
     assert np.array_equal(host_bits16(Ws), Ws_ref)
     assert Ws_ref[0].tolist() == [grp["scale_bits"] for grp in g["groups"]]
 
@@ -117,7 +122,7 @@ def test_w4a4_parity(M, N, K, variant):
     W, X = _case(12, M, N, K)
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
-    Y, P = q.gemm_w4a4(dev(Xq), dev(Xs), dev(Wq), dev_f16(Ws), variant=variant, partials=True)
+    Y, P = q.gemm_w4a4(dev(Xq), dev(Xs), dev_w(Wq), dev_f16(Ws), variant=variant, partials=True)
     assert np.array_equal(host(P), oracle.w4a4_partials(Xq, Wq))
     assert_close(host(Y), oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4")
 
@@ -127,7 +132,7 @@ def test_w4a4_gpu_quantized_chain():
     W, X = _case(13, 8, 1024, 1024, outliers=4)
     Wq, Ws = oracle.pack_w4(W)
     Xq_d, Xs_d = q.quant_act(dev_bf16(X))
-    Y = q.gemm_w4a4(Xq_d, Xs_d, dev(Wq), dev_f16(Ws))
+    Y = q.gemm_w4a4(Xq_d, Xs_d, dev_w(Wq), dev_f16(Ws))
     Xq, Xs = oracle.quant_act(X)
     assert_close(host(Y), oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4 chain")
 
@@ -139,7 +144,7 @@ def test_w4a16_parity(M, N, K, variant):
     say(f"w4a16 M={M} N={N} K={K} variant={variant}")
     W, X = _case(14, M, N, K)
     Wq, Ws = oracle.pack_w4(W)
-    Y = q.gemm_w4a16(dev_bf16(X), dev(Wq), dev_f16(Ws), variant=variant)
+    Y = q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_f16(Ws), variant=variant)
     assert_close(host(Y), oracle.gemm_w4a16(X, Wq, Ws), what="w4a16")
 
 
@@ -156,10 +161,10 @@ def test_w4a16_zero_and_lossless_rows():
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
     for v in W4A16_VARIANTS:
-        Y16 = host(q.gemm_w4a16(dev_bf16(X), dev(Wq), dev_f16(Ws), variant=v))
+        Y16 = host(q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_f16(Ws), variant=v))
         assert np.all(Y16[1] == 0)
         assert_close(Y16, oracle.gemm_w4a16(X, Wq, Ws))
-    Y4 = host(q.gemm_w4a4(dev(Xq), dev(Xs), dev(Wq), dev_f16(Ws)))
+    Y4 = host(q.gemm_w4a4(dev(Xq), dev(Xs), dev_w(Wq), dev_f16(Ws)))
     assert np.all(Y4[1] == 0)
     assert_close(Y4, oracle.gemm_w4a16(X, Wq, Ws))
 
@@ -171,7 +176,7 @@ def test_w4a16_row_invariance(variant):
     N, K = 2048, 2048
     W, X = _case(16, 80, N, K)
     Wq, Ws = oracle.pack_w4(W)
-    Wq_d, Ws_d, X_d = dev(Wq), dev_f16(Ws), dev_bf16(X)
+    Wq_d, Ws_d, X_d = dev_w(Wq), dev_f16(Ws), dev_bf16(X)
     Y80 = host(q.gemm_w4a16(X_d, Wq_d, Ws_d, variant=variant))
     Y16 = host(q.gemm_w4a16(X_d[:16].contiguous(), Wq_d, Ws_d, variant=variant))
     assert np.array_equal(Y80[:16].view(np.uint32), Y16.view(np.uint32))
@@ -185,7 +190,7 @@ def test_w4a4_row_invariance():
     W, X = _case(17, 80, N, K)
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
-    args = (dev(Wq), dev_f16(Ws))
+    args = (dev_w(Wq), dev_f16(Ws))
     Y80 = host(q.gemm_w4a4(dev(Xq), dev(Xs), *args, variant=q.GEMM_SKINNY))
     for r in (0, 41):
         Y1 = host(q.gemm_w4a4(dev(Xq[r:r + 1]), dev(Xs[r:r + 1]), *args, variant=q.GEMM_SKINNY))
@@ -196,8 +201,8 @@ def test_determinism():
     W, X = _case(18, 40, 4608, 3584)
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
-    a16 = (dev_bf16(X), dev(Wq), dev_f16(Ws))
-    a4 = (dev(Xq), dev(Xs), dev(Wq), dev_f16(Ws))
+    a16 = (dev_bf16(X), dev_w(Wq), dev_f16(Ws))
+    a4 = (dev(Xq), dev(Xs), dev_w(Wq), dev_f16(Ws))
     y1 = host(q.gemm_w4a16(*a16))
     y2 = host(q.gemm_w4a16(*a16))
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
@@ -227,7 +232,7 @@ def test_qwen7b_decode_shapes(proj):
     cols = _sampled_cols(N, rng)
     Wq, Ws = oracle.pack_w4(W[cols])          # oracle packs the sampled rows only
     Wq_d, Ws_d = q.pack_w4(dev(W))            # the device packs everything
-    assert np.array_equal(host(Wq_d)[cols], Wq)
+    assert np.array_equal(oracle.untile_w4(host(Wq_d), N)[cols], Wq)
     for M in (1, 8, 32):
         say(f"{proj} w4a4 M={M}")
         Xq_d, Xs_d = q.quant_act(dev_bf16(X[:M].copy()))
@@ -275,3 +280,57 @@ def test_llama8b_lm_head_gemv():
         say(f"lm_head variant={v}")
         Y = host(q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=v))
         assert_close(Y[:, cols], oracle.gemm_w4a16(X, Wq, Ws))
+
+
+# ------------------------------------------------------------------ graphs
+def test_graph_replays_match_eager():
+    """The library's launches captured in a HIP graph (split-K shapes whose
+    in-kernel reduction relies on workspace counters the kernels reset) give
+    the eager result on every replay, with eager work in between."""
+    M4, M16, N, K = 8, 40, 3584, 18944          # a split-K shape in both modes
+    W, X = _case(19, M16, N, K)
+    Wq, Ws = oracle.pack_w4(W)
+    Wq_d, Ws_d, X_d = dev_w(Wq), dev_f16(Ws), dev_bf16(X)
+    X4 = X_d[:M4].contiguous()
+    Xq, Xs = q.quant_act(X4)
+    Y4 = torch.empty((M4, N), dtype=torch.float32, device="cuda")
+    Y16 = torch.empty((M16, N), dtype=torch.float32, device="cuda")
+    ws4 = torch.empty(q.workspace_bytes(1, M4, N, K), dtype=torch.uint8, device="cuda")
+    ws16 = torch.empty(q.workspace_bytes(2, M16, N, K), dtype=torch.uint8, device="cuda")
+
+    def body():
+        q.quant_act(X4, Xq, Xs)
+        q.gemm_w4a4(Xq, Xs, Wq_d, Ws_d, Y=Y4, ws=ws4)
+        q.gemm_w4a16(X_d, Wq_d, Ws_d, Y=Y16, ws=ws16)
+
+    body()
+    torch.cuda.synchronize()
+    e4, e16 = host(Y4).copy(), host(Y16).copy()
+    assert_close(e16, oracle.gemm_w4a16(X, Wq, Ws))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        body()
+    for rep in range(3):
+        Y4.zero_()
+        Y16.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Y4).view(np.uint32), e4.view(np.uint32)), rep
+        assert np.array_equal(host(Y16).view(np.uint32), e16.view(np.uint32)), rep
+        body()                                   # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Y16).view(np.uint32), e16.view(np.uint32)), rep
+
+
+def test_fresh_garbage_workspace():
+    """A workspace full of arbitrary bytes (not zeroed) still gives the right
+    split-K result: the arrival counters are tagged with a per-call epoch."""
+    M, N, K = 8, 3584, 18944
+    W, X = _case(20, M, N, K)
+    Wq, Ws = oracle.pack_w4(W)
+    nb = q.workspace_bytes(2, M, N, K)
+    ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda")
+    Y = q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_f16(Ws), variant=q.GEMM_SKINNY, ws=ws)
+    assert_close(host(Y), oracle.gemm_w4a16(X, Wq, Ws))

@@ -327,3 +327,34 @@ def test_w4a4_is_lossy_with_outliers():
     Y4 = oracle.gemm_w4a4(Xq, Xs, Wq, Ws)
     Y16 = oracle.gemm_w4a16(X, Wq, Ws)
     assert np.abs(Y4 - Y16).max() > 0.05 * np.abs(Y16).max()
+
+
+# ----------------------------------------------------------------------------
+# storage order of the shared buffer
+# ----------------------------------------------------------------------------
+def test_tile_is_a_permutation_with_zero_padding():
+    rng = np.random.default_rng(3)
+    for N, K in ((1, 128), (16, 256), (37, 384), (64, 1024)):
+        Wq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+        T = oracle.tile_w4(Wq)
+        Np = -(-N // 16) * 16
+        assert T.shape == (Np, K // 2)
+        assert np.array_equal(oracle.untile_w4(T, N), Wq)
+        # multiset of bytes = the row-major bytes plus zero padding
+        pad = np.zeros((Np - N) * (K // 2), np.uint8)
+        assert np.array_equal(np.sort(T.ravel()), np.sort(np.concatenate([Wq.ravel(), pad])))
+
+
+def test_tile_hand_positions():
+    """Tile (b, g) starts at byte (b*G + g)*1024; slot l holds row 16b + l%16,
+    row bytes 64g + 16(l//16) .. +16 (hand-derived from the definition)."""
+    N, K = 32, 256                      # G = 2 groups, 2 row blocks
+    Wq = np.zeros((N, K // 2), np.uint8)
+    Wq[17, 64 + 16 * 2 + 5] = 0xAB     # row 17 = block 1, r 1; group 1, chunk 2, byte 5
+    Wq[3, 0] = 0x11                     # row 3 = block 0, r 3; group 0, chunk 0, byte 0
+    flat = oracle.tile_w4(Wq).ravel()
+    G = 2
+    pos1 = ((1 * G + 1) * 64 + (16 * 2 + 1)) * 16 + 5
+    pos2 = ((0 * G + 0) * 64 + (16 * 0 + 3)) * 16 + 0
+    assert flat[pos1] == 0xAB and flat[pos2] == 0x11
+    assert np.count_nonzero(flat) == 2
