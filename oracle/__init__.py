@@ -35,6 +35,8 @@ from .quant import (  # noqa: F401
     pack_w4,
     tile_w4,
     untile_w4,
+    tile_scales,
+    untile_scales,
     dequant_w4,
     quant_act,
     w4a4_partials,

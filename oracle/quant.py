@@ -24,8 +24,10 @@ group size, no scale precision and no bit layout.  Readings taken here:
   are padded with zero codes to a multiple of 16 and the row-major bytes are
   re-ordered in 1 KiB tiles, one per (16-row block b, group g); inside a tile,
   16-byte slot l holds the 32 codes k in [128 g + 32 (l // 16), +32) of row
-  16 b + (l % 16).  ``tile_w4`` / ``untile_w4`` convert; the scales stay
-  row-major [N][K/128].
+  16 b + (l % 16).  The fp16 scales are padded the same way and stored as
+  32-byte tiles, one per (16-row block b, group g), row order inside.
+  ``tile_w4`` / ``untile_w4`` and ``tile_scales`` / ``untile_scales``
+  convert.
 * W4A4: per-group integer partials P[m,n,g] = sum_k qa*qw (exact), then
   Y = a_scale[m] * sum_g w_scale[n,g] * P[m,n,g].
 * W4A16: Y = sum_g w_scale[n,g] * sum_k x[m,k]*q[n,k] with x the bf16 value.
@@ -119,6 +121,25 @@ def tile_w4(Wq):
     # tile order [b, g, c, r, j]: slot l = 16c + r
     T = T.transpose(0, 2, 3, 1, 4)
     return np.ascontiguousarray(T).reshape(Np, KB)
+
+
+def tile_scales(Ws):
+    """row-major fp16 scale bits [N, G] -> tiled [ceil(N/16)*16, G]:
+    element (b*G + g)*16 + r of the flat buffer = scale of row 16b + r, group g."""
+    Ws = np.asarray(Ws, dtype=np.uint16)
+    N, G = Ws.shape
+    Np = -(-N // TILE_ROWS) * TILE_ROWS
+    R = np.zeros((Np, G), dtype=np.uint16)
+    R[:N] = Ws
+    T = R.reshape(Np // 16, 16, G).transpose(0, 2, 1)
+    return np.ascontiguousarray(T).reshape(Np, G)
+
+
+def untile_scales(Wt, N):
+    Wt = np.asarray(Wt, dtype=np.uint16)
+    Np, G = Wt.shape
+    T = Wt.reshape(Np // 16, G, 16).transpose(0, 2, 1)
+    return np.ascontiguousarray(T).reshape(Np, G)[:N]
 
 
 def untile_w4(Wt, N):

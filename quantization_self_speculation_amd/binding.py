@@ -95,6 +95,14 @@ def _need(t, name, dtype, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _out_n(N, Y, Wq):
+    if N is not None:
+        return int(N)
+    if Y is not None:
+        return int(Y.shape[1])
+    return int(Wq.shape[0])
+
+
 def workspace_bytes(op, a, b, c):
     return int(lib().qspec_workspace_bytes(op, a, b, c))
 
@@ -114,14 +122,15 @@ def padded_rows(N):
 
 
 def pack_w4(W, Wq=None, Ws=None, N=None):
-    """fp32 [N, K] -> (Wq uint8 [ceil(N/16)*16, K/2] in the tiled storage
-    order, Ws float16 [N, K/128])."""
+    """fp32 [N, K] -> (Wq uint8 [Np, K/2], Ws float16 [Np, K/128]), Np =
+    ceil(N/16)*16, both in the tiled storage order.  Pass N to the GEMMs."""
     _need(W, "W", torch.float32)
     N, K = W.shape
     if Wq is None:
         Wq = torch.empty((padded_rows(N), K // 2), dtype=torch.uint8, device=W.device)
     if Ws is None:
-        Ws = torch.empty((N, max(K // GROUP, 1)), dtype=torch.float16, device=W.device)
+        Ws = torch.empty((padded_rows(N), max(K // GROUP, 1)), dtype=torch.float16,
+                         device=W.device)
     _check(lib().qspec_pack_w4(_ptr(W), N, K, GROUP, _ptr(Wq), _ptr(Ws), _stream()),
            "qspec_pack_w4")
     return Wq, Ws
@@ -139,18 +148,19 @@ def quant_act(X, Xq=None, Xs=None):
     return Xq, Xs
 
 
-def gemm_w4a4(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, partials=False, Y=None, P=None, ws=None):
+def gemm_w4a4(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, partials=False, Y=None, P=None, ws=None, N=None):
     """Draft-mode linear layer -> Y fp32 [M, N] (and int32 partials [M, N, K/128]).
-    N is taken from the scales Ws [N, K/128]; Wq is the tiled buffer."""
+    Wq, Ws are the tiled buffers of qspec_pack_w4 ([Np, ...], Np = ceil(N/16)*16);
+    N defaults to Y's width, else Np."""
     _need(Xq, "Xq", torch.uint8)
     _need(Wq, "Wq", torch.uint8)
     _need(Xs, "Xs", torch.float32)
     _need(Ws, "Ws", torch.float16)
     M, K = Xq.shape[0], 2 * Xq.shape[1]
-    N = Ws.shape[0]
+    N = _out_n(N, Y, Wq)
     _need(Xs, "Xs", torch.float32, (M,))
     _need(Wq, "Wq", torch.uint8, (padded_rows(N), K // 2))
-    _need(Ws, "Ws", torch.float16, (N, K // GROUP))
+    _need(Ws, "Ws", torch.float16, (padded_rows(N), K // GROUP))
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
     if partials and P is None:
@@ -161,13 +171,13 @@ def gemm_w4a4(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, partials=False, Y=None, P=None,
     return (Y, P) if partials else Y
 
 
-def gemm_w4a16(X, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None):
-    """Verify-mode linear layer -> Y fp32 [M, N]."""
+def gemm_w4a16(X, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None, N=None):
+    """Verify-mode linear layer -> Y fp32 [M, N] (N as for gemm_w4a4)."""
     _need(X, "X", torch.bfloat16)
     M, K = X.shape
-    N = Ws.shape[0]
+    N = _out_n(N, Y, Wq)
     _need(Wq, "Wq", torch.uint8, (padded_rows(N), K // 2))
-    _need(Ws, "Ws", torch.float16, (N, K // GROUP))
+    _need(Ws, "Ws", torch.float16, (padded_rows(N), K // GROUP))
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
     w, wb = _workspace(workspace_bytes(OP_GEMM_W4A16, M, N, K), X.device, ws)

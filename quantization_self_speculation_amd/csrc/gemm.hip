@@ -14,8 +14,9 @@
 // gfx950 design
 //  * Codes are widened in registers only; the shared buffer stays 4-bit.
 //    W4A16 turns a nibble into the bf16 of 136 + q with one AND-OR (exact),
-//    runs v_mfma_f32_16x16x32_bf16 and removes the bias with the group sum of
-//    x in the fp32 epilogue.  W4A4 turns nibbles into int8 holding 16 q with
+//    runs v_mfma_f32_16x16x32_bf16 and removes the bias with a second MFMA
+//    chain whose A operand is the constant -136 (the skinny family) or with
+//    the group sum of x (the GEMV family), in fp32 before the scale.  W4A4 turns nibbles into int8 holding 16 q with
 //    one AND (exact) and runs v_mfma_i32_16x16x64_i8; the int32 group partial
 //    is 256 P exactly.
 //  * MFMA operand A = 16 weight rows (n), operand B = 16 activation rows (m),
@@ -58,8 +59,11 @@
 #ifndef QSPEC_SK_B4
 #define QSPEC_SK_B4 1, 4
 #endif
+#ifndef QSPEC_SK_NB16
+#define QSPEC_SK_NB16 1    // W4A16, M > 16: 16-row blocks per wavefront
+#endif
 #ifndef QSPEC_SK_TARGET_WG
-#define QSPEC_SK_TARGET_WG 512
+#define QSPEC_SK_TARGET_WG 256
 #endif
 
 
@@ -67,6 +71,9 @@ namespace qspec {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// two bf16 -136.0 (0xC308): removes the +136 bias of the widened codes
+constexpr uint32_t kNegBiasPair = 0xC308C308u;
 
 // streaming (non-temporal) 16-byte load: weights are read exactly once
 __device__ __forceinline__ uint4 ld_stream(const void* p) {
@@ -107,9 +114,9 @@ __device__ __forceinline__ float group_sum16(float v) {
 //     kernel by the last slice to arrive, in fixed slice order; arrival is
 //     counted with an epoch-tagged 64-bit counter per tile in the caller's
 //     workspace that the last slice resets to 0;
-//   * block -> (tile, slice) mapping keeps the S slices of a tile on one XCD
-//     (blocks are dealt round-robin to the 8 XCDs), so partials stay in that
-//     XCD's L2.
+//   * block -> (tile, slice) mapping deals the S slices of a tile to one XCD
+//     when blocks go round-robin to the 8 XCDs (a locality hint only: the
+//     hand-off of partials is correct on any placement).
 // ============================================================================
 enum { kW4A16 = 0, kW4A4 = 1 };
 
@@ -126,32 +133,136 @@ struct SkinnyArgs {
   unsigned epoch;
 };
 
-// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15) with a fixed
-// rotate-and-add tree; the value in lane 16r is what callers use.  The tree
-// depends only on a value's position in the row.
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));  // row_ror:8
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));  // row_ror:4
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));   // quad xor 2
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // quad xor 1
-  return v;
+// End of a (tile, slice): store Y (times Xs for W4A4) when the k-range is not
+// split, else publish this slice's partial and let the last slice to arrive
+// reduce all S partials in slice order.  Partials are written and read with
+// system-scope atomic accesses (coherent whatever XCD each slice ran on: they
+// do not stay in an XCD's L2), the writer waits for its stores to complete
+// before the arrival count, and the arrival counter (epoch-tagged, in the
+// caller's workspace) is reset by the last slice.
+template <int MODE, int MB, int NB>
+__device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot)[NB][MB], int t,
+                                            int slice, int m0, int n_wg, int n_w, int l16, int lg,
+                                            int* s_last_ptr) {
+  constexpr int ROWS = 16 * MB;
+  constexpr int WROWS = 64 * NB;
+  const int M = a.M, N = a.N;
+  int& s_last = *s_last_ptr;
+  const bool vec = (N & 3) == 0;
+  if (a.S == 1) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = m0 + mb * 16 + l16;
+        const int n = n_w + nb * 16 + lg * 4;
+        if (m < M && n < N) {
+          const float xsc = MODE == kW4A4 ? a.Xs[m] : 1.0f;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = MODE == kW4A4 ? xsc * tot[nb][mb][r] : tot[nb][mb][r];
+          float* dst = a.Y + (int64_t)m * N + n;
+          if (vec) {
+            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) dst[r] = v[r];
+          }
+        }
+      }
+    return;
+  }
+
+  float* o = a.part + (int64_t)slice * M * N;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + mb * 16 + l16;
+      const int n = n_w + nb * 16 + lg * 4;
+      if (m < M) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N)
+            __hip_atomic_store(o + (int64_t)m * N + n + r, tot[nb][mb][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long* slot = a.cnt + t;
+    unsigned long long cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    unsigned int count = 0;
+    for (;;) {
+      const unsigned long long nxt = ((unsigned int)(cur >> 32) == a.epoch)
+                                         ? cur + 1ull
+                                         : (((unsigned long long)a.epoch << 32) | 1ull);
+      if (__hip_atomic_compare_exchange_strong(slot, &cur, nxt, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
+        count = (unsigned int)(nxt & 0xffffffffull);
+        break;
+      }
+    }
+    s_last = count == (unsigned int)a.S;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // all partials of an element are requested before any is added (in slice
+  // order), 8 slices per batch
+  const int64_t MN = (int64_t)M * N;
+  constexpr int EPT = ROWS * WROWS / 256;
+  float acc[EPT];
+  const float* src[EPT];
+  bool ok[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = threadIdx.x + 256 * e;
+    const int m = m0 + i / WROWS, n = n_wg + i % WROWS;
+    ok[e] = m < M && n < N;
+    src[e] = a.part + (int64_t)min(m, M - 1) * N + min(n, N - 1);
+    acc[e] = 0.f;
+  }
+  for (int s0 = 0; s0 < a.S; s0 += 8) {
+    float v[EPT][8];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[e][k] = __hip_atomic_load(src[e] + (int64_t)min(s0 + k, a.S - 1) * MN, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < a.S) acc[e] = (s0 + k == 0) ? v[e][k] : acc[e] + v[e][k];
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = threadIdx.x + 256 * e;
+    const int m = m0 + i / WROWS, n = n_wg + i % WROWS;
+    if (ok[e]) a.Y[(int64_t)m * N + n] = MODE == kW4A4 ? a.Xs[m] * acc[e] : acc[e];
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.cnt + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // Straight-line main loop: every global load is issued unconditionally (from
 // a clamped, valid address) so the compiler keeps exact load counters and the
 // weight ring stays in flight across waits; only the arithmetic of groups past
 // the end of the slice is skipped (a branch uniform over the workgroup).
-template <int MODE, int MB, int CH, int PD, bool WITHP>
+template <int MODE, int MB, int NB, int CH, int PD, bool WITHP>
 __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
   static_assert(PD % CH == 0, "prefetch depth must be a multiple of the chunk");
-  constexpr int ROWS = 16 * MB;
+  constexpr int ROWS = 16 * MB;      // activation rows of an m-chunk
+  constexpr int WROWS = 64 * NB;     // weight rows of a tile (4 wavefronts x NB blocks of 16)
   constexpr int XSTB = (MODE == kW4A16 ? CH * 256 : CH * 128) + 16;  // LDS row bytes
   constexpr int XCH = MODE == kW4A16 ? ROWS * CH * 16 : ROWS * CH * 4;  // 16-B chunks
   constexpr int XPT = (XCH + 255) / 256;
-  constexpr int SPT = (CH * 64 + 255) / 256;
+  constexpr int SPT = (CH * WROWS + 255) / 256;
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][ROWS * XSTB];
-  __shared__ float xsum[2][MODE == kW4A16 ? ROWS * CH : 1];
-  __shared__ uint16_t wsl[2][CH * 64];
+  __shared__ uint16_t wsl[2][CH * WROWS];
   __shared__ int s_last;
 
   const int b = blockIdx.x;
@@ -165,16 +276,20 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
   const int nblk = (ng + PD - 1) / PD;  // PD-group blocks, the last may be partial
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int n_wg = ntile * 64, n_w = n_wg + wave * 16;
+  const int n_wg = ntile * WROWS, n_w = n_wg + wave * 16 * NB;
   const int m0 = mchunk * ROWS;
   const int M = a.M, N = a.N, K = a.K;
 
-  // tiled weights: the wave's 16 rows x one group = one contiguous 1 KiB tile,
-  // lane l's 16 bytes = row l%16, codes 32*(l/16) .. +32 of the group
+  // tiled weights: 16 rows x one group = one contiguous 1 KiB tile; lane l's
+  // 16 bytes = row l%16, codes 32*(l/16) .. +32 of the group
   const int nrb = (N + 15) / 16;
-  const uint8_t* wrow =
-      a.Wq + ((int64_t)min(n_w / 16, nrb - 1) * G + g_begin) * 1024 + lane * 16;
-  auto wload = [&](int gi) { return ld_stream(wrow + (int64_t)min(gi, ng - 1) * 1024); };
+  const uint8_t* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    wrow[nb] = a.Wq + ((int64_t)min(n_w / 16 + nb, nrb - 1) * G + g_begin) * 1024 + lane * 16;
+  auto wload = [&](int nb, int gi) {
+    return ld_stream(wrow[nb] + (int64_t)min(gi, ng - 1) * 1024);
+  };
 
   uint4 xr[XPT];
   uint16_t sr[SPT];
@@ -202,9 +317,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
-      const int idx = min((int)threadIdx.x + 256 * i, CH * 64 - 1);
-      const int gl = idx / 64, rr = idx % 64;
-      sr[i] = a.Ws[(int64_t)min(n_wg + rr, N - 1) * G + min(gc + gl, G - 1)];
+      const int idx = min((int)threadIdx.x + 256 * i, CH * WROWS - 1);
+      const int gl = idx / WROWS, rr = idx % WROWS;
+      const int rb = min((n_wg + rr) >> 4, nrb - 1);
+      sr[i] = a.Ws[((int64_t)rb * G + min(gc + gl, G - 1)) * 16 + (rr & 15)];
     }
   };
   auto x_store = [&](int buf) {
@@ -217,8 +333,6 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
         uint32_t p[4];
         bf16x8_interleave(v, p);
         *reinterpret_cast<uint4*>(&xs[buf][r * XSTB + cc * 16]) = make_uint4(p[0], p[1], p[2], p[3]);
-        const float s = row16_sum(bf16x8_sum(v));  // 16 chunks of a group = one DPP row
-        if ((cc & 15) == 0) xsum[buf][r * CH + (cc >> 4)] = s;
       } else if (idx < XCH) {
         const int r = idx / (CH * 4), cc = idx % (CH * 4);
         const uint4 p = xr[i];
@@ -232,19 +346,25 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int idx = threadIdx.x + 256 * i;
-      if (idx < CH * 64) wsl[buf][idx] = sr[i];
+      if (idx < CH * WROWS) wsl[buf][idx] = sr[i];
     }
   };
 
-  v4f tot[MB];
+  v4f tot[NB][MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) tot[mb] = v4f{0.f, 0.f, 0.f, 0.f};
-  uint4 wr[PD];
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) tot[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 wr[PD][NB];
 
   x_load(0);
   x_store(0);
 #pragma unroll
-  for (int s = 0; s < PD; ++s) wr[s] = wload(s);
+  for (int s = 0; s < PD; ++s) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) wr[s][nb] = wload(nb, s);
+    __builtin_amdgcn_sched_barrier(0);  // slot order, as in the steady state
+  }
   __syncthreads();
   x_load(1);
 
@@ -255,70 +375,100 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
       const int gl = s % CH;  // compile-time after unrolling
       const int c = gi / CH;
       const int buf = c & 1;
-      const uint4 w = wr[s];
-      const uint16_t* wp = &wsl[buf][gl * 64 + wave * 16 + lg * 4];
       if (gi >= ng) {
         // past the end of the slice: nothing to add
       } else if (MODE == kW4A16) {
-        v4f acc[MB];
+        // acc = sum x (136 + q) per row and the bias term -136 sum x per m
+        // (one more MFMA chain with a constant A operand), both in fp32
+        v4f acc[NB][MB], corr[MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int mb = 0; mb < MB; ++mb) {
+          corr[mb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        const v8bf cneg = as_v8bf(kNegBiasPair, kNegBiasPair, kNegBiasPair, kNegBiasPair);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t wd = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
-          uint32_t a4[4];
-          w4_to_bf16_biased(wd, a4);
-          const v8bf av = as_v8bf(a4[0], a4[1], a4[2], a4[3]);
+          v8bf bv[MB];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const v8bf bv = *reinterpret_cast<const v8bf*>(
+          for (int mb = 0; mb < MB; ++mb)
+            bv[mb] = *reinterpret_cast<const v8bf*>(
                 &xs[buf][(mb * 16 + l16) * XSTB + gl * 256 + lg * 64 + j * 16]);
-            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mb], 0, 0, 0);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const uint4 w = wr[s][nb];
+            const uint32_t wd = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
+            uint32_t a4[4];
+            w4_to_bf16_biased(wd, a4);
+            const v8bf av = as_v8bf(a4[0], a4[1], a4[2], a4[3]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[mb], acc[nb][mb], 0, 0, 0);
           }
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            corr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cneg, bv[mb], corr[mb], 0, 0, 0);
         }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const float xsm = xsum[buf][(mb * 16 + l16) * CH + gl];
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint16_t* wp = &wsl[buf][gl * WROWS + wave * 16 * NB + nb * 16 + lg * 4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            tot[mb][r] = fmaf(half_bits_to_float(wp[r]), fmaf(-kW4Bias, xsm, acc[mb][r]),
-                              tot[mb][r]);
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              tot[nb][mb][r] = fmaf(half_bits_to_float(wp[r]), acc[nb][mb][r] + corr[mb][r],
+                                    tot[nb][mb][r]);
         }
       } else {
-        v4i acc[MB];
+        v4i acc[NB][MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = v4i{0, 0, 0, 0};
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const uint32_t p0 = j == 0 ? w.x : w.z, p1 = j == 0 ? w.y : w.w;
-          const v4i av = as_v4i(w4_lo_x16(p0), w4_hi_x16(p0), w4_lo_x16(p1), w4_hi_x16(p1));
+          v4i bv[MB];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const v4i bv = *reinterpret_cast<const v4i*>(
+          for (int mb = 0; mb < MB; ++mb)
+            bv[mb] = *reinterpret_cast<const v4i*>(
                 &xs[buf][(mb * 16 + l16) * XSTB + gl * 128 + lg * 32 + j * 16]);
-            acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[mb], 0, 0, 0);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const uint4 w = wr[s][nb];
+            const uint32_t p0 = j == 0 ? w.x : w.z, p1 = j == 0 ? w.y : w.w;
+            const v4i av = as_v4i(w4_lo_x16(p0), w4_hi_x16(p0), w4_lo_x16(p1), w4_hi_x16(p1));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              acc[nb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv[mb], acc[nb][mb], 0, 0, 0);
           }
         }
-        float sc[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = half_bits_to_float(wp[r]) * 0.00390625f;  // /256
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint16_t* wp = &wsl[buf][gl * WROWS + wave * 16 * NB + nb * 16 + lg * 4];
+          float sc[4];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+          for (int r = 0; r < 4; ++r) sc[r] = half_bits_to_float(wp[r]) * 0.00390625f;  // /256
 #pragma unroll
-          for (int r = 0; r < 4; ++r) tot[mb][r] = fmaf(sc[r], (float)acc[mb][r], tot[mb][r]);
-          if (WITHP) {
-            const int m = m0 + mb * 16 + l16, n = n_w + lg * 4;
-            if (m < M) {
+          for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (n + r < N) a.P[((int64_t)m * N + n + r) * G + g_begin + gi] = acc[mb][r] >> 8;
+            for (int r = 0; r < 4; ++r)
+              tot[nb][mb][r] = fmaf(sc[r], (float)acc[nb][mb][r], tot[nb][mb][r]);
+            if (WITHP) {
+              const int m = m0 + mb * 16 + l16, n = n_w + nb * 16 + lg * 4;
+              if (m < M) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (n + r < N) a.P[((int64_t)m * N + n + r) * G + g_begin + gi] = acc[nb][mb][r] >> 8;
+              }
             }
           }
         }
       }
       // refill the slot only after its old value is dead, so the new load can
       // land in the same registers (no copies, no drain at the loop edge)
-      wr[s] = wload(gi + PD);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) wr[s][nb] = wload(nb, gi + PD);
       if (gl == CH - 1) {  // end of activation chunk c: publish chunk c+1, fetch c+2
         x_store((c + 1) & 1);
         __syncthreads();
@@ -326,105 +476,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
       }
     }
   }
-
-  const bool vec = (N & 3) == 0;
-  if (a.S == 1) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + mb * 16 + l16;
-      const int n = n_w + lg * 4;
-      if (m < M && n < N) {
-        const float xsc = MODE == kW4A4 ? a.Xs[m] : 1.0f;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = MODE == kW4A4 ? xsc * tot[mb][r] : tot[mb][r];
-        float* dst = a.Y + (int64_t)m * N + n;
-        if (vec) {
-          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = v[r];
-        }
-      }
-    }
-    return;
-  }
-
-  // ---- split-K.  Partials are written and read with agent-coherent atomic
-  // accesses (they bypass the non-coherent caches), the writer waits for its
-  // stores to complete before the arrival count, and the last slice of the
-  // tile to arrive sums the S partials in slice order.
-  float* o = a.part + (int64_t)slice * M * N;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = m0 + mb * 16 + l16;
-    const int n = n_w + lg * 4;
-    if (m < M) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N)
-          __hip_atomic_store(o + (int64_t)m * N + n + r, tot[mb][r], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long* slot = a.cnt + t;
-    unsigned long long cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned int count = 0;
-    for (;;) {
-      const unsigned long long nxt = ((unsigned int)(cur >> 32) == a.epoch)
-                                         ? cur + 1ull
-                                         : (((unsigned long long)a.epoch << 32) | 1ull);
-      if (__hip_atomic_compare_exchange_strong(slot, &cur, nxt, __ATOMIC_RELAXED,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-        count = (unsigned int)(nxt & 0xffffffffull);
-        break;
-      }
-    }
-    s_last = count == (unsigned int)a.S;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // all partials of an element are requested before any is added (in slice
-  // order), 8 slices per batch
-  const int64_t MN = (int64_t)M * N;
-  constexpr int EPT = ROWS * 64 / 256;
-  float acc[EPT];
-  const float* src[EPT];
-  bool ok[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int i = threadIdx.x + 256 * e;
-    const int m = m0 + i / 64, n = n_wg + i % 64;
-    ok[e] = m < M && n < N;
-    src[e] = a.part + (int64_t)min(m, M - 1) * N + min(n, N - 1);
-    acc[e] = 0.f;
-  }
-  for (int s0 = 0; s0 < a.S; s0 += 8) {
-    float v[EPT][8];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e)
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        v[e][k] = __hip_atomic_load(src[e] + (int64_t)min(s0 + k, a.S - 1) * MN, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int e = 0; e < EPT; ++e)
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (s0 + k < a.S) acc[e] = (s0 + k == 0) ? v[e][k] : acc[e] + v[e][k];
-  }
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int i = threadIdx.x + 256 * e;
-    const int m = m0 + i / 64, n = n_wg + i % 64;
-    if (ok[e]) a.Y[(int64_t)m * N + n] = MODE == kW4A4 ? a.Xs[m] * acc[e] : acc[e];
-  }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(a.cnt + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  finish_tile<MODE, MB, NB>(a, tot, t, slice, m0, n_wg, n_w, l16, lg, &s_last);
 }
 
 // ============================================================================
@@ -475,9 +527,8 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
 
   const int nrb = (N + 15) / 16;
   const int rb = min(blockIdx.x * 4 + wave, nrb - 1);
-  const int n = min(rb * 16 + r, N - 1);
   const uint8_t* wrow = Wq + ((int64_t)rb * G + g0) * 1024 + lane * 16;
-  const uint16_t* srow = Ws + (int64_t)n * G + g0;
+  const uint16_t* srow = Ws + ((int64_t)rb * G + g0) * 16 + r;  // tiled scales
   auto wload = [&](int gi) { return ld_stream(wrow + (int64_t)min(gi, ng - 1) * 1024); };
 
   float tot[MM];
@@ -488,7 +539,8 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
 #pragma unroll
   for (int s = 0; s < PD; ++s) {
     wr[s] = wload(s);
-    sr[s] = srow[min(s, ng - 1)];
+    sr[s] = srow[min(s, ng - 1) * 16];
+    __builtin_amdgcn_sched_barrier(0);  // slot order, as in the steady state
   }
   for (int b0 = 0; b0 < ng; b0 += PD) {
 #pragma unroll
@@ -521,7 +573,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
           tot[m] = fmaf(sc, fmaf(-kW4Bias, xsum[m][gi * 4 + c], acc[m]), tot[m]);
       }
       wr[s] = wload(gi + PD);
-      sr[s] = srow[min(gi + PD, ng - 1)];
+      sr[s] = srow[min(gi + PD, ng - 1) * 16];
     }
   }
   // the four lanes of a row (r, r+16, r+32, r+48) hold disjoint 32-chunks
@@ -555,24 +607,28 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
 // Split-K depends on (N, K) only: an output row's operation order is the
 // same for every M within one family.
 struct SkinnyPlan {
-  int S, gps, MB, mchunks, ntiles, T;
+  int S, gps, MB, NB, mchunks, ntiles, T;
   int64_t blocks;
   size_t cnt_bytes, part_bytes;
 };
 
-SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
+SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K) {
   SkinnyPlan p;
   const int64_t G = K / kGroup;
-  p.ntiles = (int)cdiv(N, 64);
+  const int64_t t64 = cdiv(N, 64);  // the split depends on N and K only
   int64_t S = 1;
-  if (p.ntiles < QSPEC_SK_TARGET_WG) {
-    S = cdiv(QSPEC_SK_TARGET_WG, p.ntiles);
+  if (t64 < QSPEC_SK_TARGET_WG) {
+    S = cdiv(QSPEC_SK_TARGET_WG, t64);
     const int64_t smax = std::max<int64_t>(1, G / 4);  // at least 4 groups per slice
     if (S > smax) S = smax;
   }
   p.gps = (int)cdiv(G, S);
   p.S = (int)cdiv(G, p.gps);
   p.MB = (int)(M >= 64 ? 4 : cdiv(M, 16));
+  // two 16-row blocks per wavefront halve the LDS activation reads once the
+  // activation tile spans several m-blocks (the bf16 verifier shapes)
+  p.NB = (mode == 0 && p.MB >= 2) ? QSPEC_SK_NB16 : 1;
+  p.ntiles = (int)cdiv(N, 64 * p.NB);
   p.mchunks = (int)cdiv(M, 16 * p.MB);
   p.T = p.ntiles * p.mchunks;
   p.blocks = 8 * cdiv(p.T, 8) * p.S;
@@ -594,17 +650,17 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
   dim3 grid((unsigned)p.blocks), block(256);
   if (MODE == kW4A16) {
     switch (p.MB) {
-      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, QSPEC_SK_B1, WITHP>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_B2, WITHP>), grid, block, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_B3, WITHP>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_B4, WITHP>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, WITHP>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_NB16, QSPEC_SK_B2, WITHP>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, WITHP>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_NB16, QSPEC_SK_B4, WITHP>), grid, block, 0, s, a); break;
     }
   } else {
     switch (p.MB) {
-      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, QSPEC_SK_A1, WITHP>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A4, 2, QSPEC_SK_A2, WITHP>), grid, block, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A4, 3, QSPEC_SK_A3, WITHP>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<kW4A4, 4, QSPEC_SK_A4, WITHP>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, 1, QSPEC_SK_A1, WITHP>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A4, 2, 1, QSPEC_SK_A2, WITHP>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A4, 3, 1, QSPEC_SK_A3, WITHP>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A4, 4, 1, QSPEC_SK_A4, WITHP>), grid, block, 0, s, a); break;
     }
   }
   return hipGetLastError();
@@ -612,7 +668,9 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
 
 template <int MODE>
 hipError_t launch_skinny(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
-  if (MODE == kW4A4 && a.P != nullptr) return launch_skinny_t<MODE, true>(a, p, s);
+  if constexpr (MODE == kW4A4) {
+    if (a.P != nullptr) return launch_skinny_t<MODE, true>(a, p, s);
+  }
   return launch_skinny_t<MODE, false>(a, p, s);
 }
 
@@ -639,7 +697,7 @@ hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* X
 }  // namespace
 
 size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  const SkinnyPlan p = plan_skinny(M, N, K);
+  const SkinnyPlan p = plan_skinny(0, M, N, K);
   const GemvPlan q = plan_gemv(K);
   const size_t a = p.cnt_bytes + p.part_bytes;
   const size_t b = q.S > 1 ? (size_t)q.S * std::min<int64_t>(M, 4) * N * sizeof(float) : 0;
@@ -674,7 +732,7 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
     return hipSuccess;
   }
   // SKINNY (TILED shares it until the prefill family lands)
-  const SkinnyPlan p = plan_skinny(M, N, K);
+  const SkinnyPlan p = plan_skinny(0, M, N, K);
   SkinnyArgs a{};
   a.X = X;
   a.Wq = Wq;
@@ -688,7 +746,7 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
 }
 
 size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  const SkinnyPlan p = plan_skinny(M, N, K);
+  const SkinnyPlan p = plan_skinny(1, M, N, K);
   return p.cnt_bytes + p.part_bytes;
 }
 
@@ -696,7 +754,7 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
                        void* ws, hipStream_t s) {
   (void)variant;
-  const SkinnyPlan p = plan_skinny(M, N, K);
+  const SkinnyPlan p = plan_skinny(1, M, N, K);
   SkinnyArgs a{};
   a.X = Xq;
   a.Xs = Xs;

@@ -23,7 +23,9 @@ __device__ __forceinline__ int quant_code(float v, float s) {
 // k = 2l, 2l+1 of the group, i.e. byte l of the group's 64 row-major bytes,
 // and writes it to its place in the tiled storage order: 1 KiB tile per
 // (16-row block, group); inside it, 16-byte slot 16*(l/16) + n%16 holds row n's
-// bytes [16*(l/16), +16) of the group.  Padding rows (n >= N) get zero codes.
+// bytes [16*(l/16), +16) of the group.  The scale goes to element n%16 of the
+// (block, group) 32-byte scale tile.  Padding rows (n >= N) get zero codes
+// and zero scales.
 __global__ __launch_bounds__(256) void pack_w4_kernel(const float* __restrict__ W, int64_t N,
                                                       int64_t Np, int64_t K,
                                                       uint8_t* __restrict__ Wq,
@@ -45,7 +47,9 @@ __global__ __launch_bounds__(256) void pack_w4_kernel(const float* __restrict__ 
       q1 = quant_code(w.y, s);
     }
     byte = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
-    if (lane == 0) Ws[n * G + g] = __builtin_bit_cast(uint16_t, sh);
+    if (lane == 0) Ws[((n >> 4) * G + g) * 16 + (n & 15)] = __builtin_bit_cast(uint16_t, sh);
+  } else if (lane == 0) {
+    Ws[((n >> 4) * G + g) * 16 + (n & 15)] = 0;  // padding row
   }
   const int64_t tile = (n >> 4) * G + g;
   const int slot = (lane >> 4) * 16 + (int)(n & 15);

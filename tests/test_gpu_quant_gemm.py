@@ -37,6 +37,11 @@ def dev_w(Wq):
     return dev(oracle.tile_w4(Wq))
 
 
+def dev_s(Ws):
+    """oracle row-major fp16 scale bits -> device buffer in the tiled order"""
+    return dev_f16(oracle.tile_scales(Ws))
+
+
 def _case(seed, M, N, K, outliers=None):
     rng = synth.make_rng(seed)
     W = synth.weights(rng, N, K)
@@ -55,7 +60,7 @@ def test_pack_w4_bitexact(N, K):
     Wq_ref, Ws_ref = oracle.pack_w4(W)
     Wq, Ws = q.pack_w4(dev(W))
     assert np.array_equal(host(Wq), oracle.tile_w4(Wq_ref))
-    assert np.array_equal(host_bits16(Ws), Ws_ref)
+    assert np.array_equal(host_bits16(Ws), oracle.tile_scales(Ws_ref))
 
 
 def test_pack_w4_hand_and_subnormal(golden):
@@ -70,7 +75,7 @@ def test_pack_w4_hand_and_subnormal(golden):
     Wq_ref, Ws_ref = oracle.pack_w4(W)
     Wq, Ws = q.pack_w4(dev(W))
     assert np.array_equal(host(Wq), oracle.tile_w4(Wq_ref))
-    assert np.array_equal(host_bits16(Ws), Ws_ref)
+    assert np.array_equal(host_bits16(Ws), oracle.tile_scales(Ws_ref))
     assert Ws_ref[0].tolist() == [grp["scale_bits"] for grp in g["groups"]]
 
 
@@ -122,17 +127,19 @@ def test_w4a4_parity(M, N, K, variant):
     W, X = _case(12, M, N, K)
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
-    Y, P = q.gemm_w4a4(dev(Xq), dev(Xs), dev_w(Wq), dev_f16(Ws), variant=variant, partials=True)
+    Y, P = q.gemm_w4a4(dev(Xq), dev(Xs), dev_w(Wq), dev_s(Ws), variant=variant, partials=True, N=N)
     assert np.array_equal(host(P), oracle.w4a4_partials(Xq, Wq))
     assert_close(host(Y), oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4")
 
 
 def test_w4a4_gpu_quantized_chain():
     """quant_act on the GPU feeding the GEMM equals the oracle chain."""
-    W, X = _case(13, 8, 1024, 1024, outliers=4)
+    N = 1024
+    W, X = _case(13, 8, N, 1024, outliers=4)
     Wq, Ws = oracle.pack_w4(W)
-    Xq_d, Xs_d = q.quant_act(dev_bf16(X))
-    Y = q.gemm_w4a4(Xq_d, Xs_d, dev_w(Wq), dev_f16(Ws))
+    X_d, Wq_d, Ws_d = dev_bf16(X), dev_w(Wq), dev_s(Ws)   # kept alive across the launches
+    Xq_d, Xs_d = q.quant_act(X_d)
+    Y = q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d, N=N)
     Xq, Xs = oracle.quant_act(X)
     assert_close(host(Y), oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4 chain")
 
@@ -144,7 +151,7 @@ def test_w4a16_parity(M, N, K, variant):
     say(f"w4a16 M={M} N={N} K={K} variant={variant}")
     W, X = _case(14, M, N, K)
     Wq, Ws = oracle.pack_w4(W)
-    Y = q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_f16(Ws), variant=variant)
+    Y = q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_s(Ws), variant=variant, N=N)
     assert_close(host(Y), oracle.gemm_w4a16(X, Wq, Ws), what="w4a16")
 
 
@@ -161,10 +168,10 @@ def test_w4a16_zero_and_lossless_rows():
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
     for v in W4A16_VARIANTS:
-        Y16 = host(q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_f16(Ws), variant=v))
+        Y16 = host(q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_s(Ws), variant=v, N=N))
         assert np.all(Y16[1] == 0)
         assert_close(Y16, oracle.gemm_w4a16(X, Wq, Ws))
-    Y4 = host(q.gemm_w4a4(dev(Xq), dev(Xs), dev_w(Wq), dev_f16(Ws)))
+    Y4 = host(q.gemm_w4a4(dev(Xq), dev(Xs), dev_w(Wq), dev_s(Ws), N=N))
     assert np.all(Y4[1] == 0)
     assert_close(Y4, oracle.gemm_w4a16(X, Wq, Ws))
 
@@ -176,12 +183,12 @@ def test_w4a16_row_invariance(variant):
     N, K = 2048, 2048
     W, X = _case(16, 80, N, K)
     Wq, Ws = oracle.pack_w4(W)
-    Wq_d, Ws_d, X_d = dev_w(Wq), dev_f16(Ws), dev_bf16(X)
-    Y80 = host(q.gemm_w4a16(X_d, Wq_d, Ws_d, variant=variant))
-    Y16 = host(q.gemm_w4a16(X_d[:16].contiguous(), Wq_d, Ws_d, variant=variant))
+    Wq_d, Ws_d, X_d = dev_w(Wq), dev_s(Ws), dev_bf16(X)
+    Y80 = host(q.gemm_w4a16(X_d, Wq_d, Ws_d, variant=variant, N=N))
+    Y16 = host(q.gemm_w4a16(X_d[:16].contiguous(), Wq_d, Ws_d, variant=variant, N=N))
     assert np.array_equal(Y80[:16].view(np.uint32), Y16.view(np.uint32))
     for r in (0, 37, 79):
-        Y1 = host(q.gemm_w4a16(X_d[r:r + 1].contiguous(), Wq_d, Ws_d, variant=variant))
+        Y1 = host(q.gemm_w4a16(X_d[r:r + 1].contiguous(), Wq_d, Ws_d, variant=variant, N=N))
         assert np.array_equal(Y80[r:r + 1].view(np.uint32), Y1.view(np.uint32)), r
 
 
@@ -190,24 +197,25 @@ def test_w4a4_row_invariance():
     W, X = _case(17, 80, N, K)
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
-    args = (dev_w(Wq), dev_f16(Ws))
-    Y80 = host(q.gemm_w4a4(dev(Xq), dev(Xs), *args, variant=q.GEMM_SKINNY))
+    args = (dev_w(Wq), dev_s(Ws))
+    Y80 = host(q.gemm_w4a4(dev(Xq), dev(Xs), *args, variant=q.GEMM_SKINNY, N=N))
     for r in (0, 41):
-        Y1 = host(q.gemm_w4a4(dev(Xq[r:r + 1]), dev(Xs[r:r + 1]), *args, variant=q.GEMM_SKINNY))
+        Y1 = host(q.gemm_w4a4(dev(Xq[r:r + 1]), dev(Xs[r:r + 1]), *args, variant=q.GEMM_SKINNY, N=N))
         assert np.array_equal(Y80[r:r + 1].view(np.uint32), Y1.view(np.uint32))
 
 
 def test_determinism():
-    W, X = _case(18, 40, 4608, 3584)
+    N = 4608
+    W, X = _case(18, 40, N, 3584)
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
-    a16 = (dev_bf16(X), dev_w(Wq), dev_f16(Ws))
-    a4 = (dev(Xq), dev(Xs), dev_w(Wq), dev_f16(Ws))
-    y1 = host(q.gemm_w4a16(*a16))
-    y2 = host(q.gemm_w4a16(*a16))
+    a16 = (dev_bf16(X), dev_w(Wq), dev_s(Ws))
+    a4 = (dev(Xq), dev(Xs), dev_w(Wq), dev_s(Ws))
+    y1 = host(q.gemm_w4a16(*a16, N=N))
+    y2 = host(q.gemm_w4a16(*a16, N=N))
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
-    z1 = host(q.gemm_w4a4(*a4))
-    z2 = host(q.gemm_w4a4(*a4))
+    z1 = host(q.gemm_w4a4(*a4, N=N))
+    z2 = host(q.gemm_w4a4(*a4, N=N))
     assert np.array_equal(z1.view(np.uint32), z2.view(np.uint32))
 
 
@@ -233,16 +241,17 @@ def test_qwen7b_decode_shapes(proj):
     Wq, Ws = oracle.pack_w4(W[cols])          # oracle packs the sampled rows only
     Wq_d, Ws_d = q.pack_w4(dev(W))            # the device packs everything
     assert np.array_equal(oracle.untile_w4(host(Wq_d), N)[cols], Wq)
+    assert np.array_equal(oracle.untile_scales(host_bits16(Ws_d), N)[cols], Ws)
     for M in (1, 8, 32):
         say(f"{proj} w4a4 M={M}")
         Xq_d, Xs_d = q.quant_act(dev_bf16(X[:M].copy()))
-        Y = host(q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d))
+        Y = host(q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d, N=N))
         Xq, Xs = oracle.quant_act(X[:M])
         assert np.array_equal(host(Xq_d), Xq)
         assert_close(Y[:, cols], oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what=f"w4a4 M={M}")
     for M in (5, 40):
         say(f"{proj} w4a16 M={M}")
-        Y = host(q.gemm_w4a16(dev_bf16(X[:M].copy()), Wq_d, Ws_d))
+        Y = host(q.gemm_w4a16(dev_bf16(X[:M].copy()), Wq_d, Ws_d, N=N))
         assert_close(Y[:, cols], oracle.gemm_w4a16(X[:M], Wq, Ws), what=f"w4a16 M={M}")
 
 
@@ -258,11 +267,11 @@ def test_qwen7b_prefill_shapes(proj):
     Wq, Ws = oracle.pack_w4(W[cols])
     Wq_d, Ws_d = q.pack_w4(dev(W))
     say(f"{proj} prefill w4a16")
-    Y = host(q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d))
+    Y = host(q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, N=N))
     assert_close(Y[np.ix_(rows, cols)], oracle.gemm_w4a16(X[rows], Wq, Ws))
     say(f"{proj} prefill w4a4")
     Xq_d, Xs_d = q.quant_act(dev_bf16(X))
-    Y4 = host(q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d))
+    Y4 = host(q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d, N=N))
     Xq, Xs = oracle.quant_act(X[rows])
     assert_close(Y4[np.ix_(rows, cols)], oracle.gemm_w4a4(Xq, Xs, Wq, Ws))
 
@@ -278,7 +287,7 @@ def test_llama8b_lm_head_gemv():
     del W
     for v in W4A16_VARIANTS:
         say(f"lm_head variant={v}")
-        Y = host(q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=v))
+        Y = host(q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=v, N=N))
         assert_close(Y[:, cols], oracle.gemm_w4a16(X, Wq, Ws))
 
 
@@ -290,7 +299,7 @@ def test_graph_replays_match_eager():
     M4, M16, N, K = 8, 40, 3584, 18944          # a split-K shape in both modes
     W, X = _case(19, M16, N, K)
     Wq, Ws = oracle.pack_w4(W)
-    Wq_d, Ws_d, X_d = dev_w(Wq), dev_f16(Ws), dev_bf16(X)
+    Wq_d, Ws_d, X_d = dev_w(Wq), dev_s(Ws), dev_bf16(X)
     X4 = X_d[:M4].contiguous()
     Xq, Xs = q.quant_act(X4)
     Y4 = torch.empty((M4, N), dtype=torch.float32, device="cuda")
@@ -300,8 +309,8 @@ def test_graph_replays_match_eager():
 
     def body():
         q.quant_act(X4, Xq, Xs)
-        q.gemm_w4a4(Xq, Xs, Wq_d, Ws_d, Y=Y4, ws=ws4)
-        q.gemm_w4a16(X_d, Wq_d, Ws_d, Y=Y16, ws=ws16)
+        q.gemm_w4a4(Xq, Xs, Wq_d, Ws_d, Y=Y4, ws=ws4, N=N)
+        q.gemm_w4a16(X_d, Wq_d, Ws_d, Y=Y16, ws=ws16, N=N)
 
     body()
     torch.cuda.synchronize()
@@ -332,5 +341,5 @@ def test_fresh_garbage_workspace():
     Wq, Ws = oracle.pack_w4(W)
     nb = q.workspace_bytes(2, M, N, K)
     ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda")
-    Y = q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_f16(Ws), variant=q.GEMM_SKINNY, ws=ws)
+    Y = q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_s(Ws), variant=q.GEMM_SKINNY, ws=ws, N=N)
     assert_close(host(Y), oracle.gemm_w4a16(X, Wq, Ws))

@@ -358,3 +358,18 @@ def test_tile_hand_positions():
     pos2 = ((0 * G + 0) * 64 + (16 * 0 + 3)) * 16 + 0
     assert flat[pos1] == 0xAB and flat[pos2] == 0x11
     assert np.count_nonzero(flat) == 2
+
+
+def test_tile_scales_permutation_and_positions():
+    rng = np.random.default_rng(4)
+    for N, G in ((1, 1), (16, 3), (37, 5)):
+        Ws = rng.integers(1, 60000, size=(N, G), dtype=np.uint16)
+        T = oracle.tile_scales(Ws)
+        Np = -(-N // 16) * 16
+        assert T.shape == (Np, G)
+        assert np.array_equal(oracle.untile_scales(T, N), Ws)
+        assert np.count_nonzero(T) == N * G
+    Ws = np.zeros((32, 2), np.uint16)
+    Ws[19, 1] = 7                      # block 1, r 3, group 1
+    flat = oracle.tile_scales(Ws).ravel()
+    assert flat[(1 * 2 + 1) * 16 + 3] == 7
