@@ -193,6 +193,66 @@ class Decode:
                            f"(all K, all M) plus the full verify step; {dt:.1f} s")
 
 
+def measure_prefill(torch, q, wl, reps=5):
+    """Prefill-shaped GEMMs (M = 2048 tokens) on the same packed buffers:
+    W4A4 (int8 MFMA) vs W4A16 (bf16 MFMA), per projection; kernel time from
+    HIP events around graph replays of 3 launches each."""
+    import synth
+    rng = synth.make_rng(2, 0)
+    M = 2048
+    out = {}
+    tot4 = tot16 = ops_all = 0.0
+    for p in wl.proj:
+        N, K = p["N"], p["K"]
+        X = synth.activations(rng, M, K)
+        Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        Xq, Xs = q.quant_act(Xd)
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        Wq, Ws = p["copies"][0]
+        t4 = _graph_time(torch, lambda: q.gemm_w4a4(Xq, Xs, Wq, Ws, Y=Y), reps)
+        t16 = _graph_time(torch, lambda: q.gemm_w4a16(Xd, Wq, Ws, Y=Y), reps)
+        tq = _graph_time(torch, lambda: q.quant_act(Xd, Xq, Xs), reps)
+        ops = 2.0 * M * N * K
+        out[p["name"]] = {"w4a4_us": round(t4, 2), "w4a4_tops": round(ops / t4 / 1e6, 1),
+                          "w4a4_frac_int8": round(ops / t4 / 1e6 / INT8_PEAK_TOPS, 4),
+                          "w4a16_us": round(t16, 2), "w4a16_tflops": round(ops / t16 / 1e6, 1),
+                          "w4a16_frac_bf16": round(ops / t16 / 1e6 / BF16_PEAK_TFLOPS, 4),
+                          "quant_act_us": round(tq, 2), "w4a16_over_w4a4": round(t16 / t4, 3)}
+        tot4 += t4
+        tot16 += t16
+        ops_all += ops
+        del Xd, Xq, Xs, Y
+    out["all"] = {"w4a4_tops": round(ops_all / tot4 / 1e6, 1),
+                  "w4a4_frac_int8": round(ops_all / tot4 / 1e6 / INT8_PEAK_TOPS, 4),
+                  "w4a16_tflops": round(ops_all / tot16 / 1e6, 1),
+                  "w4a16_frac_bf16": round(ops_all / tot16 / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
+def _graph_time(torch, fn, reps, launches=3):
+    """mean microseconds of fn() over graph replays (launches per replay)"""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * launches)
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -294,6 +354,9 @@ def run(args):
                      "us_per_launch": round(us_dom, 3), "bytes_per_launch": box["bytes"]},
         "wall_s_timed": round(wall, 4),
     }
+    if not args.no_prefill:
+        log("prefill-shaped GEMMs")
+        line["prefill_m2048"] = measure_prefill(torch, q, wl)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         line["cpu_baseline"] = wl.cpu_baseline()
@@ -307,6 +370,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

@@ -480,6 +480,405 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
 }
 
 // ============================================================================
+// MFMA "tiled" family (both modes): the prefill shapes, compute-bound.
+//   * a workgroup = 2 x 2 wavefronts = a 128 (n) x 128 (m) output tile; each
+//     wavefront owns 64 x 64 = 4 weight blocks x 4 activation blocks of 16;
+//   * weight tiles (flat 1 KiB per 16 rows x group) and their scales go from
+//     global memory straight into registers (a 2-group ring); each is read by
+//     the two wavefronts sharing its rows, the second read an L2 hit;
+//   * activations are staged through LDS, CH groups at a time, double-
+//     buffered: packed int4 for W4A4 (unpacked per wavefront), pair-
+//     interleaved bf16 for W4A16;
+//   * block order: n-tiles are dealt round-robin to the 8 XCDs and each XCD
+//     walks all m-tiles of an n-tile in a row, so a weight tile is fetched
+//     from HBM about once per XCD and then served by that XCD's L2;
+//   * the per-group arithmetic (MFMA chains, bias chain, fp32 scale
+//     epilogue) is the skinny family's, operation for operation.
+// ============================================================================
+struct TiledArgs {
+  const void* X;
+  const float* Xs;
+  const uint8_t* Wq;
+  const uint16_t* Ws;
+  float* Y;
+  int M, N, K, ntn, ntm;
+};
+
+template <int MODE, int CH>
+__global__ __launch_bounds__(256, MODE == kW4A16 ? 1 : 2) void tiled_kernel(const TiledArgs a) {
+  constexpr int BM = 128;  // activation rows per workgroup
+  constexpr int XSTB = (MODE == kW4A16 ? CH * 256 : CH * 64) + 16;  // LDS row bytes
+  constexpr int XCH = MODE == kW4A16 ? BM * CH * 16 : BM * CH * 4;   // 16-byte chunks
+  constexpr int XPT = XCH / 256;
+  constexpr int PD = 2;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * XSTB];
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, loc = b >> 3;
+  const int nt = 8 * (loc / a.ntm) + xcd, mt = loc % a.ntm;
+  if (nt >= a.ntn) return;  // padding block (uniform)
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K / kGroup;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int n_w = nt * 128 + wn * 64;
+  const int m0 = mt * BM, mw = wm * 64;  // mw: offset of the wave's rows in the tile
+  const int nrb = (N + 15) / 16;
+
+  const uint8_t* wrow[4];
+  const uint16_t* srow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rb = min(n_w / 16 + i, nrb - 1);
+    wrow[i] = a.Wq + (int64_t)rb * G * 1024 + lane * 16;
+    srow[i] = a.Ws + (int64_t)rb * G * 16 + lg * 4;
+  }
+  uint4 wr[PD][4];
+  uint2 sr[PD][4];
+  auto wload = [&](int s, int g) {
+    const int gg = min(g, G - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wr[s][i] = ld_stream(wrow[i] + (int64_t)gg * 1024);
+      sr[s][i] = *reinterpret_cast<const uint2*>(srow[i] + (int64_t)gg * 16);
+    }
+  };
+
+  uint4 xr[XPT];
+  auto x_load = [&](int c) {
+    const int gc = c * CH;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      if (MODE == kW4A16) {
+        const int r = idx / (CH * 16), cc = idx % (CH * 16);
+        xr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.X) +
+                                                (int64_t)min(m0 + r, M - 1) * K +
+                                                (int64_t)min(gc + (cc >> 4), G - 1) * kGroup +
+                                                (cc & 15) * 8);
+      } else {
+        const int r = idx / (CH * 4), cc = idx % (CH * 4);
+        xr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.X) +
+                                                (int64_t)min(m0 + r, M - 1) * (K / 2) +
+                                                (int64_t)min(gc + (cc >> 2), G - 1) * 64 +
+                                                (cc & 3) * 16);
+      }
+    }
+  };
+  auto x_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      if (MODE == kW4A16) {
+        const int r = idx / (CH * 16), cc = idx % (CH * 16);
+        const uint32_t v[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+        uint32_t p[4];
+        bf16x8_interleave(v, p);
+        *reinterpret_cast<uint4*>(&xs[buf][r * XSTB + cc * 16]) = make_uint4(p[0], p[1], p[2], p[3]);
+      } else {
+        const int r = idx / (CH * 4), cc = idx % (CH * 4);
+        *reinterpret_cast<uint4*>(&xs[buf][r * XSTB + cc * 16]) = xr[i];
+      }
+    }
+  };
+
+  v4f tot[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  x_load(0);
+  x_store(0);
+#pragma unroll
+  for (int s = 0; s < PD; ++s) {
+    wload(s, s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  x_load(1);
+  const int nchunks = (G + CH - 1) / CH;
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+#pragma unroll
+    for (int gl = 0; gl < CH; ++gl) {
+      const int g = c * CH + gl;
+      const int s = g % PD;
+      if (g < G) {  // uniform
+        uint4 w[4];
+        uint2 sw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w[i] = s == 0 ? wr[0][i] : wr[1][i];
+          sw[i] = s == 0 ? sr[0][i] : sr[1][i];
+        }
+        if (MODE == kW4A4) {
+          v4i bf[4][2];
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            const uint4 p = *reinterpret_cast<const uint4*>(
+                &xs[buf][(mw + mb * 16 + l16) * XSTB + gl * 64 + lg * 16]);
+            bf[mb][0] = as_v4i(w4_lo_x16(p.x), w4_hi_x16(p.x), w4_lo_x16(p.y), w4_hi_x16(p.y));
+            bf[mb][1] = as_v4i(w4_lo_x16(p.z), w4_hi_x16(p.z), w4_lo_x16(p.w), w4_hi_x16(p.w));
+          }
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const v4i a0 = as_v4i(w4_lo_x16(w[nb].x), w4_hi_x16(w[nb].x), w4_lo_x16(w[nb].y),
+                                  w4_hi_x16(w[nb].y));
+            const v4i a1 = as_v4i(w4_lo_x16(w[nb].z), w4_hi_x16(w[nb].z), w4_lo_x16(w[nb].w),
+                                  w4_hi_x16(w[nb].w));
+            const uint32_t sp[2] = {sw[nb].x, sw[nb].y};
+            float sc[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              sc[r] = half_bits_to_float((uint16_t)(sp[r >> 1] >> (16 * (r & 1)))) * 0.00390625f;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+              v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bf[mb][0], v4i{0, 0, 0, 0}, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bf[mb][1], acc, 0, 0, 0);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) tot[nb][mb][r] = fmaf(sc[r], (float)acc[r], tot[nb][mb][r]);
+            }
+          }
+        } else {
+          v4f acc[4][4], corr[4];
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            corr[mb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) acc[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+          }
+          const v8bf cneg = as_v8bf(kNegBiasPair, kNegBiasPair, kNegBiasPair, kNegBiasPair);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v8bf bv[4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+              bv[mb] = *reinterpret_cast<const v8bf*>(
+                  &xs[buf][(mw + mb * 16 + l16) * XSTB + gl * 256 + lg * 64 + j * 16]);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const uint32_t wd = j == 0 ? w[nb].x : j == 1 ? w[nb].y : j == 2 ? w[nb].z : w[nb].w;
+              uint32_t a4[4];
+              w4_to_bf16_biased(wd, a4);
+              const v8bf av = as_v8bf(a4[0], a4[1], a4[2], a4[3]);
+#pragma unroll
+              for (int mb = 0; mb < 4; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[mb], acc[nb][mb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+              corr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cneg, bv[mb], corr[mb], 0, 0, 0);
+          }
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const uint32_t sp[2] = {sw[nb].x, sw[nb].y};
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                tot[nb][mb][r] = fmaf(half_bits_to_float((uint16_t)(sp[r >> 1] >> (16 * (r & 1)))),
+                                      acc[nb][mb][r] + corr[mb][r], tot[nb][mb][r]);
+          }
+        }
+      }
+      // refill the ring slot of group g with group g + PD
+      if (s == 0) {
+        const int gg = min(g + PD, G - 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wr[0][i] = ld_stream(wrow[i] + (int64_t)gg * 1024);
+          sr[0][i] = *reinterpret_cast<const uint2*>(srow[i] + (int64_t)gg * 16);
+        }
+      } else {
+        const int gg = min(g + PD, G - 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wr[1][i] = ld_stream(wrow[i] + (int64_t)gg * 1024);
+          sr[1][i] = *reinterpret_cast<const uint2*>(srow[i] + (int64_t)gg * 16);
+        }
+      }
+    }
+    x_store((c + 1) & 1);
+    __syncthreads();
+    x_load(c + 2);
+  }
+
+  const bool vec = (N & 3) == 0;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + mw + mb * 16 + l16;
+      const int n = n_w + nb * 16 + lg * 4;
+      if (m < M && n < N) {
+        const float xsc = MODE == kW4A4 ? a.Xs[m] : 1.0f;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = MODE == kW4A4 ? xsc * tot[nb][mb][r] : tot[nb][mb][r];
+        float* dst = a.Y + (int64_t)m * N + n;
+        if (vec) {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = v[r];
+        }
+      }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// W4A4 prefill kernel: 8 wavefronts (4 along n x 2 along m) = a 256 (n) x
+// 128 (m) tile, 64 x 64 per wavefront.  Both operands are staged per group in
+// LDS already widened to int8 (16 q, the MFMA slot order), so each code is
+// unpacked once per workgroup; the group's scales sit in LDS as fp32 / 256.
+// Rows are padded to 144 bytes: the 16 rows a ds_read_b128 touches cover all
+// 64 banks once.  The next group's global loads are issued before the current
+// group's MFMAs and land in the other LDS buffer after them.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(512, 1) void w4a4_prefill_kernel(const TiledArgs a) {
+  constexpr int BN = 256, BM = 128, RST = 144;
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][BN * RST];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BM * RST];
+  __shared__ __attribute__((aligned(16))) float Ss[2][BN];
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, loc = b >> 3;
+  const int nt = 8 * (loc / a.ntm) + xcd, mt = loc % a.ntm;
+  if (nt >= a.ntn) return;  // padding block (uniform)
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K / kGroup;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wn = wave & 3, wm = wave >> 2;
+  const int nrb = (N + 15) / 16;
+  const int rb0 = nt * (BN / 16);
+  const int m0 = mt * BM;
+
+  // staging assignment: A = 1024 16-byte chunks (2 per thread), B = 512 (1
+  // per thread), scales = 256 (threads 0..255)
+  const uint8_t* asrc[2];
+  int adst[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 512 * i;
+    const int rbl = c >> 6, slot = c & 63;
+    asrc[i] = a.Wq + (int64_t)min(rb0 + rbl, nrb - 1) * G * 1024 + slot * 16;
+    adst[i] = (rbl * 16 + (slot & 15)) * RST + (slot >> 4) * 32;
+  }
+  const uint8_t* bsrc = static_cast<const uint8_t*>(a.X) +
+                        (int64_t)min(m0 + (tid >> 2), M - 1) * (K / 2) + (tid & 3) * 16;
+  const int bdst = (tid >> 2) * RST + (tid & 3) * 32;
+  const uint16_t* ssrc =
+      a.Ws + (int64_t)min(rb0 + ((tid & 255) >> 4), nrb - 1) * G * 16 + (tid & 15);
+
+  uint4 ra[2], rbv;
+  uint16_t rs;
+  auto gload = [&](int g) {
+    const int gg = min(g, G - 1);
+    ra[0] = ld_stream(asrc[0] + (int64_t)gg * 1024);
+    ra[1] = ld_stream(asrc[1] + (int64_t)gg * 1024);
+    rbv = *reinterpret_cast<const uint4*>(bsrc + (int64_t)gg * 64);
+    rs = ssrc[(int64_t)gg * 16];
+  };
+  auto widen_store = [&](uint8_t* dst, const uint4 p) {
+    *reinterpret_cast<uint4*>(dst) =
+        make_uint4(w4_lo_x16(p.x), w4_hi_x16(p.x), w4_lo_x16(p.y), w4_hi_x16(p.y));
+    *reinterpret_cast<uint4*>(dst + 16) =
+        make_uint4(w4_lo_x16(p.z), w4_hi_x16(p.z), w4_lo_x16(p.w), w4_hi_x16(p.w));
+  };
+  auto lstore = [&](int buf) {
+    widen_store(&As[buf][adst[0]], ra[0]);
+    widen_store(&As[buf][adst[1]], ra[1]);
+    widen_store(&Bs[buf][bdst], rbv);
+    if (tid < 256) Ss[buf][tid] = half_bits_to_float(rs) * 0.00390625f;  // / 256
+  };
+
+  v4f tot[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  gload(1);
+
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    const uint8_t* Ab = &As[buf][(wn * 64 + l16) * RST + lg * 32];
+    const uint8_t* Bb = &Bs[buf][(wm * 64 + l16) * RST + lg * 32];
+    v4i bf[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      bf[mb][0] = *reinterpret_cast<const v4i*>(Bb + mb * 16 * RST);
+      bf[mb][1] = *reinterpret_cast<const v4i*>(Bb + mb * 16 * RST + 16);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const v4i a0 = *reinterpret_cast<const v4i*>(Ab + nb * 16 * RST);
+      const v4i a1 = *reinterpret_cast<const v4i*>(Ab + nb * 16 * RST + 16);
+      const float4 sc = *reinterpret_cast<const float4*>(&Ss[buf][wn * 64 + nb * 16 + lg * 4]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bf[mb][0], v4i{0, 0, 0, 0}, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bf[mb][1], acc, 0, 0, 0);
+        tot[nb][mb][0] = fmaf(sc.x, (float)acc[0], tot[nb][mb][0]);
+        tot[nb][mb][1] = fmaf(sc.y, (float)acc[1], tot[nb][mb][1]);
+        tot[nb][mb][2] = fmaf(sc.z, (float)acc[2], tot[nb][mb][2]);
+        tot[nb][mb][3] = fmaf(sc.w, (float)acc[3], tot[nb][mb][3]);
+      }
+    }
+    lstore(buf ^ 1);  // group g+1 (loaded one group ago) into the other buffer
+    __syncthreads();
+    gload(g + 2);
+  }
+
+  const bool vec = (N & 3) == 0;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + wm * 64 + mb * 16 + l16;
+      const int n = nt * BN + wn * 64 + nb * 16 + lg * 4;
+      if (m < M && n < N) {
+        const float xsc = a.Xs[m];
+        const float v0 = xsc * tot[nb][mb][0], v1 = xsc * tot[nb][mb][1];
+        const float v2 = xsc * tot[nb][mb][2], v3 = xsc * tot[nb][mb][3];
+        float* dst = a.Y + (int64_t)m * N + n;
+        if (vec) {
+          *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+        } else {
+          const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = v[r];
+        }
+      }
+    }
+}
+
+template <int MODE>
+hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
+                        int64_t M, int64_t N, int64_t K, float* Y, hipStream_t s) {
+  TiledArgs a{X, Xs, Wq, Ws, Y, (int)M, (int)N, (int)K, (int)cdiv(N, 128), (int)cdiv(M, 128)};
+  const int64_t blocks = 8 * cdiv(a.ntn, 8) * a.ntm;
+  if (MODE == kW4A16) {
+    hipLaunchKernelGGL((tiled_kernel<kW4A16, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  } else {
+    a.ntn = (int)cdiv(N, 256);
+    const int64_t b4 = 8 * cdiv(a.ntn, 8) * a.ntm;
+    hipLaunchKernelGGL(w4a4_prefill_kernel, dim3((unsigned)b4), dim3(512), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// ============================================================================
 // W4A16 GEMV family (M <= 4 per launch): VALU dot products, no MFMA.
 //   * a wavefront owns one 16-row block for a k-slice of up to 32 groups;
 //     lane l reads the tile slot of row l%16, codes 32*(l/16) .. +32 of each
@@ -679,9 +1078,15 @@ struct GemvPlan {
 };
 GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K / kGroup, kGemvGroups)}; }
 
+// AUTO: GEMV for one or two rows, the skinny MFMA family up to 128 rows,
+// the tiled family beyond
 int w4a16_pick(int variant, int64_t M) {
   if (variant != QSPEC_GEMM_AUTO) return variant;
-  return M <= 2 ? QSPEC_GEMM_GEMV : QSPEC_GEMM_SKINNY;
+  return M <= 2 ? QSPEC_GEMM_GEMV : M <= 128 ? QSPEC_GEMM_SKINNY : QSPEC_GEMM_TILED;
+}
+int w4a4_pick(int variant, int64_t M) {
+  if (variant != QSPEC_GEMM_AUTO) return variant;
+  return M <= 128 ? QSPEC_GEMM_SKINNY : QSPEC_GEMM_TILED;
 }
 
 hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* Xs, float* Y,
@@ -731,7 +1136,7 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
     }
     return hipSuccess;
   }
-  // SKINNY (TILED shares it until the prefill family lands)
+  if (v == QSPEC_GEMM_TILED) return launch_tiled<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, s);
   const SkinnyPlan p = plan_skinny(0, M, N, K);
   SkinnyArgs a{};
   a.X = X;
@@ -753,7 +1158,9 @@ size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
                        void* ws, hipStream_t s) {
-  (void)variant;
+  // the int32 partials output is a check path served by the skinny family
+  if (w4a4_pick(variant, M) == QSPEC_GEMM_TILED && P == nullptr)
+    return launch_tiled<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, s);
   const SkinnyPlan p = plan_skinny(1, M, N, K);
   SkinnyArgs a{};
   a.X = Xq;

@@ -29,6 +29,7 @@ SHAPES = [
     (40, 48, 1152),
     (70, 130, 640),
     (3, 4608, 3584),
+    (300, 600, 1152),
 ]
 
 
@@ -127,9 +128,14 @@ def test_w4a4_parity(M, N, K, variant):
     W, X = _case(12, M, N, K)
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
-    Y, P = q.gemm_w4a4(dev(Xq), dev(Xs), dev_w(Wq), dev_s(Ws), variant=variant, partials=True, N=N)
+    Xq_d, Xs_d, Wq_d, Ws_d = dev(Xq), dev(Xs), dev_w(Wq), dev_s(Ws)
+    Y, P = q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d, variant=variant, partials=True, N=N)
     assert np.array_equal(host(P), oracle.w4a4_partials(Xq, Wq))
-    assert_close(host(Y), oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4")
+    want = oracle.gemm_w4a4(Xq, Xs, Wq, Ws)
+    assert_close(host(Y), want, what="w4a4")
+    # without the partials output (the tiled family serves this path)
+    Y2 = q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d, variant=variant, N=N)
+    assert_close(host(Y2), want, what="w4a4 no partials")
 
 
 def test_w4a4_gpu_quantized_chain():
