@@ -776,14 +776,19 @@ __global__ __launch_bounds__(512, 1) void w4a4_prefill_kernel(const TiledArgs a)
   const uint16_t* ssrc =
       a.Ws + (int64_t)min(rb0 + ((tid & 255) >> 4), nrb - 1) * G * 16 + (tid & 15);
 
-  uint4 ra[2], rbv;
-  uint16_t rs;
-  auto gload = [&](int g) {
+  // two register stages: the loads of group g+2 are issued right after the
+  // barrier that ends group g and are consumed two compute phases later
+  struct Stage {
+    uint4 a0, a1, b;
+    uint32_t s;
+  };
+  Stage st0, st1;
+  auto gload = [&](Stage& st, int g) {
     const int gg = min(g, G - 1);
-    ra[0] = ld_stream(asrc[0] + (int64_t)gg * 1024);
-    ra[1] = ld_stream(asrc[1] + (int64_t)gg * 1024);
-    rbv = *reinterpret_cast<const uint4*>(bsrc + (int64_t)gg * 64);
-    rs = ssrc[(int64_t)gg * 16];
+    st.a0 = ld_stream(asrc[0] + (int64_t)gg * 1024);
+    st.a1 = ld_stream(asrc[1] + (int64_t)gg * 1024);
+    st.b = *reinterpret_cast<const uint4*>(bsrc + (int64_t)gg * 64);
+    st.s = ssrc[(int64_t)gg * 16];
   };
   auto widen_store = [&](uint8_t* dst, const uint4 p) {
     *reinterpret_cast<uint4*>(dst) =
@@ -791,11 +796,12 @@ __global__ __launch_bounds__(512, 1) void w4a4_prefill_kernel(const TiledArgs a)
     *reinterpret_cast<uint4*>(dst + 16) =
         make_uint4(w4_lo_x16(p.z), w4_hi_x16(p.z), w4_lo_x16(p.w), w4_hi_x16(p.w));
   };
-  auto lstore = [&](int buf) {
-    widen_store(&As[buf][adst[0]], ra[0]);
-    widen_store(&As[buf][adst[1]], ra[1]);
-    widen_store(&Bs[buf][bdst], rbv);
-    if (tid < 256) Ss[buf][tid] = half_bits_to_float(rs) * 0.00390625f;  // / 256
+  auto lstore = [&](const Stage& st, int buf) {
+    widen_store(&As[buf][adst[0]], st.a0);
+    widen_store(&As[buf][adst[1]], st.a1);
+    widen_store(&Bs[buf][bdst], st.b);
+    // threads t and t + 256 write the same value: no branch, no sunk load
+    Ss[buf][tid & 255] = half_bits_to_float((uint16_t)st.s) * 0.00390625f;  // / 256
   };
 
   v4f tot[4][4];
@@ -804,13 +810,7 @@ __global__ __launch_bounds__(512, 1) void w4a4_prefill_kernel(const TiledArgs a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  gload(1);
-
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
+  auto compute = [&](int buf) {
     const uint8_t* Ab = &As[buf][(wn * 64 + l16) * RST + lg * 32];
     const uint8_t* Bb = &Bs[buf][(wm * 64 + l16) * RST + lg * 32];
     v4i bf[4][2];
@@ -834,10 +834,30 @@ __global__ __launch_bounds__(512, 1) void w4a4_prefill_kernel(const TiledArgs a)
         tot[nb][mb][3] = fmaf(sc.w, (float)acc[3], tot[nb][mb][3]);
       }
     }
-    lstore(buf ^ 1);  // group g+1 (loaded one group ago) into the other buffer
+  };
+
+  gload(st0, 0);
+  gload(st1, 1);
+  lstore(st0, 0);
+  __syncthreads();
+  gload(st0, 2);
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    // group g sits in LDS buffer 0, group g+1 in st1, group g+2 in st0
+    compute(0);
+    __builtin_amdgcn_sched_barrier(0);
+    lstore(st1, 1);
     __syncthreads();
-    gload(g + 2);
+    gload(st1, g + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    __builtin_amdgcn_sched_barrier(0);
+    lstore(st0, 0);
+    __syncthreads();
+    gload(st0, g + 4);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (g < G) compute(0);  // odd group count: the last group is in buffer 0
 
   const bool vec = (N & 3) == 0;
 #pragma unroll
