@@ -160,14 +160,14 @@ class Decode:
         return self.gamma, self.bytes_w4a4(p)
 
     # CPU oracle on a bounded sample ------------------------------------------
-    def cpu_baseline(self, frac_rows=1 / 64):
+    def cpu_baseline(self, frac_rows=1.0):
         import oracle
         import synth
         rng = synth.make_rng(1, 7)
         work = []
         bytes_sample = 0
         for name, N, K in QWEN7B:
-            n = max(16, int(N * frac_rows))
+            n = max(16, int(round(N * frac_rows)))
             W = synth.weights(rng, n, K)
             Wq, Ws = oracle.pack_w4(W)
             X = synth.activations(rng, self.B * (self.gamma + 1), K,
@@ -179,18 +179,26 @@ class Decode:
         h = self.host_inputs
         ua = np.asarray(self.vin["ua"].cpu())
         us = np.asarray(self.vin["us"].cpu())
+        # whole rounds, repeated until at least 10 s of CPU work (at most 6)
         t0 = time.perf_counter()
-        for Wq, Ws, X in work:
-            for _ in range(self.gamma):
-                Xq, Xs = oracle.quant_act(X[:self.B])
-                oracle.gemm_w4a4(Xq, Xs, Wq, Ws)
-            oracle.gemm_w4a16(X, Wq, Ws)
-        oracle.verify_sample(h["tgt"], h["drf"], h["d"], ua, us)
+        rounds = 0
+        while rounds < 6 and (rounds == 0 or time.perf_counter() - t0 < 10.0):
+            for Wq, Ws, X in work:
+                for _ in range(self.gamma):
+                    Xq, Xs = oracle.quant_act(X[:self.B])
+                    oracle.gemm_w4a4(Xq, Xs, Wq, Ws)
+                oracle.gemm_w4a16(X, Wq, Ws)
+            oracle.verify_sample(h["tgt"], h["drf"], h["d"], ua, us)
+            rounds += 1
         dt = time.perf_counter() - t0
+        bytes_sample *= rounds
         return dict(value=bytes_sample / dt / 1e9, unit="GB/s", cores=_blas_threads(),
                     kind="oracle",
-                    sample=f"one round with 1/64 of every projection's output rows "
-                           f"(all K, all M) plus the full verify step; {dt:.1f} s")
+                    sample=(f"{rounds} whole round(s) (4 draft passes, 1 verify pass, the verify "
+                            f"step) on freshly drawn weights of the same shapes; {dt:.1f} s"
+                            if frac_rows >= 1 else
+                            f"{rounds} round(s) on {frac_rows:g} of every projection's output "
+                            f"rows (all K, all M) plus the full verify step; {dt:.1f} s"))
 
 
 def measure_prefill(torch, q, wl, reps=5):
@@ -226,6 +234,81 @@ def measure_prefill(torch, q, wl, reps=5):
                   "w4a4_frac_int8": round(ops_all / tot4 / 1e6 / INT8_PEAK_TOPS, 4),
                   "w4a16_tflops": round(ops_all / tot16 / 1e6, 1),
                   "w4a16_frac_bf16": round(ops_all / tot16 / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
+def measure_decode_gemv(torch, q, wl, reps=10):
+    """W4A16 at the decode-verify shapes of batch 1 (M = 1 * (4+1) = 5) on
+    gate|up and down, and the Llama-3-8B lm_head (4096 -> 128256) at M = 1.
+    Each replay rotates through distinct weight copies (> 512 MB in total for
+    the 7B shapes; the lm_head's two copies are 541 MB), so reads come from HBM."""
+    import synth
+    rng = synth.make_rng(1, 3)
+    out = {}
+    for p in wl.proj:
+        if p["name"] not in ("gate_up", "down"):
+            continue
+        N, K = p["N"], p["K"]
+        X = p["X16"][:5].contiguous()
+        Y = torch.empty((5, N), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty(max(1, q.workspace_bytes(2, 5, N, K)), dtype=torch.uint8, device="cuda:0")
+        cps = p["copies"]
+
+        def fn():
+            for Wq, Ws in cps:
+                q.gemm_w4a16(X, Wq, Ws, Y=Y, ws=ws)
+        us = _graph_time(torch, fn, reps, launches=1) / len(cps)
+        b = wbytes(N, K) + 5 * K * 2 + 5 * N * 4
+        out[f"{p['name']}_M5"] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                                  "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)}
+    N, K = 128256, 4096
+    cps = []
+    for _ in range(2):
+        W = torch.empty((N, K), dtype=torch.float32, device="cuda:0").normal_(0.0, 0.02)
+        cps.append(q.pack_w4(W))
+        del W
+    X = torch.from_numpy(synth.activations(rng, 1, K).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    Y = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(max(1, q.workspace_bytes(2, 1, N, K)), dtype=torch.uint8, device="cuda:0")
+
+    def fh():
+        for Wq, Ws in cps:
+            q.gemm_w4a16(X, Wq, Ws, Y=Y, ws=ws)
+    us = _graph_time(torch, fh, reps, launches=1) / len(cps)
+    b = wbytes(N, K) + K * 2 + N * 4
+    out["lm_head_M1"] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
+                         "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)}
+    del cps
+    return out
+
+
+def measure_verify_llama(torch, q, reps=10):
+    """verify at batch 32, V = 128256 (Llama-3 vocabulary), gamma 4 and 8,
+    greedy and speculative sampling; bytes = one pass over the logits read
+    plus, for sampling, the residual row pair per sequence."""
+    import synth
+    rng = synth.make_rng(3, 0)
+    B, V = 32, 128256
+    out = {}
+    for gamma in (4, 8):
+        tgt, drf = synth.verify_logits(rng, B, gamma, V)
+        d = synth.gumbel_drafts(rng, drf)
+        t = lambda a: torch.from_numpy(a).to("cuda:0")  # noqa: E731
+        T, D, Dt = t(tgt), t(drf), t(d)
+        ua, us_ = t(synth.uniforms(rng, (B, gamma))), t(synth.uniforms(rng, (B,)))
+        n_acc = torch.empty((B,), dtype=torch.int32, device="cuda:0")
+        o = torch.empty((B, gamma + 1), dtype=torch.int32, device="cuda:0")
+        ws = torch.empty(q.workspace_bytes(3, B, gamma, V), dtype=torch.uint8, device="cuda:0")
+        tg = _graph_time(torch, lambda: q.verify(q.VERIFY_GREEDY, T, Dt, n_accept=n_acc,
+                                                 out_tok=o, ws=ws), reps)
+        ts = _graph_time(torch, lambda: q.verify(q.VERIFY_SAMPLE, T, Dt, D, ua, us_,
+                                                 n_accept=n_acc, out_tok=o, ws=ws), reps)
+        bg = B * (gamma + 1) * V * 4
+        bs = bg + B * gamma * V * 4 + B * 2 * V * 4
+        out[f"gamma{gamma}"] = {"greedy_us": round(tg, 2), "greedy_GBps": round(bg / tg / 1e3, 1),
+                                "sample_us": round(ts, 2), "sample_GBps": round(bs / ts / 1e3, 1),
+                                "sample_frac_hbm": round(bs / ts / 1e3 / HBM_PEAK_GBPS, 4)}
+        del T, D, Dt
     return out
 
 
@@ -328,13 +411,7 @@ def run(args):
 
     step_bytes = wl.step_bytes()
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    traffic = None
-    tf = os.path.join(ROOT, "profiles", "traffic_w4a4_gate_up_M8.json")
-    if os.path.exists(tf):
-        try:
-            traffic = json.load(open(tf)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = read_traffic()
 
     line = {
         "metric": "W4A4/W4A16 layer TOPS & HBM GB/s vs roofline; self-spec accepted tokens/s",
@@ -354,13 +431,103 @@ def run(args):
                      "us_per_launch": round(us_dom, 3), "bytes_per_launch": box["bytes"]},
         "wall_s_timed": round(wall, 4),
     }
-    if not args.no_prefill:
+    if not args.no_extra:
+        log("decode GEMV points")
+        line["decode_gemv_w4a16"] = measure_decode_gemv(torch, q, wl)
         log("prefill-shaped GEMMs")
         line["prefill_m2048"] = measure_prefill(torch, q, wl)
+        log("verify at batch 32, V=128256")
+        line["verify_b32_v128256"] = measure_verify_llama(torch, q)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         line["cpu_baseline"] = wl.cpu_baseline()
     print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel from rocprofv3 counters.
+#   1) rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- python bench.py --counters
+#   2) the same with WRITE_SIZE (a separate run: one counter block per pass)
+#   3) python bench.py --traffic <fetch counter csv> <write counter csv>
+# --counters runs a plain 1 GiB fp32 copy (calibration: 1 GiB read + 1 GiB
+# written) and the dominant kernel's launches; --traffic scales the dominant
+# kernel's mean FETCH/WRITE KiB per dispatch by the copy's measured/known ratio
+# and writes profiles/traffic_w4a4_gate_up_M8.json, stamped with the hash of
+# the GEMM source so a later kernel change voids it.
+COPY_ELEMS = 1 << 28
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w4a4_gate_up_M8.json")
+W4A4_SKINNY_TAG = "skinny_kernel<1,"
+
+
+def _gemm_source_hash():
+    import hashlib
+    src = os.path.join(ROOT, "quantization_self_speculation_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def run_counters():
+    import torch
+    import quantization_self_speculation_amd as q
+    q.lib()
+    torch.cuda.set_device(0)
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    wl = Decode(torch, q)
+    p = [x for x in wl.proj if x["name"] == "gate_up"][0]
+    q.quant_act(p["X4"], p["Xq"], p["Xs"])
+    for _ in range(5):
+        wl.dominant_launches()
+    torch.cuda.synchronize()
+    log("counters workload done: 3 copies of 1 GiB, 20 W4A4 gate|up M=8 launches")
+
+
+def _counter_means(path, counter):
+    import csv
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    copy = [v for (k, _), v in per.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+    dom = [v for (k, _), v in per.items() if W4A4_SKINNY_TAG in k.replace(" ", "")]
+    if not copy or not dom:
+        raise SystemExit(f"{path}: no copy ({len(copy)}) or W4A4 ({len(dom)}) dispatches for {counter}")
+    # the 1 GiB copy is the largest elementwise dispatch
+    return max(copy), sum(dom) / len(dom), len(dom)
+
+
+def write_traffic(fetch_csv, write_csv):
+    known_kib = COPY_ELEMS * 4 / 1024.0
+    cf, df, nf = _counter_means(fetch_csv, "FETCH_SIZE")
+    cw, dw, nw = _counter_means(write_csv, "WRITE_SIZE")
+    sf, sw = known_kib / cf, known_kib / cw
+    rec = {"kernel": "w4a4_gate_up_M8", "gemm_source_sha256_16": _gemm_source_hash(),
+           "fetch_kib_per_dispatch": round(df, 1), "write_kib_per_dispatch": round(dw, 1),
+           "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+           "fetch_scale": round(sf, 5), "write_scale": round(sw, 5),
+           "dispatches": [nf, nw],
+           "bytes_per_launch": int(round((df * sf + dw * sw) * 1024))}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def read_traffic():
+    """the stored traffic figure, or None when absent or taken on another
+    version of the GEMM source"""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except Exception:
+        return None
+    if rec.get("gemm_source_sha256_16") != _gemm_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def main():
@@ -370,12 +537,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the decode-GEMV, prefill and verify side measurements")
+    ap.add_argument("--counters", action="store_true",
+                    help="run only the copy calibration and the dominant kernel (for rocprofv3 --pmc)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter CSVs into the stored traffic figure")
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(*args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.counters:
+        run_counters()
+        return
     run(args)
 
 
