@@ -25,6 +25,9 @@ Where the pages are silent (they print no formula, layout or precision for
 any step) the module docstrings state the reading taken.
 
 Parity status per function is listed in each module's header.
+
+``oracle.model`` (imported on demand: ``import oracle.model``) holds the
+decoder used by the end-to-end self-speculative loop.
 """
 
 from .quant import (  # noqa: F401

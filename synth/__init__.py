@@ -19,14 +19,23 @@ logits, uniforms):
 * draft tokens: Gumbel-max draws from softmax(draft logits), or planted
   tokens with a forced target argmax for greedy cases;
 * uniforms: fp32 in [0, 1).
+
+Decoder model for the end-to-end self-speculative loop (sizes only, plus the
+seeded draws): ``ModelConfig`` lists the shapes and the two model constants
+(RMSNorm epsilon, RoPE base); ``model_weights`` draws, in this order, the
+embedding (N(0, 0.02), stored as bf16), then per layer the fused QKV, O,
+fused gate|up (gate rows first) and down matrices, then the lm_head, all fp32
+N(0, 0.02); ``prompts`` draws uniform token ids.
 """
+
+from dataclasses import dataclass
 
 import numpy as np
 
 __all__ = [
     "make_rng", "outlier_count", "to_bf16_bits", "from_bf16_bits", "weights",
     "activations", "verify_logits", "plant_greedy", "gumbel_drafts",
-    "uniforms",
+    "uniforms", "ModelConfig", "TINY_MODEL", "E2E_MODEL", "model_weights", "prompts",
 ]
 
 
@@ -101,3 +110,54 @@ def gumbel_drafts(rng, draft_logits):
 
 def uniforms(rng, shape):
     return rng.random(shape, dtype=np.float32)
+
+
+@dataclass(frozen=True)
+class ModelConfig:
+    vocab: int
+    d: int
+    n_layers: int
+    n_heads: int
+    n_kv: int
+    head_dim: int
+    ffn: int
+    eps: float = 1e-6
+    rope_base: float = 10000.0
+
+    @property
+    def q_dim(self):
+        return self.n_heads * self.head_dim
+
+    @property
+    def kv_dim(self):
+        return self.n_kv * self.head_dim
+
+    @property
+    def qkv_rows(self):
+        return self.q_dim + 2 * self.kv_dim
+
+
+# the end-to-end workload: 8 layers, d 2048, 16 query / 4 key-value heads of
+# 128, SwiGLU hidden 5632, vocabulary 32000
+E2E_MODEL = ModelConfig(vocab=32000, d=2048, n_layers=8, n_heads=16, n_kv=4, head_dim=128,
+                        ffn=5632)
+# a two-layer model of the same structure for CPU-sized tests
+TINY_MODEL = ModelConfig(vocab=512, d=256, n_layers=2, n_heads=2, n_kv=1, head_dim=128, ffn=768)
+
+
+def model_weights(rng, cfg, std=0.02):
+    """dict(emb = bf16 bits [V, d], layers = [dict(qkv, o, gu, down) fp32],
+    lm = fp32 [V, d]); every matrix is [out features, in features]."""
+    emb = to_bf16_bits(weights(rng, cfg.vocab, cfg.d, std))
+    layers = []
+    for _ in range(cfg.n_layers):
+        layers.append(dict(qkv=weights(rng, cfg.qkv_rows, cfg.d, std),
+                           o=weights(rng, cfg.d, cfg.q_dim, std),
+                           gu=weights(rng, 2 * cfg.ffn, cfg.d, std),
+                           down=weights(rng, cfg.d, cfg.ffn, std)))
+    lm = weights(rng, cfg.vocab, cfg.d, std)
+    return dict(emb=emb, layers=layers, lm=lm)
+
+
+def prompts(rng, B, P, vocab):
+    return rng.integers(0, vocab, size=(B, P)).astype(np.int32)
