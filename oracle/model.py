@@ -210,20 +210,41 @@ def kv_capacity(P, n_gen, gamma):
     return P + n_gen + gamma + 1
 
 
-def greedy_decode(model, prompts, n_gen, gamma=4):
+def top2_margin(logits):
+    """(largest - second largest) / max|value| per row (0 for an exact tie)."""
+    part = np.sort(logits.astype(np.float64), axis=-1)
+    scale = np.maximum(np.abs(part[..., 0]), np.abs(part[..., -1]))
+    return (part[..., -1] - part[..., -2]) / scale
+
+
+def greedy_decode(model, prompts, n_gen, gamma=4, with_margins=False):
     """Pure W4A16 greedy decoding: one token per sequence per forward.
-    Returns (tokens [B, n_gen], kv)."""
+    Returns (tokens [B, n_gen], kv), plus the relative top-2 logit margin
+    behind every token [B, n_gen] when with_margins is set."""
     B, P = prompts.shape
     kv = KVCache(model.cfg, B, kv_capacity(P, n_gen, gamma))
-    last = prefill(model, kv, prompts)
+    if with_margins:
+        Bq, Pq = prompts.shape
+        seq = np.repeat(np.arange(Bq), Pq)
+        pos = np.tile(np.arange(Pq), Bq)
+        lg = forward(model, kv, seq, pos, prompts.reshape(-1), VERIFY).reshape(Bq, Pq, -1)[:, -1]
+        last = argmax_first(lg)
+        margins = [top2_margin(lg)]
+    else:
+        last = prefill(model, kv, prompts)
     out = [last]
     L = np.full(B, P + 1)
     for _ in range(n_gen - 1):
         logits = forward(model, kv, np.arange(B), L - 1, last, VERIFY)
         last = argmax_first(logits)
         out.append(last)
+        if with_margins:
+            margins.append(top2_margin(logits))
         L += 1
-    return np.stack(out, axis=1), kv
+    toks = np.stack(out, axis=1)
+    if with_margins:
+        return toks, kv, np.stack(margins, axis=1)
+    return toks, kv
 
 
 def selfspec_greedy(model, prompts, n_gen, gamma):

@@ -5,7 +5,8 @@ verify step accepts or rewrites the drafted tokens.  Every step runs in the
 hand-written HIP kernels of ``libqspec.so`` (C ABI in ``include/qspec.h``);
 this package only marshals torch tensors (device memory and streams) into
 those calls.  There is no CPU fallback: if the library is missing the calls
-raise.
+raise.  ``e2e.Decoder`` runs greedy self-speculative decoding of a whole
+decoder on these calls (decoder kernels in ``include/qspec_harness.h``).
 """
 
 from .binding import (  # noqa: F401
@@ -25,4 +26,12 @@ from .binding import (  # noqa: F401
     GEMM_TILED,
     VERIFY_GREEDY,
     VERIFY_SAMPLE,
+    embed,
+    add_rmsnorm,
+    rope_kv,
+    attention,
+    silu_mul,
+    argmax,
+    spec_prepare,
+    spec_commit,
 )

@@ -58,6 +58,14 @@ def lib():
             "qspec_gemm_w4a4": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
             "qspec_gemm_w4a16": (I, [P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_verify": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P, SZ, P]),
+            "qspec_embed": (I, [P, I64, I64, P, I64, P, P]),
+            "qspec_add_rmsnorm": (I, [P, I64, P, I64, I64, I64, ctypes.c_double, P, P]),
+            "qspec_rope_kv": (I, [P, I64, I, I, P, P, ctypes.c_double, P, P, P, I64, I64, P]),
+            "qspec_attention": (I, [P, P, P, I64, I, I, P, P, I64, I64, P, P]),
+            "qspec_silu_mul": (I, [P, I64, I64, P, P]),
+            "qspec_argmax": (I, [P, I64, I64, P, I64, P]),
+            "qspec_spec_prepare": (I, [I, I64, I, I, P, P, P, P, P, P, P]),
+            "qspec_spec_commit": (I, [I64, I, P, P, P, P, I64, P, I64, P, I, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -207,3 +215,95 @@ def verify(mode, target_logits, draft_tok, draft_logits=None, u_accept=None, u_s
                               _ptr(target_logits), _ptr(u_accept), _ptr(u_sample), _ptr(n_accept),
                               _ptr(out_tok), _ptr(w), wb, _stream()), "qspec_verify")
     return n_accept, out_tok
+
+
+# ---------------------------------------------------------------- decoder kernels
+# These take tensors that may be views (row offsets, strided columns): the
+# pointer passed is the view's first element; shapes are given explicitly
+# where a view cannot carry them.
+def _dev(t, name, dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dtype:
+        raise TypeError(f"{name} must be a {dtype} device tensor")
+
+
+def embed(emb, tok, x):
+    """x[m] = float(emb[tok[m]]); emb bf16 [V, d], tok int32 [M], x fp32 [M, d]"""
+    _need(emb, "emb", torch.bfloat16)
+    _dev(tok, "tok", torch.int32)
+    _dev(x, "x", torch.float32)
+    V, d = emb.shape
+    _check(lib().qspec_embed(_ptr(emb), V, d, _ptr(tok), tok.numel(), _ptr(x), _stream()),
+           "qspec_embed")
+
+
+def add_rmsnorm(x, add, y, eps):
+    """x[m] += add[m] (if add is not None); y[m] = bf16(rmsnorm(x[m])).
+    x and add are 2-D (row-strided views allowed), y dense bf16 [M, d]."""
+    _dev(x, "x", torch.float32)
+    _need(y, "y", torch.bfloat16)
+    M, d = y.shape
+    if x.dim() != 2 or tuple(x.shape) != (M, d) or x.stride(1) != 1:
+        raise ValueError("x must be a row-strided [M, d] view")
+    a_stride = 0
+    if add is not None:
+        _dev(add, "add", torch.float32)
+        if add.dim() != 2 or tuple(add.shape) != (M, d) or add.stride(1) != 1:
+            raise ValueError("add must be a row-strided [M, d] view")
+        a_stride = int(add.stride(0))
+    _check(lib().qspec_add_rmsnorm(_ptr(x), int(x.stride(0)), _ptr(add), a_stride, M, d,
+                                   float(eps), _ptr(y), _stream()), "qspec_add_rmsnorm")
+
+
+def rope_kv(qkv, seq, pos, q_out, kcache, vcache, n_heads, n_kv, rope_base):
+    """RoPE on the q and k parts of qkv fp32 [M, (H + 2 Hkv) 128]; q_out fp32
+    [M, H 128]; K/V written into the bf16 caches [B, Hkv, cap, 128]"""
+    _dev(qkv, "qkv", torch.float32)
+    _dev(q_out, "q_out", torch.float32)
+    _dev(kcache, "kcache", torch.bfloat16)
+    _dev(vcache, "vcache", torch.bfloat16)
+    B, _, cap, _ = kcache.shape
+    _check(lib().qspec_rope_kv(_ptr(qkv), int(qkv.shape[0]), n_heads, n_kv, _ptr(seq), _ptr(pos),
+                               float(rope_base), _ptr(q_out), _ptr(kcache), _ptr(vcache), B, cap,
+                               _stream()), "qspec_rope_kv")
+
+
+def attention(q, kcache, vcache, seq, pos, out, n_heads, n_kv):
+    """causal GQA over the cache; q fp32 [M, H 128] -> out bf16 [M, H 128]"""
+    _dev(q, "q", torch.float32)
+    _dev(out, "out", torch.bfloat16)
+    B, _, cap, _ = kcache.shape
+    _check(lib().qspec_attention(_ptr(q), _ptr(kcache), _ptr(vcache), int(q.shape[0]), n_heads,
+                                 n_kv, _ptr(seq), _ptr(pos), B, cap, _ptr(out), _stream()),
+           "qspec_attention")
+
+
+def silu_mul(gu, a):
+    """a = bf16(silu(gate) * up); gu fp32 [M, 2F], a bf16 [M, F]"""
+    _dev(gu, "gu", torch.float32)
+    _dev(a, "a", torch.bfloat16)
+    M, F = a.shape
+    _check(lib().qspec_silu_mul(_ptr(gu), M, F, _ptr(a), _stream()), "qspec_silu_mul")
+
+
+def argmax(x, out, out_stride=1):
+    """out[m * out_stride] = first index of the row maximum of x fp32 [M, V]"""
+    _need(x, "x", torch.float32)
+    _dev(out, "out", torch.int32)
+    M, V = x.shape
+    _check(lib().qspec_argmax(_ptr(x), M, V, _ptr(out), int(out_stride), _stream()),
+           "qspec_argmax")
+
+
+def spec_prepare(phase, B, gamma, j, len_, vtok, drafts, seq, pos, tok):
+    _check(lib().qspec_spec_prepare(int(phase), int(B), int(gamma), int(j), _ptr(len_),
+                                    _ptr(vtok), _ptr(drafts), _ptr(seq), _ptr(pos), _ptr(tok),
+                                    _stream()), "qspec_spec_prepare")
+
+
+def spec_commit(B, gamma, n_accept, out_tok, len_, vtok, vtok_stride, gen, n_gen, max_gen, stats):
+    _dev(gen, "gen", torch.int32)
+    _dev(stats, "stats", torch.int64)
+    _check(lib().qspec_spec_commit(int(B), int(gamma), _ptr(n_accept), _ptr(out_tok), _ptr(len_),
+                                   _ptr(vtok), int(vtok_stride), _ptr(gen), int(gen.shape[1]),
+                                   _ptr(n_gen), int(max_gen), _ptr(stats), _stream()),
+           "qspec_spec_commit")

@@ -8,6 +8,7 @@
 #include <atomic>
 
 #include "launch.h"
+#include "qspec_harness.h"
 
 namespace qspec {
 
@@ -111,6 +112,29 @@ qspec_status check_ws(void* ws, size_t have, size_t need) {
   QS_REQUIRE(ws != nullptr && have >= need, QSPEC_ERR_WORKSPACE,
              "workspace of %zu bytes needed (got %zu%s)", need, have, ws ? "" : ", NULL");
   QS_REQUIRE(aligned16(ws), QSPEC_ERR_ALIGN, "ws is not 16-byte aligned");
+  return QSPEC_OK;
+}
+
+template <typename T>
+qspec_status check_elem(const T* p, const char* name) {
+  if (p == nullptr) return fail(QSPEC_ERR_NULL, "%s is NULL", name);
+  if ((reinterpret_cast<uintptr_t>(p) % alignof(T)) != 0)
+    return fail(QSPEC_ERR_ALIGN, "%s is not aligned to its element size", name);
+  return QSPEC_OK;
+}
+
+#define QS_EPTR(p) QS_TRY(check_elem((p), #p))
+
+qspec_status check_heads(int n_heads, int n_kv) {
+  QS_REQUIRE(n_heads >= 1 && n_kv >= 1 && n_heads % n_kv == 0 && n_heads <= 1024,
+             QSPEC_ERR_SHAPE, "need n_heads a multiple of n_kv (got %d, %d)", n_heads, n_kv);
+  return QSPEC_OK;
+}
+
+qspec_status check_cache(int64_t B, int64_t cap) {
+  QS_REQUIRE(B >= 1 && B <= kMaxDim && cap >= 1 && cap <= QSPEC_MAX_CAP, QSPEC_ERR_SHAPE,
+             "need B >= 1 and 1 <= cap <= %d (got %lld, %lld)", QSPEC_MAX_CAP, (long long)B,
+             (long long)cap);
   return QSPEC_OK;
 }
 
@@ -238,6 +262,137 @@ qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V, const int32
   return hip_result(launch_verify(mode, B, gamma, V, draft_tok, draft_logits, target_logits,
                                   u_accept, u_sample, n_accept, out_tok, ws, (hipStream_t)stream),
                     "verify launch");
+}
+
+// ---------------------------------------------------------------- decoder kernels
+qspec_status qspec_embed(const uint16_t* emb, int64_t V, int64_t d, const int32_t* tok, int64_t M,
+                         float* x, qspec_stream stream) {
+  QS_REQUIRE(V >= 1 && d >= 8 && d % 8 == 0 && d <= kMaxDim && M >= 1 && M <= kMaxDim,
+             QSPEC_ERR_SHAPE, "need V >= 1, d a positive multiple of 8, M >= 1");
+  QS_PTR(emb);
+  QS_EPTR(tok);
+  QS_EPTR(x);
+  QS_TRY(device_check());
+  return hip_result(launch_embed(emb, V, d, tok, M, x, (hipStream_t)stream), "embed launch");
+}
+
+qspec_status qspec_add_rmsnorm(float* x, int64_t x_stride, const float* add, int64_t add_stride,
+                               int64_t M, int64_t d, double eps, uint16_t* y,
+                               qspec_stream stream) {
+  QS_REQUIRE(d >= 1 && d <= QSPEC_MAX_D && x_stride >= d && M >= 1 && M <= kMaxDim,
+             QSPEC_ERR_SHAPE, "need 1 <= d <= %d, x_stride >= d, M >= 1", QSPEC_MAX_D);
+  QS_REQUIRE(add == nullptr || add_stride >= d, QSPEC_ERR_SHAPE, "need add_stride >= d");
+  QS_REQUIRE(eps >= 0.0, QSPEC_ERR_SHAPE, "eps must be >= 0");
+  QS_EPTR(x);
+  if (add != nullptr) QS_EPTR(add);
+  QS_EPTR(y);
+  QS_TRY(device_check());
+  return hip_result(launch_add_rmsnorm(x, x_stride, add, add_stride, M, d, eps, y,
+                                       (hipStream_t)stream),
+                    "add_rmsnorm launch");
+}
+
+qspec_status qspec_rope_kv(const float* qkv, int64_t M, int n_heads, int n_kv, const int32_t* seq,
+                           const int32_t* pos, double rope_base, float* q_out, uint16_t* kcache,
+                           uint16_t* vcache, int64_t B, int64_t cap, qspec_stream stream) {
+  QS_REQUIRE(M >= 1 && M <= kMaxDim, QSPEC_ERR_SHAPE, "need M >= 1");
+  QS_TRY(check_heads(n_heads, n_kv));
+  QS_TRY(check_cache(B, cap));
+  QS_REQUIRE(rope_base > 0.0, QSPEC_ERR_SHAPE, "rope_base must be > 0");
+  QS_EPTR(qkv);
+  QS_EPTR(seq);
+  QS_EPTR(pos);
+  QS_EPTR(q_out);
+  QS_EPTR(kcache);
+  QS_EPTR(vcache);
+  QS_TRY(device_check());
+  return hip_result(launch_rope_kv(qkv, M, n_heads, n_kv, QSPEC_HEAD_DIM, seq, pos, rope_base,
+                                   q_out, kcache, vcache, B, cap, (hipStream_t)stream),
+                    "rope_kv launch");
+}
+
+qspec_status qspec_attention(const float* q, const uint16_t* kcache, const uint16_t* vcache,
+                             int64_t M, int n_heads, int n_kv, const int32_t* seq,
+                             const int32_t* pos, int64_t B, int64_t cap, uint16_t* out,
+                             qspec_stream stream) {
+  QS_REQUIRE(M >= 1 && M <= kMaxDim, QSPEC_ERR_SHAPE, "need M >= 1");
+  QS_TRY(check_heads(n_heads, n_kv));
+  QS_REQUIRE(n_kv <= 65535, QSPEC_ERR_SHAPE, "n_kv too large");
+  QS_TRY(check_cache(B, cap));
+  QS_EPTR(q);
+  QS_EPTR(kcache);
+  QS_EPTR(vcache);
+  QS_EPTR(seq);
+  QS_EPTR(pos);
+  QS_EPTR(out);
+  QS_TRY(device_check());
+  return hip_result(launch_attention(q, kcache, vcache, M, n_heads, n_kv, seq, pos, B, cap, out,
+                                     (hipStream_t)stream),
+                    "attention launch");
+}
+
+qspec_status qspec_silu_mul(const float* gu, int64_t M, int64_t ffn, uint16_t* a,
+                            qspec_stream stream) {
+  QS_REQUIRE(M >= 1 && ffn >= 1 && M * ffn <= ((int64_t)1 << 40), QSPEC_ERR_SHAPE,
+             "need M >= 1 and ffn >= 1");
+  QS_EPTR(gu);
+  QS_EPTR(a);
+  QS_TRY(device_check());
+  return hip_result(launch_silu_mul(gu, M, ffn, a, (hipStream_t)stream), "silu_mul launch");
+}
+
+qspec_status qspec_argmax(const float* x, int64_t M, int64_t V, int32_t* out, int64_t out_stride,
+                          qspec_stream stream) {
+  QS_REQUIRE(M >= 1 && M <= kMaxDim && V >= 1 && V <= kMaxDim && out_stride >= 1,
+             QSPEC_ERR_SHAPE, "need M >= 1, 1 <= V < 2^31, out_stride >= 1");
+  QS_EPTR(x);
+  QS_EPTR(out);
+  QS_TRY(device_check());
+  return hip_result(launch_argmax(x, M, V, out, out_stride, (hipStream_t)stream),
+                    "argmax launch");
+}
+
+qspec_status qspec_spec_prepare(int phase, int64_t B, int gamma, int j, const int32_t* len,
+                                const int32_t* vtok, int32_t* drafts, int32_t* seq, int32_t* pos,
+                                int32_t* tok, qspec_stream stream) {
+  QS_REQUIRE(phase == 0 || phase == 1, QSPEC_ERR_UNSUPPORTED, "phase must be 0 or 1");
+  QS_REQUIRE(B >= 1 && B <= ((int64_t)1 << 24) && gamma >= 0 && gamma <= QSPEC_MAX_GAMMA,
+             QSPEC_ERR_SHAPE, "need 1 <= B <= 2^24 and 0 <= gamma <= %d", QSPEC_MAX_GAMMA);
+  if (phase == 0)
+    QS_REQUIRE(j >= 0 && j <= gamma, QSPEC_ERR_SHAPE, "draft step j must be in [0, gamma]");
+  else
+    QS_REQUIRE(gamma >= 1, QSPEC_ERR_SHAPE, "verify needs gamma >= 1");
+  QS_EPTR(len);
+  QS_EPTR(vtok);
+  if (phase == 1) QS_EPTR(drafts);
+  QS_EPTR(seq);
+  QS_EPTR(pos);
+  QS_EPTR(tok);
+  QS_TRY(device_check());
+  return hip_result(launch_spec_prepare(phase, B, gamma, j, len, vtok, drafts, seq, pos, tok,
+                                        (hipStream_t)stream),
+                    "spec_prepare launch");
+}
+
+qspec_status qspec_spec_commit(int64_t B, int gamma, const int32_t* n_accept,
+                               const int32_t* out_tok, int32_t* len, int32_t* vtok,
+                               int64_t vtok_stride, int32_t* gen, int64_t gen_cap, int32_t* n_gen,
+                               int max_gen, int64_t* stats, qspec_stream stream) {
+  QS_REQUIRE(B >= 1 && B <= 65536 && gamma >= 0 && gamma <= QSPEC_MAX_GAMMA, QSPEC_ERR_SHAPE,
+             "need 1 <= B <= 65536 and 0 <= gamma <= %d", QSPEC_MAX_GAMMA);
+  QS_REQUIRE(vtok_stride >= 1 && gen_cap >= 1 && max_gen >= 1, QSPEC_ERR_SHAPE,
+             "need vtok_stride, gen_cap and max_gen >= 1");
+  if (n_accept != nullptr) QS_EPTR(n_accept);
+  QS_EPTR(out_tok);
+  QS_EPTR(len);
+  QS_EPTR(vtok);
+  QS_EPTR(gen);
+  QS_EPTR(n_gen);
+  QS_EPTR(stats);
+  QS_TRY(device_check());
+  return hip_result(launch_spec_commit(B, gamma, n_accept, out_tok, len, vtok, vtok_stride, gen,
+                                       gen_cap, n_gen, max_gen, stats, (hipStream_t)stream),
+                    "spec_commit launch");
 }
 
 }  // extern "C"

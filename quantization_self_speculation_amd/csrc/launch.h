@@ -27,4 +27,29 @@ hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_
                          const float* u_accept, const float* u_sample, int32_t* n_accept,
                          int32_t* out_tok, void* ws, hipStream_t s);
 
+// decoder kernels of the end-to-end loop (harness.hip)
+constexpr int kHarnessHeadDim = 128;
+constexpr int64_t kHarnessMaxCap = 3968;  // attention scores fit 64 KiB of LDS
+constexpr int64_t kHarnessMaxD = 4096;
+hipError_t launch_embed(const uint16_t* emb, int64_t V, int64_t d, const int32_t* tok, int64_t M,
+                        float* x, hipStream_t s);
+hipError_t launch_add_rmsnorm(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
+                              int64_t d, double eps, uint16_t* y, hipStream_t s);
+hipError_t launch_rope_kv(const float* qkv, int64_t M, int H, int Hkv, int hd, const int32_t* seq,
+                          const int32_t* pos, double base, float* q, uint16_t* kc, uint16_t* vc,
+                          int64_t B, int64_t cap, hipStream_t s);
+hipError_t launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t M,
+                            int H, int Hkv, const int32_t* seq, const int32_t* pos, int64_t B,
+                            int64_t cap, uint16_t* out, hipStream_t s);
+hipError_t launch_silu_mul(const float* gu, int64_t M, int64_t F, uint16_t* a, hipStream_t s);
+hipError_t launch_argmax(const float* x, int64_t M, int64_t V, int32_t* out, int64_t stride,
+                         hipStream_t s);
+hipError_t launch_spec_prepare(int phase, int64_t B, int gamma, int j, const int32_t* len,
+                               const int32_t* vtok, int32_t* drafts, int32_t* seq, int32_t* pos,
+                               int32_t* tok, hipStream_t s);
+hipError_t launch_spec_commit(int64_t B, int gamma, const int32_t* n_accept, const int32_t* out_tok,
+                              int32_t* len, int32_t* vtok, int64_t vstride, int32_t* gen,
+                              int64_t gen_cap, int32_t* n_gen, int max_gen, int64_t* stats,
+                              hipStream_t s);
+
 }  // namespace qspec

@@ -1,0 +1,269 @@
+"""Greedy self-speculative decoding on one GPU, every step in libqspec.so.
+
+Per round (one HIP graph, no host work inside): gamma draft forwards with the
+W4A4 linear layers (one row per sequence, each at its own position), one
+verify forward with the W4A16 layers over [last, d_0 .. d_{gamma-1}] that
+overwrites those KV rows, the greedy verify kernel, and the device-side
+commit.  The host reads one counter per round (sequences still running).
+Both modes read the same packed INT4 weights and write the same KV cache
+("QSpec: Speculative Decoding with Complementary Quantization Schemes",
+Abstract (arXiv)); the verify step accepts the matching prefix and rewrites
+the first mismatch (the agihunt.info review of SpecQuant, method paragraph).
+
+The W4A16 layers of decode and verify forwards use one kernel family
+(`GEMM_SKINNY`), whose per-row result does not depend on the row count, and
+every other kernel computes rows independently: a verify forward therefore
+reproduces bit for bit what pure W4A16 decoding computes, and greedy
+self-speculation emits exactly the pure greedy tokens.
+
+This module is orchestration: buffers (torch allocations), graph capture and
+the host loop.  The model is described by any object with the fields
+vocab, d, n_layers, n_heads, n_kv, head_dim, ffn, eps, rope_base.
+"""
+
+import numpy as np
+import torch
+
+from . import binding as b
+
+DRAFT, VERIFY = "w4a4", "w4a16"
+
+
+def _view(buf, *shape):
+    n = 1
+    for s in shape:
+        n *= s
+    return buf[:n].view(*shape)
+
+
+class Decoder:
+    """Packed weights, KV cache and work buffers of one decoder for a batch of
+    B sequences with P-token prompts, up to `max_gen` generated tokens, draft
+    length `gamma`."""
+
+    def __init__(self, cfg, weights, B, P, max_gen, gamma, device="cuda:0",
+                 variant=b.GEMM_SKINNY):
+        if cfg.head_dim != 128:
+            raise ValueError("head_dim must be 128")
+        self.cfg, self.B, self.P, self.max_gen, self.gamma = cfg, B, P, max_gen, gamma
+        self.dev = torch.device(device)
+        self.variant = variant
+        dev = self.dev
+
+        def packed(W):
+            Wd = torch.as_tensor(np.ascontiguousarray(W)).to(dev)
+            Wq, Ws = b.pack_w4(Wd)
+            del Wd
+            return (Wq, Ws, int(W.shape[0]), int(W.shape[1]))
+
+        emb = np.ascontiguousarray(weights["emb"]).view(np.int16)
+        self.emb = torch.from_numpy(emb).to(dev).view(torch.bfloat16)
+        self.layers = [{k: packed(L[k]) for k in ("qkv", "o", "gu", "down")}
+                       for L in weights["layers"]]
+        self.lm = packed(weights["lm"])
+
+        # a frozen sequence keeps being drafted and verified at positions up to
+        # len - 1 + gamma with len <= P + max_gen + gamma
+        self.cap = P + max_gen + 2 * gamma + 1
+        kvshape = (B, cfg.n_kv, self.cap, cfg.head_dim)
+        self.kc = [torch.zeros(kvshape, dtype=torch.bfloat16, device=dev) for _ in self.layers]
+        self.vc = [torch.zeros(kvshape, dtype=torch.bfloat16, device=dev) for _ in self.layers]
+
+        Mmax = max(B * P, B * (gamma + 1))
+        d, F = cfg.d, cfg.ffn
+        qd = cfg.n_heads * cfg.head_dim
+        qkv_rows = qd + 2 * cfg.n_kv * cfg.head_dim
+        Kmax = max(d, qd, F)
+        f32, bf, i32 = torch.float32, torch.bfloat16, torch.int32
+        self.x = torch.empty(Mmax * d, dtype=f32, device=dev)
+        self.h = torch.empty(Mmax * Kmax, dtype=bf, device=dev)
+        self.qkv = torch.empty(Mmax * qkv_rows, dtype=f32, device=dev)
+        self.q = torch.empty(Mmax * qd, dtype=f32, device=dev)
+        self.att = torch.empty(Mmax * qd, dtype=bf, device=dev)
+        self.o = torch.empty(Mmax * d, dtype=f32, device=dev)
+        self.gu = torch.empty(Mmax * 2 * F, dtype=f32, device=dev)
+        self.a = torch.empty(Mmax * F, dtype=bf, device=dev)
+        self.dn = torch.empty(Mmax * d, dtype=f32, device=dev)
+        Mlog = max(B, B * (gamma + 1))
+        self.logits = torch.empty(Mlog * cfg.vocab, dtype=f32, device=dev)
+        self.Xq = torch.empty(Mmax * Kmax // 2, dtype=torch.uint8, device=dev)
+        self.Xs = torch.empty(Mmax, dtype=f32, device=dev)
+        ws = 1
+        for M in (B, B * (gamma + 1), B * P):
+            for W in [t for L in self.layers for t in L.values()] + [self.lm]:
+                _, _, N, K = W
+                ws = max(ws, b.workspace_bytes(b.OP_GEMM_W4A16, M, N, K),
+                         b.workspace_bytes(b.OP_GEMM_W4A4, M, N, K))
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.wsv = torch.empty(max(1, b.workspace_bytes(b.OP_VERIFY, B, max(gamma, 1), cfg.vocab)),
+                               dtype=torch.uint8, device=dev)
+        # row descriptors and round state
+        self.seq = torch.empty(Mmax, dtype=i32, device=dev)
+        self.pos = torch.empty(Mmax, dtype=i32, device=dev)
+        self.tok = torch.empty(Mmax, dtype=i32, device=dev)
+        self.len = torch.empty(B, dtype=i32, device=dev)
+        self.vtok = torch.zeros(B * (gamma + 1), dtype=i32, device=dev)
+        self.drafts = torch.zeros(B * max(gamma, 1), dtype=i32, device=dev)
+        self.n_acc = torch.zeros(B, dtype=i32, device=dev)
+        self.out_tok = torch.zeros(B * (gamma + 1), dtype=i32, device=dev)
+        self.first = torch.zeros(B, dtype=i32, device=dev)
+        self.gen = torch.zeros((B, max_gen + gamma + 1), dtype=i32, device=dev)
+        self.n_gen = torch.zeros(B, dtype=i32, device=dev)
+        self.stats = torch.zeros(3, dtype=torch.int64, device=dev)
+
+    # ------------------------------------------------------------ one forward
+    def _linear(self, mode, X, W, Y, variant):
+        Wq, Ws, N, K = W
+        M = X.shape[0]
+        if mode == DRAFT:
+            Xq, Xs = _view(self.Xq, M, K // 2), _view(self.Xs, M)
+            b.quant_act(X, Xq, Xs)
+            b.gemm_w4a4(Xq, Xs, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
+        else:
+            b.gemm_w4a16(X, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
+
+    def forward(self, mode, M, variant, last_of=None, trace=None):
+        """rows 0..M-1 described by self.seq/pos/tok; logits of every row (or,
+        with last_of=P, of rows P-1, 2P-1, ...) land in self.logits.  With a
+        list `trace`, copies of every linear layer's input and output are
+        appended as (layer, name, input, output) for op-by-op checks."""
+        cfg = self.cfg
+        d, F = cfg.d, cfg.ffn
+        qd = cfg.n_heads * cfg.head_dim
+        qkv_rows = qd + 2 * cfg.n_kv * cfg.head_dim
+        def lin(li, name, X, W, Y):
+            self._linear(mode, X, W, Y, variant)
+            if trace is not None:
+                trace.append((li, name, X.clone(), Y.clone()))
+
+        x = _view(self.x, M, d)
+        b.embed(self.emb, self.tok[:M], x)
+        add = None
+        for li, L in enumerate(self.layers):
+            h = _view(self.h, M, d)
+            b.add_rmsnorm(x, add, h, cfg.eps)
+            qkv = _view(self.qkv, M, qkv_rows)
+            lin(li, "qkv", h, L["qkv"], qkv)
+            q = _view(self.q, M, qd)
+            b.rope_kv(qkv, self.seq, self.pos, q, self.kc[li], self.vc[li], cfg.n_heads,
+                      cfg.n_kv, cfg.rope_base)
+            att = _view(self.att, M, qd)
+            b.attention(q, self.kc[li], self.vc[li], self.seq, self.pos, att, cfg.n_heads,
+                        cfg.n_kv)
+            o = _view(self.o, M, d)
+            lin(li, "o", att, L["o"], o)
+            b.add_rmsnorm(x, o, h, cfg.eps)
+            gu = _view(self.gu, M, 2 * F)
+            lin(li, "gu", h, L["gu"], gu)
+            a = _view(self.a, M, F)
+            b.silu_mul(gu, a)
+            dn = _view(self.dn, M, d)
+            lin(li, "down", a, L["down"], dn)
+            add = dn
+        if last_of is None:
+            rows, xs, adds = M, x, add
+        else:
+            rows = M // last_of
+            xs, adds = x[last_of - 1::last_of], add[last_of - 1::last_of]
+        hf = _view(self.h, rows, d)
+        b.add_rmsnorm(xs, adds, hf, cfg.eps)
+        logits = _view(self.logits, rows, cfg.vocab)
+        lin(len(self.layers), "lm", hf, self.lm, logits)
+        return logits
+
+    # ------------------------------------------------------------ phases
+    def reset(self):
+        for t in self.kc + self.vc:
+            t.zero_()
+        self.stats.zero_()
+        self.n_gen.zero_()
+        self.gen.zero_()
+        self.vtok.zero_()
+
+    def prefill(self, prompts):
+        """W4A16 over all prompt rows; the first generated token of every
+        sequence is committed (gen, len = P + 1, vtok[:, 0])."""
+        B, P = self.B, self.P
+        pr = torch.as_tensor(np.ascontiguousarray(prompts, dtype=np.int32)).to(self.dev)
+        self.tok[:B * P].copy_(pr.view(-1))
+        self.seq[:B * P].copy_(torch.arange(B, device=self.dev, dtype=torch.int32)
+                               .repeat_interleave(P))
+        self.pos[:B * P].copy_(torch.arange(P, device=self.dev, dtype=torch.int32).repeat(B))
+        logits = self.forward(VERIFY, B * P, b.GEMM_AUTO, last_of=P)
+        b.argmax(logits, self.first)
+        self.len.fill_(P)
+        b.spec_commit(B, 0, None, self.first, self.len, self.vtok, self.gamma + 1, self.gen,
+                      self.n_gen, self.max_gen, self.stats)
+
+    def _round(self):
+        B, g = self.B, self.gamma
+        V = self.cfg.vocab
+        for j in range(g):
+            b.spec_prepare(0, B, g, j, self.len, self.vtok, None, self.seq, self.pos, self.tok)
+            logits = self.forward(DRAFT, B, self.variant)
+            b.argmax(logits, self.vtok[j + 1:], out_stride=g + 1)
+        b.spec_prepare(1, B, g, 0, self.len, self.vtok, self.drafts, self.seq, self.pos, self.tok)
+        logits = self.forward(VERIFY, B * (g + 1), self.variant)
+        b.verify(b.VERIFY_GREEDY, logits.view(B, g + 1, V), self.drafts.view(B, g),
+                 n_accept=self.n_acc, out_tok=self.out_tok.view(B, g + 1), ws=self.wsv)
+        b.spec_commit(B, g, self.n_acc, self.out_tok, self.len, self.vtok, g + 1, self.gen,
+                      self.n_gen, self.max_gen, self.stats)
+
+    def _step(self):
+        """one pure W4A16 greedy decode step (gamma plays no part)"""
+        B = self.B
+        b.spec_prepare(0, B, 0, 0, self.len, self.vtok, None, self.seq, self.pos, self.tok)
+        logits = self.forward(VERIFY, B, self.variant)
+        b.argmax(logits, self.out_tok)
+        b.spec_commit(B, 0, None, self.out_tok, self.len, self.vtok, 1, self.gen, self.n_gen,
+                      self.max_gen, self.stats)
+
+    def _capture(self, fn):
+        s = torch.cuda.Stream(device=self.dev)
+        s.wait_stream(torch.cuda.current_stream(self.dev))
+        torch.cuda.synchronize(self.dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        torch.cuda.synchronize(self.dev)
+        return g
+
+    # ------------------------------------------------------------ loops
+    def run(self, prompts, speculative, use_graph=True, max_rounds=None):
+        """Prefill then decode greedily until every sequence has max_gen
+        tokens.  Returns dict(tokens [B, max_gen] int32 numpy, rounds,
+        accepted, drafted_rows, prefill_s, decode_s)."""
+        if speculative and self.gamma < 1:
+            raise ValueError("speculative decoding needs gamma >= 1")
+        self.reset()
+        fn = self._round if speculative else self._step
+        graph = self._capture(fn) if use_graph else None
+        torch.cuda.synchronize(self.dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self.prefill(prompts)
+        if not speculative:
+            # the pure step keeps each sequence's last token at vtok[b] (row
+            # stride 1); the prefill commit wrote it with the round's stride
+            self.vtok[:self.B].copy_(self.first)
+        e1.record()
+        rounds = 0
+        if speculative:
+            limit = self.max_gen if max_rounds is None else max_rounds
+            while rounds < limit:
+                graph.replay() if graph is not None else fn()
+                rounds += 1
+                if int(self.stats[2].item()) == 0:
+                    break
+        else:
+            for _ in range(self.max_gen - 1):
+                graph.replay() if graph is not None else fn()
+                rounds += 1
+        e2.record()
+        torch.cuda.synchronize(self.dev)
+        st = self.stats.cpu().numpy()
+        return dict(tokens=self.gen[:, :self.max_gen].cpu().numpy(), rounds=rounds,
+                    accepted=int(st[0]), active_rows=int(st[1]),
+                    prefill_s=e0.elapsed_time(e1) / 1e3, decode_s=e1.elapsed_time(e2) / 1e3)

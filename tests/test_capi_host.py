@@ -4,6 +4,7 @@ the documented status codes before touching the device (the pointers passed
 here are never dereferenced)."""
 
 import ctypes
+import glob
 import os
 import re
 
@@ -21,8 +22,10 @@ S = None                           # null stream
 
 
 def declared():
-    txt = open(os.path.join(ROOT, "include", "qspec.h")).read()
-    return sorted(set(re.findall(r"\b(qspec_[a-z0-9_]+)\s*\(", txt)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        names |= set(re.findall(r"\b(qspec_[a-z0-9_]+)\s*\(", open(h).read()))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
@@ -106,3 +109,35 @@ def test_device_check_without_gpu_is_an_error_not_a_crash():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert q.lib().qspec_device_check() in (EHIP, EDEV)
+
+
+def test_harness_validation():
+    L = q.lib()
+    I64, D = ctypes.c_int64, ctypes.c_double
+    # embed: d must be a positive multiple of 8; emb 16-byte aligned
+    assert L.qspec_embed(A, 10, 12, A, 4, A, S) == ESHAPE
+    assert L.qspec_embed(MIS, 10, 16, A, 4, A, S) == EALIGN
+    assert L.qspec_embed(A, 10, 16, NUL, 4, A, S) == ENULL
+    # add_rmsnorm: d <= 4096, stride >= d, add stride >= d when add is given
+    assert L.qspec_add_rmsnorm(A, 8192, NUL, 0, 2, 8192, D(1e-6), A, S) == ESHAPE
+    assert L.qspec_add_rmsnorm(A, 100, NUL, 0, 2, 128, D(1e-6), A, S) == ESHAPE
+    assert L.qspec_add_rmsnorm(A, 128, A, 64, 2, 128, D(1e-6), A, S) == ESHAPE
+    assert L.qspec_add_rmsnorm(A, 128, NUL, 0, 2, 128, D(-1.0), A, S) == ESHAPE
+    # rope_kv / attention: heads, cache capacity
+    assert L.qspec_rope_kv(A, 4, 6, 4, A, A, D(1e4), A, A, A, 2, 64, S) == ESHAPE
+    assert L.qspec_rope_kv(A, 4, 8, 4, A, A, D(1e4), A, A, A, 2, 4000, S) == ESHAPE
+    assert L.qspec_rope_kv(A, 4, 8, 4, A, A, D(0.0), A, A, A, 2, 64, S) == ESHAPE
+    assert L.qspec_attention(A, A, A, 4, 8, 4, A, A, 2, 0, A, S) == ESHAPE
+    assert L.qspec_attention(A, A, A, 4, 8, 3, A, A, 2, 64, A, S) == ESHAPE
+    assert L.qspec_attention(A, A, A, 4, 8, 4, NUL, A, 2, 64, A, S) == ENULL
+    # silu, argmax
+    assert L.qspec_silu_mul(A, 0, 10, A, S) == ESHAPE
+    assert L.qspec_argmax(A, 2, 10, A, 0, S) == ESHAPE
+    # round bookkeeping
+    assert L.qspec_spec_prepare(2, 4, 2, 0, A, A, A, A, A, A, S) == EUNSUP
+    assert L.qspec_spec_prepare(0, 4, 2, 3, A, A, A, A, A, A, S) == ESHAPE
+    assert L.qspec_spec_prepare(1, 4, 0, 0, A, A, A, A, A, A, S) == ESHAPE
+    assert L.qspec_spec_prepare(1, 4, 2, 0, A, A, NUL, A, A, A, S) == ENULL
+    assert L.qspec_spec_commit(4, 17, A, A, A, A, 3, A, 8, A, 5, A, S) == ESHAPE
+    assert L.qspec_spec_commit(4, 2, A, A, A, A, 0, A, 8, A, 5, A, S) == ESHAPE
+    assert L.qspec_spec_commit(4, 2, A, NUL, A, A, 3, A, 8, A, 5, A, S) == ENULL
