@@ -312,6 +312,44 @@ def measure_verify_llama(torch, q, reps=10):
     return out
 
 
+def measure_e2e(torch, B=16, P=128, n_gen=256, gamma=4):
+    """The end-to-end loop: random-init 8-layer d=2048 decoder (16 q / 4 kv
+    heads of 128, SwiGLU 5632, vocabulary 32000) on one shared INT4 buffer,
+    batch 16, 128-token random prompts, 256 generated tokens; greedy
+    self-speculation (W4A4 drafts, gamma 4, W4A16 verify) against pure W4A16
+    greedy decoding of the same model."""
+    import synth
+    from quantization_self_speculation_amd.e2e import Decoder
+    cfg = synth.E2E_MODEL
+    rng = synth.make_rng(4, 0)
+    w = synth.model_weights(rng, cfg)
+    prompts = synth.prompts(rng, B, P, cfg.vocab)
+    dec = Decoder(cfg, w, B, P, n_gen, gamma)
+    del w
+    dec.run(prompts, speculative=True, max_rounds=2)      # warm-up (graph capture, caches)
+    pure = dec.run(prompts, speculative=False)
+    spec = dec.run(prompts, speculative=True)
+    toks = B * n_gen
+    alpha = spec["accepted"] / max(1, gamma * spec["active_rows"])
+    return {
+        "model": "random-init 8L d2048 16q/4kv x128 ffn5632 V32000, shared int4 g128",
+        "batch": B, "prompt": P, "generated": n_gen, "gamma": gamma,
+        "greedy_equal": bool(np.array_equal(spec["tokens"], pure["tokens"])),
+        "acceptance_rate": round(alpha, 4),
+        "tokens_per_round": round((spec["accepted"] + spec["active_rows"]) /
+                                  max(1, spec["active_rows"]), 3),
+        "rounds": spec["rounds"],
+        "selfspec_tok_s": round(toks / spec["decode_s"], 1),
+        "selfspec_tok_s_incl_prefill": round(toks / (spec["decode_s"] + spec["prefill_s"]), 1),
+        "pure_w4a16_tok_s": round(toks / pure["decode_s"], 1),
+        "pure_w4a16_tok_s_incl_prefill": round(toks / (pure["decode_s"] + pure["prefill_s"]), 1),
+        "speedup_vs_pure": round(pure["decode_s"] / spec["decode_s"], 3),
+        "prefill_ms": round(spec["prefill_s"] * 1e3, 3),
+        "pure_ms_per_step": round(pure["decode_s"] * 1e3 / max(1, pure["rounds"]), 4),
+        "selfspec_ms_per_round": round(spec["decode_s"] * 1e3 / max(1, spec["rounds"]), 4),
+    }
+
+
 def _graph_time(torch, fn, reps, launches=3):
     """mean microseconds of fn() over graph replays (launches per replay)"""
     s = torch.cuda.Stream()
@@ -438,6 +476,8 @@ def run(args):
         line["prefill_m2048"] = measure_prefill(torch, q, wl)
         log("verify at batch 32, V=128256")
         line["verify_b32_v128256"] = measure_verify_llama(torch, q)
+        log("end-to-end self-speculative loop")
+        line["e2e_selfspec"] = measure_e2e(torch)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         line["cpu_baseline"] = wl.cpu_baseline()
