@@ -68,12 +68,17 @@ enum { QSPEC_VERIFY_GREEDY = 0, QSPEC_VERIFY_SAMPLE = 1 };
  * the same sequence of operations whatever M is, so row r of Y is bitwise
  * identical at any M; a caller that needs this (for example greedy
  * self-speculation that must reproduce plain verifier decoding token for
- * token) passes the same explicit family for every M.  AUTO picks by M. */
+ * token) passes the same explicit family for every M.  AUTO picks by M and
+ * N: STREAM for M <= 16 when N < 16384 (where SKINNY would split K across
+ * workgroups), else SKINNY up to M = 128, TILED beyond. */
 enum {
   QSPEC_GEMM_AUTO = 0,
   QSPEC_GEMM_GEMV = 1,   /* W4A16 only: VALU GEMV with wavefront reduction   */
   QSPEC_GEMM_SKINNY = 2, /* MFMA, weights streamed once per 64 rows of M     */
-  QSPEC_GEMM_TILED = 3   /* MFMA, LDS-tiled over M and N (prefill shapes)    */
+  QSPEC_GEMM_TILED = 3,  /* MFMA, LDS-tiled over M and N (prefill shapes)    */
+  QSPEC_GEMM_STREAM = 4  /* MFMA, M <= 16: one 16-row weight block per
+                            workgroup, K split across its wavefronts and
+                            reduced in LDS (decode shapes)                  */
 };
 
 #define QSPEC_GROUP 128
@@ -143,7 +148,8 @@ qspec_status qspec_quant_act(const uint16_t* X, int64_t M, int64_t K,
  *   Wq [ceil(N/16)*16][K/2] (tiled), Ws [N][K/128] from qspec_pack_w4.
  *   Y  [M][N] fp32 (out).
  *   P  [M][N][K/128] int32 (out, optional: NULL skips it).
- *   variant: QSPEC_GEMM_AUTO, _SKINNY or _TILED (GEMV is W4A16-only).
+ *   variant: QSPEC_GEMM_AUTO, _SKINNY, _TILED or _STREAM (M <= 16); GEMV is
+ *   W4A16-only.  With P requested, AUTO and STREAM run the SKINNY family.
  *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_GEMM_W4A4,M,N,K)
  *   bytes (NULL allowed when that is 0).
  * ------------------------------------------------------------------------- */
@@ -162,7 +168,7 @@ qspec_status qspec_gemm_w4a4(const uint8_t* Xq, const float* Xs,
  * products for the GEMV family) accumulating each group in fp32, and the
  * fp16 scale applied in fp32 per group.
  *   X  [M][K] bf16 bits (in);  Wq, Ws as above;  Y [M][N] fp32 (out).
- *   variant: QSPEC_GEMM_AUTO, _GEMV, _SKINNY or _TILED.
+ *   variant: QSPEC_GEMM_AUTO, _GEMV, _SKINNY, _TILED or _STREAM (M <= 16).
  *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_GEMM_W4A16,M,N,K).
  * ------------------------------------------------------------------------- */
 qspec_status qspec_gemm_w4a16(const uint16_t* X, const uint8_t* Wq,

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     GEMM_GEMV,
     GEMM_SKINNY,
     GEMM_TILED,
+    GEMM_STREAM,
     VERIFY_GREEDY,
     VERIFY_SAMPLE,
     embed,

@@ -17,7 +17,7 @@ _LIB_PATH = os.path.join(_HERE, "libqspec.so")
 _lock = threading.Lock()
 _lib = None
 
-GEMM_AUTO, GEMM_GEMV, GEMM_SKINNY, GEMM_TILED = 0, 1, 2, 3
+GEMM_AUTO, GEMM_GEMV, GEMM_SKINNY, GEMM_TILED, GEMM_STREAM = 0, 1, 2, 3, 4
 VERIFY_GREEDY, VERIFY_SAMPLE = 0, 1
 OP_GEMM_W4A4, OP_GEMM_W4A16, OP_VERIFY = 1, 2, 3
 GROUP = 128

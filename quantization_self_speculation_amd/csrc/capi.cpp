@@ -102,8 +102,11 @@ qspec_status check_gemm(int64_t M, int64_t N, int64_t K, int group, int variant,
              QSPEC_ERR_SHAPE, "size too large");
   QS_REQUIRE(cdiv(M, 64) <= 65535, QSPEC_ERR_SHAPE, "M too large (at most 65535*64 rows)");
   const bool ok = variant == QSPEC_GEMM_AUTO || variant == QSPEC_GEMM_SKINNY ||
-                  variant == QSPEC_GEMM_TILED || (w4a16 && variant == QSPEC_GEMM_GEMV);
+                  variant == QSPEC_GEMM_TILED || variant == QSPEC_GEMM_STREAM ||
+                  (w4a16 && variant == QSPEC_GEMM_GEMV);
   QS_REQUIRE(ok, QSPEC_ERR_UNSUPPORTED, "unknown variant %d", variant);
+  QS_REQUIRE(variant != QSPEC_GEMM_STREAM || M <= 16, QSPEC_ERR_UNSUPPORTED,
+             "the STREAM family takes M <= 16 (got %lld)", (long long)M);
   return QSPEC_OK;
 }
 

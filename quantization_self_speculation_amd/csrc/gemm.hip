@@ -899,6 +899,196 @@ hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const
 }
 
 // ============================================================================
+// "Stream" family (both modes, M <= 16): the decode shapes, HBM-bound.
+//   * a workgroup = nw wavefronts on ONE 16-row weight block; wavefront w
+//     takes the w-th k-slice of the groups, so the k-split is reduced inside
+//     the workgroup (LDS, fixed order) -- no partials leave the chip;
+//   * nw depends on (N, K) only: about 4096 wavefronts in flight, at most 16
+//     per workgroup, at least 2 groups per slice;
+//   * weights stream HBM -> registers through a PD-deep ring (one flat 1 KiB
+//     tile per wavefront per group); the activation rows and the group scales
+//     come from L2 through a 2-deep ring (every wavefront reads the same few
+//     KiB of activations; buffer loads, so lanes of rows >= M fetch nothing);
+//   * the per-group arithmetic is the skinny family's: W4A16 runs
+//     v_mfma_f32_16x16x32_bf16 on bf16(136 + q) with a -136 constant-operand
+//     chain; W4A4 runs v_mfma_i32_16x16x64_i8 on 16 q; fp32 scale epilogue.
+//   A row's operation order does not depend on M (rows past M are clamped
+//   duplicates whose outputs are not stored).
+// ============================================================================
+struct StreamArgs {
+  const void* X;    // W4A16: bf16 [M][K]; W4A4: packed codes [M][K/2]
+  const float* Xs;  // W4A4: [M]
+  const uint8_t* Wq;
+  const uint16_t* Ws;
+  float* Y;
+  int M, N, K, nrb;
+};
+
+// Ring depth (groups) of the stream kernels: measured on MI355X, a shallow
+// ring (fewer registers, more resident wavefronts) streams faster than a deep
+// one for these shapes.
+#ifndef QSPEC_ST_PD4
+#define QSPEC_ST_PD4 2   // W4A4
+#endif
+#ifndef QSPEC_ST_PD16
+#define QSPEC_ST_PD16 2  // W4A16
+#endif
+#ifndef QSPEC_ST_TARGET
+#define QSPEC_ST_TARGET 4096  // wavefronts the k-split aims for
+#endif
+constexpr int kStreamMaxM = 16;
+constexpr int kStreamMaxW = 16;
+
+// One ring stage: the weight tile slot of this lane, its four group scales
+// and its activation fragment, all for one group.
+template <int MODE>
+struct StreamStage {
+  uint4 w;
+  uint2 s;
+  uint4 x[MODE == kW4A16 ? 4 : 1];
+};
+
+template <int MODE>
+__global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
+  constexpr int PD = MODE == kW4A16 ? QSPEC_ST_PD16 : QSPEC_ST_PD4;
+  extern __shared__ __attribute__((aligned(16))) float red_[];  // [nw][64][4] when nw > 1
+  float(*red)[64][4] = reinterpret_cast<float(*)[64][4]>(red_);
+  const int nw = blockDim.x >> 6;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int rb = blockIdx.x;
+  const int M = a.M, K = a.K, G = K / kGroup;
+  const int gps = (G + nw - 1) / nw;
+  const int g0 = min(G, w * gps), g1 = min(G, g0 + gps);
+  const int gl = min(G - 1, max(g0, g1 - 1));  // clamp target: a valid group (empty slices too)
+
+  const uint8_t* wt = a.Wq + (int64_t)rb * G * 1024 + lane * 16;
+  const uint16_t* sc = a.Ws + (int64_t)rb * G * 16 + lg * 4;
+  // activation rows through a buffer resource: lanes of rows >= M read an
+  // out-of-range offset, which returns zeros without a memory access
+  const int xrow_bytes = MODE == kW4A16 ? K * 2 : K / 2;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.X), (short)0, M * xrow_bytes, 0x00020000);
+  const uint32_t xoff0 = (l16 < M ? (uint32_t)(l16 * xrow_bytes) : 0x80000000u) +
+                         (uint32_t)(lg * (MODE == kW4A16 ? 64 : 16));
+  constexpr int xgb = MODE == kW4A16 ? kGroup * 2 : kGroup / 2;  // activation bytes per group
+
+  auto load = [&](StreamStage<MODE>& st, int g) {
+    const int gg = min(g, gl);
+    st.w = ld_stream(wt + (int64_t)gg * 1024);
+    st.s = *reinterpret_cast<const uint2*>(sc + (int64_t)gg * 16);
+    const uint32_t o = xoff0 + (uint32_t)(gg * xgb);
+#pragma unroll
+    for (int i = 0; i < (MODE == kW4A16 ? 4 : 1); ++i) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, o + 16 * i, 0, 0);
+      st.x[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  };
+
+  v4f tot = {0.f, 0.f, 0.f, 0.f};
+  StreamStage<MODE> ring[PD];
+#pragma unroll
+  for (int i = 0; i < PD; ++i) load(ring[i], g0 + i);
+  const v8bf negb = as_v8bf(kNegBiasPair, kNegBiasPair, kNegBiasPair, kNegBiasPair);
+
+  for (int gb = g0; gb < g1; gb += PD) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) {
+      const int g = gb + i;
+      const StreamStage<MODE>& st = ring[i];
+      const uint32_t s01 = st.s.x, s23 = st.s.y;
+      if (MODE == kW4A16) {
+        // bf16(136 + q) x activations, then the -136 chain into the same
+        // accumulator: acc = sum_k x (136 + q) - 136 sum_k x
+        const uint32_t wv[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        v8bf B[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t aw[4], xi[4];
+          const uint32_t xw[4] = {st.x[j].x, st.x[j].y, st.x[j].z, st.x[j].w};
+          w4_to_bf16_biased(wv[j], aw);
+          bf16x8_interleave(xw, xi);
+          B[j] = as_v8bf(xi[0], xi[1], xi[2], xi[3]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(aw[0], aw[1], aw[2], aw[3]), B[j],
+                                                        acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(negb, B[j], acc, 0, 0, 0);
+        if (g < g1) {
+          tot[0] = fmaf(half_bits_to_float((uint16_t)(s01 & 0xFFFF)), acc[0], tot[0]);
+          tot[1] = fmaf(half_bits_to_float((uint16_t)(s01 >> 16)), acc[1], tot[1]);
+          tot[2] = fmaf(half_bits_to_float((uint16_t)(s23 & 0xFFFF)), acc[2], tot[2]);
+          tot[3] = fmaf(half_bits_to_float((uint16_t)(s23 >> 16)), acc[3], tot[3]);
+        }
+      } else {
+        const uint4 p = st.w, x = st.x[0];
+        const v4i a0 = {(int)w4_lo_x16(p.x), (int)w4_hi_x16(p.x), (int)w4_lo_x16(p.y), (int)w4_hi_x16(p.y)};
+        const v4i a1 = {(int)w4_lo_x16(p.z), (int)w4_hi_x16(p.z), (int)w4_lo_x16(p.w), (int)w4_hi_x16(p.w)};
+        const v4i b0 = {(int)w4_lo_x16(x.x), (int)w4_hi_x16(x.x), (int)w4_lo_x16(x.y), (int)w4_hi_x16(x.y)};
+        const v4i b1 = {(int)w4_lo_x16(x.z), (int)w4_hi_x16(x.z), (int)w4_lo_x16(x.w), (int)w4_hi_x16(x.w)};
+        v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
+        if (g < g1) {
+          tot[0] = fmaf(half_bits_to_float((uint16_t)(s01 & 0xFFFF)) * 0.00390625f, (float)acc[0], tot[0]);
+          tot[1] = fmaf(half_bits_to_float((uint16_t)(s01 >> 16)) * 0.00390625f, (float)acc[1], tot[1]);
+          tot[2] = fmaf(half_bits_to_float((uint16_t)(s23 & 0xFFFF)) * 0.00390625f, (float)acc[2], tot[2]);
+          tot[3] = fmaf(half_bits_to_float((uint16_t)(s23 >> 16)) * 0.00390625f, (float)acc[3], tot[3]);
+        }
+      }
+      load(ring[i], g + PD);  // refill this stage, PD groups ahead
+    }
+  }
+
+  // k-slices -> one sum per output, in slice order
+  if (nw > 1) {
+    *reinterpret_cast<v4f*>(&red[w][lane][0]) = tot;
+    __syncthreads();
+    if (w != 0) return;
+    tot = *reinterpret_cast<const v4f*>(&red[0][lane][0]);
+    for (int j = 1; j < nw; ++j) {
+      const v4f t = *reinterpret_cast<const v4f*>(&red[j][lane][0]);
+      tot[0] += t[0];
+      tot[1] += t[1];
+      tot[2] += t[2];
+      tot[3] += t[3];
+    }
+  }
+  if (l16 >= M) return;
+  const int n = rb * 16 + lg * 4;
+  const int N = a.N;
+  if (n >= N) return;
+  float xs = 1.f;
+  if (MODE == kW4A4) xs = a.Xs[l16];
+  float* dst = a.Y + (int64_t)l16 * N + n;
+  if ((N & 3) == 0) {
+    *reinterpret_cast<float4*>(dst) = make_float4(xs * tot[0], xs * tot[1], xs * tot[2], xs * tot[3]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) dst[r] = xs * tot[r];
+  }
+}
+
+int stream_waves(int64_t N, int64_t K) {
+  const int64_t nrb = cdiv(N, 16), G = K / kGroup;
+  int nw = 1;
+  while (nw < kStreamMaxW && nrb * nw < QSPEC_ST_TARGET && G / (2 * nw) >= 2) nw *= 2;
+  return nw;
+}
+
+template <int MODE>
+hipError_t launch_stream(const void* X, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
+                         int64_t M, int64_t N, int64_t K, float* Y, hipStream_t s) {
+  StreamArgs a{X, Xs, Wq, Ws, Y, (int)M, (int)N, (int)K, (int)cdiv(N, 16)};
+  const int nw = stream_waves(N, K);
+  const size_t lds = nw > 1 ? (size_t)nw * 64 * 4 * sizeof(float) : 0;
+  hipLaunchKernelGGL(stream_kernel<MODE>, dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+  return hipGetLastError();
+}
+
+// ============================================================================
 // W4A16 GEMV family (M <= 4 per launch): VALU dot products, no MFMA.
 //   * a wavefront owns one 16-row block for a k-slice of up to 32 groups;
 //     lane l reads the tile slot of row l%16, codes 32*(l/16) .. +32 of each
@@ -1100,13 +1290,19 @@ GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K / kGroup, kGemvGroup
 
 // AUTO: GEMV for one or two rows, the skinny MFMA family up to 128 rows,
 // the tiled family beyond
-int w4a16_pick(int variant, int64_t M) {
-  if (variant != QSPEC_GEMM_AUTO) return variant;
-  return M <= 2 ? QSPEC_GEMM_GEMV : M <= 128 ? QSPEC_GEMM_SKINNY : QSPEC_GEMM_TILED;
-}
-int w4a4_pick(int variant, int64_t M) {
-  if (variant != QSPEC_GEMM_AUTO) return variant;
+// AUTO: for M <= 16 the stream family where the skinny family would have to
+// split K across workgroups (fewer than QSPEC_SK_TARGET_WG 64-row tiles),
+// the skinny family otherwise and up to 128 rows, the tiled family beyond.
+// The choice depends on M and N only.
+int auto_pick(int64_t M, int64_t N) {
+  if (M <= kStreamMaxM && cdiv(N, 64) < QSPEC_SK_TARGET_WG) return QSPEC_GEMM_STREAM;
   return M <= 128 ? QSPEC_GEMM_SKINNY : QSPEC_GEMM_TILED;
+}
+int w4a16_pick(int variant, int64_t M, int64_t N) {
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N);
+}
+int w4a4_pick(int variant, int64_t M, int64_t N) {
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N);
 }
 
 hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* Xs, float* Y,
@@ -1131,7 +1327,8 @@ size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
                         int64_t N, int64_t K, int variant, float* Y, void* ws, hipStream_t s) {
-  const int v = w4a16_pick(variant, M);
+  const int v = w4a16_pick(variant, M, N);
+  if (v == QSPEC_GEMM_STREAM) return launch_stream<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, s);
   if (v == QSPEC_GEMM_GEMV) {
     const GemvPlan q = plan_gemv(K);
     // rows of X in chunks of up to 4
@@ -1179,8 +1376,11 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
                        void* ws, hipStream_t s) {
   // the int32 partials output is a check path served by the skinny family
-  if (w4a4_pick(variant, M) == QSPEC_GEMM_TILED && P == nullptr)
+  const int v = w4a4_pick(variant, M, N);
+  if (v == QSPEC_GEMM_TILED && P == nullptr)
     return launch_tiled<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, s);
+  if (v == QSPEC_GEMM_STREAM && P == nullptr)
+    return launch_stream<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, s);
   const SkinnyPlan p = plan_skinny(1, M, N, K);
   SkinnyArgs a{};
   a.X = Xq;

@@ -141,3 +141,11 @@ def test_harness_validation():
     assert L.qspec_spec_commit(4, 17, A, A, A, A, 3, A, 8, A, 5, A, S) == ESHAPE
     assert L.qspec_spec_commit(4, 2, A, A, A, A, 0, A, 8, A, 5, A, S) == ESHAPE
     assert L.qspec_spec_commit(4, 2, A, NUL, A, A, 3, A, 8, A, 5, A, S) == ENULL
+
+
+def test_stream_variant_limits():
+    L = q.lib()
+    # the STREAM family (variant 4) takes at most 16 rows
+    assert L.qspec_gemm_w4a16(A, A, A, 17, 64, 256, 128, 4, A, NUL, 0, S) == EUNSUP
+    assert L.qspec_gemm_w4a4(A, A, A, A, 17, 64, 256, 128, 4, A, NUL, NUL, 0, S) == EUNSUP
+    assert L.qspec_gemm_w4a16(A, A, A, 4, 64, 256, 128, 5, A, NUL, 0, S) == EUNSUP

@@ -16,8 +16,9 @@ from gpu_util import (assert_close, dev, dev_bf16, dev_f16, host, host_bits16, s
 
 pytestmark = pytest.mark.gpu
 
-W4A16_VARIANTS = [q.GEMM_AUTO, q.GEMM_GEMV, q.GEMM_SKINNY, q.GEMM_TILED]
-W4A4_VARIANTS = [q.GEMM_AUTO, q.GEMM_SKINNY, q.GEMM_TILED]
+W4A16_VARIANTS = [q.GEMM_AUTO, q.GEMM_GEMV, q.GEMM_SKINNY, q.GEMM_TILED, q.GEMM_STREAM]
+W4A4_VARIANTS = [q.GEMM_AUTO, q.GEMM_SKINNY, q.GEMM_TILED, q.GEMM_STREAM]
+STREAM_MAX_M = 16   # the STREAM family takes M <= 16
 
 # (M, N, K): the small single-layer case, ragged tails in M and N, odd group
 # counts, several m-chunks and split-K shapes
@@ -30,7 +31,14 @@ SHAPES = [
     (70, 130, 640),
     (3, 4608, 3584),
     (300, 600, 1152),
+    (16, 3584, 18944),
+    (11, 200, 2688),
 ]
+
+
+def _cases(variants):
+    return [(M, N, K, v) for (M, N, K) in SHAPES for v in variants
+            if v != q.GEMM_STREAM or M <= STREAM_MAX_M]
 
 
 def dev_w(Wq):
@@ -121,8 +129,7 @@ def test_quant_act_hand_ties_subnormal_and_division(golden):
 
 
 # ------------------------------------------------------------------ W4A4
-@pytest.mark.parametrize("variant", W4A4_VARIANTS)
-@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("M,N,K,variant", _cases(W4A4_VARIANTS))
 def test_w4a4_parity(M, N, K, variant):
     say(f"w4a4 M={M} N={N} K={K} variant={variant}")
     W, X = _case(12, M, N, K)
@@ -151,8 +158,7 @@ def test_w4a4_gpu_quantized_chain():
 
 
 # ------------------------------------------------------------------ W4A16
-@pytest.mark.parametrize("variant", W4A16_VARIANTS)
-@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("M,N,K,variant", _cases(W4A16_VARIANTS))
 def test_w4a16_parity(M, N, K, variant):
     say(f"w4a16 M={M} N={N} K={K} variant={variant}")
     W, X = _case(14, M, N, K)
@@ -183,6 +189,27 @@ def test_w4a16_zero_and_lossless_rows():
 
 
 # ------------------------------------------------------------------ invariance
+def test_stream_row_invariance_both_modes():
+    """STREAM family: rows bitwise identical at M = 16, 5 and 1 (a k-split of
+    up to 16 wavefronts reduced in LDS in fixed order)."""
+    N, K = 1000, 18944
+    W, X = _case(19, 16, N, K)
+    Wq, Ws = oracle.pack_w4(W)
+    Xq, Xs = oracle.quant_act(X)
+    Wq_d, Ws_d = dev_w(Wq), dev_s(Ws)
+    V = q.GEMM_STREAM
+    Y16 = host(q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=V, N=N))
+    Z16 = host(q.gemm_w4a4(dev(Xq), dev(Xs), Wq_d, Ws_d, variant=V, N=N))
+    for lo, hi in ((0, 5), (9, 10), (15, 16)):
+        Y = host(q.gemm_w4a16(dev_bf16(X[lo:hi].copy()), Wq_d, Ws_d, variant=V, N=N))
+        Z = host(q.gemm_w4a4(dev(Xq[lo:hi].copy()), dev(Xs[lo:hi].copy()), Wq_d, Ws_d,
+                             variant=V, N=N))
+        assert np.array_equal(Y16[lo:hi].view(np.uint32), Y.view(np.uint32)), (lo, hi)
+        assert np.array_equal(Z16[lo:hi].view(np.uint32), Z.view(np.uint32)), (lo, hi)
+    assert_close(Y16, oracle.gemm_w4a16(X, Wq, Ws))
+    assert_close(Z16, oracle.gemm_w4a4(Xq, Xs, Wq, Ws))
+
+
 @pytest.mark.parametrize("variant", [q.GEMM_GEMV, q.GEMM_SKINNY, q.GEMM_TILED])
 def test_w4a16_row_invariance(variant):
     """Within one kernel family row r of Y is bitwise identical at any M."""
