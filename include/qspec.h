@@ -82,6 +82,7 @@ enum {
 };
 
 #define QSPEC_GROUP 128
+#define QSPEC_MAX_K (1 << 20) /* K: a multiple of 128 in [128, 2^20] */
 #define QSPEC_MAX_GAMMA 16
 
 const char* qspec_status_str(qspec_status s);
@@ -108,7 +109,7 @@ size_t qspec_workspace_bytes(int op, int64_t a, int64_t b, int64_t c);
  * group j of 128 consecutive k,
  *     a = max|W[n,k]|;  s = fp16(a / 7.0f)  (IEEE fp32 divide, then RNE);
  *     q[n,k] = clamp(rne(W[n,k] / float(s)), -8, 7), all 0 when s == 0.
- *   W   [N][K] fp32 (in).   N >= 1, K >= 128, K % 128 == 0.
+ *   W   [N][K] fp32 (in).   N >= 1, K % 128 == 0, 128 <= K <= QSPEC_MAX_K.
  *   Wq  [Np][K/2] u8 (out), Np = ceil(N/16)*16: the codes in the tiled
  *       storage order both GEMMs read.  Codes pack two per byte, code 2i of a
  *       row in bits 0-3 and code 2i+1 in bits 4-7 (two's complement); the
@@ -131,7 +132,7 @@ qspec_status qspec_pack_w4(const float* W, int64_t N, int64_t K, int group,
  * Reading: per row m, a = max_k |x|, s = a / 7.0f kept in fp32, and
  * q = clamp(rne(x / s), -8, 7) with an IEEE fp32 divide (not a reciprocal
  * multiply), all codes 0 when a == 0; subnormals are kept.
- *   X   [M][K] bf16 bits (in).  M >= 1, K >= 128, K % 128 == 0.
+ *   X   [M][K] bf16 bits (in).  M >= 1, K % 128 == 0, 128 <= K <= QSPEC_MAX_K.
  *   Xq  [M][K/2] u8 (out), same nibble layout as Wq.
  *   Xs  [M] fp32 (out).
  * ------------------------------------------------------------------------- */

@@ -87,8 +87,8 @@ qspec_status check_ptr(const void* p, const char* name) {
 #define QS_PTR(p) QS_TRY(check_ptr((p), #p))
 
 qspec_status check_k(int64_t K) {
-  QS_REQUIRE(K >= QSPEC_GROUP && K % QSPEC_GROUP == 0 && K <= ((int64_t)1 << 26), QSPEC_ERR_SHAPE,
-             "K must be a multiple of 128 in [128, 2^26] (got %lld)", (long long)K);
+  QS_REQUIRE(K >= QSPEC_GROUP && K % QSPEC_GROUP == 0 && K <= QSPEC_MAX_K, QSPEC_ERR_SHAPE,
+             "K must be a multiple of 128 in [128, %d] (got %lld)", QSPEC_MAX_K, (long long)K);
   return QSPEC_OK;
 }
 

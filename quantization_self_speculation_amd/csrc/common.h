@@ -39,11 +39,14 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // 0x4300 | u is the bf16 of 128 + u, and u = q + 8 is the nibble with its
 // sign bit flipped, so every value is exact.
 __device__ __forceinline__ void w4_to_bf16_biased(uint32_t p, uint32_t o[4]) {
-  const uint32_t x = p ^ 0x88888888u;
-  o[0] = (x & 0x000F000Fu) | 0x43004300u;
-  o[1] = ((x >> 4) & 0x000F000Fu) | 0x43004300u;
-  o[2] = ((x >> 8) & 0x000F000Fu) | 0x43004300u;
-  o[3] = ((x >> 12) & 0x000F000Fu) | 0x43004300u;
+  // nibble pair (k_j, k_{j+4}) masked into bits 0-3 / 16-19, then one XOR
+  // flips the nibble sign bits (u = q + 8) and sets the 0x43 high bytes
+  // (the compiler fuses each mask-and-XOR into one v_bitop3_b32)
+  constexpr uint32_t mask = 0x000F000Fu, bias = 0x43084308u;
+  o[0] = (p & mask) ^ bias;
+  o[1] = ((p >> 4) & mask) ^ bias;
+  o[2] = ((p >> 8) & mask) ^ bias;
+  o[3] = ((p >> 12) & mask) ^ bias;
 }
 constexpr float kW4Bias = 136.0f;
 

@@ -293,27 +293,32 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
 
   uint4 xr[XPT];
   uint16_t sr[SPT];
-  // every load below is unconditional: rows past M and groups past the
-  // slice read clamped (valid) addresses; their results are never used
-  // (rows past M are not stored, groups past the slice are skipped)
+  // every load below is unconditional: groups past the slice read clamped
+  // (valid) addresses whose results are never used; the activation rows go
+  // through a buffer resource over this m-chunk's rows, and rows past M read
+  // an out-of-range offset (zeros, no memory access)
+  const int xrb = MODE == kW4A16 ? K * 2 : K / 2;  // activation row bytes
+  const int mrows = min(ROWS, M - m0);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(a.X) + (int64_t)m0 * xrb), (short)0,
+      mrows * xrb, 0x00020000);
   auto x_load = [&](int c) {
     const int gc = g_begin + c * CH;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = min((int)threadIdx.x + 256 * i, XCH - 1);
+      uint32_t off;
       if (MODE == kW4A16) {
         const int r = idx / (CH * 16), cc = idx % (CH * 16);
-        xr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.X) +
-                                                (int64_t)min(m0 + r, M - 1) * K +
-                                                (int64_t)min(gc + (cc >> 4), G - 1) * kGroup +
-                                                (cc & 15) * 8);
+        off = r < mrows ? (uint32_t)(r * xrb + min(gc + (cc >> 4), G - 1) * (kGroup * 2) + (cc & 15) * 16)
+                        : 0x80000000u;
       } else {
         const int r = idx / (CH * 4), cc = idx % (CH * 4);
-        xr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.X) +
-                                                (int64_t)min(m0 + r, M - 1) * (K / 2) +
-                                                (int64_t)min(gc + (cc >> 2), G - 1) * 64 +
-                                                (cc & 3) * 16);
+        off = r < mrows ? (uint32_t)(r * xrb + min(gc + (cc >> 2), G - 1) * 64 + (cc & 3) * 16)
+                        : 0x80000000u;
       }
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0);
+      xr[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
@@ -406,9 +411,15 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
             for (int mb = 0; mb < MB; ++mb)
               acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[mb], acc[nb][mb], 0, 0, 0);
           }
+          // with one weight block the bias chain runs into the same
+          // accumulator; with several it is shared and added per group
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            corr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cneg, bv[mb], corr[mb], 0, 0, 0);
+          for (int mb = 0; mb < MB; ++mb) {
+            if (NB == 1)
+              acc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cneg, bv[mb], acc[0][mb], 0, 0, 0);
+            else
+              corr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cneg, bv[mb], corr[mb], 0, 0, 0);
+          }
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -417,7 +428,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              tot[nb][mb][r] = fmaf(half_bits_to_float(wp[r]), acc[nb][mb][r] + corr[mb][r],
+              tot[nb][mb][r] = fmaf(half_bits_to_float(wp[r]),
+                                    NB == 1 ? acc[nb][mb][r] : acc[nb][mb][r] + corr[mb][r],
                                     tot[nb][mb][r]);
         }
       } else {
