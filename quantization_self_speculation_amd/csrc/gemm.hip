@@ -66,6 +66,16 @@
 #define QSPEC_SK_TARGET_WG 256
 #endif
 
+// wavefronts per SIMD the register budget of a skinny instantiation must
+// allow (the most that compiles without spills)
+constexpr int skinny_wpe(int mode, int mb) {
+#ifdef QSPEC_SK_NO_WPE
+  return 1;
+#else
+  return mb <= 2 ? 4 : (mode == 0 && mb == 3) ? 3 : 2;
+#endif
+}
+
 
 namespace qspec {
 namespace {
@@ -253,7 +263,7 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
 // weight ring stays in flight across waits; only the arithmetic of groups past
 // the end of the slice is skipped (a branch uniform over the workgroup).
 template <int MODE, int MB, int NB, int CH, int PD, bool WITHP>
-__global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(skinny_wpe(MODE, MB)))) void skinny_kernel(const SkinnyArgs a) {
   static_assert(PD % CH == 0, "prefetch depth must be a multiple of the chunk");
   constexpr int ROWS = 16 * MB;      // activation rows of an m-chunk
   constexpr int WROWS = 64 * NB;     // weight rows of a tile (4 wavefronts x NB blocks of 16)
