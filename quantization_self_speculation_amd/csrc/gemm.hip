@@ -753,16 +753,25 @@ __global__ __launch_bounds__(256, MODE == kW4A16 ? 1 : 2) void tiled_kernel(cons
 }
 
 // ----------------------------------------------------------------------------
-// W4A4 prefill kernel: 8 wavefronts (4 along n x 2 along m) = a 256 (n) x
-// 128 (m) tile, 64 x 64 per wavefront.  Both operands are staged per group in
-// LDS already widened to int8 (16 q, the MFMA slot order), so each code is
-// unpacked once per workgroup; the group's scales sit in LDS as fp32 / 256.
-// Rows are padded to 144 bytes: the 16 rows a ds_read_b128 touches cover all
-// 64 banks once.  The next group's global loads are issued before the current
-// group's MFMAs and land in the other LDS buffer after them.
+// W4A4 prefill kernel: WN x WM wavefronts, each owning a 64 (n) x 64 (m)
+// output block, so a workgroup computes a BN = 64 WN by BM = 64 WM tile.
+// Both operands are staged per group in LDS already widened to int8 (16 q,
+// the MFMA slot order), so each code is unpacked once per workgroup; the
+// group's scales sit in LDS as fp32 / 256.  LDS rows are RST bytes apart.
+// Two register stages keep the global loads of groups g+1 and g+2 in flight
+// while group g is computed; LDS is double-buffered with one barrier per
+// group.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(512, 1) void w4a4_prefill_kernel(const TiledArgs a) {
-  constexpr int BN = 256, BM = 128, RST = 144;
+#ifndef QSPEC_PF_SHAPE
+#define QSPEC_PF_SHAPE 4, 2, 160  // WN, WM, RST (measured on MI355X)
+#endif
+
+template <int WN, int WM, int RST>
+__global__ __launch_bounds__(64 * WN * WM, (WN * WM <= 4) ? 2 : 1) void w4a4_prefill_kernel(
+    const TiledArgs a) {
+  constexpr int BN = 64 * WN, BM = 64 * WM, NT = 64 * WN * WM;
+  constexpr int AC = BN * 4 / NT, BC = BM * 4 / NT;  // 16-byte chunks per thread
+  static_assert(AC * NT == BN * 4 && BC * NT == BM * 4 && NT >= BN, "staging split");
   __shared__ __attribute__((aligned(16))) uint8_t As[2][BN * RST];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BM * RST];
   __shared__ __attribute__((aligned(16))) float Ss[2][BN];
@@ -776,40 +785,45 @@ __global__ __launch_bounds__(512, 1) void w4a4_prefill_kernel(const TiledArgs a)
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int wn = wave & 3, wm = wave >> 2;
+  const int wn = wave % WN, wm = wave / WN;
   const int nrb = (N + 15) / 16;
   const int rb0 = nt * (BN / 16);
   const int m0 = mt * BM;
 
-  // staging assignment: A = 1024 16-byte chunks (2 per thread), B = 512 (1
-  // per thread), scales = 256 (threads 0..255)
-  const uint8_t* asrc[2];
-  int adst[2];
+  // staging: A chunk c = (row block c/64, tile slot c%64); B chunk c = (row
+  // c/4, 16 packed bytes c%4 of the group); scale of tile row tid % BN
+  const uint8_t* asrc[AC];
+  int adst[AC];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 512 * i;
+  for (int i = 0; i < AC; ++i) {
+    const int c = tid + NT * i;
     const int rbl = c >> 6, slot = c & 63;
     asrc[i] = a.Wq + (int64_t)min(rb0 + rbl, nrb - 1) * G * 1024 + slot * 16;
     adst[i] = (rbl * 16 + (slot & 15)) * RST + (slot >> 4) * 32;
   }
-  const uint8_t* bsrc = static_cast<const uint8_t*>(a.X) +
-                        (int64_t)min(m0 + (tid >> 2), M - 1) * (K / 2) + (tid & 3) * 16;
-  const int bdst = (tid >> 2) * RST + (tid & 3) * 32;
-  const uint16_t* ssrc =
-      a.Ws + (int64_t)min(rb0 + ((tid & 255) >> 4), nrb - 1) * G * 16 + (tid & 15);
+  const uint8_t* bsrc[BC];
+  int bdst[BC];
+#pragma unroll
+  for (int i = 0; i < BC; ++i) {
+    const int c = tid + NT * i;
+    bsrc[i] = static_cast<const uint8_t*>(a.X) + (int64_t)min(m0 + (c >> 2), M - 1) * (K / 2) +
+              (c & 3) * 16;
+    bdst[i] = (c >> 2) * RST + (c & 3) * 32;
+  }
+  const int srow = tid % BN;
+  const uint16_t* ssrc = a.Ws + (int64_t)min(rb0 + (srow >> 4), nrb - 1) * G * 16 + (srow & 15);
 
-  // two register stages: the loads of group g+2 are issued right after the
-  // barrier that ends group g and are consumed two compute phases later
   struct Stage {
-    uint4 a0, a1, b;
+    uint4 a[AC], b[BC];
     uint32_t s;
   };
   Stage st0, st1;
   auto gload = [&](Stage& st, int g) {
     const int gg = min(g, G - 1);
-    st.a0 = ld_stream(asrc[0] + (int64_t)gg * 1024);
-    st.a1 = ld_stream(asrc[1] + (int64_t)gg * 1024);
-    st.b = *reinterpret_cast<const uint4*>(bsrc + (int64_t)gg * 64);
+#pragma unroll
+    for (int i = 0; i < AC; ++i) st.a[i] = ld_stream(asrc[i] + (int64_t)gg * 1024);
+#pragma unroll
+    for (int i = 0; i < BC; ++i) st.b[i] = *reinterpret_cast<const uint4*>(bsrc[i] + (int64_t)gg * 64);
     st.s = ssrc[(int64_t)gg * 16];
   };
   auto widen_store = [&](uint8_t* dst, const uint4 p) {
@@ -819,11 +833,12 @@ __global__ __launch_bounds__(512, 1) void w4a4_prefill_kernel(const TiledArgs a)
         make_uint4(w4_lo_x16(p.z), w4_hi_x16(p.z), w4_lo_x16(p.w), w4_hi_x16(p.w));
   };
   auto lstore = [&](const Stage& st, int buf) {
-    widen_store(&As[buf][adst[0]], st.a0);
-    widen_store(&As[buf][adst[1]], st.a1);
-    widen_store(&Bs[buf][bdst], st.b);
-    // threads t and t + 256 write the same value: no branch, no sunk load
-    Ss[buf][tid & 255] = half_bits_to_float((uint16_t)st.s) * 0.00390625f;  // / 256
+#pragma unroll
+    for (int i = 0; i < AC; ++i) widen_store(&As[buf][adst[i]], st.a[i]);
+#pragma unroll
+    for (int i = 0; i < BC; ++i) widen_store(&Bs[buf][bdst[i]], st.b[i]);
+    // threads sharing a tile row write the same value: no branch, no sunk load
+    Ss[buf][srow] = half_bits_to_float((uint16_t)st.s) * 0.00390625f;  // / 256
   };
 
   v4f tot[4][4];
@@ -905,6 +920,16 @@ __global__ __launch_bounds__(512, 1) void w4a4_prefill_kernel(const TiledArgs a)
     }
 }
 
+template <int WN, int WM, int RST>
+hipError_t launch_w4a4_prefill(TiledArgs a, hipStream_t s) {
+  a.ntn = (int)cdiv(a.N, 64 * WN);
+  a.ntm = (int)cdiv(a.M, 64 * WM);
+  const int64_t blocks = 8 * cdiv(a.ntn, 8) * a.ntm;
+  hipLaunchKernelGGL((w4a4_prefill_kernel<WN, WM, RST>), dim3((unsigned)blocks),
+                     dim3(64 * WN * WM), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                         int64_t M, int64_t N, int64_t K, float* Y, hipStream_t s) {
@@ -913,9 +938,7 @@ hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const
   if (MODE == kW4A16) {
     hipLaunchKernelGGL((tiled_kernel<kW4A16, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   } else {
-    a.ntn = (int)cdiv(N, 256);
-    const int64_t b4 = 8 * cdiv(a.ntn, 8) * a.ntm;
-    hipLaunchKernelGGL(w4a4_prefill_kernel, dim3((unsigned)b4), dim3(512), 0, s, a);
+    return launch_w4a4_prefill<QSPEC_PF_SHAPE>(a, s);
   }
   return hipGetLastError();
 }
