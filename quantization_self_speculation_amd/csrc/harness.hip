@@ -84,20 +84,28 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
   float* xr = x + m * xs;
   float v[kNormPer];
   double ss = 0.0;
+  // all loads first (independent), then the residual update and the sum
 #pragma unroll
   for (int i = 0; i < kNormPer; ++i) {
     const int j = threadIdx.x + 256 * i;
-    v[i] = 0.f;
-    if (j < d) {
-      float t = xr[j];
-      if (add != nullptr) {
-        t = t + add[m * as + j];
-        xr[j] = t;
-      }
-      v[i] = t;
-      ss += (double)t * (double)t;
+    v[i] = j < d ? xr[j] : 0.f;
+  }
+  if (add != nullptr) {
+    float ad[kNormPer];
+#pragma unroll
+    for (int i = 0; i < kNormPer; ++i) {
+      const int j = threadIdx.x + 256 * i;
+      ad[i] = j < d ? add[m * as + j] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kNormPer; ++i) {
+      const int j = threadIdx.x + 256 * i;
+      v[i] = v[i] + ad[i];
+      if (j < d) xr[j] = v[i];
     }
   }
+#pragma unroll
+  for (int i = 0; i < kNormPer; ++i) ss += (double)v[i] * (double)v[i];
   ss = block_sum_256(ss, red);
   const double den = sqrt(ss / (double)d + eps);
   uint16_t* yr = y + m * d;
@@ -228,9 +236,22 @@ __global__ __launch_bounds__(256) void attention_kernel(const float* __restrict_
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float o0 = 0.f, o1 = 0.f;
-    for (int t = 0; t < T; ++t) {
+    const uint32_t* vcol = reinterpret_cast<const uint32_t*>(Vv) + lane;  // dims 2l, 2l+1
+    int t = 0;
+    for (; t + 32 <= T; t += 32) {  // 32 value rows in flight, added in order
+      uint32_t vv[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) vv[i] = vcol[(int64_t)(t + i) * (kHeadDim / 2)];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float pt = sc[t + i];
+        o0 = fmaf(pt, __uint_as_float(vv[i] << 16), o0);
+        o1 = fmaf(pt, __uint_as_float(vv[i] & 0xFFFF0000u), o1);
+      }
+    }
+    for (; t < T; ++t) {
       const float pt = sc[t];
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(Vv + (int64_t)t * kHeadDim + 2 * lane);
+      const uint32_t vv = vcol[(int64_t)t * (kHeadDim / 2)];
       o0 = fmaf(pt, __uint_as_float(vv << 16), o0);
       o1 = fmaf(pt, __uint_as_float(vv & 0xFFFF0000u), o1);
     }
@@ -264,7 +285,19 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ x
   const float* r = x + m * V;
   float best = -INFINITY;
   int idx = 0x7FFFFFFF;
-  for (int64_t j = threadIdx.x; j < V; j += 256) {
+  int64_t j = threadIdx.x;
+  for (; j + 3 * 256 < V; j += 4 * 256) {  // four loads in flight, compared in index order
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = r[j + 256 * i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (v[i] > best) {
+        best = v[i];
+        idx = (int)(j + 256 * i);
+      }
+  }
+  for (; j < V; j += 256) {
     const float v = r[j];
     if (v > best) {
       best = v;
