@@ -30,6 +30,7 @@
 //    and slices are reduced in fixed order -- no atomics -- so an output row
 //    is bitwise the same for every M.
 #include <atomic>
+#include <type_traits>
 
 #include "launch.h"
 
@@ -502,7 +503,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(skinny_wpe(
 }
 
 // ============================================================================
-// MFMA "tiled" family (both modes): the prefill shapes, compute-bound.
+// MFMA "tiled" family: the prefill shapes, compute-bound.  W4A16 runs the
+// kernel described here; W4A4 runs the prefill kernel that follows it.
 //   * a workgroup = 2 x 2 wavefronts = a 128 (n) x 128 (m) output tile; each
 //     wavefront owns 64 x 64 = 4 weight blocks x 4 activation blocks of 16;
 //   * weight tiles (flat 1 KiB per 16 rows x group) and their scales go from
@@ -753,28 +755,48 @@ __global__ __launch_bounds__(256, MODE == kW4A16 ? 1 : 2) void tiled_kernel(cons
 }
 
 // ----------------------------------------------------------------------------
-// W4A4 prefill kernel: WN x WM wavefronts, each owning a 64 (n) x 64 (m)
-// output block, so a workgroup computes a BN = 64 WN by BM = 64 WM tile.
-// Both operands are staged per group in LDS already widened to int8 (16 q,
-// the MFMA slot order), so each code is unpacked once per workgroup; the
-// group's scales sit in LDS as fp32 / 256.  LDS rows are RST bytes apart.
-// Two register stages keep the global loads of groups g+1 and g+2 in flight
-// while group g is computed; LDS is double-buffered with one barrier per
-// group.
+// W4A4 prefill kernel, register-direct weights: WN wavefronts, each owning a
+// 64 (n) x 64 (m) output block, so a workgroup computes BN = 64 WN rows of N
+// for 64 rows of M.
+//   * weights: the 1 KiB tile of (16-row block, group) is exactly one MFMA
+//     A-operand pair (lane l = slot l), so each wavefront loads its four
+//     tiles per group straight into registers (PD groups ahead) and widens
+//     them there; no LDS for the larger operand;
+//   * activations: the 64 x 64-byte group slice is staged in LDS once per
+//     workgroup, widened to int8 (16 q), double-buffered, one barrier per
+//     group;
+//   * epilogue without an int -> float conversion (with one, convert then
+//     FMA, the kernel runs at a third of this rate on MI355X): the first MFMA
+//     of each group starts from the integer bit pattern of B = 1.5 * 2^23, so
+//     its int32 result bits(B) + P' (P' = 256 P, the partial of the 16 q
+//     operands, |P'| <= 2^21) read as fp32 is exactly B + P', and one FMA per
+//     output and group adds s (B + P') to the running sum (s = scale / 256).
+//     After every CH groups the sum drops B times the sum of those CH
+//     scales, which the thread staging that column accumulates as it stages
+//     the scales.  P stays exact; what changes is that each FMA rounds at the
+//     magnitude the bias gives the running sum, up to CH B s: at most
+//     CH * scale / 341 per FMA, i.e. CH / 341 of one unit of P.
 // ----------------------------------------------------------------------------
 #ifndef QSPEC_PF_SHAPE
-#define QSPEC_PF_SHAPE 4, 2, 160  // WN, WM, RST (measured on MI355X)
+#define QSPEC_PF_SHAPE 4, 2, 4  // WN, PD (weight ring depth), CH (groups per bias chunk)
+#endif
+#ifndef QSPEC_PF_RST
+#define QSPEC_PF_RST 144  // LDS row stride of the widened activation slice (bytes)
 #endif
 
-template <int WN, int WM, int RST>
-__global__ __launch_bounds__(64 * WN * WM, (WN * WM <= 4) ? 2 : 1) void w4a4_prefill_kernel(
-    const TiledArgs a) {
-  constexpr int BN = 64 * WN, BM = 64 * WM, NT = 64 * WN * WM;
-  constexpr int AC = BN * 4 / NT, BC = BM * 4 / NT;  // 16-byte chunks per thread
-  static_assert(AC * NT == BN * 4 && BC * NT == BM * 4 && NT >= BN, "staging split");
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BN * RST];
+template <int WN, int PD, int CH>
+__global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArgs a) {
+  constexpr int BN = 64 * WN, BM = 64, NT = 64 * WN, RST = QSPEC_PF_RST;
+  constexpr int BCH = BM * 4;                          // 16-byte activation chunks per group
+  constexpr int BC = BCH >= NT ? BCH / NT : 1;         // chunks per staging thread
+  static_assert(BCH % NT == 0 || NT % BCH == 0, "staging split");
+  constexpr int U = PD;                                // unroll: ring slot and LDS buffer static
+  static_assert(PD == 2 || PD == 4, "ring depth");
+  constexpr uint32_t kBiasBits = 0x4B400000u;          // 1.5 * 2^23
+  constexpr float kBias = 12582912.0f;
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BM * RST];
   __shared__ __attribute__((aligned(16))) float Ss[2][BN];
+  __shared__ __attribute__((aligned(16))) float Cs[2][BN];
 
   const int b = blockIdx.x;
   const int xcd = b & 7, loc = b >> 3;
@@ -783,62 +805,77 @@ __global__ __launch_bounds__(64 * WN * WM, (WN * WM <= 4) ? 2 : 1) void w4a4_pre
   const int M = a.M, N = a.N, K = a.K;
   const int G = K / kGroup;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int l16 = lane & 15, lg = lane >> 4;
-  const int wn = wave % WN, wm = wave / WN;
   const int nrb = (N + 15) / 16;
-  const int rb0 = nt * (BN / 16);
   const int m0 = mt * BM;
 
-  // staging: A chunk c = (row block c/64, tile slot c%64); B chunk c = (row
-  // c/4, 16 packed bytes c%4 of the group); scale of tile row tid % BN
-  const uint8_t* asrc[AC];
-  int adst[AC];
+  // All loads go through buffer resources: the group advances a uniform
+  // offset (no per-lane address arithmetic in the loop).
+  // weight tiles of this wavefront: row blocks rbw .. rbw + 3 (clamped to
+  // the last block), slot `lane`
+  const int rbw = min(nt * (BN / 16) + wn * 4, nrb - 1);
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.Wq) + (int64_t)rbw * G * 1024, (short)0, min(4, nrb - rbw) * G * 1024,
+      0x00020000);
+  uint32_t woff[4];
 #pragma unroll
-  for (int i = 0; i < AC; ++i) {
-    const int c = tid + NT * i;
-    const int rbl = c >> 6, slot = c & 63;
-    asrc[i] = a.Wq + (int64_t)min(rb0 + rbl, nrb - 1) * G * 1024 + slot * 16;
-    adst[i] = (rbl * 16 + (slot & 15)) * RST + (slot >> 4) * 32;
-  }
-  const uint8_t* bsrc[BC];
+  for (int nb = 0; nb < 4; ++nb)
+    woff[nb] = (uint32_t)((min(nt * (BN / 16) + wn * 4 + nb, nrb - 1) - rbw) * G * 1024 + lane * 16);
+  // activation staging: chunk c = (row c / 4, 16 packed bytes c % 4 of the group)
+  const bool bstager = tid < BCH;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.X), (short)0, M * (K / 2), 0x00020000);
+  uint32_t boff[BC];
   int bdst[BC];
 #pragma unroll
   for (int i = 0; i < BC; ++i) {
-    const int c = tid + NT * i;
-    bsrc[i] = static_cast<const uint8_t*>(a.X) + (int64_t)min(m0 + (c >> 2), M - 1) * (K / 2) +
-              (c & 3) * 16;
+    const int c = min(tid + NT * i, BCH - 1);
+    boff[i] = (uint32_t)(min(m0 + (c >> 2), M - 1) * (K / 2) + (c & 3) * 16);
     bdst[i] = (c >> 2) * RST + (c & 3) * 32;
   }
-  const int srow = tid % BN;
-  const uint16_t* ssrc = a.Ws + (int64_t)min(rb0 + (srow >> 4), nrb - 1) * G * 16 + (srow & 15);
+  // scale staging: thread tid stages column tid of the tile
+  const int scol = nt * BN + tid;
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.Ws), (short)0, nrb * G * 32, 0x00020000);
+  const uint32_t soff = (uint32_t)((min(scol >> 4, nrb - 1) * G * 16 + (scol & 15)) * 2);
 
-  struct Stage {
-    uint4 a[AC], b[BC];
-    uint32_t s;
+  struct BStage {
+    uint4 x[BC];
+    uint16_t s;
   };
-  Stage st0, st1;
-  auto gload = [&](Stage& st, int g) {
+  auto bload = [&](BStage& st, int g) {
     const int gg = min(g, G - 1);
+    if (bstager) {
 #pragma unroll
-    for (int i = 0; i < AC; ++i) st.a[i] = ld_stream(asrc[i] + (int64_t)gg * 1024);
-#pragma unroll
-    for (int i = 0; i < BC; ++i) st.b[i] = *reinterpret_cast<const uint4*>(bsrc[i] + (int64_t)gg * 64);
-    st.s = ssrc[(int64_t)gg * 16];
+      for (int i = 0; i < BC; ++i) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, boff[i], gg * 64, 0);
+        st.x[i] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    }
+    st.s = __builtin_amdgcn_raw_buffer_load_b16(sres, soff, gg * 32, 0);
   };
-  auto widen_store = [&](uint8_t* dst, const uint4 p) {
-    *reinterpret_cast<uint4*>(dst) =
-        make_uint4(w4_lo_x16(p.x), w4_hi_x16(p.x), w4_lo_x16(p.y), w4_hi_x16(p.y));
-    *reinterpret_cast<uint4*>(dst + 16) =
-        make_uint4(w4_lo_x16(p.z), w4_hi_x16(p.z), w4_lo_x16(p.w), w4_hi_x16(p.w));
-  };
-  auto lstore = [&](const Stage& st, int buf) {
+  float ssum = 0.f;  // this thread's column: sum of the scales of the open chunk
+  auto bstore = [&](const BStage& st, int buf, int g) {
+    if (bstager) {
 #pragma unroll
-    for (int i = 0; i < AC; ++i) widen_store(&As[buf][adst[i]], st.a[i]);
-#pragma unroll
-    for (int i = 0; i < BC; ++i) widen_store(&Bs[buf][bdst[i]], st.b[i]);
-    // threads sharing a tile row write the same value: no branch, no sunk load
-    Ss[buf][srow] = half_bits_to_float((uint16_t)st.s) * 0.00390625f;  // / 256
+      for (int i = 0; i < BC; ++i) {
+        const uint4 p = st.x[i];
+        uint8_t* d = &Bs[buf][bdst[i]];
+        *reinterpret_cast<uint4*>(d) =
+            make_uint4(w4_lo_x16(p.x), w4_hi_x16(p.x), w4_lo_x16(p.y), w4_hi_x16(p.y));
+        *reinterpret_cast<uint4*>(d + 16) =
+            make_uint4(w4_lo_x16(p.z), w4_hi_x16(p.z), w4_lo_x16(p.w), w4_hi_x16(p.w));
+      }
+    }
+    const float sv = half_bits_to_float(st.s) * 0.00390625f;  // / 256 (both operands are 16 q)
+    Ss[buf][tid] = sv;
+    ssum += sv;
+    if (g % CH == CH - 1 || g == G - 1) {  // uniform: the chunk closes with group g
+      Cs[buf][tid] = kBias * ssum;
+      ssum = 0.f;
+    }
   };
 
   v4f tot[4][4];
@@ -846,62 +883,96 @@ __global__ __launch_bounds__(64 * WN * WM, (WN * WM <= 4) ? 2 : 1) void w4a4_pre
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  const v4i cbias = {(int)kBiasBits, (int)kBiasBits, (int)kBiasBits, (int)kBiasBits};
 
-  auto compute = [&](int buf) {
-    const uint8_t* Ab = &As[buf][(wn * 64 + l16) * RST + lg * 32];
-    const uint8_t* Bb = &Bs[buf][(wm * 64 + l16) * RST + lg * 32];
+  auto wload = [&](int nb, int g) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[nb], g * 1024, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  };
+  uint4 ring[PD][4];
+#pragma unroll
+  for (int i = 0; i < PD; ++i)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) ring[i][nb] = wload(nb, min(i, G - 1));
+  BStage bst[2];
+  bload(bst[0], 0);
+  bload(bst[1], 1);
+  bstore(bst[0], 0, 0);
+  bload(bst[0], 2);
+  __syncthreads();
+
+  // one group; u = g mod U fixes the ring slot and the LDS buffer at compile time
+  auto step = [&](auto uc, int g) {
+    constexpr int u = decltype(uc)::value;
+    const int buf = u & 1;
+    const uint8_t* Bb = &Bs[buf][l16 * RST + lg * 32];
     v4i bf[4][2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       bf[mb][0] = *reinterpret_cast<const v4i*>(Bb + mb * 16 * RST);
       bf[mb][1] = *reinterpret_cast<const v4i*>(Bb + mb * 16 * RST + 16);
     }
+    const int gn = min(g + PD, G - 1);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const v4i a0 = *reinterpret_cast<const v4i*>(Ab + nb * 16 * RST);
-      const v4i a1 = *reinterpret_cast<const v4i*>(Ab + nb * 16 * RST + 16);
+      // this group's weights of block nb, widened; the ring slot then
+      // takes group g + PD
+      const uint4 p = ring[u % PD][nb];
+      const v4i a0 = {(int)w4_lo_x16(p.x), (int)w4_hi_x16(p.x), (int)w4_lo_x16(p.y), (int)w4_hi_x16(p.y)};
+      const v4i a1 = {(int)w4_lo_x16(p.z), (int)w4_hi_x16(p.z), (int)w4_lo_x16(p.w), (int)w4_hi_x16(p.w)};
+      ring[u % PD][nb] = wload(nb, gn);
       const float4 sc = *reinterpret_cast<const float4*>(&Ss[buf][wn * 64 + nb * 16 + lg * 4]);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bf[mb][0], v4i{0, 0, 0, 0}, 0, 0, 0);
+        v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bf[mb][0], cbias, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bf[mb][1], acc, 0, 0, 0);
-        tot[nb][mb][0] = fmaf(sc.x, (float)acc[0], tot[nb][mb][0]);
-        tot[nb][mb][1] = fmaf(sc.y, (float)acc[1], tot[nb][mb][1]);
-        tot[nb][mb][2] = fmaf(sc.z, (float)acc[2], tot[nb][mb][2]);
-        tot[nb][mb][3] = fmaf(sc.w, (float)acc[3], tot[nb][mb][3]);
+        tot[nb][mb][0] = fmaf(sc.x, __int_as_float(acc[0]), tot[nb][mb][0]);
+        tot[nb][mb][1] = fmaf(sc.y, __int_as_float(acc[1]), tot[nb][mb][1]);
+        tot[nb][mb][2] = fmaf(sc.z, __int_as_float(acc[2]), tot[nb][mb][2]);
+        tot[nb][mb][3] = fmaf(sc.w, __int_as_float(acc[3]), tot[nb][mb][3]);
       }
     }
+    if (g % CH == CH - 1 || g == G - 1) {  // uniform: drop the chunk's bias
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const float4 cr = *reinterpret_cast<const float4*>(&Cs[buf][wn * 64 + nb * 16 + lg * 4]);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          tot[nb][mb][0] -= cr.x;
+          tot[nb][mb][1] -= cr.y;
+          tot[nb][mb][2] -= cr.z;
+          tot[nb][mb][3] -= cr.w;
+        }
+      }
+    }
+    // stage group g + 1 into the other buffer (its readers, group g - 1,
+    // all passed the previous barrier), then fetch group g + 3
+    if (g + 1 < G) bstore(bst[(u + 1) & 1], buf ^ 1, g + 1);
+    bload(bst[(u + 1) & 1], g + 3);
+    __syncthreads();
   };
-
-  gload(st0, 0);
-  gload(st1, 1);
-  lstore(st0, 0);
-  __syncthreads();
-  gload(st0, 2);
   int g = 0;
-  for (; g + 1 < G; g += 2) {
-    // group g sits in LDS buffer 0, group g+1 in st1, group g+2 in st0
-    compute(0);
-    __builtin_amdgcn_sched_barrier(0);
-    lstore(st1, 1);
-    __syncthreads();
-    gload(st1, g + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    __builtin_amdgcn_sched_barrier(0);
-    lstore(st0, 0);
-    __syncthreads();
-    gload(st0, g + 4);
-    __builtin_amdgcn_sched_barrier(0);
+  for (; g + U <= G; g += U) {
+    step(std::integral_constant<int, 0>{}, g);
+    step(std::integral_constant<int, 1>{}, g + 1);
+    if constexpr (U > 2) {
+      step(std::integral_constant<int, 2>{}, g + 2);
+      step(std::integral_constant<int, 3>{}, g + 3);
+    }
   }
-  if (g < G) compute(0);  // odd group count: the last group is in buffer 0
+  // tail: fewer than U groups left, g is a multiple of U
+  if (g < G) step(std::integral_constant<int, 0>{}, g);
+  if constexpr (U > 2) {
+    if (g + 1 < G) step(std::integral_constant<int, 1>{}, g + 1);
+    if (g + 2 < G) step(std::integral_constant<int, 2>{}, g + 2);
+  }
 
   const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 64 + mb * 16 + l16;
+      const int m = m0 + mb * 16 + l16;
       const int n = nt * BN + wn * 64 + nb * 16 + lg * 4;
       if (m < M && n < N) {
         const float xsc = a.Xs[m];
@@ -920,13 +991,13 @@ __global__ __launch_bounds__(64 * WN * WM, (WN * WM <= 4) ? 2 : 1) void w4a4_pre
     }
 }
 
-template <int WN, int WM, int RST>
+template <int WN, int PD, int CH>
 hipError_t launch_w4a4_prefill(TiledArgs a, hipStream_t s) {
   a.ntn = (int)cdiv(a.N, 64 * WN);
-  a.ntm = (int)cdiv(a.M, 64 * WM);
+  a.ntm = (int)cdiv(a.M, 64);
   const int64_t blocks = 8 * cdiv(a.ntn, 8) * a.ntm;
-  hipLaunchKernelGGL((w4a4_prefill_kernel<WN, WM, RST>), dim3((unsigned)blocks),
-                     dim3(64 * WN * WM), 0, s, a);
+  hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH>), dim3((unsigned)blocks), dim3(64 * WN), 0,
+                     s, a);
   return hipGetLastError();
 }
 

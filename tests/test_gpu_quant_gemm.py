@@ -33,6 +33,7 @@ SHAPES = [
     (300, 600, 1152),
     (16, 3584, 18944),
     (11, 200, 2688),
+    (9, 40, 128),
 ]
 
 
@@ -143,6 +144,31 @@ def test_w4a4_parity(M, N, K, variant):
     # without the partials output (the tiled family serves this path)
     Y2 = q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d, variant=variant, N=N)
     assert_close(host(Y2), want, what="w4a4 no partials")
+
+
+@pytest.mark.parametrize("K", [3584, 18944])
+def test_w4a4_massive_outlier_rows(K):
+    """Every row holds one channel about 1000x the others, so per-token
+    quantization zeroes every other code and |y| is small: the fp32 scale
+    epilogue's rounding must stay within the bar in every family."""
+    M, N = 70, 200
+    say(f"w4a4 massive-outlier rows K={K}")
+    rng = synth.make_rng(22)
+    W = synth.weights(rng, N, K)
+    Xf = synth.from_bf16_bits(synth.activations(rng, M, K, n_outliers=0)).copy()
+    Xf[np.arange(M), rng.integers(0, K, size=M)] = np.float32(3000.0)
+    Wq, Ws = oracle.pack_w4(W)
+    Xq, Xs = oracle.quant_act(synth.to_bf16_bits(Xf))
+    want = oracle.gemm_w4a4(Xq, Xs, Wq, Ws)
+    Xq_d, Xs_d, Wq_d, Ws_d = dev(Xq), dev(Xs), dev_w(Wq), dev_s(Ws)
+    for v in W4A4_VARIANTS:
+        if v == q.GEMM_STREAM:
+            Y = q.gemm_w4a4(dev(Xq[:16].copy()), dev(Xs[:16].copy()), Wq_d, Ws_d, variant=v, N=N)
+            e = assert_close(host(Y), want[:16], what=f"w4a4 massive outliers variant={v}")
+        else:
+            Y = q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d, variant=v, N=N)
+            e = assert_close(host(Y), want, what=f"w4a4 massive outliers variant={v}")
+        say(f"  variant={v} max|err| / max|y| = {e:.2e}")
 
 
 def test_w4a4_gpu_quantized_chain():
