@@ -499,6 +499,24 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w4a4_gate_up_M8.json")
 W4A4_SKINNY_TAG = "skinny_kernel<1,"
 
 
+def run_only(which):
+    import torch
+    import quantization_self_speculation_amd as q
+    q.lib()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    if which == "verify":
+        res = measure_verify_llama(torch, q)
+    elif which == "e2e":
+        res = measure_e2e(torch)
+    else:
+        wl = Decode(torch, q)
+        torch.cuda.synchronize()
+        res = (measure_prefill if which == "prefill" else measure_decode_gemv)(torch, q, wl)
+    print(json.dumps({which: res}), flush=True)
+
+
 def _gemm_source_hash():
     import hashlib
     src = os.path.join(ROOT, "quantization_self_speculation_amd", "csrc", "gemm.hip")
@@ -579,6 +597,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the decode-GEMV, prefill and verify side measurements")
+    ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e"],
+                    help="run one side measurement alone and print its JSON (for profiling)")
     ap.add_argument("--counters", action="store_true",
                     help="run only the copy calibration and the dominant kernel (for rocprofv3 --pmc)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -593,6 +613,9 @@ def main():
         sys.exit(2)
     if args.counters:
         run_counters()
+        return
+    if args.only:
+        run_only(args.only)
         return
     run(args)
 

@@ -65,29 +65,43 @@ __device__ __forceinline__ float absmax8(uint4 v) {
   return fmaxf(a, b);
 }
 
-__device__ __forceinline__ uint32_t pack8(uint4 v, float s) {
+// The code of v at the activation scale s = absmax / 7 (s > 0), with r the
+// IEEE reciprocal of s.  |v / s| <= 7 (about), so v * r is within 2^-20 of
+// the exact quotient and within 2^-19 of the IEEE quotient v / s; wherever
+// v * r lies farther than 2^-19 from a half-integer both round to the same
+// integer.  Nearer (or NaN, or an infinite r) the IEEE quotient decides, so
+// every code equals rne(v / s) clamped, as the divide would give it.
+__device__ __forceinline__ int quant_code_act(float v, float s, float r) {
+  const float qa = v * r;
+  float k = __builtin_rintf(qa);
+  if (!(fabsf(qa - k) < 0.5f - 0x1p-19f)) k = __builtin_rintf(v / s);
+  return (int)fminf(fmaxf(k, -8.0f), 7.0f);
+}
+
+__device__ __forceinline__ uint32_t pack8(uint4 v, float s, float r) {
   const float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                       bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
   uint32_t word = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) word |= (uint32_t)(quant_code(x[i], s) & 0xF) << (4 * i);
+  for (int i = 0; i < 8; ++i) word |= (uint32_t)(quant_code_act(x[i], s, r) & 0xF) << (4 * i);
   return word;
 }
 
-// One 256-thread block per token row.  The row is read once into registers
+// One NT-thread block per token row.  The row is read once into registers
 // (NC 16-byte chunks per thread), reduced to its absmax, then coded.
-template <int NC>
-__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ X,
-                                                        int64_t K, uint8_t* __restrict__ Xq,
-                                                        float* __restrict__ Xs) {
-  __shared__ float red[4];
+template <int NT, int NC>
+__global__ __launch_bounds__(NT) void quant_act_kernel(const uint16_t* __restrict__ X,
+                                                       int64_t K, uint8_t* __restrict__ Xq,
+                                                       float* __restrict__ Xs) {
+  constexpr int NW = NT / 64;
+  __shared__ float red[NW];
   const int64_t m = blockIdx.x;
   const uint4* row = reinterpret_cast<const uint4*>(X + m * K);
   const int nch = (int)(K / 8);
   uint4 v[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const int c = threadIdx.x + 256 * i;
+    const int c = threadIdx.x + NT * i;
     v[i] = c < nch ? row[c] : make_uint4(0, 0, 0, 0);
   }
   float a = 0.0f;
@@ -96,50 +110,21 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   a = wave_max(a);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
-  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  a = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) a = fmaxf(a, red[w]);
   const float s = a / 7.0f;
+  const float r = 1.0f / s;
   uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    if (c < nch) out[c] = s != 0.0f ? pack8(v[i], s) : 0u;
+    const int c = threadIdx.x + NT * i;
+    if (c < nch) out[c] = s != 0.0f ? pack8(v[i], s, r) : 0u;
   }
   if (threadIdx.x == 0) Xs[m] = s;
 }
 
-// Short rows (K <= 8192): one wavefront per row, no block barrier; NC 16-byte
-// chunks per lane held in registers.
-template <int NC>
-__global__ __launch_bounds__(256) void quant_act_wave_kernel(const uint16_t* __restrict__ X,
-                                                             int64_t M, int64_t K,
-                                                             uint8_t* __restrict__ Xq,
-                                                             float* __restrict__ Xs) {
-  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;  // uniform per wavefront
-  const int lane = threadIdx.x & 63;
-  const uint4* row = reinterpret_cast<const uint4*>(X + m * K);
-  const int nch = (int)(K / 8);
-  uint4 v[NC];
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = lane + 64 * i;
-    v[i] = row[min(c, nch - 1)];
-  }
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) a = fmaxf(a, absmax8(v[i]));
-  a = wave_max(a);
-  const float s = a / 7.0f;
-  uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch) out[c] = s != 0.0f ? pack8(v[i], s) : 0u;
-  }
-  if (lane == 0) Xs[m] = s;
-}
-
-// rows longer than 256 * 16 * 8 = 32768: two passes (the second hits L2)
+// rows longer than 1024 * 8 * 8 = 65536 values: two passes (the second hits L2)
 __global__ __launch_bounds__(256) void quant_act_long_kernel(const uint16_t* __restrict__ X,
                                                              int64_t K, uint8_t* __restrict__ Xq,
                                                              float* __restrict__ Xs) {
@@ -154,8 +139,9 @@ __global__ __launch_bounds__(256) void quant_act_long_kernel(const uint16_t* __r
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = a / 7.0f;
+  const float r = 1.0f / s;
   uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
-  for (int64_t c = threadIdx.x; c < nch; c += 256) out[c] = s != 0.0f ? pack8(row[c], s) : 0u;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) out[c] = s != 0.0f ? pack8(row[c], s, r) : 0u;
   if (threadIdx.x == 0) Xs[m] = s;
 }
 
@@ -172,21 +158,21 @@ hipError_t launch_pack_w4(const float* W, int64_t N, int64_t K, uint8_t* Wq, uin
 
 hipError_t launch_quant_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
                             hipStream_t s) {
-  const int64_t perw = cdiv(K / 8, 64);  // 16-byte chunks per lane, one wavefront per row
-  if (perw <= 16) {
-    const dim3 g((unsigned)cdiv(M, 4)), b(256);
-    if (perw <= 4) hipLaunchKernelGGL(quant_act_wave_kernel<4>, g, b, 0, s, X, M, K, Xq, Xs);
-    else if (perw <= 8) hipLaunchKernelGGL(quant_act_wave_kernel<8>, g, b, 0, s, X, M, K, Xq, Xs);
-    else hipLaunchKernelGGL(quant_act_wave_kernel<16>, g, b, 0, s, X, M, K, Xq, Xs);
-    return hipGetLastError();
+  // one block per row, sized so each thread holds at most a few chunks: the
+  // short latency chain (load, block max, code) is what a decode row costs
+  const int64_t nch = K / 8;  // 16-byte chunks of a row
+  const dim3 g((unsigned)M);
+  if (nch <= 512) {
+    hipLaunchKernelGGL((quant_act_kernel<256, 2>), g, dim3(256), 0, s, X, K, Xq, Xs);
+  } else if (nch <= 2048) {
+    hipLaunchKernelGGL((quant_act_kernel<1024, 2>), g, dim3(1024), 0, s, X, K, Xq, Xs);
+  } else if (nch <= 4096) {
+    hipLaunchKernelGGL((quant_act_kernel<1024, 4>), g, dim3(1024), 0, s, X, K, Xq, Xs);
+  } else if (nch <= 8192) {
+    hipLaunchKernelGGL((quant_act_kernel<1024, 8>), g, dim3(1024), 0, s, X, K, Xq, Xs);
+  } else {
+    hipLaunchKernelGGL(quant_act_long_kernel, g, dim3(256), 0, s, X, K, Xq, Xs);
   }
-  const int64_t per = cdiv(K / 8, 256);  // 16-byte chunks per thread
-  const dim3 g((unsigned)M), b(256);
-  if (per <= 2) hipLaunchKernelGGL(quant_act_kernel<2>, g, b, 0, s, X, K, Xq, Xs);
-  else if (per <= 4) hipLaunchKernelGGL(quant_act_kernel<4>, g, b, 0, s, X, K, Xq, Xs);
-  else if (per <= 8) hipLaunchKernelGGL(quant_act_kernel<8>, g, b, 0, s, X, K, Xq, Xs);
-  else if (per <= 16) hipLaunchKernelGGL(quant_act_kernel<16>, g, b, 0, s, X, K, Xq, Xs);
-  else hipLaunchKernelGGL(quant_act_long_kernel, g, b, 0, s, X, K, Xq, Xs);
   return hipGetLastError();
 }
 

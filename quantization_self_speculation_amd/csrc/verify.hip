@@ -230,9 +230,10 @@ struct Decision {
 
 // sampling decision: one 256-thread block per sequence.  The 2*gamma+1 row
 // normalizers are merged in parallel (one wavefront per row), the logits at
-// the drafted tokens are fetched in parallel, then one thread runs the
-// accept tests in order.  p(x) and q(x) are fp64: exact fp64 exponent of the
-// exact difference over the pass-1 sums.
+// the drafted tokens are fetched in parallel, then lane i of the first
+// wavefront runs the accept test of draft i and the lowest rejecting lane
+// decides.  p(x) and q(x) are fp64: exact fp64 exponent of the exact
+// difference over the pass-1 sums.
 __global__ __launch_bounds__(256) void sample_decide_kernel(
     const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
     const float* __restrict__ ua, int gamma, int64_t V, int nck, const float* __restrict__ pm,
@@ -259,20 +260,26 @@ __global__ __launch_bounds__(256) void sample_decide_kernel(
     lxd[tid] = drf[(b * gamma + tid) * V + x];
   }
   __syncthreads();
-  if (tid != 0) return;
-  Decision D{gamma, 1, lm[gamma], 0.f, lsum[gamma], 1.0};
-  for (int i = 0; i < gamma; ++i) {
-    const float mt = lm[i], md = lm[gamma + 1 + i];
-    const double st = lsum[i], sd = lsum[gamma + 1 + i];
-    const double p = exp((double)lxt[i] - (double)mt) / st;
-    const double q = exp((double)lxd[i] - (double)md) / sd;
-    const bool acc = q > 0.0 ? ((double)ua[b * gamma + i] <= p / q) : (p > 0.0);
-    if (!acc) {
-      D = Decision{i, 0, mt, md, st, sd};
-      break;
-    }
+  if (w != 0) return;
+  // every accept test at once (lane i tests draft i); the first rejection
+  // ends the run, as in the sequential rule
+  bool rej = false;
+  if (lane < gamma) {
+    const float mt = lm[lane], md = lm[gamma + 1 + lane];
+    const double st = lsum[lane], sd = lsum[gamma + 1 + lane];
+    const double p = exp((double)lxt[lane] - (double)mt) / st;
+    const double q = exp((double)lxd[lane] - (double)md) / sd;
+    const bool acc = q > 0.0 ? ((double)ua[b * gamma + lane] <= p / q) : (p > 0.0);
+    rej = !acc;
   }
-  dec[b] = D;
+  const unsigned long long mask = __ballot(rej);
+  if (lane != 0) return;
+  if (mask == 0) {
+    dec[b] = Decision{gamma, 1, lm[gamma], 0.f, lsum[gamma], 1.0};
+  } else {
+    const int i = __builtin_ctzll(mask);
+    dec[b] = Decision{i, 0, lm[i], lm[gamma + 1 + i], lsum[i], lsum[gamma + 1 + i]};
+  }
 }
 
 // r_j of the row a sequence samples from, in fp64
@@ -334,8 +341,10 @@ __global__ __launch_bounds__(256) void resid_sums_kernel(const float* __restrict
 }
 
 // inverse-CDF select: one 256-thread block per sequence, fp64 cumulative sums.
-// The chunk holding the threshold is found from the chunk totals (sequential,
-// fixed order); inside it each thread takes 8 consecutive logits, and a
+// One wavefront finds the chunk holding the threshold from the chunk totals
+// (each lane sums a run of chunks in order, a fixed-order scan over the lanes
+// gives each run its start, each lane walks its run, the lowest crossing
+// wins); inside that chunk each thread takes 8 consecutive logits, and a
 // block-wide exclusive scan gives every thread its starting cumulative sum.
 __global__ __launch_bounds__(256) void sample_select_kernel(
     const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
@@ -361,40 +370,67 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
     tp[c] = pp[b * rnck + c];
   }
   __syncthreads();
-  if (tid == 0) {  // chunk totals in fixed sequential order
+  if (w == 0) {
+    // chunk totals, one wavefront: lane l sums its run of `per` consecutive
+    // chunks in order, then an inclusive scan over the lanes (fixed order)
+    const int per = (rnck + 63) / 64;
+    const int c0 = min(rnck, lane * per), c1 = min(rnck, c0 + per);
     int kind = D.kind;
     const double* tot = tr;
-    double R = 0.0;
-    for (int c = 0; c < rnck; ++c) R += tot[c];
+    auto scan = [&](const double* t, double& excl, double& R) {
+      double v = 0.0;
+      for (int c = c0; c < c1; ++c) v += t[c];
+      double incl = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+      }
+      excl = __shfl_up(incl, 1, 64);
+      if (lane == 0) excl = 0.0;
+      R = __shfl(incl, 63, 64);
+    };
+    double excl, R;
+    scan(tot, excl, R);
     if (R == 0.0 && kind == 0) {  // p == q everywhere: sample from p
       kind = 1;
       tot = tp;
-      R = 0.0;
-      for (int c = 0; c < rnck; ++c) R += tot[c];
+      scan(tot, excl, R);
     }
     const double thr = (double)us[b] * R;
+    // each lane walks its run from its exclusive start; the lowest lane
+    // whose walk passes the threshold holds the chunk
     int cs = -1;
-    double base = 0.0, run = 0.0;
-    for (int c = 0; c < rnck; ++c) {
-      const double nx = run + tot[c];
-      if (nx > thr) {
-        cs = c;
-        base = run;
-        break;
+    double base = 0.0;
+    {
+      double run = excl;
+      for (int c = c0; c < c1; ++c) {
+        const double nx = run + tot[c];
+        if (nx > thr) {
+          cs = c;
+          base = run;
+          break;
+        }
+        run = nx;
       }
-      run = nx;
     }
-    int last_c = -1;  // fallback: last chunk with mass
-    for (int c = rnck - 1; c >= 0; --c)
+    const unsigned long long hit = __ballot(cs >= 0);
+    // last chunk with mass (fallback when the threshold is at or past the total)
+    int last_c = -1;
+    for (int c = c1 - 1; c >= c0; --c)
       if (tot[c] > 0.0) {
         last_c = c;
         break;
       }
-    sh_cs = cs;
-    sh_cc = cs >= 0 ? cs : (last_c >= 0 ? last_c : 0);
-    sh_kind = kind;
-    sh_base = base;
-    sh_thr = thr;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last_c = max(last_c, __shfl_xor(last_c, o, 64));
+    if (lane == (hit ? __builtin_ctzll(hit) : 0)) {
+      sh_cs = hit ? cs : -1;
+      sh_cc = hit ? cs : (last_c >= 0 ? last_c : 0);
+      sh_kind = kind;
+      sh_base = hit ? base : 0.0;
+      sh_thr = thr;
+    }
   }
   __syncthreads();
   const int cs = sh_cs, cc = sh_cc, kind = sh_kind;
