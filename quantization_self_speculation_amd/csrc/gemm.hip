@@ -13,12 +13,15 @@
 //
 // gfx950 design
 //  * Codes are widened in registers only; the shared buffer stays 4-bit.
-//    W4A16 turns a nibble into the bf16 of 136 + q with one AND-OR (exact),
-//    runs v_mfma_f32_16x16x32_bf16 and removes the bias with a second MFMA
-//    chain whose A operand is the constant -136 (the skinny family) or with
-//    the group sum of x (the GEMV family), in fp32 before the scale.  W4A4 turns nibbles into int8 holding 16 q with
-//    one AND (exact) and runs v_mfma_i32_16x16x64_i8; the int32 group partial
-//    is 256 P exactly.
+//    W4A16 turns a nibble into the bf16 of 136 + q with one AND-XOR
+//    (exact), runs v_mfma_f32_16x16x32_bf16 and removes the bias in fp32
+//    before the scale: with a second MFMA chain whose A operand is the
+//    constant -136 (skinny, stream and prefill kernels; the prefill kernel
+//    runs it once per activation block and seeds every weight block's
+//    accumulator with it) or with the group sum of x (GEMV).  W4A4 turns
+//    nibbles into int8 holding 16 q (a mask, and a shift for the low
+//    nibbles; exact) and runs v_mfma_i32_16x16x64_i8; the int32 group
+//    partial is 256 P exactly.
 //  * MFMA operand A = 16 weight rows (n), operand B = 16 activation rows (m),
 //    so each lane of D holds 4 consecutive n of one m: one 16-byte store.
 //  * Within a 128-group, lane l feeds the 32 consecutive k starting at
@@ -63,8 +66,11 @@
 #ifndef QSPEC_SK_NB16
 #define QSPEC_SK_NB16 1    // W4A16, M > 16: 16-row blocks per wavefront
 #endif
+#ifndef QSPEC_SK_SPLIT_WG
+#define QSPEC_SK_SPLIT_WG 128  // k-split until about this many workgroups (a function of N, K)
+#endif
 #ifndef QSPEC_SK_TARGET_WG
-#define QSPEC_SK_TARGET_WG 256
+#define QSPEC_SK_TARGET_WG 256  // M <= 16 below this many 64-row tiles: the stream family
 #endif
 
 // wavefronts per SIMD the register budget of a skinny instantiation must
@@ -1326,8 +1332,8 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K) {
   const int64_t G = K / kGroup;
   const int64_t t64 = cdiv(N, 64);  // the split depends on N and K only
   int64_t S = 1;
-  if (t64 < QSPEC_SK_TARGET_WG) {
-    S = cdiv(QSPEC_SK_TARGET_WG, t64);
+  if (t64 < QSPEC_SK_SPLIT_WG) {
+    S = cdiv(QSPEC_SK_SPLIT_WG, t64);
     const int64_t smax = std::max<int64_t>(1, G / 4);  // at least 4 groups per slice
     if (S > smax) S = smax;
   }
@@ -1388,10 +1394,8 @@ struct GemvPlan {
 };
 GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K / kGroup, kGemvGroups)}; }
 
-// AUTO: GEMV for one or two rows, the skinny MFMA family up to 128 rows,
-// the tiled family beyond
-// AUTO: for M <= 16 the stream family where the skinny family would have to
-// split K across workgroups (fewer than QSPEC_SK_TARGET_WG 64-row tiles),
+// AUTO: for M <= 16 the stream family where the skinny family would have
+// few workgroups (fewer than QSPEC_SK_TARGET_WG 64-row tiles),
 // the skinny family otherwise and up to 128 rows, the tiled family beyond.
 // The choice depends on M and N only.
 int auto_pick(int64_t M, int64_t N) {
