@@ -1340,6 +1340,9 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K) {
   p.gps = (int)cdiv(G, S);
   p.S = (int)cdiv(G, p.gps);
   p.MB = (int)(M >= 64 ? 4 : cdiv(M, 16));
+  // W4A16 with a k-split: one 16-row activation block per workgroup (more,
+  // lighter workgroups; the weight tile is re-read from L2 per block)
+  if (mode == 0 && p.S > 1) p.MB = 1;
   // two 16-row blocks per wavefront halve the LDS activation reads once the
   // activation tile spans several m-blocks (the bf16 verifier shapes)
   p.NB = (mode == 0 && p.MB >= 2) ? QSPEC_SK_NB16 : 1;
