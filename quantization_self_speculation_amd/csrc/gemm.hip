@@ -157,12 +157,13 @@ struct SkinnyArgs {
 // do not stay in an XCD's L2), the writer waits for its stores to complete
 // before the arrival count, and the arrival counter (epoch-tagged, in the
 // caller's workspace) is reset by the last slice.
-template <int MODE, int MB, int NB>
+template <int MODE, int MB, int NB, int NWV>
 __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot)[NB][MB], int t,
                                             int slice, int m0, int n_wg, int n_w, int l16, int lg,
                                             int* s_last_ptr) {
   constexpr int ROWS = 16 * MB;
-  constexpr int WROWS = 64 * NB;
+  constexpr int WROWS = 16 * NB * NWV;
+  constexpr int NT = 64 * NWV;
   const int M = a.M, N = a.N;
   int& s_last = *s_last_ptr;
   const bool vec = (N & 3) == 0;
@@ -229,13 +230,13 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   // all partials of an element are requested before any is added (in slice
   // order), 8 slices per batch
   const int64_t MN = (int64_t)M * N;
-  constexpr int EPT = ROWS * WROWS / 256;
+  constexpr int EPT = ROWS * WROWS / NT;
   float acc[EPT];
   const float* src[EPT];
   bool ok[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const int i = threadIdx.x + 256 * e;
+    const int i = threadIdx.x + NT * e;
     const int m = m0 + i / WROWS, n = n_wg + i % WROWS;
     ok[e] = m < M && n < N;
     src[e] = a.part + (int64_t)min(m, M - 1) * N + min(n, N - 1);
@@ -257,7 +258,7 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const int i = threadIdx.x + 256 * e;
+    const int i = threadIdx.x + NT * e;
     const int m = m0 + i / WROWS, n = n_wg + i % WROWS;
     if (ok[e]) a.Y[(int64_t)m * N + n] = MODE == kW4A4 ? a.Xs[m] * acc[e] : acc[e];
   }
@@ -269,15 +270,16 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
 // a clamped, valid address) so the compiler keeps exact load counters and the
 // weight ring stays in flight across waits; only the arithmetic of groups past
 // the end of the slice is skipped (a branch uniform over the workgroup).
-template <int MODE, int MB, int NB, int CH, int PD, bool WITHP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(skinny_wpe(MODE, MB)))) void skinny_kernel(const SkinnyArgs a) {
+template <int MODE, int MB, int NB, int CH, int PD, bool WITHP, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny_wpe(MODE, MB)))) void skinny_kernel(const SkinnyArgs a) {
   static_assert(PD % CH == 0, "prefetch depth must be a multiple of the chunk");
-  constexpr int ROWS = 16 * MB;      // activation rows of an m-chunk
-  constexpr int WROWS = 64 * NB;     // weight rows of a tile (4 wavefronts x NB blocks of 16)
+  constexpr int NT = 64 * NWV;             // threads of a workgroup
+  constexpr int ROWS = 16 * MB;            // activation rows of an m-chunk
+  constexpr int WROWS = 16 * NB * NWV;     // weight rows of a tile (NWV wavefronts x NB blocks of 16)
   constexpr int XSTB = (MODE == kW4A16 ? CH * 256 : CH * 128) + 16;  // LDS row bytes
   constexpr int XCH = MODE == kW4A16 ? ROWS * CH * 16 : ROWS * CH * 4;  // 16-B chunks
-  constexpr int XPT = (XCH + 255) / 256;
-  constexpr int SPT = (CH * WROWS + 255) / 256;
+  constexpr int XPT = (XCH + NT - 1) / NT;
+  constexpr int SPT = (CH * WROWS + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][ROWS * XSTB];
   __shared__ uint16_t wsl[2][CH * WROWS];
   __shared__ int s_last;
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(skinny_wpe(
     const int gc = g_begin + c * CH;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int idx = min((int)threadIdx.x + 256 * i, XCH - 1);
+      const int idx = min((int)threadIdx.x + NT * i, XCH - 1);
       uint32_t off;
       if (MODE == kW4A16) {
         const int r = idx / (CH * 16), cc = idx % (CH * 16);
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(skinny_wpe(
     }
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
-      const int idx = min((int)threadIdx.x + 256 * i, CH * WROWS - 1);
+      const int idx = min((int)threadIdx.x + NT * i, CH * WROWS - 1);
       const int gl = idx / WROWS, rr = idx % WROWS;
       const int rb = min((n_wg + rr) >> 4, nrb - 1);
       sr[i] = a.Ws[((int64_t)rb * G + min(gc + gl, G - 1)) * 16 + (rr & 15)];
@@ -348,7 +350,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(skinny_wpe(
   auto x_store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int idx = threadIdx.x + 256 * i;
+      const int idx = threadIdx.x + NT * i;
+      if (XCH % NT != 0 && idx >= XCH) continue;  // workgroup sizes that do not divide the chunk
       if (MODE == kW4A16) {
         const int r = idx / (CH * 16), cc = idx % (CH * 16);
         const uint32_t v[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(skinny_wpe(
     }
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
-      const int idx = threadIdx.x + 256 * i;
+      const int idx = threadIdx.x + NT * i;
       if (idx < CH * WROWS) wsl[buf][idx] = sr[i];
     }
   };
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(skinny_wpe(
       }
     }
   }
-  finish_tile<MODE, MB, NB>(a, tot, t, slice, m0, n_wg, n_w, l16, lg, &s_last);
+  finish_tile<MODE, MB, NB, NWV>(a, tot, t, slice, m0, n_wg, n_w, l16, lg, &s_last);
 }
 
 // ============================================================================
@@ -1322,12 +1325,36 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
 // Split-K depends on (N, K) only: an output row's operation order is the
 // same for every M within one family.
 struct SkinnyPlan {
-  int S, gps, MB, NB, mchunks, ntiles, T;
+  int S, gps, MB, NB, NWV, mchunks, ntiles, T;
   int64_t blocks;
   size_t cnt_bytes, part_bytes;
 };
 
-SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K) {
+// Wavefronts per workgroup of the one-activation-block kernels (decode
+// shapes): when every workgroup is resident at once (up to 768 four-wavefront
+// tiles), a CU that holds one workgroup more than another streams that many
+// more weight bytes through its own load queue, so take the count whose
+// workgroups spread most evenly over the 256 CUs -- fewest wavefronts on the
+// busiest CU, ties to the larger workgroup (its activation staging serves
+// more weight rows).  Larger grids run in several waves of workgroups and
+// balance themselves; they keep four wavefronts (measured on MI355X).
+constexpr int kSkinnyNWV[] = {4, 5, 8, 10};
+int skinny_nwv(int64_t N, int64_t S) {
+  if (cdiv(N, 64) * S > 768) return 4;
+  int best = 4;
+  int64_t best_cost = -1;
+  for (int nwv : kSkinnyNWV) {
+    const int64_t wgs = cdiv(N, 16 * nwv) * S;
+    const int64_t cost = cdiv(wgs, 256) * nwv;
+    if (best_cost < 0 || cost <= best_cost) {
+      best = nwv;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool withp = false) {
   SkinnyPlan p;
   const int64_t G = K / kGroup;
   const int64_t t64 = cdiv(N, 64);  // the split depends on N and K only
@@ -1346,7 +1373,8 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K) {
   // two 16-row blocks per wavefront halve the LDS activation reads once the
   // activation tile spans several m-blocks (the bf16 verifier shapes)
   p.NB = (mode == 0 && p.MB >= 2) ? QSPEC_SK_NB16 : 1;
-  p.ntiles = (int)cdiv(N, 64 * p.NB);
+  p.NWV = (p.MB == 1 && !withp) ? skinny_nwv(N, p.S) : 4;
+  p.ntiles = (int)cdiv(N, 16 * p.NB * p.NWV);
   p.mchunks = (int)cdiv(M, 16 * p.MB);
   p.T = p.ntiles * p.mchunks;
   p.blocks = 8 * cdiv(p.T, 8) * p.S;
@@ -1366,6 +1394,24 @@ unsigned int next_epoch() {
 template <int MODE, bool WITHP>
 hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
   dim3 grid((unsigned)p.blocks), block(256);
+  if (p.MB == 1 && p.NWV != 4 && !WITHP) {
+    const dim3 blk(64 * p.NWV);
+    switch (p.NWV) {
+      case 5:
+        if (MODE == kW4A16) hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 5>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, 1, QSPEC_SK_A1, false, 5>), grid, blk, 0, s, a);
+        break;
+      case 8:
+        if (MODE == kW4A16) hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 8>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, 1, QSPEC_SK_A1, false, 8>), grid, blk, 0, s, a);
+        break;
+      default:
+        if (MODE == kW4A16) hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 10>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, 1, QSPEC_SK_A1, false, 10>), grid, blk, 0, s, a);
+        break;
+    }
+    return hipGetLastError();
+  }
   if (MODE == kW4A16) {
     switch (p.MB) {
       case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, WITHP>), grid, block, 0, s, a); break;
@@ -1425,7 +1471,7 @@ hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* X
 }  // namespace
 
 size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  const SkinnyPlan p = plan_skinny(0, M, N, K);
+  const SkinnyPlan p = plan_skinny(0, M, N, K, true);  // four-wavefront tiles: the most counters
   const GemvPlan q = plan_gemv(K);
   const size_t a = p.cnt_bytes + p.part_bytes;
   const size_t b = q.S > 1 ? (size_t)q.S * std::min<int64_t>(M, 4) * N * sizeof(float) : 0;
@@ -1475,7 +1521,7 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
 }
 
 size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  const SkinnyPlan p = plan_skinny(1, M, N, K);
+  const SkinnyPlan p = plan_skinny(1, M, N, K, true);  // four-wavefront tiles: the most counters
   return p.cnt_bytes + p.part_bytes;
 }
 
@@ -1488,7 +1534,7 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
     return launch_tiled<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, s);
   if (v == QSPEC_GEMM_STREAM && P == nullptr)
     return launch_stream<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, s);
-  const SkinnyPlan p = plan_skinny(1, M, N, K);
+  const SkinnyPlan p = plan_skinny(1, M, N, K, P != nullptr);
   SkinnyArgs a{};
   a.X = Xq;
   a.Xs = Xs;

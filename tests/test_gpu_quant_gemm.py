@@ -214,6 +214,23 @@ def test_w4a16_zero_and_lossless_rows():
     assert_close(Y4, oracle.gemm_w4a16(X, Wq, Ws))
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 16448, 256), (7, 24576, 384), (2, 37888, 256)])
+def test_skinny_workgroup_sizes(M, N, K):
+    """Decode shapes whose skinny workgroups are sized to spread evenly over the
+    CUs (5, 8 and 10 wavefronts, ragged last tile): both modes against the
+    oracle."""
+    say(f"skinny workgroup sizes M={M} N={N} K={K}")
+    W, X = _case(23, M, N, K)
+    Wq, Ws = oracle.pack_w4(W)
+    Xq, Xs = oracle.quant_act(X)
+    Wq_d, Ws_d = dev_w(Wq), dev_s(Ws)
+    V = q.GEMM_SKINNY
+    assert_close(host(q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=V, N=N)),
+                 oracle.gemm_w4a16(X, Wq, Ws), what="w4a16")
+    assert_close(host(q.gemm_w4a4(dev(Xq), dev(Xs), Wq_d, Ws_d, variant=V, N=N)),
+                 oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4")
+
+
 # ------------------------------------------------------------------ invariance
 def test_stream_row_invariance_both_modes():
     """STREAM family: rows bitwise identical at M = 16, 5 and 1 (a k-split of
