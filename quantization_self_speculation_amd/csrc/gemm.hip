@@ -1373,7 +1373,7 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool withp = f
   // two 16-row blocks per wavefront halve the LDS activation reads once the
   // activation tile spans several m-blocks (the bf16 verifier shapes)
   p.NB = (mode == 0 && p.MB >= 2) ? QSPEC_SK_NB16 : 1;
-  p.NWV = (p.MB == 1 && !withp) ? skinny_nwv(N, p.S) : 4;
+  p.NWV = ((p.MB == 1 || (mode == 0 && p.MB == 3 && p.NB == 1)) && !withp) ? skinny_nwv(N, p.S) : 4;
   p.ntiles = (int)cdiv(N, 16 * p.NB * p.NWV);
   p.mchunks = (int)cdiv(M, 16 * p.MB);
   p.T = p.ntiles * p.mchunks;
@@ -1394,6 +1394,15 @@ unsigned int next_epoch() {
 template <int MODE, bool WITHP>
 hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
   dim3 grid((unsigned)p.blocks), block(256);
+  if (MODE == kW4A16 && p.MB == 3 && p.NWV != 4 && !WITHP) {
+    const dim3 blk(64 * p.NWV);
+    switch (p.NWV) {
+      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, 1, QSPEC_SK_B3, false, 5>), grid, blk, 0, s, a); break;
+      case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, 1, QSPEC_SK_B3, false, 8>), grid, blk, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, 1, QSPEC_SK_B3, false, 10>), grid, blk, 0, s, a); break;
+    }
+    return hipGetLastError();
+  }
   if (p.MB == 1 && p.NWV != 4 && !WITHP) {
     const dim3 blk(64 * p.NWV);
     switch (p.NWV) {

@@ -214,11 +214,12 @@ def test_w4a16_zero_and_lossless_rows():
     assert_close(Y4, oracle.gemm_w4a16(X, Wq, Ws))
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 16448, 256), (7, 24576, 384), (2, 37888, 256)])
+@pytest.mark.parametrize("M,N,K", [(5, 16448, 256), (7, 24576, 384), (2, 37888, 256),
+                                   (33, 16448, 256), (40, 37888, 256)])
 def test_skinny_workgroup_sizes(M, N, K):
-    """Decode shapes whose skinny workgroups are sized to spread evenly over the
-    CUs (5, 8 and 10 wavefronts, ragged last tile): both modes against the
-    oracle."""
+    """Decode and verify shapes whose skinny workgroups are sized to spread
+    evenly over the CUs (5, 8 and 10 wavefronts, ragged last tile; one and
+    three 16-row activation blocks): both modes against the oracle."""
     say(f"skinny workgroup sizes M={M} N={N} K={K}")
     W, X = _case(23, M, N, K)
     Wq, Ws = oracle.pack_w4(W)
