@@ -69,13 +69,15 @@ enum { QSPEC_VERIFY_GREEDY = 0, QSPEC_VERIFY_SAMPLE = 1 };
  * identical at any M; a caller that needs this (for example greedy
  * self-speculation that must reproduce plain verifier decoding token for
  * token) passes the same explicit family for every M.  AUTO picks by M and
- * N: STREAM for M <= 16 when N < 16384 (where SKINNY would split K across
- * workgroups), else SKINNY up to M = 128, TILED beyond. */
+ * N: STREAM for M <= 16 when N < 16384 (where SKINNY would have too few
+ * workgroups to fill the GPU), else SKINNY up to M = 128, TILED beyond. */
 enum {
   QSPEC_GEMM_AUTO = 0,
   QSPEC_GEMM_GEMV = 1,   /* W4A16 only: VALU GEMV with wavefront reduction   */
-  QSPEC_GEMM_SKINNY = 2, /* MFMA, weights streamed once per 64 rows of M     */
-  QSPEC_GEMM_TILED = 3,  /* MFMA, LDS-tiled over M and N (prefill shapes)    */
+  QSPEC_GEMM_SKINNY = 2, /* MFMA, weights streamed once per up to 64 rows of
+                            M, activations staged in LDS (decode, verify)   */
+  QSPEC_GEMM_TILED = 3,  /* MFMA, weights straight into registers, the
+                            activation slice through LDS (prefill shapes)   */
   QSPEC_GEMM_STREAM = 4  /* MFMA, M <= 16: one 16-row weight block per
                             workgroup, K split across its wavefronts and
                             reduced in LDS (decode shapes)                  */
@@ -144,7 +146,10 @@ qspec_status qspec_quant_act(const uint16_t* X, int64_t M, int64_t K,
  * quantization drafts).  Reading:
  *     P[m,n,g] = sum_{k in group g} qa[m,k] * qw[n,k]     (exact int32)
  *     Y[m,n]   = Xs[m] * sum_g float(Ws[n,g]) * P[m,n,g]  (fp32 epilogue)
- * computed with int8 MFMA on the unpacked codes.
+ * computed with int8 MFMA on the unpacked codes.  P is exact in every
+ * family; the fp32 epilogue's rounding order is the family's (TILED keeps
+ * a biased running sum, which adds at most about 1/85 of one unit of P per
+ * group to the rounding).
  *   Xq [M][K/2], Xs [M]   from qspec_quant_act.
  *   Wq [ceil(N/16)*16][K/2] (tiled), Ws [N][K/128] from qspec_pack_w4.
  *   Y  [M][N] fp32 (out).
