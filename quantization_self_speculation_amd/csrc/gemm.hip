@@ -352,14 +352,18 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
     for (int i = 0; i < XPT; ++i) {
       const int idx = threadIdx.x + NT * i;
       if (XCH % NT != 0 && idx >= XCH) continue;  // workgroup sizes that do not divide the chunk
+      // rows past M are not staged: their LDS rows feed only the MFMA
+      // output columns of rows past M, which are never stored
       if (MODE == kW4A16) {
         const int r = idx / (CH * 16), cc = idx % (CH * 16);
+        if (r >= mrows) continue;
         const uint32_t v[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
         uint32_t p[4];
         bf16x8_interleave(v, p);
         *reinterpret_cast<uint4*>(&xs[buf][r * XSTB + cc * 16]) = make_uint4(p[0], p[1], p[2], p[3]);
       } else if (idx < XCH) {
         const int r = idx / (CH * 4), cc = idx % (CH * 4);
+        if (r >= mrows) continue;
         const uint4 p = xr[i];
         uint8_t* dst = &xs[buf][r * XSTB + (cc >> 2) * 128 + (cc & 3) * 32];
         *reinterpret_cast<uint4*>(dst) =
