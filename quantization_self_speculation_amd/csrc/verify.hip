@@ -353,7 +353,6 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
     const double* __restrict__ pp, int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tok) {
   constexpr int EPT = kRCW / 256;
   __shared__ double wsum[4];
-  __shared__ double tr[kMaxRChunks], tp[kMaxRChunks];
   __shared__ int found;
   __shared__ int lastj;
   __shared__ int sh_cs, sh_cc, sh_kind;
@@ -365,11 +364,8 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
   const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
   const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
 
-  for (int c = tid; c < rnck; c += 256) {
-    tr[c] = rs[b * rnck + c];
-    tp[c] = pp[b * rnck + c];
-  }
-  __syncthreads();
+  const double* tr = rs + b * rnck;  // chunk totals, read by the first wavefront
+  const double* tp = pp + b * rnck;
   if (w == 0) {
     // chunk totals, one wavefront: lane l sums its run of `per` consecutive
     // chunks in order, then an inclusive scan over the lanes (fixed order)
