@@ -613,23 +613,27 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArg
   // activation staging: chunk c = (row (c % 16) + 16 (c / 64), 16 packed
   // bytes (c / 16) % 4 of the group): 16 consecutive lanes write 16 rows of
   // one column of chunks, the pattern of the MFMA operand reads
+  // (resources start at this tile's first row, so 32-bit offsets suffice)
   const bool bstager = tid < BCH;
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(a.X), (short)0, M * (K / 2), 0x00020000);
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(a.X)) + (int64_t)m0 * (K / 2), (short)0,
+      min(BM, M - m0) * (K / 2), 0x00020000);
   uint32_t boff[BC];
   int bdst[BC];
 #pragma unroll
   for (int i = 0; i < BC; ++i) {
     const int c = min(tid + NT * i, BCH - 1);
     const int row = (c & 15) | ((c >> 6) << 4), part = (c >> 4) & 3;
-    boff[i] = (uint32_t)(min(m0 + row, M - 1) * (K / 2) + part * 16);
+    boff[i] = (uint32_t)((min(m0 + row, M - 1) - m0) * (K / 2) + part * 16);
     bdst[i] = row * RST + part * 32;
   }
   // scale staging: thread tid stages column tid of the tile
   const int scol = nt * BN + tid;
+  const int srb0 = min(nt * (BN / 16), nrb - 1);
   const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.Ws), (short)0, nrb * G * 32, 0x00020000);
-  const uint32_t soff = (uint32_t)((min(scol >> 4, nrb - 1) * G * 16 + (scol & 15)) * 2);
+      const_cast<uint16_t*>(a.Ws) + (int64_t)srb0 * G * 16, (short)0,
+      min(BN / 16, nrb - srb0) * G * 32, 0x00020000);
+  const uint32_t soff = (uint32_t)(((min(scol >> 4, nrb - 1) - srb0) * G * 16 + (scol & 15)) * 2);
 
   struct BStage {
     uint4 x[BC];
@@ -847,14 +851,15 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a16_prefill_kernel(const TiledAr
   // (c / 16) % 16 of the row's 256-byte group slice): 16 consecutive lanes
   // write 16 rows of one column of chunks, the pattern of the operand reads
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(a.X), (short)0, M * K * 2, 0x00020000);
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(a.X)) + (int64_t)m0 * K * 2, (short)0,
+      min(BM, M - m0) * K * 2, 0x00020000);  // this tile's rows: 32-bit offsets suffice
   uint32_t boff[BC];
   int bdst[BC];
 #pragma unroll
   for (int i = 0; i < BC; ++i) {
     const int c = tid + NT * i;
     const int row = (c & 15) | ((c >> 8) << 4), part = (c >> 4) & 15;
-    boff[i] = (uint32_t)(min(m0 + row, M - 1) * K * 2 + part * 16);
+    boff[i] = (uint32_t)((min(m0 + row, M - 1) - m0) * K * 2 + part * 16);
     bdst[i] = row * RST + part * 16;
   }
   struct BStage {
