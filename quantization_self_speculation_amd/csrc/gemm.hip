@@ -552,6 +552,11 @@ struct TiledArgs {
 //   * activations: the 64 x 64-byte group slice is staged in LDS once per
 //     workgroup, widened to int8 (16 q), double-buffered, one barrier per
 //     group;
+//   * persistent grid (two workgroups per CU): each workgroup walks its
+//     tiles one after the other with the group pipeline running on across
+//     tile boundaries, so a finished tile's fp32 stores drain while the next
+//     tile's loads and MFMAs proceed (3 % faster than one tile per
+//     workgroup; the stores of a wave of tiles otherwise all land at once);
 //   * epilogue without an int -> float conversion (with one, convert then
 //     FMA, the kernel runs at a third of this rate on MI355X): the first MFMA
 //     of each group starts from the integer bit pattern of B = 1.5 * 2^23, so
@@ -585,73 +590,124 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArg
   __shared__ __attribute__((aligned(16))) float Ss[2][BN];
   __shared__ __attribute__((aligned(16))) float Cs[2][BN];
 
-  const int b = blockIdx.x;
-  const int xcd = b & 7, loc = b >> 3;
-  const int nt = 8 * (loc / a.ntm) + xcd, mt = loc % a.ntm;
-  if (nt >= a.ntn) return;  // padding block (uniform)
   const int M = a.M, N = a.N, K = a.K;
   const int G = K / kGroup;
+  const int ntn = a.ntn, ntm = a.ntm;
+  const int P = gridDim.x;  // a multiple of 8
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int l16 = lane & 15, lg = lane >> 4;
   const int nrb = (N + 15) / 16;
-  const int m0 = mt * BM;
 
-  // All loads go through buffer resources: the group advances a uniform
-  // offset (no per-lane address arithmetic in the loop).
-  // weight tiles of this wavefront: row blocks rbw .. rbw + 3 (clamped to
-  // the last block), slot `lane`
-  const int rbw = min(nt * (BN / 16) + wn * 4, nrb - 1);
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.Wq) + (int64_t)rbw * G * 1024, (short)0, min(4, nrb - rbw) * G * 1024,
-      0x00020000);
-  uint32_t woff[4];
+  // Tiles of this workgroup: tile k is tau = blockIdx.x + k P of the
+  // XCD-dealt order (tau & 7 stays this block's XCD; each XCD walks the m-tiles
+  // of an n-tile together).  nt does not decrease with k, so the valid tiles
+  // (nt < ntn) are the first nk.
+  const int ntau = 8 * ((ntn + 7) / 8) * ntm;
+  auto tile_nt = [&](int kk) {
+    const int tau = (int)blockIdx.x + kk * P;
+    return 8 * ((tau >> 3) / ntm) + (tau & 7);
+  };
+  auto tile_m0 = [&](int kk) {
+    const int tau = (int)blockIdx.x + kk * P;
+    return ((tau >> 3) % ntm) * BM;
+  };
+  int nk = 0;
+  while ((int)blockIdx.x + nk * P < ntau && tile_nt(nk) < ntn) ++nk;
+  if (nk == 0) return;  // uniform
+  const int S = nk * G;  // group steps of this workgroup, tile after tile
+
+  // Three streams walk the steps (tile k, group g) in order, each with its
+  // own position: the weight ring (PD steps ahead of the MFMAs), the
+  // activation and scale loads (3 ahead) and the compute.  Buffer resources
+  // start at the current tile of their stream, so offsets stay 32-bit; past
+  // the last step a stream re-reads its last step (never used).
+  // weights: row blocks rbw .. rbw + 3 of the tile (clamped), slot `lane`
+  __amdgpu_buffer_rsrc_t wres;
+  int woff[4];  // wavefront-uniform block offsets; the lane's slot is lane * 16
+  const uint32_t wlane = (uint32_t)lane * 16;
+  int wk = 0, wg = 0;
+  auto w_tile = [&](int kk) {
+    const int nt = tile_nt(kk);
+    const int rbw = min(nt * (BN / 16) + wn * 4, nrb - 1);
+    wres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.Wq) + (int64_t)rbw * G * 1024,
+                                             (short)0, min(4, nrb - rbw) * G * 1024, 0x00020000);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    woff[nb] = (uint32_t)((min(nt * (BN / 16) + wn * 4 + nb, nrb - 1) - rbw) * G * 1024 + lane * 16);
-  // activation staging: chunk c = (row (c % 16) + 16 (c / 64), 16 packed
-  // bytes (c / 16) % 4 of the group): 16 consecutive lanes write 16 rows of
-  // one column of chunks, the pattern of the MFMA operand reads
-  // (resources start at this tile's first row, so 32-bit offsets suffice)
+    for (int nb = 0; nb < 4; ++nb)
+      woff[nb] = (min(nt * (BN / 16) + wn * 4 + nb, nrb - 1) - rbw) * G * 1024;
+  };
+  auto w_advance = [&]() {
+    const bool wrap = wg + 1 == G, more = wk + 1 < nk;
+    wg = wrap ? (more ? 0 : G - 1) : wg + 1;
+    if (wrap && more) {  // uniform
+      wk = wk + 1;
+      w_tile(wk);
+    }
+  };
+  auto wload = [&](int nb) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wres, wlane, woff[nb] + wg * 1024, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  };
+  // activations: chunk c = (row (c % 16) + 16 (c / 64), 16 packed bytes
+  // (c / 16) % 4 of the group): 16 consecutive lanes write 16 rows of one
+  // column of chunks, the pattern of the MFMA operand reads; scales: thread
+  // tid stages column tid of the tile
   const bool bstager = tid < BCH;
-  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(static_cast<const uint8_t*>(a.X)) + (int64_t)m0 * (K / 2), (short)0,
-      min(BM, M - m0) * (K / 2), 0x00020000);
+  __amdgpu_buffer_rsrc_t xres, sres;
   uint32_t boff[BC];
   int bdst[BC];
+  uint32_t soff;
+  int xk = 0, xg = 0;
 #pragma unroll
   for (int i = 0; i < BC; ++i) {
     const int c = min(tid + NT * i, BCH - 1);
     const int row = (c & 15) | ((c >> 6) << 4), part = (c >> 4) & 3;
-    boff[i] = (uint32_t)((min(m0 + row, M - 1) - m0) * (K / 2) + part * 16);
     bdst[i] = row * RST + part * 32;
   }
-  // scale staging: thread tid stages column tid of the tile
-  const int scol = nt * BN + tid;
-  const int srb0 = min(nt * (BN / 16), nrb - 1);
-  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.Ws) + (int64_t)srb0 * G * 16, (short)0,
-      min(BN / 16, nrb - srb0) * G * 32, 0x00020000);
-  const uint32_t soff = (uint32_t)(((min(scol >> 4, nrb - 1) - srb0) * G * 16 + (scol & 15)) * 2);
-
+  auto x_tile = [&](int kk) {
+    const int nt = tile_nt(kk), m0 = tile_m0(kk);
+    xres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(a.X)) + (int64_t)m0 * (K / 2), (short)0,
+        min(BM, M - m0) * (K / 2), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < BC; ++i) {
+      const int c = min(tid + NT * i, BCH - 1);
+      const int row = (c & 15) | ((c >> 6) << 4), part = (c >> 4) & 3;
+      boff[i] = (uint32_t)((min(m0 + row, M - 1) - m0) * (K / 2) + part * 16);
+    }
+    const int scol = nt * BN + tid;
+    const int srb0 = min(nt * (BN / 16), nrb - 1);
+    sres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.Ws) + (int64_t)srb0 * G * 16,
+                                             (short)0, min(BN / 16, nrb - srb0) * G * 32, 0x00020000);
+    soff = (uint32_t)(((min(scol >> 4, nrb - 1) - srb0) * G * 16 + (scol & 15)) * 2);
+  };
+  auto x_advance = [&]() {
+    const bool wrap = xg + 1 == G, more = xk + 1 < nk;
+    xg = wrap ? (more ? 0 : G - 1) : xg + 1;
+    if (wrap && more) {  // uniform
+      xk = xk + 1;
+      x_tile(xk);
+    }
+  };
   struct BStage {
     uint4 x[BC];
     uint16_t s;
   };
-  auto bload = [&](BStage& st, int g) {
-    const int gg = min(g, G - 1);
+  auto bload = [&](BStage& st) {
     if (bstager) {
 #pragma unroll
       for (int i = 0; i < BC; ++i) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, boff[i], gg * 64, 0);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, boff[i], xg * 64, 0);
         st.x[i] = make_uint4(v.x, v.y, v.z, v.w);
       }
     }
-    st.s = __builtin_amdgcn_raw_buffer_load_b16(sres, soff, gg * 32, 0);
+    st.s = __builtin_amdgcn_raw_buffer_load_b16(sres, soff, xg * 32, 0);
+    x_advance();
   };
   float ssum = 0.f;  // this thread's column: sum of the scales of the open chunk
-  auto bstore = [&](const BStage& st, int buf, int g) {
+  // stage a step whose group index in its tile is gs
+  auto bstore = [&](const BStage& st, int buf, int gs) {
     if (bstager) {
 #pragma unroll
       for (int i = 0; i < BC; ++i) {
@@ -666,7 +722,7 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArg
     const float sv = half_bits_to_float(st.s) * 0.00390625f;  // / 256 (both operands are 16 q)
     Ss[buf][tid] = sv;
     ssum += sv;
-    if (g % CH == CH - 1 || g == G - 1) {  // uniform: the chunk closes with group g
+    if (gs % CH == CH - 1 || gs == G - 1) {  // uniform: the chunk closes with group gs
       Cs[buf][tid] = kBias * ssum;
       ssum = 0.f;
     }
@@ -679,24 +735,27 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArg
     for (int j = 0; j < 4; ++j) tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4i cbias = {(int)kBiasBits, (int)kBiasBits, (int)kBiasBits, (int)kBiasBits};
 
-  auto wload = [&](int nb, int g) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[nb], g * 1024, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
-  };
+  w_tile(0);
+  x_tile(0);
   uint4 ring[PD][4];
 #pragma unroll
-  for (int i = 0; i < PD; ++i)
+  for (int i = 0; i < PD; ++i) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) ring[i][nb] = wload(nb, min(i, G - 1));
+    for (int nb = 0; nb < 4; ++nb) ring[i][nb] = wload(nb);
+    w_advance();
+  }
   BStage bst[2];
-  bload(bst[0], 0);
-  bload(bst[1], 1);
+  bload(bst[0]);  // step 0
+  bload(bst[1]);  // step 1
   bstore(bst[0], 0, 0);
-  bload(bst[0], 2);
+  bload(bst[0]);  // step 2
   __syncthreads();
 
-  // one group; u = g mod U fixes the ring slot and the LDS buffer at compile time
-  auto step = [&](auto uc, int g) {
+  int ck = 0, cg = 0;  // the compute stream's tile and group
+  const bool vec = (N & 3) == 0;
+  // one group step; u = s mod U fixes the ring slot and the LDS buffer at
+  // compile time
+  auto step = [&](auto uc, int s) {
     constexpr int u = decltype(uc)::value;
     const int buf = u & 1;
     const uint8_t* Bb = &Bs[buf][l16 * RST + lg * 32];
@@ -706,15 +765,14 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArg
       bf[mb][0] = *reinterpret_cast<const v4i*>(Bb + mb * 16 * RST);
       bf[mb][1] = *reinterpret_cast<const v4i*>(Bb + mb * 16 * RST + 16);
     }
-    const int gn = min(g + PD, G - 1);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      // this group's weights of block nb, widened; the ring slot then
-      // takes group g + PD
+      // this step's weights of block nb, widened; the ring slot then takes
+      // the weight stream's next step
       const uint4 p = ring[u % PD][nb];
       const v4i a0 = {(int)w4_lo_x16(p.x), (int)w4_hi_x16(p.x), (int)w4_lo_x16(p.y), (int)w4_hi_x16(p.y)};
       const v4i a1 = {(int)w4_lo_x16(p.z), (int)w4_hi_x16(p.z), (int)w4_lo_x16(p.w), (int)w4_hi_x16(p.w)};
-      ring[u % PD][nb] = wload(nb, gn);
+      ring[u % PD][nb] = wload(nb);
       const float4 sc = *reinterpret_cast<const float4*>(&Ss[buf][wn * 64 + nb * 16 + lg * 4]);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
@@ -726,7 +784,8 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArg
         tot[nb][mb][3] = fmaf(sc.w, __int_as_float(acc[3]), tot[nb][mb][3]);
       }
     }
-    if (g % CH == CH - 1 || g == G - 1) {  // uniform: drop the chunk's bias
+    w_advance();
+    if (cg % CH == CH - 1 || cg == G - 1) {  // uniform: drop the chunk's bias
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const float4 cr = *reinterpret_cast<const float4*>(&Cs[buf][wn * 64 + nb * 16 + lg * 4]);
@@ -739,58 +798,70 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArg
         }
       }
     }
-    // stage group g + 1 into the other buffer (its readers, group g - 1,
-    // all passed the previous barrier), then fetch group g + 3
-    if (g + 1 < G) bstore(bst[(u + 1) & 1], buf ^ 1, g + 1);
-    bload(bst[(u + 1) & 1], g + 3);
+    if (cg == G - 1) {  // uniform: the tile is complete; its stores drain
+                        // while the next tile computes
+      const int m0 = tile_m0(ck), n0 = tile_nt(ck) * BN + wn * 64 + lg * 4;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int m = m0 + mb * 16 + l16;
+          const int n = n0 + nb * 16;
+          if (m < M && n < N) {
+            const float xsc = a.Xs[m];
+            const float v0 = xsc * tot[nb][mb][0], v1 = xsc * tot[nb][mb][1];
+            const float v2 = xsc * tot[nb][mb][2], v3 = xsc * tot[nb][mb][3];
+            float* dst = a.Y + (int64_t)m * N + n;
+            if (vec) {
+              *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+            } else {
+              const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (n + r < N) dst[r] = v[r];
+            }
+          }
+          tot[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    {
+      const bool last = cg == G - 1;
+      ck = ck + (last ? 1 : 0);
+      cg = last ? 0 : cg + 1;
+    }
+    // stage step s + 1 into the other buffer (its readers, step s - 1, all
+    // passed the previous barrier), then fetch step s + 3
+    if (s + 1 < S) bstore(bst[(u + 1) & 1], buf ^ 1, cg);
+    bload(bst[(u + 1) & 1]);
     __syncthreads();
   };
-  int g = 0;
-  for (; g + U <= G; g += U) {
-    step(std::integral_constant<int, 0>{}, g);
-    step(std::integral_constant<int, 1>{}, g + 1);
+  int s0 = 0;
+  for (; s0 + U <= S; s0 += U) {
+    step(std::integral_constant<int, 0>{}, s0);
+    step(std::integral_constant<int, 1>{}, s0 + 1);
     if constexpr (U > 2) {
-      step(std::integral_constant<int, 2>{}, g + 2);
-      step(std::integral_constant<int, 3>{}, g + 3);
+      step(std::integral_constant<int, 2>{}, s0 + 2);
+      step(std::integral_constant<int, 3>{}, s0 + 3);
     }
   }
-  // tail: fewer than U groups left, g is a multiple of U
-  if (g < G) step(std::integral_constant<int, 0>{}, g);
+  // tail: fewer than U steps left, s0 is a multiple of U
+  if (s0 < S) step(std::integral_constant<int, 0>{}, s0);
   if constexpr (U > 2) {
-    if (g + 1 < G) step(std::integral_constant<int, 1>{}, g + 1);
-    if (g + 2 < G) step(std::integral_constant<int, 2>{}, g + 2);
+    if (s0 + 1 < S) step(std::integral_constant<int, 1>{}, s0 + 1);
+    if (s0 + 2 < S) step(std::integral_constant<int, 2>{}, s0 + 2);
   }
-
-  const bool vec = (N & 3) == 0;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + mb * 16 + l16;
-      const int n = nt * BN + wn * 64 + nb * 16 + lg * 4;
-      if (m < M && n < N) {
-        const float xsc = a.Xs[m];
-        const float v0 = xsc * tot[nb][mb][0], v1 = xsc * tot[nb][mb][1];
-        const float v2 = xsc * tot[nb][mb][2], v3 = xsc * tot[nb][mb][3];
-        float* dst = a.Y + (int64_t)m * N + n;
-        if (vec) {
-          *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
-        } else {
-          const float v[4] = {v0, v1, v2, v3};
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) dst[r] = v[r];
-        }
-      }
-    }
 }
 
+#ifndef QSPEC_PF_GRID
+#define QSPEC_PF_GRID 512  // persistent workgroups: two per CU
+#endif
 template <int WN, int PD, int CH>
 hipError_t launch_w4a4_prefill(TiledArgs a, hipStream_t s) {
   a.ntn = (int)cdiv(a.N, 64 * WN);
   a.ntm = (int)cdiv(a.M, 64);
-  const int64_t blocks = 8 * cdiv(a.ntn, 8) * a.ntm;
-  hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH>), dim3((unsigned)blocks), dim3(64 * WN), 0,
+  const int64_t tiles = 8 * cdiv(a.ntn, 8) * a.ntm;  // a multiple of 8, as is the grid
+  const int64_t grid = std::min<int64_t>(tiles, QSPEC_PF_GRID);
+  hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH>), dim3((unsigned)grid), dim3(64 * WN), 0,
                      s, a);
   return hipGetLastError();
 }
