@@ -1180,55 +1180,65 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   for (int i = 0; i < PD; ++i) load(ring[i], g0 + i);
   const v8bf negb = as_v8bf(kNegBiasPair, kNegBiasPair, kNegBiasPair, kNegBiasPair);
 
-  for (int gb = g0; gb < g1; gb += PD) {
+  // one group from ring stage i
+  auto group = [&](int i) {
+    const StreamStage<MODE>& st = ring[i];
+    const uint32_t s01 = st.s.x, s23 = st.s.y;
+    if (MODE == kW4A16) {
+      // bf16(136 + q) x activations, then the -136 chain into the same
+      // accumulator: acc = sum_k x (136 + q) - 136 sum_k x
+      const uint32_t wv[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      v8bf B[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t aw[4], xi[4];
+        const uint32_t xw[4] = {st.x[j].x, st.x[j].y, st.x[j].z, st.x[j].w};
+        w4_to_bf16_biased(wv[j], aw);
+        bf16x8_interleave(xw, xi);
+        B[j] = as_v8bf(xi[0], xi[1], xi[2], xi[3]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(aw[0], aw[1], aw[2], aw[3]), B[j],
+                                                      acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(negb, B[j], acc, 0, 0, 0);
+      tot[0] = fmaf(half_bits_to_float((uint16_t)(s01 & 0xFFFF)), acc[0], tot[0]);
+      tot[1] = fmaf(half_bits_to_float((uint16_t)(s01 >> 16)), acc[1], tot[1]);
+      tot[2] = fmaf(half_bits_to_float((uint16_t)(s23 & 0xFFFF)), acc[2], tot[2]);
+      tot[3] = fmaf(half_bits_to_float((uint16_t)(s23 >> 16)), acc[3], tot[3]);
+    } else {
+      const uint4 p = st.w, x = st.x[0];
+      const v4i a0 = {(int)w4_lo_x16(p.x), (int)w4_hi_x16(p.x), (int)w4_lo_x16(p.y), (int)w4_hi_x16(p.y)};
+      const v4i a1 = {(int)w4_lo_x16(p.z), (int)w4_hi_x16(p.z), (int)w4_lo_x16(p.w), (int)w4_hi_x16(p.w)};
+      const v4i b0 = {(int)w4_lo_x16(x.x), (int)w4_hi_x16(x.x), (int)w4_lo_x16(x.y), (int)w4_hi_x16(x.y)};
+      const v4i b1 = {(int)w4_lo_x16(x.z), (int)w4_hi_x16(x.z), (int)w4_lo_x16(x.w), (int)w4_hi_x16(x.w)};
+      v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
+      tot[0] = fmaf(half_bits_to_float((uint16_t)(s01 & 0xFFFF)) * 0.00390625f, (float)acc[0], tot[0]);
+      tot[1] = fmaf(half_bits_to_float((uint16_t)(s01 >> 16)) * 0.00390625f, (float)acc[1], tot[1]);
+      tot[2] = fmaf(half_bits_to_float((uint16_t)(s23 & 0xFFFF)) * 0.00390625f, (float)acc[2], tot[2]);
+      tot[3] = fmaf(half_bits_to_float((uint16_t)(s23 >> 16)) * 0.00390625f, (float)acc[3], tot[3]);
+    }
+  };
+  // Full rounds of PD groups carry no condition, so the compiler keeps every
+  // ring load in flight across the waits (a conditional use of a ring stage
+  // inside the loop made it wait for all outstanding loads each round).
+  int gb = g0;
+  for (; gb + PD <= g1; gb += PD) {
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
-      const int g = gb + i;
-      const StreamStage<MODE>& st = ring[i];
-      const uint32_t s01 = st.s.x, s23 = st.s.y;
-      if (MODE == kW4A16) {
-        // bf16(136 + q) x activations, then the -136 chain into the same
-        // accumulator: acc = sum_k x (136 + q) - 136 sum_k x
-        const uint32_t wv[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        v8bf B[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t aw[4], xi[4];
-          const uint32_t xw[4] = {st.x[j].x, st.x[j].y, st.x[j].z, st.x[j].w};
-          w4_to_bf16_biased(wv[j], aw);
-          bf16x8_interleave(xw, xi);
-          B[j] = as_v8bf(xi[0], xi[1], xi[2], xi[3]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(aw[0], aw[1], aw[2], aw[3]), B[j],
-                                                        acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(negb, B[j], acc, 0, 0, 0);
-        if (g < g1) {
-          tot[0] = fmaf(half_bits_to_float((uint16_t)(s01 & 0xFFFF)), acc[0], tot[0]);
-          tot[1] = fmaf(half_bits_to_float((uint16_t)(s01 >> 16)), acc[1], tot[1]);
-          tot[2] = fmaf(half_bits_to_float((uint16_t)(s23 & 0xFFFF)), acc[2], tot[2]);
-          tot[3] = fmaf(half_bits_to_float((uint16_t)(s23 >> 16)), acc[3], tot[3]);
-        }
-      } else {
-        const uint4 p = st.w, x = st.x[0];
-        const v4i a0 = {(int)w4_lo_x16(p.x), (int)w4_hi_x16(p.x), (int)w4_lo_x16(p.y), (int)w4_hi_x16(p.y)};
-        const v4i a1 = {(int)w4_lo_x16(p.z), (int)w4_hi_x16(p.z), (int)w4_lo_x16(p.w), (int)w4_hi_x16(p.w)};
-        const v4i b0 = {(int)w4_lo_x16(x.x), (int)w4_hi_x16(x.x), (int)w4_lo_x16(x.y), (int)w4_hi_x16(x.y)};
-        const v4i b1 = {(int)w4_lo_x16(x.z), (int)w4_hi_x16(x.z), (int)w4_lo_x16(x.w), (int)w4_hi_x16(x.w)};
-        v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
-        if (g < g1) {
-          tot[0] = fmaf(half_bits_to_float((uint16_t)(s01 & 0xFFFF)) * 0.00390625f, (float)acc[0], tot[0]);
-          tot[1] = fmaf(half_bits_to_float((uint16_t)(s01 >> 16)) * 0.00390625f, (float)acc[1], tot[1]);
-          tot[2] = fmaf(half_bits_to_float((uint16_t)(s23 & 0xFFFF)) * 0.00390625f, (float)acc[2], tot[2]);
-          tot[3] = fmaf(half_bits_to_float((uint16_t)(s23 >> 16)) * 0.00390625f, (float)acc[3], tot[3]);
-        }
-      }
-      load(ring[i], g + PD);  // refill this stage, PD groups ahead
+      group(i);
+      load(ring[i], gb + i + PD);  // refill this stage, PD groups ahead
+      // issue the refill here, before the next group's arithmetic (left to
+      // itself the scheduler sinks every refill to the end of the round, so
+      // the next round waits for all of them)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+#pragma unroll
+  for (int i = 0; i < PD - 1; ++i)
+    if (gb + i < g1) group(i);  // tail: fewer than PD groups
 
   // k-slices -> one sum per output, in slice order
   if (nw > 1) {
