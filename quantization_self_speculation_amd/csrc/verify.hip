@@ -93,16 +93,19 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
     const int64_t q = q0 + tid + 256 * k;
     v[k] = q < q1 ? qp[q] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
   }
-  float hv = -INFINITY;  // head (chunk 0) or tail (last chunk) element
-  int hi = 0x7FFFFFFF;
+  // scalar head (chunk 0) and tail (last chunk) elements: one thread may
+  // hold one of each when the row has a single chunk
+  float hv = -INFINITY, tv = -INFINITY;
+  int hi = 0x7FFFFFFF, ti = 0x7FFFFFFF;
   if (c == 0 && tid < a0) {
     hv = rp[tid];
     hi = tid;
-  } else if (c == nck - 1) {
+  }
+  if (c == nck - 1) {
     const int64_t t0 = a0 + 4 * nq;
     if (t0 + tid < V) {
-      hv = rp[t0 + tid];
-      hi = (int)(t0 + tid);
+      tv = rp[t0 + tid];
+      ti = (int)(t0 + tid);
     }
   }
 
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
   if (GREEDY) {
     float bv = hv;
     int bi = hi;
+    argmax_merge(bv, bi, tv, ti);
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       const int i = (int)(a0 + 4 * (q0 + tid + 256 * k));
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
     return;
   }
   // sampling: the chunk max first, then every exponential relative to it
-  float mx = hv;
+  float mx = fmaxf(hv, tv);
 #pragma unroll
   for (int k = 0; k < QPT; ++k) mx = fmaxf(mx, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
   mx = wave_max(mx);
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
   mx = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
   double s = 0.0;
   if (mx != -INFINITY) {
-    s = (double)exp_diff(hv, mx);
+    s = (double)exp_diff(hv, mx) + (double)exp_diff(tv, mx);
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       // four terms in fp32 (each within ~1 ulp), then into the fp64 sum

@@ -34,6 +34,7 @@ SHAPES = [
     (16, 3584, 18944),
     (11, 200, 2688),
     (9, 40, 128),
+    (1, 1, 128),
 ]
 
 
@@ -351,6 +352,26 @@ def test_qwen7b_prefill_shapes(proj):
     Y4 = host(q.gemm_w4a4(Xq_d, Xs_d, Wq_d, Ws_d, N=N))
     Xq, Xs = oracle.quant_act(X[rows])
     assert_close(Y4[np.ix_(rows, cols)], oracle.gemm_w4a4(Xq, Xs, Wq, Ws))
+
+
+@pytest.mark.parametrize("K", [128, 384])
+def test_tiled_several_tiles_per_workgroup(K):
+    """The W4A4 prefill grid is persistent (512 workgroups walking the
+    tiles): M = 2100, N = 4000 makes 528 tile slots, so the first workgroups
+    carry a second tile, with ragged M and N tails and one or three groups
+    per tile (the group pipeline runs across the tile boundary)."""
+    M, N = 2100, 4000
+    say(f"tiled several tiles per workgroup K={K}")
+    rng = synth.make_rng(23)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K, n_outliers=1)
+    Wq, Ws = oracle.pack_w4(W)
+    Xq, Xs = oracle.quant_act(X)
+    Wq_d, Ws_d = dev_w(Wq), dev_s(Ws)
+    Y = q.gemm_w4a4(dev(Xq), dev(Xs), Wq_d, Ws_d, variant=q.GEMM_TILED, N=N)
+    assert_close(host(Y), oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4 tiled, several tiles")
+    Y16 = q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=q.GEMM_TILED, N=N)
+    assert_close(host(Y16), oracle.gemm_w4a16(X, Wq, Ws), what="w4a16 tiled")
 
 
 def test_llama8b_lm_head_gemv():

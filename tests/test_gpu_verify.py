@@ -107,6 +107,52 @@ def test_sampling_identical_logits_falls_back_to_p():
     assert np.array_equal(host(out)[ok], out_ref[ok])
 
 
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 6, 7])
+def test_degenerate_vocabularies(V):
+    """Vocabularies of one to seven tokens (rows start at every alignment, a
+    row is a scalar head and tail around at most one float4): greedy with
+    argmax drafts accepts everything; sampling follows the oracle (at V = 1,
+    p = q = 1, so every draft is accepted and the bonus token is 0)."""
+    B, gamma = 3, 2
+    say(f"verify degenerate V={V}")
+    rng, tgt, drf = _logits(36, B, gamma, V)
+    d = np.argmax(tgt[:, :gamma], axis=-1).astype(np.int32)
+    n_ref, out_ref = oracle.verify_greedy(tgt, d)
+    assert np.all(n_ref == gamma)
+    n, out = q.verify(q.VERIFY_GREEDY, dev(tgt), dev(d))
+    assert np.array_equal(host(n), n_ref)
+    assert np.array_equal(host(out), out_ref)
+    d = synth.gumbel_drafts(rng, drf)
+    ua = synth.uniforms(rng, (B, gamma))
+    us = synth.uniforms(rng, (B,))
+    n_ref, out_ref, flag = oracle.verify_sample(tgt, drf, d, ua, us)
+    n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
+    ok = ~flag
+    assert np.array_equal(host(n)[ok], n_ref[ok])
+    assert np.array_equal(host(out)[ok], out_ref[ok])
+    if V == 1:
+        assert np.all(n_ref == gamma) and np.all(out_ref == 0)
+
+
+@pytest.mark.parametrize("V", [5, 1001, 8195])
+def test_greedy_argmax_at_row_ends(V):
+    """Rows that fit one pass-1 chunk and start unaligned have a scalar head
+    and a scalar tail: the argmax planted at each of the first and last three
+    positions must be found (drafts equal to it are all accepted)."""
+    B, gamma = 2, 3
+    _, tgt0, _ = _logits(37, B, gamma, V)
+    for pos in (0, 1, 2, V - 3, V - 2, V - 1):
+        say(f"verify greedy argmax at {pos} of V={V}")
+        tgt = tgt0.copy()
+        tgt[..., pos] = 100.0
+        d = np.full((B, gamma), pos, np.int32)
+        n_ref, out_ref = oracle.verify_greedy(tgt, d)
+        assert np.all(n_ref == gamma) and np.all(out_ref == pos)
+        n, out = q.verify(q.VERIFY_GREEDY, dev(tgt), dev(d))
+        assert np.array_equal(host(n), n_ref)
+        assert np.array_equal(host(out), out_ref)
+
+
 def test_verify_deterministic():
     B, gamma, V = 32, 4, 128256
     rng, tgt, drf = _logits(35, B, gamma, V)
