@@ -103,6 +103,22 @@ def test_quant_act_bitexact(M, K, outl):
     assert np.array_equal(host(Xs).view(np.uint32), Xs_ref.view(np.uint32))
 
 
+# every row-length band of the quantizer's launch (16-byte chunks per row:
+# <= 512, <= 2048, <= 4096, <= 8192, and the two-pass kernel beyond), at
+# both sides of each boundary, up to the largest K the library accepts
+@pytest.mark.parametrize("K", [4096, 4224, 16384, 16512, 32768, 32896, 65536, 65664, 1 << 20])
+def test_quant_act_row_length_bands(K):
+    M = 3
+    say(f"quant_act band K={K}")
+    rng = synth.make_rng(24)
+    X = synth.activations(rng, M, K, n_outliers=synth.outlier_count(K))
+    X[1, K - 1] = synth.to_bf16_bits(np.array([-512.0], np.float32))[0]  # absmax at the last element
+    Xq_ref, Xs_ref = oracle.quant_act(X)
+    Xq, Xs = q.quant_act(dev_bf16(X))
+    assert np.array_equal(host(Xq), Xq_ref)
+    assert np.array_equal(host(Xs).view(np.uint32), Xs_ref.view(np.uint32))
+
+
 def test_quant_act_hand_ties_subnormal_and_division(golden):
     g = golden("quant_act_hand.json")
     rows = g["rows"]

@@ -18,9 +18,10 @@ from gpu_util import dev, host, say
 pytestmark = pytest.mark.gpu
 
 # (B, gamma, V): the single-layer case, unaligned row starts, several
-# pass-1 chunks with ragged tails, and the Llama-3-8B vocabulary at batch 32
+# pass-1 chunks with ragged tails, the Llama-3-8B vocabulary at batch 32, one
+# draft per sequence, and a second pass-1 chunk holding one quad and a tail
 CASES = [(1, 4, 1024), (3, 2, 1000), (5, 3, 50257), (2, 16, 8195), (32, 4, 128256),
-         (32, 8, 128256)]
+         (32, 8, 128256), (4, 1, 8199), (6, 1, 4099)]
 
 
 def _logits(seed, B, gamma, V):
