@@ -390,6 +390,29 @@ def test_tiled_several_tiles_per_workgroup(K):
     assert_close(host(Y16), oracle.gemm_w4a16(X, Wq, Ws), what="w4a16 tiled")
 
 
+def test_largest_k():
+    """K = 2^20 (8192 groups, the largest the library accepts) in every
+    family of both modes: the k-split plans and the 32-bit buffer offsets at
+    their limit."""
+    M, N, K = 3, 40, 1 << 20
+    rng = synth.make_rng(25)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K, n_outliers=synth.outlier_count(K))
+    Wq, Ws = oracle.pack_w4(W)
+    Xq, Xs = oracle.quant_act(X)
+    Wq_d, Ws_d = dev_w(Wq), dev_s(Ws)
+    want4 = oracle.gemm_w4a4(Xq, Xs, Wq, Ws)
+    want16 = oracle.gemm_w4a16(X, Wq, Ws)
+    for v in W4A4_VARIANTS:
+        say(f"largest K w4a4 variant={v}")
+        Y = q.gemm_w4a4(dev(Xq), dev(Xs), Wq_d, Ws_d, variant=v, N=N)
+        assert_close(host(Y), want4, what=f"w4a4 K=2^20 variant={v}")
+    for v in W4A16_VARIANTS:
+        say(f"largest K w4a16 variant={v}")
+        Y = q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=v, N=N)
+        assert_close(host(Y), want16, what=f"w4a16 K=2^20 variant={v}")
+
+
 def test_llama8b_lm_head_gemv():
     N, K = LLAMA8B_HEAD
     rng = synth.make_rng(3)
