@@ -292,14 +292,14 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ x
     for (int i = 0; i < 4; ++i) v[i] = r[j + 256 * i];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (v[i] > best) {
+      if (v[i] > best || idx == 0x7FFFFFFF) {  // the first value counts even at -inf
         best = v[i];
         idx = (int)(j + 256 * i);
       }
   }
   for (; j < V; j += 256) {
     const float v = r[j];
-    if (v > best) {
+    if (v > best || idx == 0x7FFFFFFF) {
       best = v;
       idx = (int)j;
     }

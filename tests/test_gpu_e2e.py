@@ -107,12 +107,15 @@ def test_silu_mul_and_argmax():
     x[1, 10] = x[1, 900] = x[1].max() + 1.0          # tie: the lower index wins
     x[2, :] = 0.0                                     # all equal: index 0
     x[3, V - 1] = 50.0
+    x[4, :] = -np.inf                                 # all -inf: index 0
+    x[5, :] = -np.inf
+    x[5, 777] = -1e30                                 # one finite value among -inf
     out = torch.full((12,), -7, dtype=torch.int32, device="cuda:0")
     qb.argmax(dev(x), out, out_stride=2)
     got = host(out)
     assert np.array_equal(got[0::2], om.argmax_first(x))
     assert np.all(got[1::2] == -7)
-    assert got[2] == 10 and got[4] == 0 and got[6] == V - 1
+    assert got[2] == 10 and got[4] == 0 and got[6] == V - 1 and got[8] == 0 and got[10] == 777
 
 
 def test_spec_prepare_and_commit():
