@@ -35,6 +35,8 @@ SHAPES = [
     (11, 200, 2688),
     (9, 40, 128),
     (1, 1, 128),
+    (128, 96, 256),
+    (129, 96, 256),
 ]
 
 
@@ -62,7 +64,7 @@ def _case(seed, M, N, K, outliers=None):
 
 
 # ------------------------------------------------------------------ packer
-@pytest.mark.parametrize("N,K", [(1024, 1024), (17, 384), (100, 256), (5, 18944)])
+@pytest.mark.parametrize("N,K", [(1024, 1024), (17, 384), (100, 256), (5, 18944), (1, 128)])
 def test_pack_w4_bitexact(N, K):
     say(f"pack_w4 N={N} K={K}")
     W, _ = _case(10, 1, N, K)
