@@ -237,6 +237,45 @@ def measure_prefill(torch, q, wl, reps=5):
     return out
 
 
+def measure_batch_sweep(torch, q, wl, reps=10, Ms=(8, 16, 32, 64, 128, 256, 512)):
+    """Batched serving: one pass over the four Qwen2.5-7B projections at M
+    tokens in each mode -- draft (quant_act + W4A4) and verify (W4A16) --
+    with each replay reading a different weight copy (HBM).  Where the
+    ratio w4a16/w4a4 passes 1 the drafter's lower precision pays for itself."""
+    import synth
+    rng = synth.make_rng(1, 4)
+    out = {}
+    for M in Ms:
+        t4 = t16 = 0.0
+        for p in wl.proj:
+            N, K = p["N"], p["K"]
+            X = torch.from_numpy(synth.activations(rng, M, K, n_outliers=synth.outlier_count(K))
+                                 .view(np.int16)).view(torch.bfloat16).to("cuda:0")
+            Xq = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda:0")
+            Xs = torch.empty((M,), dtype=torch.float32, device="cuda:0")
+            Y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+            ws = torch.empty(max(1, q.workspace_bytes(1, M, N, K), q.workspace_bytes(2, M, N, K)),
+                             dtype=torch.uint8, device="cuda:0")
+            cps = p["copies"]
+
+            def f4():
+                for Wq, Ws in cps:
+                    q.quant_act(X, Xq, Xs)
+                    q.gemm_w4a4(Xq, Xs, Wq, Ws, Y=Y, ws=ws)
+
+            def f16():
+                for Wq, Ws in cps:
+                    q.gemm_w4a16(X, Wq, Ws, Y=Y, ws=ws)
+            t4 += _graph_time(torch, f4, reps, launches=1) / len(cps)
+            t16 += _graph_time(torch, f16, reps, launches=1) / len(cps)
+            del X, Xq, Xs, Y, ws
+        ops = sum(2.0 * M * p["N"] * p["K"] for p in wl.proj)
+        out[f"M{M}"] = {"draft_w4a4_us": round(t4, 1), "verify_w4a16_us": round(t16, 1),
+                        "w4a16_over_w4a4": round(t16 / t4, 3),
+                        "draft_tops": round(ops / t4 / 1e6, 1), "verify_tflops": round(ops / t16 / 1e6, 1)}
+    return out
+
+
 def measure_decode_gemv(torch, q, wl, reps=10):
     """W4A16 at the decode-verify shapes of batch 1 (M = 1 * (4+1) = 5) on
     gate|up and down, and the Llama-3-8B lm_head (4096 -> 128256) at M = 1.
@@ -474,6 +513,8 @@ def run(args):
         line["decode_gemv_w4a16"] = measure_decode_gemv(torch, q, wl)
         log("prefill-shaped GEMMs")
         line["prefill_m2048"] = measure_prefill(torch, q, wl)
+        log("batched serving sweep")
+        line["batch_sweep_layer"] = measure_batch_sweep(torch, q, wl)
         log("verify at batch 32, V=128256")
         line["verify_b32_v128256"] = measure_verify_llama(torch, q)
         log("end-to-end self-speculative loop")
@@ -508,6 +549,10 @@ def run_only(which):
     torch.cuda.set_device(0)
     if which == "verify":
         res = measure_verify_llama(torch, q)
+    elif which == "batch":
+        wl = Decode(torch, q)
+        torch.cuda.synchronize()
+        res = measure_batch_sweep(torch, q, wl)
     elif which == "e2e":
         res = measure_e2e(torch)
     else:
@@ -597,7 +642,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the decode-GEMV, prefill and verify side measurements")
-    ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e"],
+    ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e", "batch"],
                     help="run one side measurement alone and print its JSON (for profiling)")
     ap.add_argument("--counters", action="store_true",
                     help="run only the copy calibration and the dominant kernel (for rocprofv3 --pmc)")

@@ -70,7 +70,8 @@ enum { QSPEC_VERIFY_GREEDY = 0, QSPEC_VERIFY_SAMPLE = 1 };
  * self-speculation that must reproduce plain verifier decoding token for
  * token) passes the same explicit family for every M.  AUTO picks by M and
  * N: STREAM for M <= 16 when N < 16384 (where SKINNY would have too few
- * workgroups to fill the GPU), else SKINNY up to M = 128, TILED beyond. */
+ * workgroups to fill the GPU), else SKINNY up to M = 128 (W4A16) or
+ * M = 256 (W4A4), TILED beyond. */
 enum {
   QSPEC_GEMM_AUTO = 0,
   QSPEC_GEMM_GEMV = 1,   /* W4A16 only: VALU GEMV with wavefront reduction   */

@@ -1543,18 +1543,20 @@ struct GemvPlan {
 GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K / kGroup, kGemvGroups)}; }
 
 // AUTO: for M <= 16 the stream family where the skinny family would have
-// few workgroups (fewer than QSPEC_SK_TARGET_WG 64-row tiles),
-// the skinny family otherwise and up to 128 rows, the tiled family beyond.
-// The choice depends on M and N only.
-int auto_pick(int64_t M, int64_t N) {
+// few workgroups (fewer than QSPEC_SK_TARGET_WG 64-row tiles), the skinny
+// family otherwise up to skinny_max rows, the tiled family beyond.  The
+// crossover measured on the Qwen2.5-7B projections lies between 128 and 192
+// rows for W4A16 and between 256 and 384 for W4A4 (whose skinny kernel has
+// half the MFMA work per weight byte).  The choice depends on M and N only.
+int auto_pick(int64_t M, int64_t N, int64_t skinny_max) {
   if (M <= kStreamMaxM && cdiv(N, 64) < QSPEC_SK_TARGET_WG) return QSPEC_GEMM_STREAM;
-  return M <= 128 ? QSPEC_GEMM_SKINNY : QSPEC_GEMM_TILED;
+  return M <= skinny_max ? QSPEC_GEMM_SKINNY : QSPEC_GEMM_TILED;
 }
 int w4a16_pick(int variant, int64_t M, int64_t N) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N);
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, 128);
 }
 int w4a4_pick(int variant, int64_t M, int64_t N) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N);
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, 256);
 }
 
 hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* Xs, float* Y,
