@@ -528,7 +528,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
 //     double-buffered, one barrier per group;
 //   * block order: n-tiles are dealt round-robin to the 8 XCDs and each XCD
 //     walks all m-tiles of an n-tile in a row, so a weight tile is fetched
-//     from HBM about once per XCD and then served by that XCD's L2;
+//     from HBM about once per XCD and then served by that XCD's L2 (the W4A4
+//     kernel walks the same order with a persistent grid, several tiles
+//     per workgroup);
 //   * all loads go through buffer resources with the group as a uniform
 //     offset.
 // ============================================================================
