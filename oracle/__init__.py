@@ -42,9 +42,17 @@ from .quant import (  # noqa: F401
     untile_scales,
     dequant_w4,
     quant_act,
+    quant_act_values,
     w4a4_partials,
     gemm_w4a4,
     gemm_w4a16,
+)
+from .rotate import (  # noqa: F401
+    fwht128_f32,
+    rotate_x,
+    rotate_x_bf16,
+    rotate_w,
+    quant_act_rot,
 )
 from .verify import (  # noqa: F401
     softmax64,

@@ -210,7 +210,13 @@ def quant_act(X_bits):
         q  = clamp( rne( x[m,k] / s ), -8, 7 )  (IEEE fp32 divide; 0 if a == 0)
     Returns (Xq uint8 [M, K/2], Xs float32 [M]).
     """
-    x = bf16_bits_to_f32(X_bits)
+    return quant_act_values(bf16_bits_to_f32(X_bits))
+
+
+def quant_act_values(x):
+    """The quantizer of ``quant_act`` on fp32 values [M, K] (the bf16 inputs
+    widened, or the fp32 output of the rotation in ``oracle.rotate``)."""
+    x = np.asarray(x, dtype=np.float32)
     if x.ndim != 2:
         raise ValueError("X must be 2-D [M, K]")
     if not np.all(np.isfinite(x)):
