@@ -143,6 +143,35 @@ qspec_status qspec_quant_act(const uint16_t* X, int64_t M, int64_t K,
                              uint8_t* Xq, float* Xs, qspec_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * Rotation ahead of the quantizers (QSpec page, Builds on: QuaRot, "Outlier-
+ * Free 4-Bit Inference in Rotated LLMs" -- the pages give the title only).
+ * Reading: per 128-group, the Sylvester Walsh-Hadamard matrix H (entries
+ * +-1, H H^T = 128 I), activations x' = H x / 16 and weights w' = H w / 8,
+ * so x' . w' = x . w and a layer on (x', w') is the layer on (x, w); the
+ * group structure of the shared buffer is kept.  H is applied as the fast
+ * transform: stages s = 0..6, the pair (i, i + 2^s) with bit s of i clear
+ * becomes (a + b, a - b), one fp32 add or subtract each, then the exact
+ * power-of-two scale -- every output bit is fixed.  With x20 outlier channels
+ * this spreads each outlier over its group, so the per-token INT4 codes keep
+ * the inlier channels (the W4A4 layer error drops about 3x).
+ *
+ * qspec_rotate_w: W [N][K] fp32 -> Wr = H W / 8 per group, fp32 (offline, then
+ *   qspec_pack_w4(Wr)).  Wr may equal W.
+ * qspec_rotate_x: X [M][K] bf16 bits -> Xr = bf16(H x / 16) (round to nearest
+ *   even), the verifier's input to qspec_gemm_w4a16.  Xr may equal X.
+ * qspec_quant_act_rot: X [M][K] bf16 bits -> the codes and scale of
+ *   qspec_quant_act applied to the fp32 values H x / 16 (not rounded to
+ *   bf16), the drafter's input to qspec_gemm_w4a4.  Xq [M][K/2], Xs [M].
+ * K % 128 == 0 (QSPEC_ERR_SHAPE otherwise); 16-byte aligned pointers.
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_rotate_w(const float* W, int64_t N, int64_t K, float* Wr,
+                            qspec_stream stream);
+qspec_status qspec_rotate_x(const uint16_t* X, int64_t M, int64_t K, uint16_t* Xr,
+                            qspec_stream stream);
+qspec_status qspec_quant_act_rot(const uint16_t* X, int64_t M, int64_t K,
+                                 uint8_t* Xq, float* Xs, qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
  * qspec_gemm_w4a4 -- the drafter's linear layer (QSpec Abstract: W4A4 joint
  * quantization drafts).  Reading:
  *     P[m,n,g] = sum_{k in group g} qa[m,k] * qw[n,k]     (exact int32)

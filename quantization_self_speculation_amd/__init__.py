@@ -16,6 +16,9 @@ from .binding import (  # noqa: F401
     pack_w4,
     padded_rows,
     quant_act,
+    quant_act_rot,
+    rotate_w,
+    rotate_x,
     gemm_w4a4,
     gemm_w4a16,
     verify,

@@ -55,6 +55,9 @@ def lib():
             "qspec_workspace_bytes": (SZ, [I, I64, I64, I64]),
             "qspec_pack_w4": (I, [P, I64, I64, I, P, P, P]),
             "qspec_quant_act": (I, [P, I64, I64, P, P, P]),
+            "qspec_rotate_w": (I, [P, I64, I64, P, P]),
+            "qspec_rotate_x": (I, [P, I64, I64, P, P]),
+            "qspec_quant_act_rot": (I, [P, I64, I64, P, P, P]),
             "qspec_gemm_w4a4": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
             "qspec_gemm_w4a16": (I, [P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_verify": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P, SZ, P]),
@@ -153,6 +156,41 @@ def quant_act(X, Xq=None, Xs=None):
     if Xs is None:
         Xs = torch.empty((M,), dtype=torch.float32, device=X.device)
     _check(lib().qspec_quant_act(_ptr(X), M, K, _ptr(Xq), _ptr(Xs), _stream()), "qspec_quant_act")
+    return Xq, Xs
+
+
+def rotate_w(W, Wr=None):
+    """fp32 [N, K] -> H W / 8 per 128-group, fp32 (then pack_w4)."""
+    _need(W, "W", torch.float32)
+    N, K = W.shape
+    if Wr is None:
+        Wr = torch.empty_like(W)
+    _need(Wr, "Wr", torch.float32, (N, K))
+    _check(lib().qspec_rotate_w(_ptr(W), N, K, _ptr(Wr), _stream()), "qspec_rotate_w")
+    return Wr
+
+
+def rotate_x(X, Xr=None):
+    """bf16 [M, K] -> bf16(H x / 16) per 128-group: the verifier's input."""
+    _need(X, "X", torch.bfloat16)
+    M, K = X.shape
+    if Xr is None:
+        Xr = torch.empty_like(X)
+    _need(Xr, "Xr", torch.bfloat16, (M, K))
+    _check(lib().qspec_rotate_x(_ptr(X), M, K, _ptr(Xr), _stream()), "qspec_rotate_x")
+    return Xr
+
+
+def quant_act_rot(X, Xq=None, Xs=None):
+    """bf16 [M, K] -> codes and scales of H x / 16 (the drafter's input)."""
+    _need(X, "X", torch.bfloat16)
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if Xs is None:
+        Xs = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _check(lib().qspec_quant_act_rot(_ptr(X), M, K, _ptr(Xq), _ptr(Xs), _stream()),
+           "qspec_quant_act_rot")
     return Xq, Xs
 
 

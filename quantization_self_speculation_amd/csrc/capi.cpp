@@ -205,6 +205,41 @@ qspec_status qspec_quant_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* X
   return hip_result(launch_quant_act(X, M, K, Xq, Xs, (hipStream_t)stream), "quant_act launch");
 }
 
+qspec_status qspec_rotate_w(const float* W, int64_t N, int64_t K, float* Wr, qspec_stream stream) {
+  QS_REQUIRE(N >= 1 && N <= kMaxDim, QSPEC_ERR_SHAPE, "need N >= 1 (got %lld)", (long long)N);
+  QS_TRY(check_k(K));
+  QS_REQUIRE(N * (K / QSPEC_GROUP) <= ((int64_t)1 << 34), QSPEC_ERR_SHAPE, "size too large");
+  QS_PTR(W);
+  QS_PTR(Wr);
+  QS_TRY(device_check());
+  return hip_result(launch_rotate(false, W, N, K, 0.125f, Wr, (hipStream_t)stream),
+                    "rotate_w launch");
+}
+
+qspec_status qspec_rotate_x(const uint16_t* X, int64_t M, int64_t K, uint16_t* Xr,
+                            qspec_stream stream) {
+  QS_REQUIRE(M >= 1 && M <= kMaxDim, QSPEC_ERR_SHAPE, "need M >= 1 (got %lld)", (long long)M);
+  QS_TRY(check_k(K));
+  QS_REQUIRE(M * (K / QSPEC_GROUP) <= ((int64_t)1 << 34), QSPEC_ERR_SHAPE, "size too large");
+  QS_PTR(X);
+  QS_PTR(Xr);
+  QS_TRY(device_check());
+  return hip_result(launch_rotate(true, X, M, K, 0.0625f, Xr, (hipStream_t)stream),
+                    "rotate_x launch");
+}
+
+qspec_status qspec_quant_act_rot(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
+                                 qspec_stream stream) {
+  QS_REQUIRE(M >= 1 && M <= kMaxDim, QSPEC_ERR_SHAPE, "need M >= 1 (got %lld)", (long long)M);
+  QS_TRY(check_k(K));
+  QS_PTR(X);
+  QS_PTR(Xq);
+  QS_PTR(Xs);
+  QS_TRY(device_check());
+  return hip_result(launch_quant_act_rot(X, M, K, Xq, Xs, (hipStream_t)stream),
+                    "quant_act_rot launch");
+}
+
 qspec_status qspec_gemm_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq,
                              const uint16_t* Ws, int64_t M, int64_t N, int64_t K, int group,
                              int variant, float* Y, int32_t* P, void* ws, size_t ws_bytes,

@@ -18,12 +18,6 @@
 namespace qspec {
 namespace {
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 // fp64 -> bf16 with one rounding: truncate to fp32 and set the lowest bit if
 // anything was dropped (round to odd keeps the information a later rounding
 // to nearest needs), then round fp32 -> bf16 to nearest even.

@@ -12,6 +12,14 @@ hipError_t launch_pack_w4(const float* W, int64_t N, int64_t K, uint8_t* Wq, uin
 hipError_t launch_quant_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
                             hipStream_t s);
 
+// per-group Walsh-Hadamard rotation: x' = H x * scale per 128-group of each
+// of R rows (bf16 in and out, or fp32 in and out); the quantizer on the
+// rotated row x' = H x / 16
+hipError_t launch_rotate(bool bf16, const void* in, int64_t R, int64_t K, float scale, void* out,
+                         hipStream_t s);
+hipError_t launch_quant_act_rot(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
+                                hipStream_t s);
+
 size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
                         int64_t N, int64_t K, int variant, float* Y, void* ws, hipStream_t s);

@@ -61,6 +61,20 @@ def test_quant_validation():
     assert L.qspec_quant_act(A, 4, 256, A, MIS, S) == EALIGN
 
 
+def test_rotation_validation():
+    L = q.lib()
+    assert L.qspec_rotate_w(A, 0, 256, A, S) == ESHAPE
+    assert L.qspec_rotate_w(A, 4, 200, A, S) == ESHAPE
+    assert L.qspec_rotate_w(NUL, 4, 256, A, S) == ENULL
+    assert L.qspec_rotate_w(A, 4, 256, MIS, S) == EALIGN
+    assert L.qspec_rotate_x(A, 0, 256, A, S) == ESHAPE
+    assert L.qspec_rotate_x(A, 4, 64, A, S) == ESHAPE
+    assert L.qspec_rotate_x(A, 4, 256, NUL, S) == ENULL
+    assert L.qspec_quant_act_rot(A, 4, 100, A, A, S) == ESHAPE
+    assert L.qspec_quant_act_rot(A, 4, 256, NUL, A, S) == ENULL
+    assert L.qspec_quant_act_rot(A, 4, 256, A, MIS, S) == EALIGN
+
+
 def test_gemm_validation():
     L = q.lib()
     f = L.qspec_gemm_w4a4
