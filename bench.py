@@ -276,6 +276,55 @@ def measure_batch_sweep(torch, q, wl, reps=10, Ms=(8, 16, 32, 64, 128, 256, 512)
     return out
 
 
+def measure_rotation(torch, q, wl, reps=20):
+    """Per-group Hadamard rotation ahead of the quantizers at the decode batch
+    (M = 8 draft rows, M = 40 verify rows): kernel times of the rotated
+    quantizer against the plain one and of the verifier's bf16 rotation, and
+    the drafter layer's relative error against the exact product with and
+    without the rotation (Qwen2.5-7B QKV shape, x20 outlier channels,
+    512 sampled output columns computed exactly on the host)."""
+    import synth
+    rng = synth.make_rng(1, 5)
+    out = {"times_us": {}}
+    warm = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda:0")
+    _graph_time(torch, lambda: q.quant_act(warm), reps)   # first graph of the process: not timed
+    for p in wl.proj:
+        K = p["K"]
+        X8 = torch.from_numpy(synth.activations(rng, 8, K, n_outliers=synth.outlier_count(K))
+                              .view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        X40 = torch.from_numpy(synth.activations(rng, 40, K, n_outliers=synth.outlier_count(K))
+                               .view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        Xq = torch.empty((8, K // 2), dtype=torch.uint8, device="cuda:0")
+        Xs = torch.empty((8,), dtype=torch.float32, device="cuda:0")
+        Xr = torch.empty_like(X40)
+        tq = _graph_time(torch, lambda: q.quant_act(X8, Xq, Xs), reps)
+        tr = _graph_time(torch, lambda: q.quant_act_rot(X8, Xq, Xs), reps)
+        tx = _graph_time(torch, lambda: q.rotate_x(X40, Xr), reps)
+        out["times_us"][p["name"]] = {"quant_act_M8": round(tq, 2), "quant_act_rot_M8": round(tr, 2),
+                                      "rotate_x_M40": round(tx, 2)}
+    N, K, ncols = 4608, 3584, 512
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, 8, K, n_outliers=synth.outlier_count(K))
+    cols = np.sort(rng.choice(N, size=ncols, replace=False))
+    x = (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    y = x @ W[cols].astype(np.float64).T
+    Wd = torch.from_numpy(W).to("cuda:0")
+    Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    Wq, Ws = q.pack_w4(Wd)
+    Y = q.gemm_w4a4(*q.quant_act(Xd), Wq, Ws, N=N)
+    Wrq, Wrs = q.pack_w4(q.rotate_w(Wd))
+    Yr = q.gemm_w4a4(*q.quant_act_rot(Xd), Wrq, Wrs, N=N)
+    Y16 = q.gemm_w4a16(Xd, Wq, Ws, N=N)
+    Y16r = q.gemm_w4a16(q.rotate_x(Xd), Wrq, Wrs, N=N)
+    torch.cuda.synchronize()
+
+    def rel(t):
+        return round(float(np.linalg.norm(t.cpu().numpy()[:, cols] - y) / np.linalg.norm(y)), 4)
+    out["rel_error_vs_exact_qkv_M8"] = {"w4a4": rel(Y), "w4a4_rotated": rel(Yr),
+                                         "w4a16": rel(Y16), "w4a16_rotated": rel(Y16r)}
+    return out
+
+
 def measure_decode_gemv(torch, q, wl, reps=10):
     """W4A16 at the decode-verify shapes of batch 1 (M = 1 * (4+1) = 5) on
     gate|up and down, and the Llama-3-8B lm_head (4096 -> 128256) at M = 1.
@@ -515,6 +564,8 @@ def run(args):
         line["prefill_m2048"] = measure_prefill(torch, q, wl)
         log("batched serving sweep")
         line["batch_sweep_layer"] = measure_batch_sweep(torch, q, wl)
+        log("rotation ahead of the quantizers")
+        line["rotation"] = measure_rotation(torch, q, wl)
         log("verify at batch 32, V=128256")
         line["verify_b32_v128256"] = measure_verify_llama(torch, q)
         log("end-to-end self-speculative loop")
@@ -549,10 +600,10 @@ def run_only(which):
     torch.cuda.set_device(0)
     if which == "verify":
         res = measure_verify_llama(torch, q)
-    elif which == "batch":
+    elif which in ("batch", "rotation"):
         wl = Decode(torch, q)
         torch.cuda.synchronize()
-        res = measure_batch_sweep(torch, q, wl)
+        res = (measure_batch_sweep if which == "batch" else measure_rotation)(torch, q, wl)
     elif which == "e2e":
         res = measure_e2e(torch)
     else:
@@ -642,7 +693,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the decode-GEMV, prefill and verify side measurements")
-    ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e", "batch"],
+    ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e", "batch", "rotation"],
                     help="run one side measurement alone and print its JSON (for profiling)")
     ap.add_argument("--counters", action="store_true",
                     help="run only the copy calibration and the dominant kernel (for rocprofv3 --pmc)")

@@ -120,13 +120,18 @@ __device__ __forceinline__ void fwht128_lane(float f[8], int l16) {
         f[e] = a + b;
         f[e | h] = a - b;
       }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float u = __shfl_xor(f[e], m, 64);
-      f[e] = (l16 & m) ? u - f[e] : f[e] + u;  // bit set: a = partner, b = mine
-    }
+  // partner lane = lane ^ m: ds_swizzle in bit-mask mode (and 0x1F, xor m)
+#define QSPEC_FWHT_XSTAGE(m)                                                              \
+  _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                         \
+    const float u = __int_as_float(                                                       \
+        __builtin_amdgcn_ds_swizzle(__float_as_int(f[e]), 0x1F | ((m) << 10)));           \
+    f[e] = (l16 & (m)) ? u - f[e] : f[e] + u; /* bit set: a = partner, b = mine */       \
+  }
+  QSPEC_FWHT_XSTAGE(1)
+  QSPEC_FWHT_XSTAGE(2)
+  QSPEC_FWHT_XSTAGE(4)
+  QSPEC_FWHT_XSTAGE(8)
+#undef QSPEC_FWHT_XSTAGE
 }
 
 // x' = H x * scale per 128-group of each row (scale a power of two: exact).
