@@ -1092,10 +1092,11 @@ hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const
 // ============================================================================
 // "Stream" family (both modes, M <= 16): the decode shapes, HBM-bound.
 //   * a workgroup = nw wavefronts on ONE 16-row weight block; wavefront w
-//     takes the w-th k-slice of the groups, so the k-split is reduced inside
+//     takes groups w, w + nw, w + 2 nw, ... (dealt round-robin: at each step
+//     the workgroup reads nw adjacent tiles), so the k-split is reduced inside
 //     the workgroup (LDS, fixed order) -- no partials leave the chip;
 //   * nw depends on (N, K) only: about 4096 wavefronts in flight, at most 16
-//     per workgroup, at least 2 groups per slice;
+//     per workgroup, at least 2 groups per wavefront;
 //   * weights stream HBM -> registers through a PD-deep ring (one flat 1 KiB
 //     tile per wavefront per group); the activation rows and the group scales
 //     come from L2 through a 2-deep ring (every wavefront reads the same few
@@ -1149,9 +1150,11 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   const int l16 = lane & 15, lg = lane >> 4;
   const int rb = blockIdx.x;
   const int M = a.M, K = a.K, G = K / kGroup;
-  const int gps = (G + nw - 1) / nw;
-  const int g0 = min(G, w * gps), g1 = min(G, g0 + gps);
-  const int gl = min(G - 1, max(g0, g1 - 1));  // clamp target: a valid group (empty slices too)
+  // groups dealt round-robin: wavefront w takes groups w, w + nw, w + 2 nw,
+  // ... (local index i -> group w + nw i), so at each step the workgroup's
+  // loads cover nw adjacent tiles; gl clamps the local index
+  const int g0 = 0, g1 = w < G ? (G - 1 - w) / nw + 1 : 0;
+  const int gl = max(0, g1 - 1);
 
   const uint8_t* wt = a.Wq + (int64_t)rb * G * 1024 + lane * 16;
   const uint16_t* sc = a.Ws + (int64_t)rb * G * 16 + lg * 4;
@@ -1165,7 +1168,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   constexpr int xgb = MODE == kW4A16 ? kGroup * 2 : kGroup / 2;  // activation bytes per group
 
   auto load = [&](StreamStage<MODE>& st, int g) {
-    const int gg = min(g, gl);
+    const int gg = min(w + nw * min(g, gl), G - 1);
     st.w = ld_stream(wt + (int64_t)gg * 1024);
     st.s = *reinterpret_cast<const uint2*>(sc + (int64_t)gg * 16);
     const uint32_t o = xoff0 + (uint32_t)(gg * xgb);
@@ -1242,7 +1245,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   for (int i = 0; i < PD - 1; ++i)
     if (gb + i < g1) group(i);  // tail: fewer than PD groups
 
-  // k-slices -> one sum per output, in slice order
+  // per-wavefront sums -> one sum per output, in wavefront order
   if (nw > 1) {
     *reinterpret_cast<v4f*>(&red[w][lane][0]) = tot;
     __syncthreads();

@@ -288,16 +288,22 @@ def test_w4a16_row_invariance(variant):
         assert np.array_equal(Y80[r:r + 1].view(np.uint32), Y1.view(np.uint32)), r
 
 
-def test_w4a4_row_invariance():
-    N, K = 1024, 2048
+@pytest.mark.parametrize("N,K", [(1024, 2048), (3584, 18944), (4608, 3584), (8192, 1024)])
+def test_w4a4_row_invariance(N, K):
+    """SKINNY family, W4A4: rows bitwise identical at M = 80 (four activation
+    blocks per workgroup), 16, 8, 5 and 1 (one block, the workgroup size
+    balanced over the CUs).  The k-split is a function of N and K only: 8, 3
+    and 2 slices for the first three shapes, none for N = 8192."""
     W, X = _case(17, 80, N, K)
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
     args = (dev_w(Wq), dev_s(Ws))
     Y80 = host(q.gemm_w4a4(dev(Xq), dev(Xs), *args, variant=q.GEMM_SKINNY, N=N))
-    for r in (0, 41):
-        Y1 = host(q.gemm_w4a4(dev(Xq[r:r + 1]), dev(Xs[r:r + 1]), *args, variant=q.GEMM_SKINNY, N=N))
-        assert np.array_equal(Y80[r:r + 1].view(np.uint32), Y1.view(np.uint32))
+    for lo, hi in ((0, 16), (16, 24), (40, 45), (41, 42), (79, 80)):
+        Y = host(q.gemm_w4a4(dev(Xq[lo:hi].copy()), dev(Xs[lo:hi].copy()), *args,
+                             variant=q.GEMM_SKINNY, N=N))
+        assert np.array_equal(Y80[lo:hi].view(np.uint32), Y.view(np.uint32)), (lo, hi)
+    assert_close(Y80, oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4 M=80")
 
 
 def test_determinism():
