@@ -386,14 +386,16 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
     for (int mb = 0; mb < MB; ++mb) tot[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
   uint4 wr[PD][NB];
 
+  // the weight ring is issued before the first activation chunk is stored,
+  // so the weight stream starts at once instead of one L2 round trip later
   x_load(0);
-  x_store(0);
 #pragma unroll
   for (int s = 0; s < PD; ++s) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) wr[s][nb] = wload(nb, s);
     __builtin_amdgcn_sched_barrier(0);  // slot order, as in the steady state
   }
+  x_store(0);
   __syncthreads();
   x_load(1);
 
