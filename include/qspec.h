@@ -196,6 +196,20 @@ qspec_status qspec_gemm_w4a4(const uint8_t* Xq, const float* Xs,
                              void* ws, size_t ws_bytes, qspec_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * qspec_gemm_w4a4_bf16 -- the drafter's linear layer with a bf16 output, for
+ * chaining into the next bf16 consumer without an fp32 round trip.  Same
+ * arguments, validation, variants and workspace as qspec_gemm_w4a4 (no P);
+ * Y [M][N] receives bf16 bits: the round-to-nearest-even bf16 of exactly the
+ * fp32 value qspec_gemm_w4a4 stores for the same variant and inputs (finite
+ * results; the conversion is the epilogue's last step, inside the kernel).
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_gemm_w4a4_bf16(const uint8_t* Xq, const float* Xs,
+                                  const uint8_t* Wq, const uint16_t* Ws,
+                                  int64_t M, int64_t N, int64_t K, int group,
+                                  int variant, uint16_t* Y,
+                                  void* ws, size_t ws_bytes, qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
  * qspec_gemm_w4a16 -- the verifier's linear layer (QSpec Abstract:
  * weight-only quantization verifies; tech-dashboard summary, paragraph 2:
  * W4A16 keeps activations at higher precision).  Reading:

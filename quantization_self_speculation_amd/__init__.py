@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     rotate_w,
     rotate_x,
     gemm_w4a4,
+    gemm_w4a4_bf16,
     gemm_w4a16,
     verify,
     workspace_bytes,

@@ -59,6 +59,7 @@ def lib():
             "qspec_rotate_x": (I, [P, I64, I64, P, P]),
             "qspec_quant_act_rot": (I, [P, I64, I64, P, P, P]),
             "qspec_gemm_w4a4": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
+            "qspec_gemm_w4a4_bf16": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_gemm_w4a16": (I, [P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_verify": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P, SZ, P]),
             "qspec_embed": (I, [P, I64, I64, P, I64, P, P]),
@@ -215,6 +216,25 @@ def gemm_w4a4(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, partials=False, Y=None, P=None,
     _check(lib().qspec_gemm_w4a4(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), M, N, K, GROUP, variant,
                                  _ptr(Y), _ptr(P), _ptr(w), wb, _stream()), "qspec_gemm_w4a4")
     return (Y, P) if partials else Y
+
+
+def gemm_w4a4_bf16(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None, N=None):
+    """Draft-mode linear layer with a bf16 output -> Y bf16 [M, N]: the
+    round-to-nearest-even of the fp32 result gemm_w4a4 gives (same variant)."""
+    _need(Xq, "Xq", torch.uint8)
+    M, K = Xq.shape[0], 2 * Xq.shape[1]
+    N = _out_n(N, Y, Wq)
+    _need(Xs, "Xs", torch.float32, (M,))
+    _need(Wq, "Wq", torch.uint8, (padded_rows(N), K // 2))
+    _need(Ws, "Ws", torch.float16, (padded_rows(N), K // GROUP))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=Xq.device)
+    _need(Y, "Y", torch.bfloat16, (M, N))
+    w, wb = _workspace(workspace_bytes(OP_GEMM_W4A4, M, N, K), Xq.device, ws)
+    _check(lib().qspec_gemm_w4a4_bf16(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), M, N, K, GROUP,
+                                      variant, _ptr(Y), _ptr(w), wb, _stream()),
+           "qspec_gemm_w4a4_bf16")
+    return Y
 
 
 def gemm_w4a16(X, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None, N=None):

@@ -253,8 +253,26 @@ qspec_status qspec_gemm_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* 
   if (P != nullptr) QS_PTR(P);
   QS_TRY(check_ws(ws, ws_bytes, w4a4_ws_bytes(M, N, K)));
   QS_TRY(device_check());
-  return hip_result(launch_w4a4(Xq, Xs, Wq, Ws, M, N, K, variant, Y, P, ws, (hipStream_t)stream),
+  return hip_result(launch_w4a4(Xq, Xs, Wq, Ws, M, N, K, variant, Y, nullptr, P, ws,
+                                (hipStream_t)stream),
                     "gemm_w4a4 launch");
+}
+
+qspec_status qspec_gemm_w4a4_bf16(const uint8_t* Xq, const float* Xs, const uint8_t* Wq,
+                                  const uint16_t* Ws, int64_t M, int64_t N, int64_t K, int group,
+                                  int variant, uint16_t* Y, void* ws, size_t ws_bytes,
+                                  qspec_stream stream) {
+  QS_TRY(check_gemm(M, N, K, group, variant, false));
+  QS_PTR(Xq);
+  QS_PTR(Xs);
+  QS_PTR(Wq);
+  QS_PTR(Ws);
+  QS_PTR(Y);
+  QS_TRY(check_ws(ws, ws_bytes, w4a4_ws_bytes(M, N, K)));
+  QS_TRY(device_check());
+  return hip_result(launch_w4a4(Xq, Xs, Wq, Ws, M, N, K, variant, nullptr, Y, nullptr, ws,
+                                (hipStream_t)stream),
+                    "gemm_w4a4_bf16 launch");
 }
 
 qspec_status qspec_gemm_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,

@@ -98,6 +98,41 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Output of a linear layer: fp32 Yf, or, when a bf16 destination Yb is
+// given (the W4A4 drafter's chaining output), the round-to-nearest-even
+// bf16 of exactly the fp32 value that would have been stored.  out_store4
+// writes the outputs o .. o + 3 of one row (those below nvalid); vec: o is a
+// multiple of 4 and all four are valid.
+__device__ __forceinline__ void out_store4(float* Yf, uint16_t* Yb, int64_t o, const float (&v)[4],
+                                           int nvalid, bool vec) {
+  if (Yb != nullptr) {
+    if (vec) {
+      *reinterpret_cast<uint2*>(Yb + o) =
+          make_uint2((uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+                     (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r < nvalid) Yb[o + r] = f32_to_bf16_rne(v[r]);
+    }
+  } else {
+    if (vec) {
+      *reinterpret_cast<float4*>(Yf + o) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r < nvalid) Yf[o + r] = v[r];
+    }
+  }
+}
+
+__device__ __forceinline__ void out_store1(float* Yf, uint16_t* Yb, int64_t o, float v) {
+  if (Yb != nullptr)
+    Yb[o] = f32_to_bf16_rne(v);
+  else
+    Yf[o] = v;
+}
+
 __device__ __forceinline__ v8bf as_v8bf(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4 t = {a, b, c, d};
   return __builtin_bit_cast(v8bf, t);
@@ -143,6 +178,7 @@ struct SkinnyArgs {
   const uint8_t* Wq;
   const uint16_t* Ws;
   float* Y;
+  uint16_t* Yb;             // bf16 output instead of Y (W4A4 only), else null
   float* part;              // [S][M][N] when S > 1
   unsigned long long* cnt;  // [T] when S > 1
   int32_t* P;               // W4A4 int32 group partials (optional)
@@ -179,14 +215,7 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = MODE == kW4A4 ? xsc * tot[nb][mb][r] : tot[nb][mb][r];
-          float* dst = a.Y + (int64_t)m * N + n;
-          if (vec) {
-            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (n + r < N) dst[r] = v[r];
-          }
+          out_store4(a.Y, a.Yb, (int64_t)m * N + n, v, N - n, vec);
         }
       }
     return;
@@ -260,7 +289,7 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   for (int e = 0; e < EPT; ++e) {
     const int i = threadIdx.x + NT * e;
     const int m = m0 + i / WROWS, n = n_wg + i % WROWS;
-    if (ok[e]) a.Y[(int64_t)m * N + n] = MODE == kW4A4 ? a.Xs[m] * acc[e] : acc[e];
+    if (ok[e]) out_store1(a.Y, a.Yb, (int64_t)m * N + n, MODE == kW4A4 ? a.Xs[m] * acc[e] : acc[e]);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(a.cnt + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -542,6 +571,7 @@ struct TiledArgs {
   const uint8_t* Wq;
   const uint16_t* Ws;
   float* Y;
+  uint16_t* Yb;  // bf16 output instead of Y (W4A4 only), else null
   int M, N, K, ntn, ntm;
 };
 
@@ -580,7 +610,7 @@ struct TiledArgs {
 #define QSPEC_PF_RST 144  // LDS row stride of the widened activation slice (bytes)
 #endif
 
-template <int WN, int PD, int CH>
+template <int WN, int PD, int CH, bool BOUT>
 __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArgs a) {
   constexpr int BN = 64 * WN, BM = 64, NT = 64 * WN, RST = QSPEC_PF_RST;
   constexpr int BCH = BM * 4;                          // 16-byte activation chunks per group
@@ -813,17 +843,12 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArg
           const int n = n0 + nb * 16;
           if (m < M && n < N) {
             const float xsc = a.Xs[m];
-            const float v0 = xsc * tot[nb][mb][0], v1 = xsc * tot[nb][mb][1];
-            const float v2 = xsc * tot[nb][mb][2], v3 = xsc * tot[nb][mb][3];
-            float* dst = a.Y + (int64_t)m * N + n;
-            if (vec) {
-              *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
-            } else {
-              const float v[4] = {v0, v1, v2, v3};
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (n + r < N) dst[r] = v[r];
-            }
+            const float v[4] = {xsc * tot[nb][mb][0], xsc * tot[nb][mb][1], xsc * tot[nb][mb][2],
+                                xsc * tot[nb][mb][3]};
+            // the output type is a template argument: the stores sit inside
+            // the main loop, so only one kind is compiled into it
+            out_store4(BOUT ? nullptr : a.Y, BOUT ? a.Yb : nullptr, (int64_t)m * N + n, v, N - n,
+                       vec);
           }
           tot[nb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
         }
@@ -865,8 +890,12 @@ hipError_t launch_w4a4_prefill(TiledArgs a, hipStream_t s) {
   a.ntm = (int)cdiv(a.M, 64);
   const int64_t tiles = 8 * cdiv(a.ntn, 8) * a.ntm;  // a multiple of 8, as is the grid
   const int64_t grid = std::min<int64_t>(tiles, QSPEC_PF_GRID);
-  hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH>), dim3((unsigned)grid), dim3(64 * WN), 0,
-                     s, a);
+  if (a.Yb != nullptr)
+    hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH, true>), dim3((unsigned)grid), dim3(64 * WN),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH, false>), dim3((unsigned)grid), dim3(64 * WN),
+                       0, s, a);
   return hipGetLastError();
 }
 
@@ -1085,8 +1114,8 @@ hipError_t launch_w4a16_prefill(TiledArgs a, hipStream_t s) {
 
 template <int MODE>
 hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
-                        int64_t M, int64_t N, int64_t K, float* Y, hipStream_t s) {
-  TiledArgs a{X, Xs, Wq, Ws, Y, (int)M, (int)N, (int)K, 0, 0};  // the launcher sets the grid
+                        int64_t M, int64_t N, int64_t K, float* Y, uint16_t* Yb, hipStream_t s) {
+  TiledArgs a{X, Xs, Wq, Ws, Y, Yb, (int)M, (int)N, (int)K, 0, 0};  // the launcher sets the grid
   if (MODE == kW4A16) return launch_w4a16_prefill<QSPEC_PF16_SHAPE>(a, s);
   return launch_w4a4_prefill<QSPEC_PF_SHAPE>(a, s);
 }
@@ -1115,6 +1144,7 @@ struct StreamArgs {
   const uint8_t* Wq;
   const uint16_t* Ws;
   float* Y;
+  uint16_t* Yb;  // bf16 output instead of Y (W4A4 only), else null
   int M, N, K, nrb;
 };
 
@@ -1267,14 +1297,8 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   if (n >= N) return;
   float xs = 1.f;
   if (MODE == kW4A4) xs = a.Xs[l16];
-  float* dst = a.Y + (int64_t)l16 * N + n;
-  if ((N & 3) == 0) {
-    *reinterpret_cast<float4*>(dst) = make_float4(xs * tot[0], xs * tot[1], xs * tot[2], xs * tot[3]);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (n + r < N) dst[r] = xs * tot[r];
-  }
+  const float v[4] = {xs * tot[0], xs * tot[1], xs * tot[2], xs * tot[3]};
+  out_store4(a.Y, a.Yb, (int64_t)l16 * N + n, v, N - n, (N & 3) == 0);
 }
 
 int stream_waves(int64_t N, int64_t K) {
@@ -1286,8 +1310,8 @@ int stream_waves(int64_t N, int64_t K) {
 
 template <int MODE>
 hipError_t launch_stream(const void* X, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
-                         int64_t M, int64_t N, int64_t K, float* Y, hipStream_t s) {
-  StreamArgs a{X, Xs, Wq, Ws, Y, (int)M, (int)N, (int)K, (int)cdiv(N, 16)};
+                         int64_t M, int64_t N, int64_t K, float* Y, uint16_t* Yb, hipStream_t s) {
+  StreamArgs a{X, Xs, Wq, Ws, Y, Yb, (int)M, (int)N, (int)K, (int)cdiv(N, 16)};
   const int nw = stream_waves(N, K);
   const size_t lds = nw > 1 ? (size_t)nw * 64 * 4 * sizeof(float) : 0;
   hipLaunchKernelGGL(stream_kernel<MODE>, dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
@@ -1589,7 +1613,7 @@ size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
                         int64_t N, int64_t K, int variant, float* Y, void* ws, hipStream_t s) {
   const int v = w4a16_pick(variant, M, N);
-  if (v == QSPEC_GEMM_STREAM) return launch_stream<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, s);
+  if (v == QSPEC_GEMM_STREAM) return launch_stream<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, nullptr, s);
   if (v == QSPEC_GEMM_GEMV) {
     const GemvPlan q = plan_gemv(K);
     // rows of X in chunks of up to 4
@@ -1614,7 +1638,7 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
     }
     return hipSuccess;
   }
-  if (v == QSPEC_GEMM_TILED) return launch_tiled<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, s);
+  if (v == QSPEC_GEMM_TILED) return launch_tiled<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, nullptr, s);
   const SkinnyPlan p = plan_skinny(0, M, N, K);
   SkinnyArgs a{};
   a.X = X;
@@ -1634,14 +1658,15 @@ size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
-                       int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
-                       void* ws, hipStream_t s) {
-  // the int32 partials output is a check path served by the skinny family
+                       int64_t M, int64_t N, int64_t K, int variant, float* Y, uint16_t* Yb,
+                       int32_t* P, void* ws, hipStream_t s) {
+  // the int32 partials output is a check path served by the skinny family;
+  // exactly one of Y (fp32) and Yb (bf16) is given
   const int v = w4a4_pick(variant, M, N);
   if (v == QSPEC_GEMM_TILED && P == nullptr)
-    return launch_tiled<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, s);
+    return launch_tiled<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, Yb, s);
   if (v == QSPEC_GEMM_STREAM && P == nullptr)
-    return launch_stream<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, s);
+    return launch_stream<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, Yb, s);
   const SkinnyPlan p = plan_skinny(1, M, N, K, P != nullptr);
   SkinnyArgs a{};
   a.X = Xq;
@@ -1649,6 +1674,7 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
   a.Wq = Wq;
   a.Ws = Ws;
   a.Y = Y;
+  a.Yb = Yb;
   a.P = P;
   a.cnt = p.S > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
   a.part = p.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.cnt_bytes) : nullptr;

@@ -26,8 +26,8 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
 
 size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
-                       int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
-                       void* ws, hipStream_t s);
+                       int64_t M, int64_t N, int64_t K, int variant, float* Y, uint16_t* Yb,
+                       int32_t* P, void* ws, hipStream_t s);
 
 size_t verify_ws_bytes(int64_t B, int gamma, int64_t V);
 hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_t* draft_tok,

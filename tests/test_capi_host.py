@@ -94,6 +94,16 @@ def test_gemm_validation():
     assert need > 0
     assert g(A, A, A, 40, 4608, 3584, 128, 2, A, NUL, 0, S) == EWS
     assert g(A, A, A, 40, 4608, 3584, 128, 2, A, A, need - 1, S) == EWS
+    h = L.qspec_gemm_w4a4_bf16   # same checks as the fp32 call, bf16 Y
+    assert h(A, A, A, A, 8, 64, 256, 64, 0, A, NUL, 0, S) == EUNSUP
+    assert h(A, A, A, A, 8, 64, 250, 128, 0, A, NUL, 0, S) == ESHAPE
+    assert h(A, A, A, A, 8, 64, 256, 128, 1, A, NUL, 0, S) == EUNSUP
+    assert h(A, A, A, A, 17, 64, 256, 128, 4, A, NUL, 0, S) == EUNSUP
+    assert h(A, A, A, A, 8, 64, 256, 128, 0, NUL, NUL, 0, S) == ENULL
+    assert h(A, A, A, A, 8, 64, 256, 128, 0, MIS, NUL, 0, S) == EALIGN
+    need4 = q.workspace_bytes(b.OP_GEMM_W4A4, 8, 1024, 2048)
+    assert need4 > 0
+    assert h(A, A, A, A, 8, 1024, 2048, 128, 2, A, NUL, 0, S) == EWS
 
 
 def test_verify_validation():

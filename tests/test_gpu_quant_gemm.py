@@ -306,6 +306,38 @@ def test_w4a4_row_invariance(N, K):
     assert_close(Y80, oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4 M=80")
 
 
+# ------------------------------------------------------------------ bf16 output
+# every W4A4 family, vector and ragged N, with and without a k-split
+BF16_CASES = [
+    (8, 1001, 2048, q.GEMM_STREAM),     # ragged N
+    (8, 4608, 3584, q.GEMM_AUTO),
+    (5, 1028, 1024, q.GEMM_SKINNY),     # k-split over several workgroups
+    (40, 9000, 1024, q.GEMM_SKINNY),    # three activation blocks, no k-split
+    (40, 1030, 2048, q.GEMM_SKINNY),    # k-split, ragged N
+    (300, 1030, 1024, q.GEMM_TILED),    # ragged N
+    (300, 4096, 1024, q.GEMM_AUTO),
+]
+
+
+@pytest.mark.parametrize("M,N,K,variant", BF16_CASES)
+def test_w4a4_bf16_output(M, N, K, variant):
+    """qspec_gemm_w4a4_bf16: each output is the round-to-nearest-even bf16 of
+    the fp32 value qspec_gemm_w4a4 stores (same variant), bit for bit, and so
+    within the fp32 tolerance plus half a bf16 unit (2^-9 relative) of the
+    oracle."""
+    say(f"w4a4 bf16 output M={M} N={N} K={K} variant={variant}")
+    W, X = _case(31, M, N, K)
+    Wq, Ws = oracle.pack_w4(W)
+    Xq, Xs = oracle.quant_act(X)
+    args = (dev(Xq), dev(Xs), dev_w(Wq), dev_s(Ws))
+    y32 = host(q.gemm_w4a4(*args, variant=variant, N=N))
+    bits = host_bits16(q.gemm_w4a4_bf16(*args, variant=variant, N=N))
+    assert np.array_equal(bits, oracle.f32_to_bf16_bits(y32.astype(np.float32)))
+    want = oracle.gemm_w4a4(Xq, Xs, Wq, Ws)
+    err = np.abs(oracle.bf16_bits_to_f32(bits).astype(np.float64) - want)
+    assert np.all(err <= 2e-3 * np.abs(want).max() + 2.0 ** -9 * np.abs(want) + 1e-30)
+
+
 def test_determinism():
     N = 4608
     W, X = _case(18, 40, N, 3584)
