@@ -47,6 +47,7 @@ from .quant import (  # noqa: F401
     gemm_w4a4,
     gemm_w4a16,
 )
+from .w4a8 import gemm_w4a8, quant_act8, w4a8_partials  # noqa: F401
 from .rotate import (  # noqa: F401
     fwht128_f32,
     rotate_x,
