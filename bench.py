@@ -325,6 +325,61 @@ def measure_rotation(torch, q, wl, reps=20):
     return out
 
 
+def measure_w4a8_tier(torch, q, wl, reps=10):
+    """The W4A8 middle tier on the shared buffer at the draft batch (M = 8):
+    per projection the time of quantizer + GEMM against W4A4 and W4A16 (each
+    replay reads another weight copy), and on the QKV shape with x20 outlier
+    channels each layer's relative error against the exact product
+    (512 sampled output columns computed exactly on the host)."""
+    import synth
+    rng = synth.make_rng(1, 6)
+    out = {"times_us": {}}
+    for p in wl.proj:
+        N, K = p["N"], p["K"]
+        X8 = p["X16"][:8].contiguous()
+        Y = torch.empty((8, N), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty(max(1, q.workspace_bytes(1, 8, N, K), q.workspace_bytes(2, 8, N, K),
+                             q.workspace_bytes(4, 8, N, K)), dtype=torch.uint8, device="cuda:0")
+        q4 = (torch.empty((8, K // 2), dtype=torch.uint8, device="cuda:0"),
+              torch.empty((8,), dtype=torch.float32, device="cuda:0"))
+        q8 = (torch.empty((8, K), dtype=torch.int8, device="cuda:0"),
+              torch.empty((8,), dtype=torch.float32, device="cuda:0"))
+        cps = p["copies"]
+
+        def f4():
+            for Wq, Ws in cps:
+                q.gemm_w4a4(*q.quant_act(X8, *q4), Wq, Ws, variant=q.GEMM_SKINNY, Y=Y, ws=ws)
+
+        def f8():
+            for Wq, Ws in cps:
+                q.gemm_w4a8(*q.quant_act8(X8, *q8), Wq, Ws, Y=Y, ws=ws)
+
+        def f16():
+            for Wq, Ws in cps:
+                q.gemm_w4a16(X8, Wq, Ws, variant=q.GEMM_SKINNY, Y=Y, ws=ws)
+        t = [_graph_time(torch, f, reps, launches=1) / len(cps) for f in (f4, f8, f16)]
+        out["times_us"][p["name"]] = {"w4a4": round(t[0], 2), "w4a8": round(t[1], 2),
+                                      "w4a16": round(t[2], 2)}
+    N, K, ncols = 4608, 3584, 512
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, 8, K, n_outliers=synth.outlier_count(K))
+    cols = np.sort(rng.choice(N, size=ncols, replace=False))
+    x = (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    y = x @ W[cols].astype(np.float64).T
+    Wq, Ws = q.pack_w4(torch.from_numpy(W).to("cuda:0"))
+    Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    Ys = {"w4a4": q.gemm_w4a4(*q.quant_act(Xd), Wq, Ws, N=N),
+          "w4a8": q.gemm_w4a8(*q.quant_act8(Xd), Wq, Ws, N=N),
+          "w4a16": q.gemm_w4a16(Xd, Wq, Ws, N=N)}
+    torch.cuda.synchronize()
+    out["rel_error_vs_exact_qkv_M8"] = {
+        k: round(float(np.linalg.norm(v.cpu().numpy()[:, cols] - y) / np.linalg.norm(y)), 4)
+        for k, v in Ys.items()}
+    out["note"] = ("draft-side times include the quantizer; W4A8 reads the same packed INT4 buffer "
+                   "(no extra weight copy)")
+    return out
+
+
 def measure_decode_gemv(torch, q, wl, reps=10):
     """W4A16 at the decode-verify shapes of batch 1 (M = 1 * (4+1) = 5) on
     gate|up and down, and the Llama-3-8B lm_head (4096 -> 128256) at M = 1.
@@ -566,6 +621,8 @@ def run(args):
         line["batch_sweep_layer"] = measure_batch_sweep(torch, q, wl)
         log("rotation ahead of the quantizers")
         line["rotation"] = measure_rotation(torch, q, wl)
+        log("W4A8 middle tier")
+        line["w4a8_tier"] = measure_w4a8_tier(torch, q, wl)
         log("verify at batch 32, V=128256")
         line["verify_b32_v128256"] = measure_verify_llama(torch, q)
         log("end-to-end self-speculative loop")
@@ -600,10 +657,11 @@ def run_only(which):
     torch.cuda.set_device(0)
     if which == "verify":
         res = measure_verify_llama(torch, q)
-    elif which in ("batch", "rotation"):
+    elif which in ("batch", "rotation", "w4a8"):
         wl = Decode(torch, q)
         torch.cuda.synchronize()
-        res = (measure_batch_sweep if which == "batch" else measure_rotation)(torch, q, wl)
+        res = {"batch": measure_batch_sweep, "rotation": measure_rotation,
+               "w4a8": measure_w4a8_tier}[which](torch, q, wl)
     elif which == "e2e":
         res = measure_e2e(torch)
     else:
@@ -693,7 +751,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the decode-GEMV, prefill and verify side measurements")
-    ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e", "batch", "rotation"],
+    ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e", "batch", "rotation", "w4a8"],
                     help="run one side measurement alone and print its JSON (for profiling)")
     ap.add_argument("--counters", action="store_true",
                     help="run only the copy calibration and the dominant kernel (for rocprofv3 --pmc)")

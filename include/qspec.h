@@ -59,7 +59,7 @@ enum {
 };
 
 /* operation ids for qspec_workspace_bytes */
-enum { QSPEC_OP_GEMM_W4A4 = 1, QSPEC_OP_GEMM_W4A16 = 2, QSPEC_OP_VERIFY = 3 };
+enum { QSPEC_OP_GEMM_W4A4 = 1, QSPEC_OP_GEMM_W4A16 = 2, QSPEC_OP_VERIFY = 3, QSPEC_OP_GEMM_W4A8 = 4 };
 
 /* verify modes */
 enum { QSPEC_VERIFY_GREEDY = 0, QSPEC_VERIFY_SAMPLE = 1 };
@@ -98,7 +98,7 @@ const char* qspec_version(void);
 qspec_status qspec_device_check(void);
 
 /* Bytes of scratch `ws` that the call with these sizes needs (0 = none).
- *   QSPEC_OP_GEMM_W4A4 / QSPEC_OP_GEMM_W4A16: (M, N, K)
+ *   QSPEC_OP_GEMM_W4A4 / _W4A16 / _W4A8:      (M, N, K)
  *   QSPEC_OP_VERIFY:                           (B, gamma, V)
  * The answer is the maximum over all variants and modes, so one workspace
  * sized by it serves every call of that op with sizes no larger. */
@@ -208,6 +208,33 @@ qspec_status qspec_gemm_w4a4_bf16(const uint8_t* Xq, const float* Xs,
                                   int64_t M, int64_t N, int64_t K, int group,
                                   int variant, uint16_t* Y,
                                   void* ws, size_t ws_bytes, qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * A W4A8 middle tier on the same shared buffer.  SpecQuant (Abstract) derives
+ * an 8-bit variant between INT4 and FP16 from one base model; QSpec's
+ * Builds-on list names QServe (4-bit weights, 8-bit activations).  Reading:
+ * the packed INT4 weights and fp16 group scales are read unchanged (no extra
+ * copy); only the activations move to 8 bits.
+ *
+ * qspec_quant_act8 -- per token row: a = max|x|, s = a / 127 (fp32 IEEE
+ *   divide) stored in Xs[m]; code = clamp(rne(x / s), -128, 127), one signed
+ *   byte each; a == 0 gives s = 0 and zero codes.
+ *   X [M][K] bf16 bits; Xq [M][K] int8 (out); Xs [M] fp32 (out).
+ * qspec_gemm_w4a8 -- Y[m,n] = Xs[m] * sum_g float(Ws[n,g]) * P[m,n,g] with
+ *   P the exact int32 group partial of the 8-bit codes and the 4-bit
+ *   weights, computed with int8 MFMA; the SKINNY family at every M (variant
+ *   AUTO or SKINNY, anything else QSPEC_ERR_UNSUPPORTED); a row's result does
+ *   not depend on M.  Wq/Ws as for qspec_gemm_w4a4; Y [M][N] fp32 (out);
+ *   ws/ws_bytes: qspec_workspace_bytes(QSPEC_OP_GEMM_W4A8, M, N, K) bytes
+ *   (the W4A4 size).  Validation and errors as for qspec_gemm_w4a4.
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_quant_act8(const uint16_t* X, int64_t M, int64_t K,
+                              int8_t* Xq, float* Xs, qspec_stream stream);
+qspec_status qspec_gemm_w4a8(const int8_t* Xq, const float* Xs,
+                             const uint8_t* Wq, const uint16_t* Ws,
+                             int64_t M, int64_t N, int64_t K, int group,
+                             int variant, float* Y,
+                             void* ws, size_t ws_bytes, qspec_stream stream);
 
 /* ---------------------------------------------------------------------------
  * qspec_gemm_w4a16 -- the verifier's linear layer (QSpec Abstract:

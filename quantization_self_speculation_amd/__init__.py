@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     rotate_x,
     gemm_w4a4,
     gemm_w4a4_bf16,
+    gemm_w4a8,
+    quant_act8,
     gemm_w4a16,
     verify,
     workspace_bytes,

@@ -19,7 +19,7 @@ _lib = None
 
 GEMM_AUTO, GEMM_GEMV, GEMM_SKINNY, GEMM_TILED, GEMM_STREAM = 0, 1, 2, 3, 4
 VERIFY_GREEDY, VERIFY_SAMPLE = 0, 1
-OP_GEMM_W4A4, OP_GEMM_W4A16, OP_VERIFY = 1, 2, 3
+OP_GEMM_W4A4, OP_GEMM_W4A16, OP_VERIFY, OP_GEMM_W4A8 = 1, 2, 3, 4
 GROUP = 128
 
 
@@ -61,6 +61,8 @@ def lib():
             "qspec_gemm_w4a4": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
             "qspec_gemm_w4a4_bf16": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_gemm_w4a16": (I, [P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
+            "qspec_quant_act8": (I, [P, I64, I64, P, P, P]),
+            "qspec_gemm_w4a8": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_verify": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P, SZ, P]),
             "qspec_embed": (I, [P, I64, I64, P, I64, P, P]),
             "qspec_add_rmsnorm": (I, [P, I64, P, I64, I64, I64, ctypes.c_double, P, P]),
@@ -234,6 +236,37 @@ def gemm_w4a4_bf16(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None, N=None):
     _check(lib().qspec_gemm_w4a4_bf16(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), M, N, K, GROUP,
                                       variant, _ptr(Y), _ptr(w), wb, _stream()),
            "qspec_gemm_w4a4_bf16")
+    return Y
+
+
+def quant_act8(X, Xq=None, Xs=None):
+    """bf16 activations [M, K] -> (int8 codes [M, K], fp32 scales [M]): the
+    8-bit per-token quantizer of the W4A8 tier."""
+    _need(X, "X", torch.bfloat16)
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if Xs is None:
+        Xs = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _need(Xq, "Xq", torch.int8, (M, K))
+    _need(Xs, "Xs", torch.float32, (M,))
+    _check(lib().qspec_quant_act8(_ptr(X), M, K, _ptr(Xq), _ptr(Xs), _stream()), "qspec_quant_act8")
+    return Xq, Xs
+
+
+def gemm_w4a8(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None, N=None):
+    """W4A8 linear layer on the shared buffer -> Y fp32 [M, N] (N as for gemm_w4a4)."""
+    _need(Xq, "Xq", torch.int8)
+    M, K = Xq.shape
+    N = _out_n(N, Y, Wq)
+    _need(Xs, "Xs", torch.float32, (M,))
+    _need(Wq, "Wq", torch.uint8, (padded_rows(N), K // 2))
+    _need(Ws, "Ws", torch.float16, (padded_rows(N), K // GROUP))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    w, wb = _workspace(workspace_bytes(OP_GEMM_W4A8, M, N, K), Xq.device, ws)
+    _check(lib().qspec_gemm_w4a8(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), M, N, K, GROUP, variant,
+                                 _ptr(Y), _ptr(w), wb, _stream()), "qspec_gemm_w4a8")
     return Y
 
 

@@ -168,6 +168,7 @@ qspec_status qspec_device_check(void) { return device_check(); }
 size_t qspec_workspace_bytes(int op, int64_t a, int64_t b, int64_t c) {
   switch (op) {
     case QSPEC_OP_GEMM_W4A4:
+    case QSPEC_OP_GEMM_W4A8:
       if (a < 1 || b < 1 || c < QSPEC_GROUP || c % QSPEC_GROUP) return 0;
       return w4a4_ws_bytes(a, b, c);
     case QSPEC_OP_GEMM_W4A16:
@@ -203,6 +204,17 @@ qspec_status qspec_quant_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* X
   QS_PTR(Xs);
   QS_TRY(device_check());
   return hip_result(launch_quant_act(X, M, K, Xq, Xs, (hipStream_t)stream), "quant_act launch");
+}
+
+qspec_status qspec_quant_act8(const uint16_t* X, int64_t M, int64_t K, int8_t* Xq, float* Xs,
+                              qspec_stream stream) {
+  QS_REQUIRE(M >= 1 && M <= kMaxDim, QSPEC_ERR_SHAPE, "need M >= 1 (got %lld)", (long long)M);
+  QS_TRY(check_k(K));
+  QS_PTR(X);
+  QS_PTR(Xq);
+  QS_PTR(Xs);
+  QS_TRY(device_check());
+  return hip_result(launch_quant_act8(X, M, K, Xq, Xs, (hipStream_t)stream), "quant_act8 launch");
 }
 
 qspec_status qspec_rotate_w(const float* W, int64_t N, int64_t K, float* Wr, qspec_stream stream) {
@@ -273,6 +285,24 @@ qspec_status qspec_gemm_w4a4_bf16(const uint8_t* Xq, const float* Xs, const uint
   return hip_result(launch_w4a4(Xq, Xs, Wq, Ws, M, N, K, variant, nullptr, Y, nullptr, ws,
                                 (hipStream_t)stream),
                     "gemm_w4a4_bf16 launch");
+}
+
+qspec_status qspec_gemm_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq,
+                             const uint16_t* Ws, int64_t M, int64_t N, int64_t K, int group,
+                             int variant, float* Y, void* ws, size_t ws_bytes,
+                             qspec_stream stream) {
+  QS_TRY(check_gemm(M, N, K, group, variant, false));
+  QS_REQUIRE(variant == QSPEC_GEMM_AUTO || variant == QSPEC_GEMM_SKINNY, QSPEC_ERR_UNSUPPORTED,
+             "W4A8 runs the SKINNY family (variant AUTO or SKINNY, got %d)", variant);
+  QS_PTR(Xq);
+  QS_PTR(Xs);
+  QS_PTR(Wq);
+  QS_PTR(Ws);
+  QS_PTR(Y);
+  QS_TRY(check_ws(ws, ws_bytes, w4a4_ws_bytes(M, N, K)));
+  QS_TRY(device_check());
+  return hip_result(launch_w4a8(Xq, Xs, Wq, Ws, M, N, K, variant, Y, ws, (hipStream_t)stream),
+                    "gemm_w4a8 launch");
 }
 
 qspec_status qspec_gemm_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,

@@ -170,11 +170,11 @@ __device__ __forceinline__ float group_sum16(float v) {
 //     when blocks go round-robin to the 8 XCDs (a locality hint only: the
 //     hand-off of partials is correct on any placement).
 // ============================================================================
-enum { kW4A16 = 0, kW4A4 = 1 };
+enum { kW4A16 = 0, kW4A4 = 1, kW4A8 = 2 };  // W4A8: skinny family only
 
 struct SkinnyArgs {
-  const void* X;            // W4A16: bf16 [M][K]; W4A4: packed codes [M][K/2]
-  const float* Xs;          // W4A4: [M]
+  const void* X;            // W4A16: bf16 [M][K]; W4A4: packed codes [M][K/2]; W4A8: int8 [M][K]
+  const float* Xs;          // W4A4 / W4A8: [M]
   const uint8_t* Wq;
   const uint16_t* Ws;
   float* Y;
@@ -211,10 +211,10 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
         const int m = m0 + mb * 16 + l16;
         const int n = n_w + nb * 16 + lg * 4;
         if (m < M && n < N) {
-          const float xsc = MODE == kW4A4 ? a.Xs[m] : 1.0f;
+          const float xsc = MODE != kW4A16 ? a.Xs[m] : 1.0f;
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = MODE == kW4A4 ? xsc * tot[nb][mb][r] : tot[nb][mb][r];
+          for (int r = 0; r < 4; ++r) v[r] = MODE != kW4A16 ? xsc * tot[nb][mb][r] : tot[nb][mb][r];
           out_store4(a.Y, a.Yb, (int64_t)m * N + n, v, N - n, vec);
         }
       }
@@ -289,7 +289,7 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   for (int e = 0; e < EPT; ++e) {
     const int i = threadIdx.x + NT * e;
     const int m = m0 + i / WROWS, n = n_wg + i % WROWS;
-    if (ok[e]) out_store1(a.Y, a.Yb, (int64_t)m * N + n, MODE == kW4A4 ? a.Xs[m] * acc[e] : acc[e]);
+    if (ok[e]) out_store1(a.Y, a.Yb, (int64_t)m * N + n, MODE != kW4A16 ? a.Xs[m] * acc[e] : acc[e]);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(a.cnt + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -302,11 +302,12 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
 template <int MODE, int MB, int NB, int CH, int PD, bool WITHP, int NWV = 4>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny_wpe(MODE, MB)))) void skinny_kernel(const SkinnyArgs a) {
   static_assert(PD % CH == 0, "prefetch depth must be a multiple of the chunk");
+  static_assert(!(WITHP && MODE != kW4A4), "the int32 partials output is a W4A4 check path");
   constexpr int NT = 64 * NWV;             // threads of a workgroup
   constexpr int ROWS = 16 * MB;            // activation rows of an m-chunk
   constexpr int WROWS = 16 * NB * NWV;     // weight rows of a tile (NWV wavefronts x NB blocks of 16)
   constexpr int XSTB = (MODE == kW4A16 ? CH * 256 : CH * 128) + 16;  // LDS row bytes
-  constexpr int XCH = MODE == kW4A16 ? ROWS * CH * 16 : ROWS * CH * 4;  // 16-B chunks
+  constexpr int XCH = MODE == kW4A16 ? ROWS * CH * 16 : MODE == kW4A8 ? ROWS * CH * 8 : ROWS * CH * 4;  // 16-B chunks
   constexpr int XPT = (XCH + NT - 1) / NT;
   constexpr int SPT = (CH * WROWS + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][ROWS * XSTB];
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
   // (valid) addresses whose results are never used; the activation rows go
   // through a buffer resource over this m-chunk's rows, and rows past M read
   // an out-of-range offset (zeros, no memory access)
-  const int xrb = MODE == kW4A16 ? K * 2 : K / 2;  // activation row bytes
+  const int xrb = MODE == kW4A16 ? K * 2 : MODE == kW4A8 ? K : K / 2;  // activation row bytes
   const int mrows = min(ROWS, M - m0);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(static_cast<const uint8_t*>(a.X) + (int64_t)m0 * xrb), (short)0,
@@ -359,6 +360,10 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
       if (MODE == kW4A16) {
         const int r = idx / (CH * 16), cc = idx % (CH * 16);
         off = r < mrows ? (uint32_t)(r * xrb + min(gc + (cc >> 4), G - 1) * (kGroup * 2) + (cc & 15) * 16)
+                        : 0x80000000u;
+      } else if (MODE == kW4A8) {
+        const int r = idx / (CH * 8), cc = idx % (CH * 8);
+        off = r < mrows ? (uint32_t)(r * xrb + min(gc + (cc >> 3), G - 1) * kGroup + (cc & 7) * 16)
                         : 0x80000000u;
       } else {
         const int r = idx / (CH * 4), cc = idx % (CH * 4);
@@ -390,6 +395,20 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
         uint32_t p[4];
         bf16x8_interleave(v, p);
         *reinterpret_cast<uint4*>(&xs[buf][r * XSTB + cc * 16]) = make_uint4(p[0], p[1], p[2], p[3]);
+      } else if (MODE == kW4A8) {
+        // 16 codes k0 .. k15 of the group slot cc & 7, reordered to the order
+        // the widened 4-bit path stages (even k of each 8, then odd k), so
+        // both modes meet the weights' lo/hi widening in the same k order
+        if (idx >= XCH) continue;
+        const int r = idx / (CH * 8), cc = idx % (CH * 8);
+        if (r >= mrows) continue;
+        const uint4 p = xr[i];
+        const uint4 o = make_uint4(
+            (p.x & 0xFFu) | ((p.x >> 8) & 0xFF00u) | ((p.y & 0xFFu) << 16) | ((p.y << 8) & 0xFF000000u),
+            ((p.x >> 8) & 0xFFu) | ((p.x >> 16) & 0xFF00u) | ((p.y << 8) & 0xFF0000u) | (p.y & 0xFF000000u),
+            (p.z & 0xFFu) | ((p.z >> 8) & 0xFF00u) | ((p.w & 0xFFu) << 16) | ((p.w << 8) & 0xFF000000u),
+            ((p.z >> 8) & 0xFFu) | ((p.z >> 16) & 0xFF00u) | ((p.w << 8) & 0xFF0000u) | (p.w & 0xFF000000u));
+        *reinterpret_cast<uint4*>(&xs[buf][r * XSTB + (cc >> 3) * 128 + (cc & 7) * 16]) = o;
       } else if (idx < XCH) {
         const int r = idx / (CH * 4), cc = idx % (CH * 4);
         if (r >= mrows) continue;
@@ -515,7 +534,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
           const uint16_t* wp = &wsl[buf][gl * WROWS + wave * 16 * NB + nb * 16 + lg * 4];
           float sc[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc[r] = half_bits_to_float(wp[r]) * 0.00390625f;  // /256
+          // / 256 when both operands carry the x16 of the widening, / 16 for
+          // 8-bit activation codes
+          for (int r = 0; r < 4; ++r) sc[r] = half_bits_to_float(wp[r]) * (MODE == kW4A8 ? 0.0625f : 0.00390625f);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -1526,23 +1547,22 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
   }
   if (p.MB == 1 && p.NWV != 4 && !WITHP) {
     const dim3 blk(64 * p.NWV);
-    switch (p.NWV) {
-      case 5:
-        if (MODE == kW4A16) hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 5>), grid, blk, 0, s, a);
-        else hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, 1, QSPEC_SK_A1, false, 5>), grid, blk, 0, s, a);
-        break;
-      case 8:
-        if (MODE == kW4A16) hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 8>), grid, blk, 0, s, a);
-        else hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, 1, QSPEC_SK_A1, false, 8>), grid, blk, 0, s, a);
-        break;
-      default:
-        if (MODE == kW4A16) hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 10>), grid, blk, 0, s, a);
-        else hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, 1, QSPEC_SK_A1, false, 10>), grid, blk, 0, s, a);
-        break;
+    if constexpr (MODE == kW4A16) {
+      switch (p.NWV) {
+        case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 5>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 8>), grid, blk, 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 10>), grid, blk, 0, s, a); break;
+      }
+    } else {  // W4A4 and W4A8 share the int8 data flow and its parameters
+      switch (p.NWV) {
+        case 5: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, false, 5>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, false, 8>), grid, blk, 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, false, 10>), grid, blk, 0, s, a); break;
+      }
     }
     return hipGetLastError();
   }
-  if (MODE == kW4A16) {
+  if constexpr (MODE == kW4A16) {
     switch (p.MB) {
       case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, WITHP>), grid, block, 0, s, a); break;
       case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_NB16, QSPEC_SK_B2, WITHP>), grid, block, 0, s, a); break;
@@ -1551,10 +1571,10 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
     }
   } else {
     switch (p.MB) {
-      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A4, 1, 1, QSPEC_SK_A1, WITHP>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A4, 2, 1, QSPEC_SK_A2, WITHP>), grid, block, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A4, 3, 1, QSPEC_SK_A3, WITHP>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<kW4A4, 4, 1, QSPEC_SK_A4, WITHP>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<MODE, 2, 1, QSPEC_SK_A2, WITHP>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<MODE, 3, 1, QSPEC_SK_A3, WITHP>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<MODE, 4, 1, QSPEC_SK_A4, WITHP>), grid, block, 0, s, a); break;
     }
   }
   return hipGetLastError();
@@ -1681,6 +1701,26 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
   a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;
   a.epoch = next_epoch();
   return launch_skinny<kW4A4>(a, p, s);
+}
+
+// W4A8: the skinny family at every M, on the W4A4 plan (same k-split, same
+// workspace); AUTO and SKINNY are the accepted variants.
+hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
+                       int64_t M, int64_t N, int64_t K, int variant, float* Y, void* ws,
+                       hipStream_t s) {
+  (void)variant;
+  const SkinnyPlan p = plan_skinny(1, M, N, K);
+  SkinnyArgs a{};
+  a.X = Xq;
+  a.Xs = Xs;
+  a.Wq = Wq;
+  a.Ws = Ws;
+  a.Y = Y;
+  a.cnt = p.S > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
+  a.part = p.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.cnt_bytes) : nullptr;
+  a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;
+  a.epoch = next_epoch();
+  return launch_skinny_t<kW4A8, false>(a, p, s);
 }
 
 }  // namespace qspec

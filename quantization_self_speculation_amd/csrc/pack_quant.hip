@@ -103,6 +103,27 @@ __device__ __forceinline__ uint32_t pack8(uint4 v, float s, float r) {
   return pack8f(x, s, r);
 }
 
+// The 8-bit code of v at s = absmax / 127 (s > 0), r = 1 / s: here
+// |v / s| <= 127, so v * r is within 127 * 2^-23 < 2^-16 of the exact
+// quotient and within 2^-15 of the IEEE quotient; farther than that from a
+// half-integer both round alike, nearer the IEEE quotient decides.
+__device__ __forceinline__ int quant_code_act8(float v, float s, float r) {
+  const float qa = v * r;
+  float k = __builtin_rintf(qa);
+  if (!(fabsf(qa - k) < 0.5f - 0x1p-15f)) k = __builtin_rintf(v / s);
+  return (int)fminf(fmaxf(k, -128.0f), 127.0f);
+}
+
+// eight bf16 values -> their eight 8-bit codes, code i in byte i
+__device__ __forceinline__ uint2 pack8_i8(uint4 v, float s, float r) {
+  float x[8];
+  bf16x8_to_f32(v, x);
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(quant_code_act8(x[i], s, r) & 0xFF) << (8 * (i & 3));
+  return make_uint2(w[0], w[1]);
+}
+
 // ------------------------------------------------------------------ rotation
 // Walsh-Hadamard transform of one 128-value group (Sylvester order), held by
 // 16 consecutive lanes with 8 consecutive values each: stages 0-2 inside the
@@ -262,7 +283,7 @@ __global__ __launch_bounds__(256) void quant_act_rot_long_kernel(const uint16_t*
 
 // One NT-thread block per token row.  The row is read once into registers
 // (NC 16-byte chunks per thread), reduced to its absmax, then coded.
-template <int NT, int NC>
+template <int NT, int NC, int BITS>
 __global__ __launch_bounds__(NT) void quant_act_kernel(const uint16_t* __restrict__ X,
                                                        int64_t K, uint8_t* __restrict__ Xq,
                                                        float* __restrict__ Xs) {
@@ -286,18 +307,28 @@ __global__ __launch_bounds__(NT) void quant_act_kernel(const uint16_t* __restric
   a = red[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) a = fmaxf(a, red[w]);
-  const float s = a / 7.0f;
+  const float s = a / (BITS == 4 ? 7.0f : 127.0f);
   const float r = 1.0f / s;
-  uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
+  if (BITS == 4) {
+    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = threadIdx.x + NT * i;
-    if (c < nch) out[c] = s != 0.0f ? pack8(v[i], s, r) : 0u;
+    for (int i = 0; i < NC; ++i) {
+      const int c = threadIdx.x + NT * i;
+      if (c < nch) out[c] = s != 0.0f ? pack8(v[i], s, r) : 0u;
+    }
+  } else {
+    uint2* out = reinterpret_cast<uint2*>(Xq + m * K);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = threadIdx.x + NT * i;
+      if (c < nch) out[c] = s != 0.0f ? pack8_i8(v[i], s, r) : make_uint2(0u, 0u);
+    }
   }
   if (threadIdx.x == 0) Xs[m] = s;
 }
 
 // rows longer than 1024 * 8 * 8 = 65536 values: two passes (the second hits L2)
+template <int BITS>
 __global__ __launch_bounds__(256) void quant_act_long_kernel(const uint16_t* __restrict__ X,
                                                              int64_t K, uint8_t* __restrict__ Xq,
                                                              float* __restrict__ Xs) {
@@ -311,10 +342,16 @@ __global__ __launch_bounds__(256) void quant_act_long_kernel(const uint16_t* __r
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = a / 7.0f;
+  const float s = a / (BITS == 4 ? 7.0f : 127.0f);
   const float r = 1.0f / s;
-  uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
-  for (int64_t c = threadIdx.x; c < nch; c += 256) out[c] = s != 0.0f ? pack8(row[c], s, r) : 0u;
+  if (BITS == 4) {
+    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + m * (K / 2));
+    for (int64_t c = threadIdx.x; c < nch; c += 256) out[c] = s != 0.0f ? pack8(row[c], s, r) : 0u;
+  } else {
+    uint2* out = reinterpret_cast<uint2*>(Xq + m * K);
+    for (int64_t c = threadIdx.x; c < nch; c += 256)
+      out[c] = s != 0.0f ? pack8_i8(row[c], s, r) : make_uint2(0u, 0u);
+  }
   if (threadIdx.x == 0) Xs[m] = s;
 }
 
@@ -329,24 +366,35 @@ hipError_t launch_pack_w4(const float* W, int64_t N, int64_t K, uint8_t* Wq, uin
   return hipGetLastError();
 }
 
-hipError_t launch_quant_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
-                            hipStream_t s) {
+template <int BITS>
+hipError_t launch_quant_act_bits(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
+                                 hipStream_t s) {
   // one block per row, sized so each thread holds at most a few chunks: the
   // short latency chain (load, block max, code) is what a decode row costs
   const int64_t nch = K / 8;  // 16-byte chunks of a row
   const dim3 g((unsigned)M);
   if (nch <= 512) {
-    hipLaunchKernelGGL((quant_act_kernel<256, 2>), g, dim3(256), 0, s, X, K, Xq, Xs);
+    hipLaunchKernelGGL((quant_act_kernel<256, 2, BITS>), g, dim3(256), 0, s, X, K, Xq, Xs);
   } else if (nch <= 2048) {
-    hipLaunchKernelGGL((quant_act_kernel<1024, 2>), g, dim3(1024), 0, s, X, K, Xq, Xs);
+    hipLaunchKernelGGL((quant_act_kernel<1024, 2, BITS>), g, dim3(1024), 0, s, X, K, Xq, Xs);
   } else if (nch <= 4096) {
-    hipLaunchKernelGGL((quant_act_kernel<1024, 4>), g, dim3(1024), 0, s, X, K, Xq, Xs);
+    hipLaunchKernelGGL((quant_act_kernel<1024, 4, BITS>), g, dim3(1024), 0, s, X, K, Xq, Xs);
   } else if (nch <= 8192) {
-    hipLaunchKernelGGL((quant_act_kernel<1024, 8>), g, dim3(1024), 0, s, X, K, Xq, Xs);
+    hipLaunchKernelGGL((quant_act_kernel<1024, 8, BITS>), g, dim3(1024), 0, s, X, K, Xq, Xs);
   } else {
-    hipLaunchKernelGGL(quant_act_long_kernel, g, dim3(256), 0, s, X, K, Xq, Xs);
+    hipLaunchKernelGGL(quant_act_long_kernel<BITS>, g, dim3(256), 0, s, X, K, Xq, Xs);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
+                            hipStream_t s) {
+  return launch_quant_act_bits<4>(X, M, K, Xq, Xs, s);
+}
+
+hipError_t launch_quant_act8(const uint16_t* X, int64_t M, int64_t K, int8_t* Xq, float* Xs,
+                             hipStream_t s) {
+  return launch_quant_act_bits<8>(X, M, K, reinterpret_cast<uint8_t*>(Xq), Xs, s);
 }
 
 hipError_t launch_rotate(bool bf16, const void* in, int64_t R, int64_t K, float scale, void* out,

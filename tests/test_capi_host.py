@@ -94,6 +94,19 @@ def test_gemm_validation():
     assert need > 0
     assert g(A, A, A, 40, 4608, 3584, 128, 2, A, NUL, 0, S) == EWS
     assert g(A, A, A, 40, 4608, 3584, 128, 2, A, A, need - 1, S) == EWS
+    u = L.qspec_gemm_w4a8        # the W4A8 tier: SKINNY family only
+    for v in (1, 3, 4, 9):
+        assert u(A, A, A, A, 8, 64, 256, 128, v, A, NUL, 0, S) == EUNSUP
+    assert u(A, A, A, A, 8, 64, 250, 128, 0, A, NUL, 0, S) == ESHAPE
+    assert u(NUL, A, A, A, 8, 64, 256, 128, 0, A, NUL, 0, S) == ENULL
+    assert u(A, A, A, A, 8, 64, 256, 128, 2, MIS, NUL, 0, S) == EALIGN
+    assert u(A, A, A, A, 8, 1024, 2048, 128, 2, A, NUL, 0, S) == EWS
+    assert q.workspace_bytes(b.OP_GEMM_W4A8, 8, 1024, 2048) == q.workspace_bytes(b.OP_GEMM_W4A4, 8, 1024, 2048)
+    qa8 = L.qspec_quant_act8
+    assert qa8(A, 0, 256, A, A, S) == ESHAPE
+    assert qa8(A, 4, 250, A, A, S) == ESHAPE
+    assert qa8(A, 4, 256, NUL, A, S) == ENULL
+    assert qa8(A, 4, 256, A, MIS, S) == EALIGN
     h = L.qspec_gemm_w4a4_bf16   # same checks as the fp32 call, bf16 Y
     assert h(A, A, A, A, 8, 64, 256, 64, 0, A, NUL, 0, S) == EUNSUP
     assert h(A, A, A, A, 8, 64, 250, 128, 0, A, NUL, 0, S) == ESHAPE
