@@ -1,5 +1,6 @@
 // The dual-mode linear layer: W4A16 (verifier) and W4A4 (drafter) GEMMs over
-// the one shared packed INT4 weight buffer.
+// the one shared packed INT4 weight buffer, and a W4A8 middle tier on the
+// same buffer (8-bit activation codes, the skinny family only).
 //
 // Pages: "QSpec: Speculative Decoding with Complementary Quantization
 // Schemes", Abstract (arXiv) -- low-precision joint quantization (W4A4) for
@@ -10,6 +11,7 @@
 // Arithmetic (the reading of the pages, which give no formula):
 //   W4A16: Y[m,n] = sum_g s[n,g] * sum_{k in g} x[m,k] * q[n,k]
 //   W4A4:  Y[m,n] = a[m] * sum_g s[n,g] * P[m,n,g],  P exact in int32
+//   W4A8:  the same with 8-bit activation codes
 //
 // gfx950 design
 //  * Codes are widened in registers only; the shared buffer stays 4-bit.
@@ -21,7 +23,10 @@
 //    accumulator with it) or with the group sum of x (GEMV).  W4A4 turns
 //    nibbles into int8 holding 16 q (a mask, and a shift for the low
 //    nibbles; exact) and runs v_mfma_i32_16x16x64_i8; the int32 group
-//    partial is 256 P exactly.
+//    partial is 256 P exactly (16 P for W4A8, whose codes are staged as
+//    they are, in the same k order).
+//  * Outputs are fp32, or, for the W4A4 drafter on request, the bf16
+//    rounding (to nearest even) of that fp32 value.
 //  * MFMA operand A = 16 weight rows (n), operand B = 16 activation rows (m),
 //    so each lane of D holds 4 consecutive n of one m: one 16-byte store.
 //  * Within a 128-group, lane l feeds the 32 consecutive k starting at
@@ -154,7 +159,7 @@ __device__ __forceinline__ float group_sum16(float v) {
 }
 
 // ============================================================================
-// MFMA "skinny" family (both modes): the decode / verify shapes.
+// MFMA "skinny" family (all three modes): the decode / verify shapes.
 //   * a workgroup = 4 wavefronts x 16 weight rows = one 64-row n-tile, one
 //     k-slice of the groups, one m-chunk of up to 64 activation rows;
 //   * weights go straight from HBM into a register ring PD groups deep (each
