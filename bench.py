@@ -763,7 +763,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     if args.counters:
         run_counters()
