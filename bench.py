@@ -425,6 +425,47 @@ def measure_decode_gemv(torch, q, wl, reps=10):
     return out
 
 
+def measure_llama_verify_batch(torch, q, reps=5):
+    """Llama-3-8B-shaped layers in W4A16 at the verify batch of 32 sequences:
+    M = 32 (gamma + 1) = 160 and 288 (gamma 4 / 8), AUTO family, each replay
+    reading another weight copy (> 512 MB per shape); TFLOPS and the
+    fraction of the dense bf16 MFMA peak."""
+    shapes = [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096),
+              ("down", 4096, 14336), ("lm_head", 128256, 4096)]
+    out = {}
+    tot = {160: [0.0, 0.0], 288: [0.0, 0.0]}
+    for name, N, K in shapes:
+        W = torch.empty((N, K), dtype=torch.float32, device="cuda:0").normal_(0.0, 0.02)
+        Wq, Ws = q.pack_w4(W)
+        del W
+        nc = max(2, -(-600_000_000 // wbytes(N, K)))
+        cps = [(Wq, Ws)] + [(Wq.clone(), Ws.clone()) for _ in range(nc - 1)]
+        X = torch.randn((288, K), device="cuda:0").to(torch.bfloat16)
+        Y = torch.empty((288, N), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty(max(1, q.workspace_bytes(2, 288, N, K)), dtype=torch.uint8, device="cuda:0")
+        r = {}
+        for M in (160, 288):
+            Xm = X[:M].contiguous()
+            Ym = Y[:M]
+
+            def fn():
+                for Wc, Sc in cps:
+                    q.gemm_w4a16(Xm, Wc, Sc, Y=Ym, ws=ws)
+            us = _graph_time(torch, fn, reps, launches=1) / len(cps)
+            tf = 2.0 * M * N * K / us / 1e6
+            r[f"M{M}"] = {"us": round(us, 2), "tflops": round(tf, 1),
+                          "frac_bf16": round(tf / BF16_PEAK_TFLOPS, 4)}
+            tot[M][0] += 2.0 * M * N * K
+            tot[M][1] += us
+        out[name] = r
+        del cps, Wq, Ws
+        torch.cuda.empty_cache()
+    for M, (fl, us) in tot.items():
+        out[f"all_M{M}"] = {"tflops": round(fl / us / 1e6, 1),
+                            "frac_bf16": round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
 def measure_verify_llama(torch, q, reps=10):
     """verify at batch 32, V = 128256 (Llama-3 vocabulary), gamma 4 and 8,
     greedy and speculative sampling; bytes = one pass over the logits read
@@ -623,6 +664,8 @@ def run(args):
         line["rotation"] = measure_rotation(torch, q, wl)
         log("W4A8 middle tier")
         line["w4a8_tier"] = measure_w4a8_tier(torch, q, wl)
+        log("Llama-3-8B layers at the verify batch (M = 160, 288)")
+        line["llama8b_w4a16_verify_batch"] = measure_llama_verify_batch(torch, q)
         log("verify at batch 32, V=128256")
         line["verify_b32_v128256"] = measure_verify_llama(torch, q)
         log("end-to-end self-speculative loop")
@@ -662,6 +705,8 @@ def run_only(which):
         torch.cuda.synchronize()
         res = {"batch": measure_batch_sweep, "rotation": measure_rotation,
                "w4a8": measure_w4a8_tier}[which](torch, q, wl)
+    elif which == "llama":
+        res = measure_llama_verify_batch(torch, q)
     elif which == "e2e":
         res = measure_e2e(torch)
     else:
@@ -751,7 +796,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the decode-GEMV, prefill and verify side measurements")
-    ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e", "batch", "rotation", "w4a8"],
+    ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e", "batch", "rotation", "w4a8", "llama"],
                     help="run one side measurement alone and print its JSON (for profiling)")
     ap.add_argument("--counters", action="store_true",
                     help="run only the copy calibration and the dominant kernel (for rocprofv3 --pmc)")

@@ -68,10 +68,12 @@ enum { QSPEC_VERIFY_GREEDY = 0, QSPEC_VERIFY_SAMPLE = 1 };
  * the same sequence of operations whatever M is, so row r of Y is bitwise
  * identical at any M; a caller that needs this (for example greedy
  * self-speculation that must reproduce plain verifier decoding token for
- * token) passes the same explicit family for every M.  AUTO picks by M and
- * N: STREAM for M <= 16 when N < 16384 (where SKINNY would have too few
+ * token) passes the same explicit family for every M.  AUTO picks by M, N
+ * and K: STREAM for M <= 16 when N < 16384 (where SKINNY would have too few
  * workgroups to fill the GPU), else SKINNY up to M = 128 (W4A16) or
- * M = 256 (W4A4), TILED beyond. */
+ * M = 256 (W4A4), TILED beyond -- except that up to M = 512 SKINNY stays
+ * when K has at least 64 groups and TILED would have fewer than 128 tiles
+ * (32 x 256 for W4A16, 64 x 256 for W4A4). */
 enum {
   QSPEC_GEMM_AUTO = 0,
   QSPEC_GEMM_GEMV = 1,   /* W4A16 only: VALU GEMV with wavefront reduction   */

@@ -1603,16 +1603,24 @@ GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K / kGroup, kGemvGroup
 // family otherwise up to skinny_max rows, the tiled family beyond.  The
 // crossover measured on the Qwen2.5-7B projections lies between 128 and 192
 // rows for W4A16 and between 256 and 384 for W4A4 (whose skinny kernel has
-// half the MFMA work per weight byte).  The choice depends on M and N only.
-int auto_pick(int64_t M, int64_t N, int64_t skinny_max) {
+// half the MFMA work per weight byte).  Up to 512 rows the skinny family
+// stays where the tiled grid would leave most of the chip idle on a long K
+// (fewer than 128 tiles of bm x 256 and at least 64 groups): it splits K,
+// the tiled kernel walks it on few workgroups (measured on the Qwen2.5-7B
+// and Llama-3-8B down projections at M = 160 ... 512: W4A16 at M = 160
+// 83 / 74 us against 129 / 98 us, W4A4 at M = 288 79 / 76 us against
+// 123 / 95 us).  The choice depends on M, N and K only.
+int auto_pick(int64_t M, int64_t N, int64_t K, int64_t skinny_max, int64_t bm) {
   if (M <= kStreamMaxM && cdiv(N, 64) < QSPEC_SK_TARGET_WG) return QSPEC_GEMM_STREAM;
-  return M <= skinny_max ? QSPEC_GEMM_SKINNY : QSPEC_GEMM_TILED;
+  if (M <= skinny_max) return QSPEC_GEMM_SKINNY;
+  if (M <= 512 && K / kGroup >= 64 && cdiv(N, 256) * cdiv(M, bm) < 128) return QSPEC_GEMM_SKINNY;
+  return QSPEC_GEMM_TILED;
 }
-int w4a16_pick(int variant, int64_t M, int64_t N) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, 128);
+int w4a16_pick(int variant, int64_t M, int64_t N, int64_t K) {
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 128, 32);
 }
-int w4a4_pick(int variant, int64_t M, int64_t N) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, 256);
+int w4a4_pick(int variant, int64_t M, int64_t N, int64_t K) {
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 256, 64);
 }
 
 hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* Xs, float* Y,
@@ -1637,7 +1645,7 @@ size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
                         int64_t N, int64_t K, int variant, float* Y, void* ws, hipStream_t s) {
-  const int v = w4a16_pick(variant, M, N);
+  const int v = w4a16_pick(variant, M, N, K);
   if (v == QSPEC_GEMM_STREAM) return launch_stream<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, nullptr, s);
   if (v == QSPEC_GEMM_GEMV) {
     const GemvPlan q = plan_gemv(K);
@@ -1687,7 +1695,7 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
                        int32_t* P, void* ws, hipStream_t s) {
   // the int32 partials output is a check path served by the skinny family;
   // exactly one of Y (fp32) and Yb (bf16) is given
-  const int v = w4a4_pick(variant, M, N);
+  const int v = w4a4_pick(variant, M, N, K);
   if (v == QSPEC_GEMM_TILED && P == nullptr)
     return launch_tiled<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, Yb, s);
   if (v == QSPEC_GEMM_STREAM && P == nullptr)

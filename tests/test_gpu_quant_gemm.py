@@ -338,6 +338,27 @@ def test_w4a4_bf16_output(M, N, K, variant):
     assert np.all(err <= 2e-3 * np.abs(want).max() + 2.0 ** -9 * np.abs(want) + 1e-30)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 1000, 8192), (200, 1000, 8192), (300, 1000, 1024)])
+def test_auto_beyond_the_skinny_limit(M, N, K):
+    """AUTO between the SKINNY limit and 512 rows: with a long K (>= 64 groups)
+    and a small tiled grid it keeps the SKINNY family (the first two shapes:
+    bitwise the SKINNY result), otherwise TILED (the third: bitwise the TILED
+    result); either way within tolerance of the oracle."""
+    say(f"auto beyond the skinny limit M={M} N={N} K={K}")
+    W, X = _case(33, M, N, K)
+    Wq, Ws = oracle.pack_w4(W)
+    Xq, Xs = oracle.quant_act(X)
+    a4 = (dev(Xq), dev(Xs), dev_w(Wq), dev_s(Ws))
+    fam = q.GEMM_SKINNY if K >= 8192 else q.GEMM_TILED
+    y4 = host(q.gemm_w4a4(*a4, N=N))
+    assert np.array_equal(y4.view(np.uint32), host(q.gemm_w4a4(*a4, variant=fam, N=N)).view(np.uint32))
+    assert_close(y4, oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4 auto")
+    a16 = (dev_bf16(X), dev_w(Wq), dev_s(Ws))
+    y16 = host(q.gemm_w4a16(*a16, N=N))
+    assert np.array_equal(y16.view(np.uint32), host(q.gemm_w4a16(*a16, variant=fam, N=N)).view(np.uint32))
+    assert_close(y16, oracle.gemm_w4a16(X, Wq, Ws), what="w4a16 auto")
+
+
 def test_determinism():
     N = 4608
     W, X = _case(18, 40, N, 3584)
@@ -451,6 +472,29 @@ def test_largest_k():
         say(f"largest K w4a16 variant={v}")
         Y = q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=v, N=N)
         assert_close(host(Y), want16, what=f"w4a16 K=2^20 variant={v}")
+
+
+LLAMA8B = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096),
+           "down": (4096, 14336), "lm_head": (128256, 4096)}
+
+
+@pytest.mark.parametrize("proj", list(LLAMA8B))
+def test_llama8b_verify_batch_shapes(proj):
+    """Llama-3-8B-shaped layers at the verify batch of 32 sequences
+    (M = 32 (gamma + 1) = 160 and 288, gamma 4 / 8) in W4A16, AUTO: sampled
+    output columns against the oracle, computed from those weight rows."""
+    N, K = LLAMA8B[proj]
+    rng = synth.make_rng(4)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, 288, K, n_outliers=synth.outlier_count(K))
+    cols = _sampled_cols(N, rng, 384)
+    Wq, Ws = oracle.pack_w4(W[cols])
+    Wq_d, Ws_d = q.pack_w4(dev(W))
+    del W
+    for M in (160, 288):
+        say(f"llama8b {proj} w4a16 M={M}")
+        Y = host(q.gemm_w4a16(dev_bf16(X[:M].copy()), Wq_d, Ws_d, N=N))
+        assert_close(Y[:, cols], oracle.gemm_w4a16(X[:M], Wq, Ws), what=f"{proj} M={M}")
 
 
 def test_llama8b_lm_head_gemv():
