@@ -76,6 +76,16 @@ qspec_status qspec_attention(const float* q, const uint16_t* kcache, const uint1
                              const int32_t* pos, int64_t B, int64_t cap, uint16_t* out,
                              qspec_stream stream);
 
+/* qspec_add_rmsnorm with the drafter's input in the same pass: besides y,
+ * yq [M][d/2] and ys [M] receive exactly what qspec_quant_act gives for the
+ * bf16 rows y (per-token absmax / 7, codes rne(y / s) clamped, nibble
+ * packed), one launch instead of two in every draft forward.  d is a
+ * multiple of 128 (<= 4096); yq, ys 16-byte aligned; other arguments and
+ * errors as for qspec_add_rmsnorm. */
+qspec_status qspec_add_rmsnorm_quant(float* x, int64_t x_stride, const float* add,
+                                     int64_t add_stride, int64_t M, int64_t d, double eps,
+                                     uint16_t* y, uint8_t* yq, float* ys, qspec_stream stream);
+
 /* SwiGLU: a[m][j] = bf16(silu(g) * u), g = gu[m][j], u = gu[m][ffn + j],
  * silu(g) = g / (1 + exp(-g)).  gu fp32 [M][2 ffn], a bf16 bits [M][ffn]. */
 qspec_status qspec_silu_mul(const float* gu, int64_t M, int64_t ffn, uint16_t* a,

@@ -38,6 +38,7 @@ from .binding import (  # noqa: F401
     rope_kv,
     attention,
     silu_mul,
+    add_rmsnorm_quant,
     argmax,
     spec_prepare,
     spec_commit,

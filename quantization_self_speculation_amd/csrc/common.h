@@ -91,6 +91,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// The code of v at the activation scale s = absmax / 7 (s > 0), with r the
+// IEEE reciprocal of s.  |v / s| <= 7 (about), so v * r is within 2^-20 of
+// the exact quotient and within 2^-19 of the IEEE quotient v / s; wherever
+// v * r lies farther than 2^-19 from a half-integer both round to the same
+// integer.  Nearer (or NaN, or an infinite r) the IEEE quotient decides, so
+// every code equals rne(v / s) clamped, as the divide would give it.
+__device__ __forceinline__ int quant_code_act(float v, float s, float r) {
+  const float qa = v * r;
+  float k = __builtin_rintf(qa);
+  if (!(fabsf(qa - k) < 0.5f - 0x1p-19f)) k = __builtin_rintf(v / s);
+  return (int)fminf(fmaxf(k, -8.0f), 7.0f);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }

@@ -69,11 +69,45 @@ __global__ __launch_bounds__(256) void embed_kernel(const uint16_t* __restrict__
 // row; each thread keeps up to kNormPer elements.
 constexpr int kNormPer = 16;  // d <= 4096
 
+// The drafter's per-token 4-bit codes of a row that a block has just
+// produced as bf16 (thread t holds elements t + 256 i): the row's absmax, the
+// scale s = absmax / 7 and each code exactly as the stand-alone quantizer
+// takes them, so the codes equal that quantizer's on the stored bf16 row.
+// The even thread of each pair packs its element's code (low nibble) with
+// its neighbour's (high nibble).
+template <int PER>
+__device__ __forceinline__ void quant_row_bf16(const uint16_t (&yb)[PER], int n, float* red,
+                                               uint8_t* __restrict__ q, float* __restrict__ qs) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if ((int)threadIdx.x + 256 * i < n) a = fmaxf(a, fabsf(__uint_as_float((uint32_t)yb[i] << 16)));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+  __syncthreads();  // red may still be read by an earlier reduction
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = a / 7.0f;
+  const float r = 1.0f / s;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = (int)threadIdx.x + 256 * i;
+    const int c = (j < n && s != 0.0f) ? quant_code_act(__uint_as_float((uint32_t)yb[i] << 16), s, r) : 0;
+    const int nb = __shfl_xor(c, 1, 64);
+    if (!(threadIdx.x & 1) && j < n) q[j >> 1] = (uint8_t)((c & 0xF) | ((nb & 0xF) << 4));
+  }
+  if (threadIdx.x == 0) *qs = s;
+}
+
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x, int64_t xs,
                                                           const float* __restrict__ add, int64_t as,
                                                           int d, double eps,
-                                                          uint16_t* __restrict__ y) {
+                                                          uint16_t* __restrict__ y,
+                                                          uint8_t* __restrict__ yq,
+                                                          float* __restrict__ ys) {
   __shared__ double red[4];
+  __shared__ float redf[4];
   const int64_t m = blockIdx.x;
   float* xr = x + m * xs;
   float v[kNormPer];
@@ -103,11 +137,14 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
   ss = block_sum_256(ss, red);
   const double den = sqrt(ss / (double)d + eps);
   uint16_t* yr = y + m * d;
+  uint16_t yb[kNormPer];
 #pragma unroll
   for (int i = 0; i < kNormPer; ++i) {
     const int j = threadIdx.x + 256 * i;
-    if (j < d) yr[j] = f64_to_bf16_rne((double)v[i] / den);
+    yb[i] = f64_to_bf16_rne((double)v[i] / den);
+    if (j < d) yr[j] = yb[i];
   }
+  if (yq != nullptr) quant_row_bf16<kNormPer>(yb, d, redf, yq + m * (d / 2), ys + m);  // uniform
 }
 
 // ------------------------------------------------------------------ RoPE + KV write
@@ -409,7 +446,15 @@ hipError_t launch_embed(const uint16_t* emb, int64_t V, int64_t d, const int32_t
 hipError_t launch_add_rmsnorm(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
                               int64_t d, double eps, uint16_t* y, hipStream_t s) {
   hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
-                     (int)d, eps, y);
+                     (int)d, eps, y, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_rmsnorm_quant(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
+                                    int64_t d, double eps, uint16_t* y, uint8_t* yq, float* ys,
+                                    hipStream_t s) {
+  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
+                     (int)d, eps, y, yq, ys);
   return hipGetLastError();
 }
 

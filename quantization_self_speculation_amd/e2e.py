@@ -112,12 +112,18 @@ class Decoder:
         self.stats = torch.zeros(3, dtype=torch.int64, device=dev)
 
     # ------------------------------------------------------------ one forward
-    def _linear(self, mode, X, W, Y, variant):
+    def _codes(self, M, K):
+        return _view(self.Xq, M, K // 2), _view(self.Xs, M)
+
+    def _linear(self, mode, X, W, Y, variant, coded=False):
+        """coded: the producer of X already wrote its 4-bit codes into the
+        code buffers (draft mode)."""
         Wq, Ws, N, K = W
         M = X.shape[0]
         if mode == DRAFT:
-            Xq, Xs = _view(self.Xq, M, K // 2), _view(self.Xs, M)
-            b.quant_act(X, Xq, Xs)
+            Xq, Xs = self._codes(M, K)
+            if not coded:
+                b.quant_act(X, Xq, Xs)
             b.gemm_w4a4(Xq, Xs, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
         else:
             b.gemm_w4a16(X, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
@@ -131,19 +137,29 @@ class Decoder:
         d, F = cfg.d, cfg.ffn
         qd = cfg.n_heads * cfg.head_dim
         qkv_rows = qd + 2 * cfg.n_kv * cfg.head_dim
-        def lin(li, name, X, W, Y):
-            self._linear(mode, X, W, Y, variant)
+        def lin(li, name, X, W, Y, coded=False):
+            self._linear(mode, X, W, Y, variant, coded)
             if trace is not None:
                 trace.append((li, name, X.clone(), Y.clone()))
+
+        # in draft mode the RMSNorm kernel also writes the drafter's 4-bit
+        # codes of its bf16 output (one launch, not two)
+        draft = mode == DRAFT
+
+        def norm(x_, add_, h_):
+            if draft:
+                b.add_rmsnorm_quant(x_, add_, h_, *self._codes(h_.shape[0], d), cfg.eps)
+            else:
+                b.add_rmsnorm(x_, add_, h_, cfg.eps)
 
         x = _view(self.x, M, d)
         b.embed(self.emb, self.tok[:M], x)
         add = None
         for li, L in enumerate(self.layers):
             h = _view(self.h, M, d)
-            b.add_rmsnorm(x, add, h, cfg.eps)
+            norm(x, add, h)
             qkv = _view(self.qkv, M, qkv_rows)
-            lin(li, "qkv", h, L["qkv"], qkv)
+            lin(li, "qkv", h, L["qkv"], qkv, coded=draft)
             q = _view(self.q, M, qd)
             b.rope_kv(qkv, self.seq, self.pos, q, self.kc[li], self.vc[li], cfg.n_heads,
                       cfg.n_kv, cfg.rope_base)
@@ -152,9 +168,9 @@ class Decoder:
                         cfg.n_kv)
             o = _view(self.o, M, d)
             lin(li, "o", att, L["o"], o)
-            b.add_rmsnorm(x, o, h, cfg.eps)
+            norm(x, o, h)
             gu = _view(self.gu, M, 2 * F)
-            lin(li, "gu", h, L["gu"], gu)
+            lin(li, "gu", h, L["gu"], gu, coded=draft)
             a = _view(self.a, M, F)
             b.silu_mul(gu, a)
             dn = _view(self.dn, M, d)
@@ -166,9 +182,9 @@ class Decoder:
             rows = M // last_of
             xs, adds = x[last_of - 1::last_of], add[last_of - 1::last_of]
         hf = _view(self.h, rows, d)
-        b.add_rmsnorm(xs, adds, hf, cfg.eps)
+        norm(xs, adds, hf)
         logits = _view(self.logits, rows, cfg.vocab)
-        lin(len(self.layers), "lm", hf, self.lm, logits)
+        lin(len(self.layers), "lm", hf, self.lm, logits, coded=draft)
         return logits
 
     # ------------------------------------------------------------ phases

@@ -167,6 +167,10 @@ def test_harness_validation():
     assert L.qspec_attention(A, A, A, 4, 8, 4, A, A, 2, 0, A, S) == ESHAPE
     assert L.qspec_attention(A, A, A, 4, 8, 3, A, A, 2, 64, A, S) == ESHAPE
     assert L.qspec_attention(A, A, A, 4, 8, 4, NUL, A, 2, 64, A, S) == ENULL
+    # the RMSNorm with the drafter's codes: d a multiple of 128, code buffers aligned
+    assert L.qspec_add_rmsnorm_quant(A, 200, NUL, 0, 2, 200, D(1e-6), A, A, A, S) == ESHAPE
+    assert L.qspec_add_rmsnorm_quant(A, 256, NUL, 0, 2, 256, D(1e-6), A, NUL, A, S) == ENULL
+    assert L.qspec_add_rmsnorm_quant(A, 256, NUL, 0, 2, 256, D(1e-6), A, A, MIS, S) == EALIGN
     # silu, argmax
     assert L.qspec_silu_mul(A, 0, 10, A, S) == ESHAPE
     assert L.qspec_argmax(A, 2, 10, A, 0, S) == ESHAPE

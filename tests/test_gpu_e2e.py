@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import oracle.model as om
 import synth
 import quantization_self_speculation_amd as q
@@ -116,6 +117,34 @@ def test_silu_mul_and_argmax():
     assert np.array_equal(got[0::2], om.argmax_first(x))
     assert np.all(got[1::2] == -7)
     assert got[2] == 10 and got[4] == 0 and got[6] == V - 1 and got[8] == 0 and got[10] == 777
+
+
+@pytest.mark.parametrize("M,d", [(9, 256), (37, 2048), (3, 4096)])
+def test_quantizer_fused_into_rmsnorm(M, d):
+    """add_rmsnorm_quant: the bf16 output and the residual are bitwise those
+    of add_rmsnorm, and the 4-bit codes and scales bitwise those of quant_act
+    on the bf16 rows -- and of the oracle's quantizer on them (with and
+    without the residual add, row-strided x)."""
+    say(f"fused quantizer M={M} d={d}")
+    rng = synth.make_rng(56)
+    big = torch.from_numpy(rng.standard_normal((M, d + 128)).astype(np.float32)).to("cuda:0")
+    add = torch.from_numpy(rng.standard_normal((M, d)).astype(np.float32)).to("cuda:0")
+    for a_ in (None, add):
+        x1 = big.clone()[:, :d]
+        x2 = big.clone()[:, :d]
+        y1 = torch.empty((M, d), dtype=torch.bfloat16, device="cuda:0")
+        y2 = torch.empty_like(y1)
+        yq = torch.empty((M, d // 2), dtype=torch.uint8, device="cuda:0")
+        ys = torch.empty((M,), dtype=torch.float32, device="cuda:0")
+        qb.add_rmsnorm(x1, a_, y1, 1e-6)
+        qb.add_rmsnorm_quant(x2, a_, y2, yq, ys, 1e-6)
+        q1, s1 = q.quant_act(y1)
+        assert np.array_equal(host_bits16(y1), host_bits16(y2))
+        assert np.array_equal(host(x1).view(np.uint32), host(x2).view(np.uint32))
+        assert np.array_equal(host(yq), host(q1))
+        assert np.array_equal(host(ys).view(np.uint32), host(s1).view(np.uint32))
+        qo, so = oracle.quant_act(host_bits16(y2))
+        assert np.array_equal(host(yq), qo) and np.array_equal(host(ys), so)
 
 
 def test_spec_prepare_and_commit():
