@@ -527,31 +527,46 @@ def test_graph_replays_match_eager():
     Y16 = torch.empty((M16, N), dtype=torch.float32, device="cuda")
     ws4 = torch.empty(q.workspace_bytes(1, M4, N, K), dtype=torch.uint8, device="cuda")
     ws16 = torch.empty(q.workspace_bytes(2, M16, N, K), dtype=torch.uint8, device="cuda")
+    # the W4A8 tier and the bf16 output on the same split-K shape, each with
+    # a workspace of its own
+    X8q, X8s = q.quant_act8(X4)
+    Y8 = torch.empty((M4, N), dtype=torch.float32, device="cuda")
+    Yb = torch.empty((M4, N), dtype=torch.bfloat16, device="cuda")
+    ws8 = torch.empty(q.workspace_bytes(4, M4, N, K), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(q.workspace_bytes(1, M4, N, K), dtype=torch.uint8, device="cuda")
 
     def body():
         q.quant_act(X4, Xq, Xs)
         q.gemm_w4a4(Xq, Xs, Wq_d, Ws_d, Y=Y4, ws=ws4, N=N)
         q.gemm_w4a16(X_d, Wq_d, Ws_d, Y=Y16, ws=ws16, N=N)
+        q.quant_act8(X4, X8q, X8s)
+        q.gemm_w4a8(X8q, X8s, Wq_d, Ws_d, Y=Y8, ws=ws8, N=N)
+        q.gemm_w4a4_bf16(Xq, Xs, Wq_d, Ws_d, variant=q.GEMM_SKINNY, Y=Yb, ws=wsb, N=N)
 
     body()
     torch.cuda.synchronize()
     e4, e16 = host(Y4).copy(), host(Y16).copy()
+    e8, eb = host(Y8).copy(), host_bits16(Yb).copy()
     assert_close(e16, oracle.gemm_w4a16(X, Wq, Ws))
+    assert_close(e8, oracle.gemm_w4a8(*oracle.quant_act8(X[:M4]), Wq, Ws), what="w4a8")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         body()
     for rep in range(3):
-        Y4.zero_()
-        Y16.zero_()
+        for t in (Y4, Y16, Y8, Yb):
+            t.zero_()
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(Y4).view(np.uint32), e4.view(np.uint32)), rep
         assert np.array_equal(host(Y16).view(np.uint32), e16.view(np.uint32)), rep
+        assert np.array_equal(host(Y8).view(np.uint32), e8.view(np.uint32)), rep
+        assert np.array_equal(host_bits16(Yb), eb), rep
         body()                                   # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(host(Y16).view(np.uint32), e16.view(np.uint32)), rep
+        assert np.array_equal(host(Y8).view(np.uint32), e8.view(np.uint32)), rep
 
 
 def test_fresh_garbage_workspace():
