@@ -327,8 +327,9 @@ def measure_rotation(torch, q, wl, reps=20):
 
 def measure_w4a8_tier(torch, q, wl, reps=10):
     """The W4A8 middle tier on the shared buffer at the draft batch (M = 8):
-    per projection the time of quantizer + GEMM against W4A4 and W4A16 (each
-    replay reads another weight copy), and on the QKV shape with x20 outlier
+    per projection the time of quantizer + GEMM against W4A4 and W4A16, all
+    three in the AUTO family (each replay reads another weight copy), and on
+    the QKV shape with x20 outlier
     channels each layer's relative error against the exact product
     (512 sampled output columns computed exactly on the host)."""
     import synth
@@ -348,7 +349,7 @@ def measure_w4a8_tier(torch, q, wl, reps=10):
 
         def f4():
             for Wq, Ws in cps:
-                q.gemm_w4a4(*q.quant_act(X8, *q4), Wq, Ws, variant=q.GEMM_SKINNY, Y=Y, ws=ws)
+                q.gemm_w4a4(*q.quant_act(X8, *q4), Wq, Ws, Y=Y, ws=ws)
 
         def f8():
             for Wq, Ws in cps:
@@ -356,7 +357,7 @@ def measure_w4a8_tier(torch, q, wl, reps=10):
 
         def f16():
             for Wq, Ws in cps:
-                q.gemm_w4a16(X8, Wq, Ws, variant=q.GEMM_SKINNY, Y=Y, ws=ws)
+                q.gemm_w4a16(X8, Wq, Ws, Y=Y, ws=ws)
         t = [_graph_time(torch, f, reps, launches=1) / len(cps) for f in (f4, f8, f16)]
         out["times_us"][p["name"]] = {"w4a4": round(t[0], 2), "w4a8": round(t[1], 2),
                                       "w4a16": round(t[2], 2)}

@@ -224,9 +224,10 @@ qspec_status qspec_gemm_w4a4_bf16(const uint8_t* Xq, const float* Xs,
  *   X [M][K] bf16 bits; Xq [M][K] int8 (out); Xs [M] fp32 (out).
  * qspec_gemm_w4a8 -- Y[m,n] = Xs[m] * sum_g float(Ws[n,g]) * P[m,n,g] with
  *   P the exact int32 group partial of the 8-bit codes and the 4-bit
- *   weights, computed with int8 MFMA; the SKINNY family at every M (variant
- *   AUTO or SKINNY, anything else QSPEC_ERR_UNSUPPORTED); a row's result does
- *   not depend on M.  Wq/Ws as for qspec_gemm_w4a4; Y [M][N] fp32 (out);
+ *   weights, computed with int8 MFMA; variant AUTO (STREAM where W4A4's AUTO
+ *   takes it, else SKINNY), SKINNY or STREAM (M <= 16); GEMV and TILED give
+ *   QSPEC_ERR_UNSUPPORTED.  Within one family a row's result does not depend
+ *   on M.  Wq/Ws as for qspec_gemm_w4a4; Y [M][N] fp32 (out);
  *   ws/ws_bytes: qspec_workspace_bytes(QSPEC_OP_GEMM_W4A8, M, N, K) bytes
  *   (the W4A4 size).  Validation and errors as for qspec_gemm_w4a4.
  * ------------------------------------------------------------------------- */

@@ -292,8 +292,10 @@ qspec_status qspec_gemm_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* W
                              int variant, float* Y, void* ws, size_t ws_bytes,
                              qspec_stream stream) {
   QS_TRY(check_gemm(M, N, K, group, variant, false));
-  QS_REQUIRE(variant == QSPEC_GEMM_AUTO || variant == QSPEC_GEMM_SKINNY, QSPEC_ERR_UNSUPPORTED,
-             "W4A8 runs the SKINNY family (variant AUTO or SKINNY, got %d)", variant);
+  QS_REQUIRE(variant == QSPEC_GEMM_AUTO || variant == QSPEC_GEMM_SKINNY ||
+                 variant == QSPEC_GEMM_STREAM,
+             QSPEC_ERR_UNSUPPORTED, "W4A8 runs the SKINNY or STREAM family (got variant %d)",
+             variant);
   QS_PTR(Xq);
   QS_PTR(Xs);
   QS_PTR(Wq);

@@ -1,6 +1,6 @@
 // The dual-mode linear layer: W4A16 (verifier) and W4A4 (drafter) GEMMs over
 // the one shared packed INT4 weight buffer, and a W4A8 middle tier on the
-// same buffer (8-bit activation codes, the skinny family only).
+// same buffer (8-bit activation codes; the skinny and stream families).
 //
 // Pages: "QSpec: Speculative Decoding with Complementary Quantization
 // Schemes", Abstract (arXiv) -- low-precision joint quantization (W4A4) for
@@ -147,6 +147,17 @@ __device__ __forceinline__ v4i as_v4i(uint32_t a, uint32_t b, uint32_t c, uint32
   return t;
 }
 
+// 16 8-bit codes k0 .. k15 (natural order) -> the order the widened 4-bit
+// codes take in an MFMA operand (even k of each 8, then odd k), so 8-bit
+// activations meet the weights' lo/hi widening in the same k order
+__device__ __forceinline__ uint4 i8x16_to_widened_order(const uint4 p) {
+  return make_uint4(
+      (p.x & 0xFFu) | ((p.x >> 8) & 0xFF00u) | ((p.y & 0xFFu) << 16) | ((p.y << 8) & 0xFF000000u),
+      ((p.x >> 8) & 0xFFu) | ((p.x >> 16) & 0xFF00u) | ((p.y << 8) & 0xFF0000u) | (p.y & 0xFF000000u),
+      (p.z & 0xFFu) | ((p.z >> 8) & 0xFF00u) | ((p.w & 0xFFu) << 16) | ((p.w << 8) & 0xFF000000u),
+      ((p.z >> 8) & 0xFFu) | ((p.z >> 16) & 0xFF00u) | ((p.w << 8) & 0xFF0000u) | (p.w & 0xFF000000u));
+}
+
 // Sum of a 128-element activation group held as 16 chunks of 8 by 16
 // consecutive lanes (aligned to 16): fixed butterfly, identical bits in all
 // 16 lanes and in every kernel that calls it.
@@ -175,7 +186,7 @@ __device__ __forceinline__ float group_sum16(float v) {
 //     when blocks go round-robin to the 8 XCDs (a locality hint only: the
 //     hand-off of partials is correct on any placement).
 // ============================================================================
-enum { kW4A16 = 0, kW4A4 = 1, kW4A8 = 2 };  // W4A8: skinny family only
+enum { kW4A16 = 0, kW4A4 = 1, kW4A8 = 2 };  // W4A8: skinny and stream families
 
 struct SkinnyArgs {
   const void* X;            // W4A16: bf16 [M][K]; W4A4: packed codes [M][K/2]; W4A8: int8 [M][K]
@@ -407,13 +418,8 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
         if (idx >= XCH) continue;
         const int r = idx / (CH * 8), cc = idx % (CH * 8);
         if (r >= mrows) continue;
-        const uint4 p = xr[i];
-        const uint4 o = make_uint4(
-            (p.x & 0xFFu) | ((p.x >> 8) & 0xFF00u) | ((p.y & 0xFFu) << 16) | ((p.y << 8) & 0xFF000000u),
-            ((p.x >> 8) & 0xFFu) | ((p.x >> 16) & 0xFF00u) | ((p.y << 8) & 0xFF0000u) | (p.y & 0xFF000000u),
-            (p.z & 0xFFu) | ((p.z >> 8) & 0xFF00u) | ((p.w & 0xFFu) << 16) | ((p.w << 8) & 0xFF000000u),
-            ((p.z >> 8) & 0xFFu) | ((p.z >> 16) & 0xFF00u) | ((p.w << 8) & 0xFF0000u) | (p.w & 0xFF000000u));
-        *reinterpret_cast<uint4*>(&xs[buf][r * XSTB + (cc >> 3) * 128 + (cc & 7) * 16]) = o;
+        *reinterpret_cast<uint4*>(&xs[buf][r * XSTB + (cc >> 3) * 128 + (cc & 7) * 16]) =
+            i8x16_to_widened_order(xr[i]);
       } else if (idx < XCH) {
         const int r = idx / (CH * 4), cc = idx % (CH * 4);
         if (r >= mrows) continue;
@@ -1147,7 +1153,7 @@ hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const
 }
 
 // ============================================================================
-// "Stream" family (both modes, M <= 16): the decode shapes, HBM-bound.
+// "Stream" family (all three modes, M <= 16): the decode shapes, HBM-bound.
 //   * a workgroup = nw wavefronts on ONE 16-row weight block; wavefront w
 //     takes groups w, w + nw, w + 2 nw, ... (dealt round-robin: at each step
 //     the workgroup reads nw adjacent tiles), so the k-split is reduced inside
@@ -1165,8 +1171,8 @@ hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const
 //   duplicates whose outputs are not stored).
 // ============================================================================
 struct StreamArgs {
-  const void* X;    // W4A16: bf16 [M][K]; W4A4: packed codes [M][K/2]
-  const float* Xs;  // W4A4: [M]
+  const void* X;    // W4A16: bf16 [M][K]; W4A4: packed codes [M][K/2]; W4A8: int8 [M][K]
+  const float* Xs;  // W4A4 / W4A8: [M]
   const uint8_t* Wq;
   const uint16_t* Ws;
   float* Y;
@@ -1195,8 +1201,9 @@ template <int MODE>
 struct StreamStage {
   uint4 w;
   uint2 s;
-  uint4 x[MODE == kW4A16 ? 4 : 1];
+  uint4 x[MODE == kW4A16 ? 4 : MODE == kW4A8 ? 2 : 1];
 };
+
 
 template <int MODE>
 __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
@@ -1218,12 +1225,14 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   const uint16_t* sc = a.Ws + (int64_t)rb * G * 16 + lg * 4;
   // activation rows through a buffer resource: lanes of rows >= M read an
   // out-of-range offset, which returns zeros without a memory access
-  const int xrow_bytes = MODE == kW4A16 ? K * 2 : K / 2;
+  const int xrow_bytes = MODE == kW4A16 ? K * 2 : MODE == kW4A8 ? K : K / 2;
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(a.X), (short)0, M * xrow_bytes, 0x00020000);
   const uint32_t xoff0 = (l16 < M ? (uint32_t)(l16 * xrow_bytes) : 0x80000000u) +
-                         (uint32_t)(lg * (MODE == kW4A16 ? 64 : 16));
-  constexpr int xgb = MODE == kW4A16 ? kGroup * 2 : kGroup / 2;  // activation bytes per group
+                         (uint32_t)(lg * (MODE == kW4A16 ? 64 : MODE == kW4A8 ? 32 : 16));
+  // activation bytes per group
+  constexpr int xgb = MODE == kW4A16 ? kGroup * 2 : MODE == kW4A8 ? kGroup : kGroup / 2;
+  constexpr int nxl = MODE == kW4A16 ? 4 : MODE == kW4A8 ? 2 : 1;  // 16-byte loads per stage
 
   auto load = [&](StreamStage<MODE>& st, int g) {
     const int gg = min(w + nw * min(g, gl), G - 1);
@@ -1231,7 +1240,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
     st.s = *reinterpret_cast<const uint2*>(sc + (int64_t)gg * 16);
     const uint32_t o = xoff0 + (uint32_t)(gg * xgb);
 #pragma unroll
-    for (int i = 0; i < (MODE == kW4A16 ? 4 : 1); ++i) {
+    for (int i = 0; i < nxl; ++i) {
       const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, o + 16 * i, 0, 0);
       st.x[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
@@ -1271,17 +1280,29 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
       tot[2] = fmaf(half_bits_to_float((uint16_t)(s23 & 0xFFFF)), acc[2], tot[2]);
       tot[3] = fmaf(half_bits_to_float((uint16_t)(s23 >> 16)), acc[3], tot[3]);
     } else {
-      const uint4 p = st.w, x = st.x[0];
+      const uint4 p = st.w;
       const v4i a0 = {(int)w4_lo_x16(p.x), (int)w4_hi_x16(p.x), (int)w4_lo_x16(p.y), (int)w4_hi_x16(p.y)};
       const v4i a1 = {(int)w4_lo_x16(p.z), (int)w4_hi_x16(p.z), (int)w4_lo_x16(p.w), (int)w4_hi_x16(p.w)};
-      const v4i b0 = {(int)w4_lo_x16(x.x), (int)w4_hi_x16(x.x), (int)w4_lo_x16(x.y), (int)w4_hi_x16(x.y)};
-      const v4i b1 = {(int)w4_lo_x16(x.z), (int)w4_hi_x16(x.z), (int)w4_lo_x16(x.w), (int)w4_hi_x16(x.w)};
+      v4i b0, b1;
+      if (MODE == kW4A8) {
+        const uint4 x0 = i8x16_to_widened_order(st.x[0]);
+        const uint4 x1 = i8x16_to_widened_order(st.x[nxl - 1]);
+        b0 = as_v4i(x0.x, x0.y, x0.z, x0.w);
+        b1 = as_v4i(x1.x, x1.y, x1.z, x1.w);
+      } else {
+        const uint4 x = st.x[0];
+        b0 = as_v4i(w4_lo_x16(x.x), w4_hi_x16(x.x), w4_lo_x16(x.y), w4_hi_x16(x.y));
+        b1 = as_v4i(w4_lo_x16(x.z), w4_hi_x16(x.z), w4_lo_x16(x.w), w4_hi_x16(x.w));
+      }
       v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
-      tot[0] = fmaf(half_bits_to_float((uint16_t)(s01 & 0xFFFF)) * 0.00390625f, (float)acc[0], tot[0]);
-      tot[1] = fmaf(half_bits_to_float((uint16_t)(s01 >> 16)) * 0.00390625f, (float)acc[1], tot[1]);
-      tot[2] = fmaf(half_bits_to_float((uint16_t)(s23 & 0xFFFF)) * 0.00390625f, (float)acc[2], tot[2]);
-      tot[3] = fmaf(half_bits_to_float((uint16_t)(s23 >> 16)) * 0.00390625f, (float)acc[3], tot[3]);
+      // / 256 when both operands carry the x16 of the widening, / 16 for
+      // 8-bit activation codes
+      constexpr float f = MODE == kW4A8 ? 0.0625f : 0.00390625f;
+      tot[0] = fmaf(half_bits_to_float((uint16_t)(s01 & 0xFFFF)) * f, (float)acc[0], tot[0]);
+      tot[1] = fmaf(half_bits_to_float((uint16_t)(s01 >> 16)) * f, (float)acc[1], tot[1]);
+      tot[2] = fmaf(half_bits_to_float((uint16_t)(s23 & 0xFFFF)) * f, (float)acc[2], tot[2]);
+      tot[3] = fmaf(half_bits_to_float((uint16_t)(s23 >> 16)) * f, (float)acc[3], tot[3]);
     }
   };
   // Full rounds of PD groups carry no condition, so the compiler keeps every
@@ -1322,7 +1343,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   const int N = a.N;
   if (n >= N) return;
   float xs = 1.f;
-  if (MODE == kW4A4) xs = a.Xs[l16];
+  if (MODE != kW4A16) xs = a.Xs[l16];
   const float v[4] = {xs * tot[0], xs * tot[1], xs * tot[2], xs * tot[3]};
   out_store4(a.Y, a.Yb, (int64_t)l16 * N + n, v, N - n, (N & 3) == 0);
 }
@@ -1716,12 +1737,15 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
   return launch_skinny<kW4A4>(a, p, s);
 }
 
-// W4A8: the skinny family at every M, on the W4A4 plan (same k-split, same
-// workspace); AUTO and SKINNY are the accepted variants.
+// W4A8: the stream family where AUTO picks it for W4A4 (M <= 16, N < 16384)
+// or on request, else the skinny family, on the W4A4 plan (same k-split,
+// same workspace); AUTO, SKINNY and STREAM are the accepted variants.
 hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, void* ws,
                        hipStream_t s) {
-  (void)variant;
+  const int v = variant == QSPEC_GEMM_AUTO ? auto_pick(M, N, K, 256, 64) : variant;
+  if (v == QSPEC_GEMM_STREAM)
+    return launch_stream<kW4A8>(Xq, Xs, Wq, Ws, M, N, K, Y, nullptr, s);
   const SkinnyPlan p = plan_skinny(1, M, N, K);
   SkinnyArgs a{};
   a.X = Xq;

@@ -94,8 +94,9 @@ def test_gemm_validation():
     assert need > 0
     assert g(A, A, A, 40, 4608, 3584, 128, 2, A, NUL, 0, S) == EWS
     assert g(A, A, A, 40, 4608, 3584, 128, 2, A, A, need - 1, S) == EWS
-    u = L.qspec_gemm_w4a8        # the W4A8 tier: SKINNY family only
-    for v in (1, 3, 4, 9):
+    u = L.qspec_gemm_w4a8        # the W4A8 tier: SKINNY and STREAM families
+    assert u(A, A, A, A, 17, 64, 256, 128, 4, A, NUL, 0, S) == EUNSUP   # STREAM: M <= 16
+    for v in (1, 3, 9):
         assert u(A, A, A, A, 8, 64, 256, 128, v, A, NUL, 0, S) == EUNSUP
     assert u(A, A, A, A, 8, 64, 250, 128, 0, A, NUL, 0, S) == ESHAPE
     assert u(NUL, A, A, A, 8, 64, 256, 128, 0, A, NUL, 0, S) == ENULL

@@ -1,5 +1,5 @@
-"""GPU parity of the W4A8 middle tier (qspec_quant_act8, qspec_gemm_w4a8)
-against the oracle (oracle/w4a8.py), through the C ABI: the 8-bit codes and
+"""GPU parity of the W4A8 middle tier (qspec_quant_act8, qspec_gemm_w4a8;
+SKINNY and STREAM families) against the oracle (oracle/w4a8.py), through the C ABI: the 8-bit codes and
 scales bit-exact in every row-length band of the quantizer's launch, Y
 within 2e-3 * max|y| on ragged shapes with and without a k-split, rows
 bitwise independent of M, and the lossless case where W4A8 meets W4A16."""
@@ -61,8 +61,10 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
-@pytest.mark.parametrize("variant", [q.GEMM_AUTO, q.GEMM_SKINNY])
+@pytest.mark.parametrize("variant", [q.GEMM_AUTO, q.GEMM_SKINNY, q.GEMM_STREAM])
 def test_gemm_w4a8_parity(M, N, K, variant):
+    if variant == q.GEMM_STREAM and M > 16:
+        pytest.skip("the STREAM family takes M <= 16")
     say(f"gemm_w4a8 M={M} N={N} K={K} variant={variant}")
     W, X = _case(132, M, N, K)
     Wq, Ws = oracle.pack_w4(W)
@@ -72,15 +74,23 @@ def test_gemm_w4a8_parity(M, N, K, variant):
 
 
 def test_gemm_w4a8_row_invariance():
+    """Within a family rows are bitwise independent of M: SKINNY at M = 80 and
+    its subsets, STREAM at M = 16 and its subsets."""
     N, K = 3584, 18944
     W, X = _case(133, 80, N, K)
     Wq, Ws = oracle.pack_w4(W)
     qa, s = oracle.quant_act8(X)
     args = (dev_w(Wq), dev_s(Ws))
-    Y80 = host(q.gemm_w4a8(dev(qa), dev(s), *args, N=N))
+    SK, ST = q.GEMM_SKINNY, q.GEMM_STREAM
+    Y80 = host(q.gemm_w4a8(dev(qa), dev(s), *args, variant=SK, N=N))
     for lo, hi in ((0, 16), (16, 24), (41, 42), (79, 80)):
-        Y = host(q.gemm_w4a8(dev(qa[lo:hi].copy()), dev(s[lo:hi].copy()), *args, N=N))
+        Y = host(q.gemm_w4a8(dev(qa[lo:hi].copy()), dev(s[lo:hi].copy()), *args, variant=SK, N=N))
         assert np.array_equal(Y80[lo:hi].view(np.uint32), Y.view(np.uint32)), (lo, hi)
+    Y16 = host(q.gemm_w4a8(dev(qa[:16].copy()), dev(s[:16].copy()), *args, variant=ST, N=N))
+    for lo, hi in ((0, 5), (9, 10), (15, 16)):
+        Y = host(q.gemm_w4a8(dev(qa[lo:hi].copy()), dev(s[lo:hi].copy()), *args, variant=ST, N=N))
+        assert np.array_equal(Y16[lo:hi].view(np.uint32), Y.view(np.uint32)), (lo, hi)
+    assert_close(Y16, oracle.gemm_w4a8(qa[:16], s[:16], Wq, Ws), what="w4a8 stream")
 
 
 def test_gemm_w4a8_lossless_meets_w4a16():
@@ -106,6 +116,6 @@ def test_gemm_w4a8_rejects_other_families():
     W, X = _case(135, 8, 64, 256)
     Wq, Ws = oracle.pack_w4(W)
     qa, s = oracle.quant_act8(X)
-    for v in (q.GEMM_GEMV, q.GEMM_TILED, q.GEMM_STREAM):
+    for v in (q.GEMM_GEMV, q.GEMM_TILED):
         with pytest.raises(QSpecError):
             q.gemm_w4a8(dev(qa), dev(s), dev_w(Wq), dev_s(Ws), variant=v, N=64)
