@@ -353,6 +353,17 @@ hipError_t launch_pack_w4(const float* W, int64_t N, int64_t K, uint8_t* Wq, uin
   return hipGetLastError();
 }
 
+// launch shape of the short-row band (threads x 16-byte chunks per thread,
+// at least 512 chunks) and the threads of the <= 4096-chunk band
+#ifndef QSPEC_QA_SNT
+#define QSPEC_QA_SNT 256
+#endif
+#ifndef QSPEC_QA_SNC
+#define QSPEC_QA_SNC 2
+#endif
+#ifndef QSPEC_QA_MNT
+#define QSPEC_QA_MNT 1024
+#endif
 template <int BITS>
 hipError_t launch_quant_act_bits(const uint16_t* X, int64_t M, int64_t K, uint8_t* Xq, float* Xs,
                                  hipStream_t s) {
@@ -360,12 +371,14 @@ hipError_t launch_quant_act_bits(const uint16_t* X, int64_t M, int64_t K, uint8_
   // short latency chain (load, block max, code) is what a decode row costs
   const int64_t nch = K / 8;  // 16-byte chunks of a row
   const dim3 g((unsigned)M);
-  if (nch <= 512) {
-    hipLaunchKernelGGL((quant_act_kernel<256, 2, BITS>), g, dim3(256), 0, s, X, K, Xq, Xs);
+  if (nch <= QSPEC_QA_SNT * QSPEC_QA_SNC) {
+    hipLaunchKernelGGL((quant_act_kernel<QSPEC_QA_SNT, QSPEC_QA_SNC, BITS>), g, dim3(QSPEC_QA_SNT), 0,
+                       s, X, K, Xq, Xs);
   } else if (nch <= 2048) {
     hipLaunchKernelGGL((quant_act_kernel<1024, 2, BITS>), g, dim3(1024), 0, s, X, K, Xq, Xs);
   } else if (nch <= 4096) {
-    hipLaunchKernelGGL((quant_act_kernel<1024, 4, BITS>), g, dim3(1024), 0, s, X, K, Xq, Xs);
+    hipLaunchKernelGGL((quant_act_kernel<QSPEC_QA_MNT, 4096 / QSPEC_QA_MNT, BITS>), g,
+                       dim3(QSPEC_QA_MNT), 0, s, X, K, Xq, Xs);
   } else if (nch <= 8192) {
     hipLaunchKernelGGL((quant_act_kernel<1024, 8, BITS>), g, dim3(1024), 0, s, X, K, Xq, Xs);
   } else {
