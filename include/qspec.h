@@ -71,9 +71,11 @@ enum { QSPEC_VERIFY_GREEDY = 0, QSPEC_VERIFY_SAMPLE = 1 };
  * token) passes the same explicit family for every M.  AUTO picks by M, N
  * and K: STREAM for M <= 16 when N < 16384 (where SKINNY would have too few
  * workgroups to fill the GPU), else SKINNY up to M = 128 (W4A16) or
- * M = 256 (W4A4), TILED beyond -- except that up to M = 512 SKINNY stays
- * when K has at least 64 groups and TILED would have fewer than 128 tiles
- * (32 x 256 for W4A16, 64 x 256 for W4A4). */
+ * M = 256 (W4A4), TILED beyond -- except that TILED is taken from M = 64
+ * (W4A16) or M = 96 (W4A4) when its grid has at least 256 tiles (32 x 256
+ * for W4A16, 64 x 256 for W4A4), and that up to M = 512 SKINNY stays when K
+ * has at least 64 groups and TILED would have fewer than 128 tiles.  The
+ * W4A8 tier follows the same rule but runs SKINNY wherever it says TILED. */
 enum {
   QSPEC_GEMM_AUTO = 0,
   QSPEC_GEMM_GEMV = 1,   /* W4A16 only: VALU GEMV with wavefront reduction   */

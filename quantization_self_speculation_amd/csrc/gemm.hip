@@ -1630,18 +1630,26 @@ GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K / kGroup, kGemvGroup
 // the tiled kernel walks it on few workgroups (measured on the Qwen2.5-7B
 // and Llama-3-8B down projections at M = 160 ... 512: W4A16 at M = 160
 // 83 / 74 us against 129 / 98 us, W4A4 at M = 288 79 / 76 us against
-// 123 / 95 us).  The choice depends on M, N and K only.
-int auto_pick(int64_t M, int64_t N, int64_t K, int64_t skinny_max, int64_t bm) {
+// 123 / 95 us).  Below the skinny limit the tiled family takes over from
+// tiled_min rows when its grid fills the chip (at least 256 tiles): on the
+// gate|up projection (N = 37888) W4A16 at M = 64 / 96 / 128 runs 45 / 45 /
+// 65 us tiled against 52 / 78 / 80 us skinny, W4A4 at M = 96 / 128 40 / 42
+// against 46 / 48 us, while at M = 40 the skinny family is ahead (32 against
+// 44 us).  The choice depends on M, N and K only.
+int auto_pick(int64_t M, int64_t N, int64_t K, int64_t skinny_max, int64_t bm,
+              int64_t tiled_min) {
   if (M <= kStreamMaxM && cdiv(N, 64) < QSPEC_SK_TARGET_WG) return QSPEC_GEMM_STREAM;
-  if (M <= skinny_max) return QSPEC_GEMM_SKINNY;
-  if (M <= 512 && K / kGroup >= 64 && cdiv(N, 256) * cdiv(M, bm) < 128) return QSPEC_GEMM_SKINNY;
+  const int64_t tiles = cdiv(N, 256) * cdiv(M, bm);
+  if (M <= skinny_max)
+    return (M >= tiled_min && tiles >= 256) ? QSPEC_GEMM_TILED : QSPEC_GEMM_SKINNY;
+  if (M <= 512 && K / kGroup >= 64 && tiles < 128) return QSPEC_GEMM_SKINNY;
   return QSPEC_GEMM_TILED;
 }
 int w4a16_pick(int variant, int64_t M, int64_t N, int64_t K) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 128, 32);
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 128, 32, 64);
 }
 int w4a4_pick(int variant, int64_t M, int64_t N, int64_t K) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 256, 64);
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 256, 64, 96);
 }
 
 hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* Xs, float* Y,
@@ -1743,7 +1751,7 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
 hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, void* ws,
                        hipStream_t s) {
-  const int v = variant == QSPEC_GEMM_AUTO ? auto_pick(M, N, K, 256, 64) : variant;
+  const int v = variant == QSPEC_GEMM_AUTO ? auto_pick(M, N, K, 256, 64, 96) : variant;
   if (v == QSPEC_GEMM_STREAM)
     return launch_stream<kW4A8>(Xq, Xs, Wq, Ws, M, N, K, Y, nullptr, s);
   const SkinnyPlan p = plan_skinny(1, M, N, K);

@@ -338,24 +338,31 @@ def test_w4a4_bf16_output(M, N, K, variant):
     assert np.all(err <= 2e-3 * np.abs(want).max() + 2.0 ** -9 * np.abs(want) + 1e-30)
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 1000, 8192), (200, 1000, 8192), (300, 1000, 1024)])
-def test_auto_beyond_the_skinny_limit(M, N, K):
-    """AUTO between the SKINNY limit and 512 rows: with a long K (>= 64 groups)
-    and a small tiled grid it keeps the SKINNY family (the first two shapes:
-    bitwise the SKINNY result), otherwise TILED (the third: bitwise the TILED
-    result); either way within tolerance of the oracle."""
-    say(f"auto beyond the skinny limit M={M} N={N} K={K}")
+SK, TI = q.GEMM_SKINNY, q.GEMM_TILED
+
+
+@pytest.mark.parametrize("M,N,K,fam16,fam4", [
+    (300, 1000, 8192, SK, SK),    # long K, small tiled grid: SKINNY beyond the limit
+    (200, 1000, 8192, SK, SK),
+    (300, 1000, 1024, TI, TI),    # short K: TILED beyond the limit
+    (96, 37888, 1024, TI, TI),    # wide N: TILED below the limit (>= 256 tiles)
+    (64, 37888, 1024, TI, SK),    # W4A4 takes TILED only from 96 rows
+    (40, 37888, 1024, SK, SK),    # the verify batch stays SKINNY
+])
+def test_auto_family_choice(M, N, K, fam16, fam4):
+    """AUTO names one family per (M, N, K): its result is bitwise that
+    family's, and within tolerance of the oracle, in both modes."""
+    say(f"auto family M={M} N={N} K={K}")
     W, X = _case(33, M, N, K)
     Wq, Ws = oracle.pack_w4(W)
     Xq, Xs = oracle.quant_act(X)
     a4 = (dev(Xq), dev(Xs), dev_w(Wq), dev_s(Ws))
-    fam = q.GEMM_SKINNY if K >= 8192 else q.GEMM_TILED
     y4 = host(q.gemm_w4a4(*a4, N=N))
-    assert np.array_equal(y4.view(np.uint32), host(q.gemm_w4a4(*a4, variant=fam, N=N)).view(np.uint32))
+    assert np.array_equal(y4.view(np.uint32), host(q.gemm_w4a4(*a4, variant=fam4, N=N)).view(np.uint32))
     assert_close(y4, oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4 auto")
     a16 = (dev_bf16(X), dev_w(Wq), dev_s(Ws))
     y16 = host(q.gemm_w4a16(*a16, N=N))
-    assert np.array_equal(y16.view(np.uint32), host(q.gemm_w4a16(*a16, variant=fam, N=N)).view(np.uint32))
+    assert np.array_equal(y16.view(np.uint32), host(q.gemm_w4a16(*a16, variant=fam16, N=N)).view(np.uint32))
     assert_close(y16, oracle.gemm_w4a16(X, Wq, Ws), what="w4a16 auto")
 
 
