@@ -29,8 +29,10 @@
  *    error nothing is launched and the status says why (qspec_last_error()
  *    gives a thread-local message).  A failed launch returns QSPEC_ERR_HIP.
  *    Faults inside a kernel surface at the caller's next synchronisation.
- *  - Calls never abort or exit the process.  They are thread-safe; the only
- *    global state is a per-device cache of the device check.
+ *  - Calls never abort or exit the process.  They are thread-safe.  Global
+ *    state: a per-device cache of the device check, a process-wide atomic
+ *    call counter that tags the split-K arrival counters in a GEMM's
+ *    workspace (so a workspace never needs clearing).
  *  - Non-finite inputs (NaN/Inf weights, activations or logits) are not
  *    supported: results are unspecified, but every kernel still terminates.
  */
@@ -117,15 +119,19 @@ size_t qspec_workspace_bytes(int op, int64_t a, int64_t b, int64_t c);
  *     a = max|W[n,k]|;  s = fp16(a / 7.0f)  (IEEE fp32 divide, then RNE);
  *     q[n,k] = clamp(rne(W[n,k] / float(s)), -8, 7), all 0 when s == 0.
  *   W   [N][K] fp32 (in).   N >= 1, K % 128 == 0, 128 <= K <= QSPEC_MAX_K.
- *   Wq  [Np][K/2] u8 (out), Np = ceil(N/16)*16: the codes in the tiled
- *       storage order both GEMMs read.  Codes pack two per byte, code 2i of a
- *       row in bits 0-3 and code 2i+1 in bits 4-7 (two's complement); the
- *       row-major byte rows (padded with zero codes to Np rows) are stored as
- *       1 KiB tiles, tile (b, g) for rows 16b..16b+15 and group g at byte
- *       (b*(K/128) + g)*1024; in a tile, 16-byte slot l holds row 16b + l%16,
- *       row bytes [64g + 16*(l/16), +16).  Each wavefront's weight load is
- *       then one contiguous 1 KiB.
- *   Ws  [N][K/128] fp16 bits (out).
+ *   Wq  [Np][K/2] u8 (out), Np = ceil(N/16)*16, so Np*K/2 bytes: the codes
+ *       in the tiled storage order both GEMMs read.  Codes pack two per byte,
+ *       code 2i of a row in bits 0-3 and code 2i+1 in bits 4-7 (two's
+ *       complement); the row-major byte rows (padded with zero codes to Np
+ *       rows) are stored as 1 KiB tiles, tile (b, g) for rows 16b..16b+15 and
+ *       group g at byte (b*(K/128) + g)*1024; in a tile, 16-byte slot l holds
+ *       row 16b + l%16, row bytes [64g + 16*(l/16), +16).  Each wavefront's
+ *       weight load is then one contiguous 1 KiB.
+ *   Ws  [Np][K/128] fp16 bits (out), so Np*(K/128) elements -- every one is
+ *       written, padding rows with scale 0: the scale of row n and group g
+ *       is element ((n/16)*(K/128) + g)*16 + n%16 (the same 16-row tiling).
+ *   A caller that sizes Wq or Ws for N rather than Np rows when N % 16 != 0
+ *   gets writes past its buffers.
  *   group must be 128.  Non-finite W, or a/7 beyond the fp16 range, is
  *   unsupported (results unspecified).
  * ------------------------------------------------------------------------- */
@@ -185,11 +191,14 @@ qspec_status qspec_quant_act_rot(const uint16_t* X, int64_t M, int64_t K,
  * a biased running sum, which adds at most about 1/85 of one unit of P per
  * group to the rounding).
  *   Xq [M][K/2], Xs [M]   from qspec_quant_act.
- *   Wq [ceil(N/16)*16][K/2] (tiled), Ws [N][K/128] from qspec_pack_w4.
- *   Y  [M][N] fp32 (out).
- *   P  [M][N][K/128] int32 (out, optional: NULL skips it).
+ *   Wq [Np][K/2], Ws [Np][K/128], Np = ceil(N/16)*16, tiled, from
+ *   qspec_pack_w4.
+ *   Y  [M][N] fp32 (out); exactly M*N elements are written.
+ *   P  [M][N][K/128] int32 (out, optional: NULL skips it).  When given, the
+ *   family that computes Y (the one `variant` or AUTO names) stores the
+ *   integer group sums its own MFMA chain produced, so P checks that family.
  *   variant: QSPEC_GEMM_AUTO, _SKINNY, _TILED or _STREAM (M <= 16); GEMV is
- *   W4A16-only.  With P requested, AUTO and STREAM run the SKINNY family.
+ *   W4A16-only.
  *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_GEMM_W4A4,M,N,K)
  *   bytes (NULL allowed when that is 0).
  * ------------------------------------------------------------------------- */
@@ -229,16 +238,18 @@ qspec_status qspec_gemm_w4a4_bf16(const uint8_t* Xq, const float* Xs,
  *   weights, computed with int8 MFMA; variant AUTO (STREAM where W4A4's AUTO
  *   takes it, else SKINNY), SKINNY or STREAM (M <= 16); GEMV and TILED give
  *   QSPEC_ERR_UNSUPPORTED.  Within one family a row's result does not depend
- *   on M.  Wq/Ws as for qspec_gemm_w4a4; Y [M][N] fp32 (out);
- *   ws/ws_bytes: qspec_workspace_bytes(QSPEC_OP_GEMM_W4A8, M, N, K) bytes
- *   (the W4A4 size).  Validation and errors as for qspec_gemm_w4a4.
+ *   on M.  Wq/Ws as for qspec_gemm_w4a4; Y [M][N] fp32 (out); P [M][N][K/128]
+ *   int32 (out, optional: NULL skips it), the exact group partials of the
+ *   family that computes Y; ws/ws_bytes: qspec_workspace_bytes(
+ *   QSPEC_OP_GEMM_W4A8, M, N, K) bytes (the W4A4 size).  Validation and
+ *   errors as for qspec_gemm_w4a4.
  * ------------------------------------------------------------------------- */
 qspec_status qspec_quant_act8(const uint16_t* X, int64_t M, int64_t K,
                               int8_t* Xq, float* Xs, qspec_stream stream);
 qspec_status qspec_gemm_w4a8(const int8_t* Xq, const float* Xs,
                              const uint8_t* Wq, const uint16_t* Ws,
                              int64_t M, int64_t N, int64_t K, int group,
-                             int variant, float* Y,
+                             int variant, float* Y, int32_t* P,
                              void* ws, size_t ws_bytes, qspec_stream stream);
 
 /* ---------------------------------------------------------------------------
@@ -249,7 +260,8 @@ qspec_status qspec_gemm_w4a8(const int8_t* Xq, const float* Xs,
  * with the codes turned into bf16 in registers, bf16 MFMA (or VALU dot
  * products for the GEMV family) accumulating each group in fp32, and the
  * fp16 scale applied in fp32 per group.
- *   X  [M][K] bf16 bits (in);  Wq, Ws as above;  Y [M][N] fp32 (out).
+ *   X  [M][K] bf16 bits (in);  Wq [Np][K/2], Ws [Np][K/128] (tiled, from
+ *   qspec_pack_w4, Np = ceil(N/16)*16);  Y [M][N] fp32 (out).
  *   variant: QSPEC_GEMM_AUTO, _GEMV, _SKINNY, _TILED or _STREAM (M <= 16).
  *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_GEMM_W4A16,M,N,K).
  * ------------------------------------------------------------------------- */

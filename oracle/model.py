@@ -247,13 +247,16 @@ def greedy_decode(model, prompts, n_gen, gamma=4, with_margins=False):
     return toks, kv
 
 
-def selfspec_greedy(model, prompts, n_gen, gamma):
+def selfspec_greedy(model, prompts, n_gen, gamma, trace=None):
     """Greedy self-speculation: per round, gamma W4A4 draft forwards (one row
     per active sequence, each at its own position), one W4A16 verify forward
     over [last, d_0 .. d_{gamma-1}] that overwrites those KV rows, then the
     greedy acceptance rule; each sequence advances by n_accept + 1.  A
     sequence stops once it has n_gen tokens.  Returns (tokens [B, n_gen],
-    kv, stats) with stats = dict(accepted, drafted, rounds)."""
+    kv, stats) with stats = dict(accepted, drafted, rounds).  With a list
+    `trace`, every round appends dict(act = the active sequences, drafts
+    [nA, gamma], n_accept [nA], draft_margin [nA, gamma] = the relative top-2
+    margin of the draft logits behind each drafted token)."""
     B, P = prompts.shape
     kv = KVCache(model.cfg, B, kv_capacity(P, n_gen, gamma))
     last = prefill(model, kv, prompts)
@@ -268,13 +271,18 @@ def selfspec_greedy(model, prompts, n_gen, gamma):
         nA = act.size
         vtok = np.zeros((nA, gamma + 1), dtype=np.int32)
         vtok[:, 0] = last[act]
+        dmargin = np.zeros((nA, gamma))
         for j in range(gamma):
             logits = forward(model, kv, act, L[act] - 1 + j, vtok[:, j], DRAFT)
             vtok[:, j + 1] = argmax_first(logits)
+            dmargin[:, j] = top2_margin(logits)
         seq = np.repeat(act, gamma + 1)
         pos = (L[act][:, None] - 1 + np.arange(gamma + 1)[None, :]).reshape(-1)
         logits = forward(model, kv, seq, pos, vtok.reshape(-1), VERIFY)
         n, out = verify_greedy(logits.reshape(nA, gamma + 1, -1), vtok[:, 1:].copy())
+        if trace is not None:
+            trace.append(dict(act=act.copy(), drafts=vtok[:, 1:].copy(), n_accept=n.copy(),
+                              draft_margin=dmargin))
         for i, b in enumerate(act):
             k = int(n[i])
             gen[b].extend(int(t) for t in out[i, :k + 1])

@@ -62,7 +62,7 @@ def lib():
             "qspec_gemm_w4a4_bf16": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_gemm_w4a16": (I, [P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_quant_act8": (I, [P, I64, I64, P, P, P]),
-            "qspec_gemm_w4a8": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
+            "qspec_gemm_w4a8": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
             "qspec_verify": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P, SZ, P]),
             "qspec_embed": (I, [P, I64, I64, P, I64, P, P]),
             "qspec_add_rmsnorm": (I, [P, I64, P, I64, I64, I64, ctypes.c_double, P, P]),
@@ -255,8 +255,10 @@ def quant_act8(X, Xq=None, Xs=None):
     return Xq, Xs
 
 
-def gemm_w4a8(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None, N=None):
-    """W4A8 linear layer on the shared buffer -> Y fp32 [M, N] (N as for gemm_w4a4)."""
+def gemm_w4a8(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, partials=False, Y=None, P=None, ws=None,
+              N=None):
+    """W4A8 linear layer on the shared buffer -> Y fp32 [M, N] (and int32
+    partials [M, N, K/128]); N as for gemm_w4a4."""
     _need(Xq, "Xq", torch.int8)
     M, K = Xq.shape
     N = _out_n(N, Y, Wq)
@@ -265,10 +267,12 @@ def gemm_w4a8(Xq, Xs, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None, N=None):
     _need(Ws, "Ws", torch.float16, (padded_rows(N), K // GROUP))
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    if partials and P is None:
+        P = torch.empty((M, N, K // GROUP), dtype=torch.int32, device=Xq.device)
     w, wb = _workspace(workspace_bytes(OP_GEMM_W4A8, M, N, K), Xq.device, ws)
     _check(lib().qspec_gemm_w4a8(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), M, N, K, GROUP, variant,
-                                 _ptr(Y), _ptr(w), wb, _stream()), "qspec_gemm_w4a8")
-    return Y
+                                 _ptr(Y), _ptr(P), _ptr(w), wb, _stream()), "qspec_gemm_w4a8")
+    return (Y, P) if partials else Y
 
 
 def gemm_w4a16(X, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None, N=None):

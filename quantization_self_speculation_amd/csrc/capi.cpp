@@ -118,6 +118,11 @@ qspec_status check_ws(void* ws, size_t have, size_t need) {
   return QSPEC_OK;
 }
 
+qspec_status check_verify(int mode, int64_t B, int gamma, int64_t V, const int32_t* draft_tok,
+                          const float* draft_logits, const float* target_logits,
+                          const float* u_accept, const float* u_sample, int32_t* n_accept,
+                          int32_t* out_tok);
+
 template <typename T>
 qspec_status check_elem(const T* p, const char* name) {
   if (p == nullptr) return fail(QSPEC_ERR_NULL, "%s is NULL", name);
@@ -289,7 +294,7 @@ qspec_status qspec_gemm_w4a4_bf16(const uint8_t* Xq, const float* Xs, const uint
 
 qspec_status qspec_gemm_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq,
                              const uint16_t* Ws, int64_t M, int64_t N, int64_t K, int group,
-                             int variant, float* Y, void* ws, size_t ws_bytes,
+                             int variant, float* Y, int32_t* P, void* ws, size_t ws_bytes,
                              qspec_stream stream) {
   QS_TRY(check_gemm(M, N, K, group, variant, false));
   QS_REQUIRE(variant == QSPEC_GEMM_AUTO || variant == QSPEC_GEMM_SKINNY ||
@@ -301,9 +306,10 @@ qspec_status qspec_gemm_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* W
   QS_PTR(Wq);
   QS_PTR(Ws);
   QS_PTR(Y);
+  if (P != nullptr) QS_PTR(P);
   QS_TRY(check_ws(ws, ws_bytes, w4a4_ws_bytes(M, N, K)));
   QS_TRY(device_check());
-  return hip_result(launch_w4a8(Xq, Xs, Wq, Ws, M, N, K, variant, Y, ws, (hipStream_t)stream),
+  return hip_result(launch_w4a8(Xq, Xs, Wq, Ws, M, N, K, variant, Y, P, ws, (hipStream_t)stream),
                     "gemm_w4a8 launch");
 }
 
@@ -325,6 +331,22 @@ qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V, const int32
                           const float* draft_logits, const float* target_logits,
                           const float* u_accept, const float* u_sample, int32_t* n_accept,
                           int32_t* out_tok, void* ws, size_t ws_bytes, qspec_stream stream) {
+  QS_TRY(check_verify(mode, B, gamma, V, draft_tok, draft_logits, target_logits, u_accept,
+                      u_sample, n_accept, out_tok));
+  QS_TRY(check_ws(ws, ws_bytes, verify_ws_bytes(B, gamma, V)));
+  QS_TRY(device_check());
+  return hip_result(launch_verify(mode, B, gamma, V, draft_tok, draft_logits, target_logits,
+                                  u_accept, u_sample, n_accept, out_tok, ws, (hipStream_t)stream),
+                    "verify launch");
+}
+
+}  // extern "C"
+
+namespace {
+qspec_status check_verify(int mode, int64_t B, int gamma, int64_t V, const int32_t* draft_tok,
+                          const float* draft_logits, const float* target_logits,
+                          const float* u_accept, const float* u_sample, int32_t* n_accept,
+                          int32_t* out_tok) {
   QS_REQUIRE(mode == QSPEC_VERIFY_GREEDY || mode == QSPEC_VERIFY_SAMPLE, QSPEC_ERR_UNSUPPORTED,
              "unknown verify mode %d", mode);
   QS_REQUIRE(gamma >= 1 && gamma <= QSPEC_MAX_GAMMA, QSPEC_ERR_SHAPE,
@@ -345,12 +367,11 @@ qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V, const int32
     QS_REQUIRE(draft_logits == nullptr && u_accept == nullptr && u_sample == nullptr,
                QSPEC_ERR_UNSUPPORTED, "greedy mode takes no draft logits or uniforms");
   }
-  QS_TRY(check_ws(ws, ws_bytes, verify_ws_bytes(B, gamma, V)));
-  QS_TRY(device_check());
-  return hip_result(launch_verify(mode, B, gamma, V, draft_tok, draft_logits, target_logits,
-                                  u_accept, u_sample, n_accept, out_tok, ws, (hipStream_t)stream),
-                    "verify launch");
+  return QSPEC_OK;
 }
+}  // namespace
+
+extern "C" {
 
 // ---------------------------------------------------------------- decoder kernels
 qspec_status qspec_embed(const uint16_t* emb, int64_t V, int64_t d, const int32_t* tok, int64_t M,

@@ -197,7 +197,7 @@ struct SkinnyArgs {
   uint16_t* Yb;             // bf16 output instead of Y (W4A4 only), else null
   float* part;              // [S][M][N] when S > 1
   unsigned long long* cnt;  // [T] when S > 1
-  int32_t* P;               // W4A4 int32 group partials (optional)
+  int32_t* P;               // W4A4 / W4A8 int32 group partials (optional)
   int M, N, K, S, gps, ntiles, T;
   unsigned epoch;
 };
@@ -255,6 +255,9 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
+    // release: every partial the workgroup stored (ordered before this point
+    // by the barrier) happens-before the arrival count at system scope
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
     unsigned long long* slot = a.cnt + t;
     unsigned long long cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     unsigned int count = 0;
@@ -272,6 +275,9 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   }
   __syncthreads();
   if (!s_last) return;
+  // acquire: the other slices' partials (released before their counts) are
+  // visible to every thread's loads below
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
   // all partials of an element are requested before any is added (in slice
   // order), 8 slices per batch
   const int64_t MN = (int64_t)M * N;
@@ -318,7 +324,7 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
 template <int MODE, int MB, int NB, int CH, int PD, bool WITHP, int NWV = 4>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny_wpe(MODE, MB)))) void skinny_kernel(const SkinnyArgs a) {
   static_assert(PD % CH == 0, "prefetch depth must be a multiple of the chunk");
-  static_assert(!(WITHP && MODE != kW4A4), "the int32 partials output is a W4A4 check path");
+  static_assert(!(WITHP && MODE == kW4A16), "the int32 partials output is an integer-mode path");
   constexpr int NT = 64 * NWV;             // threads of a workgroup
   constexpr int ROWS = 16 * MB;            // activation rows of an m-chunk
   constexpr int WROWS = 16 * NB * NWV;     // weight rows of a tile (NWV wavefronts x NB blocks of 16)
@@ -558,7 +564,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
               if (m < M) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                  if (n + r < N) a.P[((int64_t)m * N + n + r) * G + g_begin + gi] = acc[nb][mb][r] >> 8;
+                  if (n + r < N)
+                    a.P[((int64_t)m * N + n + r) * G + g_begin + gi] =
+                        acc[nb][mb][r] >> (MODE == kW4A8 ? 4 : 8);
               }
             }
           }
@@ -604,6 +612,7 @@ struct TiledArgs {
   const uint16_t* Ws;
   float* Y;
   uint16_t* Yb;  // bf16 output instead of Y (W4A4 only), else null
+  int32_t* P;    // W4A4 int32 group partials [M][N][K/128] (optional)
   int M, N, K, ntn, ntm;
 };
 
@@ -642,7 +651,7 @@ struct TiledArgs {
 #define QSPEC_PF_RST 144  // LDS row stride of the widened activation slice (bytes)
 #endif
 
-template <int WN, int PD, int CH, bool BOUT>
+template <int WN, int PD, int CH, bool BOUT, bool WITHP>
 __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArgs a) {
   constexpr int BN = 64 * WN, BM = 64, NT = 64 * WN, RST = QSPEC_PF_RST;
   constexpr int BCH = BM * 4;                          // 16-byte activation chunks per group
@@ -844,6 +853,16 @@ __global__ __launch_bounds__(64 * WN, 2) void w4a4_prefill_kernel(const TiledArg
       for (int mb = 0; mb < 4; ++mb) {
         v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bf[mb][0], cbias, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bf[mb][1], acc, 0, 0, 0);
+        if constexpr (WITHP) {
+          // the same accumulator, as integers: bits(B) + 256 P exactly
+          const int m = tile_m0(ck) + mb * 16 + l16;
+          const int n = tile_nt(ck) * BN + wn * 64 + nb * 16 + lg * 4;
+          if (m < M) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) a.P[((int64_t)m * N + n + r) * G + cg] = (acc[r] - (int)kBiasBits) >> 8;
+          }
+        }
         tot[nb][mb][0] = fmaf(sc.x, __int_as_float(acc[0]), tot[nb][mb][0]);
         tot[nb][mb][1] = fmaf(sc.y, __int_as_float(acc[1]), tot[nb][mb][1]);
         tot[nb][mb][2] = fmaf(sc.z, __int_as_float(acc[2]), tot[nb][mb][2]);
@@ -923,11 +942,14 @@ hipError_t launch_w4a4_prefill(TiledArgs a, hipStream_t s) {
   const int64_t tiles = 8 * cdiv(a.ntn, 8) * a.ntm;  // a multiple of 8, as is the grid
   const int64_t grid = std::min<int64_t>(tiles, QSPEC_PF_GRID);
   if (a.Yb != nullptr)
-    hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH, true>), dim3((unsigned)grid), dim3(64 * WN),
-                       0, s, a);
+    hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH, true, false>), dim3((unsigned)grid),
+                       dim3(64 * WN), 0, s, a);
+  else if (a.P != nullptr)
+    hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH, false, true>), dim3((unsigned)grid),
+                       dim3(64 * WN), 0, s, a);
   else
-    hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH, false>), dim3((unsigned)grid), dim3(64 * WN),
-                       0, s, a);
+    hipLaunchKernelGGL((w4a4_prefill_kernel<WN, PD, CH, false, false>), dim3((unsigned)grid),
+                       dim3(64 * WN), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1146,8 +1168,9 @@ hipError_t launch_w4a16_prefill(TiledArgs a, hipStream_t s) {
 
 template <int MODE>
 hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
-                        int64_t M, int64_t N, int64_t K, float* Y, uint16_t* Yb, hipStream_t s) {
-  TiledArgs a{X, Xs, Wq, Ws, Y, Yb, (int)M, (int)N, (int)K, 0, 0};  // the launcher sets the grid
+                        int64_t M, int64_t N, int64_t K, float* Y, uint16_t* Yb, int32_t* P,
+                        hipStream_t s) {
+  TiledArgs a{X, Xs, Wq, Ws, Y, Yb, P, (int)M, (int)N, (int)K, 0, 0};  // the launcher sets the grid
   if (MODE == kW4A16) return launch_w4a16_prefill<QSPEC_PF16_SHAPE>(a, s);
   return launch_w4a4_prefill<QSPEC_PF_SHAPE>(a, s);
 }
@@ -1177,6 +1200,7 @@ struct StreamArgs {
   const uint16_t* Ws;
   float* Y;
   uint16_t* Yb;  // bf16 output instead of Y (W4A4 only), else null
+  int32_t* P;    // W4A4 / W4A8 int32 group partials [M][N][K/128] (optional)
   int M, N, K, nrb;
 };
 
@@ -1205,8 +1229,9 @@ struct StreamStage {
 };
 
 
-template <int MODE>
+template <int MODE, bool WITHP>
 __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
+  static_assert(!(WITHP && MODE == kW4A16), "the int32 partials output is an integer-mode path");
   constexpr int PD = MODE == kW4A16 ? QSPEC_ST_PD16 : QSPEC_ST_PD4;
   extern __shared__ __attribute__((aligned(16))) float red_[];  // [nw][64][4] when nw > 1
   float(*red)[64][4] = reinterpret_cast<float(*)[64][4]>(red_);
@@ -1252,8 +1277,8 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   for (int i = 0; i < PD; ++i) load(ring[i], g0 + i);
   const v8bf negb = as_v8bf(kNegBiasPair, kNegBiasPair, kNegBiasPair, kNegBiasPair);
 
-  // one group from ring stage i
-  auto group = [&](int i) {
+  // one group from ring stage i, holding this wavefront's local group li
+  auto group = [&](int i, int li) {
     const StreamStage<MODE>& st = ring[i];
     const uint32_t s01 = st.s.x, s23 = st.s.y;
     if (MODE == kW4A16) {
@@ -1296,6 +1321,16 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
       }
       v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
+      if constexpr (WITHP) {
+        // the accumulator is 256 P (both operands x16) or 16 P (8-bit codes)
+        const int n = rb * 16 + lg * 4;
+        if (l16 < M) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < a.N)
+              a.P[((int64_t)l16 * a.N + n + r) * G + w + nw * li] = acc[r] >> (MODE == kW4A8 ? 4 : 8);
+        }
+      }
       // / 256 when both operands carry the x16 of the widening, / 16 for
       // 8-bit activation codes
       constexpr float f = MODE == kW4A8 ? 0.0625f : 0.00390625f;
@@ -1312,7 +1347,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   for (; gb + PD <= g1; gb += PD) {
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
-      group(i);
+      group(i, gb + i);
       load(ring[i], gb + i + PD);  // refill this stage, PD groups ahead
       // issue the refill here, before the next group's arithmetic (left to
       // itself the scheduler sinks every refill to the end of the round, so
@@ -1322,7 +1357,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < PD - 1; ++i)
-    if (gb + i < g1) group(i);  // tail: fewer than PD groups
+    if (gb + i < g1) group(i, gb + i);  // tail: fewer than PD groups
 
   // per-wavefront sums -> one sum per output, in wavefront order
   if (nw > 1) {
@@ -1357,11 +1392,18 @@ int stream_waves(int64_t N, int64_t K) {
 
 template <int MODE>
 hipError_t launch_stream(const void* X, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
-                         int64_t M, int64_t N, int64_t K, float* Y, uint16_t* Yb, hipStream_t s) {
-  StreamArgs a{X, Xs, Wq, Ws, Y, Yb, (int)M, (int)N, (int)K, (int)cdiv(N, 16)};
+                         int64_t M, int64_t N, int64_t K, float* Y, uint16_t* Yb, int32_t* P,
+                         hipStream_t s) {
+  StreamArgs a{X, Xs, Wq, Ws, Y, Yb, P, (int)M, (int)N, (int)K, (int)cdiv(N, 16)};
   const int nw = stream_waves(N, K);
   const size_t lds = nw > 1 ? (size_t)nw * 64 * 4 * sizeof(float) : 0;
-  hipLaunchKernelGGL(stream_kernel<MODE>, dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+  if constexpr (MODE != kW4A16) {
+    if (P != nullptr) {
+      hipLaunchKernelGGL((stream_kernel<MODE, true>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((stream_kernel<MODE, false>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1522,7 +1564,9 @@ int skinny_nwv(int64_t N, int64_t S) {
   return best;
 }
 
-SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool withp = false) {
+// max_tiles: the plan with four-wavefront tiles (the most arrival counters),
+// which sizes the workspace for every plan of these (M, N, K)
+SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool max_tiles = false) {
   SkinnyPlan p;
   const int64_t G = K / kGroup;
   const int64_t t64 = cdiv(N, 64);  // the split depends on N and K only
@@ -1541,7 +1585,7 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool withp = f
   // two 16-row blocks per wavefront halve the LDS activation reads once the
   // activation tile spans several m-blocks (the bf16 verifier shapes)
   p.NB = (mode == 0 && p.MB >= 2) ? QSPEC_SK_NB16 : 1;
-  p.NWV = ((p.MB == 1 || (mode == 0 && p.MB == 3 && p.NB == 1)) && !withp) ? skinny_nwv(N, p.S) : 4;
+  p.NWV = ((p.MB == 1 || (mode == 0 && p.MB == 3 && p.NB == 1)) && !max_tiles) ? skinny_nwv(N, p.S) : 4;
   p.ntiles = (int)cdiv(N, 16 * p.NB * p.NWV);
   p.mchunks = (int)cdiv(M, 16 * p.MB);
   p.T = p.ntiles * p.mchunks;
@@ -1561,9 +1605,10 @@ unsigned int next_epoch() {
 
 template <int MODE, bool WITHP>
 hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
-  dim3 grid((unsigned)p.blocks), block(256);
-  if (MODE == kW4A16 && p.MB == 3 && p.NWV != 4 && !WITHP) {
-    const dim3 blk(64 * p.NWV);
+  const dim3 grid((unsigned)p.blocks), blk(64 * p.NWV);
+  // W4A16 with three activation blocks, or any mode with one: the workgroup
+  // size balanced over the CUs (5, 8 or 10 wavefronts; 4 is the generic case)
+  if (MODE == kW4A16 && p.MB == 3 && p.NWV != 4) {
     switch (p.NWV) {
       case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, 1, QSPEC_SK_B3, false, 5>), grid, blk, 0, s, a); break;
       case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, 1, QSPEC_SK_B3, false, 8>), grid, blk, 0, s, a); break;
@@ -1571,8 +1616,7 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
     }
     return hipGetLastError();
   }
-  if (p.MB == 1 && p.NWV != 4 && !WITHP) {
-    const dim3 blk(64 * p.NWV);
+  if (p.MB == 1 && p.NWV != 4) {
     if constexpr (MODE == kW4A16) {
       switch (p.NWV) {
         case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 5>), grid, blk, 0, s, a); break;
@@ -1581,26 +1625,26 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
       }
     } else {  // W4A4 and W4A8 share the int8 data flow and its parameters
       switch (p.NWV) {
-        case 5: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, false, 5>), grid, blk, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, false, 8>), grid, blk, 0, s, a); break;
-        default: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, false, 10>), grid, blk, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP, 5>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP, 8>), grid, blk, 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP, 10>), grid, blk, 0, s, a); break;
       }
     }
     return hipGetLastError();
   }
   if constexpr (MODE == kW4A16) {
     switch (p.MB) {
-      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, WITHP>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_NB16, QSPEC_SK_B2, WITHP>), grid, block, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, WITHP>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_NB16, QSPEC_SK_B4, WITHP>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false>), grid, blk, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_NB16, QSPEC_SK_B2, false>), grid, blk, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, false>), grid, blk, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_NB16, QSPEC_SK_B4, false>), grid, blk, 0, s, a); break;
     }
   } else {
     switch (p.MB) {
-      case 1: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((skinny_kernel<MODE, 2, 1, QSPEC_SK_A2, WITHP>), grid, block, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((skinny_kernel<MODE, 3, 1, QSPEC_SK_A3, WITHP>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<MODE, 4, 1, QSPEC_SK_A4, WITHP>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP>), grid, blk, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<MODE, 2, 1, QSPEC_SK_A2, WITHP>), grid, blk, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<MODE, 3, 1, QSPEC_SK_A3, WITHP>), grid, blk, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<MODE, 4, 1, QSPEC_SK_A4, WITHP>), grid, blk, 0, s, a); break;
     }
   }
   return hipGetLastError();
@@ -1608,7 +1652,7 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
 
 template <int MODE>
 hipError_t launch_skinny(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
-  if constexpr (MODE == kW4A4) {
+  if constexpr (MODE != kW4A16) {
     if (a.P != nullptr) return launch_skinny_t<MODE, true>(a, p, s);
   }
   return launch_skinny_t<MODE, false>(a, p, s);
@@ -1675,7 +1719,8 @@ size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
                         int64_t N, int64_t K, int variant, float* Y, void* ws, hipStream_t s) {
   const int v = w4a16_pick(variant, M, N, K);
-  if (v == QSPEC_GEMM_STREAM) return launch_stream<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, nullptr, s);
+  if (v == QSPEC_GEMM_STREAM)
+    return launch_stream<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, nullptr, nullptr, s);
   if (v == QSPEC_GEMM_GEMV) {
     const GemvPlan q = plan_gemv(K);
     // rows of X in chunks of up to 4
@@ -1700,7 +1745,8 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
     }
     return hipSuccess;
   }
-  if (v == QSPEC_GEMM_TILED) return launch_tiled<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, nullptr, s);
+  if (v == QSPEC_GEMM_TILED)
+    return launch_tiled<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, nullptr, nullptr, s);
   const SkinnyPlan p = plan_skinny(0, M, N, K);
   SkinnyArgs a{};
   a.X = X;
@@ -1722,14 +1768,13 @@ size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, uint16_t* Yb,
                        int32_t* P, void* ws, hipStream_t s) {
-  // the int32 partials output is a check path served by the skinny family;
-  // exactly one of Y (fp32) and Yb (bf16) is given
+  // exactly one of Y (fp32) and Yb (bf16) is given; the int32 partials P
+  // (with Y only) come from the family that computes Y, the same kernel
+  // code instantiated with its partials store
   const int v = w4a4_pick(variant, M, N, K);
-  if (v == QSPEC_GEMM_TILED && P == nullptr)
-    return launch_tiled<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, Yb, s);
-  if (v == QSPEC_GEMM_STREAM && P == nullptr)
-    return launch_stream<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, Yb, s);
-  const SkinnyPlan p = plan_skinny(1, M, N, K, P != nullptr);
+  if (v == QSPEC_GEMM_TILED) return launch_tiled<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, Yb, P, s);
+  if (v == QSPEC_GEMM_STREAM) return launch_stream<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, Yb, P, s);
+  const SkinnyPlan p = plan_skinny(1, M, N, K);
   SkinnyArgs a{};
   a.X = Xq;
   a.Xs = Xs;
@@ -1749,11 +1794,11 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
 // or on request, else the skinny family, on the W4A4 plan (same k-split,
 // same workspace); AUTO, SKINNY and STREAM are the accepted variants.
 hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
-                       int64_t M, int64_t N, int64_t K, int variant, float* Y, void* ws,
-                       hipStream_t s) {
+                       int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
+                       void* ws, hipStream_t s) {
   const int v = variant == QSPEC_GEMM_AUTO ? auto_pick(M, N, K, 256, 64, 96) : variant;
   if (v == QSPEC_GEMM_STREAM)
-    return launch_stream<kW4A8>(Xq, Xs, Wq, Ws, M, N, K, Y, nullptr, s);
+    return launch_stream<kW4A8>(Xq, Xs, Wq, Ws, M, N, K, Y, nullptr, P, s);
   const SkinnyPlan p = plan_skinny(1, M, N, K);
   SkinnyArgs a{};
   a.X = Xq;
@@ -1761,11 +1806,12 @@ hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, con
   a.Wq = Wq;
   a.Ws = Ws;
   a.Y = Y;
+  a.P = P;
   a.cnt = p.S > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
   a.part = p.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.cnt_bytes) : nullptr;
   a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;
   a.epoch = next_epoch();
-  return launch_skinny_t<kW4A8, false>(a, p, s);
+  return launch_skinny<kW4A8>(a, p, s);
 }
 
 }  // namespace qspec

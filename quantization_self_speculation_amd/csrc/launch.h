@@ -33,8 +33,8 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
                        int32_t* P, void* ws, hipStream_t s);
 
 hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
-                       int64_t M, int64_t N, int64_t K, int variant, float* Y, void* ws,
-                       hipStream_t s);
+                       int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
+                       void* ws, hipStream_t s);
 
 size_t verify_ws_bytes(int64_t B, int gamma, int64_t V);
 hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_t* draft_tok,

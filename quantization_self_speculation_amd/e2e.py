@@ -42,12 +42,18 @@ class Decoder:
     length `gamma`."""
 
     def __init__(self, cfg, weights, B, P, max_gen, gamma, device="cuda:0",
-                 variant=b.GEMM_SKINNY):
+                 variant=b.GEMM_SKINNY, draft_mode=DRAFT):
         if cfg.head_dim != 128:
             raise ValueError("head_dim must be 128")
         self.cfg, self.B, self.P, self.max_gen, self.gamma = cfg, B, P, max_gen, gamma
         self.dev = torch.device(device)
         self.variant = variant
+        # the drafter's layers: W4A4 (the method); W4A16 turns the drafter
+        # into the verifier itself, which must then accept every draft (a
+        # check of the loop's bookkeeping)
+        if draft_mode not in (DRAFT, VERIFY):
+            raise ValueError("draft_mode must be 'w4a4' or 'w4a16'")
+        self.draft_mode = draft_mode
         dev = self.dev
 
         def packed(W):
@@ -216,7 +222,7 @@ class Decoder:
         V = self.cfg.vocab
         for j in range(g):
             b.spec_prepare(0, B, g, j, self.len, self.vtok, None, self.seq, self.pos, self.tok)
-            logits = self.forward(DRAFT, B, self.variant)
+            logits = self.forward(self.draft_mode, B, self.variant)
             b.argmax(logits, self.vtok[j + 1:], out_stride=g + 1)
         b.spec_prepare(1, B, g, 0, self.len, self.vtok, self.drafts, self.seq, self.pos, self.tok)
         logits = self.forward(VERIFY, B * (g + 1), self.variant)
@@ -245,10 +251,14 @@ class Decoder:
         return g
 
     # ------------------------------------------------------------ loops
-    def run(self, prompts, speculative, use_graph=True, max_rounds=None):
+    def run(self, prompts, speculative, use_graph=True, max_rounds=None, record=None):
         """Prefill then decode greedily until every sequence has max_gen
         tokens.  Returns dict(tokens [B, max_gen] int32 numpy, rounds,
-        accepted, drafted_rows, prefill_s, decode_s)."""
+        accepted, drafted_rows, prefill_s, decode_s).  With a list `record`
+        (speculative only; it reads device state after every round, so the
+        timings then include those reads), every round appends dict(n_gen [B]
+        = tokens generated before the round, active [B] bool = n_gen <
+        max_gen, drafts [B, gamma], n_accept [B])."""
         if speculative and self.gamma < 1:
             raise ValueError("speculative decoding needs gamma >= 1")
         self.reset()
@@ -268,9 +278,16 @@ class Decoder:
         rounds = 0
         if speculative:
             limit = self.max_gen if max_rounds is None else max_rounds
+            B, g = self.B, self.gamma
             while rounds < limit:
+                if record is not None:
+                    n_gen0 = self.n_gen.cpu().numpy()
                 graph.replay() if graph is not None else fn()
                 rounds += 1
+                if record is not None:
+                    record.append(dict(n_gen=n_gen0, active=n_gen0 < self.max_gen,
+                                       drafts=self.vtok.view(B, g + 1)[:, 1:].cpu().numpy(),
+                                       n_accept=self.n_acc.cpu().numpy()))
                 if int(self.stats[2].item()) == 0:
                     break
         else:

@@ -141,6 +141,10 @@ class ModelConfig:
 # 128, SwiGLU hidden 5632, vocabulary 32000
 E2E_MODEL = ModelConfig(vocab=32000, d=2048, n_layers=8, n_heads=16, n_kv=4, head_dim=128,
                         ffn=5632)
+# the same layer shapes (16 query / 4 key-value heads, d 2048, SwiGLU 5632,
+# vocabulary 32000) with two layers, small enough for the CPU oracle
+E2E_MODEL_2L = ModelConfig(vocab=32000, d=2048, n_layers=2, n_heads=16, n_kv=4, head_dim=128,
+                           ffn=5632)
 # a two-layer model of the same structure for CPU-sized tests
 TINY_MODEL = ModelConfig(vocab=512, d=256, n_layers=2, n_heads=2, n_kv=1, head_dim=128, ffn=768)
 

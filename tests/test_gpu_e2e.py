@@ -221,7 +221,7 @@ def test_e2e_tiny_selfspec_equals_pure_and_oracle(seed, gamma):
     assert matched >= B * n_gen // 2
 
 
-def test_e2e_forwards_against_oracle():
+def _forwards_against_oracle(cfg, w, prompts, gamma=2):
     """After a shared prefill, every linear layer of a W4A16 and of a W4A4
     forward matches the oracle layer applied to the GPU's own bf16 input,
     within the fp tolerance (op-by-op parity).  The whole W4A16 forward's
@@ -229,20 +229,19 @@ def test_e2e_forwards_against_oracle():
     differ at the bf16 rounding points, where a value computed in a different
     order can round one bf16 unit (2**-8 relative) the other way, so that
     comparison allows 1e-2 of max|logit|.  The W4A4 forward is checked op by op
-    only:
-    each linear layer's output against the oracle layer applied to the GPU's
-    own bf16 input (the quantizer rounds, so a one-ulp difference upstream may
-    move a code, and whole-forward W4A4 values are not comparable)."""
-    B, P = 2, 8
-    cfg, w, prompts = _tiny_case(7, B, P)
-    dec = Decoder(cfg, w, B, P, 4, 2)
+    only: each linear layer's output against the oracle layer applied to the
+    GPU's own bf16 input (the quantizer rounds, so a one-ulp difference
+    upstream may move a code, and whole-forward W4A4 values are not
+    comparable)."""
+    B, P = prompts.shape
+    dec = Decoder(cfg, w, B, P, 4, gamma)
     dec.reset()
     dec.prefill(prompts)
     model = om.Model(cfg, w)
     kv = om.KVCache(cfg, B, dec.cap)
     first = om.prefill(model, kv, prompts)
     assert np.array_equal(host(dec.first), first)
-    toks = np.array([3, 77], np.int32)
+    toks = np.arange(3, 3 + 74 * B, 74, dtype=np.int32) % cfg.vocab
     packed = {(li, k): model.layers[li][k] for li in range(cfg.n_layers)
               for k in ("qkv", "o", "gu", "down")}
     packed.update({(cfg.n_layers, "lm"): model.lm})
@@ -262,10 +261,132 @@ def test_e2e_forwards_against_oracle():
         if mode == om.VERIFY:
             kv2 = om.KVCache(cfg, B, dec.cap)
             kv2.k[:], kv2.v[:] = kv.k, kv.v
-            want = om.forward(model, kv2, [0, 1], [P, P], toks, mode)
+            want = om.forward(model, kv2, list(range(B)), [P] * B, toks, mode)
             err = np.abs(got - want).max() / np.abs(want).max()
             say(f"  w4a16 forward logits rel err {err:.2e}")
             assert err <= 1e-2
+
+
+def test_e2e_forwards_against_oracle():
+    B, P = 2, 8
+    cfg, w, prompts = _tiny_case(7, B, P)
+    _forwards_against_oracle(cfg, w, prompts)
+
+
+def _pure_tokens_against_oracle(tokens, model, prompts, n_gen, gamma):
+    """GPU pure-decode tokens equal the oracle's up to the first divergence,
+    which may only come where the oracle's top-2 logits are within twice the
+    logit error the fp tolerance allows (2 * 2e-3 of the row's max|logit|)."""
+    B = prompts.shape[0]
+    want, _, margins = om.greedy_decode(model, prompts, n_gen, gamma, with_margins=True)
+    for bi in range(B):
+        k = _first_divergence(tokens[bi], want[bi])
+        if k is not None:
+            say(f"  seq {bi}: diverges at {k}, oracle relative margin {margins[bi, k]:.3e}")
+            assert margins[bi, k] <= 4e-3, (bi, k, margins[bi, k])
+    return sum((_first_divergence(tokens[i], want[i]) or n_gen) for i in range(B))
+
+
+def test_e2e_config4_layers_against_oracle():
+    """The end-to-end model's layer shapes (d 2048, 16 query / 4 key-value
+    heads of 128 -- four query heads per KV head --, SwiGLU 5632, vocabulary
+    32000) with two layers, three sequences of 8-token prompts: every linear
+    layer of a draft and a verify forward against the oracle op by op, the
+    verify forward's logits against the oracle forward, greedy
+    self-speculation equal to pure W4A16 decoding on the GPU, and the pure
+    tokens equal to the oracle's greedy decode under the near-tie rule."""
+    cfg = synth.E2E_MODEL_2L
+    rng = synth.make_rng(42, 0)
+    w = synth.model_weights(rng, cfg)
+    B, P, n_gen, gamma = 3, 8, 8, 4
+    prompts = synth.prompts(rng, B, P, cfg.vocab)
+    say("config-4 layers: op-by-op")
+    _forwards_against_oracle(cfg, w, prompts, gamma)
+    say("config-4 layers: decode")
+    dec = Decoder(cfg, w, B, P, n_gen, gamma)
+    pure = dec.run(prompts, speculative=False)
+    spec = dec.run(prompts, speculative=True)
+    assert np.array_equal(spec["tokens"], pure["tokens"])
+    matched = _pure_tokens_against_oracle(pure["tokens"], om.Model(cfg, w), prompts, n_gen, gamma)
+    assert matched >= B * n_gen // 2
+
+
+@pytest.mark.parametrize("seed,gamma", [(0, 4), (1, 3)])
+def test_e2e_self_draft_accepts_everything(seed, gamma):
+    """The loop's bookkeeping, exactly: with the verifier itself as the
+    drafter (W4A16 layers of the same kernel family, whose rows do not depend
+    on the row count) every draft is the token the verifier would emit at
+    that position, so every round accepts all gamma drafts, the drafts of a
+    round are the next gamma tokens of pure decoding, and the emitted tokens
+    are the pure ones.  A wrong draft position, token feed or KV row would
+    break this."""
+    B, P, n_gen = 4, 16, 40
+    cfg, w, prompts = _tiny_case(seed, B, P)
+    say(f"self-draft seed={seed} gamma={gamma}")
+    dec = Decoder(cfg, w, B, P, n_gen, gamma, draft_mode="w4a16")
+    pure = dec.run(prompts, speculative=False)["tokens"]
+    rec = []
+    spec = dec.run(prompts, speculative=True, record=rec)
+    assert np.array_equal(spec["tokens"], pure)
+    for r, g in enumerate(rec):
+        for b in np.nonzero(g["active"])[0]:
+            k = int(g["n_gen"][b])
+            assert g["n_accept"][b] == gamma, (r, b)
+            want = pure[b, k:k + gamma]
+            assert np.array_equal(g["drafts"][b][:want.size], want), (r, b)
+    assert spec["accepted"] == gamma * spec["active_rows"]
+
+
+@pytest.mark.parametrize("seed,gamma", [(0, 4), (2, 3)])
+def test_e2e_tiny_drafts_match_oracle(seed, gamma):
+    """The W4A4 drafter against the oracle's self-speculation: round by
+    round, every active sequence's gamma drafted tokens and its accepted
+    count equal the oracle's up to the round where that sequence's drafts
+    part.  A parting is allowed only at a drafted token whose oracle draft
+    logits have a relative top-2 margin within 0.1: one bf16 unit of
+    difference in a W4A4 layer input (the two sides sum the fp32 residual
+    stream in different orders) can move one 4-bit activation code, and that
+    shifts the layer's outputs by a few percent -- the oracle's own drafts
+    part at margins of several percent under a one-ulp perturbation of its
+    GEMM outputs (tests/test_oracle_model.py).  The whole-run acceptance
+    rates must agree within 0.1, and the emitted tokens equal pure W4A16
+    decoding on the GPU."""
+    B, P, n_gen = 4, 16, 32
+    cfg, w, prompts = _tiny_case(seed, B, P)
+    say(f"tiny drafts seed={seed} gamma={gamma}")
+    dec = Decoder(cfg, w, B, P, n_gen, gamma)
+    rec = []
+    spec = dec.run(prompts, speculative=True, record=rec)
+    tr = []
+    toks, _, st = om.selfspec_greedy(om.Model(cfg, w), prompts, n_gen, gamma, trace=tr)
+    a_gpu = spec["accepted"] / (gamma * spec["active_rows"])
+    a_or = st["accepted"] / st["drafted"]
+    say(f"  GPU accepted {spec['accepted']} of {gamma * spec['active_rows']} drafted, "
+        f"oracle {st['accepted']} of {st['drafted']}; rounds {spec['rounds']} / {st['rounds']}")
+    assert abs(a_gpu - a_or) <= 0.1
+    alive = set(range(B))          # sequences not yet parted from the oracle
+    compared = 0
+    for r, (g, o) in enumerate(zip(rec, tr)):
+        act = [int(b) for b in o["act"]]
+        for b in sorted(alive):
+            # a sequence that has matched so far has the same length on both sides
+            assert bool(g["active"][b]) == (b in act), (r, b)
+            if b not in act:
+                continue
+            i = act.index(b)
+            if np.array_equal(g["drafts"][b], o["drafts"][i]):
+                assert g["n_accept"][b] == o["n_accept"][i], (r, b)
+                compared += 1
+                continue
+            j = int(np.nonzero(g["drafts"][b] != o["drafts"][i])[0][0])
+            m = o["draft_margin"][i, j]
+            say(f"  round {r} seq {b}: drafts part at {j}, oracle draft margin {m:.3e}")
+            assert m <= 0.1, (r, b, j, m)
+            alive.discard(b)
+        if not alive:
+            break
+    say(f"  {compared} (round, sequence) pairs equal to the oracle before parting")
+    assert np.array_equal(spec["tokens"], dec.run(prompts, speculative=False)["tokens"])
 
 
 def test_e2e_model_selfspec_equals_pure():

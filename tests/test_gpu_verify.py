@@ -4,13 +4,19 @@ Greedy: n_accept and out_tok bit-exact.  Sampling: identical decisions on
 every sequence the oracle does not flag as a near tie (u within 1e-6 of p/q,
 or the inverse-CDF threshold within 5e-7 * R of a cumulative boundary); the
 flagged share is bounded (at a vocabulary of 128256 about 6 % of sequences
-fall in the window).
+fall in the window).  On a flagged sequence the GPU's decisions are checked
+too: they must equal the oracle's, or else each differing decision must be
+one that exact arithmetic admits within that same window (every accepted
+draft has u <= (1 + 1e-6) p/q, the reject has u >= (1 - 1e-6) p/q, and the
+emitted token's cumulative interval [C_{j-1}, C_j] of the exact residual
+reaches u R within 5e-7 R); the agreement count is reported.
 """
 
 import numpy as np
 import pytest
 
 import oracle
+import oracle.verify as ov
 import synth
 import quantization_self_speculation_amd as q
 from gpu_util import dev, host, say
@@ -28,6 +34,65 @@ def _logits(seed, B, gamma, V):
     rng = synth.make_rng(seed)
     tgt, drf = synth.verify_logits(rng, B, gamma, V)
     return rng, tgt, drf
+
+
+def _admissible(tgt, drf, d, ua, us, b, n, out):
+    """Whether the decisions (n, out) on sequence b are ones exact arithmetic
+    admits within the near-tie windows of the oracle (fp64 softmax)."""
+    gamma, V = d.shape[1], tgt.shape[2]
+    ra, rc = ov.NEAR_TIE_ACCEPT_REL, ov.NEAR_TIE_CDF_REL
+    if not (0 <= n <= gamma and 0 <= out[n] < V):
+        return False
+    if not (np.array_equal(out[:n], d[b, :n]) and np.all(out[n + 1:] == -1)):
+        return False
+    for i in range(n + (1 if n < gamma else 0)):
+        p = oracle.softmax64(tgt[b, i])
+        q_ = oracle.softmax64(drf[b, i])
+        x = int(d[b, i])
+        accepted = i < n
+        if q_[x] > 0:
+            ratio = p[x] / q_[x]
+            ok = ua[b, i] <= ratio * (1 + ra) if accepted else ua[b, i] >= ratio * (1 - ra)
+        else:
+            ok = (p[x] > 0) == accepted
+        if not ok:
+            return False
+    p = oracle.softmax64(tgt[b, n])
+    if n < gamma:
+        r = np.maximum(0.0, p - oracle.softmax64(drf[b, n]))
+        if r.sum() == 0:
+            r = p
+    else:
+        r = p
+    C = np.cumsum(r)
+    R = C[-1]
+    thr, w, j = float(us[b]) * R, rc * R, int(out[n])
+    lo = C[j - 1] if j > 0 else 0.0
+    if C[j] >= thr - w and lo <= thr + w:
+        return True
+    return thr >= R - w and j == int(np.nonzero(r > 0)[0][-1])   # the fallback
+
+
+def _check_sampling(tgt, drf, d, ua, us, n, out, max_flag=None):
+    """Unflagged sequences equal to the oracle; flagged ones equal or
+    admissible; returns (flagged, flagged and equal)."""
+    B = tgt.shape[0]
+    n_ref, out_ref, flag = oracle.verify_sample(tgt, drf, d, ua, us)
+    ok = ~flag
+    assert np.array_equal(n[ok], n_ref[ok])
+    assert np.array_equal(out[ok], out_ref[ok])
+    same = 0
+    for b in np.nonzero(flag)[0]:
+        if n[b] == n_ref[b] and np.array_equal(out[b], out_ref[b]):
+            same += 1
+        else:
+            assert _admissible(tgt, drf, d, ua, us, b, int(n[b]), out[b]), \
+                f"sequence {b}: decision ({n[b]}, {out[b].tolist()}) outside the near-tie window"
+    if max_flag is not None:
+        assert flag.sum() <= max_flag, f"{flag.sum()} near ties"
+    if flag.any():
+        say(f"  flagged {int(flag.sum())} of {B}, GPU equal to the oracle on {same}")
+    return int(flag.sum()), same
 
 
 @pytest.mark.parametrize("B,gamma,V", CASES)
@@ -65,13 +130,8 @@ def test_sampling_matches_oracle(B, gamma, V):
     d = synth.gumbel_drafts(rng, drf)
     ua = synth.uniforms(rng, (B, gamma))
     us = synth.uniforms(rng, (B,))
-    n_ref, out_ref, flag = oracle.verify_sample(tgt, drf, d, ua, us)
     n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
-    n, out = host(n), host(out)
-    ok = ~flag
-    assert flag.sum() <= max(1, B // 4), f"{flag.sum()} near ties"
-    assert np.array_equal(n[ok], n_ref[ok])
-    assert np.array_equal(out[ok], out_ref[ok])
+    _check_sampling(tgt, drf, d, ua, us, host(n), host(out), max_flag=max(1, B // 4))
 
 
 def test_sampling_forced_paths():
@@ -83,12 +143,10 @@ def test_sampling_forced_paths():
     us = synth.uniforms(rng, (B,))
     for ua_val in (0.0, 0.9999999):
         ua = np.full((B, gamma), ua_val, np.float32)
-        n_ref, out_ref, flag = oracle.verify_sample(tgt, drf, d, ua, us)
         n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
-        ok = ~flag
-        assert np.array_equal(host(n)[ok], n_ref[ok])
-        assert np.array_equal(host(out)[ok], out_ref[ok])
-    assert np.all(n_ref <= gamma)
+        _check_sampling(tgt, drf, d, ua, us, host(n), host(out))
+        if ua_val == 0.0:
+            assert np.all(host(n) == gamma)
 
 
 def test_sampling_identical_logits_falls_back_to_p():
@@ -101,11 +159,8 @@ def test_sampling_identical_logits_falls_back_to_p():
     d = synth.gumbel_drafts(rng, drf)
     ua = synth.uniforms(rng, (B, gamma))
     us = synth.uniforms(rng, (B,))
-    n_ref, out_ref, flag = oracle.verify_sample(tgt, drf, d, ua, us)
     n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
-    ok = ~flag
-    assert np.array_equal(host(n)[ok], n_ref[ok])
-    assert np.array_equal(host(out)[ok], out_ref[ok])
+    _check_sampling(tgt, drf, d, ua, us, host(n), host(out))
 
 
 @pytest.mark.parametrize("V", [1, 2, 3, 5, 6, 7])
@@ -126,11 +181,9 @@ def test_degenerate_vocabularies(V):
     d = synth.gumbel_drafts(rng, drf)
     ua = synth.uniforms(rng, (B, gamma))
     us = synth.uniforms(rng, (B,))
-    n_ref, out_ref, flag = oracle.verify_sample(tgt, drf, d, ua, us)
+    n_ref, out_ref, _ = oracle.verify_sample(tgt, drf, d, ua, us)
     n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
-    ok = ~flag
-    assert np.array_equal(host(n)[ok], n_ref[ok])
-    assert np.array_equal(host(out)[ok], out_ref[ok])
+    _check_sampling(tgt, drf, d, ua, us, host(n), host(out))
     if V == 1:
         assert np.all(n_ref == gamma) and np.all(out_ref == 0)
 
@@ -164,3 +217,26 @@ def test_verify_deterministic():
     a = [host(t) for t in q.verify(q.VERIFY_SAMPLE, *args)]
     b = [host(t) for t in q.verify(q.VERIFY_SAMPLE, *args)]
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_sampling_many_sequences_flagged_agreement():
+    """A larger sampling sweep at the Llama-3-8B vocabulary (8 calls of 32
+    sequences, gamma 4): decisions equal on every unflagged sequence, equal or
+    admissible on every flagged one, and the GPU agrees with the oracle on
+    most flagged sequences as well (the windows are several times the
+    kernels' error, so most near ties still fall the same way)."""
+    B, gamma, V = 32, 4, 128256
+    flagged = same = 0
+    for trial in range(8):
+        rng = synth.make_rng(38, trial)
+        tgt, drf = synth.verify_logits(rng, B, gamma, V)
+        d = synth.gumbel_drafts(rng, drf)
+        ua = synth.uniforms(rng, (B, gamma))
+        us = synth.uniforms(rng, (B,))
+        n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us))
+        f, e = _check_sampling(tgt, drf, d, ua, us, host(n), host(out))
+        flagged += f
+        same += e
+    say(f"  over 256 sequences: flagged {flagged}, GPU equal on {same}")
+    assert flagged <= 256 // 4
+    assert same >= flagged - max(1, flagged // 4)

@@ -69,8 +69,14 @@ def test_gemm_w4a8_parity(M, N, K, variant):
     W, X = _case(132, M, N, K)
     Wq, Ws = oracle.pack_w4(W)
     qa, s = oracle.quant_act8(X)
-    Y = host(q.gemm_w4a8(dev(qa), dev(s), dev_w(Wq), dev_s(Ws), variant=variant, N=N))
+    args = (dev(qa), dev(s), dev_w(Wq), dev_s(Ws))
+    Y = host(q.gemm_w4a8(*args, variant=variant, N=N))
     assert_close(Y, oracle.gemm_w4a8(qa, s, Wq, Ws), what="w4a8")
+    # the same family with its int32 group partials stored: P exact, Y bitwise
+    # the same as without them
+    Yp, P = q.gemm_w4a8(*args, variant=variant, partials=True, N=N)
+    assert np.array_equal(host(P), oracle.w4a8_partials(qa, Wq))
+    assert np.array_equal(host(Yp).view(np.uint32), Y.view(np.uint32))
 
 
 def test_gemm_w4a8_row_invariance():
