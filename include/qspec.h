@@ -32,7 +32,8 @@
  *  - Calls never abort or exit the process.  They are thread-safe.  Global
  *    state: a per-device cache of the device check, a process-wide atomic
  *    call counter that tags the split-K arrival counters in a GEMM's
- *    workspace (so a workspace never needs clearing).
+ *    workspace (so a workspace never needs clearing), and the per-device
+ *    scratch array of qspec_verify_noalloc (read its note).
  *  - Non-finite inputs (NaN/Inf weights, activations or logits) are not
  *    supported: results are unspecified, but every kernel still terminates.
  */
@@ -307,6 +308,29 @@ qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V,
                           const float* u_sample, int32_t* n_accept,
                           int32_t* out_tok, void* ws, size_t ws_bytes,
                           qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * qspec_verify_noalloc -- qspec_verify without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * modes, validation and results as qspec_verify (bitwise); the scratch the
+ * verify kernels need lives in a fixed array of QSPEC_VERIFY_NOALLOC_SCRATCH
+ * bytes per device, part of the library's code object and held until the
+ * process ends.  Sizes whose qspec_workspace_bytes(QSPEC_OP_VERIFY, B, gamma,
+ * V) exceeds it are rejected with QSPEC_ERR_WORKSPACE before anything is
+ * enqueued (B = 256, gamma = 8, V = 152064 needs about 1.4 MiB).  Nothing is
+ * allocated: no hipMalloc, no hipFree.  Every call on one device shares that
+ * device's array and leaves its contents behind (no call depends on them);
+ * calls that overlap in time on one device -- on different streams, or from
+ * different threads -- race on the array and must be serialised by the
+ * caller.
+ * ------------------------------------------------------------------------- */
+#define QSPEC_VERIFY_NOALLOC_SCRATCH (8u << 20)
+qspec_status qspec_verify_noalloc(int mode, int64_t B, int gamma, int64_t V,
+                                  const int32_t* draft_tok, const float* draft_logits,
+                                  const float* target_logits, const float* u_accept,
+                                  const float* u_sample, int32_t* n_accept,
+                                  int32_t* out_tok, qspec_stream stream);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     quant_act8,
     gemm_w4a16,
     verify,
+    verify_noalloc,
     workspace_bytes,
     GEMM_AUTO,
     GEMM_GEMV,

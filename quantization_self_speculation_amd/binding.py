@@ -64,6 +64,7 @@ def lib():
             "qspec_quant_act8": (I, [P, I64, I64, P, P, P]),
             "qspec_gemm_w4a8": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
             "qspec_verify": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P, SZ, P]),
+            "qspec_verify_noalloc": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P]),
             "qspec_embed": (I, [P, I64, I64, P, I64, P, P]),
             "qspec_add_rmsnorm": (I, [P, I64, P, I64, I64, I64, ctypes.c_double, P, P]),
             "qspec_rope_kv": (I, [P, I64, I, I, P, P, ctypes.c_double, P, P, P, I64, I64, P]),
@@ -310,6 +311,32 @@ def verify(mode, target_logits, draft_tok, draft_logits=None, u_accept=None, u_s
     _check(lib().qspec_verify(mode, B, gamma, V, _ptr(draft_tok), _ptr(draft_logits),
                               _ptr(target_logits), _ptr(u_accept), _ptr(u_sample), _ptr(n_accept),
                               _ptr(out_tok), _ptr(w), wb, _stream()), "qspec_verify")
+    return n_accept, out_tok
+
+
+def verify_noalloc(mode, target_logits, draft_tok, draft_logits=None, u_accept=None,
+                   u_sample=None, n_accept=None, out_tok=None):
+    """verify() on the library's fixed per-device scratch (no workspace);
+    the outputs must be given for a call that may not allocate."""
+    _need(target_logits, "target_logits", torch.float32)
+    B, G1, V = target_logits.shape
+    gamma = G1 - 1
+    _need(draft_tok, "draft_tok", torch.int32, (B, gamma))
+    if mode == VERIFY_SAMPLE:
+        _need(draft_logits, "draft_logits", torch.float32, (B, gamma, V))
+        _need(u_accept, "u_accept", torch.float32, (B, gamma))
+        _need(u_sample, "u_sample", torch.float32, (B,))
+    dev = target_logits.device
+    if n_accept is None:
+        n_accept = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_tok is None:
+        out_tok = torch.empty((B, G1), dtype=torch.int32, device=dev)
+    _need(n_accept, "n_accept", torch.int32, (B,))
+    _need(out_tok, "out_tok", torch.int32, (B, G1))
+    _check(lib().qspec_verify_noalloc(mode, B, gamma, V, _ptr(draft_tok), _ptr(draft_logits),
+                                      _ptr(target_logits), _ptr(u_accept), _ptr(u_sample),
+                                      _ptr(n_accept), _ptr(out_tok), _stream()),
+           "qspec_verify_noalloc")
     return n_accept, out_tok
 
 

@@ -340,6 +340,25 @@ qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V, const int32
                     "verify launch");
 }
 
+qspec_status qspec_verify_noalloc(int mode, int64_t B, int gamma, int64_t V,
+                                  const int32_t* draft_tok, const float* draft_logits,
+                                  const float* target_logits, const float* u_accept,
+                                  const float* u_sample, int32_t* n_accept, int32_t* out_tok,
+                                  qspec_stream stream) {
+  QS_TRY(check_verify(mode, B, gamma, V, draft_tok, draft_logits, target_logits, u_accept,
+                      u_sample, n_accept, out_tok));
+  const size_t need = verify_ws_bytes(B, gamma, V);
+  QS_REQUIRE(need <= kVerifyScratchBytes, QSPEC_ERR_WORKSPACE,
+             "these sizes need %zu bytes of scratch; the fixed scratch of "
+             "qspec_verify_noalloc holds %zu (call qspec_verify with a workspace)",
+             need, kVerifyScratchBytes);
+  QS_TRY(device_check());
+  return hip_result(launch_verify_noalloc(mode, B, gamma, V, draft_tok, draft_logits,
+                                          target_logits, u_accept, u_sample, n_accept, out_tok,
+                                          (hipStream_t)stream),
+                    "verify_noalloc launch");
+}
+
 }  // extern "C"
 
 namespace {

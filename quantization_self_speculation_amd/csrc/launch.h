@@ -37,6 +37,13 @@ hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, con
                        void* ws, hipStream_t s);
 
 size_t verify_ws_bytes(int64_t B, int gamma, int64_t V);
+// the fixed per-device scratch of the allocation-free verify entry point
+constexpr size_t kVerifyScratchBytes = (size_t)QSPEC_VERIFY_NOALLOC_SCRATCH;
+hipError_t launch_verify_noalloc(int mode, int64_t B, int gamma, int64_t V,
+                                 const int32_t* draft_tok, const float* draft_logits,
+                                 const float* target_logits, const float* u_accept,
+                                 const float* u_sample, int32_t* n_accept, int32_t* out_tok,
+                                 hipStream_t s);
 hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_t* draft_tok,
                          const float* draft_logits, const float* target_logits,
                          const float* u_accept, const float* u_sample, int32_t* n_accept,

@@ -15,10 +15,23 @@
 //             accept tests) -> residual chunk sums -> inverse-CDF select
 // Chunks are reduced in fixed order (no atomics): the same inputs give the
 // same bits.
+#include <atomic>
+#include <mutex>
+
 #include "launch.h"
 
 namespace qspec {
 namespace {
+
+// Scratch of qspec_verify_noalloc, for callers that cannot allocate: one
+// array per device, allocated with the code object and held until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in); the device address comes from hipGetSymbolAddress,
+// once per device, and is cached below.
+static __device__ __align__(256) uint8_t scratch[kVerifyScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[64];
 
 constexpr int kQPC = 2048;        // float4 quads per pass-1 chunk (8192 logits)
 constexpr int kRCW = 2048;        // logits per residual chunk (8 per thread)
@@ -525,6 +538,44 @@ VerifyLayout layout(int64_t B, int gamma, int64_t V) {
 }  // namespace
 
 size_t verify_ws_bytes(int64_t B, int gamma, int64_t V) { return layout(B, gamma, V).total; }
+
+// The device address of this device's scratch array, looked up once per
+// device with that device current.
+hipError_t verify_scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+// qspec_verify on this device's scratch array.  The kernels write every
+// scratch element they read later in the same call, so nothing is cleared;
+// calls that overlap in time on one device share the array and race.
+hipError_t launch_verify_noalloc(int mode, int64_t B, int gamma, int64_t V,
+                                 const int32_t* draft_tok, const float* draft_logits,
+                                 const float* target_logits, const float* u_accept,
+                                 const float* u_sample, int32_t* n_accept, int32_t* out_tok,
+                                 hipStream_t s) {
+  if (verify_ws_bytes(B, gamma, V) > kVerifyScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = verify_scratch_ptr(&ws);
+  if (e != hipSuccess) return e;
+  return launch_verify(mode, B, gamma, V, draft_tok, draft_logits, target_logits, u_accept,
+                       u_sample, n_accept, out_tok, ws, s);
+}
 
 hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_t* draft_tok,
                          const float* draft_logits, const float* target_logits,
