@@ -82,8 +82,8 @@ class Decode:
                 Xs=torch.empty((M4,), dtype=torch.float32, device=dev),
                 Y4=torch.empty((M4, N), dtype=torch.float32, device=dev),
                 Y16=torch.empty((M16, N), dtype=torch.float32, device=dev),
-                ws4=torch.empty(max(1, q.workspace_bytes(1, M4, N, K)), dtype=torch.uint8, device=dev),
-                ws16=torch.empty(max(1, q.workspace_bytes(2, M16, N, K)), dtype=torch.uint8, device=dev),
+                ws4=torch.zeros(max(1, q.workspace_bytes(1, M4, N, K)), dtype=torch.uint8, device=dev),
+                ws16=torch.zeros(max(1, q.workspace_bytes(2, M16, N, K)), dtype=torch.uint8, device=dev),
             ))
         tgt, drf = synth.verify_logits(rng, B, gamma, V)
         d = synth.gumbel_drafts(rng, drf)
@@ -254,7 +254,7 @@ def measure_batch_sweep(torch, q, wl, reps=10, Ms=(8, 16, 32, 64, 128, 256, 512)
             Xq = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda:0")
             Xs = torch.empty((M,), dtype=torch.float32, device="cuda:0")
             Y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
-            ws = torch.empty(max(1, q.workspace_bytes(1, M, N, K), q.workspace_bytes(2, M, N, K)),
+            ws = torch.zeros(max(1, q.workspace_bytes(1, M, N, K), q.workspace_bytes(2, M, N, K)),
                              dtype=torch.uint8, device="cuda:0")
             cps = p["copies"]
 
@@ -339,7 +339,7 @@ def measure_w4a8_tier(torch, q, wl, reps=10):
         N, K = p["N"], p["K"]
         X8 = p["X16"][:8].contiguous()
         Y = torch.empty((8, N), dtype=torch.float32, device="cuda:0")
-        ws = torch.empty(max(1, q.workspace_bytes(1, 8, N, K), q.workspace_bytes(2, 8, N, K),
+        ws = torch.zeros(max(1, q.workspace_bytes(1, 8, N, K), q.workspace_bytes(2, 8, N, K),
                              q.workspace_bytes(4, 8, N, K)), dtype=torch.uint8, device="cuda:0")
         q4 = (torch.empty((8, K // 2), dtype=torch.uint8, device="cuda:0"),
               torch.empty((8,), dtype=torch.float32, device="cuda:0"))
@@ -395,7 +395,7 @@ def measure_decode_gemv(torch, q, wl, reps=10):
         N, K = p["N"], p["K"]
         X = p["X16"][:5].contiguous()
         Y = torch.empty((5, N), dtype=torch.float32, device="cuda:0")
-        ws = torch.empty(max(1, q.workspace_bytes(2, 5, N, K)), dtype=torch.uint8, device="cuda:0")
+        ws = torch.zeros(max(1, q.workspace_bytes(2, 5, N, K)), dtype=torch.uint8, device="cuda:0")
         cps = p["copies"]
 
         def fn():
@@ -413,7 +413,7 @@ def measure_decode_gemv(torch, q, wl, reps=10):
         del W
     X = torch.from_numpy(synth.activations(rng, 1, K).view(np.int16)).view(torch.bfloat16).to("cuda:0")
     Y = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(max(1, q.workspace_bytes(2, 1, N, K)), dtype=torch.uint8, device="cuda:0")
+    ws = torch.zeros(max(1, q.workspace_bytes(2, 1, N, K)), dtype=torch.uint8, device="cuda:0")
 
     def fh():
         for Wq, Ws in cps:
@@ -443,7 +443,7 @@ def measure_llama_verify_batch(torch, q, reps=5):
         cps = [(Wq, Ws)] + [(Wq.clone(), Ws.clone()) for _ in range(nc - 1)]
         X = torch.randn((288, K), device="cuda:0").to(torch.bfloat16)
         Y = torch.empty((288, N), dtype=torch.float32, device="cuda:0")
-        ws = torch.empty(max(1, q.workspace_bytes(2, 288, N, K)), dtype=torch.uint8, device="cuda:0")
+        ws = torch.zeros(max(1, q.workspace_bytes(2, 288, N, K)), dtype=torch.uint8, device="cuda:0")
         r = {}
         for M in (160, 288):
             Xm = X[:M].contiguous()

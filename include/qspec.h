@@ -32,8 +32,9 @@
  *  - Calls never abort or exit the process.  They are thread-safe.  Global
  *    state: a per-device cache of the device check, a process-wide atomic
  *    call counter that tags the split-K arrival counters in a GEMM's
- *    workspace (so a workspace never needs clearing), and the per-device
- *    scratch array of qspec_verify_noalloc (read its note).
+ *    workspace (a counter left by a call that never finished is not taken
+ *    for one of the current call), and the per-device scratch array of
+ *    qspec_verify_noalloc (read its note).
  *  - Non-finite inputs (NaN/Inf weights, activations or logits) are not
  *    supported: results are unspecified, but every kernel still terminates.
  */
@@ -108,7 +109,13 @@ qspec_status qspec_device_check(void);
  *   QSPEC_OP_GEMM_W4A4 / _W4A16 / _W4A8:      (M, N, K)
  *   QSPEC_OP_VERIFY:                           (B, gamma, V)
  * The answer is the maximum over all variants and modes, so one workspace
- * sized by it serves every call of that op with sizes no larger. */
+ * sized by it serves every call of that op with sizes no larger.
+ * A GEMM workspace must hold zeros the first time it is used (hipMemset it
+ * once): the k-split's arrival counters live in it, and no tag can tell
+ * leftover data from a counter reliably.  Every GEMM call leaves its
+ * counters at zero again, so a workspace is reused without clearing by any
+ * later GEMM call on the same stream (calls that overlap in time must not
+ * share one).  A verify workspace needs no initialisation. */
 size_t qspec_workspace_bytes(int op, int64_t a, int64_t b, int64_t c);
 
 /* ---------------------------------------------------------------------------
@@ -201,7 +208,8 @@ qspec_status qspec_quant_act_rot(const uint16_t* X, int64_t M, int64_t K,
  *   variant: QSPEC_GEMM_AUTO, _SKINNY, _TILED or _STREAM (M <= 16); GEMV is
  *   W4A16-only.
  *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_GEMM_W4A4,M,N,K)
- *   bytes (NULL allowed when that is 0).
+ *   bytes (NULL allowed when that is 0), zero-filled before its first use
+ *   (read qspec_workspace_bytes).
  * ------------------------------------------------------------------------- */
 qspec_status qspec_gemm_w4a4(const uint8_t* Xq, const float* Xs,
                              const uint8_t* Wq, const uint16_t* Ws,
@@ -264,7 +272,8 @@ qspec_status qspec_gemm_w4a8(const int8_t* Xq, const float* Xs,
  *   X  [M][K] bf16 bits (in);  Wq [Np][K/2], Ws [Np][K/128] (tiled, from
  *   qspec_pack_w4, Np = ceil(N/16)*16);  Y [M][N] fp32 (out).
  *   variant: QSPEC_GEMM_AUTO, _GEMV, _SKINNY, _TILED or _STREAM (M <= 16).
- *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_GEMM_W4A16,M,N,K).
+ *   ws/ws_bytes: scratch of qspec_workspace_bytes(QSPEC_OP_GEMM_W4A16,M,N,K),
+ *   zero-filled before its first use (read qspec_workspace_bytes).
  * ------------------------------------------------------------------------- */
 qspec_status qspec_gemm_w4a16(const uint16_t* X, const uint8_t* Wq,
                               const uint16_t* Ws, int64_t M, int64_t N,

@@ -256,7 +256,8 @@ def selfspec_greedy(model, prompts, n_gen, gamma, trace=None):
     kv, stats) with stats = dict(accepted, drafted, rounds).  With a list
     `trace`, every round appends dict(act = the active sequences, drafts
     [nA, gamma], n_accept [nA], draft_margin [nA, gamma] = the relative top-2
-    margin of the draft logits behind each drafted token)."""
+    margin of the draft logits behind each drafted token, verify_margin
+    [nA, gamma + 1] = the same for the verify logits at each position)."""
     B, P = prompts.shape
     kv = KVCache(model.cfg, B, kv_capacity(P, n_gen, gamma))
     last = prefill(model, kv, prompts)
@@ -282,7 +283,8 @@ def selfspec_greedy(model, prompts, n_gen, gamma, trace=None):
         n, out = verify_greedy(logits.reshape(nA, gamma + 1, -1), vtok[:, 1:].copy())
         if trace is not None:
             trace.append(dict(act=act.copy(), drafts=vtok[:, 1:].copy(), n_accept=n.copy(),
-                              draft_margin=dmargin))
+                              draft_margin=dmargin,
+                              verify_margin=top2_margin(logits).reshape(nA, gamma + 1)))
         for i, b in enumerate(act):
             k = int(n[i])
             gen[b].extend(int(t) for t in out[i, :k + 1])

@@ -74,6 +74,9 @@ def lib():
             "qspec_argmax": (I, [P, I64, I64, P, I64, P]),
             "qspec_spec_prepare": (I, [I, I64, I, I, P, P, P, P, P, P, P]),
             "qspec_spec_commit": (I, [I64, I, P, P, P, P, I64, P, I64, P, I, P, P]),
+            "qspec_probe_read": (I, [P, I64, I, I, P, P]),
+            "qspec_probe_mfma": (I, [I, I, I, P, P]),
+            "qspec_probe_empty": (I, [P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -124,11 +127,13 @@ def workspace_bytes(op, a, b, c):
 
 
 def _workspace(nbytes, device, ws):
+    """the caller's workspace, or a zero-filled one for this call (a GEMM
+    workspace must hold zeros when first used; the calls keep it that way)"""
     if nbytes == 0:
         return None, 0
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws, ws.numel() * ws.element_size()
-    w = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    w = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return w, nbytes
 
 
@@ -451,3 +456,20 @@ def spec_commit(B, gamma, n_accept, out_tok, len_, vtok, vtok_stride, gen, n_gen
                                    _ptr(vtok), int(vtok_stride), _ptr(gen), int(gen.shape[1]),
                                    _ptr(n_gen), int(max_gen), _ptr(stats), _stream()),
            "qspec_spec_commit")
+
+
+# ---------------------------------------------------------------- ceiling probes
+def probe_read(buf, blocks, unroll, sink):
+    """read every byte of the device tensor `buf` once (see qspec_probe.h)"""
+    _check(lib().qspec_probe_read(_ptr(buf), buf.numel() * buf.element_size(), int(blocks),
+                                  int(unroll), _ptr(sink), _stream()), "qspec_probe_read")
+
+
+def probe_mfma(kind, blocks, iters, sink):
+    """independent MFMA chains: kind 0 int8 16x16x64, 1 bf16 16x16x32"""
+    _check(lib().qspec_probe_mfma(int(kind), int(blocks), int(iters), _ptr(sink), _stream()),
+           "qspec_probe_mfma")
+
+
+def probe_empty():
+    _check(lib().qspec_probe_empty(_stream()), "qspec_probe_empty")

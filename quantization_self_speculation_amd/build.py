@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqspec.so")
 
-SOURCES = ["capi.cpp", "pack_quant.hip", "gemm.hip", "verify.hip", "harness.hip"]
+SOURCES = ["capi.cpp", "pack_quant.hip", "gemm.hip", "verify.hip", "harness.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -9,6 +9,7 @@
 
 #include "launch.h"
 #include "qspec_harness.h"
+#include "qspec_probe.h"
 
 namespace qspec {
 
@@ -540,6 +541,36 @@ qspec_status qspec_spec_commit(int64_t B, int gamma, const int32_t* n_accept,
   return hip_result(launch_spec_commit(B, gamma, n_accept, out_tok, len, vtok, vtok_stride, gen,
                                        gen_cap, n_gen, max_gen, stats, (hipStream_t)stream),
                     "spec_commit launch");
+}
+
+// ---------------------------------------------------------------- ceiling probes
+qspec_status qspec_probe_read(const void* buf, int64_t bytes, int blocks, int unroll,
+                              uint32_t* sink, qspec_stream stream) {
+  QS_REQUIRE(bytes >= 16 && bytes % 16 == 0, QSPEC_ERR_SHAPE,
+             "bytes must be a positive multiple of 16");
+  QS_REQUIRE(blocks >= 1 && blocks <= (1 << 20), QSPEC_ERR_SHAPE, "need 1 <= blocks <= 2^20");
+  QS_REQUIRE(unroll == 1 || unroll == 2 || unroll == 4 || unroll == 8 || unroll == 16,
+             QSPEC_ERR_UNSUPPORTED, "unroll must be 1, 2, 4, 8 or 16");
+  QS_PTR(buf);
+  QS_EPTR(sink);
+  QS_TRY(device_check());
+  return hip_result(launch_probe_read(buf, bytes, blocks, unroll, sink, (hipStream_t)stream),
+                    "probe_read launch");
+}
+
+qspec_status qspec_probe_mfma(int kind, int blocks, int iters, float* sink, qspec_stream stream) {
+  QS_REQUIRE(kind == 0 || kind == 1, QSPEC_ERR_UNSUPPORTED, "kind must be 0 or 1");
+  QS_REQUIRE(blocks >= 1 && blocks <= (1 << 20) && iters >= 1, QSPEC_ERR_SHAPE,
+             "need 1 <= blocks <= 2^20 and iters >= 1");
+  QS_EPTR(sink);
+  QS_TRY(device_check());
+  return hip_result(launch_probe_mfma(kind, blocks, iters, sink, (hipStream_t)stream),
+                    "probe_mfma launch");
+}
+
+qspec_status qspec_probe_empty(qspec_stream stream) {
+  QS_TRY(device_check());
+  return hip_result(launch_probe_empty((hipStream_t)stream), "probe_empty launch");
 }
 
 }  // extern "C"

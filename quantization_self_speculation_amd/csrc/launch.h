@@ -49,6 +49,12 @@ hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_
                          const float* u_accept, const float* u_sample, int32_t* n_accept,
                          int32_t* out_tok, void* ws, hipStream_t s);
 
+// ceiling probes (probe.hip)
+hipError_t launch_probe_read(const void* buf, int64_t bytes, int blocks, int unroll,
+                             uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_mfma(int kind, int blocks, int iters, float* sink, hipStream_t s);
+hipError_t launch_probe_empty(hipStream_t s);
+
 // decoder kernels of the end-to-end loop (harness.hip)
 constexpr int kHarnessHeadDim = 128;
 constexpr int64_t kHarnessMaxCap = 3968;  // attention scores fit 64 KiB of LDS

@@ -100,7 +100,7 @@ class Decoder:
                 _, _, N, K = W
                 ws = max(ws, b.workspace_bytes(b.OP_GEMM_W4A16, M, N, K),
                          b.workspace_bytes(b.OP_GEMM_W4A4, M, N, K))
-        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(ws, dtype=torch.uint8, device=dev)   # zero before first use
         self.wsv = torch.empty(max(1, b.workspace_bytes(b.OP_VERIFY, B, max(gamma, 1), cfg.vocab)),
                                dtype=torch.uint8, device=dev)
         # row descriptors and round state
@@ -274,6 +274,9 @@ class Decoder:
             # the pure step keeps each sequence's last token at vtok[b] (row
             # stride 1); the prefill commit wrote it with the round's stride
             self.vtok[:self.B].copy_(self.first)
+        # the round statistics count decode rounds only (the prefill commit
+        # counts its rows as active)
+        self.stats[:2].zero_()
         e1.record()
         rounds = 0
         if speculative:

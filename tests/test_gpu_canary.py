@@ -3,7 +3,8 @@
 Each call is made through ctypes with output buffers of exactly the size
 include/qspec.h states (Wq [Np][K/2], Ws [Np][K/128] with Np = ceil(N/16)*16;
 Y [M][N]; P [M][N][K/128]; Xq, Xs; n_accept, out_tok; the workspace of
-qspec_workspace_bytes), each followed by 4 KiB of poisoned slack.  After the
+qspec_workspace_bytes, zero-filled for a GEMM), each followed by 4 KiB of
+poisoned slack.  After the
 call the slack must hold the poison, the inputs must be unchanged, and the
 outputs must match the oracle -- over ragged M and N in every GEMM family of
 every mode, the quantizers, the rotations and both verify modes.
@@ -57,7 +58,9 @@ def _stream():
 
 
 def _ws(op, a, b, c):
-    return Guarded(max(q.workspace_bytes(op, a, b, c), 0), fill=0x3C)
+    # a GEMM workspace holds zeros when first used (the header's contract);
+    # a verify workspace may hold anything
+    return Guarded(max(q.workspace_bytes(op, a, b, c), 0), fill=0x3C if op == 3 else 0)
 
 
 def _pack(W):

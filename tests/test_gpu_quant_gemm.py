@@ -555,15 +555,15 @@ def test_graph_replays_match_eager():
     Xq, Xs = q.quant_act(X4)
     Y4 = torch.empty((M4, N), dtype=torch.float32, device="cuda")
     Y16 = torch.empty((M16, N), dtype=torch.float32, device="cuda")
-    ws4 = torch.empty(q.workspace_bytes(1, M4, N, K), dtype=torch.uint8, device="cuda")
-    ws16 = torch.empty(q.workspace_bytes(2, M16, N, K), dtype=torch.uint8, device="cuda")
+    ws4 = torch.zeros(q.workspace_bytes(1, M4, N, K), dtype=torch.uint8, device="cuda")
+    ws16 = torch.zeros(q.workspace_bytes(2, M16, N, K), dtype=torch.uint8, device="cuda")
     # the W4A8 tier and the bf16 output on the same split-K shape, each with
     # a workspace of its own
     X8q, X8s = q.quant_act8(X4)
     Y8 = torch.empty((M4, N), dtype=torch.float32, device="cuda")
     Yb = torch.empty((M4, N), dtype=torch.bfloat16, device="cuda")
-    ws8 = torch.empty(q.workspace_bytes(4, M4, N, K), dtype=torch.uint8, device="cuda")
-    wsb = torch.empty(q.workspace_bytes(1, M4, N, K), dtype=torch.uint8, device="cuda")
+    ws8 = torch.zeros(q.workspace_bytes(4, M4, N, K), dtype=torch.uint8, device="cuda")
+    wsb = torch.zeros(q.workspace_bytes(1, M4, N, K), dtype=torch.uint8, device="cuda")
 
     def body():
         q.quant_act(X4, Xq, Xs)
@@ -599,13 +599,24 @@ def test_graph_replays_match_eager():
         assert np.array_equal(host(Y8).view(np.uint32), e8.view(np.uint32)), rep
 
 
-def test_fresh_garbage_workspace():
-    """A workspace full of arbitrary bytes (not zeroed) still gives the right
-    split-K result: the arrival counters are tagged with a per-call epoch."""
-    M, N, K = 8, 3584, 18944
-    W, X = _case(20, M, N, K)
-    Wq, Ws = oracle.pack_w4(W)
-    nb = q.workspace_bytes(2, M, N, K)
-    ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda")
-    Y = q.gemm_w4a16(dev_bf16(X), dev_w(Wq), dev_s(Ws), variant=q.GEMM_SKINNY, ws=ws, N=N)
-    assert_close(host(Y), oracle.gemm_w4a16(X, Wq, Ws))
+def test_workspace_reused_across_shapes():
+    """One zero-filled workspace serves a run of k-split calls of different
+    shapes and modes (different counter counts and slice counts): each call
+    leaves its arrival counters at zero, so the next finds them clear,
+    whatever partials the earlier calls left behind."""
+    shapes = [(8, 3584, 18944), (40, 4608, 3584), (5, 1028, 1024), (16, 2048, 5632)]
+    nb = max(q.workspace_bytes(op, M, N, K) for (M, N, K) in shapes for op in (1, 2))
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    cases = []
+    for i, (M, N, K) in enumerate(shapes):
+        W, X = _case(20 + i, M, N, K)
+        Wq, Ws = oracle.pack_w4(W)
+        Xq, Xs = oracle.quant_act(X)
+        cases.append((M, N, K, X, Xq, Xs, Wq, Ws, dev_w(Wq), dev_s(Ws)))
+    for rep in range(2):
+        for (M, N, K, X, Xq, Xs, Wq, Ws, Wq_d, Ws_d) in cases:
+            say(f"workspace reuse rep={rep} M={M} N={N} K={K}")
+            Y = q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=q.GEMM_SKINNY, ws=ws, N=N)
+            assert_close(host(Y), oracle.gemm_w4a16(X, Wq, Ws), what="w4a16 reused ws")
+            Y = q.gemm_w4a4(dev(Xq), dev(Xs), Wq_d, Ws_d, variant=q.GEMM_SKINNY, ws=ws, N=N)
+            assert_close(host(Y), oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4 reused ws")
