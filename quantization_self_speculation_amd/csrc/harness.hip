@@ -199,20 +199,52 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------------ attention
-// One 256-thread block per (row, kv head); wave w serves the query heads
-// g*grp + w, w+4, ...  Each lane scores keys t = lane, lane+64, ... (a full
-// 128-term dot product, fp32, fixed order), the scores sit in LDS; softmax
-// with the max subtracted; then lane l accumulates output dims 2l, 2l+1 over
-// t in increasing order.  Output bf16.
+// One block of kAttnWaves wavefronts per (row, kv head): the block serves all
+// grp = H / Hkv query heads of the kv head, kAttnHeads at a time, so each key
+// and value row is read once for all of them.  The T = pos + 1 keys are
+// split into kAttnWaves contiguous ranges (a function of T only); a
+// wavefront walks its range in chunks of up to kAttnChunk keys, issuing all
+// of a chunk's key and value loads at once, and keeps a running softmax:
+//   scores: 16 lanes share a key (lane l reads dims 8 (l % 16) .. + 7 of key
+//     4 j + l / 16, one coalesced 16-byte load), each lane's 8 products are
+//     summed in order and the 16 partials by fixed DPP lane moves, fp32; the
+//     first lane of the 16 keeps the score;
+//   per chunk: its max m', the running max m = max(m, m'), the old sums
+//     scaled by exp(m_old - m), p = exp(s - m), sum of p in a fixed order,
+//     and lane l accumulates p * v for dims 2l, 2l+1 over the chunk's keys
+//     in increasing order;
+//   the wavefronts' (m, sum, o) are merged in wave order.
+// Every step depends on T alone, so a row's output is the same whatever
+// other rows share the launch.  Output bf16.
 constexpr int kHeadDim = 128;
+constexpr int kAttnWaves = 8;
 
-__global__ __launch_bounds__(256) void attention_kernel(const float* __restrict__ q,
-                                                        const uint16_t* __restrict__ kc,
-                                                        const uint16_t* __restrict__ vc, int H,
-                                                        int Hkv, const int32_t* __restrict__ seq,
-                                                        const int32_t* __restrict__ pos, int64_t B,
-                                                        int64_t cap, uint16_t* __restrict__ out) {
-  extern __shared__ float lds[];  // [4][kHeadDim + cap]
+// Sum over the 16 lanes of a DPP row, by VALU lane moves (no LDS round trip):
+// swap neighbours, swap pairs (now every lane holds its quad's sum), then add
+// the quads 4 and 8 lanes around the row.  Every lane ends with the row's sum;
+// the association differs between quads, so a caller keeps the value of one
+// fixed lane (it is then a fixed function of the 16 inputs).
+__device__ __forceinline__ float sum16_dpp(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row rotate 4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row rotate 8
+  return v;
+}
+constexpr int kAttnHeads = 4;    // query heads per pass
+constexpr int kAttnChunk = 64;   // keys per wavefront chunk (all loads in flight)
+constexpr int kAttnQuads = kAttnChunk / 4;
+
+__global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
+    const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    int H, int Hkv, const int32_t* __restrict__ seq, const int32_t* __restrict__ pos, int64_t B,
+    int64_t cap, uint16_t* __restrict__ out) {
+  // LDS: per wavefront, the chunk's scores [kAttnHeads][kAttnChunk]; then the
+  // wavefronts' results: o [kAttnWaves][kAttnHeads][128], m and sum
+  // [kAttnWaves][kAttnHeads]
+  __shared__ float sc[kAttnWaves][kAttnHeads][kAttnChunk];
+  __shared__ float po[kAttnWaves][kAttnHeads][kHeadDim];
+  __shared__ float pm[kAttnWaves][kAttnHeads], pl[kAttnWaves][kAttnHeads];
   const int64_t m = blockIdx.x;
   const int g = blockIdx.y;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -223,74 +255,138 @@ __global__ __launch_bounds__(256) void attention_kernel(const float* __restrict_
   const int T = ok ? pos[m] + 1 : 0;
   const int64_t bb = ok ? b : 0;
   const uint16_t* K = kc + (bb * Hkv + g) * cap * kHeadDim;
-  const uint16_t* Vv = vc + (bb * Hkv + g) * cap * kHeadDim;
-  float* qs = lds + w * (kHeadDim + cap);
-  float* sc = qs + kHeadDim;
+  const uint32_t* Vw = reinterpret_cast<const uint32_t*>(vc + (bb * Hkv + g) * cap * kHeadDim) + lane;
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
-  for (int hh = w; hh < grp; hh += 4) {
-    const int h = g * grp + hh;
-    const float* qr = q + m * (H * kHeadDim) + h * kHeadDim;
-    qs[lane] = qr[lane];
-    qs[lane + 64] = qr[lane + 64];
+  // this wave's keys [t0, t1): contiguous, whole quads except the last
+  const int per = ((T + 3) / 4 + kAttnWaves - 1) / kAttnWaves;
+  const int t0 = min(T, w * per * 4), t1 = min(T, t0 + per * 4);
+  const int kk = lane >> 4, dc = (lane & 15) * 8;
+  float* scw = &sc[w][0][0];
+  auto wave_sync = [] {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float mx = -INFINITY;
-    for (int t = lane; t < T; t += 64) {
-      const uint16_t* kr = K + (int64_t)t * kHeadDim;
-      float acc = 0.f;
-#pragma unroll 4
-      for (int j = 0; j < kHeadDim; j += 8) {
-        const uint4 p = *reinterpret_cast<const uint4*>(kr + j);
-        const uint32_t wv[4] = {p.x, p.y, p.z, p.w};
+  };
+
+  for (int h0 = 0; h0 < grp; h0 += kAttnHeads) {
+    const int nh = min(kAttnHeads, grp - h0);
+    float rm[kAttnHeads], rl[kAttnHeads], o0[kAttnHeads], o1[kAttnHeads];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc = fmaf(qs[j + 2 * i], __uint_as_float(wv[i] << 16), acc);
-          acc = fmaf(qs[j + 2 * i + 1], __uint_as_float(wv[i] & 0xFFFF0000u), acc);
+    for (int hh = 0; hh < kAttnHeads; ++hh) {
+      rm[hh] = -INFINITY;
+      rl[hh] = o0[hh] = o1[hh] = 0.f;
+    }
+    float qf[kAttnHeads][8];
+    for (int c0 = t0; c0 < t1; c0 += kAttnChunk) {
+      const int len = min(kAttnChunk, t1 - c0);
+      // every key and value load of the chunk, then (first chunk) the queries
+      uint4 kr[kAttnQuads];
+      uint32_t vv[kAttnChunk];
+#pragma unroll
+      for (int j = 0; j < kAttnQuads; ++j)
+        if (4 * j < len)  // uniform
+          kr[j] = *reinterpret_cast<const uint4*>(K + (int64_t)min(c0 + 4 * j + kk, t1 - 1) * kHeadDim + dc);
+#pragma unroll
+      for (int i = 0; i < kAttnChunk; ++i)
+        if (i < len) vv[i] = Vw[(int64_t)(c0 + i) * (kHeadDim / 2)];
+      if (c0 == t0) {
+#pragma unroll
+        for (int hh = 0; hh < kAttnHeads; ++hh) {
+          const float* qr = q + m * (H * kHeadDim) +
+                            (int64_t)(g * grp + h0 + min(hh, nh - 1)) * kHeadDim + dc;
+          const float4 x0 = *reinterpret_cast<const float4*>(qr);
+          const float4 x1 = *reinterpret_cast<const float4*>(qr + 4);
+          qf[hh][0] = x0.x; qf[hh][1] = x0.y; qf[hh][2] = x0.z; qf[hh][3] = x0.w;
+          qf[hh][4] = x1.x; qf[hh][5] = x1.y; qf[hh][6] = x1.z; qf[hh][7] = x1.w;
         }
       }
-      const float s = acc * scale;
-      sc[t] = s;
-      mx = fmaxf(mx, s);
+      // scores and the chunk max
+      float cm[kAttnHeads];
+#pragma unroll
+      for (int hh = 0; hh < kAttnHeads; ++hh) cm[hh] = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kAttnQuads; ++j) {
+        if (4 * j >= len) break;     // uniform
+        const int t = 4 * j + kk;    // within the chunk
+        const uint32_t wv[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
+#pragma unroll
+        for (int hh = 0; hh < kAttnHeads; ++hh) {
+          float part = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            part = fmaf(qf[hh][2 * i], __uint_as_float(wv[i] << 16), part);
+            part = fmaf(qf[hh][2 * i + 1], __uint_as_float(wv[i] & 0xFFFF0000u), part);
+          }
+          part = sum16_dpp(part);
+          const float sv = part * scale;
+          if (t < len && (lane & 15) == 0) {  // lane 16 j of the row keeps the score
+            cm[hh] = fmaxf(cm[hh], sv);
+            scw[hh * kAttnChunk + t] = sv;
+          }
+        }
+      }
+      wave_sync();
+      // running max, rescale, p = exp(s - m), chunk sums (lane t of the chunk)
+#pragma unroll
+      for (int hh = 0; hh < kAttnHeads; ++hh) {
+        cm[hh] = wave_max(cm[hh]);  // exact: every lane gets the chunk's largest score
+        const float mn = fmaxf(rm[hh], cm[hh]);
+        const float f = rm[hh] == -INFINITY ? 0.f : __expf(rm[hh] - mn);
+        rl[hh] *= f;
+        o0[hh] *= f;
+        o1[hh] *= f;
+        rm[hh] = mn;
+        float pv = 0.f;
+        if (lane < len) {
+          pv = __expf(scw[hh * kAttnChunk + lane] - mn);
+          scw[hh * kAttnChunk + lane] = pv;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) pv += __shfl_xor(pv, o);
+        rl[hh] += pv;
+      }
+      wave_sync();
+      // values: dims 2 lane, 2 lane + 1 over the chunk's keys in order
+#pragma unroll
+      for (int i = 0; i < kAttnChunk; ++i) {
+        if (i < len) {  // uniform
+          const float va = __uint_as_float(vv[i] << 16), vb = __uint_as_float(vv[i] & 0xFFFF0000u);
+#pragma unroll
+          for (int hh = 0; hh < kAttnHeads; ++hh) {
+            const float pt = scw[hh * kAttnChunk + i];
+            o0[hh] = fmaf(pt, va, o0[hh]);
+            o1[hh] = fmaf(pt, vb, o1[hh]);
+          }
+        }
+      }
+      wave_sync();  // the next chunk rewrites this wave's scores
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float den = 0.f;
-    for (int t = lane; t < T; t += 64) {
-      const float e = __expf(sc[t] - mx);
-      sc[t] = e;
-      den += e;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float o0 = 0.f, o1 = 0.f;
-    const uint32_t* vcol = reinterpret_cast<const uint32_t*>(Vv) + lane;  // dims 2l, 2l+1
-    int t = 0;
-    for (; t + 32 <= T; t += 32) {  // 32 value rows in flight, added in order
-      uint32_t vv[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) vv[i] = vcol[(int64_t)(t + i) * (kHeadDim / 2)];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float pt = sc[t + i];
-        o0 = fmaf(pt, __uint_as_float(vv[i] << 16), o0);
-        o1 = fmaf(pt, __uint_as_float(vv[i] & 0xFFFF0000u), o1);
+    for (int hh = 0; hh < kAttnHeads; ++hh) {
+      po[w][hh][2 * lane] = o0[hh];
+      po[w][hh][2 * lane + 1] = o1[hh];
+      if (lane == 0) {
+        pm[w][hh] = rm[hh];
+        pl[w][hh] = rl[hh];
       }
     }
-    for (; t < T; ++t) {
-      const float pt = sc[t];
-      const uint32_t vv = vcol[(int64_t)t * (kHeadDim / 2)];
-      o0 = fmaf(pt, __uint_as_float(vv << 16), o0);
-      o1 = fmaf(pt, __uint_as_float(vv & 0xFFFF0000u), o1);
+    __syncthreads();
+    // the wavefronts merged in wave order; one output element per thread
+    for (int e = threadIdx.x; e < nh * kHeadDim; e += 64 * kAttnWaves) {
+      const int hh = e / kHeadDim, d = e % kHeadDim;
+      float M_ = pm[0][hh];
+      for (int ww = 1; ww < kAttnWaves; ++ww) M_ = fmaxf(M_, pm[ww][hh]);
+      float o = 0.f, l = 0.f;
+      for (int ww = 0; ww < kAttnWaves; ++ww) {
+        if (pm[ww][hh] == -INFINITY) continue;  // an empty range
+        const float f = __expf(pm[ww][hh] - M_);
+        o = fmaf(po[ww][hh][d], f, o);
+        l = fmaf(pl[ww][hh], f, l);
+      }
+      const float inv = T > 0 ? 1.0f / l : 0.f;
+      out[m * (H * kHeadDim) + (int64_t)(g * grp + h0 + hh) * kHeadDim + d] = f32_to_bf16_rne(o * inv);
     }
-    const float inv = T > 0 ? 1.0f / den : 0.f;
-    uint16_t* orow = out + m * (H * kHeadDim) + h * kHeadDim;
-    orow[2 * lane] = f32_to_bf16_rne(o0 * inv);
-    orow[2 * lane + 1] = f32_to_bf16_rne(o1 * inv);
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();  // before the next head pass reuses the LDS
   }
 }
 
@@ -307,33 +403,68 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------------ argmax
-// out[m * stride] = the first index of the largest value of row m
-__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ x, int64_t V,
-                                                     int32_t* __restrict__ out, int64_t stride) {
-  __shared__ float bv[4];
-  __shared__ int bi[4];
+// out[m * stride] = the first index of the largest value of row m.  One
+// 1024-thread block per row; thread t takes 16-byte groups t, t + 1024, ...
+// (or single values when the row is not 16-byte aligned), kArgmaxBatch loads
+// in flight, each thread's values in index order; the lowest index wins among
+// equal values, so the answer does not depend on the merge order.
+constexpr int kArgmaxThreads = 1024;
+constexpr int kArgmaxBatch = 8;
+
+__device__ __forceinline__ void argmax_take(float& best, int& idx, float v, int i) {
+  if (v > best || idx == 0x7FFFFFFF) {  // the first value counts even at -inf
+    best = v;
+    idx = i;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float* __restrict__ x,
+                                                                int64_t V,
+                                                                int32_t* __restrict__ out,
+                                                                int64_t stride) {
+  __shared__ float bv[kArgmaxThreads / 64];
+  __shared__ int bi[kArgmaxThreads / 64];
   const int64_t m = blockIdx.x;
   const float* r = x + m * V;
   float best = -INFINITY;
   int idx = 0x7FFFFFFF;
-  int64_t j = threadIdx.x;
-  for (; j + 3 * 256 < V; j += 4 * 256) {  // four loads in flight, compared in index order
-    float v[4];
+  const int t = threadIdx.x;
+  if (VEC) {
+    const float4* r4 = reinterpret_cast<const float4*>(r);
+    const int64_t n4 = V / 4;
+    int64_t g = t;
+    for (; g + (kArgmaxBatch - 1) * kArgmaxThreads < n4; g += kArgmaxBatch * kArgmaxThreads) {
+      float4 v[kArgmaxBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = r[j + 256 * i];
+      for (int i = 0; i < kArgmaxBatch; ++i) v[i] = r4[g + i * kArgmaxThreads];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (v[i] > best || idx == 0x7FFFFFFF) {  // the first value counts even at -inf
-        best = v[i];
-        idx = (int)(j + 256 * i);
+      for (int i = 0; i < kArgmaxBatch; ++i) {
+        const int e = (int)(4 * (g + i * kArgmaxThreads));
+        argmax_take(best, idx, v[i].x, e);
+        argmax_take(best, idx, v[i].y, e + 1);
+        argmax_take(best, idx, v[i].z, e + 2);
+        argmax_take(best, idx, v[i].w, e + 3);
       }
-  }
-  for (; j < V; j += 256) {
-    const float v = r[j];
-    if (v > best || idx == 0x7FFFFFFF) {
-      best = v;
-      idx = (int)j;
     }
+    for (; g < n4; g += kArgmaxThreads) {
+      const float4 v = r4[g];
+      const int e = (int)(4 * g);
+      argmax_take(best, idx, v.x, e);
+      argmax_take(best, idx, v.y, e + 1);
+      argmax_take(best, idx, v.z, e + 2);
+      argmax_take(best, idx, v.w, e + 3);
+    }
+  } else {
+    int64_t j = t;
+    for (; j + (kArgmaxBatch - 1) * kArgmaxThreads < V; j += kArgmaxBatch * kArgmaxThreads) {
+      float v[kArgmaxBatch];
+#pragma unroll
+      for (int i = 0; i < kArgmaxBatch; ++i) v[i] = r[j + i * kArgmaxThreads];
+#pragma unroll
+      for (int i = 0; i < kArgmaxBatch; ++i) argmax_take(best, idx, v[i], (int)(j + i * kArgmaxThreads));
+    }
+    for (; j < V; j += kArgmaxThreads) argmax_take(best, idx, r[j], (int)j);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -344,14 +475,14 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ x
       idx = oi;
     }
   }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  const int w = t >> 6;
+  if ((t & 63) == 0) {
     bv[w] = best;
     bi[w] = idx;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < 4; ++i)
+  if (t == 0) {
+    for (int i = 1; i < kArgmaxThreads / 64; ++i)
       if (bv[i] > best || (bv[i] == best && bi[i] < idx)) {
         best = bv[i];
         idx = bi[i];
@@ -466,13 +597,11 @@ hipError_t launch_rope_kv(const float* qkv, int64_t M, int H, int Hkv, int hd, c
   return hipGetLastError();
 }
 
-size_t attention_lds_bytes(int64_t cap) { return (size_t)4 * (kHeadDim + cap) * sizeof(float); }
-
 hipError_t launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t M,
                             int H, int Hkv, const int32_t* seq, const int32_t* pos, int64_t B,
                             int64_t cap, uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)M, (unsigned)Hkv), dim3(256),
-                     attention_lds_bytes(cap), s, q, kc, vc, H, Hkv, seq, pos, B, cap, out);
+  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)M, (unsigned)Hkv), dim3(64 * kAttnWaves), 0, s,
+                     q, kc, vc, H, Hkv, seq, pos, B, cap, out);
   return hipGetLastError();
 }
 
@@ -485,7 +614,13 @@ hipError_t launch_silu_mul(const float* gu, int64_t M, int64_t F, uint16_t* a, h
 
 hipError_t launch_argmax(const float* x, int64_t M, int64_t V, int32_t* out, int64_t stride,
                          hipStream_t s) {
-  hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)M), dim3(256), 0, s, x, V, out, stride);
+  // 16-byte loads when every row starts 16-byte aligned
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0 && (V & 3) == 0)
+    hipLaunchKernelGGL((argmax_kernel<true>), dim3((unsigned)M), dim3(kArgmaxThreads), 0, s, x, V, out,
+                       stride);
+  else
+    hipLaunchKernelGGL((argmax_kernel<false>), dim3((unsigned)M), dim3(kArgmaxThreads), 0, s, x, V,
+                       out, stride);
   return hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ hipError_t launch_probe_empty(hipStream_t s);
 
 // decoder kernels of the end-to-end loop (harness.hip)
 constexpr int kHarnessHeadDim = 128;
-constexpr int64_t kHarnessMaxCap = 3968;  // attention scores fit 64 KiB of LDS
+constexpr int64_t kHarnessMaxCap = 3968;  // positions per sequence in a KV cache (the API limit)
 constexpr int64_t kHarnessMaxD = 4096;
 hipError_t launch_embed(const uint16_t* emb, int64_t V, int64_t d, const int32_t* tok, int64_t M,
                         float* x, hipStream_t s);

@@ -14,7 +14,10 @@ The W4A16 layers of decode and verify forwards use one kernel family
 (`GEMM_SKINNY`), whose per-row result does not depend on the row count, and
 every other kernel computes rows independently: a verify forward therefore
 reproduces bit for bit what pure W4A16 decoding computes, and greedy
-self-speculation emits exactly the pure greedy tokens.
+self-speculation emits exactly the pure greedy tokens.  The drafter's layers
+need no such invariance (greedy verification fixes the tokens, and the
+verify forward overwrites the drafter's KV rows), so they take the fastest
+family for their shape (`GEMM_AUTO`).
 
 This module is orchestration: buffers (torch allocations), graph capture and
 the host loop.  The model is described by any object with the fields
@@ -42,12 +45,13 @@ class Decoder:
     length `gamma`."""
 
     def __init__(self, cfg, weights, B, P, max_gen, gamma, device="cuda:0",
-                 variant=b.GEMM_SKINNY, draft_mode=DRAFT):
+                 variant=b.GEMM_SKINNY, draft_mode=DRAFT, draft_variant=b.GEMM_AUTO):
         if cfg.head_dim != 128:
             raise ValueError("head_dim must be 128")
         self.cfg, self.B, self.P, self.max_gen, self.gamma = cfg, B, P, max_gen, gamma
         self.dev = torch.device(device)
         self.variant = variant
+        self.draft_variant = draft_variant
         # the drafter's layers: W4A4 (the method); W4A16 turns the drafter
         # into the verifier itself, which must then accept every draft (a
         # check of the loop's bookkeeping)
@@ -222,7 +226,10 @@ class Decoder:
         V = self.cfg.vocab
         for j in range(g):
             b.spec_prepare(0, B, g, j, self.len, self.vtok, None, self.seq, self.pos, self.tok)
-            logits = self.forward(self.draft_mode, B, self.variant)
+            # a W4A16 drafter stays in the verifier's family (its drafts must
+            # be exactly the verifier's tokens); the W4A4 drafter takes its own
+            dv = self.variant if self.draft_mode == VERIFY else self.draft_variant
+            logits = self.forward(self.draft_mode, B, dv)
             b.argmax(logits, self.vtok[j + 1:], out_stride=g + 1)
         b.spec_prepare(1, B, g, 0, self.len, self.vtok, self.drafts, self.seq, self.pos, self.tok)
         logits = self.forward(VERIFY, B * (g + 1), self.variant)
