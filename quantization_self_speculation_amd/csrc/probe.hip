@@ -43,47 +43,50 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4p* __restric
   if (acc == never) sink[t & 255] = acc;
 }
 
-// CH independent accumulators per wavefront, `iters` rounds of one MFMA each.
-template <bool I8, int CH>
-__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float never,
-                                                         float* __restrict__ sink) {
+// Eight independent accumulators per wavefront, `iters` rounds of one MFMA
+// each (four rounds per loop trip); eight named chains rather than an array,
+// so every accumulator keeps its registers from round to round.
+#define QSPEC_PROBE_ROUND(F) \
+  c0 = F(a, b, c0, 0, 0, 0); c1 = F(a, b, c1, 0, 0, 0); c2 = F(a, b, c2, 0, 0, 0); \
+  c3 = F(a, b, c3, 0, 0, 0); c4 = F(a, b, c4, 0, 0, 0); c5 = F(a, b, c5, 0, 0, 0); \
+  c6 = F(a, b, c6, 0, 0, 0); c7 = F(a, b, c7, 0, 0, 0);
+
+__global__ __launch_bounds__(256) void probe_mfma_i8_kernel(int iters, float never,
+                                                            float* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
-  if (I8) {
-    v4i acc[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) acc[c] = v4i{0, 0, 0, 0};
-    const v4i a = {lane, lane + 1, lane + 2, lane + 3};
-    const v4i b = {lane ^ 5, lane ^ 7, lane ^ 9, lane ^ 11};
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[c], 0, 0, 0);
-    }
-    int s = 0;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
-    if ((float)s == never) sink[threadIdx.x] = (float)s;
-  } else {
-    v4f acc[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-    const uint32_t w = 0x3F803F80u + (uint32_t)lane;  // small bf16 values
-    v8bf a, b;
-    {
-      typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-      const u4 ta = {w, w + 1, w + 2, w + 3}, tb = {w ^ 1, w ^ 2, w ^ 3, w ^ 4};
-      a = __builtin_bit_cast(v8bf, ta);
-      b = __builtin_bit_cast(v8bf, tb);
-    }
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
-    }
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
-    if (s == never) sink[threadIdx.x] = s;
+  const v4i a = {lane, lane + 1, lane + 2, lane + 3};
+  const v4i b = {lane ^ 5, lane ^ 7, lane ^ 9, lane ^ 11};
+  v4i c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0, c4 = c0, c5 = c0, c6 = c0, c7 = c0;
+  for (int it = 0; it < iters; it += 4) {
+    QSPEC_PROBE_ROUND(__builtin_amdgcn_mfma_i32_16x16x64_i8)
+    QSPEC_PROBE_ROUND(__builtin_amdgcn_mfma_i32_16x16x64_i8)
+    QSPEC_PROBE_ROUND(__builtin_amdgcn_mfma_i32_16x16x64_i8)
+    QSPEC_PROBE_ROUND(__builtin_amdgcn_mfma_i32_16x16x64_i8)
   }
+  const v4i t = c0 + c1 + c2 + c3 + c4 + c5 + c6 + c7;
+  const int s = t[0] + t[1] + t[2] + t[3];
+  if ((float)s == never) sink[threadIdx.x] = (float)s;
 }
+
+__global__ __launch_bounds__(256) void probe_mfma_bf16_kernel(int iters, float never,
+                                                              float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const uint32_t w = 0x3F803F80u + (uint32_t)lane;  // small bf16 values
+  const u4 ta = {w, w + 1, w + 2, w + 3}, tb = {w ^ 1, w ^ 2, w ^ 3, w ^ 4};
+  const v8bf a = __builtin_bit_cast(v8bf, ta), b = __builtin_bit_cast(v8bf, tb);
+  v4f c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0, c4 = c0, c5 = c0, c6 = c0, c7 = c0;
+  for (int it = 0; it < iters; it += 4) {
+    QSPEC_PROBE_ROUND(__builtin_amdgcn_mfma_f32_16x16x32_bf16)
+    QSPEC_PROBE_ROUND(__builtin_amdgcn_mfma_f32_16x16x32_bf16)
+    QSPEC_PROBE_ROUND(__builtin_amdgcn_mfma_f32_16x16x32_bf16)
+    QSPEC_PROBE_ROUND(__builtin_amdgcn_mfma_f32_16x16x32_bf16)
+  }
+  const v4f t = c0 + c1 + c2 + c3 + c4 + c5 + c6 + c7;
+  const float s = t[0] + t[1] + t[2] + t[3];
+  if (s == never) sink[threadIdx.x] = s;
+}
+#undef QSPEC_PROBE_ROUND
 
 __global__ void probe_empty_kernel() {}
 
@@ -104,10 +107,11 @@ hipError_t launch_probe_read(const void* buf, int64_t bytes, int blocks, int unr
 }
 
 hipError_t launch_probe_mfma(int kind, int blocks, int iters, float* sink, hipStream_t s) {
+  // iters rounds to a multiple of four (the loop's trip)
   if (kind == 0)
-    hipLaunchKernelGGL((probe_mfma_kernel<true, 8>), dim3(blocks), dim3(256), 0, s, iters, -1.5f, sink);
+    hipLaunchKernelGGL(probe_mfma_i8_kernel, dim3(blocks), dim3(256), 0, s, iters, -1.5f, sink);
   else
-    hipLaunchKernelGGL((probe_mfma_kernel<false, 8>), dim3(blocks), dim3(256), 0, s, iters, -1.5f, sink);
+    hipLaunchKernelGGL(probe_mfma_bf16_kernel, dim3(blocks), dim3(256), 0, s, iters, -1.5f, sink);
   return hipGetLastError();
 }
 

@@ -11,8 +11,9 @@
 // The work is one streaming pass over the logits (HBM-bound) plus, when
 // sampling, one pass over the one or two rows each sequence samples from:
 //   greedy:   pass1 (chunk argmax, lowest index on ties) -> decide
-//   sampling: pass1 (chunk max and sum of exp) -> decide (merge chunks,
-//             accept tests) -> residual chunk sums -> inverse-CDF select
+//   sampling: pass1 (chunk max and sum of exp) -> residual chunk sums ->
+//             inverse-CDF select, the decision (merge chunks, accept tests)
+//             taken at the start of each of the last two
 // Chunks are reduced in fixed order (no atomics): the same inputs give the
 // same bits.
 #include <atomic>
@@ -245,20 +246,23 @@ struct Decision {
   double St, Sd;
 };
 
-// sampling decision: one 256-thread block per sequence.  The 2*gamma+1 row
-// normalizers are merged in parallel (one wavefront per row), the logits at
-// the drafted tokens are fetched in parallel, then lane i of the first
-// wavefront runs the accept test of draft i and the lowest rejecting lane
-// decides.  p(x) and q(x) are fp64: exact fp64 exponent of the exact
-// difference over the pass-1 sums.
-__global__ __launch_bounds__(256) void sample_decide_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
-    const float* __restrict__ ua, int gamma, int64_t V, int nck, const float* __restrict__ pm,
-    const double* __restrict__ ps, int64_t rows_t, Decision* __restrict__ dec) {
+// The sampling decision of sequence b, taken by a whole 256-thread block and
+// returned to every thread: the 2*gamma+1 row normalizers are merged in
+// parallel (one wavefront per row), the logits at the drafted tokens are
+// fetched in parallel, then lane i of the first wavefront runs the accept
+// test of draft i and the lowest rejecting lane decides.  p(x) and q(x) are
+// fp64: exact fp64 exponent of the exact difference over the pass-1 sums.
+// The kernels that need the decision each take it this way (the same
+// operations on the same data, so every block of a sequence agrees), which
+// saves a launch between pass 1 and the residual pass.
+__device__ Decision block_decide(const float* __restrict__ tgt, const float* __restrict__ drf,
+                                 const int32_t* __restrict__ dt, const float* __restrict__ ua,
+                                 int gamma, int64_t V, int nck, const float* __restrict__ pm,
+                                 const double* __restrict__ ps, int64_t rows_t, int64_t b) {
   __shared__ float lm[2 * QSPEC_MAX_GAMMA + 1];
   __shared__ double lsum[2 * QSPEC_MAX_GAMMA + 1];
   __shared__ float lxt[QSPEC_MAX_GAMMA], lxd[QSPEC_MAX_GAMMA];
-  const int64_t b = blockIdx.x;
+  __shared__ Decision sdec;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nr = 2 * gamma + 1;  // target rows 0..gamma, then draft rows
   for (int r = w; r < nr; r += 4) {
@@ -277,26 +281,30 @@ __global__ __launch_bounds__(256) void sample_decide_kernel(
     lxd[tid] = drf[(b * gamma + tid) * V + x];
   }
   __syncthreads();
-  if (w != 0) return;
-  // every accept test at once (lane i tests draft i); the first rejection
-  // ends the run, as in the sequential rule
-  bool rej = false;
-  if (lane < gamma) {
-    const float mt = lm[lane], md = lm[gamma + 1 + lane];
-    const double st = lsum[lane], sd = lsum[gamma + 1 + lane];
-    const double p = exp((double)lxt[lane] - (double)mt) / st;
-    const double q = exp((double)lxd[lane] - (double)md) / sd;
-    const bool acc = q > 0.0 ? ((double)ua[b * gamma + lane] <= p / q) : (p > 0.0);
-    rej = !acc;
+  if (w == 0) {
+    // every accept test at once (lane i tests draft i); the first rejection
+    // ends the run, as in the sequential rule
+    bool rej = false;
+    if (lane < gamma) {
+      const float mt = lm[lane], md = lm[gamma + 1 + lane];
+      const double st = lsum[lane], sd = lsum[gamma + 1 + lane];
+      const double p = exp((double)lxt[lane] - (double)mt) / st;
+      const double q = exp((double)lxd[lane] - (double)md) / sd;
+      const bool acc = q > 0.0 ? ((double)ua[b * gamma + lane] <= p / q) : (p > 0.0);
+      rej = !acc;
+    }
+    const unsigned long long mask = __ballot(rej);
+    if (lane == 0) {
+      if (mask == 0) {
+        sdec = Decision{gamma, 1, lm[gamma], 0.f, lsum[gamma], 1.0};
+      } else {
+        const int i = __builtin_ctzll(mask);
+        sdec = Decision{i, 0, lm[i], lm[gamma + 1 + i], lsum[i], lsum[gamma + 1 + i]};
+      }
+    }
   }
-  const unsigned long long mask = __ballot(rej);
-  if (lane != 0) return;
-  if (mask == 0) {
-    dec[b] = Decision{gamma, 1, lm[gamma], 0.f, lsum[gamma], 1.0};
-  } else {
-    const int i = __builtin_ctzll(mask);
-    dec[b] = Decision{i, 0, lm[i], lm[gamma + 1 + i], lsum[i], lsum[gamma + 1 + i]};
-  }
+  __syncthreads();
+  return sdec;
 }
 
 // r_j of the row a sequence samples from, in fp64
@@ -310,17 +318,16 @@ __device__ __forceinline__ double resid(const float* rt, const float* rd, int64_
 
 // residual chunk sums: grid = (rnck, B), kRCW logits per block (8 per
 // thread, coalesced).  rs[b][c] = sum r, pp[b][c] = sum p (fp64).
-__global__ __launch_bounds__(256) void resid_sums_kernel(const float* __restrict__ tgt,
-                                                         const float* __restrict__ drf, int gamma,
-                                                         int64_t V, int rnck,
-                                                         const Decision* __restrict__ dec,
-                                                         double* __restrict__ rs,
-                                                         double* __restrict__ pp) {
+__global__ __launch_bounds__(256) void resid_sums_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
+    const float* __restrict__ ua, int gamma, int64_t V, int nck, const float* __restrict__ pm,
+    const double* __restrict__ ps, int64_t rows_t, int rnck, double* __restrict__ rs,
+    double* __restrict__ pp) {
   constexpr int EPT = kRCW / 256;
   __shared__ double red[2][4];
   const int c = blockIdx.x;
   const int64_t b = blockIdx.y;
-  const Decision D = dec[b];
+  const Decision D = block_decide(tgt, drf, dt, ua, gamma, V, nck, pm, ps, rows_t, b);
   const double iSt = 1.0 / D.St, iSd = 1.0 / D.Sd;
   const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
   const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
@@ -365,9 +372,10 @@ __global__ __launch_bounds__(256) void resid_sums_kernel(const float* __restrict
 // block-wide exclusive scan gives every thread its starting cumulative sum.
 __global__ __launch_bounds__(256) void sample_select_kernel(
     const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
-    const float* __restrict__ us, int gamma, int64_t V, int rnck,
-    const Decision* __restrict__ dec, const double* __restrict__ rs,
-    const double* __restrict__ pp, int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tok) {
+    const float* __restrict__ ua, const float* __restrict__ us, int gamma, int64_t V, int nck,
+    const float* __restrict__ pm, const double* __restrict__ ps, int64_t rows_t, int rnck,
+    const double* __restrict__ rs, const double* __restrict__ pp, int32_t* __restrict__ n_accept,
+    int32_t* __restrict__ out_tok) {
   constexpr int EPT = kRCW / 256;
   __shared__ double wsum[4];
   __shared__ int found;
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
   __shared__ double sh_base, sh_thr;
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const Decision D = dec[b];
+  const Decision D = block_decide(tgt, drf, dt, ua, gamma, V, nck, pm, ps, rows_t, b);
   const double iSt = 1.0 / D.St, iSd = 1.0 / D.Sd;
   const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
   const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
@@ -511,7 +519,7 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
 
 struct VerifyLayout {
   int nck, rnck;
-  size_t pm, ps, pi, dec, rs, pp, total;  // byte offsets
+  size_t pm, ps, pi, rs, pp, total;  // byte offsets
 };
 
 VerifyLayout layout(int64_t B, int gamma, int64_t V) {
@@ -528,7 +536,6 @@ VerifyLayout layout(int64_t B, int gamma, int64_t V) {
   L.pm = take((size_t)rows * L.nck * sizeof(float));
   L.ps = take((size_t)rows * L.nck * sizeof(double));
   L.pi = take((size_t)B * (gamma + 1) * L.nck * sizeof(int));
-  L.dec = take((size_t)B * sizeof(Decision));
   L.rs = take((size_t)B * L.rnck * sizeof(double));
   L.pp = take((size_t)B * L.rnck * sizeof(double));
   L.total = off;
@@ -586,7 +593,6 @@ hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_
   float* pm = reinterpret_cast<float*>(w + L.pm);
   double* ps = reinterpret_cast<double*>(w + L.ps);
   int* pi = reinterpret_cast<int*>(w + L.pi);
-  Decision* dec = reinterpret_cast<Decision*>(w + L.dec);
   double* rs = reinterpret_cast<double*>(w + L.rs);
   double* pp = reinterpret_cast<double*>(w + L.pp);
   const int64_t rows_t = B * (gamma + 1);
@@ -604,15 +610,13 @@ hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_
                      target_logits, draft_logits, rows_t, V, L.nck, pm, ps, pi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sample_decide_kernel, dim3((unsigned)B), dim3(256), 0, s, target_logits,
-                     draft_logits, draft_tok, u_accept, gamma, V, L.nck, pm, ps, rows_t, dec);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(resid_sums_kernel, dim3(L.rnck, (unsigned)B), dim3(256), 0, s,
-                     target_logits, draft_logits, gamma, V, L.rnck, dec, rs, pp);
+                     target_logits, draft_logits, draft_tok, u_accept, gamma, V, L.nck, pm, ps,
+                     rows_t, L.rnck, rs, pp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(sample_select_kernel, dim3((unsigned)B), dim3(256), 0, s, target_logits,
-                     draft_logits, draft_tok, u_sample, gamma, V, L.rnck, dec, rs, pp, n_accept,
-                     out_tok);
+                     draft_logits, draft_tok, u_accept, u_sample, gamma, V, L.nck, pm, ps, rows_t,
+                     L.rnck, rs, pp, n_accept, out_tok);
   return hipGetLastError();
 }
 
