@@ -30,11 +30,8 @@
  *    gives a thread-local message).  A failed launch returns QSPEC_ERR_HIP.
  *    Faults inside a kernel surface at the caller's next synchronisation.
  *  - Calls never abort or exit the process.  They are thread-safe.  Global
- *    state: a per-device cache of the device check, a process-wide atomic
- *    call counter that tags the split-K arrival counters in a GEMM's
- *    workspace (a counter left by a call that never finished is not taken
- *    for one of the current call), and the per-device scratch array of
- *    qspec_verify_noalloc (read its note).
+ *    state: a per-device cache of the device check and the per-device
+ *    scratch array of qspec_verify_noalloc (read its note).
  *  - Non-finite inputs (NaN/Inf weights, activations or logits) are not
  *    supported: results are unspecified, but every kernel still terminates.
  */
@@ -111,11 +108,14 @@ qspec_status qspec_device_check(void);
  * The answer is the maximum over all variants and modes, so one workspace
  * sized by it serves every call of that op with sizes no larger.
  * A GEMM workspace must hold zeros the first time it is used (hipMemset it
- * once): the k-split's arrival counters live in it, and no tag can tell
- * leftover data from a counter reliably.  Every GEMM call leaves its
- * counters at zero again, so a workspace is reused without clearing by any
- * later GEMM call on the same stream (calls that overlap in time must not
- * share one).  A verify workspace needs no initialisation. */
+ * once): the k-split's arrival counters live in its first half and count up
+ * from zero; every family's partials go to its second half (the halves are
+ * taken from ws_bytes, so pass one workspace with the same ws_bytes every
+ * time).  Every GEMM call leaves its counters at zero again, so a workspace
+ * is reused without clearing by any later GEMM call of any shape on the
+ * same stream (calls that overlap in time must not share one; a call that
+ * never finished, e.g. after a device fault, leaves the workspace to be
+ * zeroed again).  A verify workspace needs no initialisation. */
 size_t qspec_workspace_bytes(int op, int64_t a, int64_t b, int64_t c);
 
 /* ---------------------------------------------------------------------------

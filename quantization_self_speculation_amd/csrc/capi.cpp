@@ -271,7 +271,7 @@ qspec_status qspec_gemm_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* 
   if (P != nullptr) QS_PTR(P);
   QS_TRY(check_ws(ws, ws_bytes, w4a4_ws_bytes(M, N, K)));
   QS_TRY(device_check());
-  return hip_result(launch_w4a4(Xq, Xs, Wq, Ws, M, N, K, variant, Y, nullptr, P, ws,
+  return hip_result(launch_w4a4(Xq, Xs, Wq, Ws, M, N, K, variant, Y, nullptr, P, ws, ws_bytes,
                                 (hipStream_t)stream),
                     "gemm_w4a4 launch");
 }
@@ -288,7 +288,7 @@ qspec_status qspec_gemm_w4a4_bf16(const uint8_t* Xq, const float* Xs, const uint
   QS_PTR(Y);
   QS_TRY(check_ws(ws, ws_bytes, w4a4_ws_bytes(M, N, K)));
   QS_TRY(device_check());
-  return hip_result(launch_w4a4(Xq, Xs, Wq, Ws, M, N, K, variant, nullptr, Y, nullptr, ws,
+  return hip_result(launch_w4a4(Xq, Xs, Wq, Ws, M, N, K, variant, nullptr, Y, nullptr, ws, ws_bytes,
                                 (hipStream_t)stream),
                     "gemm_w4a4_bf16 launch");
 }
@@ -310,7 +310,8 @@ qspec_status qspec_gemm_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* W
   if (P != nullptr) QS_PTR(P);
   QS_TRY(check_ws(ws, ws_bytes, w4a4_ws_bytes(M, N, K)));
   QS_TRY(device_check());
-  return hip_result(launch_w4a8(Xq, Xs, Wq, Ws, M, N, K, variant, Y, P, ws, (hipStream_t)stream),
+  return hip_result(launch_w4a8(Xq, Xs, Wq, Ws, M, N, K, variant, Y, P, ws, ws_bytes,
+                                 (hipStream_t)stream),
                     "gemm_w4a8 launch");
 }
 
@@ -324,7 +325,7 @@ qspec_status qspec_gemm_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16
   QS_PTR(Y);
   QS_TRY(check_ws(ws, ws_bytes, w4a16_ws_bytes(M, N, K)));
   QS_TRY(device_check());
-  return hip_result(launch_w4a16(X, Wq, Ws, M, N, K, variant, Y, ws, (hipStream_t)stream),
+  return hip_result(launch_w4a16(X, Wq, Ws, M, N, K, variant, Y, ws, ws_bytes, (hipStream_t)stream),
                     "gemm_w4a16 launch");
 }
 

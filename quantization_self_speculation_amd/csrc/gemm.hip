@@ -180,8 +180,8 @@ __device__ __forceinline__ float group_sum16(float v) {
 //     double-buffered, in the MFMA k-slot order, once per workgroup;
 //   * split-K (S slices, a function of N and K only) is reduced inside the
 //     kernel by the last slice to arrive, in fixed slice order; arrival is
-//     counted with an epoch-tagged 64-bit counter per tile in the caller's
-//     workspace that the last slice resets to 0;
+//     counted with one atomic add on a 64-bit counter per tile in the
+//     caller's (zero-filled) workspace, which the last slice resets to 0;
 //   * block -> (tile, slice) mapping deals the S slices of a tile to one XCD
 //     when blocks go round-robin to the 8 XCDs (a locality hint only: the
 //     hand-off of partials is correct on any placement).
@@ -199,7 +199,6 @@ struct SkinnyArgs {
   unsigned long long* cnt;  // [T] when S > 1
   int32_t* P;               // W4A4 / W4A8 int32 group partials (optional)
   int M, N, K, S, gps, ntiles, T;
-  unsigned epoch;
 };
 
 // End of a (tile, slice): store Y (times Xs for W4A4) when the k-range is not
@@ -207,8 +206,8 @@ struct SkinnyArgs {
 // reduce all S partials in slice order.  Partials are written and read with
 // system-scope atomic accesses (coherent whatever XCD each slice ran on: they
 // do not stay in an XCD's L2), the writer waits for its stores to complete
-// before the arrival count, and the arrival counter (epoch-tagged, in the
-// caller's workspace) is reset by the last slice.
+// before the arrival count, and the arrival counter (in the caller's
+// workspace, zero at rest) is reset by the last slice.
 template <int MODE, int MB, int NB, int NWV>
 __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot)[NB][MB], int t,
                                             int slice, int m0, int n_wg, int n_w, int l16, int lg,
@@ -264,21 +263,13 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   // data.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // One atomic add per slice: slices that finish together queue at the
+  // counter instead of retrying (a compare-and-swap loop costs one memory
+  // round trip per competitor, quadratic in S).
   if (threadIdx.x == 0) {
-    unsigned long long* slot = a.cnt + t;
-    unsigned long long cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    unsigned int count = 0;
-    for (;;) {
-      const unsigned long long nxt = ((unsigned int)(cur >> 32) == a.epoch)
-                                         ? cur + 1ull
-                                         : (((unsigned long long)a.epoch << 32) | 1ull);
-      if (__hip_atomic_compare_exchange_strong(slot, &cur, nxt, __ATOMIC_RELAXED,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
-        count = (unsigned int)(nxt & 0xffffffffull);
-        break;
-      }
-    }
-    s_last = count == (unsigned int)a.S;
+    const unsigned long long old = __hip_atomic_fetch_add(a.cnt + t, 1ull, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_SYSTEM);
+    s_last = old + 1ull == (unsigned long long)a.S;
   }
   __syncthreads();
   if (!s_last) return;
@@ -1599,14 +1590,6 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool max_tiles
   return p;
 }
 
-std::atomic<unsigned int> g_epoch{1};
-
-unsigned int next_epoch() {
-  unsigned int e = g_epoch.fetch_add(1, std::memory_order_relaxed);
-  if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed);  // 0 marks a free slot
-  return e;
-}
-
 template <int MODE, bool WITHP>
 hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
   const dim3 grid((unsigned)p.blocks), blk(64 * p.NWV);
@@ -1662,6 +1645,26 @@ hipError_t launch_skinny(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s
   return launch_skinny_t<MODE, false>(a, p, s);
 }
 
+// A GEMM workspace of ws_bytes holds the k-split arrival counters in its
+// first half and every family's partials in its second half.  The split
+// depends on ws_bytes alone, so no call's partials can land on the counters
+// of a later call that shares the workspace, whatever the two calls' shapes
+// (a counter must read zero when its call starts).
+struct WsSplit {
+  unsigned long long* cnt;
+  float* part;
+};
+WsSplit ws_split(void* ws, size_t ws_bytes) {
+  const size_t half = ws_bytes / 2 / 256 * 256;
+  return WsSplit{static_cast<unsigned long long*>(ws),
+                 reinterpret_cast<float*>(static_cast<char*>(ws) + half)};
+}
+// bytes that hold both halves: twice the larger of counters and partials
+size_t ws_need(size_t cnt_bytes, size_t part_bytes) {
+  const size_t h = round_up(std::max(cnt_bytes, part_bytes), 256);
+  return 2 * h;
+}
+
 struct GemvPlan {
   int S;
 };
@@ -1715,14 +1718,16 @@ hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* X
 size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const SkinnyPlan p = plan_skinny(0, M, N, K, true);  // four-wavefront tiles: the most counters
   const GemvPlan q = plan_gemv(K);
-  const size_t a = p.cnt_bytes + p.part_bytes;
-  const size_t b = q.S > 1 ? (size_t)q.S * std::min<int64_t>(M, 4) * N * sizeof(float) : 0;
-  return std::max(a, b);
+  const size_t gemv_part = q.S > 1 ? (size_t)q.S * std::min<int64_t>(M, 4) * N * sizeof(float) : 0;
+  const size_t part = std::max(p.part_bytes, gemv_part);
+  return p.cnt_bytes + part == 0 ? 0 : ws_need(p.cnt_bytes, part);
 }
 
 hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
-                        int64_t N, int64_t K, int variant, float* Y, void* ws, hipStream_t s) {
+                        int64_t N, int64_t K, int variant, float* Y, void* ws, size_t ws_bytes,
+                        hipStream_t s) {
   const int v = w4a16_pick(variant, M, N, K);
+  const WsSplit w = ws_split(ws, ws_bytes);
   if (v == QSPEC_GEMM_STREAM)
     return launch_stream<kW4A16>(X, nullptr, Wq, Ws, M, N, K, Y, nullptr, nullptr, s);
   if (v == QSPEC_GEMM_GEMV) {
@@ -1730,7 +1735,7 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
     // rows of X in chunks of up to 4
     for (int64_t m0 = 0; m0 < M; m0 += 4) {
       const int mm = (int)std::min<int64_t>(4, M - m0);
-      float* out = q.S > 1 ? static_cast<float*>(ws) : Y + m0 * N;
+      float* out = q.S > 1 ? w.part : Y + m0 * N;
       const int64_t stride = (int64_t)mm * N;
       dim3 grid((unsigned)cdiv(N, 64), (unsigned)q.S);
       const uint16_t* Xm = X + m0 * K;
@@ -1757,21 +1762,20 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
   a.Wq = Wq;
   a.Ws = Ws;
   a.Y = Y;
-  a.cnt = p.S > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
-  a.part = p.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.cnt_bytes) : nullptr;
+  a.cnt = p.S > 1 ? w.cnt : nullptr;
+  a.part = p.S > 1 ? w.part : nullptr;
   a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;
-  a.epoch = next_epoch();
   return launch_skinny<kW4A16>(a, p, s);
 }
 
 size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const SkinnyPlan p = plan_skinny(1, M, N, K, true);  // four-wavefront tiles: the most counters
-  return p.cnt_bytes + p.part_bytes;
+  return p.cnt_bytes + p.part_bytes == 0 ? 0 : ws_need(p.cnt_bytes, p.part_bytes);
 }
 
 hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, uint16_t* Yb,
-                       int32_t* P, void* ws, hipStream_t s) {
+                       int32_t* P, void* ws, size_t ws_bytes, hipStream_t s) {
   // exactly one of Y (fp32) and Yb (bf16) is given; the int32 partials P
   // (with Y only) come from the family that computes Y, the same kernel
   // code instantiated with its partials store
@@ -1779,6 +1783,7 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
   if (v == QSPEC_GEMM_TILED) return launch_tiled<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, Yb, P, s);
   if (v == QSPEC_GEMM_STREAM) return launch_stream<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, Y, Yb, P, s);
   const SkinnyPlan p = plan_skinny(1, M, N, K);
+  const WsSplit w = ws_split(ws, ws_bytes);
   SkinnyArgs a{};
   a.X = Xq;
   a.Xs = Xs;
@@ -1787,10 +1792,9 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
   a.Y = Y;
   a.Yb = Yb;
   a.P = P;
-  a.cnt = p.S > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
-  a.part = p.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.cnt_bytes) : nullptr;
+  a.cnt = p.S > 1 ? w.cnt : nullptr;
+  a.part = p.S > 1 ? w.part : nullptr;
   a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;
-  a.epoch = next_epoch();
   return launch_skinny<kW4A4>(a, p, s);
 }
 
@@ -1799,11 +1803,12 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
 // same workspace); AUTO, SKINNY and STREAM are the accepted variants.
 hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
-                       void* ws, hipStream_t s) {
+                       void* ws, size_t ws_bytes, hipStream_t s) {
   const int v = variant == QSPEC_GEMM_AUTO ? auto_pick(M, N, K, 256, 64, 96) : variant;
   if (v == QSPEC_GEMM_STREAM)
     return launch_stream<kW4A8>(Xq, Xs, Wq, Ws, M, N, K, Y, nullptr, P, s);
   const SkinnyPlan p = plan_skinny(1, M, N, K);
+  const WsSplit w = ws_split(ws, ws_bytes);
   SkinnyArgs a{};
   a.X = Xq;
   a.Xs = Xs;
@@ -1811,10 +1816,9 @@ hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, con
   a.Ws = Ws;
   a.Y = Y;
   a.P = P;
-  a.cnt = p.S > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
-  a.part = p.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.cnt_bytes) : nullptr;
+  a.cnt = p.S > 1 ? w.cnt : nullptr;
+  a.part = p.S > 1 ? w.part : nullptr;
   a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;
-  a.epoch = next_epoch();
   return launch_skinny<kW4A8>(a, p, s);
 }
 

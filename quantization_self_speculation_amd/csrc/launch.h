@@ -25,16 +25,17 @@ hipError_t launch_quant_act8(const uint16_t* X, int64_t M, int64_t K, int8_t* Xq
 
 size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
-                        int64_t N, int64_t K, int variant, float* Y, void* ws, hipStream_t s);
+                        int64_t N, int64_t K, int variant, float* Y, void* ws, size_t ws_bytes,
+                        hipStream_t s);
 
 size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, uint16_t* Yb,
-                       int32_t* P, void* ws, hipStream_t s);
+                       int32_t* P, void* ws, size_t ws_bytes, hipStream_t s);
 
 hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
-                       void* ws, hipStream_t s);
+                       void* ws, size_t ws_bytes, hipStream_t s);
 
 size_t verify_ws_bytes(int64_t B, int gamma, int64_t V);
 // the fixed per-device scratch of the allocation-free verify entry point

@@ -601,9 +601,10 @@ def test_graph_replays_match_eager():
 
 def test_workspace_reused_across_shapes():
     """One zero-filled workspace serves a run of k-split calls of different
-    shapes and modes (different counter counts and slice counts): each call
-    leaves its arrival counters at zero, so the next finds them clear,
-    whatever partials the earlier calls left behind."""
+    shapes and modes (different counter counts and slice counts) and of the
+    GEMV family: each call leaves its arrival counters at zero, and every
+    family's partials go to the other half of the workspace, so each call
+    finds its counters clear whatever partials the earlier calls left."""
     shapes = [(8, 3584, 18944), (40, 4608, 3584), (5, 1028, 1024), (16, 2048, 5632)]
     nb = max(q.workspace_bytes(op, M, N, K) for (M, N, K) in shapes for op in (1, 2))
     ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
@@ -615,8 +616,13 @@ def test_workspace_reused_across_shapes():
         cases.append((M, N, K, X, Xq, Xs, Wq, Ws, dev_w(Wq), dev_s(Ws)))
     for rep in range(2):
         for (M, N, K, X, Xq, Xs, Wq, Ws, Wq_d, Ws_d) in cases:
+            want16, want4 = oracle.gemm_w4a16(X, Wq, Ws), oracle.gemm_w4a4(Xq, Xs, Wq, Ws)
+            # k-split calls of both modes and the GEMV family's partials,
+            # interleaved on one workspace
             say(f"workspace reuse rep={rep} M={M} N={N} K={K}")
             Y = q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=q.GEMM_SKINNY, ws=ws, N=N)
-            assert_close(host(Y), oracle.gemm_w4a16(X, Wq, Ws), what="w4a16 reused ws")
+            assert_close(host(Y), want16, what="w4a16 reused ws")
+            Y = q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=q.GEMM_GEMV, ws=ws, N=N)
+            assert_close(host(Y), want16, what="w4a16 GEMV reused ws")
             Y = q.gemm_w4a4(dev(Xq), dev(Xs), Wq_d, Ws_d, variant=q.GEMM_SKINNY, ws=ws, N=N)
-            assert_close(host(Y), oracle.gemm_w4a4(Xq, Xs, Wq, Ws), what="w4a4 reused ws")
+            assert_close(host(Y), want4, what="w4a4 reused ws")
