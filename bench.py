@@ -523,7 +523,8 @@ def measure_e2e(torch, B=16, P=128, n_gen=256, gamma=4):
     heads of 128, SwiGLU 5632, vocabulary 32000) on one shared INT4 buffer,
     batch 16, 128-token random prompts, 256 generated tokens; greedy
     self-speculation (W4A4 drafts, gamma 4, W4A16 verify) against pure W4A16
-    greedy decoding of the same model."""
+    greedy decoding of the same model, and the same loop with the W4A8 tier
+    drafting."""
     import synth
     from quantization_self_speculation_amd.e2e import Decoder
     cfg = synth.E2E_MODEL
@@ -531,12 +532,17 @@ def measure_e2e(torch, B=16, P=128, n_gen=256, gamma=4):
     w = synth.model_weights(rng, cfg)
     prompts = synth.prompts(rng, B, P, cfg.vocab)
     dec = Decoder(cfg, w, B, P, n_gen, gamma)
+    dec8 = Decoder(cfg, w, B, P, n_gen, gamma, draft_mode="w4a8")
     del w
     dec.run(prompts, speculative=True, max_rounds=2)      # warm-up (graph capture, caches)
     pure = dec.run(prompts, speculative=False)
     spec = dec.run(prompts, speculative=True)
+    dec8.run(prompts, speculative=True, max_rounds=2)
+    spec8 = dec8.run(prompts, speculative=True)
+    del dec8
     toks = B * n_gen
     alpha = spec["accepted"] / max(1, gamma * spec["active_rows"])
+    alpha8 = spec8["accepted"] / max(1, gamma * spec8["active_rows"])
     return {
         "model": "random-init 8L d2048 16q/4kv x128 ffn5632 V32000, shared int4 g128",
         "batch": B, "prompt": P, "generated": n_gen, "gamma": gamma,
@@ -553,6 +559,17 @@ def measure_e2e(torch, B=16, P=128, n_gen=256, gamma=4):
         "prefill_ms": round(spec["prefill_s"] * 1e3, 3),
         "pure_ms_per_step": round(pure["decode_s"] * 1e3 / max(1, pure["rounds"]), 4),
         "selfspec_ms_per_round": round(spec["decode_s"] * 1e3 / max(1, spec["rounds"]), 4),
+        # the W4A8 tier as the drafter of the same loop (same weights, same verify)
+        "w4a8_drafter": {
+            "greedy_equal": bool(np.array_equal(spec8["tokens"], pure["tokens"])),
+            "acceptance_rate": round(alpha8, 4),
+            "tokens_per_round": round((spec8["accepted"] + spec8["active_rows"]) /
+                                      max(1, spec8["active_rows"]), 3),
+            "rounds": spec8["rounds"],
+            "selfspec_tok_s": round(toks / spec8["decode_s"], 1),
+            "speedup_vs_pure": round(pure["decode_s"] / spec8["decode_s"], 3),
+            "selfspec_ms_per_round": round(spec8["decode_s"] * 1e3 / max(1, spec8["rounds"]), 4),
+        },
     }
 
 

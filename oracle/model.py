@@ -19,6 +19,12 @@ What the pages fix, and what is a reading:
 * [QSpec-blog, paragraph 2]: W4A4 drafts, W4A16 verifies; verification keeps
   the output that of the high-precision scheme.  Consequence used as a pin:
   greedy self-speculation emits exactly the pure W4A16 greedy tokens.
+* [SpecQuant, Abstract (arXiv)] and ["Speculative Decoding Meets
+  Quantization: Compatibility Evaluation and Hierarchical Framework Design",
+  Abstract (arXiv)]: variants of one base model at several precisions, a
+  middle precision among the drafters.  Here a third mode, ``w4a8``: the
+  same INT4 weights with 8-bit per-token activation codes (``w4a8.py``), as
+  the drafter of the same loop; the same pin holds for it.
 
 The pages name no architecture.  Reading (plain Llama-style decoder):
 pre-norm RMSNorm (weight 1, epsilon from the config); RoPE, rotate-half
@@ -45,8 +51,9 @@ import numpy as np
 
 from .quant import bf16_bits_to_f32, gemm_w4a4, gemm_w4a16, pack_w4, quant_act
 from .verify import verify_greedy
+from .w4a8 import gemm_w4a8, quant_act8
 
-DRAFT, VERIFY = "w4a4", "w4a16"
+DRAFT, VERIFY, DRAFT8 = "w4a4", "w4a16", "w4a8"
 
 
 # --------------------------------------------------------------------------
@@ -133,13 +140,17 @@ class KVCache:
 
 
 def linear(mode, x_bits, packed):
-    """bf16 input bits [M, K] -> fp32 output [M, N] in draft or verify mode."""
+    """bf16 input bits [M, K] -> fp32 output [M, N] in draft (W4A4 or W4A8)
+    or verify mode."""
     Wq, Ws = packed
     if mode == VERIFY:
         y = gemm_w4a16(x_bits, Wq, Ws)
     elif mode == DRAFT:
         Xq, Xs = quant_act(x_bits)
         y = gemm_w4a4(Xq, Xs, Wq, Ws)
+    elif mode == DRAFT8:
+        Xq8, Xs8 = quant_act8(x_bits)
+        y = gemm_w4a8(Xq8, Xs8, Wq, Ws)
     else:
         raise ValueError(mode)
     return y.astype(np.float32)
@@ -247,9 +258,10 @@ def greedy_decode(model, prompts, n_gen, gamma=4, with_margins=False):
     return toks, kv
 
 
-def selfspec_greedy(model, prompts, n_gen, gamma, trace=None):
-    """Greedy self-speculation: per round, gamma W4A4 draft forwards (one row
-    per active sequence, each at its own position), one W4A16 verify forward
+def selfspec_greedy(model, prompts, n_gen, gamma, trace=None, draft_mode=DRAFT):
+    """Greedy self-speculation: per round, gamma draft forwards in
+    `draft_mode` (W4A4, or the W4A8 tier; one row per active sequence, each
+    at its own position), one W4A16 verify forward
     over [last, d_0 .. d_{gamma-1}] that overwrites those KV rows, then the
     greedy acceptance rule; each sequence advances by n_accept + 1.  A
     sequence stops once it has n_gen tokens.  Returns (tokens [B, n_gen],
@@ -274,7 +286,7 @@ def selfspec_greedy(model, prompts, n_gen, gamma, trace=None):
         vtok[:, 0] = last[act]
         dmargin = np.zeros((nA, gamma))
         for j in range(gamma):
-            logits = forward(model, kv, act, L[act] - 1 + j, vtok[:, j], DRAFT)
+            logits = forward(model, kv, act, L[act] - 1 + j, vtok[:, j], draft_mode)
             vtok[:, j + 1] = argmax_first(logits)
             dmargin[:, j] = top2_margin(logits)
         seq = np.repeat(act, gamma + 1)

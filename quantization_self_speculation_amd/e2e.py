@@ -9,6 +9,9 @@ Both modes read the same packed INT4 weights and write the same KV cache
 ("QSpec: Speculative Decoding with Complementary Quantization Schemes",
 Abstract (arXiv)); the verify step accepts the matching prefix and rewrites
 the first mismatch (the agihunt.info review of SpecQuant, method paragraph).
+The drafter may instead run the W4A8 tier (8-bit activation codes on the
+same INT4 weights: a middle precision over one base, "SpecQuant", Abstract
+(arXiv)), with the same verify step.
 
 The W4A16 layers of decode and verify forwards use one kernel family
 (`GEMM_SKINNY`), whose per-row result does not depend on the row count, and
@@ -29,7 +32,7 @@ import torch
 
 from . import binding as b
 
-DRAFT, VERIFY = "w4a4", "w4a16"
+DRAFT, VERIFY, DRAFT8 = "w4a4", "w4a16", "w4a8"
 
 
 def _view(buf, *shape):
@@ -52,11 +55,12 @@ class Decoder:
         self.dev = torch.device(device)
         self.variant = variant
         self.draft_variant = draft_variant
-        # the drafter's layers: W4A4 (the method); W4A16 turns the drafter
-        # into the verifier itself, which must then accept every draft (a
-        # check of the loop's bookkeeping)
-        if draft_mode not in (DRAFT, VERIFY):
-            raise ValueError("draft_mode must be 'w4a4' or 'w4a16'")
+        # the drafter's layers: W4A4 (the method); W4A8 (the middle tier of
+        # several precisions over one base, on the same INT4 weights);
+        # W4A16 turns the drafter into the verifier itself, which must then
+        # accept every draft (a check of the loop's bookkeeping)
+        if draft_mode not in (DRAFT, DRAFT8, VERIFY):
+            raise ValueError("draft_mode must be 'w4a4', 'w4a8' or 'w4a16'")
         self.draft_mode = draft_mode
         dev = self.dev
 
@@ -98,12 +102,15 @@ class Decoder:
         self.logits = torch.empty(Mlog * cfg.vocab, dtype=f32, device=dev)
         self.Xq = torch.empty(Mmax * Kmax // 2, dtype=torch.uint8, device=dev)
         self.Xs = torch.empty(Mmax, dtype=f32, device=dev)
+        # 8-bit codes of a W4A8 forward (draft forwards have B rows)
+        self.Xq8 = torch.empty(B * Kmax, dtype=torch.int8, device=dev)
         ws = 1
         for M in (B, B * (gamma + 1), B * P):
             for W in [t for L in self.layers for t in L.values()] + [self.lm]:
                 _, _, N, K = W
                 ws = max(ws, b.workspace_bytes(b.OP_GEMM_W4A16, M, N, K),
-                         b.workspace_bytes(b.OP_GEMM_W4A4, M, N, K))
+                         b.workspace_bytes(b.OP_GEMM_W4A4, M, N, K),
+                         b.workspace_bytes(b.OP_GEMM_W4A8, M, N, K))
         self.ws = torch.zeros(ws, dtype=torch.uint8, device=dev)   # zero before first use
         self.wsv = torch.empty(max(1, b.workspace_bytes(b.OP_VERIFY, B, max(gamma, 1), cfg.vocab)),
                                dtype=torch.uint8, device=dev)
@@ -135,6 +142,10 @@ class Decoder:
             if not coded:
                 b.quant_act(X, Xq, Xs)
             b.gemm_w4a4(Xq, Xs, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
+        elif mode == DRAFT8:
+            Xq8, Xs = _view(self.Xq8, M, K), _view(self.Xs, M)
+            b.quant_act8(X, Xq8, Xs)
+            b.gemm_w4a8(Xq8, Xs, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
         else:
             b.gemm_w4a16(X, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
 

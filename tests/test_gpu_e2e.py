@@ -193,12 +193,12 @@ def _first_divergence(a, b):
     return int(d[0]) if d.size else None
 
 
-@pytest.mark.parametrize("seed,gamma", [(0, 4), (1, 2)])
-def test_e2e_tiny_selfspec_equals_pure_and_oracle(seed, gamma):
+@pytest.mark.parametrize("seed,gamma,draft", [(0, 4, "w4a4"), (1, 2, "w4a4"), (0, 4, "w4a8")])
+def test_e2e_tiny_selfspec_equals_pure_and_oracle(seed, gamma, draft):
     B, P, n_gen = 4, 16, 32
     cfg, w, prompts = _tiny_case(seed, B, P)
-    say(f"tiny e2e seed={seed} gamma={gamma}")
-    dec = Decoder(cfg, w, B, P, n_gen, gamma)
+    say(f"tiny e2e seed={seed} gamma={gamma} drafter={draft}")
+    dec = Decoder(cfg, w, B, P, n_gen, gamma, draft_mode=draft)
     pure = dec.run(prompts, speculative=False)
     spec = dec.run(prompts, speculative=True)
     assert np.array_equal(spec["tokens"], pure["tokens"])
@@ -222,17 +222,17 @@ def test_e2e_tiny_selfspec_equals_pure_and_oracle(seed, gamma):
 
 
 def _forwards_against_oracle(cfg, w, prompts, gamma=2):
-    """After a shared prefill, every linear layer of a W4A16 and of a W4A4
-    forward matches the oracle layer applied to the GPU's own bf16 input,
+    """After a shared prefill, every linear layer of a W4A16, a W4A4 and a
+    W4A8 forward matches the oracle layer applied to the GPU's own bf16 input,
     within the fp tolerance (op-by-op parity).  The whole W4A16 forward's
     logits are also compared with the oracle forward: there the two sides
     differ at the bf16 rounding points, where a value computed in a different
     order can round one bf16 unit (2**-8 relative) the other way, so that
-    comparison allows 1e-2 of max|logit|.  The W4A4 forward is checked op by op
-    only: each linear layer's output against the oracle layer applied to the
-    GPU's own bf16 input (the quantizer rounds, so a one-ulp difference
-    upstream may move a code, and whole-forward W4A4 values are not
-    comparable)."""
+    comparison allows 1e-2 of max|logit|.  The W4A4 and W4A8 forwards are
+    checked op by op only: each linear layer's output against the oracle
+    layer applied to the GPU's own bf16 input (the quantizer rounds, so a
+    one-ulp difference upstream may move a code, and whole-forward values
+    of the quantized-activation modes are not comparable)."""
     B, P = prompts.shape
     dec = Decoder(cfg, w, B, P, 4, gamma)
     dec.reset()
@@ -245,7 +245,7 @@ def _forwards_against_oracle(cfg, w, prompts, gamma=2):
     packed = {(li, k): model.layers[li][k] for li in range(cfg.n_layers)
               for k in ("qkv", "o", "gu", "down")}
     packed.update({(cfg.n_layers, "lm"): model.lm})
-    for mode in (om.VERIFY, om.DRAFT):
+    for mode in (om.VERIFY, om.DRAFT, om.DRAFT8):
         dec.seq[:B].copy_(torch.arange(B, dtype=torch.int32))
         dec.pos[:B].fill_(P)
         dec.tok[:B].copy_(torch.from_numpy(toks))
@@ -337,9 +337,11 @@ def test_e2e_self_draft_accepts_everything(seed, gamma):
     assert spec["accepted"] == gamma * spec["active_rows"]
 
 
-@pytest.mark.parametrize("seed,gamma", [(0, 4), (2, 3)])
-def test_e2e_tiny_drafts_match_oracle(seed, gamma):
-    """The W4A4 drafter's trajectory against the oracle's self-speculation.
+@pytest.mark.parametrize("seed,gamma,draft", [(0, 4, "w4a4"), (2, 3, "w4a4"), (0, 4, "w4a8"),
+                                              (1, 3, "w4a8")])
+def test_e2e_tiny_drafts_match_oracle(seed, gamma, draft):
+    """The drafter's trajectory (W4A4, or the W4A8 tier) against the
+    oracle's self-speculation with the same drafter.
     Round by round, a sequence that has matched the oracle so far must have
     the same length on both sides, and where its gamma drafted tokens are
     equal its accepted count must be equal too, unless the oracle's verify
@@ -356,12 +358,13 @@ def test_e2e_tiny_drafts_match_oracle(seed, gamma):
     op by op by test_e2e_forwards_against_oracle.)"""
     B, P, n_gen = 4, 16, 32
     cfg, w, prompts = _tiny_case(seed, B, P)
-    say(f"tiny drafts seed={seed} gamma={gamma}")
-    dec = Decoder(cfg, w, B, P, n_gen, gamma)
+    say(f"tiny drafts seed={seed} gamma={gamma} drafter={draft}")
+    dec = Decoder(cfg, w, B, P, n_gen, gamma, draft_mode=draft)
     rec = []
     spec = dec.run(prompts, speculative=True, record=rec)
     tr = []
-    toks, _, st = om.selfspec_greedy(om.Model(cfg, w), prompts, n_gen, gamma, trace=tr)
+    toks, _, st = om.selfspec_greedy(om.Model(cfg, w), prompts, n_gen, gamma, trace=tr,
+                                     draft_mode=draft)
     a_gpu = spec["accepted"] / (gamma * spec["active_rows"])
     a_or = st["accepted"] / st["drafted"]
     say(f"  GPU accepted {spec['accepted']} of {gamma * spec['active_rows']} drafted, "

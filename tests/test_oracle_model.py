@@ -103,14 +103,16 @@ def _tiny(seed, B=3, P=12):
     return model, synth.prompts(rng, B, P, cfg.vocab)
 
 
-@pytest.mark.parametrize("seed,gamma", [(0, 4), (1, 1), (2, 3)])
-def test_selfspec_equals_pure_greedy(seed, gamma):
+@pytest.mark.parametrize("seed,gamma,draft", [(0, 4, om.DRAFT), (1, 1, om.DRAFT), (2, 3, om.DRAFT),
+                                              (0, 4, om.DRAFT8), (3, 2, om.DRAFT8)])
+def test_selfspec_equals_pure_greedy(seed, gamma, draft):
     """Greedy self-speculation emits exactly the pure W4A16 greedy tokens,
-    and the KV rows of every committed position equal pure decoding's."""
+    and the KV rows of every committed position equal pure decoding's, with
+    the W4A4 drafter and with the W4A8 tier as the drafter."""
     model, prompts = _tiny(seed)
     n_gen = 20
     want, kv_ref = om.greedy_decode(model, prompts, n_gen, gamma)
-    got, kv, st = om.selfspec_greedy(model, prompts, n_gen, gamma)
+    got, kv, st = om.selfspec_greedy(model, prompts, n_gen, gamma, draft_mode=draft)
     assert np.array_equal(got, want)
     assert 0 <= st["accepted"] <= st["drafted"] and st["rounds"] >= (n_gen - 1 + gamma) // (gamma + 1)
     # committed positions: prompt + generated tokens that were fed back
@@ -136,6 +138,12 @@ def test_draft_mode_differs_and_rows_are_independent():
     kv3.k[:], kv3.v[:] = kv.k, kv.v
     dr = om.forward(model, kv3, [0, 1], [6, 6], [3, 9], om.DRAFT)
     assert not np.array_equal(dr, both)
+    # the W4A8 tier lies between: closer to the verify logits than W4A4
+    kv4 = om.KVCache(cfg, 2, 16)
+    kv4.k[:], kv4.v[:] = kv.k, kv.v
+    d8 = om.forward(model, kv4, [0, 1], [6, 6], [3, 9], om.DRAFT8)
+    assert not np.array_equal(d8, both)
+    assert np.abs(d8 - both).max() < np.abs(dr - both).max()
 
 
 def test_w4a4_drafts_part_under_one_ulp_perturbation():
