@@ -30,7 +30,7 @@ Sampling (temperature 1):
               if none, the last j with r_j > 0.
 Near ties: the kernels compute the same quantities from fp32 logits with
 their own summation order -- fp32 exponentials of the exactly carried
-difference (about 1 ulp), fp64 sums -- so a decision can differ from exact
+difference (about 2 ulp), fp64 sums -- so a decision can differ from exact
 arithmetic only where the oracle's value sits close to the threshold:
 within 1e-6 (relative) of p/q for an accept test, or within 5e-7 * R of a
 cumulative boundary for the inverse-CDF draw (R = total residual mass; at a

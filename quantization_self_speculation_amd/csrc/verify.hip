@@ -34,8 +34,15 @@ static __device__ __align__(256) uint8_t scratch[kVerifyScratchBytes];
 std::mutex g_scratch_mu;
 std::atomic<void*> g_scratch_ptr[64];
 
-constexpr int kQPC = 2048;        // float4 quads per pass-1 chunk (8192 logits)
-constexpr int kRCW = 2048;        // logits per residual chunk (8 per thread)
+// chunk sizes (measured on MI355X; overridable at build time for sweeps)
+#ifndef QSPEC_VF_QPC
+#define QSPEC_VF_QPC 1024
+#endif
+#ifndef QSPEC_VF_RCW
+#define QSPEC_VF_RCW 2048
+#endif
+constexpr int kQPC = QSPEC_VF_QPC;  // float4 quads per pass-1 chunk (4096 logits)
+constexpr int kRCW = QSPEC_VF_RCW;  // logits per residual chunk (8 per thread)
 constexpr int kMaxRChunks = 4096; // V <= kRCW * kMaxRChunks
 
 __device__ __forceinline__ void argmax_merge(float& bv, int& bi, float v, int i) {
@@ -45,26 +52,28 @@ __device__ __forceinline__ void argmax_merge(float& bv, int& bi, float v, int i)
   }
 }
 
-// exp(a - b) for fp32 a, b: the rounding error of the subtraction is carried
-// (two-sum) and applied to first order, so the result is within about 1 ulp
-// of exp of the exact difference.  a == -inf gives 0.
+// exp(a - b) for fp32 a, b <= a + 88: the rounding error of the subtraction
+// is carried (Knuth's two-sum), s log2(e) is split into its fp32 rounding h
+// and the remainder l (the FMA error-free product, TwoProduct of Ogita, Rump
+// and Oishi, with log2(e) itself as a two-float constant), the hardware
+// exp2 (v_exp_f32, about 1 ulp) takes h, and the remainder and the
+// subtraction error are applied to first order: exp(x) = 2^h (1 + l ln 2 +
+// err) up to terms below 1e-10 relative.  The result is within about 2 ulp
+// of exp of the exact difference; a == -inf gives 0, and results below the
+// fp32 normal range may be flushed to zero (they cannot move a sum of terms
+// of which the largest is 1).
 __device__ __forceinline__ float exp_diff(float a, float b) {
   if (a == -INFINITY) return 0.f;
+  constexpr float kLog2eHi = 1.44269502162933349609375f;    // fp32 rounding of log2(e)
+  constexpr float kLog2eLo = 1.925962991126e-8f;          // log2(e) - kLog2eHi
+  constexpr float kLn2 = 0.693147182464599609375f;          // fp32 rounding of ln(2)
   const float s = a - b;
   const float bb = s - a;
   const float err = (a - (s - bb)) + (-b - bb);
-  const float e = expf(s);
-  return fmaf(e, err, e);
-}
-
-// merge two (max m, sum s = sum exp(x - m)) pairs; sums are fp64 and the
-// rescale uses the fp64 exp of an exact fp64 difference
-__device__ __forceinline__ void lse_merge(float& m, double& s, float m2, double s2) {
-  const float mm = fmaxf(m, m2);
-  const double a = (m == -INFINITY) ? 0.0 : s * exp((double)m - (double)mm);
-  const double b = (m2 == -INFINITY) ? 0.0 : s2 * exp((double)m2 - (double)mm);
-  s = a + b;
-  m = mm;
+  const float h = s * kLog2eHi;
+  const float l = fmaf(s, kLog2eHi, -h) + s * kLog2eLo;
+  const float e = __builtin_amdgcn_exp2f(h);
+  return fmaf(e, fmaf(l, kLn2, err), e);
 }
 
 // Geometry of a row's pass-1 split: elements [0, a0) are a scalar head, then
@@ -232,7 +241,7 @@ __device__ __forceinline__ void row_lse(const float* pm, const double* ps, int64
   double s = 0.0;
   for (int c = lane; c < nck; c += 64) {
     const float mc = pm[row * nck + c];
-    if (mc != -INFINITY) s += ps[row * nck + c] * exp((double)mc - (double)m);
+    s += ps[row * nck + c] * (double)exp_diff(mc, m);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
@@ -265,20 +274,60 @@ __device__ Decision block_decide(const float* __restrict__ tgt, const float* __r
   __shared__ Decision sdec;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nr = 2 * gamma + 1;  // target rows 0..gamma, then draft rows
-  for (int r = w; r < nr; r += 4) {
-    const int64_t row = r <= gamma ? b * (gamma + 1) + r : rows_t + b * gamma + (r - gamma - 1);
-    float M;
-    double S;
-    row_lse(pm, ps, row, nck, lane, M, S);
-    if (lane == 0) {
-      lm[r] = M;
-      lsum[r] = S;
+  auto row_of = [&](int r) -> int64_t {
+    return r <= gamma ? b * (gamma + 1) + r : rows_t + b * gamma + (r - gamma - 1);
+  };
+  // the drafted tokens' logits are requested first: they do not depend on
+  // the merges
+  float xt = 0.f, xd = 0.f;
+  if (tid < gamma) {
+    const int x = min(max(dt[b * gamma + tid], 0), (int)(V - 1));
+    xt = tgt[(b * (gamma + 1) + tid) * V + x];
+    xd = drf[(b * gamma + tid) * V + x];
+  }
+  if (nck <= 64) {
+    // every row of this wavefront (rows w, w + 4, ...) with its chunk pairs
+    // requested at once, one chunk per lane, then merged row by row
+    constexpr int RPW = (2 * QSPEC_MAX_GAMMA + 1 + 3) / 4;
+    float pmv[RPW];
+    double psv[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int r = w + 4 * k;
+      pmv[k] = -INFINITY;
+      psv[k] = 0.0;
+      if (r < nr && lane < nck) {
+        pmv[k] = pm[row_of(r) * nck + lane];
+        psv[k] = ps[row_of(r) * nck + lane];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int r = w + 4 * k;
+      if (r >= nr) break;  // uniform over the wavefront
+      const float M = wave_max(pmv[k]);
+      double S = psv[k] * (double)exp_diff(pmv[k], M);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
+      if (lane == 0) {
+        lm[r] = M;
+        lsum[r] = S;
+      }
+    }
+  } else {
+    for (int r = w; r < nr; r += 4) {
+      float M;
+      double S;
+      row_lse(pm, ps, row_of(r), nck, lane, M, S);
+      if (lane == 0) {
+        lm[r] = M;
+        lsum[r] = S;
+      }
     }
   }
   if (tid < gamma) {
-    const int x = min(max(dt[b * gamma + tid], 0), (int)(V - 1));
-    lxt[tid] = tgt[(b * (gamma + 1) + tid) * V + x];
-    lxd[tid] = drf[(b * gamma + tid) * V + x];
+    lxt[tid] = xt;
+    lxd[tid] = xd;
   }
   __syncthreads();
   if (w == 0) {

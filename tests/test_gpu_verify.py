@@ -240,3 +240,27 @@ def test_sampling_many_sequences_flagged_agreement():
     say(f"  over 256 sequences: flagged {flagged}, GPU equal on {same}")
     assert flagged <= 256 // 4
     assert same >= flagged - max(1, flagged // 4)
+
+
+def test_workspace_reused_across_shapes_and_modes():
+    """One workspace (never cleared, first filled with garbage) serves a run
+    of greedy and sampling calls of different (B, gamma, V): every call
+    writes each workspace element it reads later, so no call depends on what
+    an earlier one left behind."""
+    import torch
+    from quantization_self_speculation_amd import binding as b
+    shapes = [(32, 4, 50257), (5, 16, 8195), (64, 2, 4096), (3, 8, 128256)]
+    nb = max(q.workspace_bytes(b.OP_VERIFY, B, g, V) for (B, g, V) in shapes)
+    ws = torch.full((nb,), 0x5A, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for i, (B, gamma, V) in enumerate(shapes):
+            say(f"verify workspace reuse rep={rep} B={B} gamma={gamma} V={V}")
+            rng, tgt, drf = _logits(60 + i, B, gamma, V)
+            d = synth.gumbel_drafts(rng, drf)
+            n_ref, out_ref = oracle.verify_greedy(tgt, d)
+            n, out = q.verify(q.VERIFY_GREEDY, dev(tgt), dev(d), ws=ws)
+            assert np.array_equal(host(n), n_ref) and np.array_equal(host(out), out_ref)
+            ua = synth.uniforms(rng, (B, gamma))
+            us = synth.uniforms(rng, (B,))
+            n, out = q.verify(q.VERIFY_SAMPLE, dev(tgt), dev(d), dev(drf), dev(ua), dev(us), ws=ws)
+            _check_sampling(tgt, drf, d, ua, us, host(n), host(out), max_flag=max(1, B // 4))
