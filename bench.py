@@ -748,6 +748,7 @@ def run(args):
             c = ceil["hbm_read_GBps"][k]
             v["read_ceiling_GBps"] = c
             v["frac_of_measured"] = round(v["GBps"] / c, 4)
+            v["traffic"] = read_traffic("w4a16_" + k)
         log("prefill-shaped GEMMs")
         line["prefill_m2048"] = measure_prefill(torch, q, wl)
         al = line["prefill_m2048"]["all"]
@@ -772,18 +773,23 @@ def run(args):
 
 
 # ---------------------------------------------------------------------------
-# HBM traffic of the dominant kernel from rocprofv3 counters.
-#   1) rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- python bench.py --counters
+# HBM traffic of a GEMM from rocprofv3 counters.
+#   1) rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- python bench.py --counters T
 #   2) the same with WRITE_SIZE (a separate run: one counter block per pass)
-#   3) python bench.py --traffic <fetch counter csv> <write counter csv>
-# --counters runs a plain 1 GiB fp32 copy (calibration: 1 GiB read + 1 GiB
-# written) and the dominant kernel's launches; --traffic scales the dominant
-# kernel's mean FETCH/WRITE KiB per dispatch by the copy's measured/known ratio
-# and writes profiles/traffic_w4a4_gate_up_M8.json, stamped with the hash of
-# the GEMM source so a later kernel change voids it.
+#   3) python bench.py --traffic <fetch counter csv> <write counter csv> --counters T
+# --counters T runs a plain 1 GiB fp32 copy (calibration: 1 GiB read + 1 GiB
+# written) and 20 launches of target T (the dominant kernel by default, or
+# one of the W4A16 decode points); --traffic scales T's mean FETCH/WRITE KiB
+# per dispatch by the copy's measured/known ratio and writes
+# profiles/traffic_<T>.json, stamped with the hash of the GEMM source so a
+# later kernel change voids it.
 COPY_ELEMS = 1 << 28
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w4a4_gate_up_M8.json")
-W4A4_SKINNY_TAG = "skinny_kernel<1,"
+COUNTER_TARGETS = ("w4a4_gate_up_M8", "w4a16_gate_up_M5", "w4a16_down_M5", "w4a16_lm_head_M1")
+GEMM_KERNEL_TAGS = ("skinny_kernel", "stream_kernel", "gemv_kernel", "prefill_kernel")
+
+
+def traffic_file(target):
+    return os.path.join(ROOT, "profiles", f"traffic_{target}.json")
 
 
 def run_only(which):
@@ -817,7 +823,50 @@ def _gemm_source_hash():
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def run_counters():
+def _counter_workload(torch, q, target):
+    """-> (launch(), algorithmic bytes of one launch) for a counter target"""
+    wl = Decode(torch, q)
+    if target == "w4a4_gate_up_M8":
+        p = [x for x in wl.proj if x["name"] == "gate_up"][0]
+        q.quant_act(p["X4"], p["Xq"], p["Xs"])
+        cps = p["copies"][:4]
+
+        def f():
+            for Wq, Ws in cps:
+                q.gemm_w4a4(p["Xq"], p["Xs"], Wq, Ws, Y=p["Y4"], ws=p["ws4"])
+        return f, 4, wl.bytes_w4a4(p)
+    if target in ("w4a16_gate_up_M5", "w4a16_down_M5"):
+        p = [x for x in wl.proj if x["name"] == target.split("_", 1)[1].rsplit("_", 1)[0]][0]
+        N, K = p["N"], p["K"]
+        X = p["X16"][:5].contiguous()
+        Y = torch.empty((5, N), dtype=torch.float32, device="cuda:0")
+        ws = torch.zeros(max(1, q.workspace_bytes(2, 5, N, K)), dtype=torch.uint8, device="cuda:0")
+        cps = p["copies"]
+
+        def f():
+            for Wq, Ws in cps:
+                q.gemm_w4a16(X, Wq, Ws, Y=Y, ws=ws)
+        return f, len(cps), wbytes(N, K) + 5 * K * 2 + 5 * N * 4
+    import synth
+    del wl
+    N, K = 128256, 4096
+    cps = []
+    for _ in range(2):
+        W = torch.empty((N, K), dtype=torch.float32, device="cuda:0").normal_(0.0, 0.02)
+        cps.append(q.pack_w4(W))
+        del W
+    X = torch.from_numpy(synth.activations(synth.make_rng(1, 3), 1, K).view(np.int16)).view(
+        torch.bfloat16).to("cuda:0")
+    Y = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
+    ws = torch.zeros(max(1, q.workspace_bytes(2, 1, N, K)), dtype=torch.uint8, device="cuda:0")
+
+    def f():
+        for Wq, Ws in cps:
+            q.gemm_w4a16(X, Wq, Ws, Y=Y, ws=ws)
+    return f, 2, wbytes(N, K) + K * 2 + N * 4
+
+
+def run_counters(target):
     import torch
     import quantization_self_speculation_amd as q
     q.lib()
@@ -828,13 +877,12 @@ def run_counters():
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    wl = Decode(torch, q)
-    p = [x for x in wl.proj if x["name"] == "gate_up"][0]
-    q.quant_act(p["X4"], p["Xq"], p["Xs"])
-    for _ in range(5):
-        wl.dominant_launches()
+    f, per_call, _ = _counter_workload(torch, q, target)
+    calls = -(-20 // per_call)
+    for _ in range(calls):
+        f()
     torch.cuda.synchronize()
-    log("counters workload done: 3 copies of 1 GiB, 20 W4A4 gate|up M=8 launches")
+    log(f"counters workload done: 3 copies of 1 GiB, {calls * per_call} launches of {target}")
 
 
 def _counter_means(path, counter):
@@ -847,34 +895,41 @@ def _counter_means(path, counter):
             key = (r["Kernel_Name"], r["Dispatch_Id"])
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     copy = [v for (k, _), v in per.items() if "copy" in k.lower() or "elementwise" in k.lower()]
-    dom = [v for (k, _), v in per.items() if W4A4_SKINNY_TAG in k.replace(" ", "")]
+    dom = [v for (k, _), v in per.items() if any(t in k for t in GEMM_KERNEL_TAGS)]
     if not copy or not dom:
-        raise SystemExit(f"{path}: no copy ({len(copy)}) or W4A4 ({len(dom)}) dispatches for {counter}")
+        raise SystemExit(f"{path}: no copy ({len(copy)}) or GEMM ({len(dom)}) dispatches for {counter}")
     # the 1 GiB copy is the largest elementwise dispatch
     return max(copy), sum(dom) / len(dom), len(dom)
 
 
-def write_traffic(fetch_csv, write_csv):
+def write_traffic(fetch_csv, write_csv, target):
+    import torch  # noqa: F401  (the algorithmic bytes come from the workload's shapes)
     known_kib = COPY_ELEMS * 4 / 1024.0
     cf, df, nf = _counter_means(fetch_csv, "FETCH_SIZE")
     cw, dw, nw = _counter_means(write_csv, "WRITE_SIZE")
     sf, sw = known_kib / cf, known_kib / cw
-    rec = {"kernel": "w4a4_gate_up_M8", "gemm_source_sha256_16": _gemm_source_hash(),
+    alg = {"w4a4_gate_up_M8": wbytes(37888, 3584) + 8 * 3584 // 2 + 8 * 4 + 8 * 37888 * 4,
+           "w4a16_gate_up_M5": wbytes(37888, 3584) + 5 * 3584 * 2 + 5 * 37888 * 4,
+           "w4a16_down_M5": wbytes(3584, 18944) + 5 * 18944 * 2 + 5 * 3584 * 4,
+           "w4a16_lm_head_M1": wbytes(128256, 4096) + 4096 * 2 + 128256 * 4}[target]
+    moved = int(round((df * sf + dw * sw) * 1024))
+    rec = {"kernel": target, "gemm_source_sha256_16": _gemm_source_hash(),
            "fetch_kib_per_dispatch": round(df, 1), "write_kib_per_dispatch": round(dw, 1),
            "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
            "fetch_scale": round(sf, 5), "write_scale": round(sw, 5),
            "dispatches": [nf, nw],
-           "bytes_per_launch": int(round((df * sf + dw * sw) * 1024))}
-    with open(TRAFFIC_FILE, "w") as f:
+           "bytes_per_launch": moved, "algorithmic_bytes": alg,
+           "traffic_over_algorithmic": round(moved / alg, 4)}
+    with open(traffic_file(target), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
 
-def read_traffic():
+def read_traffic(target="w4a4_gate_up_M8"):
     """the stored traffic figure, or None when absent or taken on another
     version of the GEMM source"""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(target)))
     except Exception:
         return None
     if rec.get("gemm_source_sha256_16") != _gemm_source_hash():
@@ -893,20 +948,22 @@ def main():
                     help="skip the decode-GEMV, prefill and verify side measurements")
     ap.add_argument("--only", choices=["decode_gemv", "prefill", "verify", "e2e", "batch", "rotation", "w4a8", "llama"],
                     help="run one side measurement alone and print its JSON (for profiling)")
-    ap.add_argument("--counters", action="store_true",
-                    help="run only the copy calibration and the dominant kernel (for rocprofv3 --pmc)")
+    ap.add_argument("--counters", nargs="?", const=COUNTER_TARGETS[0], choices=COUNTER_TARGETS,
+                    help="run only the copy calibration and 20 launches of one GEMM (the dominant "
+                         "kernel by default; for rocprofv3 --pmc)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 counter CSVs into the stored traffic figure")
+                    help="turn two rocprofv3 counter CSVs of --counters [T] into the stored "
+                         "traffic figure of T")
     args = ap.parse_args()
     if args.traffic:
-        write_traffic(*args.traffic)
+        write_traffic(*args.traffic, target=args.counters or COUNTER_TARGETS[0])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     if args.counters:
-        run_counters()
+        run_counters(args.counters)
         return
     if args.only:
         run_only(args.only)
