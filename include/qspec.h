@@ -327,7 +327,7 @@ qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V,
  * bytes per device, part of the library's code object and held until the
  * process ends.  Sizes whose qspec_workspace_bytes(QSPEC_OP_VERIFY, B, gamma,
  * V) exceeds it are rejected with QSPEC_ERR_WORKSPACE before anything is
- * enqueued (B = 256, gamma = 8, V = 152064 needs about 1.4 MiB).  Nothing is
+ * enqueued (B = 256, gamma = 8, V = 152064 needs about 2.5 MiB).  Nothing is
  * allocated: no hipMalloc, no hipFree.  Every call on one device shares that
  * device's array and leaves its contents behind (no call depends on them);
  * calls that overlap in time on one device -- on different streams, or from
