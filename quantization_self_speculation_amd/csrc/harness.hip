@@ -217,7 +217,17 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
 // Every step depends on T alone, so a row's output is the same whatever
 // other rows share the launch.  Output bf16.
 constexpr int kHeadDim = 128;
-constexpr int kAttnWaves = 8;
+// Block shape (measured on MI355X; the key split is part of a row's result,
+// so one shape serves every M: 8 wavefronts with 32-key chunks beat 64-key
+// chunks at every decode, verify and prefill point -- 192 instead of 256
+// registers -- and 4 or 16 wavefronts lose at one end or the other).
+#ifndef QSPEC_ATTN_WAVES
+#define QSPEC_ATTN_WAVES 8
+#endif
+#ifndef QSPEC_ATTN_CHUNK
+#define QSPEC_ATTN_CHUNK 32
+#endif
+constexpr int kAttnWaves = QSPEC_ATTN_WAVES;
 
 // Sum over the 16 lanes of a DPP row, by VALU lane moves (no LDS round trip):
 // swap neighbours, swap pairs (now every lane holds its quad's sum), then add
@@ -232,7 +242,7 @@ __device__ __forceinline__ float sum16_dpp(float v) {
   return v;
 }
 constexpr int kAttnHeads = 4;    // query heads per pass
-constexpr int kAttnChunk = 64;   // keys per wavefront chunk (all loads in flight)
+constexpr int kAttnChunk = QSPEC_ATTN_CHUNK;  // keys per wavefront chunk (all loads in flight)
 constexpr int kAttnQuads = kAttnChunk / 4;
 
 __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
