@@ -11,9 +11,8 @@
 // The work is one streaming pass over the logits (HBM-bound) plus, when
 // sampling, one pass over the one or two rows each sequence samples from:
 //   greedy:   pass1 (chunk argmax, lowest index on ties) -> decide
-//   sampling: pass1 (chunk max and sum of exp) -> residual chunk sums ->
-//             inverse-CDF select, the decision (merge chunks, accept tests)
-//             taken at the start of each of the last two
+//   sampling: pass1 (chunk max and sum of exp) -> decide (merge chunks,
+//             accept tests) -> residual chunk sums -> inverse-CDF select
 // Chunks are reduced in fixed order (no atomics): the same inputs give the
 // same bits.
 #include <atomic>
@@ -261,9 +260,8 @@ struct Decision {
 // fetched in parallel, then lane i of the first wavefront runs the accept
 // test of draft i and the lowest rejecting lane decides.  p(x) and q(x) are
 // fp64: exact fp64 exponent of the exact difference over the pass-1 sums.
-// The kernels that need the decision each take it this way (the same
-// operations on the same data, so every block of a sequence agrees), which
-// saves a launch between pass 1 and the residual pass.
+// Taken once per sequence (sample_decide_kernel): repeated at the start of
+// every residual block it cost more than the launch it saved (measured).
 __device__ Decision block_decide(const float* __restrict__ tgt, const float* __restrict__ drf,
                                  const int32_t* __restrict__ dt, const float* __restrict__ ua,
                                  int gamma, int64_t V, int nck, const float* __restrict__ pm,
@@ -356,6 +354,17 @@ __device__ Decision block_decide(const float* __restrict__ tgt, const float* __r
   return sdec;
 }
 
+// The sampling decision of each sequence, once (one block per sequence), for
+// the residual and select passes to read.
+__global__ __launch_bounds__(256) void sample_decide_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
+    const float* __restrict__ ua, int gamma, int64_t V, int nck, const float* __restrict__ pm,
+    const double* __restrict__ ps, int64_t rows_t, Decision* __restrict__ dec) {
+  const int64_t b = blockIdx.x;
+  const Decision D = block_decide(tgt, drf, dt, ua, gamma, V, nck, pm, ps, rows_t, b);
+  if (threadIdx.x == 0) dec[b] = D;
+}
+
 // r_j of the row a sequence samples from, in fp64
 __device__ __forceinline__ double resid(const float* rt, const float* rd, int64_t j, int kind,
                                         float Mt, double iSt, float Md, double iSd) {
@@ -369,14 +378,13 @@ __device__ __forceinline__ double resid(const float* rt, const float* rd, int64_
 // thread, coalesced).  rs[b][c] = sum r, pp[b][c] = sum p (fp64).
 __global__ __launch_bounds__(256) void resid_sums_kernel(
     const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
-    const float* __restrict__ ua, int gamma, int64_t V, int nck, const float* __restrict__ pm,
-    const double* __restrict__ ps, int64_t rows_t, int rnck, double* __restrict__ rs,
+    int gamma, int64_t V, int rnck, const Decision* __restrict__ dec, double* __restrict__ rs,
     double* __restrict__ pp) {
   constexpr int EPT = kRCW / 256;
   __shared__ double red[2][4];
   const int c = blockIdx.x;
   const int64_t b = blockIdx.y;
-  const Decision D = block_decide(tgt, drf, dt, ua, gamma, V, nck, pm, ps, rows_t, b);
+  const Decision D = dec[b];
   const double iSt = 1.0 / D.St, iSd = 1.0 / D.Sd;
   const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
   const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
@@ -421,8 +429,7 @@ __global__ __launch_bounds__(256) void resid_sums_kernel(
 // block-wide exclusive scan gives every thread its starting cumulative sum.
 __global__ __launch_bounds__(256) void sample_select_kernel(
     const float* __restrict__ tgt, const float* __restrict__ drf, const int32_t* __restrict__ dt,
-    const float* __restrict__ ua, const float* __restrict__ us, int gamma, int64_t V, int nck,
-    const float* __restrict__ pm, const double* __restrict__ ps, int64_t rows_t, int rnck,
+    const float* __restrict__ us, int gamma, int64_t V, int rnck, const Decision* __restrict__ dec,
     const double* __restrict__ rs, const double* __restrict__ pp, int32_t* __restrict__ n_accept,
     int32_t* __restrict__ out_tok) {
   constexpr int EPT = kRCW / 256;
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
   __shared__ double sh_base, sh_thr;
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const Decision D = block_decide(tgt, drf, dt, ua, gamma, V, nck, pm, ps, rows_t, b);
+  const Decision D = dec[b];
   const double iSt = 1.0 / D.St, iSd = 1.0 / D.Sd;
   const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
   const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
@@ -568,7 +575,7 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
 
 struct VerifyLayout {
   int nck, rnck;
-  size_t pm, ps, pi, rs, pp, total;  // byte offsets
+  size_t pm, ps, pi, dec, rs, pp, total;  // byte offsets
 };
 
 VerifyLayout layout(int64_t B, int gamma, int64_t V) {
@@ -585,6 +592,7 @@ VerifyLayout layout(int64_t B, int gamma, int64_t V) {
   L.pm = take((size_t)rows * L.nck * sizeof(float));
   L.ps = take((size_t)rows * L.nck * sizeof(double));
   L.pi = take((size_t)B * (gamma + 1) * L.nck * sizeof(int));
+  L.dec = take((size_t)B * sizeof(Decision));
   L.rs = take((size_t)B * L.rnck * sizeof(double));
   L.pp = take((size_t)B * L.rnck * sizeof(double));
   L.total = off;
@@ -642,6 +650,7 @@ hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_
   float* pm = reinterpret_cast<float*>(w + L.pm);
   double* ps = reinterpret_cast<double*>(w + L.ps);
   int* pi = reinterpret_cast<int*>(w + L.pi);
+  Decision* dec = reinterpret_cast<Decision*>(w + L.dec);
   double* rs = reinterpret_cast<double*>(w + L.rs);
   double* pp = reinterpret_cast<double*>(w + L.pp);
   const int64_t rows_t = B * (gamma + 1);
@@ -659,13 +668,15 @@ hipError_t launch_verify(int mode, int64_t B, int gamma, int64_t V, const int32_
                      target_logits, draft_logits, rows_t, V, L.nck, pm, ps, pi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sample_decide_kernel, dim3((unsigned)B), dim3(256), 0, s, target_logits,
+                     draft_logits, draft_tok, u_accept, gamma, V, L.nck, pm, ps, rows_t, dec);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(resid_sums_kernel, dim3(L.rnck, (unsigned)B), dim3(256), 0, s,
-                     target_logits, draft_logits, draft_tok, u_accept, gamma, V, L.nck, pm, ps,
-                     rows_t, L.rnck, rs, pp);
+                     target_logits, draft_logits, draft_tok, gamma, V, L.rnck, dec, rs, pp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(sample_select_kernel, dim3((unsigned)B), dim3(256), 0, s, target_logits,
-                     draft_logits, draft_tok, u_accept, u_sample, gamma, V, L.nck, pm, ps, rows_t,
-                     L.rnck, rs, pp, n_accept, out_tok);
+                     draft_logits, draft_tok, u_sample, gamma, V, L.rnck, dec, rs, pp, n_accept,
+                     out_tok);
   return hipGetLastError();
 }
 
