@@ -76,6 +76,17 @@ qspec_status qspec_attention(const float* q, const uint16_t* kcache, const uint1
                              const int32_t* pos, int64_t B, int64_t cap, uint16_t* out,
                              qspec_stream stream);
 
+/* qspec_rope_kv followed by qspec_attention, in one launch, for launches
+ * whose M rows belong to M different sequences (decode and draft forwards:
+ * one row per sequence).  Same arguments, results (bit for bit) and errors as
+ * the two calls; out bf16 [M][n_heads * 128].  Precondition, not checked:
+ * no two rows share a sequence (rows of one sequence would race on its
+ * cache rows; results are then undefined, every access stays in bounds). */
+qspec_status qspec_rope_attention(const float* qkv, int64_t M, int n_heads, int n_kv,
+                                  const int32_t* seq, const int32_t* pos, double rope_base,
+                                  float* q_out, uint16_t* kcache, uint16_t* vcache, int64_t B,
+                                  int64_t cap, uint16_t* out, qspec_stream stream);
+
 /* qspec_add_rmsnorm with the drafter's input in the same pass: besides y,
  * yq [M][d/2] and ys [M] receive exactly what qspec_quant_act gives for the
  * bf16 rows y (per-token absmax / 7, codes rne(y / s) clamped, nibble

@@ -38,6 +38,7 @@ from .binding import (  # noqa: F401
     add_rmsnorm,
     rope_kv,
     attention,
+    rope_attention,
     silu_mul,
     add_rmsnorm_quant,
     argmax,

@@ -69,6 +69,8 @@ def lib():
             "qspec_add_rmsnorm": (I, [P, I64, P, I64, I64, I64, ctypes.c_double, P, P]),
             "qspec_rope_kv": (I, [P, I64, I, I, P, P, ctypes.c_double, P, P, P, I64, I64, P]),
             "qspec_attention": (I, [P, P, P, I64, I, I, P, P, I64, I64, P, P]),
+            "qspec_rope_attention": (I, [P, I64, I, I, P, P, ctypes.c_double, P, P, P, I64, I64, P,
+                                         P]),
             "qspec_silu_mul": (I, [P, I64, I64, P, P]),
             "qspec_add_rmsnorm_quant": (I, [P, I64, P, I64, I64, I64, ctypes.c_double, P, P, P, P]),
             "qspec_argmax": (I, [P, I64, I64, P, I64, P]),
@@ -424,6 +426,21 @@ def attention(q, kcache, vcache, seq, pos, out, n_heads, n_kv):
     _check(lib().qspec_attention(_ptr(q), _ptr(kcache), _ptr(vcache), int(q.shape[0]), n_heads,
                                  n_kv, _ptr(seq), _ptr(pos), B, cap, _ptr(out), _stream()),
            "qspec_attention")
+
+
+def rope_attention(qkv, seq, pos, q_out, kcache, vcache, out, n_heads, n_kv, rope_base):
+    """rope_kv then attention in one launch; the rows must belong to
+    different sequences (one row per sequence)"""
+    _dev(qkv, "qkv", torch.float32)
+    _dev(q_out, "q_out", torch.float32)
+    _dev(kcache, "kcache", torch.bfloat16)
+    _dev(vcache, "vcache", torch.bfloat16)
+    _dev(out, "out", torch.bfloat16)
+    B, _, cap, _ = kcache.shape
+    _check(lib().qspec_rope_attention(_ptr(qkv), int(qkv.shape[0]), n_heads, n_kv, _ptr(seq),
+                                      _ptr(pos), float(rope_base), _ptr(q_out), _ptr(kcache),
+                                      _ptr(vcache), B, cap, _ptr(out), _stream()),
+           "qspec_rope_attention")
 
 
 def silu_mul(gu, a):

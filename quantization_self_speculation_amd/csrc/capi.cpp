@@ -480,6 +480,28 @@ qspec_status qspec_attention(const float* q, const uint16_t* kcache, const uint1
                     "attention launch");
 }
 
+qspec_status qspec_rope_attention(const float* qkv, int64_t M, int n_heads, int n_kv,
+                                  const int32_t* seq, const int32_t* pos, double rope_base,
+                                  float* q_out, uint16_t* kcache, uint16_t* vcache, int64_t B,
+                                  int64_t cap, uint16_t* out, qspec_stream stream) {
+  QS_REQUIRE(M >= 1 && M <= kMaxDim, QSPEC_ERR_SHAPE, "need M >= 1");
+  QS_TRY(check_heads(n_heads, n_kv));
+  QS_REQUIRE(n_kv <= 65535, QSPEC_ERR_SHAPE, "n_kv too large");
+  QS_TRY(check_cache(B, cap));
+  QS_REQUIRE(rope_base > 0.0, QSPEC_ERR_SHAPE, "rope_base must be > 0");
+  QS_EPTR(qkv);
+  QS_EPTR(seq);
+  QS_EPTR(pos);
+  QS_EPTR(q_out);
+  QS_EPTR(kcache);
+  QS_EPTR(vcache);
+  QS_EPTR(out);
+  QS_TRY(device_check());
+  return hip_result(launch_rope_attention(qkv, M, n_heads, n_kv, seq, pos, rope_base, q_out,
+                                          kcache, vcache, B, cap, out, (hipStream_t)stream),
+                    "rope_attention launch");
+}
+
 qspec_status qspec_silu_mul(const float* gu, int64_t M, int64_t ffn, uint16_t* a,
                             qspec_stream stream) {
   QS_REQUIRE(M >= 1 && ffn >= 1 && M * ffn <= ((int64_t)1 << 40), QSPEC_ERR_SHAPE,

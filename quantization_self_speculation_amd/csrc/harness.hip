@@ -245,10 +245,11 @@ constexpr int kAttnHeads = 4;    // query heads per pass
 constexpr int kAttnChunk = QSPEC_ATTN_CHUNK;  // keys per wavefront chunk (all loads in flight)
 constexpr int kAttnQuads = kAttnChunk / 4;
 
-__global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
-    const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    int H, int Hkv, const int32_t* __restrict__ seq, const int32_t* __restrict__ pos, int64_t B,
-    int64_t cap, uint16_t* __restrict__ out) {
+__device__ __forceinline__ void attend(const float* __restrict__ q, const uint16_t* __restrict__ kc,
+                                       const uint16_t* __restrict__ vc, int H, int Hkv,
+                                       const int32_t* __restrict__ seq,
+                                       const int32_t* __restrict__ pos, int64_t B, int64_t cap,
+                                       uint16_t* __restrict__ out) {
   // LDS: per wavefront, the chunk's scores [kAttnHeads][kAttnChunk]; then the
   // wavefronts' results: o [kAttnWaves][kAttnHeads][128], m and sum
   // [kAttnWaves][kAttnHeads]
@@ -398,6 +399,65 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
     }
     __syncthreads();  // before the next head pass reuses the LDS
   }
+}
+
+__global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
+    const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    int H, int Hkv, const int32_t* __restrict__ seq, const int32_t* __restrict__ pos, int64_t B,
+    int64_t cap, uint16_t* __restrict__ out) {
+  attend(q, kc, vc, H, Hkv, seq, pos, B, cap, out);
+}
+
+// RoPE + KV write + attention in one launch, for launches whose rows belong
+// to different sequences (one row per sequence: decode and draft forwards).
+// Block (m, g) first does rope_kv's work for row m restricted to kv head g --
+// the query heads of g rotated into q, key head g rotated and value head g
+// written into the caches at the row's position, the same fp64 arithmetic
+// and roundings -- then attends exactly as attention_kernel does.  The row's
+// own key and value are written by this block before its barrier; no other
+// block writes to this sequence's cache rows.
+__global__ __launch_bounds__(64 * kAttnWaves) void rope_attention_kernel(
+    const float* __restrict__ qkv, int H, int Hkv, const int32_t* __restrict__ seq,
+    const int32_t* __restrict__ pos, double base, float* __restrict__ q, uint16_t* __restrict__ kc,
+    uint16_t* __restrict__ vc, int64_t B, int64_t cap, uint16_t* __restrict__ out) {
+  __shared__ double cs[2][kHeadDim / 2];
+  const int64_t m = blockIdx.x;
+  const int g = blockIdx.y;
+  const int hd = kHeadDim, half = hd / 2, grp = H / Hkv;
+  const int p = pos[m];
+  const int64_t b = seq[m];
+  const bool ok = b >= 0 && b < B && p >= 0 && p < cap;
+  if (ok) {  // uniform
+    if (threadIdx.x < half) {
+      const double f = pow(base, -2.0 * (double)threadIdx.x / (double)hd);
+      double sn, c;
+      sincos((double)p * f, &sn, &c);
+      cs[0][threadIdx.x] = c;
+      cs[1][threadIdx.x] = sn;
+    }
+    __syncthreads();
+    const float* r = qkv + m * (int64_t)((H + 2 * Hkv) * hd);
+    // the grp query heads of g, then key head g (index grp)
+    for (int t = threadIdx.x; t < (grp + 1) * half; t += blockDim.x) {
+      const int hh = t / half, i = t % half;
+      const int h = hh < grp ? g * grp + hh : H + g;  // column block of qkv
+      const double a = r[h * hd + i], bb = r[h * hd + i + half];
+      const double c = cs[0][i], sn = cs[1][i];
+      const double lo = a * c - bb * sn, hi = bb * c + a * sn;
+      if (hh < grp) {
+        q[m * (H * hd) + h * hd + i] = (float)lo;
+        q[m * (H * hd) + h * hd + i + half] = (float)hi;
+      } else {
+        uint16_t* dst = kc + ((b * Hkv + g) * cap + p) * hd;
+        dst[i] = f64_to_bf16_rne(lo);
+        dst[i + half] = f64_to_bf16_rne(hi);
+      }
+    }
+    for (int t = threadIdx.x; t < hd; t += blockDim.x)
+      vc[((b * Hkv + g) * cap + p) * hd + t] = f32_to_bf16_rne(r[(H + Hkv + g) * hd + t]);
+  }
+  __syncthreads();  // the rotated queries and this row's key and value are in memory
+  attend(q, kc, vc, H, Hkv, seq, pos, B, cap, out);
 }
 
 // ------------------------------------------------------------------ SiLU * up
@@ -612,6 +672,15 @@ hipError_t launch_attention(const float* q, const uint16_t* kc, const uint16_t* 
                             int64_t cap, uint16_t* out, hipStream_t s) {
   hipLaunchKernelGGL(attention_kernel, dim3((unsigned)M, (unsigned)Hkv), dim3(64 * kAttnWaves), 0, s,
                      q, kc, vc, H, Hkv, seq, pos, B, cap, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_attention(const float* qkv, int64_t M, int H, int Hkv, const int32_t* seq,
+                                 const int32_t* pos, double base, float* q, uint16_t* kc,
+                                 uint16_t* vc, int64_t B, int64_t cap, uint16_t* out,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(rope_attention_kernel, dim3((unsigned)M, (unsigned)Hkv), dim3(64 * kAttnWaves),
+                     0, s, qkv, H, Hkv, seq, pos, base, q, kc, vc, B, cap, out);
   return hipGetLastError();
 }
 

@@ -70,6 +70,10 @@ hipError_t launch_rope_kv(const float* qkv, int64_t M, int H, int Hkv, int hd, c
 hipError_t launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t M,
                             int H, int Hkv, const int32_t* seq, const int32_t* pos, int64_t B,
                             int64_t cap, uint16_t* out, hipStream_t s);
+hipError_t launch_rope_attention(const float* qkv, int64_t M, int H, int Hkv, const int32_t* seq,
+                                 const int32_t* pos, double base, float* q, uint16_t* kc,
+                                 uint16_t* vc, int64_t B, int64_t cap, uint16_t* out,
+                                 hipStream_t s);
 hipError_t launch_silu_mul(const float* gu, int64_t M, int64_t F, uint16_t* a, hipStream_t s);
 hipError_t launch_add_rmsnorm_quant(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
                                     int64_t d, double eps, uint16_t* y, uint8_t* yq, float* ys,

@@ -158,6 +158,10 @@ class Decoder:
         d, F = cfg.d, cfg.ffn
         qd = cfg.n_heads * cfg.head_dim
         qkv_rows = qd + 2 * cfg.n_kv * cfg.head_dim
+        # B rows are one row per sequence (spec_prepare's phase 0, or a
+        # one-token prefill): RoPE and attention then share one launch
+        one_per_seq = M == self.B
+
         def lin(li, name, X, W, Y, coded=False):
             self._linear(mode, X, W, Y, variant, coded)
             if trace is not None:
@@ -182,11 +186,16 @@ class Decoder:
             qkv = _view(self.qkv, M, qkv_rows)
             lin(li, "qkv", h, L["qkv"], qkv, coded=draft)
             q = _view(self.q, M, qd)
-            b.rope_kv(qkv, self.seq, self.pos, q, self.kc[li], self.vc[li], cfg.n_heads,
-                      cfg.n_kv, cfg.rope_base)
             att = _view(self.att, M, qd)
-            b.attention(q, self.kc[li], self.vc[li], self.seq, self.pos, att, cfg.n_heads,
-                        cfg.n_kv)
+            if one_per_seq:
+                # decode and draft forwards: one launch, the same bits
+                b.rope_attention(qkv, self.seq, self.pos, q, self.kc[li], self.vc[li], att,
+                                 cfg.n_heads, cfg.n_kv, cfg.rope_base)
+            else:
+                b.rope_kv(qkv, self.seq, self.pos, q, self.kc[li], self.vc[li], cfg.n_heads,
+                          cfg.n_kv, cfg.rope_base)
+                b.attention(q, self.kc[li], self.vc[li], self.seq, self.pos, att, cfg.n_heads,
+                            cfg.n_kv)
             o = _view(self.o, M, d)
             lin(li, "o", att, L["o"], o)
             norm(x, o, h)

@@ -166,6 +166,11 @@ def test_harness_validation():
     assert L.qspec_rope_kv(A, 4, 6, 4, A, A, D(1e4), A, A, A, 2, 64, S) == ESHAPE
     assert L.qspec_rope_kv(A, 4, 8, 4, A, A, D(1e4), A, A, A, 2, 4000, S) == ESHAPE
     assert L.qspec_rope_kv(A, 4, 8, 4, A, A, D(0.0), A, A, A, 2, 64, S) == ESHAPE
+    # the fused RoPE + attention call: the checks of both
+    assert L.qspec_rope_attention(A, 4, 6, 4, A, A, D(1e4), A, A, A, 2, 64, A, S) == ESHAPE
+    assert L.qspec_rope_attention(A, 4, 8, 4, A, A, D(1e4), A, A, A, 2, 4000, A, S) == ESHAPE
+    assert L.qspec_rope_attention(A, 4, 8, 4, A, A, D(0.0), A, A, A, 2, 64, A, S) == ESHAPE
+    assert L.qspec_rope_attention(A, 4, 8, 4, A, A, D(1e4), A, A, A, 2, 64, NUL, S) == ENULL
     assert L.qspec_attention(A, A, A, 4, 8, 4, A, A, 2, 0, A, S) == ESHAPE
     assert L.qspec_attention(A, A, A, 4, 8, 3, A, A, 2, 64, A, S) == ESHAPE
     assert L.qspec_attention(A, A, A, 4, 8, 4, NUL, A, 2, 64, A, S) == ENULL

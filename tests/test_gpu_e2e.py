@@ -95,6 +95,39 @@ def test_rope_kv_and_attention():
     assert np.all(err <= np.abs(want) * 2 * BF16_ULP + 1e-5), err.max()
 
 
+@pytest.mark.parametrize("H,Hkv", [(16, 4), (8, 8), (12, 2)])
+def test_rope_attention_equals_the_two_calls(H, Hkv):
+    """The fused call on one row per sequence -- among them a row outside
+    the cache (sequence -1) and one past its capacity -- gives bitwise the
+    rotated queries, cache contents and attention output of qspec_rope_kv
+    followed by qspec_attention (grp of 4, 1 and 6 query heads per KV head:
+    one or two passes over the heads)."""
+    rng = synth.make_rng(53)
+    hd, B, cap = 128, 6, 300
+    M = 6
+    seq = np.array([3, 0, 5, -1, 2, 1], np.int32)
+    pos = np.array([0, 17, 299, 4, 133, 300], np.int32)   # 300: past the capacity
+    say(f"rope_attention H={H} Hkv={Hkv}")
+    qkv = dev(rng.standard_normal((M, (H + 2 * Hkv) * hd)).astype(np.float32))
+    k0 = dev_bf16(synth.to_bf16_bits(rng.standard_normal((B, Hkv, cap, hd), dtype=np.float32)))
+    v0 = dev_bf16(synth.to_bf16_bits(rng.standard_normal((B, Hkv, cap, hd), dtype=np.float32)))
+    sq, ps = dev(seq), dev(pos)
+    res = []
+    for fused in (False, True):
+        kc, vc = k0.clone(), v0.clone()
+        qo = torch.zeros((M, H * hd), dtype=torch.float32, device="cuda:0")
+        out = torch.empty((M, H * hd), dtype=torch.bfloat16, device="cuda:0")
+        if fused:
+            qb.rope_attention(qkv, sq, ps, qo, kc, vc, out, H, Hkv, 10000.0)
+        else:
+            qb.rope_kv(qkv, sq, ps, qo, kc, vc, H, Hkv, 10000.0)
+            qb.attention(qo, kc, vc, sq, ps, out, H, Hkv)
+        res.append((host(qo), host_bits16(kc), host_bits16(vc), host_bits16(out)))
+    for a, b_ in zip(*res):
+        assert np.array_equal(a.view(np.uint8), b_.view(np.uint8))
+    assert not np.any(res[1][3][3]) and not np.any(res[1][3][5])  # rows outside the cache: zeros
+
+
 def test_silu_mul_and_argmax():
     rng = synth.make_rng(52)
     M, F = 5, 700
