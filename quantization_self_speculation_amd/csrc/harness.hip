@@ -199,12 +199,12 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------------ attention
-// One block of kAttnWaves wavefronts per (row, kv head): the block serves all
-// grp = H / Hkv query heads of the kv head, kAttnHeads at a time, so each key
-// and value row is read once for all of them.  The T = pos + 1 keys are
-// split into kAttnWaves contiguous ranges (a function of T only); a
-// wavefront walks its range in chunks of up to kAttnChunk keys, issuing all
-// of a chunk's key and value loads at once, and keeps a running softmax:
+// One block of kAttnWaves wavefronts per (row, kv head, part): the part's
+// HPB query heads of the kv head (HPB = 4, 2 or 1, chosen per launch) share
+// every key and value load.  The T = pos + 1 keys are split into kAttnWaves
+// contiguous ranges (a function of T only); a wavefront walks its range in
+// chunks of up to kAttnChunk keys, issuing all of a chunk's key and value
+// loads at once, and keeps a running softmax:
 //   scores: 16 lanes share a key (lane l reads dims 8 (l % 16) .. + 7 of key
 //     4 j + l / 16, one coalesced 16-byte load), each lane's 8 products are
 //     summed in order and the 16 partials by fixed DPP lane moves, fp32; the
@@ -214,8 +214,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
 //     and lane l accumulates p * v for dims 2l, 2l+1 over the chunk's keys
 //     in increasing order;
 //   the wavefronts' (m, sum, o) are merged in wave order.
-// Every step depends on T alone, so a row's output is the same whatever
-// other rows share the launch.  Output bf16.
+// Every step of a head depends on T alone and on no other head, so a row's
+// output is the same whatever other rows share the launch and however many
+// heads a block serves.  Output bf16.
 constexpr int kHeadDim = 128;
 // Block shape (measured on MI355X; the key split is part of a row's result,
 // so one shape serves every M: 8 wavefronts with 32-key chunks beat 64-key
@@ -241,23 +242,34 @@ __device__ __forceinline__ float sum16_dpp(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row rotate 8
   return v;
 }
-constexpr int kAttnHeads = 4;    // query heads per pass
 constexpr int kAttnChunk = QSPEC_ATTN_CHUNK;  // keys per wavefront chunk (all loads in flight)
 constexpr int kAttnQuads = kAttnChunk / 4;
 
+// The block's kv head and first query head (within the kv head's group):
+// blockIdx.y = g * parts + part, parts = ceil(grp / HPB).
+template <int HPB>
+__device__ __forceinline__ void attn_block_heads(int H, int Hkv, int& g, int& h0, int& nh) {
+  const int grp = H / Hkv, parts = (grp + HPB - 1) / HPB;
+  g = blockIdx.y / parts;
+  h0 = (blockIdx.y % parts) * HPB;
+  nh = min(HPB, grp - h0);
+}
+
+template <int HPB>
 __device__ __forceinline__ void attend(const float* __restrict__ q, const uint16_t* __restrict__ kc,
                                        const uint16_t* __restrict__ vc, int H, int Hkv,
                                        const int32_t* __restrict__ seq,
                                        const int32_t* __restrict__ pos, int64_t B, int64_t cap,
                                        uint16_t* __restrict__ out) {
-  // LDS: per wavefront, the chunk's scores [kAttnHeads][kAttnChunk]; then the
-  // wavefronts' results: o [kAttnWaves][kAttnHeads][128], m and sum
-  // [kAttnWaves][kAttnHeads]
-  __shared__ float sc[kAttnWaves][kAttnHeads][kAttnChunk];
-  __shared__ float po[kAttnWaves][kAttnHeads][kHeadDim];
-  __shared__ float pm[kAttnWaves][kAttnHeads], pl[kAttnWaves][kAttnHeads];
+  // LDS: per wavefront, the chunk's scores [HPB][kAttnChunk]; then the
+  // wavefronts' results: o [kAttnWaves][HPB][128], m and sum
+  // [kAttnWaves][HPB]
+  __shared__ float sc[kAttnWaves][HPB][kAttnChunk];
+  __shared__ float po[kAttnWaves][HPB][kHeadDim];
+  __shared__ float pm[kAttnWaves][HPB], pl[kAttnWaves][HPB];
   const int64_t m = blockIdx.x;
-  const int g = blockIdx.y;
+  int g, h0, nh;
+  attn_block_heads<HPB>(H, Hkv, g, h0, nh);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int grp = H / Hkv;
   const int64_t b = seq[m];
@@ -279,15 +291,14 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const uint16
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  for (int h0 = 0; h0 < grp; h0 += kAttnHeads) {
-    const int nh = min(kAttnHeads, grp - h0);
-    float rm[kAttnHeads], rl[kAttnHeads], o0[kAttnHeads], o1[kAttnHeads];
+  {
+    float rm[HPB], rl[HPB], o0[HPB], o1[HPB];
 #pragma unroll
-    for (int hh = 0; hh < kAttnHeads; ++hh) {
+    for (int hh = 0; hh < HPB; ++hh) {
       rm[hh] = -INFINITY;
       rl[hh] = o0[hh] = o1[hh] = 0.f;
     }
-    float qf[kAttnHeads][8];
+    float qf[HPB][8];
     for (int c0 = t0; c0 < t1; c0 += kAttnChunk) {
       const int len = min(kAttnChunk, t1 - c0);
       // every key and value load of the chunk, then (first chunk) the queries
@@ -302,7 +313,7 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const uint16
         if (i < len) vv[i] = Vw[(int64_t)(c0 + i) * (kHeadDim / 2)];
       if (c0 == t0) {
 #pragma unroll
-        for (int hh = 0; hh < kAttnHeads; ++hh) {
+        for (int hh = 0; hh < HPB; ++hh) {
           const float* qr = q + m * (H * kHeadDim) +
                             (int64_t)(g * grp + h0 + min(hh, nh - 1)) * kHeadDim + dc;
           const float4 x0 = *reinterpret_cast<const float4*>(qr);
@@ -312,16 +323,16 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const uint16
         }
       }
       // scores and the chunk max
-      float cm[kAttnHeads];
+      float cm[HPB];
 #pragma unroll
-      for (int hh = 0; hh < kAttnHeads; ++hh) cm[hh] = -INFINITY;
+      for (int hh = 0; hh < HPB; ++hh) cm[hh] = -INFINITY;
 #pragma unroll
       for (int j = 0; j < kAttnQuads; ++j) {
         if (4 * j >= len) break;     // uniform
         const int t = 4 * j + kk;    // within the chunk
         const uint32_t wv[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
 #pragma unroll
-        for (int hh = 0; hh < kAttnHeads; ++hh) {
+        for (int hh = 0; hh < HPB; ++hh) {
           float part = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -339,7 +350,7 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const uint16
       wave_sync();
       // running max, rescale, p = exp(s - m), chunk sums (lane t of the chunk)
 #pragma unroll
-      for (int hh = 0; hh < kAttnHeads; ++hh) {
+      for (int hh = 0; hh < HPB; ++hh) {
         cm[hh] = wave_max(cm[hh]);  // exact: every lane gets the chunk's largest score
         const float mn = fmaxf(rm[hh], cm[hh]);
         const float f = rm[hh] == -INFINITY ? 0.f : __expf(rm[hh] - mn);
@@ -363,7 +374,7 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const uint16
         if (i < len) {  // uniform
           const float va = __uint_as_float(vv[i] << 16), vb = __uint_as_float(vv[i] & 0xFFFF0000u);
 #pragma unroll
-          for (int hh = 0; hh < kAttnHeads; ++hh) {
+          for (int hh = 0; hh < HPB; ++hh) {
             const float pt = scw[hh * kAttnChunk + i];
             o0[hh] = fmaf(pt, va, o0[hh]);
             o1[hh] = fmaf(pt, vb, o1[hh]);
@@ -373,7 +384,7 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const uint16
       wave_sync();  // the next chunk rewrites this wave's scores
     }
 #pragma unroll
-    for (int hh = 0; hh < kAttnHeads; ++hh) {
+    for (int hh = 0; hh < HPB; ++hh) {
       po[w][hh][2 * lane] = o0[hh];
       po[w][hh][2 * lane + 1] = o1[hh];
       if (lane == 0) {
@@ -397,32 +408,36 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const uint16
       const float inv = T > 0 ? 1.0f / l : 0.f;
       out[m * (H * kHeadDim) + (int64_t)(g * grp + h0 + hh) * kHeadDim + d] = f32_to_bf16_rne(o * inv);
     }
-    __syncthreads();  // before the next head pass reuses the LDS
   }
 }
 
+template <int HPB>
 __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
     const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     int H, int Hkv, const int32_t* __restrict__ seq, const int32_t* __restrict__ pos, int64_t B,
     int64_t cap, uint16_t* __restrict__ out) {
-  attend(q, kc, vc, H, Hkv, seq, pos, B, cap, out);
+  attend<HPB>(q, kc, vc, H, Hkv, seq, pos, B, cap, out);
 }
 
 // RoPE + KV write + attention in one launch, for launches whose rows belong
 // to different sequences (one row per sequence: decode and draft forwards).
-// Block (m, g) first does rope_kv's work for row m restricted to kv head g --
-// the query heads of g rotated into q, key head g rotated and value head g
-// written into the caches at the row's position, the same fp64 arithmetic
-// and roundings -- then attends exactly as attention_kernel does.  The row's
-// own key and value are written by this block before its barrier; no other
-// block writes to this sequence's cache rows.
+// Block (m, g, part) first does rope_kv's work for row m restricted to what
+// it attends with -- its query heads rotated into q, key head g rotated and
+// value head g written into the caches at the row's position, the same fp64
+// arithmetic and roundings -- then attends exactly as attention_kernel does.
+// Every part of kv head g writes the same key and value bytes (the same
+// arithmetic on the same inputs), each before its own barrier, so each block
+// reads the row's key and value as its own stores left them; no block of
+// another row writes to this sequence's cache rows.
+template <int HPB>
 __global__ __launch_bounds__(64 * kAttnWaves) void rope_attention_kernel(
     const float* __restrict__ qkv, int H, int Hkv, const int32_t* __restrict__ seq,
     const int32_t* __restrict__ pos, double base, float* __restrict__ q, uint16_t* __restrict__ kc,
     uint16_t* __restrict__ vc, int64_t B, int64_t cap, uint16_t* __restrict__ out) {
   __shared__ double cs[2][kHeadDim / 2];
   const int64_t m = blockIdx.x;
-  const int g = blockIdx.y;
+  int g, h0, nh;
+  attn_block_heads<HPB>(H, Hkv, g, h0, nh);
   const int hd = kHeadDim, half = hd / 2, grp = H / Hkv;
   const int p = pos[m];
   const int64_t b = seq[m];
@@ -437,14 +452,14 @@ __global__ __launch_bounds__(64 * kAttnWaves) void rope_attention_kernel(
     }
     __syncthreads();
     const float* r = qkv + m * (int64_t)((H + 2 * Hkv) * hd);
-    // the grp query heads of g, then key head g (index grp)
-    for (int t = threadIdx.x; t < (grp + 1) * half; t += blockDim.x) {
+    // this block's nh query heads, then key head g (index nh)
+    for (int t = threadIdx.x; t < (nh + 1) * half; t += blockDim.x) {
       const int hh = t / half, i = t % half;
-      const int h = hh < grp ? g * grp + hh : H + g;  // column block of qkv
+      const int h = hh < nh ? g * grp + h0 + hh : H + g;  // column block of qkv
       const double a = r[h * hd + i], bb = r[h * hd + i + half];
       const double c = cs[0][i], sn = cs[1][i];
       const double lo = a * c - bb * sn, hi = bb * c + a * sn;
-      if (hh < grp) {
+      if (hh < nh) {
         q[m * (H * hd) + h * hd + i] = (float)lo;
         q[m * (H * hd) + h * hd + i + half] = (float)hi;
       } else {
@@ -457,7 +472,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void rope_attention_kernel(
       vc[((b * Hkv + g) * cap + p) * hd + t] = f32_to_bf16_rne(r[(H + Hkv + g) * hd + t]);
   }
   __syncthreads();  // the rotated queries and this row's key and value are in memory
-  attend(q, kc, vc, H, Hkv, seq, pos, B, cap, out);
+  attend<HPB>(q, kc, vc, H, Hkv, seq, pos, B, cap, out);
 }
 
 // ------------------------------------------------------------------ SiLU * up
@@ -667,11 +682,38 @@ hipError_t launch_rope_kv(const float* qkv, int64_t M, int H, int Hkv, int hd, c
   return hipGetLastError();
 }
 
+// Query heads per block: the largest of 4, 2, 1 whose grid still has
+// QSPEC_ATTN_MIN_BLOCKS blocks; a row's output does not depend on it.
+// Measured on MI355X (16 q / 4 kv heads, 128 / 256 / 384 keys): 16 decode
+// rows with RoPE fused 9.1 / 11.2 / 15.5 us with 4 heads per block (64
+// blocks), 7.4 / 9.0 / 11.9 with 2, 6.7 / 8.1 / 10.4 with 1 (256 blocks);
+// 80 verify rows 14.2 / 21.2 / 30.3 us with 4, 11.2 / 16.5 / 23.3 with 2
+// (640 blocks), 13.7 / 19.1 / 26.7 with 1.  Prefill grids keep 4 (every
+// key and value load shared by the whole group).
+#ifndef QSPEC_ATTN_MIN_BLOCKS
+#define QSPEC_ATTN_MIN_BLOCKS 512
+#endif
+static int attn_hpb(int64_t M, int H, int Hkv) {
+  const int grp = H / Hkv;
+  for (int hpb : {4, 2})
+    if (M * Hkv * ((grp + hpb - 1) / hpb) >= QSPEC_ATTN_MIN_BLOCKS) return hpb;
+  return 1;
+}
+
 hipError_t launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t M,
                             int H, int Hkv, const int32_t* seq, const int32_t* pos, int64_t B,
                             int64_t cap, uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)M, (unsigned)Hkv), dim3(64 * kAttnWaves), 0, s,
-                     q, kc, vc, H, Hkv, seq, pos, B, cap, out);
+  const int hpb = attn_hpb(M, H, Hkv), grp = H / Hkv;
+  const dim3 grid((unsigned)M, (unsigned)(Hkv * ((grp + hpb - 1) / hpb)));
+  if (hpb == 4)
+    hipLaunchKernelGGL(attention_kernel<4>, grid, dim3(64 * kAttnWaves), 0, s, q, kc, vc, H, Hkv,
+                       seq, pos, B, cap, out);
+  else if (hpb == 2)
+    hipLaunchKernelGGL(attention_kernel<2>, grid, dim3(64 * kAttnWaves), 0, s, q, kc, vc, H, Hkv,
+                       seq, pos, B, cap, out);
+  else
+    hipLaunchKernelGGL(attention_kernel<1>, grid, dim3(64 * kAttnWaves), 0, s, q, kc, vc, H, Hkv,
+                       seq, pos, B, cap, out);
   return hipGetLastError();
 }
 
@@ -679,8 +721,17 @@ hipError_t launch_rope_attention(const float* qkv, int64_t M, int H, int Hkv, co
                                  const int32_t* pos, double base, float* q, uint16_t* kc,
                                  uint16_t* vc, int64_t B, int64_t cap, uint16_t* out,
                                  hipStream_t s) {
-  hipLaunchKernelGGL(rope_attention_kernel, dim3((unsigned)M, (unsigned)Hkv), dim3(64 * kAttnWaves),
-                     0, s, qkv, H, Hkv, seq, pos, base, q, kc, vc, B, cap, out);
+  const int hpb = attn_hpb(M, H, Hkv), grp = H / Hkv;
+  const dim3 grid((unsigned)M, (unsigned)(Hkv * ((grp + hpb - 1) / hpb)));
+  if (hpb == 4)
+    hipLaunchKernelGGL(rope_attention_kernel<4>, grid, dim3(64 * kAttnWaves), 0, s, qkv, H, Hkv,
+                       seq, pos, base, q, kc, vc, B, cap, out);
+  else if (hpb == 2)
+    hipLaunchKernelGGL(rope_attention_kernel<2>, grid, dim3(64 * kAttnWaves), 0, s, qkv, H, Hkv,
+                       seq, pos, base, q, kc, vc, B, cap, out);
+  else
+    hipLaunchKernelGGL(rope_attention_kernel<1>, grid, dim3(64 * kAttnWaves), 0, s, qkv, H, Hkv,
+                       seq, pos, base, q, kc, vc, B, cap, out);
   return hipGetLastError();
 }
 

@@ -95,19 +95,62 @@ def test_rope_kv_and_attention():
     assert np.all(err <= np.abs(want) * 2 * BF16_ULP + 1e-5), err.max()
 
 
-@pytest.mark.parametrize("H,Hkv", [(16, 4), (8, 8), (12, 2)])
-def test_rope_attention_equals_the_two_calls(H, Hkv):
+@pytest.mark.parametrize("H,Hkv", [(16, 4), (12, 2)])
+def test_attention_rows_independent_of_heads_per_block(H, Hkv):
+    """The launch picks how many query heads of a KV head one block serves
+    (4, 2 or 1) from the grid size; a row's output must not depend on it.
+    128 rows run with 4 heads per block (with 6 heads per KV head: blocks of
+    4 and of 2), their first 64 with 2 (16/4) or 1 (12/2), their first 16
+    with 1: bitwise the same rows; sampled rows of the 128-row launch
+    against the oracle."""
+    rng = synth.make_rng(54)
+    hd, B, cap, M = 128, 40, 300, 128
+    seq = rng.integers(0, B, M).astype(np.int32)
+    pos = rng.integers(0, cap, M).astype(np.int32)
+    pos[:3] = [0, cap - 1, 1]
+    say(f"attention heads-per-block H={H} Hkv={Hkv}")
+    kb = synth.to_bf16_bits(rng.standard_normal((B, Hkv, cap, hd), dtype=np.float32))
+    vb = synth.to_bf16_bits(rng.standard_normal((B, Hkv, cap, hd), dtype=np.float32))
+    kc, vc = dev_bf16(kb), dev_bf16(vb)
+    Q = rng.standard_normal((M, H * hd)).astype(np.float32)
+    outs = {}
+    for n in (M, 64, 16):
+        out = torch.empty((n, H * hd), dtype=torch.bfloat16, device="cuda:0")
+        qb.attention(dev(Q[:n]), kc, vc, dev(seq[:n]), dev(pos[:n]), out, H, Hkv)
+        outs[n] = host_bits16(out)
+    for n in (64, 16):
+        assert np.array_equal(outs[n], outs[M][:n]), n
+    K, Vv = om.bf16_values(kb), om.bf16_values(vb)
+    Qh = Q.reshape(M, H, hd).astype(np.float64)
+    got = om.bf16_values(outs[M]).reshape(M, H, hd)
+    for m in (0, 1, 2, 31, 77, 127):
+        for h in range(H):
+            g, T = h // (H // Hkv), pos[m] + 1
+            want = om.attend(Qh[m, h], K[seq[m], g, :T], Vv[seq[m], g, :T])
+            assert np.all(np.abs(got[m, h] - want) <= np.abs(want) * 2 * BF16_ULP + 1e-5), (m, h)
+
+
+@pytest.mark.parametrize("H,Hkv,M", [(16, 4, 6), (8, 8, 6), (12, 2, 6), (16, 4, 64),
+                                     (16, 4, 128), (12, 2, 128)])
+def test_rope_attention_equals_the_two_calls(H, Hkv, M):
     """The fused call on one row per sequence -- among them a row outside
     the cache (sequence -1) and one past its capacity -- gives bitwise the
     rotated queries, cache contents and attention output of qspec_rope_kv
-    followed by qspec_attention (grp of 4, 1 and 6 query heads per KV head:
-    one or two passes over the heads)."""
+    followed by qspec_attention (grp of 4, 1 and 6 query heads per KV head;
+    6, 64 and 128 rows: 1, 2 and 4 query heads per block, and blocks of 4
+    and 2 heads when a KV head has 6)."""
     rng = synth.make_rng(53)
-    hd, B, cap = 128, 6, 300
-    M = 6
-    seq = np.array([3, 0, 5, -1, 2, 1], np.int32)
-    pos = np.array([0, 17, 299, 4, 133, 300], np.int32)   # 300: past the capacity
-    say(f"rope_attention H={H} Hkv={Hkv}")
+    hd, cap = 128, 300
+    if M == 6:
+        B = 6
+        seq = np.array([3, 0, 5, -1, 2, 1], np.int32)
+        pos = np.array([0, 17, 299, 4, 133, 300], np.int32)   # 300: past the capacity
+    else:
+        B = M
+        seq = rng.permutation(M).astype(np.int32)
+        pos = rng.integers(0, cap, M).astype(np.int32)
+        seq[3], pos[5] = -1, cap
+    say(f"rope_attention H={H} Hkv={Hkv} M={M}")
     qkv = dev(rng.standard_normal((M, (H + 2 * Hkv) * hd)).astype(np.float32))
     k0 = dev_bf16(synth.to_bf16_bits(rng.standard_normal((B, Hkv, cap, hd), dtype=np.float32)))
     v0 = dev_bf16(synth.to_bf16_bits(rng.standard_normal((B, Hkv, cap, hd), dtype=np.float32)))
