@@ -147,6 +147,150 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
   if (yq != nullptr) quant_row_bf16<kNormPer>(yb, d, redf, yq + m * (d / 2), ys + m);  // uniform
 }
 
+// The same add + RMSNorm (+ codes) for 16-byte aligned rows with d % 4 == 0:
+// thread t owns the four consecutive elements of each float4 t + NT i, so
+// every access is one 16-byte (x, add), 8-byte (y) or 2-byte (codes) vector
+// per group, and a group's two code bytes are packed in-thread.  The
+// reductions run over DPP lane moves within each 16-lane row, the four row
+// values of a wavefront read in a fixed order, then the wavefronts' values
+// through LDS in wave order: one barrier per reduction, no LDS round trip
+// inside a wavefront.  The sum of squares is fp64 in a fixed order (a
+// different order from add_rmsnorm_kernel's: the two kernels may differ in
+// the last bit of den, never a row from another launch of the same kernel);
+// the absmax is order-free, so the codes are exactly the stand-alone
+// quantizer's on the stored bf16 row.
+#ifndef QSPEC_NORM_THREADS
+#define QSPEC_NORM_THREADS 512
+#endif
+constexpr int kNormThreads = QSPEC_NORM_THREADS;
+constexpr int kNormV4 = 4096 / (4 * kNormThreads);  // float4 groups per thread (d <= 4096)
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Sum over the wavefront, the same value in every lane: each 16-lane row by
+// DPP moves (lane 0 of the row keeps a fixed association), then the rows'
+// sums (r0 + r1) + (r2 + r3).  Every lane must be active.
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+  v += dpp_f64<0xB1>(v);   // lane ^ 1
+  v += dpp_f64<0x4E>(v);   // lane ^ 2
+  v += dpp_f64<0x124>(v);  // row rotate 4
+  v += dpp_f64<0x128>(v);  // row rotate 8
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
+}
+
+__global__ __launch_bounds__(kNormThreads) void add_rmsnorm_v4_kernel(
+    float* __restrict__ x, int64_t xs, const float* __restrict__ add, int64_t as, int d, double eps,
+    uint16_t* __restrict__ y, uint8_t* __restrict__ yq, float* __restrict__ ys) {
+  constexpr int NW = kNormThreads / 64;
+  __shared__ double red[NW];
+  __shared__ float redf[NW];
+  const int64_t m = blockIdx.x;
+  const int w = threadIdx.x >> 6;
+  float4* xr = reinterpret_cast<float4*>(x + m * xs);
+  const int ng = d / 4;
+  float4 v[kNormV4];
+#pragma unroll
+  for (int i = 0; i < kNormV4; ++i) {
+    const int gi = (int)threadIdx.x + kNormThreads * i;
+    v[i] = gi < ng ? xr[gi] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (add != nullptr) {
+    const float4* ar = reinterpret_cast<const float4*>(add + m * as);
+    float4 ad[kNormV4];
+#pragma unroll
+    for (int i = 0; i < kNormV4; ++i) {
+      const int gi = (int)threadIdx.x + kNormThreads * i;
+      ad[i] = gi < ng ? ar[gi] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < kNormV4; ++i) {
+      const int gi = (int)threadIdx.x + kNormThreads * i;
+      v[i].x += ad[i].x;
+      v[i].y += ad[i].y;
+      v[i].z += ad[i].z;
+      v[i].w += ad[i].w;
+      if (gi < ng) xr[gi] = v[i];
+    }
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < kNormV4; ++i) {
+    ss += (double)v[i].x * (double)v[i].x;
+    ss += (double)v[i].y * (double)v[i].y;
+    ss += (double)v[i].z * (double)v[i].z;
+    ss += (double)v[i].w * (double)v[i].w;
+  }
+  ss = wave_sum_f64_dpp(ss);
+  if ((threadIdx.x & 63) == 0) red[w] = ss;
+  __syncthreads();
+  ss = red[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) ss += red[k];
+  const double den = sqrt(ss / (double)d + eps);
+  uint2* yr = reinterpret_cast<uint2*>(y + m * d);
+  uint16_t yb[kNormV4][4];
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormV4; ++i) {
+    const int gi = (int)threadIdx.x + kNormThreads * i;
+    yb[i][0] = f64_to_bf16_rne((double)v[i].x / den);
+    yb[i][1] = f64_to_bf16_rne((double)v[i].y / den);
+    yb[i][2] = f64_to_bf16_rne((double)v[i].z / den);
+    yb[i][3] = f64_to_bf16_rne((double)v[i].w / den);
+    if (gi < ng) {
+      yr[gi] = make_uint2((uint32_t)yb[i][0] | ((uint32_t)yb[i][1] << 16),
+                          (uint32_t)yb[i][2] | ((uint32_t)yb[i][3] << 16));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a = fmaxf(a, fabsf(bf16_to_f32(yb[i][c])));
+    }
+  }
+  if (yq == nullptr) return;  // uniform
+  a = wave_max_dpp(a);
+  if ((threadIdx.x & 63) == 0) redf[w] = a;
+  __syncthreads();
+  a = redf[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) a = fmaxf(a, redf[k]);
+  const float sc = a / 7.0f;
+  const float r = 1.0f / sc;
+  uint16_t* qr = reinterpret_cast<uint16_t*>(yq + m * (d / 2));
+#pragma unroll
+  for (int i = 0; i < kNormV4; ++i) {
+    const int gi = (int)threadIdx.x + kNormThreads * i;
+    if (gi < ng) {
+      int c[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[k] = sc != 0.0f ? quant_code_act(bf16_to_f32(yb[i][k]), sc, r) : 0;
+      qr[gi] = (uint16_t)((c[0] & 0xF) | ((c[1] & 0xF) << 4) | ((c[2] & 0xF) << 8) | ((c[3] & 0xF) << 12));
+    }
+  }
+  if (threadIdx.x == 0) ys[m] = sc;
+}
+
 // ------------------------------------------------------------------ RoPE + KV write
 // qkv[m] = [q (H*hd) | k (Hkv*hd) | v (Hkv*hd)] fp32.  q -> fp32 after RoPE,
 // k -> bf16 after RoPE, v -> bf16, both written at [seq][g][pos][:] of the
@@ -659,18 +803,38 @@ hipError_t launch_embed(const uint16_t* emb, int64_t V, int64_t d, const int32_t
   return hipGetLastError();
 }
 
+// The vector kernel wherever its alignment holds: x, add and their row
+// strides in whole 16-byte groups, y 8-byte and the codes 2-byte aligned.
+static bool norm_v4_ok(const float* x, int64_t xs, const float* add, int64_t as, int64_t d,
+                       const uint16_t* y, const uint8_t* yq) {
+#ifdef QSPEC_NORM_SCALAR
+  return false;
+#endif
+  const auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+  return d % 4 == 0 && al(x, 16) && xs % 4 == 0 && (add == nullptr || (al(add, 16) && as % 4 == 0)) &&
+         al(y, 8) && (yq == nullptr || al(yq, 2));
+}
+
 hipError_t launch_add_rmsnorm(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
                               int64_t d, double eps, uint16_t* y, hipStream_t s) {
-  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
-                     (int)d, eps, y, nullptr, nullptr);
+  if (norm_v4_ok(x, xs, add, as, d, y, nullptr))
+    hipLaunchKernelGGL(add_rmsnorm_v4_kernel, dim3((unsigned)M), dim3(kNormThreads), 0, s, x, xs,
+                       add, as, (int)d, eps, y, nullptr, nullptr);
+  else
+    hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
+                       (int)d, eps, y, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_add_rmsnorm_quant(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
                                     int64_t d, double eps, uint16_t* y, uint8_t* yq, float* ys,
                                     hipStream_t s) {
-  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
-                     (int)d, eps, y, yq, ys);
+  if (norm_v4_ok(x, xs, add, as, d, y, yq))
+    hipLaunchKernelGGL(add_rmsnorm_v4_kernel, dim3((unsigned)M), dim3(kNormThreads), 0, s, x, xs,
+                       add, as, (int)d, eps, y, yq, ys);
+  else
+    hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
+                       (int)d, eps, y, yq, ys);
   return hipGetLastError();
 }
 

@@ -50,6 +50,30 @@ def test_embed_and_add_rmsnorm():
     _bf16_close(host_bits16(y2), om.to_bf16_bits(om.rmsnorm(xs[2::3], 1e-6)), frac_exact=0.999)
 
 
+@pytest.mark.parametrize("d,off", [(250, 0), (256, 1), (2048, 0)])
+def test_add_rmsnorm_layouts(d, off):
+    """Rows that the 16-byte kernel takes (d % 4 == 0, aligned) and rows
+    that fall back to the scalar kernel (d = 250; rows starting one float
+    past a 16-byte boundary): the same residual bits and the oracle's
+    RMSNorm within one bf16 unit."""
+    rng = synth.make_rng(55, d + off)
+    M = 7
+    say(f"add_rmsnorm d={d} offset={off}")
+    x0 = rng.standard_normal((M, d)).astype(np.float32)
+    add = rng.standard_normal((M, d)).astype(np.float32)
+    xb = torch.zeros(M * d + off, dtype=torch.float32, device="cuda:0")
+    ab = torch.zeros(M * d + off, dtype=torch.float32, device="cuda:0")
+    x = xb[off:].view(M, d)
+    a = ab[off:].view(M, d)
+    x.copy_(dev(x0))
+    a.copy_(dev(add))
+    y = torch.empty((M, d), dtype=torch.bfloat16, device="cuda:0")
+    qb.add_rmsnorm(x, a, y, 1e-6)
+    xs = (x0 + add).astype(np.float32)
+    assert np.array_equal(host(x), xs)
+    _bf16_close(host_bits16(y), om.to_bf16_bits(om.rmsnorm(xs, 1e-6)), frac_exact=0.999)
+
+
 def test_rope_kv_and_attention():
     rng = synth.make_rng(51)
     H, Hkv, hd, B, cap = 4, 2, 128, 3, 40
