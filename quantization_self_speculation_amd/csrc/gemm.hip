@@ -1574,6 +1574,11 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool max_tiles
   p.gps = (int)cdiv(G, S);
   p.S = (int)cdiv(G, p.gps);
   p.MB = (int)(M >= 64 ? 4 : cdiv(M, 16));
+#ifndef QSPEC_SK_NO_MB5
+  // W4A16 at 65-80 rows (a verify pass of 16 sequences, 5 rows each): one
+  // 80-row block reads every weight tile once instead of twice (64 + 16)
+  if (mode == 0 && cdiv(M, 16) == 5) p.MB = 5;
+#endif
   // W4A16 with a k-split: one 16-row activation block per workgroup (more,
   // lighter workgroups; the weight tile is re-read from L2 per block)
   if (mode == 0 && p.S > 1) p.MB = 1;
@@ -1624,6 +1629,7 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
       case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false>), grid, blk, 0, s, a); break;
       case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_NB16, QSPEC_SK_B2, false>), grid, blk, 0, s, a); break;
       case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, false>), grid, blk, 0, s, a); break;
+      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 5, QSPEC_SK_NB16, QSPEC_SK_B4, false>), grid, blk, 0, s, a); break;
       default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_NB16, QSPEC_SK_B4, false>), grid, blk, 0, s, a); break;
     }
   } else {
