@@ -84,6 +84,49 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wavefront reductions over DPP lane moves (no LDS round trip): each
+// 16-lane row by swapping neighbours and pairs and rotating by 4 and 8 lanes,
+// then the four rows' values (lanes 0, 16, 32, 48) read in a fixed order, so
+// the result is a fixed function of the 64 inputs and every lane gets it.
+// Every lane of the wavefront must be active.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Sum over the wavefront, the same value in every lane: each 16-lane row by
+// DPP moves (lane 0 of the row keeps a fixed association), then the rows'
+// sums (r0 + r1) + (r2 + r3).  Every lane must be active.
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+  v += dpp_f64<0xB1>(v);   // lane ^ 1
+  v += dpp_f64<0x4E>(v);   // lane ^ 2
+  v += dpp_f64<0x124>(v);  // row rotate 4
+  v += dpp_f64<0x128>(v);  // row rotate 8
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
+}
+
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -165,43 +165,6 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
 constexpr int kNormThreads = QSPEC_NORM_THREADS;
 constexpr int kNormV4 = 4096 / (4 * kNormThreads);  // float4 groups per thread (d <= 4096)
 
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
-  return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
-}
-
-__device__ __forceinline__ double readlane_f64(double v, int lane) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
-  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-
-// Sum over the wavefront, the same value in every lane: each 16-lane row by
-// DPP moves (lane 0 of the row keeps a fixed association), then the rows'
-// sums (r0 + r1) + (r2 + r3).  Every lane must be active.
-__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
-  v += dpp_f64<0xB1>(v);   // lane ^ 1
-  v += dpp_f64<0x4E>(v);   // lane ^ 2
-  v += dpp_f64<0x124>(v);  // row rotate 4
-  v += dpp_f64<0x128>(v);  // row rotate 8
-  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
-}
-
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
-  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
-                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))),
-               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
-                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
-}
-
 __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_v4_kernel(
     float* __restrict__ x, int64_t xs, const float* __restrict__ add, int64_t as, int d, double eps,
     uint16_t* __restrict__ y, uint8_t* __restrict__ yq, float* __restrict__ ys) {
