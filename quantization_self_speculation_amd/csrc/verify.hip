@@ -440,23 +440,42 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
   __shared__ double sh_base, sh_thr;
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const double* tr = rs + b * rnck;  // chunk totals, read by the first wavefront
+  const double* tp = pp + b * rnck;
+  const int per = (rnck + 63) / 64;
+  const int c0 = min(rnck, lane * per), c1 = min(rnck, c0 + per);
+  // the first wavefront's totals depend on b alone: with at most two chunks
+  // per lane they are requested together with the decision (one memory
+  // round trip instead of two)
+  double r0 = 0.0, r1 = 0.0, p0 = 0.0, p1 = 0.0;  // chunks c0, c0 + 1: residual, target
+  if (w == 0 && per <= 2) {
+    if (c0 < c1) {
+      r0 = tr[c0];
+      p0 = tp[c0];
+    }
+    if (c0 + 1 < c1) {
+      r1 = tr[c0 + 1];
+      p1 = tp[c0 + 1];
+    }
+  }
+  const float ub = us[b];
   const Decision D = dec[b];
   const double iSt = 1.0 / D.St, iSd = 1.0 / D.Sd;
   const float* rt = tgt + (b * (gamma + 1) + D.n) * V;
   const float* rd = drf + (b * gamma + min(D.n, gamma - 1)) * V;
 
-  const double* tr = rs + b * rnck;  // chunk totals, read by the first wavefront
-  const double* tp = pp + b * rnck;
   if (w == 0) {
     // chunk totals, one wavefront: lane l sums its run of `per` consecutive
     // chunks in order, then an inclusive scan over the lanes (fixed order)
-    const int per = (rnck + 63) / 64;
-    const int c0 = min(rnck, lane * per), c1 = min(rnck, c0 + per);
     int kind = D.kind;
-    const double* tot = tr;
-    auto scan = [&](const double* t, double& excl, double& R) {
+    int sel = 0;  // 0: residual totals, 1: target-probability totals
+    // total of chunk c (c0 <= c < c1) of the selected kind
+#define QSPEC_TOT(c) (per <= 2 ? (sel == 0 ? ((c) == c0 ? r0 : r1) : ((c) == c0 ? p0 : p1)) \
+                               : (sel == 0 ? tr : tp)[(c)])
+    double excl = 0.0, R = 0.0;
+    for (int pass = 0; pass < 2; ++pass) {  // a second pass only to fall back to p
       double v = 0.0;
-      for (int c = c0; c < c1; ++c) v += t[c];
+      for (int c = c0; c < c1; ++c) v += QSPEC_TOT(c);
       double incl = v;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -466,15 +485,11 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
       excl = __shfl_up(incl, 1, 64);
       if (lane == 0) excl = 0.0;
       R = __shfl(incl, 63, 64);
-    };
-    double excl, R;
-    scan(tot, excl, R);
-    if (R == 0.0 && kind == 0) {  // p == q everywhere: sample from p
-      kind = 1;
-      tot = tp;
-      scan(tot, excl, R);
+      if (!(R == 0.0 && kind == 0)) break;  // uniform
+      kind = 1;  // p == q everywhere: sample from p
+      sel = 1;
     }
-    const double thr = (double)us[b] * R;
+    const double thr = (double)ub * R;
     // each lane walks its run from its exclusive start; the lowest lane
     // whose walk passes the threshold holds the chunk
     int cs = -1;
@@ -482,7 +497,7 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
     {
       double run = excl;
       for (int c = c0; c < c1; ++c) {
-        const double nx = run + tot[c];
+        const double nx = run + QSPEC_TOT(c);
         if (nx > thr) {
           cs = c;
           base = run;
@@ -495,10 +510,11 @@ __global__ __launch_bounds__(256) void sample_select_kernel(
     // last chunk with mass (fallback when the threshold is at or past the total)
     int last_c = -1;
     for (int c = c1 - 1; c >= c0; --c)
-      if (tot[c] > 0.0) {
+      if (QSPEC_TOT(c) > 0.0) {
         last_c = c;
         break;
       }
+#undef QSPEC_TOT
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) last_c = max(last_c, __shfl_xor(last_c, o, 64));
     if (lane == (hit ? __builtin_ctzll(hit) : 0)) {
