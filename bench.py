@@ -894,11 +894,14 @@ def _counter_means(path, counter):
                 continue
             key = (r["Kernel_Name"], r["Dispatch_Id"])
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
-    copy = [v for (k, _), v in per.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+    # the calibration is the 1 GiB device-to-device copy: the largest copy
+    # dispatch (weight copies are smaller; torch's fill and random-number
+    # kernels are not copies -- the one that fills the lm_head weights writes
+    # 2 GB)
+    copy = [v for (k, _), v in per.items() if "copybuffer" in k.lower()]
     dom = [v for (k, _), v in per.items() if any(t in k for t in GEMM_KERNEL_TAGS)]
     if not copy or not dom:
         raise SystemExit(f"{path}: no copy ({len(copy)}) or GEMM ({len(dom)}) dispatches for {counter}")
-    # the 1 GiB copy is the largest elementwise dispatch
     return max(copy), sum(dom) / len(dom), len(dom)
 
 
