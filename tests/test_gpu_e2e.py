@@ -50,12 +50,13 @@ def test_embed_and_add_rmsnorm():
     _bf16_close(host_bits16(y2), om.to_bf16_bits(om.rmsnorm(xs[2::3], 1e-6)), frac_exact=0.999)
 
 
-@pytest.mark.parametrize("d,off", [(250, 0), (256, 1), (2048, 0)])
+@pytest.mark.parametrize("d,off", [(250, 0), (256, 1), (2048, 0), (2048, 2)])
 def test_add_rmsnorm_layouts(d, off):
     """Rows that the 16-byte kernel takes (d % 4 == 0, aligned) and rows
-    that fall back to the scalar kernel (d = 250; rows starting one float
-    past a 16-byte boundary): the same residual bits and the oracle's
-    RMSNorm within one bf16 unit."""
+    that fall back to the scalar kernel (d = 250; rows starting one or two
+    floats past a 16-byte boundary): the same residual bits and the oracle's
+    RMSNorm within one bf16 unit; with the drafter's codes (d % 128 == 0),
+    the same rows and the stand-alone quantizer's codes."""
     rng = synth.make_rng(55, d + off)
     M = 7
     say(f"add_rmsnorm d={d} offset={off}")
@@ -72,6 +73,18 @@ def test_add_rmsnorm_layouts(d, off):
     xs = (x0 + add).astype(np.float32)
     assert np.array_equal(host(x), xs)
     _bf16_close(host_bits16(y), om.to_bf16_bits(om.rmsnorm(xs, 1e-6)), frac_exact=0.999)
+    if d % 128 == 0:
+        # the same rows with the drafter's codes: the residual again, and the
+        # codes of the bf16 rows exactly as the stand-alone quantizer gives them
+        x.copy_(dev(x0))
+        yq = torch.empty((M, d // 2), dtype=torch.uint8, device="cuda:0")
+        ys = torch.empty((M,), dtype=torch.float32, device="cuda:0")
+        y2 = torch.empty((M, d), dtype=torch.bfloat16, device="cuda:0")
+        qb.add_rmsnorm_quant(x, a, y2, yq, ys, 1e-6)
+        assert np.array_equal(host(x), xs)
+        assert np.array_equal(host_bits16(y2), host_bits16(y))
+        Xq, Xs = q.quant_act(y2)
+        assert np.array_equal(host(yq), host(Xq)) and np.array_equal(host(ys), host(Xs))
 
 
 def test_rope_kv_and_attention():
