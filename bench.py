@@ -213,34 +213,43 @@ class Decode:
 def measure_prefill(torch, q, wl, reps=5):
     """Prefill-shaped GEMMs (M = 2048 tokens) on the same packed buffers:
     W4A4 (int8 MFMA) vs W4A16 (bf16 MFMA), per projection; kernel time from
-    HIP events around graph replays of 3 launches each."""
+    HIP events around graph replays of 3 launches each.  Also the W4A4 layer
+    with a bf16 output (what a chained prefill hands the next op: half the
+    output bytes)."""
     import synth
     rng = synth.make_rng(2, 0)
     M = 2048
     out = {}
-    tot4 = tot16 = ops_all = 0.0
+    tot4 = tot4b = tot16 = ops_all = 0.0
     for p in wl.proj:
         N, K = p["N"], p["K"]
         X = synth.activations(rng, M, K)
         Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to("cuda:0")
         Xq, Xs = q.quant_act(Xd)
         Y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        Yb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
         Wq, Ws = p["copies"][0]
         t4 = _graph_time(torch, lambda: q.gemm_w4a4(Xq, Xs, Wq, Ws, Y=Y), reps)
+        t4b = _graph_time(torch, lambda: q.gemm_w4a4_bf16(Xq, Xs, Wq, Ws, Y=Yb), reps)
         t16 = _graph_time(torch, lambda: q.gemm_w4a16(Xd, Wq, Ws, Y=Y), reps)
         tq = _graph_time(torch, lambda: q.quant_act(Xd, Xq, Xs), reps)
         ops = 2.0 * M * N * K
         out[p["name"]] = {"w4a4_us": round(t4, 2), "w4a4_tops": round(ops / t4 / 1e6, 1),
                           "w4a4_frac_int8": round(ops / t4 / 1e6 / INT8_PEAK_TOPS, 4),
+                          "w4a4_bf16out_us": round(t4b, 2),
+                          "w4a4_bf16out_frac_int8": round(ops / t4b / 1e6 / INT8_PEAK_TOPS, 4),
                           "w4a16_us": round(t16, 2), "w4a16_tflops": round(ops / t16 / 1e6, 1),
                           "w4a16_frac_bf16": round(ops / t16 / 1e6 / BF16_PEAK_TFLOPS, 4),
                           "quant_act_us": round(tq, 2), "w4a16_over_w4a4": round(t16 / t4, 3)}
         tot4 += t4
+        tot4b += t4b
         tot16 += t16
         ops_all += ops
-        del Xd, Xq, Xs, Y
+        del Xd, Xq, Xs, Y, Yb
     out["all"] = {"w4a4_tops": round(ops_all / tot4 / 1e6, 1),
                   "w4a4_frac_int8": round(ops_all / tot4 / 1e6 / INT8_PEAK_TOPS, 4),
+                  "w4a4_bf16out_tops": round(ops_all / tot4b / 1e6, 1),
+                  "w4a4_bf16out_frac_int8": round(ops_all / tot4b / 1e6 / INT8_PEAK_TOPS, 4),
                   "w4a16_tflops": round(ops_all / tot16 / 1e6, 1),
                   "w4a16_frac_bf16": round(ops_all / tot16 / 1e6 / BF16_PEAK_TFLOPS, 4)}
     return out
@@ -753,6 +762,7 @@ def run(args):
         line["prefill_m2048"] = measure_prefill(torch, q, wl)
         al = line["prefill_m2048"]["all"]
         al["w4a4_frac_of_measured_int8"] = round(al["w4a4_tops"] / ceil["mfma_int8_TOPS"], 4)
+        al["w4a4_bf16out_frac_of_measured_int8"] = round(al["w4a4_bf16out_tops"] / ceil["mfma_int8_TOPS"], 4)
         al["w4a16_frac_of_measured_bf16"] = round(al["w4a16_tflops"] / ceil["mfma_bf16_TFLOPS"], 4)
         log("batched serving sweep")
         line["batch_sweep_layer"] = measure_batch_sweep(torch, q, wl)
