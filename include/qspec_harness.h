@@ -50,7 +50,12 @@ qspec_status qspec_embed(const uint16_t* emb, int64_t V, int64_t d, const int32_
  * is rounded to fp32 and stored back into x), then
  * y[m] = bf16(x[m] / sqrt(mean(x[m]^2) + eps)).  x and add are fp32 rows of
  * strides x_stride, add_stride >= d elements (add may be NULL), y bf16 bits
- * [M][d] (dense); 1 <= d <= 4096. */
+ * [M][d] (dense); 1 <= d <= 4096.  A row's result does not depend on the
+ * other rows of the call; it is computed by one of two kernels whose fp64
+ * sums of squares associate differently -- the 16-byte one when d % 4 == 0,
+ * x, add (and their strides) are 16-byte aligned and y 8-byte aligned, a
+ * scalar one otherwise -- so the same row given in the two layouts may
+ * round y one bf16 unit apart. */
 qspec_status qspec_add_rmsnorm(float* x, int64_t x_stride, const float* add, int64_t add_stride,
                                int64_t M, int64_t d, double eps, uint16_t* y,
                                qspec_stream stream);
