@@ -1211,6 +1211,9 @@ struct StreamArgs {
 #ifndef QSPEC_ST_TARGET
 #define QSPEC_ST_TARGET 4096  // wavefronts the k-split aims for
 #endif
+#ifndef QSPEC_ST_WIDE
+#define QSPEC_ST_WIDE 512     // integer modes: row blocks from which the ring is three deep
+#endif
 constexpr int kStreamMaxM = 16;
 constexpr int kStreamMaxW = 16;
 
@@ -1224,10 +1227,9 @@ struct StreamStage {
 };
 
 
-template <int MODE, bool WITHP>
+template <int MODE, bool WITHP, int PD = (MODE == kW4A16 ? QSPEC_ST_PD16 : QSPEC_ST_PD4)>
 __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   static_assert(!(WITHP && MODE == kW4A16), "the int32 partials output is an integer-mode path");
-  constexpr int PD = MODE == kW4A16 ? QSPEC_ST_PD16 : QSPEC_ST_PD4;
   extern __shared__ __attribute__((aligned(16))) float red_[];  // [nw][64][4] when nw > 1
   float(*red)[64][4] = reinterpret_cast<float(*)[64][4]>(red_);
   const int nw = blockDim.x >> 6;
@@ -1395,6 +1397,16 @@ hipError_t launch_stream(const void* X, const float* Xs, const uint8_t* Wq, cons
   if constexpr (MODE != kW4A16) {
     if (P != nullptr) {
       hipLaunchKernelGGL((stream_kernel<MODE, true>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+      return hipGetLastError();
+    }
+    // integer modes on wide grids (at least QSPEC_ST_WIDE row blocks, few
+    // groups per wavefront): a three-group ring.  Measured on MI355X at
+    // M = 16, K = 2048: N = 11264 7.35 -> 5.72 us; the narrower shapes
+    // (N <= 4608) keep two groups, which streams faster there.  The ring
+    // depth changes when loads are issued, not what is computed: the rows
+    // are bitwise the same either way.
+    if (a.nrb >= QSPEC_ST_WIDE) {
+      hipLaunchKernelGGL((stream_kernel<MODE, false, 3>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
       return hipGetLastError();
     }
   }

@@ -38,6 +38,7 @@ SHAPES = [
     (128, 96, 256),
     (129, 96, 256),
     (72, 8200, 256),    # W4A16 SKINNY without a k-split: one 80-row activation block
+    (9, 8208, 256),     # STREAM on a wide grid (513 row blocks: the integer modes' 3-deep ring)
 ]
 
 
