@@ -281,6 +281,27 @@ qspec_status qspec_gemm_w4a16(const uint16_t* X, const uint8_t* Wq,
                               void* ws, size_t ws_bytes, qspec_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * qspec_gemm_w4a16_swiglu -- the verifier's gate|up layer with its SwiGLU
+ * in the GEMM's epilogue (one launch instead of the layer and
+ * qspec_silu_mul).  The N = 2F rows of the packed buffer are in pair order:
+ * in 16-row block b, rows 16b .. 16b+7 are gate rows 8b .. 8b+7 and rows
+ * 16b+8 .. 16b+15 the matching up rows.  With Y the SKINNY-family result of
+ * qspec_gemm_w4a16 on the same buffer (the same k-split, a function of
+ * N and K),
+ *     A[m, 8b+i] = bf16(silu(Y[m,16b+i]) * Y[m,16b+8+i]),
+ *     silu(g) = g / (1 + exp(-g)), fp64 with one rounding,
+ * bitwise what qspec_silu_mul_pairs gives on that Y.
+ *   X [M][K] bf16 bits (in); Wq, Ws tiled as for qspec_gemm_w4a16 (pair
+ *   order, N % 16 == 0); A [M][N/2] bf16 bits (out, 16-byte aligned).
+ *   ws/ws_bytes: as for qspec_gemm_w4a16 (QSPEC_OP_GEMM_W4A16, M, N, K).
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_gemm_w4a16_swiglu(const uint16_t* X, const uint8_t* Wq,
+                                     const uint16_t* Ws, int64_t M, int64_t N,
+                                     int64_t K, int group, uint16_t* A,
+                                     void* ws, size_t ws_bytes,
+                                     qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
  * qspec_verify -- accept or reject gamma drafted tokens per sequence.
  * Greedy (mode 0; SpecQuant review, method paragraph: a full match is
  * accepted and the first mismatch is rewritten by the parent):

@@ -107,6 +107,14 @@ qspec_status qspec_add_rmsnorm_quant(float* x, int64_t x_stride, const float* ad
 qspec_status qspec_silu_mul(const float* gu, int64_t M, int64_t ffn, uint16_t* a,
                             qspec_stream stream);
 
+/* SwiGLU over gate|up outputs in pair order (the row order of
+ * qspec_gemm_w4a16_swiglu's buffer): gu fp32 [M][2 ffn], in each 16-column
+ * block b columns 16b .. 16b+7 gate and 16b+8 .. 16b+15 the matching up
+ * values; a[m][8b + i] = bf16(silu(gu[m][16b+i]) * gu[m][16b+8+i]) as in
+ * qspec_silu_mul.  ffn % 8 == 0. */
+qspec_status qspec_silu_mul_pairs(const float* gu, int64_t M, int64_t ffn, uint16_t* a,
+                                  qspec_stream stream);
+
 /* out[m * out_stride] = the lowest index of the largest value of row m of
  * x fp32 [M][V]. */
 qspec_status qspec_argmax(const float* x, int64_t M, int64_t V, int32_t* out,

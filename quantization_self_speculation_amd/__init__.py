@@ -24,6 +24,8 @@ from .binding import (  # noqa: F401
     gemm_w4a8,
     quant_act8,
     gemm_w4a16,
+    gemm_w4a16_swiglu,
+    pair_rows,
     verify,
     verify_noalloc,
     workspace_bytes,
@@ -40,6 +42,7 @@ from .binding import (  # noqa: F401
     attention,
     rope_attention,
     silu_mul,
+    silu_mul_pairs,
     add_rmsnorm_quant,
     argmax,
     spec_prepare,

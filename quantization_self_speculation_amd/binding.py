@@ -61,6 +61,7 @@ def lib():
             "qspec_gemm_w4a4": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
             "qspec_gemm_w4a4_bf16": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_gemm_w4a16": (I, [P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
+            "qspec_gemm_w4a16_swiglu": (I, [P, P, P, I64, I64, I64, I, P, P, SZ, P]),
             "qspec_quant_act8": (I, [P, I64, I64, P, P, P]),
             "qspec_gemm_w4a8": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
             "qspec_verify": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P, SZ, P]),
@@ -72,6 +73,7 @@ def lib():
             "qspec_rope_attention": (I, [P, I64, I, I, P, P, ctypes.c_double, P, P, P, I64, I64, P,
                                          P]),
             "qspec_silu_mul": (I, [P, I64, I64, P, P]),
+            "qspec_silu_mul_pairs": (I, [P, I64, I64, P, P]),
             "qspec_add_rmsnorm_quant": (I, [P, I64, P, I64, I64, I64, ctypes.c_double, P, P, P, P]),
             "qspec_argmax": (I, [P, I64, I64, P, I64, P]),
             "qspec_spec_prepare": (I, [I, I64, I, I, P, P, P, P, P, P, P]),
@@ -298,6 +300,40 @@ def gemm_w4a16(X, Wq, Ws, variant=GEMM_AUTO, Y=None, ws=None, N=None):
     return Y
 
 
+def gemm_w4a16_swiglu(X, Wq, Ws, A=None, ws=None, N=None):
+    """Verify-mode gate|up layer with its SwiGLU fused -> A bf16 [M, N/2]:
+    Wq, Ws hold the N = 2F gate|up rows in pair order (see pair_rows), the
+    SKINNY family's k-split; bitwise silu_mul_pairs of gemm_w4a16(SKINNY)."""
+    _need(X, "X", torch.bfloat16)
+    M, K = X.shape
+    if N is None:
+        N = 2 * A.shape[1] if A is not None else Wq.shape[0]
+    _need(Wq, "Wq", torch.uint8, (padded_rows(N), K // 2))
+    _need(Ws, "Ws", torch.float16, (padded_rows(N), K // GROUP))
+    if A is None:
+        A = torch.empty((M, N // 2), dtype=torch.bfloat16, device=X.device)
+    _need(A, "A", torch.bfloat16, (M, N // 2))
+    w, wb = _workspace(workspace_bytes(OP_GEMM_W4A16, M, N, K), X.device, ws)
+    _check(lib().qspec_gemm_w4a16_swiglu(_ptr(X), _ptr(Wq), _ptr(Ws), M, N, K, GROUP, _ptr(A),
+                                         _ptr(w), wb, _stream()), "qspec_gemm_w4a16_swiglu")
+    return A
+
+
+def pair_rows(gate_up):
+    """[2F, ...] gate|up rows (gate rows first) -> the pair order the fused
+    gate|up layer reads: in each block of 16 rows, 8 gate rows then the 8
+    matching up rows.  F % 8 == 0; works on numpy arrays and torch tensors."""
+    F = gate_up.shape[0] // 2
+    if F % 8 != 0 or 2 * F != gate_up.shape[0]:
+        raise ValueError("pair order needs 2F rows with F a multiple of 8")
+    g = gate_up[:F].reshape(F // 8, 8, *gate_up.shape[1:])
+    u = gate_up[F:].reshape(F // 8, 8, *gate_up.shape[1:])
+    if isinstance(gate_up, torch.Tensor):
+        return torch.stack((g, u), dim=1).reshape(gate_up.shape)
+    import numpy as _np
+    return _np.stack((g, u), axis=1).reshape(gate_up.shape)
+
+
 def verify(mode, target_logits, draft_tok, draft_logits=None, u_accept=None, u_sample=None,
            n_accept=None, out_tok=None, ws=None):
     """-> (n_accept int32 [B], out_tok int32 [B, gamma+1] padded with -1)."""
@@ -449,6 +485,15 @@ def silu_mul(gu, a):
     _dev(a, "a", torch.bfloat16)
     M, F = a.shape
     _check(lib().qspec_silu_mul(_ptr(gu), M, F, _ptr(a), _stream()), "qspec_silu_mul")
+
+
+def silu_mul_pairs(gu, a):
+    """silu_mul over gate|up outputs in pair order (the columns of a layer
+    whose rows are in pair_rows order); gu fp32 [M, 2F], a bf16 [M, F]"""
+    _dev(gu, "gu", torch.float32)
+    _dev(a, "a", torch.bfloat16)
+    M, F = a.shape
+    _check(lib().qspec_silu_mul_pairs(_ptr(gu), M, F, _ptr(a), _stream()), "qspec_silu_mul_pairs")
 
 
 def argmax(x, out, out_stride=1):

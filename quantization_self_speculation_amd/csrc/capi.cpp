@@ -329,6 +329,22 @@ qspec_status qspec_gemm_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16
                     "gemm_w4a16 launch");
 }
 
+qspec_status qspec_gemm_w4a16_swiglu(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws,
+                                     int64_t M, int64_t N, int64_t K, int group, uint16_t* A,
+                                     void* ws, size_t ws_bytes, qspec_stream stream) {
+  QS_TRY(check_gemm(M, N, K, group, QSPEC_GEMM_SKINNY, true));
+  QS_REQUIRE(N % 16 == 0, QSPEC_ERR_SHAPE,
+             "N (gate|up rows) must be a multiple of 16 (got %lld)", (long long)N);
+  QS_PTR(X);
+  QS_PTR(Wq);
+  QS_PTR(Ws);
+  QS_PTR(A);
+  QS_TRY(check_ws(ws, ws_bytes, w4a16_ws_bytes(M, N, K)));
+  QS_TRY(device_check());
+  return hip_result(launch_w4a16_swiglu(X, Wq, Ws, M, N, K, A, ws, ws_bytes, (hipStream_t)stream),
+                    "gemm_w4a16_swiglu launch");
+}
+
 qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V, const int32_t* draft_tok,
                           const float* draft_logits, const float* target_logits,
                           const float* u_accept, const float* u_sample, int32_t* n_accept,
@@ -510,6 +526,17 @@ qspec_status qspec_silu_mul(const float* gu, int64_t M, int64_t ffn, uint16_t* a
   QS_EPTR(a);
   QS_TRY(device_check());
   return hip_result(launch_silu_mul(gu, M, ffn, a, (hipStream_t)stream), "silu_mul launch");
+}
+
+qspec_status qspec_silu_mul_pairs(const float* gu, int64_t M, int64_t ffn, uint16_t* a,
+                                  qspec_stream stream) {
+  QS_REQUIRE(M >= 1 && ffn >= 8 && ffn % 8 == 0 && M * ffn <= ((int64_t)1 << 40), QSPEC_ERR_SHAPE,
+             "need M >= 1 and ffn a positive multiple of 8");
+  QS_EPTR(gu);
+  QS_EPTR(a);
+  QS_TRY(device_check());
+  return hip_result(launch_silu_mul_pairs(gu, M, ffn, a, (hipStream_t)stream),
+                    "silu_mul_pairs launch");
 }
 
 qspec_status qspec_argmax(const float* x, int64_t M, int64_t V, int32_t* out, int64_t out_stride,

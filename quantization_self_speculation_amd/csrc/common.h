@@ -134,6 +134,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// fp64 -> bf16 with one rounding: truncate to fp32 and set the lowest bit if
+// anything was dropped (round to odd keeps the information a later rounding
+// to nearest needs), then round fp32 -> bf16 to nearest even.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
+  float t = __double2float_rz(v);
+  uint32_t u = __float_as_uint(t);
+  if ((double)t != v) u |= 1u;
+  return f32_to_bf16_rne(__uint_as_float(u));
+}
+
+// SwiGLU of one gate / up pair of fp32 GEMM outputs: bf16(silu(g) * u),
+// silu(g) = g / (1 + exp(-g)), in fp64 with one rounding.
+__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
+  const double gd = g, ud = u;
+  return f64_to_bf16_rne(gd / (1.0 + exp(-gd)) * ud);
+}
+
 // The code of v at the activation scale s = absmax / 7 (s > 0), with r the
 // IEEE reciprocal of s.  |v / s| <= 7 (about), so v * r is within 2^-20 of
 // the exact quotient and within 2^-19 of the IEEE quotient v / s; wherever

@@ -198,6 +198,7 @@ struct SkinnyArgs {
   float* part;              // [S][M][N] when S > 1
   unsigned long long* cnt;  // [T] when S > 1
   int32_t* P;               // W4A4 / W4A8 int32 group partials (optional)
+  uint16_t* A;              // W4A16 gate|up in pair order: bf16 SwiGLU [M][N/2] instead of Y
   int M, N, K, S, gps, ntiles, T;
 };
 
@@ -208,7 +209,7 @@ struct SkinnyArgs {
 // do not stay in an XCD's L2), the writer waits for its stores to complete
 // before the arrival count, and the arrival counter (in the caller's
 // workspace, zero at rest) is reset by the last slice.
-template <int MODE, int MB, int NB, int NWV>
+template <int MODE, int MB, int NB, int NWV, bool SW>
 __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot)[NB][MB], int t,
                                             int slice, int m0, int n_wg, int n_w, int l16, int lg,
                                             int* s_last_ptr) {
@@ -218,6 +219,30 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   const int M = a.M, N = a.N;
   int& s_last = *s_last_ptr;
   const bool vec = (N & 3) == 0;
+  if (SW && a.S == 1) {
+    // W4A16 gate|up with the SwiGLU output (a.A): lanes lg = 0, 1 hold gate
+    // columns 0 .. 7 of each 16-row block, lanes lg = 2, 3 (32 lanes on)
+    // the matching up columns
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        float u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = __shfl_xor(tot[nb][mb][r], 32, 64);
+        const int m = m0 + mb * 16 + l16;
+        const int n16 = n_w + nb * 16;  // the block's first row
+        if (lg < 2 && m < M && n16 < N) {
+          const int j = n16 / 2 + lg * 4;
+          uint16_t h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = swiglu_bf16(tot[nb][mb][r], u[r]);
+          *reinterpret_cast<uint2*>(a.A + (int64_t)m * (N / 2) + j) =
+              make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        }
+      }
+    return;
+  }
   if (a.S == 1) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -273,9 +298,35 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   }
   __syncthreads();
   if (!s_last) return;
+  const int64_t MN = (int64_t)M * N;
+  if constexpr (SW) {
+    // SwiGLU epilogue: each thread takes gate / up pairs (columns c and c + 8
+    // of a 16-row block) and sums both over the slices exactly as the
+    // element loop below sums one column
+    constexpr int PPT = ROWS * WROWS / 2 / NT;
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+      const int pr = threadIdx.x + NT * e;
+      const int m = m0 + pr / (WROWS / 2), qq = pr % (WROWS / 2);
+      const int ng = n_wg + (qq >> 3) * 16 + (qq & 7);
+      if (m < M && ng < N) {
+        const float* sg = a.part + (int64_t)m * N + ng;
+        float g = 0.f, u = 0.f;
+        for (int s = 0; s < a.S; ++s) {
+          const float vg = __hip_atomic_load(sg + s * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          const float vu = __hip_atomic_load(sg + 8 + s * MN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          g = s == 0 ? vg : g + vg;
+          u = s == 0 ? vu : u + vu;
+        }
+        a.A[(int64_t)m * (N / 2) + n_wg / 2 + qq] = swiglu_bf16(g, u);
+      }
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(a.cnt + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return;
+  }
   // all partials of an element are requested before any is added (in slice
   // order), 8 slices per batch
-  const int64_t MN = (int64_t)M * N;
   constexpr int EPT = ROWS * WROWS / NT;
   float acc[EPT];
   const float* src[EPT];
@@ -316,10 +367,11 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
 // a clamped, valid address) so the compiler keeps exact load counters and the
 // weight ring stays in flight across waits; only the arithmetic of groups past
 // the end of the slice is skipped (a branch uniform over the workgroup).
-template <int MODE, int MB, int NB, int CH, int PD, bool WITHP, int NWV = 4>
+template <int MODE, int MB, int NB, int CH, int PD, bool XOUT, int NWV = 4>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny_wpe(MODE, MB)))) void skinny_kernel(const SkinnyArgs a) {
   static_assert(PD % CH == 0, "prefetch depth must be a multiple of the chunk");
-  static_assert(!(WITHP && MODE == kW4A16), "the int32 partials output is an integer-mode path");
+  // XOUT: the extra output -- the int32 group partials (a.P) in the integer
+  // modes, the SwiGLU of gate|up rows in pair order (a.A) in W4A16
   constexpr int NT = 64 * NWV;             // threads of a workgroup
   constexpr int ROWS = 16 * MB;            // activation rows of an m-chunk
   constexpr int WROWS = 16 * NB * NWV;     // weight rows of a tile (NWV wavefronts x NB blocks of 16)
@@ -554,7 +606,7 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               tot[nb][mb][r] = fmaf(sc[r], (float)acc[nb][mb][r], tot[nb][mb][r]);
-            if (WITHP) {
+            if (XOUT) {
               const int m = m0 + mb * 16 + l16, n = n_w + nb * 16 + lg * 4;
               if (m < M) {
 #pragma unroll
@@ -578,7 +630,8 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
       }
     }
   }
-  finish_tile<MODE, MB, NB, NWV>(a, tot, t, slice, m0, n_wg, n_w, l16, lg, &s_last);
+  finish_tile<MODE, MB, NB, NWV, MODE == kW4A16 && XOUT>(a, tot, t, slice, m0, n_wg, n_w, l16, lg,
+                                                        &s_last);
 }
 
 // ============================================================================
@@ -1607,49 +1660,49 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool max_tiles
   return p;
 }
 
-template <int MODE, bool WITHP>
+template <int MODE, bool XOUT>
 hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
   const dim3 grid((unsigned)p.blocks), blk(64 * p.NWV);
   // W4A16 with three activation blocks, or any mode with one: the workgroup
   // size balanced over the CUs (5, 8 or 10 wavefronts; 4 is the generic case)
   if (MODE == kW4A16 && p.MB == 3 && p.NWV != 4) {
     switch (p.NWV) {
-      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, false, 5>), grid, blk, 0, s, a); break;
-      case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, false, 8>), grid, blk, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, false, 10>), grid, blk, 0, s, a); break;
+      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 5>), grid, blk, 0, s, a); break;
+      case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 8>), grid, blk, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 10>), grid, blk, 0, s, a); break;
     }
     return hipGetLastError();
   }
   if (p.MB == 1 && p.NWV != 4) {
     if constexpr (MODE == kW4A16) {
       switch (p.NWV) {
-        case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 5>), grid, blk, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 8>), grid, blk, 0, s, a); break;
-        default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false, 10>), grid, blk, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 5>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 8>), grid, blk, 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 10>), grid, blk, 0, s, a); break;
       }
     } else {  // W4A4 and W4A8 share the int8 data flow and its parameters
       switch (p.NWV) {
-        case 5: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP, 5>), grid, blk, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP, 8>), grid, blk, 0, s, a); break;
-        default: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP, 10>), grid, blk, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT, 5>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT, 8>), grid, blk, 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT, 10>), grid, blk, 0, s, a); break;
       }
     }
     return hipGetLastError();
   }
   if constexpr (MODE == kW4A16) {
     switch (p.MB) {
-      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, false>), grid, blk, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_NB16, QSPEC_SK_B2, false>), grid, blk, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, false>), grid, blk, 0, s, a); break;
-      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 5, QSPEC_SK_NB16, QSPEC_SK_B4, false>), grid, blk, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_NB16, QSPEC_SK_B4, false>), grid, blk, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT>), grid, blk, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_NB16, QSPEC_SK_B2, XOUT>), grid, blk, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT>), grid, blk, 0, s, a); break;
+      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 5, QSPEC_SK_NB16, QSPEC_SK_B4, XOUT>), grid, blk, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_NB16, QSPEC_SK_B4, XOUT>), grid, blk, 0, s, a); break;
     }
   } else {
     switch (p.MB) {
-      case 1: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, WITHP>), grid, blk, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((skinny_kernel<MODE, 2, 1, QSPEC_SK_A2, WITHP>), grid, blk, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((skinny_kernel<MODE, 3, 1, QSPEC_SK_A3, WITHP>), grid, blk, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<MODE, 4, 1, QSPEC_SK_A4, WITHP>), grid, blk, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT>), grid, blk, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<MODE, 2, 1, QSPEC_SK_A2, XOUT>), grid, blk, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<MODE, 3, 1, QSPEC_SK_A3, XOUT>), grid, blk, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<MODE, 4, 1, QSPEC_SK_A4, XOUT>), grid, blk, 0, s, a); break;
     }
   }
   return hipGetLastError();
@@ -1657,9 +1710,8 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
 
 template <int MODE>
 hipError_t launch_skinny(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
-  if constexpr (MODE != kW4A16) {
-    if (a.P != nullptr) return launch_skinny_t<MODE, true>(a, p, s);
-  }
+  // the extra output: partials in the integer modes, the SwiGLU in W4A16
+  if (MODE != kW4A16 ? a.P != nullptr : a.A != nullptr) return launch_skinny_t<MODE, true>(a, p, s);
   return launch_skinny_t<MODE, false>(a, p, s);
 }
 
@@ -1780,6 +1832,25 @@ hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws
   a.Wq = Wq;
   a.Ws = Ws;
   a.Y = Y;
+  a.cnt = p.S > 1 ? w.cnt : nullptr;
+  a.part = p.S > 1 ? w.part : nullptr;
+  a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;
+  return launch_skinny<kW4A16>(a, p, s);
+}
+
+// The gate|up layer with the SwiGLU in the epilogue: the SKINNY family's
+// plan for (M, N, K) -- the same k-split as qspec_gemm_w4a16 with the
+// SKINNY variant, so A is bitwise the pair-order SiLU * up of that Y.
+hipError_t launch_w4a16_swiglu(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
+                               int64_t N, int64_t K, uint16_t* A, void* ws, size_t ws_bytes,
+                               hipStream_t s) {
+  const WsSplit w = ws_split(ws, ws_bytes);
+  const SkinnyPlan p = plan_skinny(0, M, N, K);
+  SkinnyArgs a{};
+  a.X = X;
+  a.Wq = Wq;
+  a.Ws = Ws;
+  a.A = A;
   a.cnt = p.S > 1 ? w.cnt : nullptr;
   a.part = p.S > 1 ? w.part : nullptr;
   a.M = (int)M; a.N = (int)N; a.K = (int)K; a.S = p.S; a.gps = p.gps; a.ntiles = p.ntiles; a.T = p.T;

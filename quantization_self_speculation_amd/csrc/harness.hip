@@ -18,16 +18,6 @@
 namespace qspec {
 namespace {
 
-// fp64 -> bf16 with one rounding: truncate to fp32 and set the lowest bit if
-// anything was dropped (round to odd keeps the information a later rounding
-// to nearest needs), then round fp32 -> bf16 to nearest even.
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
-  float t = __double2float_rz(v);
-  uint32_t u = __float_as_uint(t);
-  if ((double)t != v) u |= 1u;
-  return f32_to_bf16_rne(__uint_as_float(u));
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 template <typename T>
@@ -589,8 +579,23 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
   const int64_t n = M * F;
   for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n; t += (int64_t)gridDim.x * 256) {
     const int64_t m = t / F, j = t % F;
-    const double g = gu[m * 2 * F + j], u = gu[m * 2 * F + F + j];
-    a[t] = f64_to_bf16_rne(g / (1.0 + exp(-g)) * u);
+    a[t] = swiglu_bf16(gu[m * 2 * F + j], gu[m * 2 * F + F + j]);
+  }
+}
+
+// The same over gate|up outputs in pair order (the row order the fused
+// gate|up GEMM reads): in each 16-column block b of gu[m], columns 16b ..
+// 16b + 7 are gate rows 8b .. 8b + 7 and columns 16b + 8 .. 16b + 15 the
+// matching up rows, so a[m][8b + i] = bf16(silu(gu[m][16b + i]) *
+// gu[m][16b + 8 + i]).  F % 8 == 0.
+__global__ __launch_bounds__(256) void silu_mul_pairs_kernel(const float* __restrict__ gu,
+                                                             int64_t M, int64_t F,
+                                                             uint16_t* __restrict__ a) {
+  const int64_t n = M * F;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n; t += (int64_t)gridDim.x * 256) {
+    const int64_t m = t / F, j = t % F;
+    const int64_t c = m * 2 * F + (j >> 3) * 16 + (j & 7);
+    a[t] = swiglu_bf16(gu[c], gu[c + 8]);
   }
 }
 
@@ -866,6 +871,14 @@ hipError_t launch_silu_mul(const float* gu, int64_t M, int64_t F, uint16_t* a, h
   const int64_t n = M * F;
   const int64_t blocks = std::min<int64_t>(cdiv(n, 256), 4096);
   hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, s, gu, M, F, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_pairs(const float* gu, int64_t M, int64_t F, uint16_t* a,
+                                 hipStream_t s) {
+  const int64_t n = M * F;
+  const int64_t blocks = std::min<int64_t>(cdiv(n, 256), 4096);
+  hipLaunchKernelGGL(silu_mul_pairs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, gu, M, F, a);
   return hipGetLastError();
 }
 

@@ -27,6 +27,11 @@ size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
                         int64_t N, int64_t K, int variant, float* Y, void* ws, size_t ws_bytes,
                         hipStream_t s);
+// the W4A16 gate|up layer in the SKINNY family with its SwiGLU in the
+// epilogue: rows of Wq/Ws in pair order, A bf16 [M][N/2]
+hipError_t launch_w4a16_swiglu(const uint16_t* X, const uint8_t* Wq, const uint16_t* Ws, int64_t M,
+                               int64_t N, int64_t K, uint16_t* A, void* ws, size_t ws_bytes,
+                               hipStream_t s);
 
 size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
@@ -75,6 +80,8 @@ hipError_t launch_rope_attention(const float* qkv, int64_t M, int H, int Hkv, co
                                  uint16_t* vc, int64_t B, int64_t cap, uint16_t* out,
                                  hipStream_t s);
 hipError_t launch_silu_mul(const float* gu, int64_t M, int64_t F, uint16_t* a, hipStream_t s);
+hipError_t launch_silu_mul_pairs(const float* gu, int64_t M, int64_t F, uint16_t* a,
+                                 hipStream_t s);
 hipError_t launch_add_rmsnorm_quant(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
                                     int64_t d, double eps, uint16_t* y, uint8_t* yq, float* ys,
                                     hipStream_t s);

@@ -14,7 +14,9 @@ same INT4 weights: a middle precision over one base, "SpecQuant", Abstract
 (arXiv)), with the same verify step.
 
 The W4A16 layers of decode and verify forwards use one kernel family
-(`GEMM_SKINNY`), whose per-row result does not depend on the row count, and
+(`GEMM_SKINNY`), whose per-row result does not depend on the row count (the
+gate|up layer with its SwiGLU in the epilogue, on rows packed in pair
+order), and
 every other kernel computes rows independently: a verify forward therefore
 reproduces bit for bit what pure W4A16 decoding computes, and greedy
 self-speculation emits exactly the pure greedy tokens.  The drafter's layers
@@ -33,6 +35,13 @@ import torch
 from . import binding as b
 
 DRAFT, VERIFY, DRAFT8 = "w4a4", "w4a16", "w4a8"
+
+
+def _unpair_cols(Y):
+    """[M, 2F] columns in pair order (see binding.pair_rows) -> gate columns
+    then up columns (a copy)."""
+    M, N = Y.shape
+    return Y.reshape(M, N // 16, 2, 8).transpose(1, 2).reshape(M, N).clone()
 
 
 def _view(buf, *shape):
@@ -72,7 +81,14 @@ class Decoder:
 
         emb = np.ascontiguousarray(weights["emb"]).view(np.int16)
         self.emb = torch.from_numpy(emb).to(dev).view(torch.bfloat16)
-        self.layers = [{k: packed(L[k]) for k in ("qkv", "o", "gu", "down")}
+        # gate|up rows in pair order (8 gate rows, then their 8 up rows, per
+        # 16-row block): the W4A16 layer can then finish with the SwiGLU in
+        # its epilogue (qspec_gemm_w4a16_swiglu); the drafters' outputs go
+        # through the pair-order silu_mul
+        if cfg.ffn % 8 != 0:
+            raise ValueError("ffn must be a multiple of 8")
+        self.layers = [{k: packed(b.pair_rows(L[k]) if k == "gu" else L[k])
+                        for k in ("qkv", "o", "gu", "down")}
                        for L in weights["layers"]]
         self.lm = packed(weights["lm"])
 
@@ -165,7 +181,8 @@ class Decoder:
         def lin(li, name, X, W, Y, coded=False):
             self._linear(mode, X, W, Y, variant, coded)
             if trace is not None:
-                trace.append((li, name, X.clone(), Y.clone()))
+                # gate|up outputs back in gate-then-up column order
+                trace.append((li, name, X.clone(), _unpair_cols(Y) if name == "gu" else Y.clone()))
 
         # in draft mode the RMSNorm kernel also writes the drafter's 4-bit
         # codes of its bf16 output (one launch, not two)
@@ -200,9 +217,16 @@ class Decoder:
             lin(li, "o", att, L["o"], o)
             norm(x, o, h)
             gu = _view(self.gu, M, 2 * F)
-            lin(li, "gu", h, L["gu"], gu, coded=draft)
             a = _view(self.a, M, F)
-            b.silu_mul(gu, a)
+            if mode == VERIFY and variant == b.GEMM_SKINNY:
+                # one launch: the gate|up layer and its SwiGLU
+                Wq, Ws, N, _ = L["gu"]
+                b.gemm_w4a16_swiglu(h, Wq, Ws, A=a, ws=self.ws, N=N)
+                if trace is not None:
+                    trace.append((li, "gu_swiglu", h.clone(), a.clone()))
+            else:
+                lin(li, "gu", h, L["gu"], gu, coded=draft)
+                b.silu_mul_pairs(gu, a)
             dn = _view(self.dn, M, d)
             lin(li, "down", a, L["down"], dn)
             add = dn

@@ -94,6 +94,13 @@ def test_gemm_validation():
     assert need > 0
     assert g(A, A, A, 40, 4608, 3584, 128, 2, A, NUL, 0, S) == EWS
     assert g(A, A, A, 40, 4608, 3584, 128, 2, A, A, need - 1, S) == EWS
+    sw = L.qspec_gemm_w4a16_swiglu   # gate|up in pair order, SwiGLU in the epilogue
+    assert sw(A, A, A, 8, 72, 256, 128, A, NUL, 0, S) == ESHAPE     # N % 16 != 0
+    assert sw(A, A, A, 8, 64, 250, 128, A, NUL, 0, S) == ESHAPE
+    assert sw(A, A, A, 8, 64, 256, 64, A, NUL, 0, S) == EUNSUP
+    assert sw(A, A, A, 8, 64, 256, 128, NUL, NUL, 0, S) == ENULL
+    assert sw(A, A, A, 8, 64, 256, 128, MIS, NUL, 0, S) == EALIGN
+    assert sw(A, A, A, 40, 4608, 3584, 128, A, NUL, 0, S) == EWS   # a k-split needs scratch
     u = L.qspec_gemm_w4a8        # the W4A8 tier: SKINNY and STREAM families; P after Y
     assert u(A, A, A, A, 17, 64, 256, 128, 4, A, NUL, NUL, 0, S) == EUNSUP   # STREAM: M <= 16
     for v in (1, 3, 9):
@@ -180,6 +187,9 @@ def test_harness_validation():
     assert L.qspec_add_rmsnorm_quant(A, 256, NUL, 0, 2, 256, D(1e-6), A, A, MIS, S) == EALIGN
     # silu, argmax
     assert L.qspec_silu_mul(A, 0, 10, A, S) == ESHAPE
+    assert L.qspec_silu_mul_pairs(A, 4, 12, A, S) == ESHAPE       # ffn % 8 != 0
+    assert L.qspec_silu_mul_pairs(A, 0, 16, A, S) == ESHAPE
+    assert L.qspec_silu_mul_pairs(NUL, 4, 16, A, S) == ENULL
     assert L.qspec_argmax(A, 2, 10, A, 0, S) == ESHAPE
     # round bookkeeping
     assert L.qspec_spec_prepare(2, 4, 2, 0, A, A, A, A, A, A, S) == EUNSUP

@@ -10,7 +10,7 @@ import oracle.model as om
 import synth
 import quantization_self_speculation_amd as q
 from quantization_self_speculation_amd import binding as qb
-from quantization_self_speculation_amd.e2e import Decoder
+from quantization_self_speculation_amd.e2e import Decoder, _unpair_cols
 from gpu_util import dev, dev_bf16, host, host_bits16, say
 
 pytestmark = pytest.mark.gpu
@@ -232,6 +232,37 @@ def test_silu_mul_and_argmax():
     assert got[2] == 10 and got[4] == 0 and got[6] == V - 1 and got[8] == 0 and got[10] == 777
 
 
+@pytest.mark.parametrize("M,F,K", [(1, 8, 128), (5, 504, 256), (16, 5632, 2048), (40, 1000, 384),
+                                   (80, 5632, 2048), (100, 4104, 256), (16, 96, 5632),
+                                   (40, 96, 2048)])
+def test_gate_up_swiglu_fused(M, F, K):
+    """qspec_gemm_w4a16_swiglu on gate|up rows in pair order: bitwise the
+    pair-order silu_mul of the SKINNY W4A16 layer on the same buffer (with
+    and without a k-split: 2F = 16 .. 11264), and that layer's columns, back
+    in gate-then-up order, within the fp tolerance of the oracle layer on
+    the unpaired weights; silu_mul_pairs bitwise silu_mul on the unpaired
+    columns."""
+    rng = synth.make_rng(56, M * 7 + F)
+    say(f"gate|up swiglu M={M} F={F} K={K}")
+    W = synth.weights(rng, 2 * F, K)
+    X = synth.activations(rng, M, K, n_outliers=synth.outlier_count(K))
+    Wq, Ws = q.pack_w4(dev(q.pair_rows(W)))
+    Xd = dev_bf16(X)
+    A = q.gemm_w4a16_swiglu(Xd, Wq, Ws, N=2 * F)
+    Yp = q.gemm_w4a16(Xd, Wq, Ws, variant=q.GEMM_SKINNY, N=2 * F)
+    A2 = torch.empty_like(A)
+    q.silu_mul_pairs(Yp, A2)
+    assert np.array_equal(host_bits16(A), host_bits16(A2))
+    Yn = _unpair_cols(Yp)
+    A3 = torch.empty_like(A)
+    qb.silu_mul(Yn.contiguous(), A3)
+    assert np.array_equal(host_bits16(A3), host_bits16(A2))
+    Wq_o, Ws_o = oracle.pack_w4(W)
+    want = oracle.gemm_w4a16(X, Wq_o, Ws_o)
+    got = host(Yn).astype(np.float64)
+    assert np.abs(got - want).max() <= 2e-3 * np.abs(want).max()
+
+
 @pytest.mark.parametrize("M,d", [(9, 256), (37, 2048), (3, 4096)])
 def test_quantizer_fused_into_rmsnorm(M, d):
     """add_rmsnorm_quant: the bf16 output and the residual are bitwise those
@@ -367,6 +398,20 @@ def _forwards_against_oracle(cfg, w, prompts, gamma=2):
         assert len(trace) == 4 * cfg.n_layers + 1
         for li, name, X, Y in trace:
             xb = X.cpu().view(torch.int16).numpy().view(np.uint16)
+            if name == "gu_swiglu":
+                # the fused gate|up layer: bitwise the pair-order silu_mul of
+                # the SKINNY layer on the same buffer, and that layer (its
+                # columns back in gate-then-up order) against the oracle
+                Wq, Ws, N, _ = dec.layers[li]["gu"]
+                Yp = q.gemm_w4a16(X, Wq, Ws, variant=q.GEMM_SKINNY, N=N)
+                A2 = torch.empty_like(Y)
+                q.silu_mul_pairs(Yp, A2)
+                assert np.array_equal(host_bits16(A2), host_bits16(Y)), (li, "gu_swiglu")
+                ref = om.linear(mode, xb, packed[(li, "gu")])
+                yg = host(_unpair_cols(Yp)).astype(np.float64)
+                e = np.abs(yg - ref).max() / np.abs(ref).max()
+                assert e <= 2e-3, (mode, li, name, e)
+                continue
             ref = om.linear(mode, xb, packed[(li, name)])
             yg = Y.cpu().numpy().astype(np.float64)
             e = np.abs(yg - ref).max() / np.abs(ref).max()
