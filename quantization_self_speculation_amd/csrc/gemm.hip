@@ -222,23 +222,30 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
   if (SW && a.S == 1) {
     // W4A16 gate|up with the SwiGLU output (a.A): lanes lg = 0, 1 hold gate
     // columns 0 .. 7 of each 16-row block, lanes lg = 2, 3 (32 lanes on)
-    // the matching up columns
+    // the matching up columns; after the exchange both lanes of a pair hold
+    // its four gate / up values, and each finishes two of them
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        float u[4];
+        float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = __shfl_xor(tot[nb][mb][r], 32, 64);
+        for (int r = 0; r < 4; ++r) o[r] = __shfl_xor(tot[nb][mb][r], 32, 64);
         const int m = m0 + mb * 16 + l16;
         const int n16 = n_w + nb * 16;  // the block's first row
-        if (lg < 2 && m < M && n16 < N) {
-          const int j = n16 / 2 + lg * 4;
-          uint16_t h[4];
+        if (m < M && n16 < N) {
+          const bool gate_lane = lg < 2;
+          const int r0 = gate_lane ? 0 : 2;  // the two pairs this lane finishes
+          const int j = n16 / 2 + (lg & 1) * 4 + r0;
+          uint16_t h[2];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = swiglu_bf16(tot[nb][mb][r], u[r]);
-          *reinterpret_cast<uint2*>(a.A + (int64_t)m * (N / 2) + j) =
-              make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+          for (int k = 0; k < 2; ++k) {
+            const float g = gate_lane ? tot[nb][mb][r0 + k] : o[r0 + k];
+            const float u = gate_lane ? o[r0 + k] : tot[nb][mb][r0 + k];
+            h[k] = swiglu_bf16(g, u);
+          }
+          *reinterpret_cast<uint32_t*>(a.A + (int64_t)m * (N / 2) + j) =
+              (uint32_t)h[0] | ((uint32_t)h[1] << 16);
         }
       }
     return;
