@@ -118,6 +118,15 @@ qspec_status qspec_device_check(void);
  * zeroed again).  A verify workspace needs no initialisation. */
 size_t qspec_workspace_bytes(int op, int64_t a, int64_t b, int64_t c);
 
+/* The GEMM family (QSPEC_GEMM_GEMV, _SKINNY, _TILED or _STREAM) that a call
+ * of QSPEC_OP_GEMM_W4A4 / _W4A16 / _W4A8 with these M, N, K and `variant`
+ * runs: AUTO resolved, which depends on M, N and K only.  Within one family
+ * a row's result does not depend on M; the fused SwiGLU entries reproduce
+ * their family's layer bit for bit.  Returns -1 (qspec_last_error() says
+ * why) for sizes or a variant the GEMM call would reject; reads no device
+ * state. */
+int qspec_gemm_family(int op, int64_t M, int64_t N, int64_t K, int variant);
+
 /* ---------------------------------------------------------------------------
  * qspec_pack_w4 -- quantize fp32 weights to the shared INT4 buffer.
  * One buffer serves both modes (QSpec Abstract: weights reused across the
@@ -300,6 +309,28 @@ qspec_status qspec_gemm_w4a16_swiglu(const uint16_t* X, const uint8_t* Wq,
                                      int64_t K, int group, uint16_t* A,
                                      void* ws, size_t ws_bytes,
                                      qspec_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * qspec_gemm_w4a4_swiglu, qspec_gemm_w4a8_swiglu -- the drafters' gate|up
+ * layer (QSpec Abstract: W4A4 joint quantization drafts; the W4A8 tier
+ * above) with its SwiGLU in the epilogue of the STREAM family (M <= 16).  Rows in pair order as for qspec_gemm_w4a16_swiglu;
+ * with Y the STREAM-family result of qspec_gemm_w4a4 (qspec_gemm_w4a8) on the
+ * same operands,
+ *     A[m, 8b+i] = bf16(silu(Y[m,16b+i]) * Y[m,16b+8+i]),
+ * bitwise what qspec_silu_mul_pairs gives on that Y.
+ *   Xq, Xs as for qspec_gemm_w4a4 (qspec_gemm_w4a8); Wq, Ws tiled, pair
+ *   order, N % 16 == 0; A [M][N/2] bf16 bits (out, 16-byte aligned).  No
+ *   workspace.  M > 16 gives QSPEC_ERR_UNSUPPORTED; other validation as for
+ *   qspec_gemm_w4a4.
+ * ------------------------------------------------------------------------- */
+qspec_status qspec_gemm_w4a4_swiglu(const uint8_t* Xq, const float* Xs,
+                                    const uint8_t* Wq, const uint16_t* Ws,
+                                    int64_t M, int64_t N, int64_t K, int group,
+                                    uint16_t* A, qspec_stream stream);
+qspec_status qspec_gemm_w4a8_swiglu(const int8_t* Xq, const float* Xs,
+                                    const uint8_t* Wq, const uint16_t* Ws,
+                                    int64_t M, int64_t N, int64_t K, int group,
+                                    uint16_t* A, qspec_stream stream);
 
 /* ---------------------------------------------------------------------------
  * qspec_verify -- accept or reject gamma drafted tokens per sequence.

@@ -25,10 +25,16 @@ from .binding import (  # noqa: F401
     quant_act8,
     gemm_w4a16,
     gemm_w4a16_swiglu,
+    gemm_w4a4_swiglu,
+    gemm_w4a8_swiglu,
+    gemm_family,
     pair_rows,
     verify,
     verify_noalloc,
     workspace_bytes,
+    OP_GEMM_W4A4,
+    OP_GEMM_W4A16,
+    OP_GEMM_W4A8,
     GEMM_AUTO,
     GEMM_GEMV,
     GEMM_SKINNY,

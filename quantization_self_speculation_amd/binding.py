@@ -62,6 +62,9 @@ def lib():
             "qspec_gemm_w4a4_bf16": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_gemm_w4a16": (I, [P, P, P, I64, I64, I64, I, I, P, P, SZ, P]),
             "qspec_gemm_w4a16_swiglu": (I, [P, P, P, I64, I64, I64, I, P, P, SZ, P]),
+            "qspec_gemm_family": (I, [I, I64, I64, I64, I]),
+            "qspec_gemm_w4a4_swiglu": (I, [P, P, P, P, I64, I64, I64, I, P, P]),
+            "qspec_gemm_w4a8_swiglu": (I, [P, P, P, P, I64, I64, I64, I, P, P]),
             "qspec_quant_act8": (I, [P, I64, I64, P, P, P]),
             "qspec_gemm_w4a8": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
             "qspec_verify": (I, [I, I64, I, I64, P, P, P, P, P, P, P, P, SZ, P]),
@@ -316,6 +319,44 @@ def gemm_w4a16_swiglu(X, Wq, Ws, A=None, ws=None, N=None):
     w, wb = _workspace(workspace_bytes(OP_GEMM_W4A16, M, N, K), X.device, ws)
     _check(lib().qspec_gemm_w4a16_swiglu(_ptr(X), _ptr(Wq), _ptr(Ws), M, N, K, GROUP, _ptr(A),
                                          _ptr(w), wb, _stream()), "qspec_gemm_w4a16_swiglu")
+    return A
+
+
+def gemm_family(op, M, N, K, variant=GEMM_AUTO):
+    """The GEMM family (GEMM_GEMV / _SKINNY / _TILED / _STREAM) a call of
+    `op` (OP_GEMM_W4A4 / _W4A16 / _W4A8) with these sizes and `variant` runs."""
+    f = lib().qspec_gemm_family(op, M, N, K, variant)
+    if f < 0:
+        raise QSpecError(f, "qspec_gemm_family", lib().qspec_last_error().decode())
+    return f
+
+
+def gemm_w4a4_swiglu(Xq, Xs, Wq, Ws, A=None, N=None):
+    """Draft-mode gate|up layer with its SwiGLU fused (STREAM family, M <= 16)
+    -> A bf16 [M, N/2]; rows in pair order; bitwise silu_mul_pairs of
+    gemm_w4a4(STREAM)."""
+    return _int_swiglu("qspec_gemm_w4a4_swiglu", torch.uint8, Xq, Xs, Wq, Ws, A, N)
+
+
+def gemm_w4a8_swiglu(Xq, Xs, Wq, Ws, A=None, N=None):
+    """W4A8 gate|up layer with its SwiGLU fused, as gemm_w4a4_swiglu."""
+    return _int_swiglu("qspec_gemm_w4a8_swiglu", torch.int8, Xq, Xs, Wq, Ws, A, N)
+
+
+def _int_swiglu(fn, code_dtype, Xq, Xs, Wq, Ws, A, N):
+    _need(Xq, "Xq", code_dtype)
+    M = Xq.shape[0]
+    K = Xq.shape[1] * (2 if code_dtype == torch.uint8 else 1)
+    if N is None:
+        N = 2 * A.shape[1] if A is not None else Wq.shape[0]
+    _need(Xs, "Xs", torch.float32, (M,))
+    _need(Wq, "Wq", torch.uint8, (padded_rows(N), K // 2))
+    _need(Ws, "Ws", torch.float16, (padded_rows(N), K // GROUP))
+    if A is None:
+        A = torch.empty((M, N // 2), dtype=torch.bfloat16, device=Xq.device)
+    _need(A, "A", torch.bfloat16, (M, N // 2))
+    _check(getattr(lib(), fn)(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), M, N, K, GROUP, _ptr(A),
+                              _stream()), fn)
     return A
 
 

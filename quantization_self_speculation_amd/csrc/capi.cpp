@@ -188,6 +188,23 @@ size_t qspec_workspace_bytes(int op, int64_t a, int64_t b, int64_t c) {
   }
 }
 
+int qspec_gemm_family(int op, int64_t M, int64_t N, int64_t K, int variant) {
+  const bool w4a16 = op == QSPEC_OP_GEMM_W4A16;
+  if (!w4a16 && op != QSPEC_OP_GEMM_W4A4 && op != QSPEC_OP_GEMM_W4A8) {
+    set_error("op %d is not a GEMM op", op);
+    return -1;
+  }
+  if (check_gemm(M, N, K, QSPEC_GROUP, variant, w4a16) != QSPEC_OK) return -1;
+  if (op == QSPEC_OP_GEMM_W4A8) {
+    if (variant == QSPEC_GEMM_TILED) {
+      set_error("W4A8 runs the SKINNY or STREAM family (got variant %d)", variant);
+      return -1;
+    }
+    return w4a8_pick(variant, M, N, K);
+  }
+  return w4a16 ? w4a16_pick(variant, M, N, K) : w4a4_pick(variant, M, N, K);
+}
+
 qspec_status qspec_pack_w4(const float* W, int64_t N, int64_t K, int group, uint8_t* Wq,
                            uint16_t* Ws, qspec_stream stream) {
   QS_REQUIRE(group == QSPEC_GROUP, QSPEC_ERR_UNSUPPORTED, "group must be 128 (got %d)", group);
@@ -343,6 +360,38 @@ qspec_status qspec_gemm_w4a16_swiglu(const uint16_t* X, const uint8_t* Wq, const
   QS_TRY(device_check());
   return hip_result(launch_w4a16_swiglu(X, Wq, Ws, M, N, K, A, ws, ws_bytes, (hipStream_t)stream),
                     "gemm_w4a16_swiglu launch");
+}
+
+qspec_status qspec_gemm_w4a4_swiglu(const uint8_t* Xq, const float* Xs, const uint8_t* Wq,
+                                    const uint16_t* Ws, int64_t M, int64_t N, int64_t K, int group,
+                                    uint16_t* A, qspec_stream stream) {
+  QS_TRY(check_gemm(M, N, K, group, QSPEC_GEMM_STREAM, false));
+  QS_REQUIRE(N % 16 == 0, QSPEC_ERR_SHAPE,
+             "N (gate|up rows) must be a multiple of 16 (got %lld)", (long long)N);
+  QS_PTR(Xq);
+  QS_PTR(Xs);
+  QS_PTR(Wq);
+  QS_PTR(Ws);
+  QS_PTR(A);
+  QS_TRY(device_check());
+  return hip_result(launch_w4a4_swiglu(Xq, Xs, Wq, Ws, M, N, K, A, (hipStream_t)stream),
+                    "gemm_w4a4_swiglu launch");
+}
+
+qspec_status qspec_gemm_w4a8_swiglu(const int8_t* Xq, const float* Xs, const uint8_t* Wq,
+                                    const uint16_t* Ws, int64_t M, int64_t N, int64_t K, int group,
+                                    uint16_t* A, qspec_stream stream) {
+  QS_TRY(check_gemm(M, N, K, group, QSPEC_GEMM_STREAM, false));
+  QS_REQUIRE(N % 16 == 0, QSPEC_ERR_SHAPE,
+             "N (gate|up rows) must be a multiple of 16 (got %lld)", (long long)N);
+  QS_PTR(Xq);
+  QS_PTR(Xs);
+  QS_PTR(Wq);
+  QS_PTR(Ws);
+  QS_PTR(A);
+  QS_TRY(device_check());
+  return hip_result(launch_w4a8_swiglu(Xq, Xs, Wq, Ws, M, N, K, A, (hipStream_t)stream),
+                    "gemm_w4a8_swiglu launch");
 }
 
 qspec_status qspec_verify(int mode, int64_t B, int gamma, int64_t V, const int32_t* draft_tok,

@@ -1257,6 +1257,7 @@ struct StreamArgs {
   uint16_t* Yb;  // bf16 output instead of Y (W4A4 only), else null
   int32_t* P;    // W4A4 / W4A8 int32 group partials [M][N][K/128] (optional)
   int M, N, K, nrb;
+  uint16_t* A;   // integer modes, gate|up rows in pair order: bf16 SwiGLU [M][N/2] instead of Y
 };
 
 // Ring depth (groups) of the stream kernels: measured on MI355X, a shallow
@@ -1287,7 +1288,8 @@ struct StreamStage {
 };
 
 
-template <int MODE, bool WITHP, int PD = (MODE == kW4A16 ? QSPEC_ST_PD16 : QSPEC_ST_PD4)>
+template <int MODE, bool WITHP, int PD = (MODE == kW4A16 ? QSPEC_ST_PD16 : QSPEC_ST_PD4),
+          bool SW = false>
 __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   static_assert(!(WITHP && MODE == kW4A16), "the int32 partials output is an integer-mode path");
   extern __shared__ __attribute__((aligned(16))) float red_[];  // [nw][64][4] when nw > 1
@@ -1430,6 +1432,26 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
       tot[3] += t[3];
     }
   }
+  if constexpr (SW) {
+    // gate|up rows in pair order, the SwiGLU output (a.A): the same values
+    // as the stored Y, paired across the two halves of the wavefront (lanes
+    // lg = 0, 1 hold gate columns 0 .. 7 of the block, lanes lg = 2, 3 the
+    // matching up columns); each lane of a pair finishes two of its four
+    // (gate lanes take outputs 0, 1 of their four, up lanes 2, 3; each
+    // sends the two its partner takes)
+    const float xs = l16 < M ? a.Xs[l16] : 0.f;
+    const float v0 = xs * tot[0], v1 = xs * tot[1], v2 = xs * tot[2], v3 = xs * tot[3];
+    const bool gate_lane = lg < 2;
+    const float o0 = __shfl_xor(gate_lane ? v2 : v0, 32, 64);
+    const float o1 = __shfl_xor(gate_lane ? v3 : v1, 32, 64);
+    if (l16 >= M) return;
+    const int N = a.N;
+    const int j = rb * 8 + (lg & 1) * 4 + (gate_lane ? 0 : 2);
+    const uint16_t h0 = swiglu_bf16(gate_lane ? v0 : o0, gate_lane ? o0 : v2);
+    const uint16_t h1 = swiglu_bf16(gate_lane ? v1 : o1, gate_lane ? o1 : v3);
+    *reinterpret_cast<uint32_t*>(a.A + (int64_t)l16 * (N / 2) + j) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    return;
+  }
   if (l16 >= M) return;
   const int n = rb * 16 + lg * 4;
   const int N = a.N;
@@ -1450,11 +1472,18 @@ int stream_waves(int64_t N, int64_t K) {
 template <int MODE>
 hipError_t launch_stream(const void* X, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                          int64_t M, int64_t N, int64_t K, float* Y, uint16_t* Yb, int32_t* P,
-                         hipStream_t s) {
-  StreamArgs a{X, Xs, Wq, Ws, Y, Yb, P, (int)M, (int)N, (int)K, (int)cdiv(N, 16)};
+                         hipStream_t s, uint16_t* A = nullptr) {
+  StreamArgs a{X, Xs, Wq, Ws, Y, Yb, P, (int)M, (int)N, (int)K, (int)cdiv(N, 16), A};
   const int nw = stream_waves(N, K);
   const size_t lds = nw > 1 ? (size_t)nw * 64 * 4 * sizeof(float) : 0;
   if constexpr (MODE != kW4A16) {
+    if (A != nullptr) {  // the SwiGLU output (the gate|up layer of a drafter)
+      if (a.nrb >= QSPEC_ST_WIDE)
+        hipLaunchKernelGGL((stream_kernel<MODE, false, 3, true>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+      else
+        hipLaunchKernelGGL((stream_kernel<MODE, false, QSPEC_ST_PD4, true>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+      return hipGetLastError();
+    }
     if (P != nullptr) {
       hipLaunchKernelGGL((stream_kernel<MODE, true>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
       return hipGetLastError();
@@ -1773,12 +1802,6 @@ int auto_pick(int64_t M, int64_t N, int64_t K, int64_t skinny_max, int64_t bm,
   if (M <= 512 && K / kGroup >= 64 && tiles < 128) return QSPEC_GEMM_SKINNY;
   return QSPEC_GEMM_TILED;
 }
-int w4a16_pick(int variant, int64_t M, int64_t N, int64_t K) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 128, 32, 64);
-}
-int w4a4_pick(int variant, int64_t M, int64_t N, int64_t K) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 256, 64, 96);
-}
 
 hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* Xs, float* Y,
                   hipStream_t s) {
@@ -1791,6 +1814,17 @@ hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* X
 }
 
 }  // namespace
+
+int w4a16_pick(int variant, int64_t M, int64_t N, int64_t K) {
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 128, 32, 64);
+}
+int w4a4_pick(int variant, int64_t M, int64_t N, int64_t K) {
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 256, 64, 96);
+}
+// W4A8 runs the stream family where W4A4 would, the skinny family otherwise
+int w4a8_pick(int variant, int64_t M, int64_t N, int64_t K) {
+  return w4a4_pick(variant, M, N, K) == QSPEC_GEMM_STREAM ? QSPEC_GEMM_STREAM : QSPEC_GEMM_SKINNY;
+}
 
 size_t w4a16_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const SkinnyPlan p = plan_skinny(0, M, N, K, true);  // four-wavefront tiles: the most counters
@@ -1864,6 +1898,20 @@ hipError_t launch_w4a16_swiglu(const uint16_t* X, const uint8_t* Wq, const uint1
   return launch_skinny<kW4A16>(a, p, s);
 }
 
+// The drafters' gate|up layer with the SwiGLU in the STREAM epilogue (M <=
+// 16): A bitwise the pair-order silu_mul of that family's Y.
+hipError_t launch_w4a4_swiglu(const uint8_t* Xq, const float* Xs, const uint8_t* Wq,
+                              const uint16_t* Ws, int64_t M, int64_t N, int64_t K, uint16_t* A,
+                              hipStream_t s) {
+  return launch_stream<kW4A4>(Xq, Xs, Wq, Ws, M, N, K, nullptr, nullptr, nullptr, s, A);
+}
+
+hipError_t launch_w4a8_swiglu(const int8_t* Xq, const float* Xs, const uint8_t* Wq,
+                              const uint16_t* Ws, int64_t M, int64_t N, int64_t K, uint16_t* A,
+                              hipStream_t s) {
+  return launch_stream<kW4A8>(Xq, Xs, Wq, Ws, M, N, K, nullptr, nullptr, nullptr, s, A);
+}
+
 size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const SkinnyPlan p = plan_skinny(1, M, N, K, true);  // four-wavefront tiles: the most counters
   return p.cnt_bytes + p.part_bytes == 0 ? 0 : ws_need(p.cnt_bytes, p.part_bytes);
@@ -1900,8 +1948,7 @@ hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, co
 hipError_t launch_w4a8(const int8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, int32_t* P,
                        void* ws, size_t ws_bytes, hipStream_t s) {
-  const int v = variant == QSPEC_GEMM_AUTO ? auto_pick(M, N, K, 256, 64, 96) : variant;
-  if (v == QSPEC_GEMM_STREAM)
+  if (w4a8_pick(variant, M, N, K) == QSPEC_GEMM_STREAM)
     return launch_stream<kW4A8>(Xq, Xs, Wq, Ws, M, N, K, Y, nullptr, P, s);
   const SkinnyPlan p = plan_skinny(1, M, N, K);
   const WsSplit w = ws_split(ws, ws_bytes);

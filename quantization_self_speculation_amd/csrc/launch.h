@@ -33,6 +33,20 @@ hipError_t launch_w4a16_swiglu(const uint16_t* X, const uint8_t* Wq, const uint1
                                int64_t N, int64_t K, uint16_t* A, void* ws, size_t ws_bytes,
                                hipStream_t s);
 
+// the drafters' gate|up layer (STREAM family, M <= 16) with its SwiGLU in
+// the epilogue: rows in pair order, A bf16 [M][N/2]
+hipError_t launch_w4a4_swiglu(const uint8_t* Xq, const float* Xs, const uint8_t* Wq,
+                              const uint16_t* Ws, int64_t M, int64_t N, int64_t K, uint16_t* A,
+                              hipStream_t s);
+hipError_t launch_w4a8_swiglu(const int8_t* Xq, const float* Xs, const uint8_t* Wq,
+                              const uint16_t* Ws, int64_t M, int64_t N, int64_t K, uint16_t* A,
+                              hipStream_t s);
+
+// the family a GEMM call runs (AUTO resolved; M, N, K only)
+int w4a16_pick(int variant, int64_t M, int64_t N, int64_t K);
+int w4a4_pick(int variant, int64_t M, int64_t N, int64_t K);
+int w4a8_pick(int variant, int64_t M, int64_t N, int64_t K);
+
 size_t w4a4_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a4(const uint8_t* Xq, const float* Xs, const uint8_t* Wq, const uint16_t* Ws,
                        int64_t M, int64_t N, int64_t K, int variant, float* Y, uint16_t* Yb,

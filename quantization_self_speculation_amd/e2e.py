@@ -165,6 +165,17 @@ class Decoder:
         else:
             b.gemm_w4a16(X, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
 
+    def _gu_family(self, mode, M, variant):
+        """The family of the fused gate|up + SwiGLU launch for this forward,
+        or None where the layer runs unfused: the verifier's SKINNY family
+        (a row's bits the same at every M) and the drafters' STREAM family."""
+        N, K = 2 * self.cfg.ffn, self.cfg.d
+        if mode == VERIFY:
+            return b.GEMM_SKINNY if variant == b.GEMM_SKINNY else None
+        op = b.OP_GEMM_W4A4 if mode == DRAFT else b.OP_GEMM_W4A8
+        fam = b.gemm_family(op, M, N, K, variant)
+        return fam if fam == b.GEMM_STREAM else None
+
     def forward(self, mode, M, variant, last_of=None, trace=None):
         """rows 0..M-1 described by self.seq/pos/tok; logits of every row (or,
         with last_of=P, of rows P-1, 2P-1, ...) land in self.logits.  With a
@@ -218,10 +229,18 @@ class Decoder:
             norm(x, o, h)
             gu = _view(self.gu, M, 2 * F)
             a = _view(self.a, M, F)
-            if mode == VERIFY and variant == b.GEMM_SKINNY:
+            fam = self._gu_family(mode, M, variant)
+            if fam is not None:
                 # one launch: the gate|up layer and its SwiGLU
-                Wq, Ws, N, _ = L["gu"]
-                b.gemm_w4a16_swiglu(h, Wq, Ws, A=a, ws=self.ws, N=N)
+                Wq, Ws, N, K = L["gu"]
+                if mode == VERIFY:
+                    b.gemm_w4a16_swiglu(h, Wq, Ws, A=a, ws=self.ws, N=N)
+                elif mode == DRAFT:
+                    b.gemm_w4a4_swiglu(*self._codes(M, K), Wq, Ws, A=a, N=N)
+                else:
+                    Xq8, Xs = _view(self.Xq8, M, K), _view(self.Xs, M)
+                    b.quant_act8(h, Xq8, Xs)
+                    b.gemm_w4a8_swiglu(Xq8, Xs, Wq, Ws, A=a, N=N)
                 if trace is not None:
                     trace.append((li, "gu_swiglu", h.clone(), a.clone()))
             else:

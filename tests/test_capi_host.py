@@ -101,6 +101,29 @@ def test_gemm_validation():
     assert sw(A, A, A, 8, 64, 256, 128, NUL, NUL, 0, S) == ENULL
     assert sw(A, A, A, 8, 64, 256, 128, MIS, NUL, 0, S) == EALIGN
     assert sw(A, A, A, 40, 4608, 3584, 128, A, NUL, 0, S) == EWS   # a k-split needs scratch
+    for fn in (L.qspec_gemm_w4a4_swiglu, L.qspec_gemm_w4a8_swiglu):  # drafters, STREAM only
+        assert fn(A, A, A, A, 8, 72, 256, 128, A, S) == ESHAPE      # N % 16 != 0
+        assert fn(A, A, A, A, 8, 64, 250, 128, A, S) == ESHAPE
+        assert fn(A, A, A, A, 8, 64, 256, 64, A, S) == EUNSUP
+        assert fn(A, A, A, A, 17, 64, 256, 128, A, S) == EUNSUP     # M <= 16
+        assert fn(A, A, A, A, 8, 64, 256, 128, NUL, S) == ENULL
+        assert fn(A, NUL, A, A, 8, 64, 256, 128, A, S) == ENULL
+        assert fn(A, A, A, A, 8, 64, 256, 128, MIS, S) == EALIGN
+    fam = L.qspec_gemm_family    # the family a call runs, AUTO resolved, no device work
+    W4A4, W4A16, W4A8 = b.OP_GEMM_W4A4, b.OP_GEMM_W4A16, b.OP_GEMM_W4A8
+    assert fam(W4A4, 16, 11264, 2048, 0) == b.GEMM_STREAM
+    assert fam(W4A8, 16, 11264, 2048, 0) == b.GEMM_STREAM
+    assert fam(W4A16, 5, 11264, 2048, 0) == b.GEMM_STREAM
+    assert fam(W4A4, 8, 37888, 3584, 0) == b.GEMM_SKINNY
+    assert fam(W4A4, 17, 11264, 2048, 0) == b.GEMM_SKINNY
+    assert fam(W4A4, 256, 37888, 3584, 0) == b.GEMM_TILED
+    assert fam(W4A8, 256, 37888, 3584, 0) == b.GEMM_SKINNY    # W4A8 has no TILED family
+    assert fam(W4A16, 40, 37888, 3584, 1) == b.GEMM_GEMV
+    assert fam(W4A4, 8, 64, 256, 3) == b.GEMM_TILED             # an explicit variant stands
+    for args in ((W4A4, 8, 64, 256, 1), (W4A8, 8, 64, 256, 3), (W4A16, 17, 64, 256, 4),
+                 (W4A16, 8, 64, 250, 0), (b.OP_VERIFY, 8, 64, 256, 0), (W4A4, 0, 64, 256, 0)):
+        assert fam(*args) == -1, args
+        assert L.qspec_last_error()
     u = L.qspec_gemm_w4a8        # the W4A8 tier: SKINNY and STREAM families; P after Y
     assert u(A, A, A, A, 17, 64, 256, 128, 4, A, NUL, NUL, 0, S) == EUNSUP   # STREAM: M <= 16
     for v in (1, 3, 9):

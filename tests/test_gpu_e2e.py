@@ -11,7 +11,7 @@ import synth
 import quantization_self_speculation_amd as q
 from quantization_self_speculation_amd import binding as qb
 from quantization_self_speculation_amd.e2e import Decoder, _unpair_cols
-from gpu_util import dev, dev_bf16, host, host_bits16, say
+from gpu_util import assert_close, dev, dev_bf16, host, host_bits16, say
 
 pytestmark = pytest.mark.gpu
 
@@ -263,6 +263,40 @@ def test_gate_up_swiglu_fused(M, F, K):
     assert np.abs(got - want).max() <= 2e-3 * np.abs(want).max()
 
 
+@pytest.mark.parametrize("mode", ["w4a4", "w4a8"])
+@pytest.mark.parametrize("M,F,K", [(1, 8, 128), (5, 504, 256), (8, 5632, 2048), (16, 5632, 2048),
+                                   (3, 18944, 3584), (16, 96, 5632), (11, 4104, 384)])
+def test_drafter_gate_up_swiglu_fused(mode, M, F, K):
+    """qspec_gemm_w4a4_swiglu / _w4a8_swiglu on gate|up rows in pair order:
+    bitwise the pair-order silu_mul of the STREAM layer of the same mode on
+    the same codes and buffer (row blocks below and above the width where
+    the ring deepens: 2F = 16 .. 37888), and that layer's columns, back in
+    gate-then-up order, within the fp tolerance of the oracle layer on the
+    unpaired weights."""
+    rng = synth.make_rng(57, M * 7 + F)
+    say(f"drafter gate|up swiglu {mode} M={M} F={F} K={K}")
+    W = synth.weights(rng, 2 * F, K)
+    X = synth.activations(rng, M, K, n_outliers=synth.outlier_count(K))
+    Wq, Ws = q.pack_w4(dev(q.pair_rows(W)))
+    Wq_o, Ws_o = oracle.pack_w4(W)
+    if mode == "w4a4":
+        xq, xs = oracle.quant_act(X)
+        Xq, Xs = dev(xq), dev(xs)
+        A = q.gemm_w4a4_swiglu(Xq, Xs, Wq, Ws, N=2 * F)
+        Yp = q.gemm_w4a4(Xq, Xs, Wq, Ws, variant=q.GEMM_STREAM, N=2 * F)
+        want = oracle.gemm_w4a4(xq, xs, Wq_o, Ws_o)
+    else:
+        xq, xs = oracle.quant_act8(X)
+        Xq, Xs = dev(xq), dev(xs)
+        A = q.gemm_w4a8_swiglu(Xq, Xs, Wq, Ws, N=2 * F)
+        Yp = q.gemm_w4a8(Xq, Xs, Wq, Ws, variant=q.GEMM_STREAM, N=2 * F)
+        want = oracle.gemm_w4a8(xq, xs, Wq_o, Ws_o)
+    A2 = torch.empty_like(A)
+    q.silu_mul_pairs(Yp, A2)
+    assert np.array_equal(host_bits16(A), host_bits16(A2))
+    assert_close(host(_unpair_cols(Yp)), want, what=f"{mode} gate|up")
+
+
 @pytest.mark.parametrize("M,d", [(9, 256), (37, 2048), (3, 4096)])
 def test_quantizer_fused_into_rmsnorm(M, d):
     """add_rmsnorm_quant: the bf16 output and the residual are bitwise those
@@ -389,24 +423,36 @@ def _forwards_against_oracle(cfg, w, prompts, gamma=2):
     packed = {(li, k): model.layers[li][k] for li in range(cfg.n_layers)
               for k in ("qkv", "o", "gu", "down")}
     packed.update({(cfg.n_layers, "lm"): model.lm})
-    for mode in (om.VERIFY, om.DRAFT, om.DRAFT8):
+    runs = [(om.VERIFY, q.GEMM_SKINNY), (om.DRAFT, q.GEMM_SKINNY), (om.DRAFT8, q.GEMM_SKINNY)]
+    if B <= 16:
+        # the drafters' STREAM family, whose gate|up layer runs fused
+        runs += [(om.DRAFT, q.GEMM_STREAM), (om.DRAFT8, q.GEMM_STREAM)]
+    for mode, variant in runs:
         dec.seq[:B].copy_(torch.arange(B, dtype=torch.int32))
         dec.pos[:B].fill_(P)
         dec.tok[:B].copy_(torch.from_numpy(toks))
         trace = []
-        got = host(dec.forward(mode, B, q.GEMM_SKINNY, trace=trace)).astype(np.float64)
+        got = host(dec.forward(mode, B, variant, trace=trace)).astype(np.float64)
         assert len(trace) == 4 * cfg.n_layers + 1
+        fused = [name for _, name, _, _ in trace if name == "gu_swiglu"]
+        assert len(fused) == (cfg.n_layers if mode == om.VERIFY or variant == q.GEMM_STREAM else 0)
         for li, name, X, Y in trace:
             xb = X.cpu().view(torch.int16).numpy().view(np.uint16)
             if name == "gu_swiglu":
                 # the fused gate|up layer: bitwise the pair-order silu_mul of
-                # the SKINNY layer on the same buffer, and that layer (its
-                # columns back in gate-then-up order) against the oracle
+                # the same family's layer on the same buffer (codes of the
+                # bf16 input for the drafters), and that layer (its columns
+                # back in gate-then-up order) against the oracle
                 Wq, Ws, N, _ = dec.layers[li]["gu"]
-                Yp = q.gemm_w4a16(X, Wq, Ws, variant=q.GEMM_SKINNY, N=N)
+                if mode == om.VERIFY:
+                    Yp = q.gemm_w4a16(X, Wq, Ws, variant=variant, N=N)
+                elif mode == om.DRAFT:
+                    Yp = q.gemm_w4a4(*q.quant_act(X), Wq, Ws, variant=variant, N=N)
+                else:
+                    Yp = q.gemm_w4a8(*q.quant_act8(X), Wq, Ws, variant=variant, N=N)
                 A2 = torch.empty_like(Y)
                 q.silu_mul_pairs(Yp, A2)
-                assert np.array_equal(host_bits16(A2), host_bits16(Y)), (li, "gu_swiglu")
+                assert np.array_equal(host_bits16(A2), host_bits16(Y)), (mode, li, "gu_swiglu")
                 ref = om.linear(mode, xb, packed[(li, "gu")])
                 yg = host(_unpair_cols(Yp)).astype(np.float64)
                 e = np.abs(yg - ref).max() / np.abs(ref).max()
