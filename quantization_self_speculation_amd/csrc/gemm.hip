@@ -74,6 +74,12 @@
 #ifndef QSPEC_SK_SPLIT_WG
 #define QSPEC_SK_SPLIT_WG 128  // k-split until about this many workgroups (a function of N, K)
 #endif
+#ifndef QSPEC_SK_VBIAS_N
+#define QSPEC_SK_VBIAS_N 16384  // W4A16 from this many rows: the bias term from staged group sums
+#endif
+#ifndef QSPEC_SK_MIN_GPS
+#define QSPEC_SK_MIN_GPS 4     // the k-split leaves at least this many groups per slice
+#endif
 #ifndef QSPEC_SK_TARGET_WG
 #define QSPEC_SK_TARGET_WG 256  // M <= 16 below this many 64-row tiles: the stream family
 #endif
@@ -374,11 +380,13 @@ __device__ __forceinline__ void finish_tile(const SkinnyArgs& a, const v4f (&tot
 // a clamped, valid address) so the compiler keeps exact load counters and the
 // weight ring stays in flight across waits; only the arithmetic of groups past
 // the end of the slice is skipped (a branch uniform over the workgroup).
-template <int MODE, int MB, int NB, int CH, int PD, bool XOUT, int NWV = 4>
+template <int MODE, int MB, int NB, int CH, int PD, bool XOUT, int NWV = 4, bool VB = false>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny_wpe(MODE, MB)))) void skinny_kernel(const SkinnyArgs a) {
   static_assert(PD % CH == 0, "prefetch depth must be a multiple of the chunk");
   // XOUT: the extra output -- the int32 group partials (a.P) in the integer
-  // modes, the SwiGLU of gate|up rows in pair order (a.A) in W4A16
+  // modes, the SwiGLU of gate|up rows in pair order (a.A) in W4A16.
+  // VB (W4A16): the bias term from group sums staged with the activations
+  // instead of a second MFMA chain
   constexpr int NT = 64 * NWV;             // threads of a workgroup
   constexpr int ROWS = 16 * MB;            // activation rows of an m-chunk
   constexpr int WROWS = 16 * NB * NWV;     // weight rows of a tile (NWV wavefronts x NB blocks of 16)
@@ -388,6 +396,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
   constexpr int SPT = (CH * WROWS + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][ROWS * XSTB];
   __shared__ uint16_t wsl[2][CH * WROWS];
+  static_assert(!VB || MODE == kW4A16, "the staged bias sums are a W4A16 path");
+  // W4A16 with VB: each staged row's activation sum per group (the bias term)
+  __shared__ float xsum[2][VB ? ROWS * CH : 1];
   __shared__ int s_last;
 
   const int b = blockIdx.x;
@@ -458,6 +469,31 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
     }
   };
   auto x_store = [&](int buf) {
+    if constexpr (VB) {
+      // each staged row's group sums: a group's 16 chunks of a row sit in
+      // the 16 lanes of one DPP row (chunk = lane % 16); eight values per
+      // lane by a fixed dot2 chain, then the row's fixed tree -- the same
+      // for every M.  All lanes take part (rows past M hold zeros, chunks
+      // past the tile repeat the last one and are not stored).
+      const v2bf one2 = __builtin_bit_cast(v2bf, 0x3F803F80u);
+      float sx[XPT];
+#pragma unroll
+      for (int i = 0; i < XPT; ++i) {
+        float s8 = 0.f;
+        const uint32_t v[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s8 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, v[e]), one2, s8, false);
+        sx[i] = s8;
+      }
+#pragma unroll
+      for (int i = 0; i < XPT; ++i) sx[i] = row16_sum_dpp(sx[i]);
+#pragma unroll
+      for (int i = 0; i < XPT; ++i) {
+        const int idx = threadIdx.x + NT * i;
+        if (l16 == 0 && idx < XCH) xsum[buf][(idx / (CH * 16)) * CH + (idx % (CH * 16)) / 16] = sx[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = threadIdx.x + NT * i;
@@ -528,8 +564,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
       if (gi >= ng) {
         // past the end of the slice: nothing to add
       } else if (MODE == kW4A16) {
-        // acc = sum x (136 + q) per row and the bias term -136 sum x per m
-        // (one more MFMA chain with a constant A operand), both in fp32
+        // acc = sum x (136 + q) per row; the bias term -136 sum x per m comes
+        // from one more MFMA chain with a constant A operand, or with VB
+        // from the group sums staged with the activations (one FMA)
         v4f acc[NB][MB], corr[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -558,12 +595,25 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
           }
           // with one weight block the bias chain runs into the same
           // accumulator; with several it is shared and added per group
+          if constexpr (!VB) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              if (NB == 1)
+                acc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cneg, bv[mb], acc[0][mb], 0, 0, 0);
+              else
+                corr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cneg, bv[mb], corr[mb], 0, 0, 0);
+            }
+          }
+        }
+        if constexpr (VB) {
+          (void)cneg;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            if (NB == 1)
-              acc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cneg, bv[mb], acc[0][mb], 0, 0, 0);
-            else
-              corr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cneg, bv[mb], corr[mb], 0, 0, 0);
+            const float sx = xsum[buf][(mb * 16 + l16) * CH + gl];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[nb][mb][r] = fmaf(-kW4Bias, sx, acc[nb][mb][r]);
           }
         }
 #pragma unroll
@@ -574,7 +624,7 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               tot[nb][mb][r] = fmaf(half_bits_to_float(wp[r]),
-                                    NB == 1 ? acc[nb][mb][r] : acc[nb][mb][r] + corr[mb][r],
+                                    (NB == 1 || VB) ? acc[nb][mb][r] : acc[nb][mb][r] + corr[mb][r],
                                     tot[nb][mb][r]);
         }
       } else {
@@ -1632,6 +1682,7 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
 // same for every M within one family.
 struct SkinnyPlan {
   int S, gps, MB, NB, NWV, mchunks, ntiles, T;
+  bool VB;  // W4A16: the bias term from staged group sums (a function of N)
   int64_t blocks;
   size_t cnt_bytes, part_bytes;
 };
@@ -1669,7 +1720,7 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool max_tiles
   int64_t S = 1;
   if (t64 < QSPEC_SK_SPLIT_WG) {
     S = cdiv(QSPEC_SK_SPLIT_WG, t64);
-    const int64_t smax = std::max<int64_t>(1, G / 4);  // at least 4 groups per slice
+    const int64_t smax = std::max<int64_t>(1, G / QSPEC_SK_MIN_GPS);  // groups per slice
     if (S > smax) S = smax;
   }
   p.gps = (int)cdiv(G, S);
@@ -1691,47 +1742,54 @@ SkinnyPlan plan_skinny(int mode, int64_t M, int64_t N, int64_t K, bool max_tiles
   p.mchunks = (int)cdiv(M, 16 * p.MB);
   p.T = p.ntiles * p.mchunks;
   p.blocks = 8 * cdiv(p.T, 8) * p.S;
+  // W4A16 on wide layers: the bias term from group sums staged with the
+  // activations instead of a second MFMA chain per 16-row block (measured:
+  // gate|up N = 37888 at M = 5 / 16 / 40 17.1 / 18.1 / 32.3 -> 15.2 / 16.6 /
+  // 30.6 us, the 128256-row lm_head at M = 1 47.7 -> 47.2 us; on the narrow
+  // layers it is level or slower, e.g. N = 11264, K = 2048 at M = 80 17.2 ->
+  // 19.7 us).  A function of N alone, so a row's bits do not depend on M.
+  p.VB = mode == 0 && N >= QSPEC_SK_VBIAS_N;
   p.cnt_bytes = p.S > 1 ? round_up((size_t)p.T * 8, 256) : 0;
   p.part_bytes = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
   return p;
 }
 
-template <int MODE, bool XOUT>
+template <int MODE, bool XOUT, bool VB>
 hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
   const dim3 grid((unsigned)p.blocks), blk(64 * p.NWV);
   // W4A16 with three activation blocks, or any mode with one: the workgroup
   // size balanced over the CUs (5, 8 or 10 wavefronts; 4 is the generic case)
   if (MODE == kW4A16 && p.MB == 3 && p.NWV != 4) {
     switch (p.NWV) {
-      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 5>), grid, blk, 0, s, a); break;
-      case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 8>), grid, blk, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 10>), grid, blk, 0, s, a); break;
+      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 5, VB>), grid, blk, 0, s, a); break;
+      case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 8, VB>), grid, blk, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 10, VB>), grid, blk, 0, s, a); break;
     }
     return hipGetLastError();
   }
   if (p.MB == 1 && p.NWV != 4) {
     if constexpr (MODE == kW4A16) {
       switch (p.NWV) {
-        case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 5>), grid, blk, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 8>), grid, blk, 0, s, a); break;
-        default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 10>), grid, blk, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 5, VB>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 8, VB>), grid, blk, 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 10, VB>), grid, blk, 0, s, a); break;
       }
     } else {  // W4A4 and W4A8 share the int8 data flow and its parameters
       switch (p.NWV) {
-        case 5: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT, 5>), grid, blk, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT, 8>), grid, blk, 0, s, a); break;
-        default: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT, 10>), grid, blk, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT, 5, VB>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT, 8, VB>), grid, blk, 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_kernel<MODE, 1, 1, QSPEC_SK_A1, XOUT, 10, VB>), grid, blk, 0, s, a); break;
       }
     }
     return hipGetLastError();
   }
   if constexpr (MODE == kW4A16) {
     switch (p.MB) {
-      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT>), grid, blk, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_NB16, QSPEC_SK_B2, XOUT>), grid, blk, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT>), grid, blk, 0, s, a); break;
-      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 5, QSPEC_SK_NB16, QSPEC_SK_B4, XOUT>), grid, blk, 0, s, a); break;
-      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_NB16, QSPEC_SK_B4, XOUT>), grid, blk, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((skinny_kernel<kW4A16, 1, 1, QSPEC_SK_B1, XOUT, 4, VB>), grid, blk, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((skinny_kernel<kW4A16, 2, QSPEC_SK_NB16, QSPEC_SK_B2, XOUT, 4, VB>), grid, blk, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((skinny_kernel<kW4A16, 3, QSPEC_SK_NB16, QSPEC_SK_B3, XOUT, 4, VB>), grid, blk, 0, s, a); break;
+      case 5: hipLaunchKernelGGL((skinny_kernel<kW4A16, 5, QSPEC_SK_NB16, QSPEC_SK_B4, XOUT, 4, VB>), grid, blk, 0, s, a); break;
+      default: hipLaunchKernelGGL((skinny_kernel<kW4A16, 4, QSPEC_SK_NB16, QSPEC_SK_B4, XOUT, 4, VB>), grid, blk, 0, s, a); break;
     }
   } else {
     switch (p.MB) {
@@ -1747,8 +1805,14 @@ hipError_t launch_skinny_t(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t
 template <int MODE>
 hipError_t launch_skinny(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s) {
   // the extra output: partials in the integer modes, the SwiGLU in W4A16
-  if (MODE != kW4A16 ? a.P != nullptr : a.A != nullptr) return launch_skinny_t<MODE, true>(a, p, s);
-  return launch_skinny_t<MODE, false>(a, p, s);
+  if constexpr (MODE == kW4A16) {
+    if (p.VB) {
+      if (a.A != nullptr) return launch_skinny_t<MODE, true, true>(a, p, s);
+      return launch_skinny_t<MODE, false, true>(a, p, s);
+    }
+  }
+  if (MODE != kW4A16 ? a.P != nullptr : a.A != nullptr) return launch_skinny_t<MODE, true, false>(a, p, s);
+  return launch_skinny_t<MODE, false, false>(a, p, s);
 }
 
 // A GEMM workspace of ws_bytes holds the k-split arrival counters in its
