@@ -402,8 +402,10 @@ def measure_w4a8_tier(torch, q, wl, reps=10):
 def measure_decode_gemv(torch, q, wl, reps=10):
     """W4A16 at the decode-verify shapes of batch 1 (M = 1 * (4+1) = 5) on
     gate|up and down, and the Llama-3-8B lm_head (4096 -> 128256) at M = 1.
-    Each replay rotates through distinct weight copies (> 512 MB in total for
-    the 7B shapes; the lm_head's two copies are 541 MB), so reads come from HBM."""
+    Each replay rotates through distinct weight copies, more than 512 MB for
+    every shape (the lm_head's two copies are 541 MB), so no launch finds its
+    weights in the 256 MB Infinity Cache, and a replay holds enough launches
+    (16 or more) that its own start-up cost is not charged to them."""
     import synth
     rng = synth.make_rng(1, 3)
     out = {}
@@ -414,7 +416,9 @@ def measure_decode_gemv(torch, q, wl, reps=10):
         X = p["X16"][:5].contiguous()
         Y = torch.empty((5, N), dtype=torch.float32, device="cuda:0")
         ws = torch.zeros(max(1, q.workspace_bytes(2, 5, N, K)), dtype=torch.uint8, device="cuda:0")
-        cps = p["copies"]
+        cps = list(p["copies"])
+        while len(cps) < 16 or len(cps) * wbytes(N, K) <= (512 << 20):
+            cps.append((cps[0][0].clone(), cps[0][1].clone()))
 
         def fn():
             for Wq, Ws in cps:
@@ -422,7 +426,9 @@ def measure_decode_gemv(torch, q, wl, reps=10):
         us = _graph_time(torch, fn, reps, launches=1) / len(cps)
         b = wbytes(N, K) + 5 * K * 2 + 5 * N * 4
         out[f"{p['name']}_M5"] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
-                                  "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)}
+                                  "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBPS, 4),
+                                  "weight_copies": len(cps)}
+        del cps
     N, K = 128256, 4096
     cps = []
     for _ in range(2):
@@ -436,7 +442,7 @@ def measure_decode_gemv(torch, q, wl, reps=10):
     def fh():
         for Wq, Ws in cps:
             q.gemm_w4a16(X, Wq, Ws, Y=Y, ws=ws)
-    us = _graph_time(torch, fh, reps, launches=1) / len(cps)
+    us = _graph_time(torch, fh, reps, launches=8) / len(cps)
     b = wbytes(N, K) + K * 2 + N * 4
     out["lm_head_M1"] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1),
                          "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)}

@@ -1290,8 +1290,11 @@ hipError_t launch_tiled(const void* X, const float* Xs, const uint8_t* Wq, const
 //     per workgroup, at least 2 groups per wavefront;
 //   * weights stream HBM -> registers through a PD-deep ring (one flat 1 KiB
 //     tile per wavefront per group); the activation rows and the group scales
-//     come from L2 through a 2-deep ring (every wavefront reads the same few
+//     come from L2 in the same ring stages (every wavefront reads the same few
 //     KiB of activations; buffer loads, so lanes of rows >= M fetch nothing);
+//     W4A16 with at most 8 (4) rows takes two (one) 16-byte activation loads
+//     per lane and group instead of four, and DPP row shifts move each MFMA's
+//     fragment into place (stream_xfrag);
 //   * the per-group arithmetic is the skinny family's: W4A16 runs
 //     v_mfma_f32_16x16x32_bf16 on bf16(136 + q) with a -136 constant-operand
 //     chain; W4A4 runs v_mfma_i32_16x16x64_i8 on 16 q; fp32 scale epilogue.
@@ -1319,6 +1322,9 @@ struct StreamArgs {
 #ifndef QSPEC_ST_PD16
 #define QSPEC_ST_PD16 2  // W4A16
 #endif
+#ifndef QSPEC_ST_PD16X
+#define QSPEC_ST_PD16X 2  // W4A16 with one or two activation loads per group
+#endif
 #ifndef QSPEC_ST_TARGET
 #define QSPEC_ST_TARGET 4096  // wavefronts the k-split aims for
 #endif
@@ -1329,18 +1335,48 @@ constexpr int kStreamMaxM = 16;
 constexpr int kStreamMaxW = 16;
 
 // One ring stage: the weight tile slot of this lane, its four group scales
-// and its activation fragment, all for one group.
-template <int MODE>
+// and its activation loads (XL 16-byte loads), all for one group.
+template <int MODE, int XL>
 struct StreamStage {
   uint4 w;
   uint2 s;
-  uint4 x[MODE == kW4A16 ? 4 : MODE == kW4A8 ? 2 : 1];
+  uint4 x[MODE == kW4A16 ? XL : MODE == kW4A8 ? 2 : 1];
 };
+
+// W4A16 activation fragments of few rows.  MFMA j of a group reads, in lane
+// (l16, lg), the 16-byte chunk 4 lg + j of activation row l16.  With XL = 4
+// every lane loads its own four chunks (one load each, whether or not its
+// row exists).  With M <= 8 (XL = 2) load i gives lane (8 t + m, lg) chunk
+// 4 lg + 2 i + t of row m, and with M <= 4 (XL = 1) the one load gives lane
+// (4 j + m, lg) chunk 4 lg + j of row m; a DPP shift left inside each
+// 16-lane row (lane l takes lane l + d) then hands chunk j to lane (m, lg).
+// Lanes of rows >= M receive other rows' values there, which only reach
+// output columns that are not stored, so each row's operands -- and its
+// result -- are bitwise those of XL = 4.
+template <int D>
+__device__ __forceinline__ uint4 row_shl(uint4 v) {
+  constexpr int ctrl = 0x100 + D;  // DPP row_shl:D
+  return make_uint4((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, ctrl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, ctrl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, ctrl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, ctrl, 0xF, 0xF, false));
+}
+template <int XL>
+__device__ __forceinline__ uint4 stream_xfrag(const uint4 (&x)[XL], int j) {
+  if constexpr (XL == 4) {
+    return x[j];
+  } else if constexpr (XL == 2) {
+    return (j & 1) ? row_shl<8>(x[j >> 1]) : x[j >> 1];
+  } else {
+    return j == 0 ? x[0] : j == 1 ? row_shl<4>(x[0]) : j == 2 ? row_shl<8>(x[0]) : row_shl<12>(x[0]);
+  }
+}
 
 
 template <int MODE, bool WITHP, int PD = (MODE == kW4A16 ? QSPEC_ST_PD16 : QSPEC_ST_PD4),
-          bool SW = false>
+          bool SW = false, int XL = 4>
 __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
+  static_assert(MODE == kW4A16 || XL == 4, "few-row activation loads are a W4A16 path");
   static_assert(!(WITHP && MODE == kW4A16), "the int32 partials output is an integer-mode path");
   extern __shared__ __attribute__((aligned(16))) float red_[];  // [nw][64][4] when nw > 1
   float(*red)[64][4] = reinterpret_cast<float(*)[64][4]>(red_);
@@ -1362,33 +1398,38 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   const int xrow_bytes = MODE == kW4A16 ? K * 2 : MODE == kW4A8 ? K : K / 2;
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(a.X), (short)0, M * xrow_bytes, 0x00020000);
-  const uint32_t xoff0 = (l16 < M ? (uint32_t)(l16 * xrow_bytes) : 0x80000000u) +
-                         (uint32_t)(lg * (MODE == kW4A16 ? 64 : MODE == kW4A8 ? 32 : 16));
+  // the row this lane loads and the chunk offset of its first load (W4A16:
+  // see stream_xfrag; XL = 4 and the integer modes: row l16)
+  const int xr = XL == 4 ? l16 : XL == 2 ? (l16 & 7) : (l16 & 3);
+  const int xc = XL == 4 ? 0 : XL == 2 ? (l16 >> 3) : (l16 >> 2);
+  const uint32_t xoff0 = (xr < M ? (uint32_t)(xr * xrow_bytes) : 0x80000000u) +
+                         (uint32_t)(lg * (MODE == kW4A16 ? 64 : MODE == kW4A8 ? 32 : 16) + 16 * xc);
   // activation bytes per group
   constexpr int xgb = MODE == kW4A16 ? kGroup * 2 : MODE == kW4A8 ? kGroup : kGroup / 2;
-  constexpr int nxl = MODE == kW4A16 ? 4 : MODE == kW4A8 ? 2 : 1;  // 16-byte loads per stage
+  constexpr int nxl = MODE == kW4A16 ? XL : MODE == kW4A8 ? 2 : 1;  // 16-byte loads per stage
+  constexpr int xstep = MODE == kW4A16 ? 64 / XL : 16;               // bytes between them
 
-  auto load = [&](StreamStage<MODE>& st, int g) {
+  auto load = [&](StreamStage<MODE, XL>& st, int g) {
     const int gg = min(w + nw * min(g, gl), G - 1);
     st.w = ld_stream(wt + (int64_t)gg * 1024);
     st.s = *reinterpret_cast<const uint2*>(sc + (int64_t)gg * 16);
     const uint32_t o = xoff0 + (uint32_t)(gg * xgb);
 #pragma unroll
     for (int i = 0; i < nxl; ++i) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, o + 16 * i, 0, 0);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, o + xstep * i, 0, 0);
       st.x[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
 
   v4f tot = {0.f, 0.f, 0.f, 0.f};
-  StreamStage<MODE> ring[PD];
+  StreamStage<MODE, XL> ring[PD];
 #pragma unroll
   for (int i = 0; i < PD; ++i) load(ring[i], g0 + i);
   const v8bf negb = as_v8bf(kNegBiasPair, kNegBiasPair, kNegBiasPair, kNegBiasPair);
 
   // one group from ring stage i, holding this wavefront's local group li
   auto group = [&](int i, int li) {
-    const StreamStage<MODE>& st = ring[i];
+    const StreamStage<MODE, XL>& st = ring[i];
     const uint32_t s01 = st.s.x, s23 = st.s.y;
     if (MODE == kW4A16) {
       // bf16(136 + q) x activations, then the -136 chain into the same
@@ -1399,7 +1440,8 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t aw[4], xi[4];
-        const uint32_t xw[4] = {st.x[j].x, st.x[j].y, st.x[j].z, st.x[j].w};
+        const uint4 xf = stream_xfrag<XL>(reinterpret_cast<const uint4(&)[XL]>(st.x), j);
+        const uint32_t xw[4] = {xf.x, xf.y, xf.z, xf.w};
         w4_to_bf16_biased(wv[j], aw);
         bf16x8_interleave(xw, xi);
         B[j] = as_v8bf(xi[0], xi[1], xi[2], xi[3]);
@@ -1539,13 +1581,35 @@ hipError_t launch_stream(const void* X, const float* Xs, const uint8_t* Wq, cons
       return hipGetLastError();
     }
     // integer modes on wide grids (at least QSPEC_ST_WIDE row blocks, few
-    // groups per wavefront): a three-group ring.  Measured on MI355X at
-    // M = 16, K = 2048: N = 11264 7.35 -> 5.72 us; the narrower shapes
-    // (N <= 4608) keep two groups, which streams faster there.  The ring
-    // depth changes when loads are issued, not what is computed: the rows
-    // are bitwise the same either way.
-    if (a.nrb >= QSPEC_ST_WIDE) {
+    // groups per wavefront) or where each wavefront walks at least 6 groups
+    // (a long K): a three-group ring.  Measured on MI355X at M = 16,
+    // K = 2048: N = 11264 7.35 -> 5.72 us; the Qwen2.5-7B down projection
+    // (9 groups per wavefront) at M = 8 / 16 10.1 / 11.9 -> 9.9 / 10.9 us.
+    // The narrower shapes with 3-4 groups per wavefront keep two (O at
+    // M = 8 4.2 against 4.8 us with three).  The ring depth changes when
+    // loads are issued, not what is computed: the rows are bitwise the same
+    // either way.
+    if (a.nrb >= QSPEC_ST_WIDE || (K / kGroup) / nw >= 6) {
       hipLaunchKernelGGL((stream_kernel<MODE, false, 3>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (MODE == kW4A16) {
+    // few rows: one or two activation loads per group instead of four
+    // (stream_xfrag); the rows are bitwise those of the four-load kernel
+    if (M <= 4) {
+      hipLaunchKernelGGL((stream_kernel<MODE, false, QSPEC_ST_PD16X, false, 1>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+      return hipGetLastError();
+    }
+    if (M <= 8) {
+      // a three-group ring where each wavefront walks at least 6 groups
+      // (measured at M = 5 / 8: down, 9 groups per wavefront, 12.5 / 15.4 ->
+      // 11.9 / 14.3 us; on 3-4 groups per wavefront QKV gains 0.6-0.9 us and
+      // O loses 0.3-0.7 us, so those keep two)
+      if ((K / kGroup) / nw >= 6)
+        hipLaunchKernelGGL((stream_kernel<MODE, false, 3, false, 2>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+      else
+        hipLaunchKernelGGL((stream_kernel<MODE, false, QSPEC_ST_PD16X, false, 2>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
       return hipGetLastError();
     }
   }
@@ -1856,10 +1920,14 @@ GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K / kGroup, kGemvGroup
 // gate|up projection (N = 37888) W4A16 at M = 64 / 96 / 128 runs 45 / 45 /
 // 65 us tiled against 52 / 78 / 80 us skinny, W4A4 at M = 96 / 128 40 / 42
 // against 46 / 48 us, while at M = 40 the skinny family is ahead (32 against
-// 44 us).  The choice depends on M, N and K only.
-int auto_pick(int64_t M, int64_t N, int64_t K, int64_t skinny_max, int64_t bm,
+// 44 us).  W4A16 takes the stream family up to 8 rows only: from 9 rows its
+// four activation loads per group cost more than the skinny family's LDS
+// staging (measured at M = 16: down 25.8 against 20.0 us, QKV 13.0 against
+// 9.4 us; at M = 5 down 11.9 against 18.3 us).  The choice depends on M, N
+// and K only.
+int auto_pick(int64_t M, int64_t N, int64_t K, int64_t stream_max, int64_t skinny_max, int64_t bm,
               int64_t tiled_min) {
-  if (M <= kStreamMaxM && cdiv(N, 64) < QSPEC_SK_TARGET_WG) return QSPEC_GEMM_STREAM;
+  if (M <= stream_max && cdiv(N, 64) < QSPEC_SK_TARGET_WG) return QSPEC_GEMM_STREAM;
   const int64_t tiles = cdiv(N, 256) * cdiv(M, bm);
   if (M <= skinny_max)
     return (M >= tiled_min && tiles >= 256) ? QSPEC_GEMM_TILED : QSPEC_GEMM_SKINNY;
@@ -1880,10 +1948,10 @@ hipError_t reduce(const float* part, int S, int64_t M, int64_t N, const float* X
 }  // namespace
 
 int w4a16_pick(int variant, int64_t M, int64_t N, int64_t K) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 128, 32, 64);
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 8, 128, 32, 64);
 }
 int w4a4_pick(int variant, int64_t M, int64_t N, int64_t K) {
-  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, 256, 64, 96);
+  return variant != QSPEC_GEMM_AUTO ? variant : auto_pick(M, N, K, kStreamMaxM, 256, 64, 96);
 }
 // W4A8 runs the stream family where W4A4 would, the skinny family otherwise
 int w4a8_pick(int variant, int64_t M, int64_t N, int64_t K) {

@@ -114,6 +114,9 @@ def test_gemm_validation():
     assert fam(W4A4, 16, 11264, 2048, 0) == b.GEMM_STREAM
     assert fam(W4A8, 16, 11264, 2048, 0) == b.GEMM_STREAM
     assert fam(W4A16, 5, 11264, 2048, 0) == b.GEMM_STREAM
+    assert fam(W4A16, 8, 3584, 18944, 0) == b.GEMM_STREAM
+    assert fam(W4A16, 9, 3584, 18944, 0) == b.GEMM_SKINNY      # W4A16 STREAM up to 8 rows
+    assert fam(W4A4, 16, 3584, 18944, 0) == b.GEMM_STREAM
     assert fam(W4A4, 8, 37888, 3584, 0) == b.GEMM_SKINNY
     assert fam(W4A4, 17, 11264, 2048, 0) == b.GEMM_SKINNY
     assert fam(W4A4, 256, 37888, 3584, 0) == b.GEMM_TILED

@@ -257,8 +257,10 @@ def test_skinny_workgroup_sizes(M, N, K):
 
 # ------------------------------------------------------------------ invariance
 def test_stream_row_invariance_both_modes():
-    """STREAM family: rows bitwise identical at M = 16, 5 and 1 (a k-split of
-    up to 16 wavefronts reduced in LDS in fixed order)."""
+    """STREAM family: rows bitwise identical at M = 16, 8, 5, 4 and 1 (a k-split
+    of up to 16 wavefronts reduced in LDS in fixed order; W4A16 loads the
+    activations of at most 4 / 8 rows with one / two loads per group and
+    moves them to their MFMA lanes by DPP shifts)."""
     N, K = 1000, 18944
     W, X = _case(19, 16, N, K)
     Wq, Ws = oracle.pack_w4(W)
@@ -267,7 +269,7 @@ def test_stream_row_invariance_both_modes():
     V = q.GEMM_STREAM
     Y16 = host(q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=V, N=N))
     Z16 = host(q.gemm_w4a4(dev(Xq), dev(Xs), Wq_d, Ws_d, variant=V, N=N))
-    for lo, hi in ((0, 5), (9, 10), (15, 16)):
+    for lo, hi in ((0, 5), (9, 10), (15, 16), (0, 4), (12, 16), (3, 11), (8, 16), (5, 8)):
         Y = host(q.gemm_w4a16(dev_bf16(X[lo:hi].copy()), Wq_d, Ws_d, variant=V, N=N))
         Z = host(q.gemm_w4a4(dev(Xq[lo:hi].copy()), dev(Xs[lo:hi].copy()), Wq_d, Ws_d,
                              variant=V, N=N))
