@@ -279,6 +279,27 @@ def test_stream_row_invariance_both_modes():
     assert_close(Z16, oracle.gemm_w4a4(Xq, Xs, Wq, Ws))
 
 
+@pytest.mark.parametrize("N,K", [(200, 18944), (1001, 2688)])
+def test_w4a16_stream_few_rows(N, K):
+    """W4A16 STREAM with at most 8 rows: one (M <= 4) or two (M <= 8)
+    activation loads per lane and group, each MFMA fragment moved into its
+    lane by a DPP row shift.  Every M from 1 to 8 against the oracle, and
+    bitwise the rows of the 16-row call (four loads per lane); ragged N, on
+    the three-group ring (K = 18944: 9 groups per wavefront) and the
+    two-group one (K = 2688: 2 groups per wavefront)."""
+    W, X = _case(41, 16, N, K)
+    Wq, Ws = oracle.pack_w4(W)
+    Wq_d, Ws_d = dev_w(Wq), dev_s(Ws)
+    V = q.GEMM_STREAM
+    Y16 = host(q.gemm_w4a16(dev_bf16(X), Wq_d, Ws_d, variant=V, N=N))
+    for M in range(1, 9):
+        say(f"stream few rows N={N} K={K} M={M}")
+        lo = (3 * M) % (17 - M)  # a window that is not always at row 0
+        Y = host(q.gemm_w4a16(dev_bf16(X[lo:lo + M].copy()), Wq_d, Ws_d, variant=V, N=N))
+        assert np.array_equal(Y.view(np.uint32), Y16[lo:lo + M].view(np.uint32)), (M, lo)
+        assert_close(Y, oracle.gemm_w4a16(X[lo:lo + M], Wq, Ws), what=f"w4a16 stream M={M}")
+
+
 @pytest.mark.parametrize("variant,N", [(q.GEMM_GEMV, 2048), (q.GEMM_SKINNY, 2048),
                                        (q.GEMM_SKINNY, 11264), (q.GEMM_TILED, 2048)])
 def test_w4a16_row_invariance(variant, N):
