@@ -80,6 +80,9 @@
 #ifndef QSPEC_SK_MIN_GPS
 #define QSPEC_SK_MIN_GPS 4     // the k-split leaves at least this many groups per slice
 #endif
+#ifndef QSPEC_SK_BIG_NWV
+#define QSPEC_SK_BIG_NWV 4      // wavefronts per workgroup on grids of more than 768 64-row tiles
+#endif
 #ifndef QSPEC_SK_TARGET_WG
 #define QSPEC_SK_TARGET_WG 256  // M <= 16 below this many 64-row tiles: the stream family
 #endif
@@ -1325,6 +1328,9 @@ struct StreamArgs {
 #ifndef QSPEC_ST_PD16X
 #define QSPEC_ST_PD16X 2  // W4A16 with one or two activation loads per group
 #endif
+#ifndef QSPEC_ST_PDL
+#define QSPEC_ST_PDL 1    // ring depth where each wavefront walks at least 6 groups (a long K)
+#endif
 #ifndef QSPEC_ST_TARGET
 #define QSPEC_ST_TARGET 4096  // wavefronts the k-split aims for
 #endif
@@ -1581,16 +1587,20 @@ hipError_t launch_stream(const void* X, const float* Xs, const uint8_t* Wq, cons
       return hipGetLastError();
     }
     // integer modes on wide grids (at least QSPEC_ST_WIDE row blocks, few
-    // groups per wavefront) or where each wavefront walks at least 6 groups
-    // (a long K): a three-group ring.  Measured on MI355X at M = 16,
-    // K = 2048: N = 11264 7.35 -> 5.72 us; the Qwen2.5-7B down projection
-    // (9 groups per wavefront) at M = 8 / 16 10.1 / 11.9 -> 9.9 / 10.9 us.
-    // The narrower shapes with 3-4 groups per wavefront keep two (O at
-    // M = 8 4.2 against 4.8 us with three).  The ring depth changes when
-    // loads are issued, not what is computed: the rows are bitwise the same
-    // either way.
-    if (a.nrb >= QSPEC_ST_WIDE || (K / kGroup) / nw >= 6) {
+    // groups per wavefront): a three-group ring.  Measured on MI355X at
+    // M = 16, K = 2048: N = 11264 7.35 -> 5.72 us.  Where each wavefront
+    // walks at least 6 groups (a long K) one group: the Qwen2.5-7B down
+    // projection (9 groups per wavefront) at M = 8 / 16 10.0 / 11.0 us
+    // against 10.2 / 12.1 (two groups) and 10.6 / 12.7 (three), one box.
+    // The narrower shapes with 3-4 groups per wavefront keep two (O at M = 8
+    // 4.2 against 4.8 us with one).  The ring depth changes when loads are
+    // issued, not what is computed: the rows are bitwise the same either way.
+    if (a.nrb >= QSPEC_ST_WIDE) {
       hipLaunchKernelGGL((stream_kernel<MODE, false, 3>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+      return hipGetLastError();
+    }
+    if ((K / kGroup) / nw >= 6) {
+      hipLaunchKernelGGL((stream_kernel<MODE, false, QSPEC_ST_PDL>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
       return hipGetLastError();
     }
   }
@@ -1602,12 +1612,14 @@ hipError_t launch_stream(const void* X, const float* Xs, const uint8_t* Wq, cons
       return hipGetLastError();
     }
     if (M <= 8) {
-      // a three-group ring where each wavefront walks at least 6 groups
-      // (measured at M = 5 / 8: down, 9 groups per wavefront, 12.5 / 15.4 ->
-      // 11.9 / 14.3 us; on 3-4 groups per wavefront QKV gains 0.6-0.9 us and
-      // O loses 0.3-0.7 us, so those keep two)
+      // where each wavefront walks at least 6 groups (a long K), the next
+      // group is requested only once the current one is consumed: measured
+      // on the down projection (9 groups per wavefront) at M = 5 / 8, one
+      // box, 12.3 / 14.5 us against 12.7 / 15.6 (two groups) and 13.2 / 16.9
+      // (three); on 3-4 groups per wavefront one group helps QKV (6.7 ->
+      // 6.1 us at M = 5) but costs O 0.4-0.8 us, so those keep two
       if ((K / kGroup) / nw >= 6)
-        hipLaunchKernelGGL((stream_kernel<MODE, false, 3, false, 2>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
+        hipLaunchKernelGGL((stream_kernel<MODE, false, QSPEC_ST_PDL, false, 2>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
       else
         hipLaunchKernelGGL((stream_kernel<MODE, false, QSPEC_ST_PD16X, false, 2>), dim3((unsigned)a.nrb), dim3(64 * nw), lds, s, a);
       return hipGetLastError();
@@ -1761,7 +1773,7 @@ struct SkinnyPlan {
 // balance themselves; they keep four wavefronts (measured on MI355X).
 constexpr int kSkinnyNWV[] = {4, 5, 8, 10};
 int skinny_nwv(int64_t N, int64_t S, int NB) {
-  if (cdiv(N, 64 * NB) * S > 768) return 4;
+  if (cdiv(N, 64 * NB) * S > 768) return QSPEC_SK_BIG_NWV;
   int best = 4;
   int64_t best_cost = -1;
   for (int nwv : kSkinnyNWV) {
