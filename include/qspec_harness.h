@@ -102,6 +102,19 @@ qspec_status qspec_add_rmsnorm_quant(float* x, int64_t x_stride, const float* ad
                                      int64_t add_stride, int64_t M, int64_t d, double eps,
                                      uint16_t* y, uint8_t* yq, float* ys, qspec_stream stream);
 
+/* qspec_add_rmsnorm with the W4A8 drafter's input in the same pass: besides
+ * y, yq int8 [M][d] and ys [M] receive exactly what qspec_quant_act8 gives
+ * for the bf16 rows y (per-token absmax / 127, codes rne(y / s) clamped to
+ * [-128, 127]; the 8-bit middle tier on the shared INT4 weights, a reading
+ * of the 8-bit variant in "SpecQuant: Speculative Decoding with
+ * Multi-Parent Quantization for Adaptive LLM Inference", Abstract), one
+ * launch instead of two in every W4A8 draft forward.  d is a multiple of
+ * 128 (<= 4096); yq, ys 16-byte aligned; other arguments and errors as for
+ * qspec_add_rmsnorm. */
+qspec_status qspec_add_rmsnorm_quant8(float* x, int64_t x_stride, const float* add,
+                                      int64_t add_stride, int64_t M, int64_t d, double eps,
+                                      uint16_t* y, int8_t* yq, float* ys, qspec_stream stream);
+
 /* SwiGLU: a[m][j] = bf16(silu(g) * u), g = gu[m][j], u = gu[m][ffn + j],
  * silu(g) = g / (1 + exp(-g)).  gu fp32 [M][2 ffn], a bf16 bits [M][ffn]. */
 qspec_status qspec_silu_mul(const float* gu, int64_t M, int64_t ffn, uint16_t* a,

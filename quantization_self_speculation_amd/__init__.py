@@ -50,6 +50,7 @@ from .binding import (  # noqa: F401
     silu_mul,
     silu_mul_pairs,
     add_rmsnorm_quant,
+    add_rmsnorm_quant8,
     argmax,
     spec_prepare,
     spec_commit,

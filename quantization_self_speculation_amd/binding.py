@@ -78,6 +78,7 @@ def lib():
             "qspec_silu_mul": (I, [P, I64, I64, P, P]),
             "qspec_silu_mul_pairs": (I, [P, I64, I64, P, P]),
             "qspec_add_rmsnorm_quant": (I, [P, I64, P, I64, I64, I64, ctypes.c_double, P, P, P, P]),
+            "qspec_add_rmsnorm_quant8": (I, [P, I64, P, I64, I64, I64, ctypes.c_double, P, P, P, P]),
             "qspec_argmax": (I, [P, I64, I64, P, I64, P]),
             "qspec_spec_prepare": (I, [I, I64, I, I, P, P, P, P, P, P, P]),
             "qspec_spec_commit": (I, [I64, I, P, P, P, P, I64, P, I64, P, I, P, P]),
@@ -480,6 +481,27 @@ def add_rmsnorm_quant(x, add, y, yq, ys, eps):
     _check(lib().qspec_add_rmsnorm_quant(_ptr(x), int(x.stride(0)), _ptr(add), a_stride, M, d,
                                          float(eps), _ptr(y), _ptr(yq), _ptr(ys), _stream()),
            "qspec_add_rmsnorm_quant")
+
+
+def add_rmsnorm_quant8(x, add, y, yq, ys, eps):
+    """add_rmsnorm, and the 8-bit codes / scales of y (as quant_act8(y) gives
+    them) into yq int8 [M, d] and ys fp32 [M] in the same pass."""
+    _dev(x, "x", torch.float32)
+    _need(y, "y", torch.bfloat16)
+    M, d = y.shape
+    _need(yq, "yq", torch.int8, (M, d))
+    _need(ys, "ys", torch.float32, (M,))
+    if x.dim() != 2 or tuple(x.shape) != (M, d) or x.stride(1) != 1:
+        raise ValueError("x must be a row-strided [M, d] view")
+    a_stride = 0
+    if add is not None:
+        _dev(add, "add", torch.float32)
+        if add.dim() != 2 or tuple(add.shape) != (M, d) or add.stride(1) != 1:
+            raise ValueError("add must be a row-strided [M, d] view")
+        a_stride = int(add.stride(0))
+    _check(lib().qspec_add_rmsnorm_quant8(_ptr(x), int(x.stride(0)), _ptr(add), a_stride, M, d,
+                                          float(eps), _ptr(y), _ptr(yq), _ptr(ys), _stream()),
+           "qspec_add_rmsnorm_quant8")
 
 
 def rope_kv(qkv, seq, pos, q_out, kcache, vcache, n_heads, n_kv, rope_base):

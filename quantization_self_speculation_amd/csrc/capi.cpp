@@ -506,6 +506,25 @@ qspec_status qspec_add_rmsnorm_quant(float* x, int64_t x_stride, const float* ad
                     "add_rmsnorm_quant launch");
 }
 
+qspec_status qspec_add_rmsnorm_quant8(float* x, int64_t x_stride, const float* add,
+                                      int64_t add_stride, int64_t M, int64_t d, double eps,
+                                      uint16_t* y, int8_t* yq, float* ys, qspec_stream stream) {
+  QS_REQUIRE(d >= 1 && d <= QSPEC_MAX_D && x_stride >= d && M >= 1 && M <= kMaxDim,
+             QSPEC_ERR_SHAPE, "need 1 <= d <= %d, x_stride >= d, M >= 1", QSPEC_MAX_D);
+  QS_TRY(check_k(d));
+  QS_REQUIRE(add == nullptr || add_stride >= d, QSPEC_ERR_SHAPE, "need add_stride >= d");
+  QS_REQUIRE(eps >= 0.0, QSPEC_ERR_SHAPE, "eps must be >= 0");
+  QS_EPTR(x);
+  if (add != nullptr) QS_EPTR(add);
+  QS_EPTR(y);
+  QS_PTR(yq);
+  QS_PTR(ys);
+  QS_TRY(device_check());
+  return hip_result(launch_add_rmsnorm_quant8(x, x_stride, add, add_stride, M, d, eps, y, yq, ys,
+                                              (hipStream_t)stream),
+                    "add_rmsnorm_quant8 launch");
+}
+
 qspec_status qspec_rope_kv(const float* qkv, int64_t M, int n_heads, int n_kv, const int32_t* seq,
                            const int32_t* pos, double rope_base, float* q_out, uint16_t* kcache,
                            uint16_t* vcache, int64_t B, int64_t cap, qspec_stream stream) {

@@ -175,6 +175,17 @@ __device__ __forceinline__ int quant_code_act(float v, float s, float r) {
   return (int)fminf(fmaxf(k, -8.0f), 7.0f);
 }
 
+// The 8-bit per-token code (W4A8 tier): rne(v / s) clamped to [-128, 127].
+// |v / s| <= 127, so v * r is within 127 * 2^-23 < 2^-16 of the exact
+// quotient and within 2^-15 of the IEEE quotient; farther than that from a
+// half-integer both round alike, nearer the IEEE quotient decides.
+__device__ __forceinline__ int quant_code_act8(float v, float s, float r) {
+  const float qa = v * r;
+  float k = __builtin_rintf(qa);
+  if (!(fabsf(qa - k) < 0.5f - 0x1p-15f)) k = __builtin_rintf(v / s);
+  return (int)fminf(fmaxf(k, -128.0f), 127.0f);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }

@@ -65,7 +65,9 @@ constexpr int kNormPer = 16;  // d <= 4096
 // takes them, so the codes equal that quantizer's on the stored bf16 row.
 // The even thread of each pair packs its element's code (low nibble) with
 // its neighbour's (high nibble).
-template <int PER>
+// BITS = 8: the W4A8 drafter's codes instead (absmax / 127, one byte per
+// element, as the stand-alone 8-bit quantizer takes them).
+template <int PER, int BITS>
 __device__ __forceinline__ void quant_row_bf16(const uint16_t (&yb)[PER], int n, float* red,
                                                uint8_t* __restrict__ q, float* __restrict__ qs) {
   float a = 0.f;
@@ -78,18 +80,24 @@ __device__ __forceinline__ void quant_row_bf16(const uint16_t (&yb)[PER], int n,
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = a / 7.0f;
+  const float s = a / (BITS == 4 ? 7.0f : 127.0f);
   const float r = 1.0f / s;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int j = (int)threadIdx.x + 256 * i;
-    const int c = (j < n && s != 0.0f) ? quant_code_act(__uint_as_float((uint32_t)yb[i] << 16), s, r) : 0;
+    const float v = __uint_as_float((uint32_t)yb[i] << 16);
+    if (BITS == 8) {
+      if (j < n) q[j] = (uint8_t)(s != 0.0f ? quant_code_act8(v, s, r) : 0);
+      continue;
+    }
+    const int c = (j < n && s != 0.0f) ? quant_code_act(v, s, r) : 0;
     const int nb = __shfl_xor(c, 1, 64);
     if (!(threadIdx.x & 1) && j < n) q[j >> 1] = (uint8_t)((c & 0xF) | ((nb & 0xF) << 4));
   }
   if (threadIdx.x == 0) *qs = s;
 }
 
+template <int BITS>
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x, int64_t xs,
                                                           const float* __restrict__ add, int64_t as,
                                                           int d, double eps,
@@ -134,7 +142,8 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
     yb[i] = f64_to_bf16_rne((double)v[i] / den);
     if (j < d) yr[j] = yb[i];
   }
-  if (yq != nullptr) quant_row_bf16<kNormPer>(yb, d, redf, yq + m * (d / 2), ys + m);  // uniform
+  if (yq != nullptr)  // uniform
+    quant_row_bf16<kNormPer, BITS>(yb, d, redf, yq + m * (BITS == 4 ? d / 2 : d), ys + m);
 }
 
 // The same add + RMSNorm (+ codes) for 16-byte aligned rows with d % 4 == 0:
@@ -155,6 +164,7 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
 constexpr int kNormThreads = QSPEC_NORM_THREADS;
 constexpr int kNormV4 = 4096 / (4 * kNormThreads);  // float4 groups per thread (d <= 4096)
 
+template <int BITS>
 __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_v4_kernel(
     float* __restrict__ x, int64_t xs, const float* __restrict__ add, int64_t as, int d, double eps,
     uint16_t* __restrict__ y, uint8_t* __restrict__ yq, float* __restrict__ ys) {
@@ -228,17 +238,33 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_v4_kernel(
   a = redf[0];
 #pragma unroll
   for (int k = 1; k < NW; ++k) a = fmaxf(a, redf[k]);
-  const float sc = a / 7.0f;
+  const float sc = a / (BITS == 4 ? 7.0f : 127.0f);
   const float r = 1.0f / sc;
-  uint16_t* qr = reinterpret_cast<uint16_t*>(yq + m * (d / 2));
+  if (BITS == 8) {
+    // one byte per element: a thread's four codes are one 4-byte store
+    uint32_t* qr = reinterpret_cast<uint32_t*>(yq + m * d);
 #pragma unroll
-  for (int i = 0; i < kNormV4; ++i) {
-    const int gi = (int)threadIdx.x + kNormThreads * i;
-    if (gi < ng) {
-      int c[4];
+    for (int i = 0; i < kNormV4; ++i) {
+      const int gi = (int)threadIdx.x + kNormThreads * i;
+      if (gi < ng) {
+        uint32_t wv = 0u;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = sc != 0.0f ? quant_code_act(bf16_to_f32(yb[i][k]), sc, r) : 0;
-      qr[gi] = (uint16_t)((c[0] & 0xF) | ((c[1] & 0xF) << 4) | ((c[2] & 0xF) << 8) | ((c[3] & 0xF) << 12));
+        for (int k = 0; k < 4; ++k)
+          wv |= (uint32_t)((sc != 0.0f ? quant_code_act8(bf16_to_f32(yb[i][k]), sc, r) : 0) & 0xFF) << (8 * k);
+        qr[gi] = wv;
+      }
+    }
+  } else {
+    uint16_t* qr = reinterpret_cast<uint16_t*>(yq + m * (d / 2));
+#pragma unroll
+    for (int i = 0; i < kNormV4; ++i) {
+      const int gi = (int)threadIdx.x + kNormThreads * i;
+      if (gi < ng) {
+        int c[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = sc != 0.0f ? quant_code_act(bf16_to_f32(yb[i][k]), sc, r) : 0;
+        qr[gi] = (uint16_t)((c[0] & 0xF) | ((c[1] & 0xF) << 4) | ((c[2] & 0xF) << 8) | ((c[3] & 0xF) << 12));
+      }
     }
   }
   if (threadIdx.x == 0) ys[m] = sc;
@@ -774,22 +800,22 @@ hipError_t launch_embed(const uint16_t* emb, int64_t V, int64_t d, const int32_t
 // The vector kernel wherever its alignment holds: x, add and their row
 // strides in whole 16-byte groups, y 8-byte and the codes 2-byte aligned.
 static bool norm_v4_ok(const float* x, int64_t xs, const float* add, int64_t as, int64_t d,
-                       const uint16_t* y, const uint8_t* yq) {
+                       const uint16_t* y, const uint8_t* yq, int qalign = 2) {
 #ifdef QSPEC_NORM_SCALAR
   return false;
 #endif
   const auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
   return d % 4 == 0 && al(x, 16) && xs % 4 == 0 && (add == nullptr || (al(add, 16) && as % 4 == 0)) &&
-         al(y, 8) && (yq == nullptr || al(yq, 2));
+         al(y, 8) && (yq == nullptr || al(yq, qalign));
 }
 
 hipError_t launch_add_rmsnorm(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
                               int64_t d, double eps, uint16_t* y, hipStream_t s) {
   if (norm_v4_ok(x, xs, add, as, d, y, nullptr))
-    hipLaunchKernelGGL(add_rmsnorm_v4_kernel, dim3((unsigned)M), dim3(kNormThreads), 0, s, x, xs,
+    hipLaunchKernelGGL(add_rmsnorm_v4_kernel<4>, dim3((unsigned)M), dim3(kNormThreads), 0, s, x, xs,
                        add, as, (int)d, eps, y, nullptr, nullptr);
   else
-    hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
+    hipLaunchKernelGGL(add_rmsnorm_kernel<4>, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
                        (int)d, eps, y, nullptr, nullptr);
   return hipGetLastError();
 }
@@ -798,11 +824,26 @@ hipError_t launch_add_rmsnorm_quant(float* x, int64_t xs, const float* add, int6
                                     int64_t d, double eps, uint16_t* y, uint8_t* yq, float* ys,
                                     hipStream_t s) {
   if (norm_v4_ok(x, xs, add, as, d, y, yq))
-    hipLaunchKernelGGL(add_rmsnorm_v4_kernel, dim3((unsigned)M), dim3(kNormThreads), 0, s, x, xs,
+    hipLaunchKernelGGL(add_rmsnorm_v4_kernel<4>, dim3((unsigned)M), dim3(kNormThreads), 0, s, x, xs,
                        add, as, (int)d, eps, y, yq, ys);
   else
-    hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
+    hipLaunchKernelGGL(add_rmsnorm_kernel<4>, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
                        (int)d, eps, y, yq, ys);
+  return hipGetLastError();
+}
+
+// the W4A8 drafter's 8-bit codes: the 16-byte kernel stores a thread's four
+// codes as one 4-byte word, so yq must be 4-byte aligned for it
+hipError_t launch_add_rmsnorm_quant8(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
+                                     int64_t d, double eps, uint16_t* y, int8_t* yq, float* ys,
+                                     hipStream_t s) {
+  uint8_t* q = reinterpret_cast<uint8_t*>(yq);
+  if (norm_v4_ok(x, xs, add, as, d, y, q, 4))
+    hipLaunchKernelGGL(add_rmsnorm_v4_kernel<8>, dim3((unsigned)M), dim3(kNormThreads), 0, s, x, xs,
+                       add, as, (int)d, eps, y, q, ys);
+  else
+    hipLaunchKernelGGL(add_rmsnorm_kernel<8>, dim3((unsigned)M), dim3(256), 0, s, x, xs, add, as,
+                       (int)d, eps, y, q, ys);
   return hipGetLastError();
 }
 

@@ -99,6 +99,9 @@ hipError_t launch_silu_mul_pairs(const float* gu, int64_t M, int64_t F, uint16_t
 hipError_t launch_add_rmsnorm_quant(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
                                     int64_t d, double eps, uint16_t* y, uint8_t* yq, float* ys,
                                     hipStream_t s);
+hipError_t launch_add_rmsnorm_quant8(float* x, int64_t xs, const float* add, int64_t as, int64_t M,
+                                     int64_t d, double eps, uint16_t* y, int8_t* yq, float* ys,
+                                     hipStream_t s);
 hipError_t launch_argmax(const float* x, int64_t M, int64_t V, int32_t* out, int64_t stride,
                          hipStream_t s);
 hipError_t launch_spec_prepare(int phase, int64_t B, int gamma, int j, const int32_t* len,

@@ -91,15 +91,6 @@ __device__ __forceinline__ uint32_t pack8(uint4 v, float s, float r) {
 }
 
 // The 8-bit code of v at s = absmax / 127 (s > 0), r = 1 / s: here
-// |v / s| <= 127, so v * r is within 127 * 2^-23 < 2^-16 of the exact
-// quotient and within 2^-15 of the IEEE quotient; farther than that from a
-// half-integer both round alike, nearer the IEEE quotient decides.
-__device__ __forceinline__ int quant_code_act8(float v, float s, float r) {
-  const float qa = v * r;
-  float k = __builtin_rintf(qa);
-  if (!(fabsf(qa - k) < 0.5f - 0x1p-15f)) k = __builtin_rintf(v / s);
-  return (int)fminf(fmaxf(k, -128.0f), 127.0f);
-}
 
 // eight bf16 values -> their eight 8-bit codes, code i in byte i
 __device__ __forceinline__ uint2 pack8_i8(uint4 v, float s, float r) {

@@ -160,7 +160,8 @@ class Decoder:
             b.gemm_w4a4(Xq, Xs, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
         elif mode == DRAFT8:
             Xq8, Xs = _view(self.Xq8, M, K), _view(self.Xs, M)
-            b.quant_act8(X, Xq8, Xs)
+            if not coded:
+                b.quant_act8(X, Xq8, Xs)
             b.gemm_w4a8(Xq8, Xs, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
         else:
             b.gemm_w4a16(X, Wq, Ws, variant=variant, Y=Y, ws=self.ws, N=N)
@@ -195,13 +196,17 @@ class Decoder:
                 # gate|up outputs back in gate-then-up column order
                 trace.append((li, name, X.clone(), _unpair_cols(Y) if name == "gu" else Y.clone()))
 
-        # in draft mode the RMSNorm kernel also writes the drafter's 4-bit
-        # codes of its bf16 output (one launch, not two)
-        draft = mode == DRAFT
+        # in draft modes the RMSNorm kernel also writes the drafter's 4-bit
+        # (W4A4) or 8-bit (W4A8) codes of its bf16 output (one launch, not two)
+        draft = mode in (DRAFT, DRAFT8)
 
         def norm(x_, add_, h_):
-            if draft:
+            if mode == DRAFT:
                 b.add_rmsnorm_quant(x_, add_, h_, *self._codes(h_.shape[0], d), cfg.eps)
+            elif mode == DRAFT8:
+                rows = h_.shape[0]
+                b.add_rmsnorm_quant8(x_, add_, h_, _view(self.Xq8, rows, d), _view(self.Xs, rows),
+                                     cfg.eps)
             else:
                 b.add_rmsnorm(x_, add_, h_, cfg.eps)
 
@@ -237,9 +242,8 @@ class Decoder:
                     b.gemm_w4a16_swiglu(h, Wq, Ws, A=a, ws=self.ws, N=N)
                 elif mode == DRAFT:
                     b.gemm_w4a4_swiglu(*self._codes(M, K), Wq, Ws, A=a, N=N)
-                else:
+                else:  # the codes of h, written by the RMSNorm above
                     Xq8, Xs = _view(self.Xq8, M, K), _view(self.Xs, M)
-                    b.quant_act8(h, Xq8, Xs)
                     b.gemm_w4a8_swiglu(Xq8, Xs, Wq, Ws, A=a, N=N)
                 if trace is not None:
                     trace.append((li, "gu_swiglu", h.clone(), a.clone()))

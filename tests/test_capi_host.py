@@ -211,6 +211,10 @@ def test_harness_validation():
     assert L.qspec_add_rmsnorm_quant(A, 200, NUL, 0, 2, 200, D(1e-6), A, A, A, S) == ESHAPE
     assert L.qspec_add_rmsnorm_quant(A, 256, NUL, 0, 2, 256, D(1e-6), A, NUL, A, S) == ENULL
     assert L.qspec_add_rmsnorm_quant(A, 256, NUL, 0, 2, 256, D(1e-6), A, A, MIS, S) == EALIGN
+    assert L.qspec_add_rmsnorm_quant8(A, 200, NUL, 0, 2, 200, D(1e-6), A, A, A, S) == ESHAPE
+    assert L.qspec_add_rmsnorm_quant8(A, 256, NUL, 0, 2, 256, D(1e-6), A, NUL, A, S) == ENULL
+    assert L.qspec_add_rmsnorm_quant8(A, 256, NUL, 0, 2, 256, D(1e-6), A, A, MIS, S) == EALIGN
+    assert L.qspec_add_rmsnorm_quant8(A, 128, NUL, 0, 2, 256, D(1e-6), A, A, A, S) == ESHAPE
     # silu, argmax
     assert L.qspec_silu_mul(A, 0, 10, A, S) == ESHAPE
     assert L.qspec_silu_mul_pairs(A, 4, 12, A, S) == ESHAPE       # ffn % 8 != 0

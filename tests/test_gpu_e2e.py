@@ -325,6 +325,39 @@ def test_quantizer_fused_into_rmsnorm(M, d):
         assert np.array_equal(host(yq), qo) and np.array_equal(host(ys), so)
 
 
+@pytest.mark.parametrize("M,d,off", [(9, 256, 0), (37, 2048, 0), (3, 4096, 0), (5, 2048, 1)])
+def test_quantizer8_fused_into_rmsnorm(M, d, off):
+    """add_rmsnorm_quant8 (the W4A8 drafter's input): the bf16 output and the
+    residual bitwise those of add_rmsnorm, and the 8-bit codes and scales
+    bitwise those of quant_act8 on the bf16 rows -- and of the oracle's 8-bit
+    quantizer on them (with and without the residual add; rows that start
+    one float past a 16-byte boundary take the scalar kernel)."""
+    say(f"fused 8-bit quantizer M={M} d={d} offset={off}")
+    rng = synth.make_rng(57, d + off)
+    big = torch.from_numpy(rng.standard_normal((M, d + 128)).astype(np.float32)).to("cuda:0")
+    add = torch.from_numpy(rng.standard_normal((M, d)).astype(np.float32)).to("cuda:0")
+    for a_ in (None, add):
+        x1 = big.clone()[:, :d]
+        buf = torch.zeros(M * (d + 128) + off, dtype=torch.float32, device="cuda:0")
+        x2 = buf[off:off + M * (d + 128)].view(M, d + 128)[:, :d]
+        x2.copy_(big[:, :d])
+        y1 = torch.empty((M, d), dtype=torch.bfloat16, device="cuda:0")
+        y2 = torch.empty_like(y1)
+        yq = torch.empty((M, d), dtype=torch.int8, device="cuda:0")
+        ys = torch.empty((M,), dtype=torch.float32, device="cuda:0")
+        qb.add_rmsnorm(x1, a_, y1, 1e-6)
+        qb.add_rmsnorm_quant8(x2, a_, y2, yq, ys, 1e-6)
+        q1, s1 = q.quant_act8(y1)
+        if off == 0:  # the same kernel as add_rmsnorm: the same bits
+            assert np.array_equal(host_bits16(y1), host_bits16(y2))
+        assert np.array_equal(host(x1).view(np.uint32), host(x2).view(np.uint32))
+        q2, s2 = q.quant_act8(y2)
+        assert np.array_equal(host(yq), host(q2))
+        assert np.array_equal(host(ys).view(np.uint32), host(s2).view(np.uint32))
+        qo, so = oracle.quant_act8(host_bits16(y2))
+        assert np.array_equal(host(yq), qo) and np.array_equal(host(ys), so)
+
+
 def test_spec_prepare_and_commit():
     B, g = 3, 2
     length = np.array([10, 4, 7], np.int32)
