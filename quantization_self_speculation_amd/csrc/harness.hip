@@ -474,7 +474,7 @@ __device__ __forceinline__ void attend(const float* __restrict__ q, const uint16
       // running max, rescale, p = exp(s - m), chunk sums (lane t of the chunk)
 #pragma unroll
       for (int hh = 0; hh < HPB; ++hh) {
-        cm[hh] = wave_max(cm[hh]);  // exact: every lane gets the chunk's largest score
+        cm[hh] = wave_max_dpp(cm[hh]);  // exact: every lane gets the chunk's largest score
         const float mn = fmaxf(rm[hh], cm[hh]);
         const float f = rm[hh] == -INFINITY ? 0.f : __expf(rm[hh] - mn);
         rl[hh] *= f;

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(NT) void quant_act_rot_kernel(const uint16_t* __res
       a = fmaxf(a, fabsf(f[i][e]));
     }
   }
-  a = wave_max(a);
+  a = wave_max_dpp(a);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
   a = red[0];
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void quant_act_rot_long_kernel(const uint16_t*
 #pragma unroll
     for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e] * 0.0625f));
   }
-  a = wave_max(a);
+  a = wave_max_dpp(a);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -279,7 +279,8 @@ __global__ __launch_bounds__(NT) void quant_act_kernel(const uint16_t* __restric
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < NC; ++i) a = fmaxf(a, absmax8(v[i]));
-  a = wave_max(a);
+  // the row max over DPP lane moves (a maximum is the same in any order)
+  a = wave_max_dpp(a);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
   a = red[0];
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(256) void quant_act_long_kernel(const uint16_t* __r
   const int64_t nch = K / 8;
   float a = 0.0f;
   for (int64_t c = threadIdx.x; c < nch; c += 256) a = fmaxf(a, absmax8(row[c]));
-  a = wave_max(a);
+  a = wave_max_dpp(a);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void pass1_kernel(const float* __restrict__ tg
   float mx = fmaxf(hv, tv);
 #pragma unroll
   for (int k = 0; k < QPT; ++k) mx = fmaxf(mx, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
-  mx = wave_max(mx);
+  mx = wave_max_dpp(mx);
   if (lane == 0) sm[w] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
@@ -236,7 +236,7 @@ __device__ __forceinline__ void row_lse(const float* pm, const double* ps, int64
                                         int lane, float& M, double& S) {
   float m = -INFINITY;
   for (int c = lane; c < nck; c += 64) m = fmaxf(m, pm[row * nck + c]);
-  m = wave_max(m);
+  m = wave_max_dpp(m);
   double s = 0.0;
   for (int c = lane; c < nck; c += 64) {
     const float mc = pm[row * nck + c];
@@ -303,7 +303,7 @@ __device__ Decision block_decide(const float* __restrict__ tgt, const float* __r
     for (int k = 0; k < RPW; ++k) {
       const int r = w + 4 * k;
       if (r >= nr) break;  // uniform over the wavefront
-      const float M = wave_max(pmv[k]);
+      const float M = wave_max_dpp(pmv[k]);
       double S = psv[k] * (double)exp_diff(pmv[k], M);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
