@@ -1437,7 +1437,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
   auto group = [&](int i, int li) {
     const StreamStage<MODE, XL>& st = ring[i];
     const uint32_t s01 = st.s.x, s23 = st.s.y;
-    if (MODE == kW4A16) {
+    if constexpr (MODE == kW4A16) {
       // bf16(136 + q) x activations, then the -136 chain into the same
       // accumulator: acc = sum_k x (136 + q) - 136 sum_k x
       const uint32_t wv[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
@@ -1446,7 +1446,7 @@ __global__ __launch_bounds__(1024) void stream_kernel(const StreamArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t aw[4], xi[4];
-        const uint4 xf = stream_xfrag<XL>(reinterpret_cast<const uint4(&)[XL]>(st.x), j);
+        const uint4 xf = stream_xfrag<XL>(st.x, j);
         const uint32_t xw[4] = {xf.x, xf.y, xf.z, xf.w};
         w4_to_bf16_biased(wv[j], aw);
         bf16x8_interleave(xw, xi);
@@ -1935,7 +1935,7 @@ GemvPlan plan_gemv(int64_t K) { return GemvPlan{(int)cdiv(K / kGroup, kGemvGroup
 // 44 us).  W4A16 takes the stream family up to 8 rows only: from 9 rows its
 // four activation loads per group cost more than the skinny family's LDS
 // staging (measured at M = 16: down 25.8 against 20.0 us, QKV 13.0 against
-// 9.4 us; at M = 5 down 11.9 against 18.3 us).  The choice depends on M, N
+// 9.4 us; at M = 5 down 12.3 against 18.3 us).  The choice depends on M, N
 // and K only.
 int auto_pick(int64_t M, int64_t N, int64_t K, int64_t stream_max, int64_t skinny_max, int64_t bm,
               int64_t tiled_min) {
